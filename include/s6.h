@@ -1,0 +1,119 @@
+/*
+ * s6.h -- C ABI of libs6, the selective-SSM scan (S6) library for AMD MI355X
+ * (gfx950).
+ *
+ * The operation.  Sources: the page "【LLM】Mamba和State Space Models详解" (a
+ * Chinese translation of a visual guide to Mamba and state space models):
+ *   §2.2  continuous SSM h'(t) = A h(t) + B x(t), y(t) = C h(t) + D x(t);
+ *         D is a skip connection.
+ *   §2.3  zero-order-hold discretisation with a learnable step Delta; the
+ *         continuous A is kept and discretised on the fly.  (The formula
+ *         image is missing; this library uses dA = exp(Delta*A[d,n]) and
+ *         dBx = Delta*B[n]*x.)
+ *   §2.4  recurrent form: h_k = dA h_{k-1} + dB x_k, then y_k = C h_k (the
+ *         output is read from the updated state).
+ *   §3.2  selection: Delta (batch, D, L), B and C (batch, N, L) vary per
+ *         token; A (D, N) does not.
+ *   §3.3  the scan over time, evaluated with associativity; §3.4 fusion of
+ *         discretisation, scan and the product with C in one pass that
+ *         never writes the (batch, D, L, N) state to memory.
+ * The news page on the Mamba paper ("屹立不倒的 Transformer 迎來了一個強勁競爭者",
+ * sections 選擇機制 and 架構) notes that a recurrent model with a finite state
+ * needs constant time per generated token: s6_state_update is that step.
+ * The optional output gate y <- y * SiLU(z), SiLU(z) = z / (1 + e^-z), is
+ * applied after the skip term; it is not drawn on the pages and is the plain
+ * reading of the gated Mamba output.
+ *
+ * Per (batch b, channel d, state n), for t = 0 .. L-1:
+ *   h[n]   = exp(delta[b,d,t] * A[d,n]) * h[n] + delta[b,d,t] * Bm[b,n,t] * x[b,d,t]
+ *   y[b,d,t] = (sum_n Cm[b,n,t] * h[n] + Dskip[d] * x[b,d,t]) * SiLU(z[b,d,t])
+ * starting from h = h0[b,d,:] (or 0); h_last[b,d,:] is h after token L-1.
+ *
+ * Conventions shared by every entry point
+ *   Layout: contiguous row-major, last index fastest.
+ *     x, delta, z, y : (batch, dim, seqlen)     Bm, Cm : (batch, dstate, seqlen)
+ *     A : (dim, dstate)   Dskip : (dim)          h0, h_last, h : (batch, dim, dstate)
+ *     decode step: x, delta, z, y : (batch, dim); Bm, Cm : (batch, dstate)
+ *   in_dtype: S6_F32 or S6_BF16; it applies to x, delta, Bm, Cm and z.  A,
+ *     Dskip, h0, h, h_last and y are always fp32; the state is fp32.
+ *   Pointers: device memory owned by the caller (for example torch
+ *     allocations), aligned to their element size; 16-byte alignment and a
+ *     seqlen that is a multiple of 8 select the vectorised load path.
+ *     Outputs must not alias inputs (except h, updated in place by
+ *     s6_state_update).
+ *   stream: a hipStream_t passed as void*; NULL is the default stream.  Every
+ *     call only enqueues work and returns; the caller synchronises.
+ *   Sizes: batch, dim, seqlen >= 0 (zero means no work; with seqlen == 0,
+ *     h_last receives h0 or zeros), 1 <= dstate <= 32, and
+ *     batch*dim*max(seqlen,1)*max(dstate,...) must fit in int64.
+ *   Errors: 0 (S6_OK) or a negative S6_ERR_* code.  All argument checks run
+ *     before any HIP call, so a rejected call has no side effect.  Values are
+ *     not checked: NaN/Inf propagate.  Accuracy is specified for A <= 0 and
+ *     delta >= 0 (decaying states).
+ *   Memory: s6_scan_fwd and s6_last_state take temporary device memory
+ *     (packed B/C and, for few long rows, per-segment carries) from the
+ *     stream-ordered allocator (hipMallocAsync) and release it on the same
+ *     stream before returning.  s6_state_update allocates nothing.
+ */
+#ifndef S6_H_
+#define S6_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define S6_F32 0
+#define S6_BF16 1
+
+#define S6_OK 0
+#define S6_ERR_NULL (-1)        /* a required pointer is NULL */
+#define S6_ERR_SHAPE (-2)       /* a size is negative or the element count overflows */
+#define S6_ERR_DTYPE (-3)       /* in_dtype is not S6_F32 or S6_BF16 */
+#define S6_ERR_UNSUPPORTED (-4) /* dstate outside 1..32 */
+#define S6_ERR_ALIGN (-5)       /* a pointer is not aligned to its element size */
+#define S6_ERR_HIP (-6)         /* a HIP call failed; s6_status_str gives the detail */
+
+/* Version of this ABI, major*10000 + minor*100 + patch. */
+int s6_version(void);
+
+/* Human-readable text for a status code.  For S6_ERR_HIP it includes the
+ * last HIP error seen by this thread.  The string is static or thread-local. */
+const char* s6_status_str(int status);
+
+/* Fused selective scan: discretisation, recurrence over the whole sequence,
+ * contraction with C, skip term and optional gate, in one pass that keeps
+ * the state on chip.
+ *   x, delta, Bm, Cm, A : required.
+ *   Dskip : nullable (no skip term).    z : nullable (no gate).
+ *   h0    : nullable (zero initial state).
+ *   y     : required output (batch, dim, seqlen) fp32.
+ *   h_last: nullable output (batch, dim, dstate) fp32, the state after the
+ *           last token. */
+int s6_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
+                const float* Dskip, const void* z, const float* h0, float* y, float* h_last,
+                void* stream);
+
+/* Final state only (prefill -> decode hand-off, or a sequence shard's
+ * carry): the recurrence of s6_scan_fwd without C, D, z or y.
+ *   h0 : nullable.   h_last : required output (batch, dim, dstate) fp32. */
+int s6_last_state(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                  const void* x, const void* delta, const float* A, const void* Bm,
+                  const float* h0, float* h_last, void* stream);
+
+/* One decode token for every (batch, channel): h is read, advanced by one
+ * step and written back in place; y receives the token's output.
+ *   h : required, in/out (batch, dim, dstate) fp32.
+ *   x, delta, z : (batch, dim); Bm, Cm : (batch, dstate); Dskip and z nullable.
+ *   y : required output (batch, dim) fp32. */
+int s6_state_update(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, float* h,
+                    const void* x, const void* delta, const float* A, const void* Bm,
+                    const void* Cm, const float* Dskip, const void* z, float* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S6_H_ */

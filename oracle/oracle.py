@@ -1,0 +1,158 @@
+"""ctypes wrapper around the fp64 C oracle (s6_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+bench's CPU-baseline leg.  The HIP library and its Python binding never import
+this module, and this module imports nothing from them.
+
+Inputs are numpy arrays of any float dtype; they are converted to fp64
+exactly (every fp32 or bf16 value is an fp64 value), so the oracle sees the
+very values the GPU reads.  Outputs are fp64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "s6_oracle.c")
+LIB = os.path.join(HERE, "liboracle_s6.so")
+CFLAGS = ["-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-fno-fast-math", "-ffp-contract=off"]
+
+
+def build(out: str = LIB, src: str = SRC) -> str:
+    """Compile the oracle with gcc.  -ffp-contract=off keeps every product
+    and sum a separately rounded fp64 operation, exactly as written."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build_from_text(text: str) -> str:
+    """Compile an oracle from source text into a fresh temporary library
+    (used by the tests that plant deliberate mistakes)."""
+    d = tempfile.mkdtemp(prefix="s6oracle_")
+    src = os.path.join(d, "s6_oracle_variant.c")
+    with open(src, "w") as f:
+        f.write(text)
+    return build(os.path.join(d, "liboracle_variant.so"), src)
+
+
+_P = ctypes.POINTER(ctypes.c_double)
+_I = ctypes.c_int64
+
+
+class Oracle:
+    def __init__(self, path: str | None = None):
+        path = path or LIB
+        if not os.path.exists(path) or (path == LIB and os.path.getmtime(path) < os.path.getmtime(SRC)):
+            if path != LIB:
+                raise FileNotFoundError(path)
+            build()
+        self.lib = ctypes.CDLL(path)
+        self.lib.oracle_scan.argtypes = [_I, _I, _I, _I] + [_P] * 12
+        self.lib.oracle_scan.restype = None
+        self.lib.oracle_step.argtypes = [_I, _I, _I] + [_P] * 11
+        self.lib.oracle_step.restype = None
+        self.lib.oracle_num_threads.restype = ctypes.c_int
+        self.path = path
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    @staticmethod
+    def _in(a, shape):
+        if a is None:
+            return None, None
+        arr = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+        if arr.shape != tuple(shape):
+            raise ValueError(f"shape {arr.shape} != {tuple(shape)}")
+        return arr, arr.ctypes.data_as(_P)
+
+    def scan(self, x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None):
+        """Full scan.  x, delta, z: (batch, D, L); Bm, Cm: (batch, N, L);
+        A: (D, N); Dskip: (D,); h0: (batch, D, N).  Returns a dict with y and
+        m (batch, D, L), h_last and H_last (batch, D, N), all fp64."""
+        x = np.asarray(x)
+        Bsz, D, L = x.shape
+        N = np.asarray(A).shape[1]
+        if N > 256:
+            raise ValueError("oracle supports N <= 256")
+        keep = []
+        args = []
+        for a, shp in ((x, (Bsz, D, L)), (delta, (Bsz, D, L)), (A, (D, N)), (Bm, (Bsz, N, L)),
+                       (Cm, (Bsz, N, L)), (Dskip, (D,)), (z, (Bsz, D, L)), (h0, (Bsz, D, N))):
+            arr, ptr = self._in(a, shp)
+            keep.append(arr)
+            args.append(ptr)
+        y = np.empty((Bsz, D, L))
+        m = np.empty((Bsz, D, L))
+        hl = np.empty((Bsz, D, N))
+        Hl = np.empty((Bsz, D, N))
+        outs = [o.ctypes.data_as(_P) for o in (y, m, hl, Hl)]
+        self.lib.oracle_scan(Bsz, D, L, N, *args, *outs)
+        return {"y": y, "m": m, "h_last": hl, "H_last": Hl}
+
+    def step(self, h, H, x, delta, A, Bm, Cm, Dskip=None, z=None):
+        """One decode token.  h, H: (batch, D, N) fp64 arrays updated in place;
+        x, delta, z: (batch, D); Bm, Cm: (batch, N).  Returns (y, m)."""
+        if h.dtype != np.float64 or not h.flags.c_contiguous or H.dtype != np.float64:
+            raise ValueError("h and H must be contiguous float64 arrays")
+        Bsz, D, N = h.shape
+        keep = []
+        args = []
+        for a, shp in ((x, (Bsz, D)), (delta, (Bsz, D)), (A, (D, N)), (Bm, (Bsz, N)),
+                       (Cm, (Bsz, N)), (Dskip, (D,)), (z, (Bsz, D))):
+            arr, ptr = self._in(a, shp)
+            keep.append(arr)
+            args.append(ptr)
+        y = np.empty((Bsz, D))
+        m = np.empty((Bsz, D))
+        self.lib.oracle_step(Bsz, D, N, h.ctypes.data_as(_P), H.ctypes.data_as(_P), *args,
+                             y.ctypes.data_as(_P), m.ctypes.data_as(_P))
+        return y, m
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def scaled_error(got, ref, mag) -> float:
+    """Largest componentwise error |got - ref| / mag, where mag is the
+    oracle's absolute-value magnitude of the same element (mag >= |ref|).
+    0/0 counts as 0; x/0 with x > 0 as infinity.  Non-finite got -> inf."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    mag = np.asarray(mag, dtype=np.float64)
+    if got.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    diff = np.abs(got - ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        e = np.where(diff == 0.0, 0.0, diff / mag)
+    return float(np.max(e))
+
+
+def relative_error(got, ref, floor_frac=1e-3) -> float:
+    """Plain max |got - ref| / |ref| over elements with |ref| >= floor_frac *
+    max|ref| (reported beside the scaled error; it is unbounded near zero
+    crossings, so elements close to zero are left out)."""
+    got = np.asarray(got, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    if ref.size == 0:
+        return 0.0
+    big = np.abs(ref) >= floor_frac * np.max(np.abs(ref))
+    if not np.any(big):
+        return 0.0
+    return float(np.max(np.abs(got[big] - ref[big]) / np.abs(ref[big])))

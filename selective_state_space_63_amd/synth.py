@@ -1,0 +1,204 @@
+"""Seeded synthetic inputs for the selective-scan workloads.
+
+This module only draws random numbers and rounds them to the input dtype.  It
+holds none of the scan's arithmetic, imports neither the HIP binding nor the
+oracle, and is the one piece both sides of a parity test share: the tests
+decode the same stored bits for the oracle (exactly, to fp64) and upload them
+for the HIP library.
+
+Workloads (sizes of the Mamba layers the pages talk about; the pages' own
+experiments use datasets and trained weights, so seeded random inputs of the
+same shapes stand in for them):
+
+  tiny     : batch 1, D 16, N 4, L 256, fp32 inputs, no gate
+  m130     : batch 2, D 1536, N 16, L 2048, bf16 inputs, SiLU gate
+  m3b      : batch 8, D 5120, N 16, L 2048, bf16 inputs, SiLU gate, final state
+  long     : batch 1, D 1536, N 16, L 2^20, bf16 inputs, SiLU gate,
+             Delta log-uniform in [1e-4, 1e-2]
+  decode   : batch 256, D 5120, N 16, 1024 single-token steps, bf16 inputs
+
+Distributions.  A[d, n] = -(n + 1) (real diagonal, S4D-real style), fp32.
+"softplus" Delta: a per-channel level u_d ~ logUniform[1e-3, 0.1] and a
+per-element eps ~ N(0, 1) give Delta = softplus(0.5 eps + ln(expm1(u_d))),
+computed in fp64.  "logu" Delta: exp(Uniform[ln 1e-4, ln 1e-2]) per element.
+x, B, C, z and D_skip ~ N(0, 1).  fp64 values are rounded to fp32 (round to
+nearest even), then to bf16 (round to nearest even) for bf16 workloads.  The
+stored bits are the ground truth: nothing downstream re-rounds them.
+
+Seeding.  Workload k uses seed 63000 + k.  Stream [seed, 0] draws, in order:
+u_d (D), D_skip (D), B (batch, N, L), C (batch, N, L).  The (batch, channel)
+pairs p = b * D + d are cut into blocks of PAIR_BLOCK rows; block j uses
+stream [seed, 1 + j] and draws eps (or the log-uniform U), then x, then z,
+each of shape (rows, L).  Any block can therefore be regenerated alone, which
+is how large workloads are produced and sampled in bounded memory.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+PAIR_BLOCK = 64
+F32, BF16 = "f32", "bf16"
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    dim: int
+    dstate: int
+    seqlen: int
+    dtype: str = BF16          # dtype of x, delta, B, C, z
+    gate: bool = True          # SiLU(z) gate present
+    delta_kind: str = "softplus"
+    seed: int = 63000
+    final_state: bool = False  # workload also returns h_L
+
+    @property
+    def pairs(self) -> int:
+        return self.batch * self.dim
+
+    @property
+    def nblocks(self) -> int:
+        return (self.pairs + PAIR_BLOCK - 1) // PAIR_BLOCK
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny_fp32_b1_d16_n4_l256", 1, 16, 4, 256, F32, False, "softplus", 63000),
+    "m130": Workload("mamba130m_layer_b2_d1536_n16_l2048", 2, 1536, 16, 2048, BF16, True,
+                     "softplus", 63001),
+    "m3b": Workload("mamba3b_layer_b8_d5120_n16_l2048", 8, 5120, 16, 2048, BF16, True,
+                    "softplus", 63002, final_state=True),
+    "long": Workload("long_b1_d1536_n16_l1048576", 1, 1536, 16, 1 << 20, BF16, True, "logu",
+                     63003),
+    # decode: seqlen is the number of single-token steps; inputs are laid out
+    # like a scan of that length and sliced one token per step.
+    "decode": Workload("decode_b256_d5120_n16_s1024", 256, 5120, 16, 1024, BF16, True,
+                       "softplus", 63004, final_state=True),
+}
+
+
+def custom(batch, dim, dstate, seqlen, dtype=BF16, gate=True, delta_kind="softplus", seed=1,
+           final_state=True) -> Workload:
+    return Workload(f"custom_b{batch}_d{dim}_n{dstate}_l{seqlen}_{dtype}_s{seed}", batch, dim,
+                    dstate, seqlen, dtype, gate, delta_kind, seed, final_state)
+
+
+# ---------------------------------------------------------------- rounding --
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16, nearest-even, returning the 16-bit patterns.
+    (The inputs are finite; no NaN handling is needed.)"""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact decode of bf16 patterns to fp32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def encode(a64: np.ndarray, dtype: str) -> np.ndarray:
+    """fp64 -> stored input bits: float32 array (F32) or uint16 patterns (BF16)."""
+    a32 = np.asarray(a64, dtype=np.float64).astype(np.float32)
+    return a32 if dtype == F32 else f32_to_bf16_bits(a32)
+
+
+def decode(stored: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored bits -> exact float32 values."""
+    return np.asarray(stored, dtype=np.float32) if dtype == F32 else bf16_bits_to_f32(stored)
+
+
+# --------------------------------------------------------------- drawing ----
+def _global_stream(w: Workload) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 0])))
+
+
+def params(w: Workload) -> dict:
+    """Per-channel and per-token parameters shared by all pairs:
+    A (D, N) f32, Dskip (D,) f32, B and C (batch, N, L) stored bits,
+    u (D,) f64 (the per-channel Delta level; softplus workloads only)."""
+    g = _global_stream(w)
+    u = np.exp(g.uniform(math.log(1e-3), math.log(0.1), size=w.dim))
+    dskip = g.standard_normal(w.dim).astype(np.float32)
+    Bm = encode(g.standard_normal((w.batch, w.dstate, w.seqlen)), w.dtype)
+    Cm = encode(g.standard_normal((w.batch, w.dstate, w.seqlen)), w.dtype)
+    A = np.tile(-(np.arange(w.dstate, dtype=np.float32) + 1.0), (w.dim, 1))
+    return {"A": A, "Dskip": dskip, "Bm": Bm, "Cm": Cm, "u": u}
+
+
+def block(w: Workload, j: int, prm: dict | None = None) -> dict:
+    """Rows of block j (pairs [j*PAIR_BLOCK, ...)): x, delta, z stored bits of
+    shape (rows, L); z is None without a gate."""
+    p0 = j * PAIR_BLOCK
+    rows = min(PAIR_BLOCK, w.pairs - p0)
+    if rows <= 0:
+        raise IndexError(f"block {j} out of range for {w.name}")
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 1 + j])))
+    shape = (rows, w.seqlen)
+    if w.delta_kind == "softplus":
+        if prm is None:
+            prm = params(w)
+        eps = g.standard_normal(shape)
+        d_idx = (np.arange(p0, p0 + rows) % w.dim)
+        bias = np.log(np.expm1(prm["u"][d_idx]))[:, None]
+        delta = np.logaddexp(0.0, 0.5 * eps + bias)
+    elif w.delta_kind == "logu":
+        delta = np.exp(g.uniform(math.log(1e-4), math.log(1e-2), size=shape))
+    else:
+        raise ValueError(w.delta_kind)
+    x = g.standard_normal(shape)
+    z = g.standard_normal(shape) if w.gate else None
+    return {
+        "x": encode(x, w.dtype),
+        "delta": encode(delta, w.dtype),
+        "z": None if z is None else encode(z, w.dtype),
+    }
+
+
+def rows_of(w: Workload, pairs_idx, prm: dict | None = None) -> dict:
+    """x, delta, z stored bits for an arbitrary list of pairs, (len, L) each."""
+    pairs_idx = np.asarray(pairs_idx, dtype=np.int64)
+    prm = prm if prm is not None else params(w)
+    out = {k: [] for k in ("x", "delta", "z")}
+    cache = {}
+    for p in pairs_idx:
+        j = int(p) // PAIR_BLOCK
+        if j not in cache:
+            cache.clear()
+            cache[j] = block(w, j, prm)
+        r = int(p) - j * PAIR_BLOCK
+        for k in out:
+            v = cache[j][k]
+            out[k].append(None if v is None else v[r])
+    return {k: (None if (len(v) and v[0] is None) else np.stack(v)) for k, v in out.items()}
+
+
+def full(w: Workload, threads: int | None = None) -> dict:
+    """The whole workload in host memory: params plus x, delta, z of shape
+    (batch, D, L).  Blocks are drawn in parallel threads (numpy releases the
+    GIL while filling); the result does not depend on the thread count."""
+    prm = params(w)
+    st = np.float32 if w.dtype == F32 else np.uint16
+    x = np.empty((w.pairs, w.seqlen), st)
+    delta = np.empty_like(x)
+    z = np.empty_like(x) if w.gate else None
+
+    def fill(j):
+        blk = block(w, j, prm)
+        s = slice(j * PAIR_BLOCK, j * PAIR_BLOCK + blk["x"].shape[0])
+        x[s] = blk["x"]
+        delta[s] = blk["delta"]
+        if z is not None:
+            z[s] = blk["z"]
+
+    nthr = threads or min(16, len(os.sched_getaffinity(0)))
+    with ThreadPoolExecutor(max_workers=nthr) as ex:
+        list(ex.map(fill, range(w.nblocks)))
+    shp = (w.batch, w.dim, w.seqlen)
+    prm.update(x=x.reshape(shp), delta=delta.reshape(shp), z=None if z is None else z.reshape(shp))
+    return prm

@@ -1,0 +1,338 @@
+"""Pins for the fp64 oracle: checks against facts that do not come from the
+oracle itself -- hand-derived values (tests/golden), closed forms, a brute
+force in 50-digit arithmetic over the materialised (all pairs of tokens) form,
+a tree-order scan, and structural invariants.
+
+Each pin is a function taking an oracle object and raising AssertionError on
+failure.  test_oracle_pins.py runs them on the real oracle;
+test_oracle_mutants.py runs them on copies of the oracle with one deliberate
+mistake planted and requires that some pin rejects every copy.
+
+Sources: "【LLM】Mamba和State Space Models详解", sections cited per pin.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand_problem(seed, Bsz=2, D=3, L=40, N=5, gate=True, h0=True, dmin=1e-3, dmax=0.3):
+    g = _rng(seed)
+    A = -np.exp(g.uniform(np.log(0.3), np.log(8.0), size=(D, N)))
+    return dict(
+        x=g.standard_normal((Bsz, D, L)),
+        delta=np.exp(g.uniform(np.log(dmin), np.log(dmax), size=(Bsz, D, L))),
+        A=A,
+        Bm=g.standard_normal((Bsz, N, L)),
+        Cm=g.standard_normal((Bsz, N, L)),
+        Dskip=g.standard_normal(D),
+        z=g.standard_normal((Bsz, D, L)) if gate else None,
+        h0=g.standard_normal((Bsz, D, N)) if h0 else None,
+    )
+
+
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def _read_golden(name):
+    rows = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            parts = line.split()
+            rows[" ".join(p for p in parts if not _isnum(p))] = [float(p) for p in parts if _isnum(p)]
+    return rows
+
+
+def _isnum(s):
+    try:
+        float(s)
+        return True
+    except ValueError:
+        return False
+
+
+# --------------------------------------------------------------------------
+def pin_zero_step_hand(o):
+    """Delta = 0: the state never moves, y = C.h0 + D x exactly (§3.2, §2.2).
+    Hand values from tests/golden/zero_step_hand.txt."""
+    g = _read_golden("zero_step_hand.txt")
+    A = np.array([g["A"]])
+    h0 = np.array([[g["h0"]]])
+    Bv = np.array(g["B"])
+    C = np.array([g["C0"], g["C1"], g["C2"]]).T  # (N, L)
+    x = np.array([[g["x"]]])
+    L = x.shape[-1]
+    Bm = np.repeat(Bv[:, None], L, axis=1)[None]
+    r = o.scan(x, np.zeros_like(x), A, Bm, C[None], Dskip=np.array(g["D"]), h0=h0)
+    assert np.array_equal(r["y"][0, 0], np.array(g["y"])), r["y"]
+    assert np.array_equal(r["h_last"], h0)
+
+
+def pin_scalar_hand(o):
+    """Scalar and two-state recurrences worked by hand (§2.3, §2.4); values
+    from tests/golden/scalar_hand.txt."""
+    g = _read_golden("scalar_hand.txt")
+    ln2 = math.log(2.0)
+    x = np.array([[[1.0, 2.0, 0.0, -1.0]]])
+    dl = np.full_like(x, ln2)
+    ones = np.ones((1, 1, 4))
+    # case 1
+    r = o.scan(x, dl, np.array([[-1.0]]), ones, ones)
+    want = np.array(g["case1 y_over_ln2"]) * ln2
+    assert np.allclose(r["y"][0, 0], want, rtol=1e-15, atol=1e-15), (r["y"], want)
+    # case 2: skip + gate
+    z = np.array([[[0.0, 1.0, -1.0, 2.0]]])
+    r = o.scan(x, dl, np.array([[-1.0]]), ones, ones, Dskip=np.array([0.5]), z=z)
+    want = np.array(g["case2 y"])
+    assert np.allclose(r["y"][0, 0], want, rtol=2e-11, atol=1e-11), (r["y"], want)
+    # case 3: two states
+    x3 = np.array([[[1.0, 0.0, 0.0, 0.0]]])
+    Bm = np.ones((1, 2, 4))
+    Cm = np.array([[[1.0] * 4, [-1.0] * 4]])
+    r = o.scan(x3, np.full_like(x3, ln2), np.array([[-1.0, -2.0]]), Bm, Cm)
+    want = np.array(g["case3 y_over_ln2"]) * ln2
+    assert np.allclose(r["y"][0, 0], want, rtol=1e-15, atol=1e-15), (r["y"], want)
+
+
+def pin_lti_convolution(o):
+    """Time-invariant Delta, B, C: the recurrence equals a causal convolution
+    of x with the kernel K_k = sum_n C[n] exp(k Delta A[n]) Delta B[n], plus
+    the skip term and the decayed initial state (§2.5 convolutional form,
+    §2.7 time invariance).  The kernel uses exp of k*Delta*A, not powers, and
+    numpy.convolve, so it is a different evaluation of the same definition."""
+    g = _rng(11)
+    Bsz, D, L, N = 2, 3, 96, 4
+    A = -np.exp(g.uniform(np.log(0.2), np.log(6.0), size=(D, N)))
+    dconst = np.exp(g.uniform(np.log(1e-2), np.log(0.5), size=(Bsz, D)))
+    Bc = g.standard_normal((Bsz, N))
+    Cc = g.standard_normal((Bsz, N))
+    x = g.standard_normal((Bsz, D, L))
+    z = g.standard_normal((Bsz, D, L))
+    Dsk = g.standard_normal(D)
+    h0 = g.standard_normal((Bsz, D, N))
+    delta = np.repeat(dconst[:, :, None], L, axis=2)
+    Bm = np.repeat(Bc[:, :, None], L, axis=2)
+    Cm = np.repeat(Cc[:, :, None], L, axis=2)
+    r = o.scan(x, delta, A, Bm, Cm, Dskip=Dsk, z=z, h0=h0)
+    k = np.arange(L)
+    for b in range(Bsz):
+        for d in range(D):
+            dt = dconst[b, d]
+            K = np.zeros(L)
+            init = np.zeros(L)
+            for n in range(N):
+                K += Cc[b, n] * np.exp(k * dt * A[d, n]) * dt * Bc[b, n]
+                init += Cc[b, n] * np.exp((k + 1) * dt * A[d, n]) * h0[b, d, n]
+            pre = np.convolve(x[b, d], K)[:L] + Dsk[d] * x[b, d] + init
+            want = pre * _silu(z[b, d])
+            err = np.max(np.abs(r["y"][b, d] - want) / r["m"][b, d])
+            assert err < 1e-12, err
+
+
+def pin_step_response(o):
+    """Constant x, Delta, B: the state is a geometric series,
+    h_t = dBx (1 - dA^(t+1)) / (1 - dA) (§2.4 unrolled recurrence)."""
+    g = _rng(12)
+    D, N, L = 2, 3, 200
+    A = -np.array([[0.5, 2.0, 7.0], [1.0, 3.0, 0.1]])
+    dt = np.array([0.05, 0.3])
+    Bv = g.standard_normal(N)
+    Cv = g.standard_normal(N)
+    xv = np.array([0.7, -1.3])
+    x = np.repeat(xv[None, :, None], L, axis=2)
+    delta = np.repeat(dt[None, :, None], L, axis=2)
+    Bm = np.repeat(Bv[None, :, None], L, axis=2)
+    Cm = np.repeat(Cv[None, :, None], L, axis=2)
+    r = o.scan(x, delta, A, Bm, Cm)
+    t = np.arange(L)
+    for d in range(D):
+        y = np.zeros(L)
+        for n in range(N):
+            dA = math.exp(dt[d] * A[d, n])
+            h = dt[d] * Bv[n] * xv[d] * (1.0 - dA ** (t + 1)) / (1.0 - dA)
+            y += Cv[n] * h
+            assert abs(r["h_last"][0, d, n] - h[-1]) <= 1e-12 * abs(h[-1]) + 1e-300
+        err = np.max(np.abs(r["y"][0, d] - y) / r["m"][0, d])
+        assert err < 1e-12, err
+
+
+def brute_force_y(p, dps=50):
+    """Materialised form in 50-digit arithmetic: for every pair of tokens
+    s <= t, the contribution of x_s to y_t is
+      sum_n C_t[n] exp(A[n] * sum_{u=s+1..t} Delta_u) Delta_s B_s[n] x_s,
+    the initial state contributes sum_n C_t[n] exp(A[n] sum_{u<=t} Delta_u) h0[n],
+    then + D x_t and times SiLU(z_t).  Exponentials of sums, not products of
+    exponentials: a different algorithm for the same definition (§3.3)."""
+    import mpmath as mp
+    mp.mp.dps = dps
+    x, dl, A, Bm, Cm = p["x"], p["delta"], p["A"], p["Bm"], p["Cm"]
+    Bsz, D, L = x.shape
+    N = A.shape[1]
+    out = np.zeros((Bsz, D, L))
+    for b in range(Bsz):
+        for d in range(D):
+            cum = [mp.mpf(0)]
+            for t in range(L):
+                cum.append(cum[-1] + mp.mpf(float(dl[b, d, t])))
+            for t in range(L):
+                acc = mp.mpf(0)
+                for n in range(N):
+                    An = mp.mpf(float(A[d, n]))
+                    Ct = mp.mpf(float(Cm[b, n, t]))
+                    for s in range(t + 1):
+                        acc += Ct * mp.exp(An * (cum[t + 1] - cum[s + 1])) * mp.mpf(float(dl[b, d, s])) \
+                            * mp.mpf(float(Bm[b, n, s])) * mp.mpf(float(x[b, d, s]))
+                    if p.get("h0") is not None:
+                        acc += Ct * mp.exp(An * cum[t + 1]) * mp.mpf(float(p["h0"][b, d, n]))
+                if p.get("Dskip") is not None:
+                    acc += mp.mpf(float(p["Dskip"][d])) * mp.mpf(float(x[b, d, t]))
+                if p.get("z") is not None:
+                    zz = mp.mpf(float(p["z"][b, d, t]))
+                    acc *= zz / (1 + mp.exp(-zz))
+                out[b, d, t] = float(acc)
+    return out
+
+
+def pin_brute_force(o):
+    """Whole oracle against the 50-digit materialised form on tiny random
+    problems with time-varying Delta, B, C, with and without h0 and gate."""
+    for seed, kw in ((21, dict(gate=True, h0=True)), (22, dict(gate=False, h0=False)),
+                     (23, dict(gate=True, h0=False, Bsz=1, D=2, N=3, L=24))):
+        base = dict(Bsz=2, D=3, L=20, N=4)
+        base.update(kw)
+        p = _rand_problem(seed, **base)
+        r = o.scan(**p)
+        want = brute_force_y(p)
+        err = np.max(np.abs(r["y"] - want) / r["m"])
+        assert err < 1e-13, (seed, err)
+
+
+def pin_tree_scan(o):
+    """Associativity (§3.3): the pairs (a, b) with h_t = a_t h_{t-1} + b_t
+    combine as (a1, b1) then (a2, b2) -> (a1 a2, a2 b1 + b2).  An inclusive
+    Hillis-Steele scan in that combine order must give the oracle's final
+    state and outputs."""
+    p = _rand_problem(31, Bsz=2, D=2, L=37, N=3)
+    r = o.scan(**p)
+    x, dl, A, Bm, Cm = p["x"], p["delta"], p["A"], p["Bm"], p["Cm"]
+    Bsz, D, L = x.shape
+    N = A.shape[1]
+    for b in range(Bsz):
+        for d in range(D):
+            y = np.zeros(L)
+            for n in range(N):
+                a = np.exp(dl[b, d] * A[d, n])
+                bb = dl[b, d] * Bm[b, n] * x[b, d]
+                bb = bb.copy()
+                bb[0] += a[0] * p["h0"][b, d, n]
+                a = a.copy()
+                step = 1
+                while step < L:
+                    a_prev = np.concatenate([np.ones(step), a[:-step]])
+                    b_prev = np.concatenate([np.zeros(step), bb[:-step]])
+                    bb = a * b_prev + bb
+                    a = a_prev * a
+                    step *= 2
+                y += Cm[b, n] * bb
+                assert abs(bb[-1] - r["h_last"][b, d, n]) <= 1e-12 * r["H_last"][b, d, n]
+            y = (y + p["Dskip"][d] * x[b, d]) * _silu(p["z"][b, d])
+            err = np.max(np.abs(y - r["y"][b, d]) / r["m"][b, d])
+            assert err < 1e-13, err
+
+
+def pin_split_resume(o):
+    """Carry semantics: scanning [0, L) equals scanning [0, L1) and then
+    [L1, L) from the final state of the first part (the finite state is the
+    whole context, §2.4).  Checked at several cut points, including 1 and
+    L-1."""
+    p = _rand_problem(41, Bsz=2, D=3, L=50, N=4)
+    full = o.scan(**p)
+    for L1 in (1, 17, 32, 49):
+        s1 = {k: (v[..., :L1] if k in ("x", "delta", "Bm", "Cm", "z") else v) for k, v in p.items()}
+        s2 = {k: (v[..., L1:] if k in ("x", "delta", "Bm", "Cm", "z") else v) for k, v in p.items()}
+        r1 = o.scan(**s1)
+        s2["h0"] = r1["h_last"]
+        r2 = o.scan(**s2)
+        y = np.concatenate([r1["y"], r2["y"]], axis=-1)
+        assert np.max(np.abs(y - full["y"]) / full["m"]) < 1e-13
+        assert np.max(np.abs(r2["h_last"] - full["h_last"]) / full["H_last"]) < 1e-13
+
+
+def pin_linearity_and_permutation(o):
+    """With h0 = 0 the output is linear in x for fixed Delta, B, C, z; pairs
+    are independent, so permuting channels (with their A, D rows) permutes
+    the outputs, and each batch row uses only its own B and C (§3.2)."""
+    p = _rand_problem(51, Bsz=2, D=4, L=30, N=3, h0=False)
+    g = _rng(52)
+    x2 = g.standard_normal(p["x"].shape)
+    r1 = o.scan(**p)
+    q = dict(p, x=x2)
+    r2 = o.scan(**q)
+    q = dict(p, x=2.5 * p["x"] - 0.75 * x2)
+    r3 = o.scan(**q)
+    lin = 2.5 * r1["y"] - 0.75 * r2["y"]
+    assert np.max(np.abs(r3["y"] - lin) / (2.5 * r1["m"] + 0.75 * r2["m"])) < 1e-13
+    perm = np.array([2, 0, 3, 1])
+    q = dict(p, x=p["x"][:, perm], delta=p["delta"][:, perm], z=p["z"][:, perm], A=p["A"][perm],
+             Dskip=p["Dskip"][perm])
+    r4 = o.scan(**q)
+    assert np.array_equal(r4["y"], r1["y"][:, perm])
+    bperm = np.array([1, 0])
+    q = {k: (v[bperm] if k in ("x", "delta", "z", "Bm", "Cm") else v) for k, v in p.items()}
+    r5 = o.scan(**q)
+    assert np.array_equal(r5["y"], r1["y"][bperm])
+
+
+def pin_gate_limits(o):
+    """SiLU gate: z = 0 gives y = 0 exactly; z = 40 passes (Ch + Dx) times 40
+    (to 1e-15 relative); z = -40 gives |y| below 1e-15 |Ch + Dx| * 40."""
+    p = _rand_problem(61, Bsz=1, D=2, L=16, N=3)
+    ungated = o.scan(**dict(p, z=None))["y"]
+    r = o.scan(**dict(p, z=np.zeros_like(p["x"])))
+    assert np.all(r["y"] == 0.0)
+    r = o.scan(**dict(p, z=np.full_like(p["x"], 40.0)))
+    assert np.allclose(r["y"], 40.0 * ungated, rtol=1e-14, atol=0)
+    r = o.scan(**dict(p, z=np.full_like(p["x"], -40.0)))
+    assert np.all(np.abs(r["y"]) <= 1e-15 * 40.0 * np.abs(ungated) + 1e-300)
+
+
+def pin_decode_equals_scan(o):
+    """S single-token steps from h0 equal one scan over the same S tokens:
+    the recurrent form needs only the previous state (§2.4)."""
+    p = _rand_problem(71, Bsz=2, D=3, L=12, N=4)
+    r = o.scan(**p)
+    h = p["h0"].copy()
+    H = np.abs(h)
+    for s in range(p["x"].shape[-1]):
+        y, m = o.step(h, H, p["x"][..., s], p["delta"][..., s], p["A"], p["Bm"][..., s],
+                      p["Cm"][..., s], Dskip=p["Dskip"], z=p["z"][..., s])
+        assert np.array_equal(y, r["y"][..., s]) and np.array_equal(m, r["m"][..., s])
+    assert np.array_equal(h, r["h_last"]) and np.array_equal(H, r["H_last"])
+
+
+def pin_magnitude_bounds(o):
+    """The magnitude m bounds |y| and equals |y| when every term is >= 0."""
+    p = _rand_problem(81, Bsz=2, D=2, L=25, N=3)
+    r = o.scan(**p)
+    assert np.all(r["m"] >= np.abs(r["y"]) * (1 - 1e-15))
+    q = dict(p, x=np.abs(p["x"]), Bm=np.abs(p["Bm"]), Cm=np.abs(p["Cm"]), Dskip=np.abs(p["Dskip"]),
+             z=None, h0=np.abs(p["h0"]))
+    r = o.scan(**q)
+    assert np.allclose(r["m"], r["y"], rtol=1e-14, atol=0)
+
+
+PINS = [pin_zero_step_hand, pin_scalar_hand, pin_lti_convolution, pin_step_response,
+        pin_brute_force, pin_tree_scan, pin_split_resume, pin_linearity_and_permutation,
+        pin_gate_limits, pin_decode_equals_scan, pin_magnitude_bounds]

@@ -1,0 +1,65 @@
+"""Plant one plausible mistake at a time in a copy of the oracle's source,
+build it, and require that at least one pin rejects it.  This shows that the
+pins constrain every part of the oracle: dropped terms, wrong signs, wrong
+indices, swapped operands, a wrong update order, the other reading of the
+discretisation.  The real oracle file is never modified."""
+import os
+
+import pytest
+
+import pins
+from oracle import oracle as O
+
+SRC = open(O.SRC).read()
+
+# (name, [(old, new), ...]) -- each `old` must occur exactly once.
+MUTANTS = [
+    ("skip_dropped", [("double skip = dskip * xt;", "double skip = 0.0 * dskip * xt;")]),
+    ("output_before_update", [
+        ("h[n] = a * h[n] + bx;               /* update first ... */",
+         "double hp_ = h[n]; h[n] = a * h[n] + bx;"),
+        ("acc += Ct[n * bstride] * h[n];      /* ... then read the output from the new state */",
+         "acc += Ct[n * bstride] * hp_;")]),
+    ("B_C_swapped", [
+        ("double bx = dt * Bt[n * bstride] * xt;", "double bx = dt * Ct[n * bstride] * xt;"),
+        ("acc += Ct[n * bstride] * h[n];      /*", "acc += Bt[n * bstride] * h[n];      /*")]),
+    ("exp_sign", [("exp(dt * Ad[n])", "exp(-dt * Ad[n])")]),
+    ("dt_dropped_from_input", [("double bx = dt * Bt[n * bstride] * xt;",
+                                "double bx = Bt[n * bstride] * xt;")]),
+    ("gate_before_skip", [("        yt *= g;\n        mag *= fabs(g);\n      }\n      y[p * L + t] = yt;",
+                           "        yt = (yt - dsk * x[p * L + t]) * g + dsk * x[p * L + t];\n"
+                           "        mag *= fabs(g);\n      }\n      y[p * L + t] = yt;")]),
+    ("h0_ignored", [("h[n] = h0 ? h0[p * N + n] : 0.0;", "h[n] = 0.0;")]),
+    ("exact_zoh_for_B", [("double bx = dt * Bt[n * bstride] * xt;",
+                          "double bx = (Ad[n] != 0.0 ? (a - 1.0) / Ad[n] : dt) * Bt[n * bstride] * xt;")]),
+    ("delta_index_shift", [("delta[p * L + t]", "delta[p * L + (t > 0 ? t - 1 : 0)]")]),
+    ("A_state_index", [("exp(dt * Ad[n])", "exp(dt * Ad[(n + 1) % N])")]),
+    ("B_batch_index", [("const double* Bb = Bm + b * N * L;", "const double* Bb = Bm;")]),
+    ("BC_layout_transposed", [("Bb + t, Cb + t,\n                               L,",
+                               "Bb + t * N, Cb + t * N,\n                               1,")]),
+    ("skip_channel_index", [("double dsk = Dskip ? Dskip[d] : 0.0;\n    for (int64_t t",
+                             "double dsk = Dskip ? Dskip[0] : 0.0;\n    for (int64_t t")]),
+    ("sigmoid_sign", [("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));")]),
+    ("input_decayed_same_step", [("h[n] = a * h[n] + bx;", "h[n] = a * (h[n] + bx);")]),
+    ("magnitude_drops_input", [("H[n] = fabs(a) * H[n] + fabs(bx);", "H[n] = fabs(a) * H[n];")]),
+]
+
+
+def _mutate(text, subs):
+    for old, new in subs:
+        assert text.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
+        text = text.replace(old, new)
+    return text
+
+
+@pytest.mark.parametrize("name,subs", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_reject_mutant(name, subs):
+    lib = O.build_from_text(_mutate(SRC, subs))
+    o = O.Oracle(lib)
+    failed = []
+    for pin in pins.PINS:
+        try:
+            pin(o)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
