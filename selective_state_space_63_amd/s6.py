@@ -1,0 +1,159 @@
+"""Thin Python binding of libs6 (ctypes over the C ABI in include/s6.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libs6.so.  Tensors are torch CUDA (ROCm) tensors; torch provides
+device memory and the current stream.  If libs6.so is missing or cannot be
+loaded, every call raises -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libs6.so")
+
+S6_F32, S6_BF16 = 0, 1
+_DT = {torch.float32: S6_F32, torch.bfloat16: S6_BF16}
+
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libs6.so once.  Raises FileNotFoundError/OSError if it is not
+    built (python -m selective_state_space_63_amd.build)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(f"{p} is not built; run `python -m selective_state_space_63_amd.build`")
+    lib = ctypes.CDLL(p)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.s6_version.restype = i32
+    lib.s6_status_str.restype = ctypes.c_char_p
+    lib.s6_status_str.argtypes = [i32]
+    lib.s6_scan_fwd.restype = i32
+    lib.s6_scan_fwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 11
+    lib.s6_last_state.restype = i32
+    lib.s6_last_state.argtypes = [i64, i64, i64, i64, i32] + [vp] * 7
+    lib.s6_state_update.restype = i32
+    lib.s6_state_update.argtypes = [i64, i64, i64, i32] + [vp] * 10
+    if path is None:
+        _lib = lib
+    return lib
+
+
+class S6Error(RuntimeError):
+    pass
+
+
+def _check(rc: int):
+    if rc != 0:
+        msg = load_library().s6_status_str(rc).decode()
+        raise S6Error(f"libs6 status {rc}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _req(t, name, shape, dtype=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t
+
+
+def _opt(t, name, shape, dtype=None):
+    return None if t is None else _req(t, name, shape, dtype)
+
+
+def scan_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, return_last_state=False, y=None,
+             h_last=None):
+    """Fused selective scan.  x, delta, z: (batch, dim, L); Bm, Cm: (batch, N, L);
+    A: (dim, N) fp32; D: (dim,) fp32; h0: (batch, dim, N) fp32.  Inputs x,
+    delta, Bm, Cm, z share one dtype (float32 or bfloat16).  Returns y
+    (batch, dim, L) fp32, and h_last (batch, dim, N) fp32 if requested."""
+    bsz, dim, L = x.shape
+    N = A.shape[1]
+    dt = x.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported input dtype {dt}")
+    _req(x, "x", (bsz, dim, L), dt)
+    _req(delta, "delta", (bsz, dim, L), dt)
+    _req(A, "A", (dim, N), torch.float32)
+    _req(Bm, "Bm", (bsz, N, L), dt)
+    _req(Cm, "Cm", (bsz, N, L), dt)
+    _opt(D, "D", (dim,), torch.float32)
+    _opt(z, "z", (bsz, dim, L), dt)
+    _opt(h0, "h0", (bsz, dim, N), torch.float32)
+    if y is None:
+        y = torch.empty((bsz, dim, L), dtype=torch.float32, device=x.device)
+    _req(y, "y", (bsz, dim, L), torch.float32)
+    if return_last_state and h_last is None:
+        h_last = torch.empty((bsz, dim, N), dtype=torch.float32, device=x.device)
+    _opt(h_last, "h_last", (bsz, dim, N), torch.float32)
+    rc = load_library().s6_scan_fwd(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
+                                    _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last),
+                                    _stream())
+    _check(rc)
+    return (y, h_last) if return_last_state else y
+
+
+def last_state(x, delta, A, Bm, h0=None, out=None):
+    """Final state of the recurrence (no output sequence): (batch, dim, N) fp32."""
+    bsz, dim, L = x.shape
+    N = A.shape[1]
+    dt = x.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported input dtype {dt}")
+    _req(x, "x", (bsz, dim, L), dt)
+    _req(delta, "delta", (bsz, dim, L), dt)
+    _req(A, "A", (dim, N), torch.float32)
+    _req(Bm, "Bm", (bsz, N, L), dt)
+    _opt(h0, "h0", (bsz, dim, N), torch.float32)
+    if out is None:
+        out = torch.empty((bsz, dim, N), dtype=torch.float32, device=x.device)
+    _req(out, "out", (bsz, dim, N), torch.float32)
+    rc = load_library().s6_last_state(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
+                                      _ptr(h0), _ptr(out), _stream())
+    _check(rc)
+    return out
+
+
+def state_update(h, x, delta, A, Bm, Cm, D=None, z=None, y=None):
+    """One decode token: h (batch, dim, N) fp32 is advanced in place; x, delta,
+    z: (batch, dim); Bm, Cm: (batch, N).  Returns y (batch, dim) fp32."""
+    bsz, dim, N = h.shape
+    dt = x.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported input dtype {dt}")
+    _req(h, "h", (bsz, dim, N), torch.float32)
+    _req(x, "x", (bsz, dim), dt)
+    _req(delta, "delta", (bsz, dim), dt)
+    _req(A, "A", (dim, N), torch.float32)
+    _req(Bm, "Bm", (bsz, N), dt)
+    _req(Cm, "Cm", (bsz, N), dt)
+    _opt(D, "D", (dim,), torch.float32)
+    _opt(z, "z", (bsz, dim), dt)
+    if y is None:
+        y = torch.empty((bsz, dim), dtype=torch.float32, device=x.device)
+    _req(y, "y", (bsz, dim), torch.float32)
+    rc = load_library().s6_state_update(bsz, dim, N, _DT[dt], _ptr(h), _ptr(x), _ptr(delta), _ptr(A),
+                                        _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(y), _stream())
+    _check(rc)
+    return y

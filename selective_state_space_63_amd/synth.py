@@ -202,3 +202,55 @@ def full(w: Workload, threads: int | None = None) -> dict:
     shp = (w.batch, w.dim, w.seqlen)
     prm.update(x=x.reshape(shp), delta=delta.reshape(shp), z=None if z is None else z.reshape(shp))
     return prm
+
+
+# ------------------------------------------------------- device generation --
+def device_full(w: Workload, device="cuda", pair_chunk: int = 256) -> dict:
+    """The whole workload generated directly in device memory with torch's
+    counter-based (Philox) CUDA generator -- for the large workloads, where
+    drawing billions of values on the host would dominate a run.  Same
+    distributions as `full` (computed in fp32 on the device, then rounded to
+    the input dtype by torch, nearest-even); different draws.  Deterministic
+    for a given workload.  Seeding: tensor kind k (0 u, 1 D_skip, 2 B, 3 C,
+    4 eps/U, 5 x, 6 z) of pair chunk j uses seed
+    ((w.seed * 8 + k) * 1_000_003 + j) mod 2^63.  Returns torch tensors:
+    x, delta, z (batch, D, L), Bm, Cm (batch, N, L) in the input dtype,
+    A (D, N) and Dskip (D,) fp32."""
+    import torch
+
+    dt = torch.float32 if w.dtype == F32 else torch.bfloat16
+
+    def gen(kind, j=0):
+        g = torch.Generator(device=device)
+        g.manual_seed(((w.seed * 8 + kind) * 1_000_003 + j) % (1 << 63))
+        return g
+
+    f32 = torch.float32
+    u = torch.exp(torch.empty(w.dim, device=device, dtype=f32).uniform_(
+        math.log(1e-3), math.log(0.1), generator=gen(0)))
+    dskip = torch.randn(w.dim, device=device, dtype=f32, generator=gen(1))
+    Bm = torch.randn((w.batch, w.dstate, w.seqlen), device=device, dtype=f32, generator=gen(2)).to(dt)
+    Cm = torch.randn((w.batch, w.dstate, w.seqlen), device=device, dtype=f32, generator=gen(3)).to(dt)
+    A = (-(torch.arange(w.dstate, device=device, dtype=f32) + 1.0)).repeat(w.dim, 1).contiguous()
+    bias = torch.log(torch.expm1(u.double())).float()
+    shp = (w.pairs, w.seqlen)
+    x = torch.empty(shp, device=device, dtype=dt)
+    delta = torch.empty(shp, device=device, dtype=dt)
+    z = torch.empty(shp, device=device, dtype=dt) if w.gate else None
+    for j, p0 in enumerate(range(0, w.pairs, pair_chunk)):
+        p1 = min(w.pairs, p0 + pair_chunk)
+        rows = p1 - p0
+        if w.delta_kind == "softplus":
+            eps = torch.randn((rows, w.seqlen), device=device, dtype=f32, generator=gen(4, j))
+            bidx = torch.arange(p0, p1, device=device) % w.dim
+            delta[p0:p1] = torch.nn.functional.softplus(0.5 * eps + bias[bidx][:, None]).to(dt)
+        else:
+            uu = torch.empty((rows, w.seqlen), device=device, dtype=f32).uniform_(
+                math.log(1e-4), math.log(1e-2), generator=gen(4, j))
+            delta[p0:p1] = torch.exp(uu).to(dt)
+        x[p0:p1] = torch.randn((rows, w.seqlen), device=device, dtype=f32, generator=gen(5, j)).to(dt)
+        if z is not None:
+            z[p0:p1] = torch.randn((rows, w.seqlen), device=device, dtype=f32, generator=gen(6, j)).to(dt)
+    s3 = (w.batch, w.dim, w.seqlen)
+    return {"x": x.view(s3), "delta": delta.view(s3), "z": None if z is None else z.view(s3),
+            "Bm": Bm, "Cm": Cm, "A": A, "Dskip": dskip}
