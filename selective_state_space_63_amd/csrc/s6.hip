@@ -10,17 +10,24 @@
 //    VALU port as FMA at a quarter of its rate) and by HBM streaming, not by
 //    a dense contraction, so no MFMA is used.
 //  * Workgroup = 64 channels of one batch row x G waves; lane = channel,
-//    wave w = states [4w, 4w+4).  B and C of a token are then the same for
-//    the whole wave and are read with scalar loads into SGPRs from a packed
-//    fp32 copy [batch][L][G][B0..B3 C0..C3] made by s6_pack_bc.  A, the
-//    state h and the per-lane partial output stay in VGPRs; the
-//    (batch, D, L, N) state is never written anywhere.
-//  * x, delta, z are staged per chunk of kT tokens into LDS with coalesced
-//    row loads (token-major tiles, padded pitch), read there by every wave.
+//    wave w = states [4w, 4w+4).  A, the state h and the per-lane partial
+//    output stay in VGPRs; the (batch, D, L, N) state is never written.
+//  * B and C of a token are the same for all 64 channels of a wave.  For 4
+//    tokens x 4 states they sit in one VGPR per tensor, replicated in each
+//    16-lane row (lane x of a row holds token x/4, state x%4), and every use
+//    reads them through a DPP row_newbcast operand folded into the multiply:
+//    no LDS traffic and no extra instruction.  They are loaded from the bf16
+//    or fp32 inputs one chunk ahead.
+//  * x, delta, z are staged per chunk of kT tokens into double-buffered,
+//    channel-major LDS tiles with coalesced row loads issued one chunk ahead;
+//    the token loop reads its lane's 16 deltas and x values in bulk, so it
+//    contains no memory waits.  Tokens past the end of the sequence are
+//    staged as delta = 0, which leaves the state unchanged, so every chunk
+//    runs the full unrolled loop.
 //  * Each wave writes its partial sum over its 4 states per token into LDS;
-//    after the chunk every wave finalises a 1/G share of the tokens (sum of
-//    G partials, skip term, gate) into the x tile, which is then stored to y
-//    with coalesced row writes.
+//    after the chunk the G waves finalise the 64 x kT outputs (sum of G
+//    partials, skip term, gate), each lane 4 consecutive tokens of one
+//    channel, stored as 16-byte writes.  Two barriers per chunk.
 //  * Few long rows (too few workgroups to fill 256 CUs) are cut into
 //    segments along L: pass 1 computes every segment's end state from zero
 //    and its summed delta, a tiny pass folds them into each segment's
@@ -34,6 +41,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "s6.h"
 
 namespace {
@@ -42,11 +52,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kCh = 64;            // channels per workgroup (one per lane)
 constexpr int kNS = 4;             // states per lane
 constexpr int kT = 16;             // tokens per chunk
-constexpr int kPitch = kCh + 1;    // LDS tile pitch in floats (token-major [t][c])
+constexpr int kP = kT;             // LDS tile pitch in floats (channel-major [c][t], swizzled)
 constexpr int kMaxN = 32;          // largest dstate supported
 constexpr int kMaxG = kMaxN / kNS; // waves per workgroup at most
-
-typedef const float __attribute__((address_space(4)))* const_f32_p;
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
@@ -57,28 +65,19 @@ __device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcp
 // SiLU(z) = z / (1 + e^-z) = z * rcp(1 + 2^(-z*log2 e))
 __device__ __forceinline__ float silu(float z) { return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e)); }
 
-// ----------------------------------------------------------------- packing --
-// B, C (batch, N, L) -> fp32 [batch][L][G][8] with slot j < 4 = B[4g + j],
-// slot 4 + j = C[4g + j]; states beyond N are zero.
-template <typename In>
-__global__ void s6_pack_bc(const In* __restrict__ Bm, const In* __restrict__ Cm,
-                           float* __restrict__ out, int64_t batch, int64_t L, int64_t N, int64_t G) {
-  const int64_t total = batch * L * G * 8;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t slot = i & 7;
-    const int64_t g = (i >> 3) % G;
-    const int64_t t = (i / (8 * G)) % L;
-    const int64_t b = i / (8 * G * L);
-    const int64_t n = g * kNS + (slot & 3);
-    float v = 0.0f;
-    if (n < N) {
-      const In* src = (slot < 4) ? Bm : Cm;
-      v = to_f32(src[(b * N + n) * L + t]);
-    }
-    out[i] = v;
-  }
+// Value of lane J of this lane's 16-lane row (DPP row_newbcast).  Used as an
+// operand of a multiply, the compiler folds it into v_mul_f32_dpp.
+template <int J>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + J,
+                                                               0xf, 0xf, true));
 }
+
+// Offset (floats) of the 4-token group `grp` of channel row c in a
+// channel-major tile of pitch kT = 16.  The group index is XORed with
+// (c >> 1) & 3 so that 16-byte reads of one group by 8 consecutive lanes
+// fall on 8 distinct 4-bank groups (no padding needed).
+__device__ __forceinline__ int tsw(int c, int grp) { return c * kP + ((grp ^ ((c >> 1) & 3)) << 2); }
 
 // -------------------------------------------------------------------- scan --
 enum { kModeY = 0, kModeState = 1 };
@@ -87,55 +86,182 @@ struct ScanArgs {
   const void* x;
   const void* delta;
   const void* z;          // gate input (kModeY with GATE only)
+  const void* Bm;         // (batch, N, L)
+  const void* Cm;         // (batch, N, L), kModeY only
   const float* A;         // (D, N)
   const float* Dskip;     // (D) or null
-  const float* bc;        // packed B/C
   const float* hinit;     // initial states or null (zero)
   float* y;               // kModeY output
   float* hout;            // final states or null
   float* sumdelta;        // kModeState: per-segment sum of delta (S, batch, D) or null
-  int64_t D, L, N, G;
+  int64_t D, L, N;
   int64_t seg_len;        // tokens per segment (multiple of kT); segment = blockIdx.z
   int64_t hinit_stride;   // elements between segments in hinit (0: same for all)
   int64_t hout_stride;    // elements between segments in hout
   int64_t hout_last_only; // 1: only the last segment writes hout (at offset 0)
 };
 
-// Load one chunk of a (rows, L) tensor into a token-major LDS tile.
-// VEC = elements per 16-byte vector (1 = element loads).
 template <typename In, int VEC>
-__device__ __forceinline__ void stage_tile(float* __restrict__ tile, const In* __restrict__ src,
-                                           int64_t row0, int64_t rows_valid, int64_t L, int64_t t0,
-                                           int64_t tend, int tid, int nthr) {
-  constexpr int kVecs = kT / VEC;  // vectors per row per chunk
-  for (int i = tid; i < kCh * kVecs; i += nthr) {
-    const int c = i / kVecs;
-    const int v = i - c * kVecs;
-    const int64_t t = t0 + v * VEC;
-    const bool ok = (c < rows_valid) && (t < tend);
+struct Stage {
+  // A chunk of one (rows, L) tensor: 64 rows x kT tokens, cut into pieces of
+  // VEC elements (16 bytes, or single elements when VEC == 1).
+  static constexpr int kPieces = kCh * (kT / VEC);
+  using Raw = typename std::conditional<VEC == 1, In, uint4>::type;
+
+  __device__ __forceinline__ static bool valid(int p, int64_t rows_valid, int64_t t0, int64_t tend) {
+    const int c = p / (kT / VEC);
+    const int v = p - c * (kT / VEC);
+    return c < rows_valid && t0 + v * VEC < tend;
+  }
+
+  // Unconditional load (a piece outside the tensor reads element 0 instead,
+  // and is replaced by zeros in store()): a conditional load would make the
+  // compiler wait for it at once and defeat the prefetch.
+  __device__ __forceinline__ static Raw load(const In* __restrict__ src, int p, int64_t row0,
+                                             int64_t rows_valid, int64_t L, int64_t t0, int64_t tend) {
+    const int c = p / (kT / VEC);
+    const int v = p - c * (kT / VEC);
+    const int64_t idx = valid(p, rows_valid, t0, tend) ? (row0 + c) * L + t0 + v * VEC : 0;
+    if constexpr (VEC == 1) return src[idx];
+    else return *reinterpret_cast<const uint4*>(src + idx);
+  }
+
+  __device__ __forceinline__ static void store(float* __restrict__ tile, int p, const Raw& r, bool ok) {
+    const int c = p / (kT / VEC);
+    const int v = p - c * (kT / VEC);
     if constexpr (VEC == 1) {
-      float val = ok ? to_f32(src[(row0 + c) * L + t]) : 0.0f;
-      tile[v * kPitch + c] = val;
+      tile[tsw(c, v >> 2) + (v & 3)] = ok ? to_f32(r) : 0.0f;
     } else {
-      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-      if (ok) raw = *reinterpret_cast<const uint4*>(src + (row0 + c) * L + t);
-      const In* e = reinterpret_cast<const In*>(&raw);
+      const In* e = reinterpret_cast<const In*>(&r);
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) tile[(v * VEC + k) * kPitch + c] = to_f32(e[k]);
+      for (int k = 0; k < VEC; k += 4)
+        *reinterpret_cast<float4*>(tile + tsw(c, (v * VEC + k) >> 2)) =
+            ok ? make_float4(to_f32(e[k]), to_f32(e[k + 1]), to_f32(e[k + 2]), to_f32(e[k + 3]))
+               : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+  }
+};
+
+// B and C of one chunk, staged like the tiles: per tensor, 4*G state rows
+// (states beyond N are zero) of kT tokens cut into VEC-element pieces.  In
+// LDS they are laid out as the DPP operands want them:
+// bcs[tensor][group g][wave w][x], x = 4*(token % 4) + state % 4, for token
+// 4g + token%4 and state 4w + state%4.
+template <typename In, int VEC, int G>
+struct StageBC {
+  static constexpr int kPiecesT = kNS * G * (kT / VEC);  // per tensor
+  static constexpr int kPieces = 2 * kPiecesT;
+  static constexpr int kFloats = 2 * 4 * G * 16;         // LDS floats per chunk
+  using Raw = typename std::conditional<VEC == 1, In, uint4>::type;
+
+  __device__ __forceinline__ static bool valid(int p, int64_t N, int64_t t0, int64_t tend) {
+    const int q = p % kPiecesT;
+    const int n = q / (kT / VEC);
+    const int v = q - n * (kT / VEC);
+    return n < N && t0 + v * VEC < tend;
+  }
+
+  __device__ __forceinline__ static Raw load(const In* __restrict__ Bm, const In* __restrict__ Cm, int p,
+                                             int64_t b, int64_t N, int64_t L, int64_t t0, int64_t tend) {
+    const int q = p % kPiecesT;
+    const int n = q / (kT / VEC);
+    const int v = q - n * (kT / VEC);
+    const In* M = (p < kPiecesT) ? Bm : Cm;
+    const int64_t idx = valid(p, N, t0, tend) ? (b * N + n) * L + t0 + v * VEC : 0;
+    if constexpr (VEC == 1) return M[idx];
+    else return *reinterpret_cast<const uint4*>(M + idx);
+  }
+
+  __device__ __forceinline__ static void store(float* __restrict__ bcs, int p, const Raw& r, bool ok) {
+    const int tens = p / kPiecesT;
+    const int q = p % kPiecesT;
+    const int n = q / (kT / VEC);
+    const int v = q - n * (kT / VEC);
+    float* base = bcs + tens * (4 * G * 16) + (n >> 2) * 16 + (n & 3);
+    if constexpr (VEC == 1) {
+      const int j = v;
+      base[(j >> 2) * (G * 16) + 4 * (j & 3)] = ok ? to_f32(r) : 0.0f;
+    } else {
+      const In* e = reinterpret_cast<const In*>(&r);
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) {
+        const int j = v * VEC + k;
+        base[(j >> 2) * (G * 16) + 4 * (j & 3)] = ok ? to_f32(e[k]) : 0.0f;
+      }
+    }
+  }
+};
+
+// Product of v with lane 4*TK+J of this lane's 16-lane row (folded into
+// v_mul_f32_dpp).
+template <int TK, int J>
+__device__ __forceinline__ float mul_bc(float bc, float v) { return row_bcast<4 * TK + J>(bc) * v; }
+
+// One group of 4 tokens.  dl/xv: this lane's deltas and inputs; Bv/Cv: the
+// group's B and C operand registers.  The work is issued phase by phase
+// (all 16 exponentials, then all 16 input terms, then the state chains, then
+// the output terms), so that every result is consumed well after it is
+// produced.
+template <int MODE>
+__device__ __forceinline__ void token_group(const float* dl, const float* xv, const float (&A2)[kNS],
+                                            float (&h)[kNS], float Bv, float Cv, float (&yv)[4]) {
+  float e[4][kNS], bx[4][kNS], u[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) e[t][j] = fast_exp2(dl[t] * A2[j]);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) u[t] = dl[t] * xv[t];
+  bx[0][0] = mul_bc<0, 0>(Bv, u[0]); bx[0][1] = mul_bc<0, 1>(Bv, u[0]);
+  bx[0][2] = mul_bc<0, 2>(Bv, u[0]); bx[0][3] = mul_bc<0, 3>(Bv, u[0]);
+  bx[1][0] = mul_bc<1, 0>(Bv, u[1]); bx[1][1] = mul_bc<1, 1>(Bv, u[1]);
+  bx[1][2] = mul_bc<1, 2>(Bv, u[1]); bx[1][3] = mul_bc<1, 3>(Bv, u[1]);
+  bx[2][0] = mul_bc<2, 0>(Bv, u[2]); bx[2][1] = mul_bc<2, 1>(Bv, u[2]);
+  bx[2][2] = mul_bc<2, 2>(Bv, u[2]); bx[2][3] = mul_bc<2, 3>(Bv, u[2]);
+  bx[3][0] = mul_bc<3, 0>(Bv, u[3]); bx[3][1] = mul_bc<3, 1>(Bv, u[3]);
+  bx[3][2] = mul_bc<3, 2>(Bv, u[3]); bx[3][3] = mul_bc<3, 3>(Bv, u[3]);
+  float hs[4][kNS];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) {
+      h[j] = __builtin_fmaf(e[t][j], h[j], bx[t][j]);
+      hs[t][j] = h[j];
+    }
+  if constexpr (MODE == kModeY) {
+    float p[4][kNS];
+    p[0][0] = mul_bc<0, 0>(Cv, hs[0][0]); p[0][1] = mul_bc<0, 1>(Cv, hs[0][1]);
+    p[0][2] = mul_bc<0, 2>(Cv, hs[0][2]); p[0][3] = mul_bc<0, 3>(Cv, hs[0][3]);
+    p[1][0] = mul_bc<1, 0>(Cv, hs[1][0]); p[1][1] = mul_bc<1, 1>(Cv, hs[1][1]);
+    p[1][2] = mul_bc<1, 2>(Cv, hs[1][2]); p[1][3] = mul_bc<1, 3>(Cv, hs[1][3]);
+    p[2][0] = mul_bc<2, 0>(Cv, hs[2][0]); p[2][1] = mul_bc<2, 1>(Cv, hs[2][1]);
+    p[2][2] = mul_bc<2, 2>(Cv, hs[2][2]); p[2][3] = mul_bc<2, 3>(Cv, hs[2][3]);
+    p[3][0] = mul_bc<3, 0>(Cv, hs[3][0]); p[3][1] = mul_bc<3, 1>(Cv, hs[3][1]);
+    p[3][2] = mul_bc<3, 2>(Cv, hs[3][2]); p[3][3] = mul_bc<3, 3>(Cv, hs[3][3]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) yv[t] = (p[t][0] + p[t][1]) + (p[t][2] + p[t][3]);
   }
 }
 
-template <typename In, int VEC, bool GATE, int MODE>
-__global__ void __launch_bounds__(kCh * kMaxG) s6_scan_kernel(ScanArgs a) {
-  extern __shared__ float lds[];
+template <typename In, int VEC, bool GATE, int MODE, int G>
+__global__ void __launch_bounds__(kCh * G) s6_scan_kernel(ScanArgs a) {
+  constexpr int NTHR = kCh * G;
+  constexpr int NTS = (MODE == kModeY && GATE) ? 3 : 2;  // staged tensors: x, delta (, z)
+  using S = Stage<In, VEC>;
+  constexpr int TILE = kCh * kP;                          // floats per tensor tile
+  constexpr int QPL = (kCh * kT / 4 + NTHR - 1) / NTHR;   // finalize groups per lane
+
+  extern __shared__ float4 lds4[];
+  float* lds = reinterpret_cast<float*>(lds4);
+  float* tiles = lds;                       // [2][NTS][64][kP], swizzled
+  float* part = lds + 2 * NTS * TILE;       // [G][64][kP], swizzled
+  float* bcs = part + (MODE == kModeY ? G * TILE : 0);  // [2][StageBC::kFloats]
+
   const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
   const int lane = tid & (kCh - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = (int)a.G;
   const int64_t D = a.D, L = a.L, N = a.N;
-  const int64_t nblk = (a.D + kCh - 1) / kCh;
+  const int64_t nblk = (D + kCh - 1) / kCh;
   const int64_t b = blockIdx.x / nblk;
   const int64_t d0 = (int64_t)(blockIdx.x % nblk) * kCh;
   const int64_t d = d0 + lane;
@@ -145,16 +271,12 @@ __global__ void __launch_bounds__(kCh * kMaxG) s6_scan_kernel(ScanArgs a) {
   const int64_t tb = seg * a.seg_len;
   const int64_t te = (tb + a.seg_len < L) ? tb + a.seg_len : L;
   const int64_t row0 = b * D + d0;
+  const int64_t nchunks = (te - tb + kT - 1) / kT;
 
-  constexpr int kTiles = (MODE == kModeY) ? (GATE ? 3 : 2) : 2;
-  float* tx = lds;
-  float* tdl = lds + kT * kPitch;
-  float* tz = lds + 2 * kT * kPitch;
-  float* part = lds + kTiles * kT * kPitch;
-
-  const In* xp = static_cast<const In*>(a.x);
-  const In* dp = static_cast<const In*>(a.delta);
-  const In* zp = static_cast<const In*>(a.z);
+  const In* src[3] = {static_cast<const In*>(a.x), static_cast<const In*>(a.delta),
+                      static_cast<const In*>(a.z)};
+  const In* Bp = static_cast<const In*>(a.Bm);
+  const In* Cp = static_cast<const In*>(MODE == kModeY ? a.Cm : a.Bm);
 
   float A2[kNS], h[kNS];
 #pragma unroll
@@ -164,68 +286,144 @@ __global__ void __launch_bounds__(kCh * kMaxG) s6_scan_kernel(ScanArgs a) {
     A2[j] = sv ? a.A[d * N + n] * kLog2e : 0.0f;
     h[j] = (sv && a.hinit) ? a.hinit[seg * a.hinit_stride + (b * D + d) * N + n] : 0.0f;
   }
-  const float dsk = (MODE == kModeY && a.Dskip && chv) ? a.Dskip[d] : 0.0f;
-  double dsum = 0.0;
-
-  for (int64_t t0 = tb; t0 < te; t0 += kT) {
-    const int nt = (int)((te - t0) < kT ? (te - t0) : kT);
-    __syncthreads();  // previous chunk fully consumed
-    stage_tile<In, VEC>(tx, xp, row0, rows_valid, L, t0, te, tid, nthr);
-    stage_tile<In, VEC>(tdl, dp, row0, rows_valid, L, t0, te, tid, nthr);
-    if constexpr (MODE == kModeY && GATE) stage_tile<In, VEC>(tz, zp, row0, rows_valid, L, t0, te, tid, nthr);
-    __syncthreads();
-
-    const float* bcrow = a.bc + ((b * L + t0) * G + w) * 8;
-    float csum = 0.0f;
-    for (int t = 0; t < nt; ++t) {
-      const float dt = tdl[t * kPitch + lane];
-      const float xt = tx[t * kPitch + lane];
-      const float u = dt * xt;
-      const_f32_p q = (const_f32_p)(bcrow + (int64_t)t * G * 8);
-      float yp = 0.0f;
+  // finalize slots: group q -> channel q/4, tokens 4*(q%4) .. +3
+  float dsk[QPL];
 #pragma unroll
-      for (int j = 0; j < kNS; ++j) {
-        const float e = fast_exp2(dt * A2[j]);
-        h[j] = __builtin_fmaf(e, h[j], u * q[j]);
-        if constexpr (MODE == kModeY) yp = __builtin_fmaf(q[kNS + j], h[j], yp);
+  for (int s = 0; s < QPL; ++s) {
+    const int q = tid + s * NTHR;
+    const int64_t dc = d0 + (q >> 2);
+    dsk[s] = (MODE == kModeY && q < kCh * kT / 4 && a.Dskip && dc < D) ? a.Dskip[dc] : 0.0f;
+  }
+  double dsum = 0.0;
+  // Let the loads above (A, h0, D) complete here: otherwise their pending
+  // state reaches the loop header and the first use of h inside the loop
+  // would wait for every outstanding load, prefetches included.
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // Staging: one flat list of pieces -- NTS tile tensors of TP pieces
+  // each, then the B/C pieces.  Loads are unconditional (invalid pieces read
+  // element 0); only the LDS writes depend on the piece.
+  using SB = StageBC<In, VEC, G>;
+  constexpr int TP = S::kPieces;
+  constexpr int TOTAL = NTS * TP + SB::kPieces;
+  constexpr int SLOTS = (TOTAL + NTHR - 1) / NTHR;
+  using Raw = typename S::Raw;
+  Raw pre[SLOTS];
+
+  auto issue_chunk = [&](int64_t t0) {
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      const int p = tid + s * NTHR;
+      if (p < NTS * TP) {
+        const int k = p / TP;
+        pre[s] = S::load(src[k], p - k * TP, row0, rows_valid, L, t0, te);
+      } else {
+        const int q = p - NTS * TP;
+        pre[s] = SB::load(Bp, Cp, q < SB::kPieces ? q : 0, b, N, L, t0, te);
       }
-      if constexpr (MODE == kModeY) part[(w * kT + t) * kCh + lane] = yp;
-      else csum += dt;
     }
-    if constexpr (MODE == kModeState) dsum += (double)csum;
+  };
+  auto write_chunk = [&](int buf, int64_t t0) {
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      const int p = tid + s * NTHR;
+      if (p < NTS * TP) {
+        const int k = p / TP;
+        const int q = p - k * TP;
+        S::store(tiles + (buf * NTS + k) * TILE, q, pre[s], S::valid(q, rows_valid, t0, te));
+      } else if (p < TOTAL) {
+        const int q = p - NTS * TP;
+        SB::store(bcs + buf * SB::kFloats, q, pre[s], SB::valid(q, N, t0, te));
+      }
+    }
+  };
+
+  if (nchunks > 0) {
+    issue_chunk(tb);
+    write_chunk(0, tb);
+    issue_chunk(tb + kT);
+  }
+  __syncthreads();
+
+  for (int64_t k = 0; k < nchunks; ++k) {
+    const int64_t t0 = tb + k * kT;
+    const int buf = (int)(k & 1);
+    const float* tx = tiles + (buf * NTS + 0) * TILE;
+    const float* tdl = tiles + (buf * NTS + 1) * TILE;
+
+    // this lane's kT deltas and inputs
+    float dl[kT], xv[kT];
+#pragma unroll
+    for (int i = 0; i < kT; i += 4) {
+      const float4 dv = *reinterpret_cast<const float4*>(tdl + tsw(lane, i >> 2));
+      const float4 xx = *reinterpret_cast<const float4*>(tx + tsw(lane, i >> 2));
+      dl[i] = dv.x; dl[i + 1] = dv.y; dl[i + 2] = dv.z; dl[i + 3] = dv.w;
+      xv[i] = xx.x; xv[i + 1] = xx.y; xv[i + 2] = xx.z; xv[i + 3] = xx.w;
+    }
+
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float* bcb = bcs + buf * SB::kFloats + g * (G * 16) + w * 16 + (lane & 15);
+      const float Bv = bcb[0];
+      const float Cv = bcb[4 * G * 16];
+      float yv[4];
+      token_group<MODE>(dl + 4 * g, xv + 4 * g, A2, h, Bv, Cv, yv);
+      if constexpr (MODE == kModeY)
+        *reinterpret_cast<float4*>(part + w * TILE + tsw(lane, g)) = make_float4(yv[0], yv[1], yv[2], yv[3]);
+    }
+    if constexpr (MODE == kModeState) {
+      float cs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kT; ++i) cs += dl[i];
+      dsum += (double)cs;
+    }
+    if constexpr (MODE == kModeY) __syncthreads();  // partial outputs of all waves are in LDS
+
+    // Stage chunk k+1 into the other buffer (its loads were issued one chunk
+    // ago; that buffer was last read before the previous barrier), then
+    // fetch chunk k+2.  Past the end of the segment the pieces are zeros.
+    write_chunk(buf ^ 1, t0 + kT);
+    issue_chunk(t0 + 2 * kT);
 
     if constexpr (MODE == kModeY) {
-      __syncthreads();
-      for (int t = w; t < nt; t += G) {
-        float ys = 0.0f;
-        for (int g = 0; g < G; ++g) ys += part[(g * kT + t) * kCh + lane];
-        ys = __builtin_fmaf(dsk, tx[t * kPitch + lane], ys);
-        if constexpr (GATE) ys *= silu(tz[t * kPitch + lane]);
-        tx[t * kPitch + lane] = ys;  // y replaces x in the tile
-      }
-      __syncthreads();
-      // coalesced store of the y tile: rows of nt fp32 values
-      constexpr int kVY = (VEC == 1) ? 1 : 4;
-      constexpr int kVecs = kT / kVY;
-      for (int i = tid; i < kCh * kVecs; i += nthr) {
-        const int c = i / kVecs;
-        const int v = i - c * kVecs;
-        const int64_t t = t0 + v * kVY;
-        if (c < rows_valid && t < te) {
-          float* dst = a.y + (row0 + c) * L + t;
-          if constexpr (kVY == 1) {
-            *dst = tx[v * kPitch + c];
-          } else {
-            float4 o;
-            o.x = tx[(v * 4 + 0) * kPitch + c];
-            o.y = tx[(v * 4 + 1) * kPitch + c];
-            o.z = tx[(v * 4 + 2) * kPitch + c];
-            o.w = tx[(v * 4 + 3) * kPitch + c];
-            *reinterpret_cast<float4*>(dst) = o;
+      const float* tz = tiles + (buf * NTS + 2) * TILE;
+#pragma unroll
+      for (int s = 0; s < QPL; ++s) {
+        const int q = tid + s * NTHR;
+        if (q < kCh * kT / 4) {
+          const int c = q >> 2;
+          const int tg = q & 3;
+          float4 acc = *reinterpret_cast<const float4*>(part + tsw(c, tg));
+#pragma unroll
+          for (int gg = 1; gg < G; ++gg) {
+            const float4 v = *reinterpret_cast<const float4*>(part + gg * TILE + tsw(c, tg));
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+          }
+          const float4 xx = *reinterpret_cast<const float4*>(tx + tsw(c, tg));
+          acc.x = __builtin_fmaf(dsk[s], xx.x, acc.x);
+          acc.y = __builtin_fmaf(dsk[s], xx.y, acc.y);
+          acc.z = __builtin_fmaf(dsk[s], xx.z, acc.z);
+          acc.w = __builtin_fmaf(dsk[s], xx.w, acc.w);
+          if constexpr (GATE) {
+            const float4 zz = *reinterpret_cast<const float4*>(tz + tsw(c, tg));
+            acc.x *= silu(zz.x); acc.y *= silu(zz.y); acc.z *= silu(zz.z); acc.w *= silu(zz.w);
+          }
+          const int64_t t = t0 + 4 * tg;
+          if (c < rows_valid) {
+            float* dst = a.y + (row0 + c) * L + t;
+            if constexpr (VEC > 1) {
+              if (t < te) *reinterpret_cast<float4*>(dst) = acc;
+            } else {
+              if (t < te) dst[0] = acc.x;
+              if (t + 1 < te) dst[1] = acc.y;
+              if (t + 2 < te) dst[2] = acc.z;
+              if (t + 3 < te) dst[3] = acc.w;
+            }
           }
         }
       }
     }
+    __syncthreads();
   }
 
   const bool write_h = a.hout && (!a.hout_last_only || seg == (int64_t)gridDim.z - 1);
@@ -242,10 +440,6 @@ __global__ void __launch_bounds__(kCh * kMaxG) s6_scan_kernel(ScanArgs a) {
   }
 }
 
-// Fold segment aggregates into every segment's incoming state:
-// H_0 = h0 (or 0); H_{s+1} = exp(A * sum_delta_s) * H_s + S_s.
-// hin (S, batch*D*N) receives H_s for s < S; hlast (nullable) gets H_S when
-// `nagg` == S aggregates are present.
 __global__ void s6_fold_carries(const float* __restrict__ A, const float* __restrict__ h0,
                                 const float* __restrict__ agg, const float* __restrict__ sumdelta,
                                 float* __restrict__ hin, float* __restrict__ hlast, int64_t batch,
@@ -362,9 +556,9 @@ int hip_fail(hipError_t e, const char* what) {
   return S6_ERR_HIP;
 }
 
-#define S6_HIP(call, what)                       \
-  do {                                           \
-    hipError_t e_ = (call);                      \
+#define S6_HIP(call, what)                           \
+  do {                                               \
+    hipError_t e_ = (call);                          \
     if (e_ != hipSuccess) return hip_fail(e_, what); \
   } while (0)
 
@@ -382,32 +576,33 @@ int check_common(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int
   if (batch < 0 || dim < 0 || seqlen < 0 || dstate < 0) return S6_ERR_SHAPE;
   if (dstate < 1 || dstate > kMaxN) return S6_ERR_UNSUPPORTED;
   int64_t t;
-  if (!mul_ok(batch, dim, &t) || !mul_ok(t, seqlen > 0 ? seqlen : 1, &t) ||
-      !mul_ok(t, 64, &t))  // headroom for packed and per-state buffers
-    return S6_ERR_SHAPE;
-  int64_t u;
-  if (!mul_ok(batch, seqlen > 0 ? seqlen : 1, &u) || !mul_ok(u, 8 * kMaxG, &u)) return S6_ERR_SHAPE;
+  if (!mul_ok(batch, dim, &t) || !mul_ok(t, seqlen > 0 ? seqlen : 1, &t) || !mul_ok(t, 64, &t))
+    return S6_ERR_SHAPE;  // element counts, with headroom for per-state buffers
   if (batch * ((dim + kCh - 1) / kCh) > INT32_MAX) return S6_ERR_SHAPE;  // grid size
   return S6_OK;
 }
 
 struct Plan {
-  int64_t G, nblk, segs, seg_len;
-  int vec;
+  int G;              // waves per workgroup (power of two, 4*G >= dstate)
+  int64_t nblk;       // channel blocks per batch row
+  int64_t segs;       // segments along L
+  int64_t seg_len;    // tokens per segment, multiple of kT
+  bool vec;           // 16-byte staging and stores
 };
 
-// Segments: enough workgroups to give every CU about three; a segment holds
-// at least 4 chunks.
+// Segments: when batch * channel blocks gives fewer than 512 workgroups,
+// cut L so that there are about 768 (three per CU), each segment holding at
+// least 4 chunks.
 Plan make_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, size_t esz,
                const void* const* ptrs, int nptr) {
   Plan p;
-  p.G = (dstate + kNS - 1) / kNS;
+  const int64_t need = (dstate + kNS - 1) / kNS;
+  p.G = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
   p.nblk = (dim + kCh - 1) / kCh;
   const int64_t wgs = p.nblk * batch;
-  const int64_t target = 768;
   int64_t segs = 1;
   if (wgs < 512) {
-    segs = (target + wgs - 1) / wgs;
+    segs = (768 + wgs - 1) / wgs;
     const int64_t max_segs = (seqlen + 4 * kT - 1) / (4 * kT);
     if (segs > max_segs) segs = max_segs;
     if (segs < 1) segs = 1;
@@ -422,57 +617,56 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, size_
   bool v = (seqlen % per_vec) == 0;
   for (int i = 0; i < nptr; ++i)
     if (ptrs[i] && !aligned(ptrs[i], 16)) v = false;
-  p.vec = v ? 1 : 0;
+  p.vec = v;
   return p;
 }
 
-template <typename In>
-int launch_pack(const void* Bm, const void* Cm, float* out, int64_t batch, int64_t L, int64_t N,
-                int64_t G, hipStream_t st) {
-  const int64_t total = batch * L * G * 8;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL((s6_pack_bc<In>), dim3((unsigned)blocks), dim3(256), 0, st,
-                     static_cast<const In*>(Bm), static_cast<const In*>(Cm), out, batch, L, N, G);
-  S6_HIP(hipGetLastError(), "s6_pack_bc launch");
-  return S6_OK;
-}
-
-template <typename In, int VEC, bool GATE, int MODE>
+template <typename In, int VEC, bool GATE, int MODE, int G>
 int launch_scan_t(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, hipStream_t st) {
-  const int tiles = (MODE == kModeY) ? (GATE ? 3 : 2) : 2;
-  size_t lds = (size_t)tiles * kT * kPitch * sizeof(float);
-  if (MODE == kModeY) lds += (size_t)a.G * kT * kCh * sizeof(float);
+  constexpr int nts = (MODE == kModeY && GATE) ? 3 : 2;
+  size_t lds = (size_t)2 * nts * kCh * kP * sizeof(float);
+  if (MODE == kModeY) lds += (size_t)G * kCh * kP * sizeof(float);
+  lds += (size_t)2 * StageBC<In, VEC, G>::kFloats * sizeof(float);
   dim3 grid((unsigned)(nblk * batch), 1u, (unsigned)segs);
-  hipLaunchKernelGGL((s6_scan_kernel<In, VEC, GATE, MODE>), grid, dim3((unsigned)(a.G * kCh)), lds, st, a);
+  hipLaunchKernelGGL((s6_scan_kernel<In, VEC, GATE, MODE, G>), grid, dim3(kCh * G), lds, st, a);
   S6_HIP(hipGetLastError(), "s6_scan_kernel launch");
   return S6_OK;
 }
 
-template <typename In, int MODE>
-int launch_scan(const ScanArgs& a, bool vec, bool gate, int64_t batch, int64_t nblk, int64_t segs,
-                hipStream_t st) {
+template <typename In, int MODE, int G>
+int launch_scan_g(const ScanArgs& a, bool vec, bool gate, int64_t batch, int64_t nblk, int64_t segs,
+                  hipStream_t st) {
   constexpr int kV = 16 / sizeof(In);
   if constexpr (MODE == kModeY) {
-    if (vec && gate) return launch_scan_t<In, kV, true, MODE>(a, batch, nblk, segs, st);
-    if (vec) return launch_scan_t<In, kV, false, MODE>(a, batch, nblk, segs, st);
-    if (gate) return launch_scan_t<In, 1, true, MODE>(a, batch, nblk, segs, st);
-    return launch_scan_t<In, 1, false, MODE>(a, batch, nblk, segs, st);
+    if (vec && gate) return launch_scan_t<In, kV, true, MODE, G>(a, batch, nblk, segs, st);
+    if (vec) return launch_scan_t<In, kV, false, MODE, G>(a, batch, nblk, segs, st);
+    if (gate) return launch_scan_t<In, 1, true, MODE, G>(a, batch, nblk, segs, st);
+    return launch_scan_t<In, 1, false, MODE, G>(a, batch, nblk, segs, st);
   } else {
-    if (vec) return launch_scan_t<In, kV, false, MODE>(a, batch, nblk, segs, st);
-    return launch_scan_t<In, 1, false, MODE>(a, batch, nblk, segs, st);
+    if (vec) return launch_scan_t<In, kV, false, MODE, G>(a, batch, nblk, segs, st);
+    return launch_scan_t<In, 1, false, MODE, G>(a, batch, nblk, segs, st);
   }
 }
 
-int launch_scan_any(int in_dtype, int mode, const ScanArgs& a, bool vec, bool gate, int64_t batch,
-                    int64_t nblk, int64_t segs, hipStream_t st) {
-  if (in_dtype == S6_BF16) {
-    return mode == kModeY ? launch_scan<uint16_t, kModeY>(a, vec, gate, batch, nblk, segs, st)
-                          : launch_scan<uint16_t, kModeState>(a, vec, gate, batch, nblk, segs, st);
+template <typename In, int MODE>
+int launch_scan(const ScanArgs& a, int G, bool vec, bool gate, int64_t batch, int64_t nblk, int64_t segs,
+                hipStream_t st) {
+  switch (G) {
+    case 1: return launch_scan_g<In, MODE, 1>(a, vec, gate, batch, nblk, segs, st);
+    case 2: return launch_scan_g<In, MODE, 2>(a, vec, gate, batch, nblk, segs, st);
+    case 4: return launch_scan_g<In, MODE, 4>(a, vec, gate, batch, nblk, segs, st);
+    default: return launch_scan_g<In, MODE, 8>(a, vec, gate, batch, nblk, segs, st);
   }
-  return mode == kModeY ? launch_scan<float, kModeY>(a, vec, gate, batch, nblk, segs, st)
-                        : launch_scan<float, kModeState>(a, vec, gate, batch, nblk, segs, st);
+}
+
+int launch_scan_any(int in_dtype, int mode, const ScanArgs& a, const Plan& p, bool gate, int64_t batch,
+                    int64_t segs, hipStream_t st) {
+  if (in_dtype == S6_BF16) {
+    return mode == kModeY ? launch_scan<uint16_t, kModeY>(a, p.G, p.vec, gate, batch, p.nblk, segs, st)
+                          : launch_scan<uint16_t, kModeState>(a, p.G, p.vec, gate, batch, p.nblk, segs, st);
+  }
+  return mode == kModeY ? launch_scan<float, kModeY>(a, p.G, p.vec, gate, batch, p.nblk, segs, st)
+                        : launch_scan<float, kModeState>(a, p.G, p.vec, gate, batch, p.nblk, segs, st);
 }
 
 // Shared implementation of s6_scan_fwd (want_y) and s6_last_state.
@@ -507,63 +701,61 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
   }
 
   const void* vecptrs[] = {x, delta, z, (const void*)y};
-  Plan p = make_plan(batch, dim, seqlen, dstate, esz, vecptrs, want_y ? 4 : 2);
+  const Plan p = make_plan(batch, dim, seqlen, dstate, esz, vecptrs, want_y ? 4 : 2);
   const bool gate = want_y && z != nullptr;
   const int64_t S = p.segs;
 
-  // workspace: packed B/C, then (segmented) aggregates, sums of delta, carries
-  const size_t bc_bytes = (size_t)batch * seqlen * p.G * 8 * sizeof(float);
-  const int64_t nagg = want_y ? S - 1 : S;
-  const size_t agg_bytes = (S > 1) ? (size_t)nagg * nstate * sizeof(float) : 0;
-  const size_t sd_bytes = (S > 1) ? (size_t)nagg * batch * dim * sizeof(float) : 0;
-  const size_t hin_bytes = (S > 1 && want_y) ? (size_t)S * nstate * sizeof(float) : 0;
-  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-  const size_t ws_bytes = up(bc_bytes) + up(agg_bytes) + up(sd_bytes) + up(hin_bytes);
-  void* ws = nullptr;
-  S6_HIP(hipMallocAsync(&ws, ws_bytes, st), "hipMallocAsync(workspace)");
-  char* wp = static_cast<char*>(ws);
-  float* bc = reinterpret_cast<float*>(wp);
-  float* agg = reinterpret_cast<float*>(wp + up(bc_bytes));
-  float* sd = reinterpret_cast<float*>(wp + up(bc_bytes) + up(agg_bytes));
-  float* hin = reinterpret_cast<float*>(wp + up(bc_bytes) + up(agg_bytes) + up(sd_bytes));
-
-  rc = (in_dtype == S6_BF16)
-           ? launch_pack<uint16_t>(Bm, want_y ? Cm : Bm, bc, batch, seqlen, dstate, p.G, st)
-           : launch_pack<float>(Bm, want_y ? Cm : Bm, bc, batch, seqlen, dstate, p.G, st);
-
   ScanArgs a;
   memset(&a, 0, sizeof(a));
-  a.x = x; a.delta = delta; a.z = z; a.A = A; a.Dskip = Dskip; a.bc = bc;
-  a.D = dim; a.L = seqlen; a.N = dstate; a.G = p.G; a.seg_len = p.seg_len;
+  a.x = x; a.delta = delta; a.z = gate ? z : nullptr; a.Bm = Bm; a.Cm = want_y ? Cm : nullptr;
+  a.A = A; a.Dskip = want_y ? Dskip : nullptr;
+  a.D = dim; a.L = seqlen; a.N = dstate; a.seg_len = p.seg_len;
 
-  if (rc == S6_OK && S > 1) {
-    // pass 1: aggregates of the first nagg segments, from a zero state
-    ScanArgs g = a;
-    g.hinit = nullptr;
-    g.hout = agg;
-    g.hout_stride = nstate;
-    g.sumdelta = sd;
-    rc = launch_scan_any(in_dtype, kModeState, g, p.vec, false, batch, p.nblk, nagg, st);
-    if (rc == S6_OK) {
-      const int64_t blocks = (nstate + 255) / 256;
-      hipLaunchKernelGGL(s6_fold_carries, dim3((unsigned)blocks), dim3(256), 0, st, A, h0, agg, sd,
-                         want_y ? hin : nullptr, want_y ? nullptr : h_last, batch, dim, dstate, S, nagg);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) rc = hip_fail(e, "s6_fold_carries launch");
-    }
+  if (S == 1) {
+    a.hinit = h0;
+    a.hout = h_last;
+    a.hout_last_only = 1;
+    a.y = y;
+    return launch_scan_any(in_dtype, want_y ? kModeY : kModeState, a, p, gate, batch, 1, st);
   }
-  if (rc == S6_OK && (want_y || S == 1)) {
+
+  // Segmented: workspace for segment end states, summed deltas and carries.
+  const int64_t nagg = want_y ? S - 1 : S;
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const size_t agg_bytes = (size_t)nagg * nstate * sizeof(float);
+  const size_t sd_bytes = (size_t)nagg * batch * dim * sizeof(float);
+  const size_t hin_bytes = want_y ? (size_t)S * nstate * sizeof(float) : 0;
+  void* ws = nullptr;
+  S6_HIP(hipMallocAsync(&ws, up(agg_bytes) + up(sd_bytes) + up(hin_bytes), st), "hipMallocAsync(workspace)");
+  char* wp = static_cast<char*>(ws);
+  float* agg = reinterpret_cast<float*>(wp);
+  float* sd = reinterpret_cast<float*>(wp + up(agg_bytes));
+  float* hin = reinterpret_cast<float*>(wp + up(agg_bytes) + up(sd_bytes));
+
+  // pass 1: end states of the first nagg segments from a zero state
+  ScanArgs g = a;
+  g.z = nullptr; g.Cm = nullptr; g.Dskip = nullptr;
+  g.hinit = nullptr;
+  g.hout = agg;
+  g.hout_stride = nstate;
+  g.sumdelta = sd;
+  rc = launch_scan_any(in_dtype, kModeState, g, p, false, batch, nagg, st);
+  if (rc == S6_OK) {
+    const int64_t blocks = (nstate + 255) / 256;
+    hipLaunchKernelGGL(s6_fold_carries, dim3((unsigned)blocks), dim3(256), 0, st, A, h0, agg, sd,
+                       want_y ? hin : nullptr, want_y ? nullptr : h_last, batch, dim, dstate, S, nagg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) rc = hip_fail(e, "s6_fold_carries launch");
+  }
+  // pass 2: the fused scan of every segment from its incoming state
+  if (rc == S6_OK && want_y) {
     ScanArgs m = a;
-    if (S > 1) {
-      m.hinit = hin;
-      m.hinit_stride = nstate;
-    } else {
-      m.hinit = h0;
-    }
+    m.hinit = hin;
+    m.hinit_stride = nstate;
     m.hout = h_last;
     m.hout_last_only = 1;
     m.y = y;
-    rc = launch_scan_any(in_dtype, want_y ? kModeY : kModeState, m, p.vec, gate, batch, p.nblk, S, st);
+    rc = launch_scan_any(in_dtype, kModeY, m, p, gate, batch, S, st);
   }
   hipError_t e = hipFreeAsync(ws, st);
   if (rc == S6_OK && e != hipSuccess) rc = hip_fail(e, "hipFreeAsync(workspace)");

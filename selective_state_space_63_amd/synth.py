@@ -205,7 +205,7 @@ def full(w: Workload, threads: int | None = None) -> dict:
 
 
 # ------------------------------------------------------- device generation --
-def device_full(w: Workload, device="cuda", pair_chunk: int = 256) -> dict:
+def device_full(w: Workload, device="cuda", pair_chunk: int | None = None) -> dict:
     """The whole workload generated directly in device memory with torch's
     counter-based (Philox) CUDA generator -- for the large workloads, where
     drawing billions of values on the host would dominate a run.  Same
@@ -213,12 +213,15 @@ def device_full(w: Workload, device="cuda", pair_chunk: int = 256) -> dict:
     the input dtype by torch, nearest-even); different draws.  Deterministic
     for a given workload.  Seeding: tensor kind k (0 u, 1 D_skip, 2 B, 3 C,
     4 eps/U, 5 x, 6 z) of pair chunk j uses seed
-    ((w.seed * 8 + k) * 1_000_003 + j) mod 2^63.  Returns torch tensors:
+    ((w.seed * 8 + k) * 1_000_003 + j) mod 2^63; a pair chunk holds
+    floor(2^26 / L) pairs unless `pair_chunk` is given.  Returns torch tensors:
     x, delta, z (batch, D, L), Bm, Cm (batch, N, L) in the input dtype,
     A (D, N) and Dskip (D,) fp32."""
     import torch
 
     dt = torch.float32 if w.dtype == F32 else torch.bfloat16
+    if pair_chunk is None:  # about 2^26 elements per temporary
+        pair_chunk = max(1, (1 << 26) // max(1, w.seqlen))
 
     def gen(kind, j=0):
         g = torch.Generator(device=device)
