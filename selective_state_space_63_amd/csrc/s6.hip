@@ -49,15 +49,20 @@
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kCh = 64;            // channels per workgroup (one per lane)
-constexpr int kNS = 4;             // states per lane
+constexpr int kCW = 32;            // channels per workgroup
 constexpr int kT = 16;             // tokens per chunk
 constexpr int kP = kT;             // LDS tile pitch in floats (channel-major [c][t], swizzled)
 constexpr int kMaxN = 32;          // largest dstate supported
-constexpr int kMaxG = kMaxN / kNS; // waves per workgroup at most
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Pointer into global memory.  Loads through it are global_load_*: a
+// generic pointer picked among several could become a flat load, which also
+// counts against the LDS wait counter and would stall LDS waits on prefetches.
+template <typename T>
+using gptr = const T __attribute__((address_space(1)))*;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // raw 16-byte piece
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 __device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
@@ -101,12 +106,13 @@ struct ScanArgs {
   int64_t hout_last_only; // 1: only the last segment writes hout (at offset 0)
 };
 
+// One chunk of a (rows, L) tensor for the kCW channels of a workgroup: kCW
+// rows x kT tokens, cut into pieces of VEC elements (16 bytes, or single
+// elements when VEC == 1).
 template <typename In, int VEC>
 struct Stage {
-  // A chunk of one (rows, L) tensor: 64 rows x kT tokens, cut into pieces of
-  // VEC elements (16 bytes, or single elements when VEC == 1).
-  static constexpr int kPieces = kCh * (kT / VEC);
-  using Raw = typename std::conditional<VEC == 1, In, uint4>::type;
+  static constexpr int kPieces = kCW * (kT / VEC);
+  using Raw = typename std::conditional<VEC == 1, In, u32x4>::type;
 
   __device__ __forceinline__ static bool valid(int p, int64_t rows_valid, int64_t t0, int64_t tend) {
     const int c = p / (kT / VEC);
@@ -117,13 +123,30 @@ struct Stage {
   // Unconditional load (a piece outside the tensor reads element 0 instead,
   // and is replaced by zeros in store()): a conditional load would make the
   // compiler wait for it at once and defeat the prefetch.
-  __device__ __forceinline__ static Raw load(const In* __restrict__ src, int p, int64_t row0,
-                                             int64_t rows_valid, int64_t L, int64_t t0, int64_t tend) {
+  __device__ __forceinline__ static Raw load(gptr<In> src, int p, int64_t row0, int64_t rows_valid,
+                                             int64_t L, int64_t t0, int64_t tend) {
     const int c = p / (kT / VEC);
     const int v = p - c * (kT / VEC);
     const int64_t idx = valid(p, rows_valid, t0, tend) ? (row0 + c) * L + t0 + v * VEC : 0;
     if constexpr (VEC == 1) return src[idx];
-    else return *reinterpret_cast<const uint4*>(src + idx);
+    else return *reinterpret_cast<gptr<u32x4>>(src + idx);
+  }
+
+  // Same layout, values kept in the input type (the gate tile).
+  __device__ __forceinline__ static void store_raw(In* __restrict__ tile, int p, const Raw& r, bool ok) {
+    const int c = p / (kT / VEC);
+    const int v = p - c * (kT / VEC);
+    if constexpr (VEC == 1) {
+      tile[tsw(c, v >> 2) + (v & 3)] = ok ? r : In(0);
+    } else {
+      const In* e = reinterpret_cast<const In*>(&r);
+#pragma unroll
+      for (int k = 0; k < VEC; k += 4) {
+        In* dst = tile + tsw(c, (v * VEC + k) >> 2);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) dst[m] = ok ? e[k + m] : In(0);
+      }
+    }
   }
 
   __device__ __forceinline__ static void store(float* __restrict__ tile, int p, const Raw& r, bool ok) {
@@ -142,17 +165,17 @@ struct Stage {
   }
 };
 
-// B and C of one chunk, staged like the tiles: per tensor, 4*G state rows
-// (states beyond N are zero) of kT tokens cut into VEC-element pieces.  In
-// LDS they are laid out as the DPP operands want them:
-// bcs[tensor][group g][wave w][x], x = 4*(token % 4) + state % 4, for token
-// 4g + token%4 and state 4w + state%4.
-template <typename In, int VEC, int G>
+// B and C of one chunk: per tensor 4*W state rows (states beyond N are zero)
+// of kT tokens, cut into VEC-element pieces.  In LDS they are laid out as
+// the DPP operands want them: for token group g (4 tokens), wave w and row
+// parity r (state pair 4w + 2r, 4w + 2r + 1), 16 slots: B of token k, state
+// pair member j at slot 2k + j, C at slot 8 + 2k + j.
+template <typename In, int VEC, int W>
 struct StageBC {
-  static constexpr int kPiecesT = kNS * G * (kT / VEC);  // per tensor
+  static constexpr int kPiecesT = 4 * W * (kT / VEC);  // per tensor
   static constexpr int kPieces = 2 * kPiecesT;
-  static constexpr int kFloats = 2 * 4 * G * 16;         // LDS floats per chunk
-  using Raw = typename std::conditional<VEC == 1, In, uint4>::type;
+  static constexpr int kFloats = (kT / 4) * W * 2 * 16;  // LDS floats per chunk
+  using Raw = typename std::conditional<VEC == 1, In, u32x4>::type;
 
   __device__ __forceinline__ static bool valid(int p, int64_t N, int64_t t0, int64_t tend) {
     const int q = p % kPiecesT;
@@ -161,15 +184,28 @@ struct StageBC {
     return n < N && t0 + v * VEC < tend;
   }
 
-  __device__ __forceinline__ static Raw load(const In* __restrict__ Bm, const In* __restrict__ Cm, int p,
-                                             int64_t b, int64_t N, int64_t L, int64_t t0, int64_t tend) {
+  __device__ __forceinline__ static Raw load(gptr<In> Bm, gptr<In> Cm, int p, int64_t b, int64_t N,
+                                             int64_t L, int64_t t0, int64_t tend) {
     const int q = p % kPiecesT;
     const int n = q / (kT / VEC);
     const int v = q - n * (kT / VEC);
-    const In* M = (p < kPiecesT) ? Bm : Cm;
+    gptr<In> M = (p < kPiecesT) ? Bm : Cm;
     const int64_t idx = valid(p, N, t0, tend) ? (b * N + n) * L + t0 + v * VEC : 0;
     if constexpr (VEC == 1) return M[idx];
-    else return *reinterpret_cast<const uint4*>(M + idx);
+    else return *reinterpret_cast<gptr<u32x4>>(M + idx);
+  }
+
+  // LDS position of slot x of (group g, wave w, row parity r).  The slot is
+  // XORed with a (g, w)-dependent mask so that the scattered writes of one
+  // instruction fall on distinct banks; readers apply the same mask, so
+  // lane x still receives slot x.
+  __device__ __forceinline__ static int pos(int g, int w, int r, int x) {
+    return ((g * W + w) * 2 + r) * 16 + (x ^ (((w & 3) << 2) ^ (((g >> 1) & 1) << 1)));
+  }
+  __device__ __forceinline__ static int slot(int tens, int n, int j) {
+    const int g = j >> 2, k = j & 3;
+    const int w = n >> 2, r = (n >> 1) & 1, m = n & 1;
+    return pos(g, w, r, tens * 8 + 2 * k + m);
   }
 
   __device__ __forceinline__ static void store(float* __restrict__ bcs, int p, const Raw& r, bool ok) {
@@ -177,94 +213,109 @@ struct StageBC {
     const int q = p % kPiecesT;
     const int n = q / (kT / VEC);
     const int v = q - n * (kT / VEC);
-    float* base = bcs + tens * (4 * G * 16) + (n >> 2) * 16 + (n & 3);
     if constexpr (VEC == 1) {
-      const int j = v;
-      base[(j >> 2) * (G * 16) + 4 * (j & 3)] = ok ? to_f32(r) : 0.0f;
+      bcs[slot(tens, n, v)] = ok ? to_f32(r) : 0.0f;
     } else {
       const In* e = reinterpret_cast<const In*>(&r);
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) {
-        const int j = v * VEC + k;
-        base[(j >> 2) * (G * 16) + 4 * (j & 3)] = ok ? to_f32(e[k]) : 0.0f;
-      }
+      for (int k = 0; k < VEC; ++k) bcs[slot(tens, n, v * VEC + k)] = ok ? to_f32(e[k]) : 0.0f;
     }
   }
 };
 
-// Product of v with lane 4*TK+J of this lane's 16-lane row (folded into
-// v_mul_f32_dpp).
-template <int TK, int J>
-__device__ __forceinline__ float mul_bc(float bc, float v) { return row_bcast<4 * TK + J>(bc) * v; }
+// Product of v with lane J of this lane's 16-lane row (v_mul_f32_dpp).
+template <int J>
+__device__ __forceinline__ float mul_bc(float bc, float v) { return row_bcast<J>(bc) * v; }
 
-// One group of 4 tokens.  dl/xv: this lane's deltas and inputs; Bv/Cv: the
-// group's B and C operand registers.  The work is issued phase by phase
-// (all 16 exponentials, then all 16 input terms, then the state chains, then
-// the output terms), so that every result is consumed well after it is
-// produced.
+// Value of lane (l ^ 16) -- the other state pair of the same channel -- via
+// the LDS crossbar (ds_swizzle, bit mode, xor mask 16).
+__device__ __forceinline__ float swap_rows(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+
+// One group of 4 tokens for this lane's 2 states.  dl/xv: the lane's deltas
+// and inputs; bc: the row's B/C operand register.  All exponentials are
+// issued first, then the input terms, the state chains and the output terms,
+// so every result is consumed well after it is produced.  On return
+// ys[0], ys[1] hold the channel's output sums over this wave's 4 states for
+// tokens 2*0 + r and 2*1 + r of the group (r = row parity), i.e. the two
+// state pairs of the channel are added across rows.
 template <int MODE>
-__device__ __forceinline__ void token_group(const float* dl, const float* xv, const float (&A2)[kNS],
-                                            float (&h)[kNS], float Bv, float Cv, float (&yv)[4]) {
-  float e[4][kNS], bx[4][kNS], u[4];
+__device__ __forceinline__ void token_group(const float* dl, const float* xv, const float (&A2)[2],
+                                            float (&h)[2], float bc, bool odd_row, float (&ys)[2]) {
+  float e[4][2], bx[4][2], u[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int j = 0; j < kNS; ++j) e[t][j] = fast_exp2(dl[t] * A2[j]);
+  for (int t = 0; t < 4; ++t) {
+    e[t][0] = fast_exp2(dl[t] * A2[0]);
+    e[t][1] = fast_exp2(dl[t] * A2[1]);
+  }
 #pragma unroll
   for (int t = 0; t < 4; ++t) u[t] = dl[t] * xv[t];
-  bx[0][0] = mul_bc<0, 0>(Bv, u[0]); bx[0][1] = mul_bc<0, 1>(Bv, u[0]);
-  bx[0][2] = mul_bc<0, 2>(Bv, u[0]); bx[0][3] = mul_bc<0, 3>(Bv, u[0]);
-  bx[1][0] = mul_bc<1, 0>(Bv, u[1]); bx[1][1] = mul_bc<1, 1>(Bv, u[1]);
-  bx[1][2] = mul_bc<1, 2>(Bv, u[1]); bx[1][3] = mul_bc<1, 3>(Bv, u[1]);
-  bx[2][0] = mul_bc<2, 0>(Bv, u[2]); bx[2][1] = mul_bc<2, 1>(Bv, u[2]);
-  bx[2][2] = mul_bc<2, 2>(Bv, u[2]); bx[2][3] = mul_bc<2, 3>(Bv, u[2]);
-  bx[3][0] = mul_bc<3, 0>(Bv, u[3]); bx[3][1] = mul_bc<3, 1>(Bv, u[3]);
-  bx[3][2] = mul_bc<3, 2>(Bv, u[3]); bx[3][3] = mul_bc<3, 3>(Bv, u[3]);
-  float hs[4][kNS];
+  bx[0][0] = mul_bc<0>(bc, u[0]); bx[0][1] = mul_bc<1>(bc, u[0]);
+  bx[1][0] = mul_bc<2>(bc, u[1]); bx[1][1] = mul_bc<3>(bc, u[1]);
+  bx[2][0] = mul_bc<4>(bc, u[2]); bx[2][1] = mul_bc<5>(bc, u[2]);
+  bx[3][0] = mul_bc<6>(bc, u[3]); bx[3][1] = mul_bc<7>(bc, u[3]);
+  float hs[4][2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int j = 0; j < kNS; ++j) {
-      h[j] = __builtin_fmaf(e[t][j], h[j], bx[t][j]);
-      hs[t][j] = h[j];
-    }
+  for (int t = 0; t < 4; ++t) {
+    h[0] = __builtin_fmaf(e[t][0], h[0], bx[t][0]);
+    h[1] = __builtin_fmaf(e[t][1], h[1], bx[t][1]);
+    hs[t][0] = h[0];
+    hs[t][1] = h[1];
+  }
   if constexpr (MODE == kModeY) {
-    float p[4][kNS];
-    p[0][0] = mul_bc<0, 0>(Cv, hs[0][0]); p[0][1] = mul_bc<0, 1>(Cv, hs[0][1]);
-    p[0][2] = mul_bc<0, 2>(Cv, hs[0][2]); p[0][3] = mul_bc<0, 3>(Cv, hs[0][3]);
-    p[1][0] = mul_bc<1, 0>(Cv, hs[1][0]); p[1][1] = mul_bc<1, 1>(Cv, hs[1][1]);
-    p[1][2] = mul_bc<1, 2>(Cv, hs[1][2]); p[1][3] = mul_bc<1, 3>(Cv, hs[1][3]);
-    p[2][0] = mul_bc<2, 0>(Cv, hs[2][0]); p[2][1] = mul_bc<2, 1>(Cv, hs[2][1]);
-    p[2][2] = mul_bc<2, 2>(Cv, hs[2][2]); p[2][3] = mul_bc<2, 3>(Cv, hs[2][3]);
-    p[3][0] = mul_bc<3, 0>(Cv, hs[3][0]); p[3][1] = mul_bc<3, 1>(Cv, hs[3][1]);
-    p[3][2] = mul_bc<3, 2>(Cv, hs[3][2]); p[3][3] = mul_bc<3, 3>(Cv, hs[3][3]);
+    float p[4];
+    p[0] = mul_bc<8>(bc, hs[0][0]) + mul_bc<9>(bc, hs[0][1]);
+    p[1] = mul_bc<10>(bc, hs[1][0]) + mul_bc<11>(bc, hs[1][1]);
+    p[2] = mul_bc<12>(bc, hs[2][0]) + mul_bc<13>(bc, hs[2][1]);
+    p[3] = mul_bc<14>(bc, hs[3][0]) + mul_bc<15>(bc, hs[3][1]);
+    // token pairs (0,1) and (2,3): even rows keep the first, odd rows the second
 #pragma unroll
-    for (int t = 0; t < 4; ++t) yv[t] = (p[t][0] + p[t][1]) + (p[t][2] + p[t][3]);
+    for (int q = 0; q < 2; ++q) {
+      const float send = odd_row ? p[2 * q] : p[2 * q + 1];
+      const float keep = odd_row ? p[2 * q + 1] : p[2 * q];
+      ys[q] = keep + swap_rows(send);
+    }
   }
 }
 
-template <typename In, int VEC, bool GATE, int MODE, int G>
-__global__ void __launch_bounds__(kCh * G) s6_scan_kernel(ScanArgs a) {
-  constexpr int NTHR = kCh * G;
+// Workgroup = kCW channels of one batch row x W waves.  Lane l of wave w:
+// channel cl = (l >> 5) * 16 + (l & 15), states 4w + 2r and 4w + 2r + 1 with
+// r = (l >> 4) & 1 (the row parity).  The lane also finalises TPL = kT/(2W)
+// consecutive tokens of its own channel (lane group 2w + r); it takes their
+// x and z from the tiles into registers before the chunk's barrier, so one
+// barrier per chunk suffices (tiles and partial outputs are double-buffered).
+template <typename In, int VEC, bool GATE, int MODE, int W>
+__global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
+  constexpr int NTHR = 64 * W;
   constexpr int NTS = (MODE == kModeY && GATE) ? 3 : 2;  // staged tensors: x, delta (, z)
   using S = Stage<In, VEC>;
-  constexpr int TILE = kCh * kP;                          // floats per tensor tile
-  constexpr int QPL = (kCh * kT / 4 + NTHR - 1) / NTHR;   // finalize groups per lane
+  using SB = StageBC<In, VEC, W>;
+  constexpr int TILE = kCW * kP;                  // floats per tensor tile
+  constexpr int PART = 2 * kCW * (kT / 2);        // partial floats per wave
+  constexpr int TPL = (kT / (2 * W)) > 0 ? kT / (2 * W) : 1;  // finalised tokens per lane
+  constexpr int LG = kT / TPL;                    // lane groups that finalise
 
   extern __shared__ float4 lds4[];
   float* lds = reinterpret_cast<float*>(lds4);
-  float* tiles = lds;                       // [2][NTS][64][kP], swizzled
-  float* part = lds + 2 * NTS * TILE;       // [G][64][kP], swizzled
-  float* bcs = part + (MODE == kModeY ? G * TILE : 0);  // [2][StageBC::kFloats]
+  float* tiles = lds;                                         // [2][2][kCW][kP] x, delta, swizzled
+  In* ztile = reinterpret_cast<In*>(tiles + 2 * 2 * TILE);    // [2][kCW][kP] gate input, input type
+  constexpr int ZFL = (MODE == kModeY && GATE) ? (2 * TILE * (int)sizeof(In) + 15) / 16 * 4 : 0;
+  float* part = tiles + 2 * 2 * TILE + ZFL;                   // [2][W][2][kCW][8]
+  float* bcs = part + (MODE == kModeY ? 2 * W * PART : 0);    // [2][SB::kFloats]
 
   const int tid = threadIdx.x;
-  const int lane = tid & (kCh - 1);
+  const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = (lane >> 4) & 1;
+  const int cl = ((lane >> 5) << 4) | (lane & 15);          // channel within the block
+  const int lg = 2 * w + r;                                  // finalize lane group
+  const bool fin = lg < LG;
   const int64_t D = a.D, L = a.L, N = a.N;
-  const int64_t nblk = (D + kCh - 1) / kCh;
+  const int64_t nblk = (D + kCW - 1) / kCW;
   const int64_t b = blockIdx.x / nblk;
-  const int64_t d0 = (int64_t)(blockIdx.x % nblk) * kCh;
-  const int64_t d = d0 + lane;
+  const int64_t d0 = (int64_t)(blockIdx.x % nblk) * kCW;
+  const int64_t d = d0 + cl;
   const bool chv = d < D;
   const int64_t rows_valid = D - d0;
   const int64_t seg = blockIdx.z;
@@ -273,44 +324,36 @@ __global__ void __launch_bounds__(kCh * G) s6_scan_kernel(ScanArgs a) {
   const int64_t row0 = b * D + d0;
   const int64_t nchunks = (te - tb + kT - 1) / kT;
 
-  const In* src[3] = {static_cast<const In*>(a.x), static_cast<const In*>(a.delta),
-                      static_cast<const In*>(a.z)};
-  const In* Bp = static_cast<const In*>(a.Bm);
-  const In* Cp = static_cast<const In*>(MODE == kModeY ? a.Cm : a.Bm);
+  gptr<In> src[3] = {(gptr<In>)a.x, (gptr<In>)a.delta, (gptr<In>)a.z};
+  gptr<In> Bp = (gptr<In>)a.Bm;
+  gptr<In> Cp = (gptr<In>)(MODE == kModeY ? a.Cm : a.Bm);
 
-  float A2[kNS], h[kNS];
+  float A2[2], h[2];
 #pragma unroll
-  for (int j = 0; j < kNS; ++j) {
-    const int64_t n = (int64_t)w * kNS + j;
+  for (int j = 0; j < 2; ++j) {
+    const int64_t n = (int64_t)w * 4 + 2 * r + j;
     const bool sv = chv && n < N;
     A2[j] = sv ? a.A[d * N + n] * kLog2e : 0.0f;
     h[j] = (sv && a.hinit) ? a.hinit[seg * a.hinit_stride + (b * D + d) * N + n] : 0.0f;
   }
-  // finalize slots: group q -> channel q/4, tokens 4*(q%4) .. +3
-  float dsk[QPL];
-#pragma unroll
-  for (int s = 0; s < QPL; ++s) {
-    const int q = tid + s * NTHR;
-    const int64_t dc = d0 + (q >> 2);
-    dsk[s] = (MODE == kModeY && q < kCh * kT / 4 && a.Dskip && dc < D) ? a.Dskip[dc] : 0.0f;
-  }
+  const float dsk = (MODE == kModeY && a.Dskip && chv) ? a.Dskip[d] : 0.0f;
   double dsum = 0.0;
   // Let the loads above (A, h0, D) complete here: otherwise their pending
   // state reaches the loop header and the first use of h inside the loop
   // would wait for every outstanding load, prefetches included.
   __builtin_amdgcn_s_waitcnt(0);
 
-  // Staging: one flat list of pieces -- NTS tile tensors of TP pieces
-  // each, then the B/C pieces.  Loads are unconditional (invalid pieces read
+  // Staging: one flat list of pieces -- NTS tile tensors of TP pieces each,
+  // then the B/C pieces.  Loads are unconditional (invalid pieces read
   // element 0); only the LDS writes depend on the piece.
-  using SB = StageBC<In, VEC, G>;
   constexpr int TP = S::kPieces;
   constexpr int TOTAL = NTS * TP + SB::kPieces;
   constexpr int SLOTS = (TOTAL + NTHR - 1) / NTHR;
-  using Raw = typename S::Raw;
-  Raw pre[SLOTS];
+  // Two register sets of loads in flight: chunk j goes to set j % 2, is
+  // issued two chunks ahead and written to LDS one chunk ahead of its use.
+  typename S::Raw preA[SLOTS], preB[SLOTS];
 
-  auto issue_chunk = [&](int64_t t0) {
+  auto issue_chunk = [&](int64_t t0, typename S::Raw (&pre)[SLOTS]) {
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
       const int p = tid + s * NTHR;
@@ -323,14 +366,15 @@ __global__ void __launch_bounds__(kCh * G) s6_scan_kernel(ScanArgs a) {
       }
     }
   };
-  auto write_chunk = [&](int buf, int64_t t0) {
+  auto write_chunk = [&](int buf, int64_t t0, typename S::Raw (&pre)[SLOTS]) {
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
       const int p = tid + s * NTHR;
       if (p < NTS * TP) {
         const int k = p / TP;
         const int q = p - k * TP;
-        S::store(tiles + (buf * NTS + k) * TILE, q, pre[s], S::valid(q, rows_valid, t0, te));
+        if (k < 2) S::store(tiles + (buf * 2 + k) * TILE, q, pre[s], S::valid(q, rows_valid, t0, te));
+        else S::store_raw(ztile + buf * TILE, q, pre[s], S::valid(q, rows_valid, t0, te));
       } else if (p < TOTAL) {
         const int q = p - NTS * TP;
         SB::store(bcs + buf * SB::kFloats, q, pre[s], SB::valid(q, N, t0, te));
@@ -339,37 +383,55 @@ __global__ void __launch_bounds__(kCh * G) s6_scan_kernel(ScanArgs a) {
   };
 
   if (nchunks > 0) {
-    issue_chunk(tb);
-    write_chunk(0, tb);
-    issue_chunk(tb + kT);
+    issue_chunk(tb, preA);
+    write_chunk(0, tb, preA);
+    issue_chunk(tb + kT, preB);
+    issue_chunk(tb + 2 * kT, preA);
   }
   __syncthreads();
 
-  for (int64_t k = 0; k < nchunks; ++k) {
+  // One chunk; `nxt` holds the loads of chunk k+1 and receives chunk k+3.
+  auto chunk = [&](int64_t k, typename S::Raw (&nxt)[SLOTS]) {
     const int64_t t0 = tb + k * kT;
     const int buf = (int)(k & 1);
-    const float* tx = tiles + (buf * NTS + 0) * TILE;
-    const float* tdl = tiles + (buf * NTS + 1) * TILE;
+    const float* tx = tiles + (buf * 2 + 0) * TILE;
+    const float* tdl = tiles + (buf * 2 + 1) * TILE;
 
     // this lane's kT deltas and inputs
     float dl[kT], xv[kT];
 #pragma unroll
     for (int i = 0; i < kT; i += 4) {
-      const float4 dv = *reinterpret_cast<const float4*>(tdl + tsw(lane, i >> 2));
-      const float4 xx = *reinterpret_cast<const float4*>(tx + tsw(lane, i >> 2));
+      const float4 dv = *reinterpret_cast<const float4*>(tdl + tsw(cl, i >> 2));
+      const float4 xx = *reinterpret_cast<const float4*>(tx + tsw(cl, i >> 2));
       dl[i] = dv.x; dl[i + 1] = dv.y; dl[i + 2] = dv.z; dl[i + 3] = dv.w;
       xv[i] = xx.x; xv[i + 1] = xx.y; xv[i + 2] = xx.z; xv[i + 3] = xx.w;
     }
 
+    // x and z of the tokens this lane finalises (the tiles are overwritten
+    // before this chunk's finalisation can run)
+    float xfin[TPL], zfin[TPL];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float* bcb = bcs + buf * SB::kFloats + g * (G * 16) + w * 16 + (lane & 15);
-      const float Bv = bcb[0];
-      const float Cv = bcb[4 * G * 16];
-      float yv[4];
-      token_group<MODE>(dl + 4 * g, xv + 4 * g, A2, h, Bv, Cv, yv);
-      if constexpr (MODE == kModeY)
-        *reinterpret_cast<float4*>(part + w * TILE + tsw(lane, g)) = make_float4(yv[0], yv[1], yv[2], yv[3]);
+    for (int i = 0; i < TPL; ++i) {
+      const int t = (fin ? lg * TPL : 0) + i;
+      xfin[i] = tx[tsw(cl, t >> 2) + (t & 3)];
+      zfin[i] = (MODE == kModeY && GATE) ? to_f32(ztile[buf * TILE + tsw(cl, t >> 2) + (t & 3)]) : 0.0f;
+    }
+
+    float ysum[kT / 2];
+#pragma unroll
+    for (int g = 0; g < kT / 4; ++g) {
+      const float bc = bcs[buf * SB::kFloats + SB::pos(g, w, r, lane & 15)];
+      float ys[2];
+      token_group<MODE>(dl + 4 * g, xv + 4 * g, A2, h, bc, r != 0, ys);
+      ysum[2 * g] = ys[0];
+      ysum[2 * g + 1] = ys[1];
+    }
+    float* pbuf = part + buf * (W * PART);
+    if constexpr (MODE == kModeY) {
+      // ysum[i] is this wave's sum for token 2i + r: part[buf][w][r][cl][i]
+      float* pp = pbuf + w * PART + (r * kCW + cl) * (kT / 2);
+      *reinterpret_cast<float4*>(pp) = make_float4(ysum[0], ysum[1], ysum[2], ysum[3]);
+      *reinterpret_cast<float4*>(pp + 4) = make_float4(ysum[4], ysum[5], ysum[6], ysum[7]);
     }
     if constexpr (MODE == kModeState) {
       float cs = 0.0f;
@@ -377,69 +439,66 @@ __global__ void __launch_bounds__(kCh * G) s6_scan_kernel(ScanArgs a) {
       for (int i = 0; i < kT; ++i) cs += dl[i];
       dsum += (double)cs;
     }
-    if constexpr (MODE == kModeY) __syncthreads();  // partial outputs of all waves are in LDS
 
-    // Stage chunk k+1 into the other buffer (its loads were issued one chunk
-    // ago; that buffer was last read before the previous barrier), then
-    // fetch chunk k+2.  Past the end of the segment the pieces are zeros.
-    write_chunk(buf ^ 1, t0 + kT);
-    issue_chunk(t0 + 2 * kT);
+    // Stage chunk k+1 into the other tile buffer (read last before the
+    // previous barrier; its loads were issued one chunk ago).
+    write_chunk(buf ^ 1, t0 + kT, nxt);
+    __syncthreads();  // partial outputs of chunk k and the tiles of chunk k+1 are complete
+    issue_chunk(t0 + 3 * kT, nxt);
 
     if constexpr (MODE == kModeY) {
-      const float* tz = tiles + (buf * NTS + 2) * TILE;
+      if (fin) {
+        float yo[TPL];
 #pragma unroll
-      for (int s = 0; s < QPL; ++s) {
-        const int q = tid + s * NTHR;
-        if (q < kCh * kT / 4) {
-          const int c = q >> 2;
-          const int tg = q & 3;
-          float4 acc = *reinterpret_cast<const float4*>(part + tsw(c, tg));
+        for (int i = 0; i < TPL; ++i) {
+          const int t = lg * TPL + i;  // token within the chunk
+          float acc = 0.0f;
 #pragma unroll
-          for (int gg = 1; gg < G; ++gg) {
-            const float4 v = *reinterpret_cast<const float4*>(part + gg * TILE + tsw(c, tg));
-            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-          }
-          const float4 xx = *reinterpret_cast<const float4*>(tx + tsw(c, tg));
-          acc.x = __builtin_fmaf(dsk[s], xx.x, acc.x);
-          acc.y = __builtin_fmaf(dsk[s], xx.y, acc.y);
-          acc.z = __builtin_fmaf(dsk[s], xx.z, acc.z);
-          acc.w = __builtin_fmaf(dsk[s], xx.w, acc.w);
-          if constexpr (GATE) {
-            const float4 zz = *reinterpret_cast<const float4*>(tz + tsw(c, tg));
-            acc.x *= silu(zz.x); acc.y *= silu(zz.y); acc.z *= silu(zz.z); acc.w *= silu(zz.w);
-          }
-          const int64_t t = t0 + 4 * tg;
-          if (c < rows_valid) {
-            float* dst = a.y + (row0 + c) * L + t;
-            if constexpr (VEC > 1) {
-              if (t < te) *reinterpret_cast<float4*>(dst) = acc;
-            } else {
-              if (t < te) dst[0] = acc.x;
-              if (t + 1 < te) dst[1] = acc.y;
-              if (t + 2 < te) dst[2] = acc.z;
-              if (t + 3 < te) dst[3] = acc.w;
-            }
+          for (int ww = 0; ww < W; ++ww) acc += pbuf[ww * PART + ((t & 1) * kCW + cl) * (kT / 2) + (t >> 1)];
+          acc = __builtin_fmaf(dsk, xfin[i], acc);
+          if constexpr (GATE) acc *= silu(zfin[i]);
+          yo[i] = acc;
+        }
+        const int64_t t = t0 + lg * TPL;
+        if (chv) {
+          float* dst = a.y + (b * D + d) * L + t;
+          if constexpr (VEC > 1 && TPL % 2 == 0) {
+#pragma unroll
+            for (int i = 0; i < TPL; i += 2)
+              if (t + i < te) *reinterpret_cast<float2*>(dst + i) = make_float2(yo[i], yo[i + 1]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < TPL; ++i)
+              if (t + i < te) dst[i] = yo[i];
           }
         }
       }
     }
-    __syncthreads();
+   };
+  for (int64_t k = 0; k < nchunks; k += 2) {
+    chunk(k, preB);
+    if (k + 1 < nchunks) chunk(k + 1, preA);
   }
 
   const bool write_h = a.hout && (!a.hout_last_only || seg == (int64_t)gridDim.z - 1);
   if (write_h && chv) {
     const int64_t off = a.hout_last_only ? 0 : seg * a.hout_stride;
 #pragma unroll
-    for (int j = 0; j < kNS; ++j) {
-      const int64_t n = (int64_t)w * kNS + j;
+    for (int j = 0; j < 2; ++j) {
+      const int64_t n = (int64_t)w * 4 + 2 * r + j;
       if (n < N) a.hout[off + (b * D + d) * N + n] = h[j];
     }
   }
   if constexpr (MODE == kModeState) {
-    if (a.sumdelta && chv && w == 0) a.sumdelta[seg * (int64_t)(gridDim.x / nblk) * D + b * D + d] = (float)dsum;
+    if (a.sumdelta && chv && w == 0 && r == 0)
+      a.sumdelta[seg * (int64_t)(gridDim.x / nblk) * D + b * D + d] = (float)dsum;
   }
 }
 
+// Fold segment aggregates into every segment's incoming state:
+// H_0 = h0 (or 0); H_{s+1} = exp(A * sum_delta_s) * H_s + S_s.
+// hin (S, batch*D*N) receives H_s for s < S; hlast (nullable) gets the state
+// after the last of the `nagg` aggregates.
 __global__ void s6_fold_carries(const float* __restrict__ A, const float* __restrict__ h0,
                                 const float* __restrict__ agg, const float* __restrict__ sumdelta,
                                 float* __restrict__ hin, float* __restrict__ hlast, int64_t batch,
@@ -578,31 +637,31 @@ int check_common(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int
   int64_t t;
   if (!mul_ok(batch, dim, &t) || !mul_ok(t, seqlen > 0 ? seqlen : 1, &t) || !mul_ok(t, 64, &t))
     return S6_ERR_SHAPE;  // element counts, with headroom for per-state buffers
-  if (batch * ((dim + kCh - 1) / kCh) > INT32_MAX) return S6_ERR_SHAPE;  // grid size
+  if (batch * ((dim + kCW - 1) / kCW) > INT32_MAX) return S6_ERR_SHAPE;  // grid size
   return S6_OK;
 }
 
 struct Plan {
-  int G;              // waves per workgroup (power of two, 4*G >= dstate)
+  int W;              // waves per workgroup (power of two, 4*W >= dstate)
   int64_t nblk;       // channel blocks per batch row
   int64_t segs;       // segments along L
   int64_t seg_len;    // tokens per segment, multiple of kT
-  bool vec;           // 16-byte staging and stores
+  bool vec;           // 16-byte staging and 8-byte stores
 };
 
-// Segments: when batch * channel blocks gives fewer than 512 workgroups,
-// cut L so that there are about 768 (three per CU), each segment holding at
-// least 4 chunks.
+// Segments: when batch * channel blocks gives fewer than 640 workgroups
+// (2.5 per CU), cut L so that there are about 1280 (five per CU), each
+// segment holding at least 4 chunks.
 Plan make_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, size_t esz,
                const void* const* ptrs, int nptr) {
   Plan p;
-  const int64_t need = (dstate + kNS - 1) / kNS;
-  p.G = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
-  p.nblk = (dim + kCh - 1) / kCh;
+  const int64_t need = (dstate + 3) / 4;
+  p.W = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+  p.nblk = (dim + kCW - 1) / kCW;
   const int64_t wgs = p.nblk * batch;
   int64_t segs = 1;
-  if (wgs < 512) {
-    segs = (768 + wgs - 1) / wgs;
+  if (wgs < 640) {
+    segs = (1280 + wgs - 1) / wgs;
     const int64_t max_segs = (seqlen + 4 * kT - 1) / (4 * kT);
     if (segs > max_segs) segs = max_segs;
     if (segs < 1) segs = 1;
@@ -621,52 +680,52 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, size_
   return p;
 }
 
-template <typename In, int VEC, bool GATE, int MODE, int G>
+template <typename In, int VEC, bool GATE, int MODE, int W>
 int launch_scan_t(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, hipStream_t st) {
-  constexpr int nts = (MODE == kModeY && GATE) ? 3 : 2;
-  size_t lds = (size_t)2 * nts * kCh * kP * sizeof(float);
-  if (MODE == kModeY) lds += (size_t)G * kCh * kP * sizeof(float);
-  lds += (size_t)2 * StageBC<In, VEC, G>::kFloats * sizeof(float);
+  size_t lds = (size_t)2 * 2 * kCW * kP * sizeof(float);                       // x, delta tiles
+  if (MODE == kModeY && GATE) lds += ((size_t)2 * kCW * kP * sizeof(In) + 15) / 16 * 16;  // gate tile
+  if (MODE == kModeY) lds += (size_t)2 * W * 2 * kCW * (kT / 2) * sizeof(float);  // partials
+  lds += (size_t)2 * StageBC<In, VEC, W>::kFloats * sizeof(float);              // B/C
   dim3 grid((unsigned)(nblk * batch), 1u, (unsigned)segs);
-  hipLaunchKernelGGL((s6_scan_kernel<In, VEC, GATE, MODE, G>), grid, dim3(kCh * G), lds, st, a);
+  hipLaunchKernelGGL((s6_scan_kernel<In, VEC, GATE, MODE, W>), grid, dim3(64 * W), lds, st, a);
   S6_HIP(hipGetLastError(), "s6_scan_kernel launch");
   return S6_OK;
 }
 
-template <typename In, int MODE, int G>
-int launch_scan_g(const ScanArgs& a, bool vec, bool gate, int64_t batch, int64_t nblk, int64_t segs,
+template <typename In, int MODE, int W>
+int launch_scan_w(const ScanArgs& a, bool vec, bool gate, int64_t batch, int64_t nblk, int64_t segs,
                   hipStream_t st) {
   constexpr int kV = 16 / sizeof(In);
   if constexpr (MODE == kModeY) {
-    if (vec && gate) return launch_scan_t<In, kV, true, MODE, G>(a, batch, nblk, segs, st);
-    if (vec) return launch_scan_t<In, kV, false, MODE, G>(a, batch, nblk, segs, st);
-    if (gate) return launch_scan_t<In, 1, true, MODE, G>(a, batch, nblk, segs, st);
-    return launch_scan_t<In, 1, false, MODE, G>(a, batch, nblk, segs, st);
+    if (vec && gate) return launch_scan_t<In, kV, true, MODE, W>(a, batch, nblk, segs, st);
+    if (vec) return launch_scan_t<In, kV, false, MODE, W>(a, batch, nblk, segs, st);
+    if (gate) return launch_scan_t<In, 1, true, MODE, W>(a, batch, nblk, segs, st);
+    return launch_scan_t<In, 1, false, MODE, W>(a, batch, nblk, segs, st);
   } else {
-    if (vec) return launch_scan_t<In, kV, false, MODE, G>(a, batch, nblk, segs, st);
-    return launch_scan_t<In, 1, false, MODE, G>(a, batch, nblk, segs, st);
+    if (vec) return launch_scan_t<In, kV, false, MODE, W>(a, batch, nblk, segs, st);
+    return launch_scan_t<In, 1, false, MODE, W>(a, batch, nblk, segs, st);
   }
 }
 
 template <typename In, int MODE>
-int launch_scan(const ScanArgs& a, int G, bool vec, bool gate, int64_t batch, int64_t nblk, int64_t segs,
+int launch_scan(const ScanArgs& a, int W, bool vec, bool gate, int64_t batch, int64_t nblk, int64_t segs,
                 hipStream_t st) {
-  switch (G) {
-    case 1: return launch_scan_g<In, MODE, 1>(a, vec, gate, batch, nblk, segs, st);
-    case 2: return launch_scan_g<In, MODE, 2>(a, vec, gate, batch, nblk, segs, st);
-    case 4: return launch_scan_g<In, MODE, 4>(a, vec, gate, batch, nblk, segs, st);
-    default: return launch_scan_g<In, MODE, 8>(a, vec, gate, batch, nblk, segs, st);
+  switch (W) {
+    case 1: return launch_scan_w<In, MODE, 1>(a, vec, gate, batch, nblk, segs, st);
+    case 2: return launch_scan_w<In, MODE, 2>(a, vec, gate, batch, nblk, segs, st);
+    case 4: return launch_scan_w<In, MODE, 4>(a, vec, gate, batch, nblk, segs, st);
+    default: return launch_scan_w<In, MODE, 8>(a, vec, gate, batch, nblk, segs, st);
   }
 }
 
 int launch_scan_any(int in_dtype, int mode, const ScanArgs& a, const Plan& p, bool gate, int64_t batch,
                     int64_t segs, hipStream_t st) {
   if (in_dtype == S6_BF16) {
-    return mode == kModeY ? launch_scan<uint16_t, kModeY>(a, p.G, p.vec, gate, batch, p.nblk, segs, st)
-                          : launch_scan<uint16_t, kModeState>(a, p.G, p.vec, gate, batch, p.nblk, segs, st);
+    return mode == kModeY ? launch_scan<uint16_t, kModeY>(a, p.W, p.vec, gate, batch, p.nblk, segs, st)
+                          : launch_scan<uint16_t, kModeState>(a, p.W, p.vec, gate, batch, p.nblk, segs, st);
   }
-  return mode == kModeY ? launch_scan<float, kModeY>(a, p.G, p.vec, gate, batch, p.nblk, segs, st)
-                        : launch_scan<float, kModeState>(a, p.G, p.vec, gate, batch, p.nblk, segs, st);
+  return mode == kModeY ? launch_scan<float, kModeY>(a, p.W, p.vec, gate, batch, p.nblk, segs, st)
+                        : launch_scan<float, kModeState>(a, p.W, p.vec, gate, batch, p.nblk, segs, st);
 }
 
 // Shared implementation of s6_scan_fwd (want_y) and s6_last_state.
