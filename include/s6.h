@@ -50,10 +50,11 @@
  *     before any HIP call, so a rejected call has no side effect.  Values are
  *     not checked: NaN/Inf propagate.  Accuracy is specified for A <= 0 and
  *     delta >= 0 (decaying states).
- *   Memory: s6_scan_fwd and s6_last_state take temporary device memory
- *     (packed B/C and, for few long rows, per-segment carries) from the
- *     stream-ordered allocator (hipMallocAsync) and release it on the same
- *     stream before returning.  s6_state_update allocates nothing.
+ *   Memory: when there are too few (batch, channel) blocks to fill the GPU
+ *     (few long rows), s6_scan_fwd and s6_last_state split the sequence into
+ *     segments and take the per-segment carries from the stream-ordered
+ *     allocator (hipMallocAsync), releasing them on the same stream before
+ *     returning; otherwise, and in s6_state_update, nothing is allocated.
  */
 #ifndef S6_H_
 #define S6_H_
