@@ -22,6 +22,35 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "selective_state_space_63_amd", "csrc", "s6.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "s6_scan_kernel_m3b_traffic.md")
+
+
+def source_digest(path=KERNEL_SRC):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(path=TRAFFIC_FILE):
+    """HBM bytes per scan launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the factor a plain copy of known
+    size gives), or None when the summary is missing or was taken on a
+    different kernel source than the one built now."""
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != source_digest():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def scan_bytes(w, in_bytes, h0=False, h_last=True):
@@ -61,18 +90,20 @@ def bench_scan(w, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    stream = torch.cuda.current_stream()  # the library launches on this stream
+    # One event between consecutive steps, on the stream the library launches
+    # on (torch's current stream): per-step times without host round trips.
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
+    ev[0].record(stream)
+    for i in range(steps):
         step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / steps
-    return inp, ms, wall
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    ms = ev[0].elapsed_time(ev[steps]) / steps
+    return inp, {"mean": ms, "median": per[len(per) // 2], "min": per[0]}, wall
 
 
 def bench_decode(steps_total, warmup):
@@ -116,9 +147,11 @@ def bench_decode(steps_total, warmup):
     }
 
 
-def cpu_baseline(w, inp, budget_s=6.0):
-    """The fp64 oracle on whole batch rows of the same inputs, one row at a
-    time until `budget_s` of wall time is spent (at least one row)."""
+def cpu_baseline(w, inp, budget_s=10.0):
+    """The fp64 oracle (as it stands, OpenMP over channels) on whole batch
+    rows of the same inputs, cycling over the rows until `budget_s` of oracle
+    time is spent (at least one row).  The inputs are copied to the host
+    outside the timed region."""
     import numpy as np
     import torch
     from oracle.oracle import Oracle
@@ -129,26 +162,80 @@ def cpu_baseline(w, inp, budget_s=6.0):
 
     A = h64(inp["A"])
     Dk = h64(inp["Dskip"])
+    rows_in = {}
     done_tc = 0
     spent = 0.0
     rows = 0
-    for b in range(w.batch):
-        args = dict(x=h64(inp["x"][b:b + 1]), delta=h64(inp["delta"][b:b + 1]), A=A,
-                    Bm=h64(inp["Bm"][b:b + 1]), Cm=h64(inp["Cm"][b:b + 1]), Dskip=Dk,
-                    z=h64(inp["z"][b:b + 1]))
+    while spent < budget_s or rows == 0:
+        b = rows % w.batch
+        if b not in rows_in:
+            rows_in[b] = dict(x=h64(inp["x"][b:b + 1]), delta=h64(inp["delta"][b:b + 1]), A=A,
+                              Bm=h64(inp["Bm"][b:b + 1]), Cm=h64(inp["Cm"][b:b + 1]), Dskip=Dk,
+                              z=h64(inp["z"][b:b + 1]))
         t0 = time.perf_counter()
-        o.scan(**args)
+        o.scan(**rows_in[b])
         spent += time.perf_counter() - t0
         done_tc += w.dim * w.seqlen
         rows += 1
-        if spent >= budget_s:
-            break
-    frac = rows / w.batch
-    gbs = scan_bytes(w, 2) * frac / spent / 1e9
+    gbs = scan_bytes(w, 2) * (rows / w.batch) / spent / 1e9
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": gbs, "unit": "GB/s", "cores": o.num_threads(), "kind": "oracle",
-            "sample": f"{rows} of {w.batch} batch rows (all {w.dim} channels x {w.seqlen} tokens each), "
-                      f"{spent:.2f} s wall; {done_tc / spent:.3e} token-channels/s",
+            "sample": f"{rows} batch rows of the same workload ({w.dim} channels x {w.seqlen} tokens each, "
+                      f"cycling over its {w.batch} rows), {spent:.2f} s of oracle time on {cpu}",
             "token_channels_per_s": done_tc / spent}
+
+
+def cpu_decode_baseline(w, budget_s=3.0):
+    """The oracle's single-token step (fp64) on the decode workload's shape,
+    repeated until `budget_s` is spent: state-element updates per second."""
+    import numpy as np
+    from oracle.oracle import Oracle
+    o = Oracle()
+    rng = np.random.default_rng(0)
+    B, D, N = w.batch, w.dim, w.dstate
+    A = -np.tile(np.arange(1, N + 1, dtype=np.float64), (D, 1))
+    h = np.zeros((B, D, N))
+    H = np.zeros((B, D, N))
+    args = dict(x=rng.standard_normal((B, D)), delta=np.full((B, D), 0.01), A=A,
+                Bm=rng.standard_normal((B, N)), Cm=rng.standard_normal((B, N)),
+                Dskip=rng.standard_normal(D), z=rng.standard_normal((B, D)))
+    steps = 0
+    spent = 0.0
+    while spent < budget_s or steps == 0:
+        t0 = time.perf_counter()
+        o.step(h, H, **args)
+        spent += time.perf_counter() - t0
+        steps += 1
+    return {"state_updates_per_s": B * D * N * steps / spent, "steps": steps, "seconds": round(spent, 2),
+            "cores": o.num_threads(), "kind": "oracle"}
+
+
+def copy_probe(mib, steps):
+    """A plain device copy (elementwise negation, read N bytes + write N
+    bytes) for calibrating the HBM byte counters: prints its size and time."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        torch.neg(src, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    byts = 2 * n * 4
+    print(json.dumps({"copy_probe": {"bytes_read": n * 4, "bytes_written": n * 4, "ms": round(ms, 4),
+                                     "GBps": round(byts / (ms * 1e-3) / 1e9, 1)}}), flush=True)
 
 
 def main():
@@ -160,6 +247,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (byte-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the scan has no cross-GPU step); got --gpus {args.gpus}",
@@ -169,15 +258,20 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, args.steps)
+        return
     from selective_state_space_63_amd import s6, synth
     s6.load_library()
     w = synth.WORKLOADS[args.workload]
     in_bytes = 2 if w.dtype == synth.BF16 else 4
     print(f"[bench] scan {w.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
-    inp, ms, wall = bench_scan(w, args.steps, args.warmup)
+    inp, tm, wall = bench_scan(w, args.steps, args.warmup)
+    ms = tm["mean"]
     byts = scan_bytes(w, in_bytes, h_last=True)
     gbs = byts / (ms * 1e-3) / 1e9
     tc = w.batch * w.dim * w.seqlen
+    traffic = measured_traffic() if w.name == synth.WORKLOADS["m3b"].name else None
     out = {
         "metric": "selective-scan fwd GB/s and % of HBM peak; decode state-updates/s",
         "value": round(gbs, 1),
@@ -196,8 +290,11 @@ def main():
                    "algorithmic_bytes": byts},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "token_channels_per_s": tc / (ms * 1e-3),
+        "step_ms": {"mean": round(ms, 4), "median": round(tm["median"], 4), "min": round(tm["min"], 4)},
+        # one s6_scan_fwd = one launch of the scan kernel on this workload, so
+        # the per-launch duration is the per-step time measured on its stream
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
     if not args.no_decode:
         print("[bench] decode", file=sys.stderr, flush=True)
@@ -205,6 +302,8 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inp)
+        if "decode" in out:
+            out["decode"]["cpu_baseline"] = cpu_decode_baseline(synth.WORKLOADS["decode"])
     print(json.dumps(out), flush=True)
 
 
