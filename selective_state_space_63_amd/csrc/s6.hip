@@ -106,120 +106,40 @@ struct ScanArgs {
   int64_t hout_last_only; // 1: only the last segment writes hout (at offset 0)
 };
 
-// One chunk of a (rows, L) tensor for the kCW channels of a workgroup: kCW
-// rows x kT tokens, cut into pieces of VEC elements (16 bytes, or single
-// elements when VEC == 1).
-template <typename In, int VEC>
-struct Stage {
-  static constexpr int kPieces = kCW * (kT / VEC);
+// One chunk of kT tokens of the kCW channel rows of x, delta (and z) and of
+// the 4W state rows of B (and C), cut into pieces of VEC elements (16 bytes;
+// single elements when VEC == 1).  Piece order: tensor, row, piece within
+// the row, so adjacent threads take adjacent pieces of a row.  A load window
+// is WIN consecutive chunks: a thread loads the same piece of each of them
+// back to back, so together they cover runs of WIN * 16 tokens of a row.
+template <typename In, int VEC, int W, int NTS, int NBC>
+struct ChunkPieces {
+  static constexpr int PPC = kT / VEC;            // pieces per row
+  static constexpr int kTens = NTS * kCW * PPC;   // x, delta (, z) pieces
+  static constexpr int kRowsBC = 4 * W;           // state rows per B/C tensor
+  static constexpr int kTotal = kTens + NBC * kRowsBC * PPC;
   using Raw = typename std::conditional<VEC == 1, In, u32x4>::type;
-
-  __device__ __forceinline__ static bool valid(int p, int64_t rows_valid, int64_t t0, int64_t tend) {
-    const int c = p / (kT / VEC);
-    const int v = p - c * (kT / VEC);
-    return c < rows_valid && t0 + v * VEC < tend;
-  }
-
-  // Unconditional load (a piece outside the tensor reads element 0 instead,
-  // and is replaced by zeros in store()): a conditional load would make the
-  // compiler wait for it at once and defeat the prefetch.
-  __device__ __forceinline__ static Raw load(gptr<In> src, int p, int64_t row0, int64_t rows_valid,
-                                             int64_t L, int64_t t0, int64_t tend) {
-    const int c = p / (kT / VEC);
-    const int v = p - c * (kT / VEC);
-    const int64_t idx = valid(p, rows_valid, t0, tend) ? (row0 + c) * L + t0 + v * VEC : 0;
-    if constexpr (VEC == 1) return src[idx];
-    else return *reinterpret_cast<gptr<u32x4>>(src + idx);
-  }
-
-  // Same layout, values kept in the input type (the gate tile).
-  __device__ __forceinline__ static void store_raw(In* __restrict__ tile, int p, const Raw& r, bool ok) {
-    const int c = p / (kT / VEC);
-    const int v = p - c * (kT / VEC);
-    if constexpr (VEC == 1) {
-      tile[tsw(c, v >> 2) + (v & 3)] = ok ? r : In(0);
-    } else {
-      const In* e = reinterpret_cast<const In*>(&r);
-#pragma unroll
-      for (int k = 0; k < VEC; k += 4) {
-        In* dst = tile + tsw(c, (v * VEC + k) >> 2);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) dst[m] = ok ? e[k + m] : In(0);
-      }
-    }
-  }
-
-  __device__ __forceinline__ static void store(float* __restrict__ tile, int p, const Raw& r, bool ok) {
-    const int c = p / (kT / VEC);
-    const int v = p - c * (kT / VEC);
-    if constexpr (VEC == 1) {
-      tile[tsw(c, v >> 2) + (v & 3)] = ok ? to_f32(r) : 0.0f;
-    } else {
-      const In* e = reinterpret_cast<const In*>(&r);
-#pragma unroll
-      for (int k = 0; k < VEC; k += 4)
-        *reinterpret_cast<float4*>(tile + tsw(c, (v * VEC + k) >> 2)) =
-            ok ? make_float4(to_f32(e[k]), to_f32(e[k + 1]), to_f32(e[k + 2]), to_f32(e[k + 3]))
-               : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
 };
 
-// B and C of one chunk: per tensor 4*W state rows (states beyond N are zero)
-// of kT tokens, cut into VEC-element pieces.  In LDS they are laid out as
-// the DPP operands want them: for token group g (4 tokens), wave w and row
-// parity r (state pair 4w + 2r, 4w + 2r + 1), 16 slots: B of token k, state
-// pair member j at slot 2k + j, C at slot 8 + 2k + j.
-template <typename In, int VEC, int W>
-struct StageBC {
-  static constexpr int kPiecesT = 4 * W * (kT / VEC);  // per tensor
-  static constexpr int kPieces = 2 * kPiecesT;
-  static constexpr int kFloats = (kT / 4) * W * 2 * 16;  // LDS floats per chunk
-  using Raw = typename std::conditional<VEC == 1, In, u32x4>::type;
-
-  __device__ __forceinline__ static bool valid(int p, int64_t N, int64_t t0, int64_t tend) {
-    const int q = p % kPiecesT;
-    const int n = q / (kT / VEC);
-    const int v = q - n * (kT / VEC);
-    return n < N && t0 + v * VEC < tend;
-  }
-
-  __device__ __forceinline__ static Raw load(gptr<In> Bm, gptr<In> Cm, int p, int64_t b, int64_t N,
-                                             int64_t L, int64_t t0, int64_t tend) {
-    const int q = p % kPiecesT;
-    const int n = q / (kT / VEC);
-    const int v = q - n * (kT / VEC);
-    gptr<In> M = (p < kPiecesT) ? Bm : Cm;
-    const int64_t idx = valid(p, N, t0, tend) ? (b * N + n) * L + t0 + v * VEC : 0;
-    if constexpr (VEC == 1) return M[idx];
-    else return *reinterpret_cast<gptr<u32x4>>(M + idx);
-  }
-
-  // LDS position of slot x of (group g, wave w, row parity r).  The slot is
-  // XORed with a (g, w)-dependent mask so that the scattered writes of one
-  // instruction fall on distinct banks; readers apply the same mask, so
-  // lane x still receives slot x.
+// B and C of one chunk in LDS, laid out as the DPP operands want them: for
+// token group g (4 tokens), wave w and row parity r (state pair 4w + 2r,
+// 4w + 2r + 1), a block of 16 slots read by the 16 lanes of the row: B of
+// pair member m, token k at slot 4m + k; C at slot 8 + 4m + k.  The four
+// 4-slot quarters of a block are permuted by XOR with f(g, w) so that the
+// 16-byte writes of one instruction spread over the banks; readers apply
+// the same permutation, so lane x of a row still receives slot x.  States
+// beyond N stay zero.
+template <int W>
+struct BCLayout {
+  static constexpr int kFloats = (kT / 4) * W * 2 * 16;  // floats per chunk
+  __device__ __forceinline__ static int quarter(int g, int w, int q) { return q ^ (((g >> 1) ^ w) & 3); }
   __device__ __forceinline__ static int pos(int g, int w, int r, int x) {
-    return ((g * W + w) * 2 + r) * 16 + (x ^ (((w & 3) << 2) ^ (((g >> 1) & 1) << 1)));
+    return ((g * W + w) * 2 + r) * 16 + (quarter(g, w, x >> 2) << 2) + (x & 3);
   }
-  __device__ __forceinline__ static int slot(int tens, int n, int j) {
-    const int g = j >> 2, k = j & 3;
+  // first of the 4 slots of token group g for tensor tens (0 = B, 1 = C), state n
+  __device__ __forceinline__ static int group_pos(int tens, int n, int g) {
     const int w = n >> 2, r = (n >> 1) & 1, m = n & 1;
-    return pos(g, w, r, tens * 8 + 2 * k + m);
-  }
-
-  __device__ __forceinline__ static void store(float* __restrict__ bcs, int p, const Raw& r, bool ok) {
-    const int tens = p / kPiecesT;
-    const int q = p % kPiecesT;
-    const int n = q / (kT / VEC);
-    const int v = q - n * (kT / VEC);
-    if constexpr (VEC == 1) {
-      bcs[slot(tens, n, v)] = ok ? to_f32(r) : 0.0f;
-    } else {
-      const In* e = reinterpret_cast<const In*>(&r);
-#pragma unroll
-      for (int k = 0; k < VEC; ++k) bcs[slot(tens, n, v * VEC + k)] = ok ? to_f32(e[k]) : 0.0f;
-    }
+    return ((g * W + w) * 2 + r) * 16 + (quarter(g, w, tens * 2 + m) << 2);
   }
 };
 
@@ -227,14 +147,21 @@ struct StageBC {
 template <int J>
 __device__ __forceinline__ float mul_bc(float bc, float v) { return row_bcast<J>(bc) * v; }
 
-// Value of lane (l ^ 16) -- the other state pair of the same channel -- via
-// the LDS crossbar (ds_swizzle, bit mode, xor mask 16).
-__device__ __forceinline__ float swap_rows(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+// Adds the output terms of the two state pairs of a channel (rows 2i and
+// 2i+1 of the wave, same lane within the row) for two tokens at once:
+// v_permlane16_swap exchanges the odd rows of its first operand with the
+// even rows of its second, so with the even token's value in the first and
+// the odd token's in the second, the sum of the two results holds the even
+// token in even rows and the odd token in odd rows.
+__device__ __forceinline__ float pair_rows(float even_tok, float odd_tok) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, even_tok),
+                                                  __builtin_bit_cast(unsigned, odd_tok), false, false);
+  return __builtin_bit_cast(float, (unsigned)s[0]) + __builtin_bit_cast(float, (unsigned)s[1]);
 }
 
 // One group of 4 tokens for this lane's 2 states.  dl/xv: the lane's deltas
-// and inputs; bc: the row's B/C operand register.  All exponentials are
+// and inputs; bc: the row's B/C operand register (lane 4m + k: B of pair
+// member m for token k, lane 8 + 4m + k: C).  All exponentials are
 // issued first, then the input terms, the state chains and the output terms,
 // so every result is consumed well after it is produced.  On return
 // ys[0], ys[1] hold the channel's output sums over this wave's 4 states for
@@ -242,7 +169,7 @@ __device__ __forceinline__ float swap_rows(float v) {
 // state pairs of the channel are added across rows.
 template <int MODE>
 __device__ __forceinline__ void token_group(const float* dl, const float* xv, const float (&A2)[2],
-                                            float (&h)[2], float bc, bool odd_row, float (&ys)[2]) {
+                                            float (&h)[2], float bc, float (&ys)[2]) {
   float e[4][2], bx[4][2], u[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -251,10 +178,10 @@ __device__ __forceinline__ void token_group(const float* dl, const float* xv, co
   }
 #pragma unroll
   for (int t = 0; t < 4; ++t) u[t] = dl[t] * xv[t];
-  bx[0][0] = mul_bc<0>(bc, u[0]); bx[0][1] = mul_bc<1>(bc, u[0]);
-  bx[1][0] = mul_bc<2>(bc, u[1]); bx[1][1] = mul_bc<3>(bc, u[1]);
-  bx[2][0] = mul_bc<4>(bc, u[2]); bx[2][1] = mul_bc<5>(bc, u[2]);
-  bx[3][0] = mul_bc<6>(bc, u[3]); bx[3][1] = mul_bc<7>(bc, u[3]);
+  bx[0][0] = mul_bc<0>(bc, u[0]); bx[0][1] = mul_bc<4>(bc, u[0]);
+  bx[1][0] = mul_bc<1>(bc, u[1]); bx[1][1] = mul_bc<5>(bc, u[1]);
+  bx[2][0] = mul_bc<2>(bc, u[2]); bx[2][1] = mul_bc<6>(bc, u[2]);
+  bx[3][0] = mul_bc<3>(bc, u[3]); bx[3][1] = mul_bc<7>(bc, u[3]);
   float hs[4][2];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -265,36 +192,48 @@ __device__ __forceinline__ void token_group(const float* dl, const float* xv, co
   }
   if constexpr (MODE == kModeY) {
     float p[4];
-    p[0] = mul_bc<8>(bc, hs[0][0]) + mul_bc<9>(bc, hs[0][1]);
-    p[1] = mul_bc<10>(bc, hs[1][0]) + mul_bc<11>(bc, hs[1][1]);
-    p[2] = mul_bc<12>(bc, hs[2][0]) + mul_bc<13>(bc, hs[2][1]);
-    p[3] = mul_bc<14>(bc, hs[3][0]) + mul_bc<15>(bc, hs[3][1]);
-    // token pairs (0,1) and (2,3): even rows keep the first, odd rows the second
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const float send = odd_row ? p[2 * q] : p[2 * q + 1];
-      const float keep = odd_row ? p[2 * q + 1] : p[2 * q];
-      ys[q] = keep + swap_rows(send);
-    }
+    p[0] = mul_bc<8>(bc, hs[0][0]) + mul_bc<12>(bc, hs[0][1]);
+    p[1] = mul_bc<9>(bc, hs[1][0]) + mul_bc<13>(bc, hs[1][1]);
+    p[2] = mul_bc<10>(bc, hs[2][0]) + mul_bc<14>(bc, hs[2][1]);
+    p[3] = mul_bc<11>(bc, hs[3][0]) + mul_bc<15>(bc, hs[3][1]);
+    // token pairs (0,1) and (2,3): even rows get the first, odd rows the second
+    ys[0] = pair_rows(p[0], p[1]);
+    ys[1] = pair_rows(p[2], p[3]);
   }
 }
 
 // Workgroup = kCW channels of one batch row x W waves.  Lane l of wave w:
 // channel cl = (l >> 5) * 16 + (l & 15), states 4w + 2r and 4w + 2r + 1 with
-// r = (l >> 4) & 1 (the row parity).  The lane also finalises TPL = kT/(2W)
-// consecutive tokens of its own channel (lane group 2w + r); it takes their
-// x and z from the tiles into registers before the chunk's barrier, so one
-// barrier per chunk suffices (tiles and partial outputs are double-buffered).
-template <typename In, int VEC, bool GATE, int MODE, int W>
+// r = (l >> 4) & 1 (the row parity).  Per chunk of kT tokens the lane reads
+// its channel's deltas and inputs from LDS, runs the recurrence for its two
+// states and writes the wave's partial outputs to LDS; after the chunk's
+// single barrier every lane finalises TPL consecutive tokens of one channel
+// (sum of the W partials, skip term, gate) and stores them.
+//
+// Staging: loads of window j (WIN chunks) go to register set j % 2 two
+// windows ahead; chunk k + 1 is converted into the other LDS buffer during
+// chunk k, before the barrier.  Only the last, partial chunk of a sequence
+// is written with per-piece masking (delta = 0 past the end keeps the
+// state), and only a window that would cross the end of the rows clamps its
+// piece addresses.
+template <typename In, int VEC, bool GATE, int MODE, int W, int WIN>
 __global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
   constexpr int NTHR = 64 * W;
   constexpr int NTS = (MODE == kModeY && GATE) ? 3 : 2;  // staged tensors: x, delta (, z)
-  using S = Stage<In, VEC>;
-  using SB = StageBC<In, VEC, W>;
+  constexpr int NBC = MODE == kModeY ? 2 : 1;             // B (, C)
+  using CP = ChunkPieces<In, VEC, W, NTS, NBC>;
+  using Raw = typename CP::Raw;
+  using BCL = BCLayout<W>;
+  constexpr int WT = WIN * kT;                    // tokens per load window
+  constexpr int SLOTS = (CP::kTotal + NTHR - 1) / NTHR;
   constexpr int TILE = kCW * kP;                  // floats per tensor tile
   constexpr int PART = 2 * kCW * (kT / 2);        // partial floats per wave
-  constexpr int TPL = (kT / (2 * W)) > 0 ? kT / (2 * W) : 1;  // finalised tokens per lane
-  constexpr int LG = kT / TPL;                    // lane groups that finalise
+  // Finalisation: lane tid owns TPL consecutive tokens of channel fc; the
+  // LPR lanes of a channel are adjacent, so one store instruction writes
+  // whole 64-byte runs of y rows.
+  constexpr int TPL = kT * kCW / NTHR;            // finalised tokens per lane
+  constexpr int LPR = kT / TPL;                   // lanes per channel
+  static_assert(TPL >= 1 && kT % TPL == 0, "finalisation layout");
 
   extern __shared__ float4 lds4[];
   float* lds = reinterpret_cast<float*>(lds4);
@@ -302,15 +241,15 @@ __global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
   In* ztile = reinterpret_cast<In*>(tiles + 2 * 2 * TILE);    // [2][kCW][kP] gate input, input type
   constexpr int ZFL = (MODE == kModeY && GATE) ? (2 * TILE * (int)sizeof(In) + 15) / 16 * 4 : 0;
   float* part = tiles + 2 * 2 * TILE + ZFL;                   // [2][W][2][kCW][8]
-  float* bcs = part + (MODE == kModeY ? 2 * W * PART : 0);    // [2][SB::kFloats]
+  float* bcs = part + (MODE == kModeY ? 2 * W * PART : 0);    // [2][BCL::kFloats]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = (lane >> 4) & 1;
   const int cl = ((lane >> 5) << 4) | (lane & 15);          // channel within the block
-  const int lg = 2 * w + r;                                  // finalize lane group
-  const bool fin = lg < LG;
+  const int fc = tid / LPR;                                   // finalised channel within the block
+  const int ft = (tid % LPR) * TPL;                          // its first token within a chunk
   const int64_t D = a.D, L = a.L, N = a.N;
   const int64_t nblk = (D + kCW - 1) / kCW;
   const int64_t b = blockIdx.x / nblk;
@@ -323,6 +262,9 @@ __global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
   const int64_t te = (tb + a.seg_len < L) ? tb + a.seg_len : L;
   const int64_t row0 = b * D + d0;
   const int64_t nchunks = (te - tb + kT - 1) / kT;
+  const int64_t nwin = (te - tb + WT - 1) / WT;
+  const int64_t lastw = tb + (nwin > 0 ? nwin - 1 : 0) * WT;  // start of the last window
+  const bool part_chunk = ((te - tb) % kT) != 0;               // last chunk only partly valid
 
   gptr<In> src[3] = {(gptr<In>)a.x, (gptr<In>)a.delta, (gptr<In>)a.z};
   gptr<In> Bp = (gptr<In>)a.Bm;
@@ -336,62 +278,145 @@ __global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
     A2[j] = sv ? a.A[d * N + n] * kLog2e : 0.0f;
     h[j] = (sv && a.hinit) ? a.hinit[seg * a.hinit_stride + (b * D + d) * N + n] : 0.0f;
   }
-  const float dsk = (MODE == kModeY && a.Dskip && chv) ? a.Dskip[d] : 0.0f;
+  const bool fchv = d0 + fc < D;
+  const float dsk = (MODE == kModeY && a.Dskip && fchv) ? a.Dskip[d0 + fc] : 0.0f;
   double dsum = 0.0;
+
+  // This thread's pieces: slot s holds piece tid + s * NTHR of every chunk.
+  // Rows past the end of the block read the last valid row (their channels
+  // are never stored); B/C state rows >= N read state N-1 and are not
+  // written, so their LDS slots stay zero.
+  gptr<In> sptr[SLOTS];  // piece at token 0
+  int scol[SLOTS];       // first token of the piece within a chunk
+  int srow[SLOTS];       // row within its tensor (channel or state)
+  int skind[SLOTS];      // 0..NTS-1: x, delta, z; NTS + m: B (m = 0) or C (m = 1); -1: idle
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    int p = tid + s * NTHR;
+    const bool idle = p >= CP::kTotal;
+    if (idle) p = 0;  // idle slot: loads piece 0, never writes
+    if (p < CP::kTens) {
+      const int k = p / (kCW * CP::PPC);
+      const int q = p - k * (kCW * CP::PPC);
+      const int row = q / CP::PPC;
+      const int64_t rowc = row < rows_valid ? row : rows_valid - 1;
+      skind[s] = k;
+      srow[s] = row;
+      scol[s] = (q - row * CP::PPC) * VEC;
+      sptr[s] = src[k] + (row0 + rowc) * L + scol[s];
+    } else {
+      const int q = p - CP::kTens;
+      const int m = q / (CP::kRowsBC * CP::PPC);
+      const int q2 = q - m * (CP::kRowsBC * CP::PPC);
+      const int n = q2 / CP::PPC;
+      const int64_t nc = n < N ? n : N - 1;
+      skind[s] = NTS + m;
+      srow[s] = n;
+      scol[s] = (q2 - n * CP::PPC) * VEC;
+      sptr[s] = (m ? Cp : Bp) + (b * N + nc) * L + scol[s];
+    }
+    if (idle) skind[s] = -1;
+  }
+
+  // B/C slots of states >= N are never written: clear both buffers once.
+  if (N < 4 * W) {
+    for (int i = tid; i < 2 * BCL::kFloats; i += NTHR) bcs[i] = 0.0f;
+    __syncthreads();
+  }
   // Let the loads above (A, h0, D) complete here: otherwise their pending
   // state reaches the loop header and the first use of h inside the loop
   // would wait for every outstanding load, prefetches included.
   __builtin_amdgcn_s_waitcnt(0);
 
-  // Staging: one flat list of pieces -- NTS tile tensors of TP pieces each,
-  // then the B/C pieces.  Loads are unconditional (invalid pieces read
-  // element 0); only the LDS writes depend on the piece.
-  constexpr int TP = S::kPieces;
-  constexpr int TOTAL = NTS * TP + SB::kPieces;
-  constexpr int SLOTS = (TOTAL + NTHR - 1) / NTHR;
-  // Two register sets of loads in flight: chunk j goes to set j % 2, is
-  // issued two chunks ahead and written to LDS one chunk ahead of its use.
-  typename S::Raw preA[SLOTS], preB[SLOTS];
+  Raw pre[2][WIN][SLOTS];  // two windows in flight
 
-  auto issue_chunk = [&](int64_t t0, typename S::Raw (&pre)[SLOTS]) {
+  // Loads of the window starting at token t0w (clamped to the segment's last
+  // window: prefetches past the end repeat it and are never used).
+  auto issue = [&](int64_t t0w, Raw (&dst)[WIN][SLOTS]) {
+    t0w = t0w < lastw ? t0w : lastw;
+    if (t0w + WT <= L) {
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      const int p = tid + s * NTHR;
-      if (p < NTS * TP) {
-        const int k = p / TP;
-        pre[s] = S::load(src[k], p - k * TP, row0, rows_valid, L, t0, te);
-      } else {
-        const int q = p - NTS * TP;
-        pre[s] = SB::load(Bp, Cp, q < SB::kPieces ? q : 0, b, N, L, t0, te);
-      }
+      for (int hh = 0; hh < WIN; ++hh)
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+          dst[hh][s] = *reinterpret_cast<gptr<Raw>>(sptr[s] + (t0w + hh * kT));
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < WIN; ++hh)
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+          // past the end of the row: reread its last piece (masked when staged)
+          int64_t tp = t0w + hh * kT;
+          const int64_t lim = L - VEC - scol[s];
+          tp = tp < lim ? tp : lim;
+          dst[hh][s] = *reinterpret_cast<gptr<Raw>>(sptr[s] + tp);
+        }
     }
   };
-  auto write_chunk = [&](int buf, int64_t t0, typename S::Raw (&pre)[SLOTS]) {
+
+  // Convert the pieces of chunk c (in `src_`) into LDS buffer `buf`.  mask:
+  // zero the tokens at or past te.
+  auto stage = [&](int buf, int64_t c, const Raw (&src_)[SLOTS], bool mask) {
+    const int64_t t0c = tb + c * kT;
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
-      const int p = tid + s * NTHR;
-      if (p < NTS * TP) {
-        const int k = p / TP;
-        const int q = p - k * TP;
-        if (k < 2) S::store(tiles + (buf * 2 + k) * TILE, q, pre[s], S::valid(q, rows_valid, t0, te));
-        else S::store_raw(ztile + buf * TILE, q, pre[s], S::valid(q, rows_valid, t0, te));
-      } else if (p < TOTAL) {
-        const int q = p - NTS * TP;
-        SB::store(bcs + buf * SB::kFloats, q, pre[s], SB::valid(q, N, t0, te));
+      const int col = scol[s];
+      if (skind[s] < 0) continue;
+      const bool ok = !mask || t0c + col < te;
+      const In* e = reinterpret_cast<const In*>(&src_[s]);
+      if (skind[s] < 2) {
+        float* tile = tiles + (buf * 2 + skind[s]) * TILE;
+        if constexpr (VEC == 1) {
+          tile[tsw(srow[s], col >> 2) + (col & 3)] = ok ? to_f32(e[0]) : 0.0f;
+        } else {
+#pragma unroll
+          for (int k = 0; k < VEC; k += 4)
+            *reinterpret_cast<float4*>(tile + tsw(srow[s], (col + k) >> 2)) =
+                ok ? make_float4(to_f32(e[k]), to_f32(e[k + 1]), to_f32(e[k + 2]), to_f32(e[k + 3]))
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      } else if (skind[s] < NTS) {
+        In* zt = ztile + buf * TILE;
+        if constexpr (VEC == 1) {
+          zt[tsw(srow[s], col >> 2) + (col & 3)] = ok ? e[0] : In(0);
+        } else if constexpr (sizeof(In) == 2) {
+          // groups of 4 elements stay contiguous (8 bytes) in the swizzled tile
+          const u32x4 v = src_[s];
+          *reinterpret_cast<uint2*>(zt + tsw(srow[s], col >> 2)) = ok ? make_uint2(v.x, v.y) : make_uint2(0u, 0u);
+          *reinterpret_cast<uint2*>(zt + tsw(srow[s], (col + 4) >> 2)) = ok ? make_uint2(v.z, v.w) : make_uint2(0u, 0u);
+        } else {
+          const u32x4 zero = {0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(zt + tsw(srow[s], col >> 2)) = ok ? src_[s] : zero;
+        }
+      } else if (srow[s] < N) {
+        float* bt = bcs + buf * BCL::kFloats;
+        const int m = skind[s] - NTS;
+        if constexpr (VEC == 1) {
+          bt[BCL::group_pos(m, srow[s], col >> 2) + (col & 3)] = ok ? to_f32(e[0]) : 0.0f;
+        } else {
+#pragma unroll
+          for (int k = 0; k < VEC; k += 4)
+            *reinterpret_cast<float4*>(bt + BCL::group_pos(m, srow[s], (col + k) >> 2)) =
+                ok ? make_float4(to_f32(e[k]), to_f32(e[k + 1]), to_f32(e[k + 2]), to_f32(e[k + 3]))
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
     }
   };
 
   if (nchunks > 0) {
-    issue_chunk(tb, preA);
-    write_chunk(0, tb, preA);
-    issue_chunk(tb + kT, preB);
-    issue_chunk(tb + 2 * kT, preA);
+    issue(tb, pre[0]);
+    issue(tb + WT, pre[1]);
+    stage(0, 0, pre[0][0], part_chunk && nchunks == 1);
+    if constexpr (WIN == 1) issue(tb + 2 * WT, pre[0]);  // window 0 is fully staged: refill its set
   }
   __syncthreads();
 
-  // One chunk; `nxt` holds the loads of chunk k+1 and receives chunk k+3.
-  auto chunk = [&](int64_t k, typename S::Raw (&nxt)[SLOTS]) {
+  // Chunk k at position P = k % (2 WIN) of the two-window cycle.
+  auto chunk = [&](int64_t k, auto pos) {
+    constexpr int P = decltype(pos)::value;
+    constexpr int NP = (P + 1) % (2 * WIN);  // position of chunk k + 1
+    constexpr int SET = NP / WIN, HALF = NP % WIN;
     const int64_t t0 = tb + k * kT;
     const int buf = (int)(k & 1);
     const float* tx = tiles + (buf * 2 + 0) * TILE;
@@ -407,22 +432,22 @@ __global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
       xv[i] = xx.x; xv[i + 1] = xx.y; xv[i + 2] = xx.z; xv[i + 3] = xx.w;
     }
 
-    // x and z of the tokens this lane finalises (the tiles are overwritten
-    // before this chunk's finalisation can run)
+    // x and z of the tokens this lane finalises (buffer `buf` is restaged
+    // before this chunk's finalisation can run in every wave)
     float xfin[TPL], zfin[TPL];
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
-      const int t = (fin ? lg * TPL : 0) + i;
-      xfin[i] = tx[tsw(cl, t >> 2) + (t & 3)];
-      zfin[i] = (MODE == kModeY && GATE) ? to_f32(ztile[buf * TILE + tsw(cl, t >> 2) + (t & 3)]) : 0.0f;
+      const int t = ft + i;
+      xfin[i] = tx[tsw(fc, t >> 2) + (t & 3)];
+      zfin[i] = (MODE == kModeY && GATE) ? to_f32(ztile[buf * TILE + tsw(fc, t >> 2) + (t & 3)]) : 0.0f;
     }
 
     float ysum[kT / 2];
 #pragma unroll
     for (int g = 0; g < kT / 4; ++g) {
-      const float bc = bcs[buf * SB::kFloats + SB::pos(g, w, r, lane & 15)];
+      const float bc = bcs[buf * BCL::kFloats + BCL::pos(g, w, r, lane & 15)];
       float ys[2];
-      token_group<MODE>(dl + 4 * g, xv + 4 * g, A2, h, bc, r != 0, ys);
+      token_group<MODE>(dl + 4 * g, xv + 4 * g, A2, h, bc, ys);
       ysum[2 * g] = ys[0];
       ysum[2 * g + 1] = ys[1];
     }
@@ -440,44 +465,54 @@ __global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
       dsum += (double)cs;
     }
 
-    // Stage chunk k+1 into the other tile buffer (read last before the
-    // previous barrier; its loads were issued one chunk ago).
-    write_chunk(buf ^ 1, t0 + kT, nxt);
-    __syncthreads();  // partial outputs of chunk k and the tiles of chunk k+1 are complete
-    issue_chunk(t0 + 3 * kT, nxt);
+    // Stage chunk k + 1 into the other buffer (read last before the previous
+    // barrier).  The register set it came from is free once its window's
+    // last chunk is staged: refill it with the window two ahead.
+    if (k + 1 < nchunks) stage(buf ^ 1, k + 1, pre[SET][HALF], part_chunk && k + 2 == nchunks);
+    __syncthreads();  // partial outputs of chunk k and the tiles of chunk k + 1 are complete
+    if constexpr (HALF == WIN - 1) issue(tb + ((k + 1) / WIN + 2) * WT, pre[SET]);
 
     if constexpr (MODE == kModeY) {
-      if (fin) {
-        float yo[TPL];
+      float yo[TPL];
 #pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-          const int t = lg * TPL + i;  // token within the chunk
-          float acc = 0.0f;
+      for (int i = 0; i < TPL; ++i) {
+        const int t = ft + i;  // token within the chunk
+        float acc = 0.0f;
 #pragma unroll
-          for (int ww = 0; ww < W; ++ww) acc += pbuf[ww * PART + ((t & 1) * kCW + cl) * (kT / 2) + (t >> 1)];
-          acc = __builtin_fmaf(dsk, xfin[i], acc);
-          if constexpr (GATE) acc *= silu(zfin[i]);
-          yo[i] = acc;
-        }
-        const int64_t t = t0 + lg * TPL;
-        if (chv) {
-          float* dst = a.y + (b * D + d) * L + t;
-          if constexpr (VEC > 1 && TPL % 2 == 0) {
+        for (int ww = 0; ww < W; ++ww) acc += pbuf[ww * PART + ((t & 1) * kCW + fc) * (kT / 2) + (t >> 1)];
+        acc = __builtin_fmaf(dsk, xfin[i], acc);
+        if constexpr (GATE) acc *= silu(zfin[i]);
+        yo[i] = acc;
+      }
+      const int64_t t = t0 + ft;
+      if (fchv) {
+        float* dst = a.y + (row0 + fc) * L + t;
+        // Vector path: L is a multiple of 8 (4 for fp32 input) and y is
+        // 16-byte aligned, so runs of 2 (or 4) tokens are all valid or all
+        // past the end, and aligned.
+        if constexpr (VEC > 1 && TPL % 4 == 0) {
 #pragma unroll
-            for (int i = 0; i < TPL; i += 2)
-              if (t + i < te) *reinterpret_cast<float2*>(dst + i) = make_float2(yo[i], yo[i + 1]);
-          } else {
+          for (int i = 0; i < TPL; i += 4)
+            if (t + i < te) *reinterpret_cast<float4*>(dst + i) = make_float4(yo[i], yo[i + 1], yo[i + 2], yo[i + 3]);
+        } else if constexpr (VEC > 1 && TPL % 2 == 0) {
 #pragma unroll
-            for (int i = 0; i < TPL; ++i)
-              if (t + i < te) dst[i] = yo[i];
-          }
+          for (int i = 0; i < TPL; i += 2)
+            if (t + i < te) *reinterpret_cast<float2*>(dst + i) = make_float2(yo[i], yo[i + 1]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < TPL; ++i)
+            if (t + i < te) dst[i] = yo[i];
         }
       }
     }
-   };
-  for (int64_t k = 0; k < nchunks; k += 2) {
-    chunk(k, preB);
-    if (k + 1 < nchunks) chunk(k + 1, preA);
+  };
+  for (int64_t k = 0; k < nchunks; k += 2 * WIN) {
+    chunk(k, std::integral_constant<int, 0>{});
+    if (k + 1 < nchunks) chunk(k + 1, std::integral_constant<int, 1>{});
+    if constexpr (WIN == 2) {
+      if (k + 2 < nchunks) chunk(k + 2, std::integral_constant<int, 2>{});
+      if (k + 3 < nchunks) chunk(k + 3, std::integral_constant<int, 3>{});
+    }
   }
 
   const bool write_h = a.hout && (!a.hout_last_only || seg == (int64_t)gridDim.z - 1);
@@ -682,12 +717,15 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, size_
 
 template <typename In, int VEC, bool GATE, int MODE, int W>
 int launch_scan_t(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, hipStream_t st) {
+  // 64-byte row runs per load: two chunks per window for bf16 vectors with
+  // enough threads to hold them, one chunk otherwise.
+  constexpr int WIN = (sizeof(In) == 2 && VEC > 1 && W >= 4) ? 2 : 1;
   size_t lds = (size_t)2 * 2 * kCW * kP * sizeof(float);                       // x, delta tiles
   if (MODE == kModeY && GATE) lds += ((size_t)2 * kCW * kP * sizeof(In) + 15) / 16 * 16;  // gate tile
   if (MODE == kModeY) lds += (size_t)2 * W * 2 * kCW * (kT / 2) * sizeof(float);  // partials
-  lds += (size_t)2 * StageBC<In, VEC, W>::kFloats * sizeof(float);              // B/C
+  lds += (size_t)2 * BCLayout<W>::kFloats * sizeof(float);                     // B/C
   dim3 grid((unsigned)(nblk * batch), 1u, (unsigned)segs);
-  hipLaunchKernelGGL((s6_scan_kernel<In, VEC, GATE, MODE, W>), grid, dim3(64 * W), lds, st, a);
+  hipLaunchKernelGGL((s6_scan_kernel<In, VEC, GATE, MODE, W, WIN>), grid, dim3(64 * W), lds, st, a);
   S6_HIP(hipGetLastError(), "s6_scan_kernel launch");
   return S6_OK;
 }
@@ -759,8 +797,8 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
     return S6_OK;
   }
 
-  const void* vecptrs[] = {x, delta, z, (const void*)y};
-  const Plan p = make_plan(batch, dim, seqlen, dstate, esz, vecptrs, want_y ? 4 : 2);
+  const void* vecptrs[] = {x, delta, Bm, Cm, z, (const void*)y};
+  const Plan p = make_plan(batch, dim, seqlen, dstate, esz, vecptrs, 6);
   const bool gate = want_y && z != nullptr;
   const int64_t S = p.segs;
 

@@ -65,6 +65,9 @@ SMALL = [
     (2, 40, 32, 48, synth.BF16, True),      # largest dstate
     (1, 200, 16, 4097, synth.BF16, True),   # segments + ragged tail + scalar path
     (1, 128, 8, 1536, synth.F32, False),    # segments, fp32 vector path
+    (2, 96, 16, 40, synth.BF16, True),      # vector path, last load window crosses the end
+    (1, 32, 16, 8, synth.BF16, True),       # a single partial chunk
+    (2, 64, 12, 48, synth.BF16, False),     # odd chunk count; states 12..15 of the last wave unused
 ]
 
 
