@@ -143,9 +143,43 @@ struct BCLayout {
   }
 };
 
-// Product of v with lane J of this lane's 16-lane row (v_mul_f32_dpp).
-template <int J>
-__device__ __forceinline__ float mul_bc(float bc, float v) { return row_bcast<J>(bc) * v; }
+// The row-broadcast products of a token group, written out as DPP
+// instructions (lane J of the 16-lane row of bc as the first operand): the
+// compiler folds such broadcasts only sometimes, and never into a
+// multiply-add with a tied accumulator.  The leading s_nop gives the two wait
+// states a DPP read needs after a VALU write of its source register.
+//
+// Input terms: bx[t][m] = bc[lane 4m + t] * u[t].
+__device__ __forceinline__ void bcast_inputs(float bc, const float (&u)[4], float (&bx)[4][2]) {
+  asm("s_nop 1\n\t"
+      "v_mul_f32_dpp %0, %8, %9 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %8, %9 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %2, %8, %10 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %3, %8, %10 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %4, %8, %11 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %5, %8, %11 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %6, %8, %12 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %7, %8, %12 row_newbcast:7 row_mask:0xf bank_mask:0xf"
+      : "=&v"(bx[0][0]), "=&v"(bx[0][1]), "=&v"(bx[1][0]), "=&v"(bx[1][1]), "=&v"(bx[2][0]),
+        "=&v"(bx[2][1]), "=&v"(bx[3][0]), "=&v"(bx[3][1])
+      : "v"(bc), "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]));
+}
+
+// Output terms: p[t] = bc[lane 8 + t] * hs[t][0] + bc[lane 12 + t] * hs[t][1].
+__device__ __forceinline__ void bcast_outputs(float bc, const float (&hs)[4][2], float (&p)[4]) {
+  asm("s_nop 1\n\t"
+      "v_mul_f32_dpp %0, %4, %5 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %4, %7 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %2, %4, %9 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %3, %4, %11 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %4, %6 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %4, %8 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %4, %10 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %4, %12 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+      : "=&v"(p[0]), "=&v"(p[1]), "=&v"(p[2]), "=&v"(p[3])
+      : "v"(bc), "v"(hs[0][0]), "v"(hs[0][1]), "v"(hs[1][0]), "v"(hs[1][1]), "v"(hs[2][0]),
+        "v"(hs[2][1]), "v"(hs[3][0]), "v"(hs[3][1]));
+}
 
 // Adds the output terms of the two state pairs of a channel (rows 2i and
 // 2i+1 of the wave, same lane within the row) for two tokens at once:
@@ -178,10 +212,7 @@ __device__ __forceinline__ void token_group(const float* dl, const float* xv, co
   }
 #pragma unroll
   for (int t = 0; t < 4; ++t) u[t] = dl[t] * xv[t];
-  bx[0][0] = mul_bc<0>(bc, u[0]); bx[0][1] = mul_bc<4>(bc, u[0]);
-  bx[1][0] = mul_bc<1>(bc, u[1]); bx[1][1] = mul_bc<5>(bc, u[1]);
-  bx[2][0] = mul_bc<2>(bc, u[2]); bx[2][1] = mul_bc<6>(bc, u[2]);
-  bx[3][0] = mul_bc<3>(bc, u[3]); bx[3][1] = mul_bc<7>(bc, u[3]);
+  bcast_inputs(bc, u, bx);
   float hs[4][2];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -192,10 +223,7 @@ __device__ __forceinline__ void token_group(const float* dl, const float* xv, co
   }
   if constexpr (MODE == kModeY) {
     float p[4];
-    p[0] = mul_bc<8>(bc, hs[0][0]) + mul_bc<12>(bc, hs[0][1]);
-    p[1] = mul_bc<9>(bc, hs[1][0]) + mul_bc<13>(bc, hs[1][1]);
-    p[2] = mul_bc<10>(bc, hs[2][0]) + mul_bc<14>(bc, hs[2][1]);
-    p[3] = mul_bc<11>(bc, hs[3][0]) + mul_bc<15>(bc, hs[3][1]);
+    bcast_outputs(bc, hs, p);
     // token pairs (0,1) and (2,3): even rows get the first, odd rows the second
     ys[0] = pair_rows(p[0], p[1]);
     ys[1] = pair_rows(p[2], p[3]);
@@ -217,7 +245,8 @@ __device__ __forceinline__ void token_group(const float* dl, const float* xv, co
 // state), and only a window that would cross the end of the rows clamps its
 // piece addresses.
 template <typename In, int VEC, bool GATE, int MODE, int W, int WIN>
-__global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ? 5 : 1)))
+s6_scan_kernel(ScanArgs a) {
   constexpr int NTHR = 64 * W;
   constexpr int NTS = (MODE == kModeY && GATE) ? 3 : 2;  // staged tensors: x, delta (, z)
   constexpr int NBC = MODE == kModeY ? 2 : 1;             // B (, C)
@@ -265,6 +294,7 @@ __global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
   const int64_t nwin = (te - tb + WT - 1) / WT;
   const int64_t lastw = tb + (nwin > 0 ? nwin - 1 : 0) * WT;  // start of the last window
   const bool part_chunk = ((te - tb) % kT) != 0;               // last chunk only partly valid
+  const int64_t nplain = nchunks - (part_chunk ? 1 : 0);        // chunks staged without masking
 
   gptr<In> src[3] = {(gptr<In>)a.x, (gptr<In>)a.delta, (gptr<In>)a.z};
   gptr<In> Bp = (gptr<In>)a.Bm;
@@ -354,15 +384,16 @@ __global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
     }
   };
 
-  // Convert the pieces of chunk c (in `src_`) into LDS buffer `buf`.  mask:
-  // zero the tokens at or past te.
-  auto stage = [&](int buf, int64_t c, const Raw (&src_)[SLOTS], bool mask) {
+  // Convert the pieces of chunk c (in `src_`) into LDS buffer `buf`.  MASK:
+  // zero the tokens at or past te (only the last chunk can need it).
+  auto stage = [&](int buf, int64_t c, const Raw (&src_)[SLOTS], auto maskc) {
+    constexpr bool MASK = decltype(maskc)::value;
     const int64_t t0c = tb + c * kT;
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
       const int col = scol[s];
       if (skind[s] < 0) continue;
-      const bool ok = !mask || t0c + col < te;
+      const bool ok = !MASK || t0c + col < te;
       const In* e = reinterpret_cast<const In*>(&src_[s]);
       if (skind[s] < 2) {
         float* tile = tiles + (buf * 2 + skind[s]) * TILE;
@@ -407,14 +438,23 @@ __global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
   if (nchunks > 0) {
     issue(tb, pre[0]);
     issue(tb + WT, pre[1]);
-    stage(0, 0, pre[0][0], part_chunk && nchunks == 1);
+    if (nplain == 0) stage(0, 0, pre[0][0], std::true_type{});
+    else stage(0, 0, pre[0][0], std::false_type{});
     if constexpr (WIN == 1) issue(tb + 2 * WT, pre[0]);  // window 0 is fully staged: refill its set
   }
   __syncthreads();
 
   // Chunk k at position P = k % (2 WIN) of the two-window cycle.
+  // The loop runs whole cycles of 2 WIN chunks: chunks past the end of the
+  // segment are staged fully masked (delta = 0 leaves the state exactly
+  // unchanged) and store nothing.  So the loop body has no conditional loads,
+  // which would make the compiler's wait placement conservative across the
+  // loop back edge.
   auto chunk = [&](int64_t k, auto pos) {
     constexpr int P = decltype(pos)::value;
+    // keep the scheduler from interleaving consecutive chunks (it raises the
+    // register pressure past five waves per SIMD)
+    __builtin_amdgcn_sched_barrier(0);
     constexpr int NP = (P + 1) % (2 * WIN);  // position of chunk k + 1
     constexpr int SET = NP / WIN, HALF = NP % WIN;
     const int64_t t0 = tb + k * kT;
@@ -422,15 +462,6 @@ __global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
     const float* tx = tiles + (buf * 2 + 0) * TILE;
     const float* tdl = tiles + (buf * 2 + 1) * TILE;
 
-    // this lane's kT deltas and inputs
-    float dl[kT], xv[kT];
-#pragma unroll
-    for (int i = 0; i < kT; i += 4) {
-      const float4 dv = *reinterpret_cast<const float4*>(tdl + tsw(cl, i >> 2));
-      const float4 xx = *reinterpret_cast<const float4*>(tx + tsw(cl, i >> 2));
-      dl[i] = dv.x; dl[i + 1] = dv.y; dl[i + 2] = dv.z; dl[i + 3] = dv.w;
-      xv[i] = xx.x; xv[i + 1] = xx.y; xv[i + 2] = xx.z; xv[i + 3] = xx.w;
-    }
 
     // x and z of the tokens this lane finalises (buffer `buf` is restaged
     // before this chunk's finalisation can run in every wave)
@@ -442,15 +473,26 @@ __global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
       zfin[i] = (MODE == kModeY && GATE) ? to_f32(ztile[buf * TILE + tsw(fc, t >> 2) + (t & 3)]) : 0.0f;
     }
 
+    // the lane's deltas and inputs, one group of 4 tokens at a time
     float ysum[kT / 2];
+    float cs = 0.0f;
 #pragma unroll
     for (int g = 0; g < kT / 4; ++g) {
+      const float4 dv = *reinterpret_cast<const float4*>(tdl + tsw(cl, g));
+      const float4 xx = *reinterpret_cast<const float4*>(tx + tsw(cl, g));
+      const float dl[4] = {dv.x, dv.y, dv.z, dv.w};
+      const float xv[4] = {xx.x, xx.y, xx.z, xx.w};
       const float bc = bcs[buf * BCL::kFloats + BCL::pos(g, w, r, lane & 15)];
       float ys[2];
-      token_group<MODE>(dl + 4 * g, xv + 4 * g, A2, h, bc, ys);
+      token_group<MODE>(dl, xv, A2, h, bc, ys);
       ysum[2 * g] = ys[0];
       ysum[2 * g + 1] = ys[1];
+      if constexpr (MODE == kModeState) cs += (dl[0] + dl[1]) + (dl[2] + dl[3]);
     }
+    // The chunk's state updates complete here.  (Without output terms nothing
+    // else ties them to the chunk, and the compiler would sink them past the
+    // barriers, keeping every chunk's inputs live at once.)
+    asm volatile("" : "+v"(h[0]), "+v"(h[1]));
     float* pbuf = part + buf * (W * PART);
     if constexpr (MODE == kModeY) {
       // ysum[i] is this wave's sum for token 2i + r: part[buf][w][r][cl][i]
@@ -458,17 +500,13 @@ __global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
       *reinterpret_cast<float4*>(pp) = make_float4(ysum[0], ysum[1], ysum[2], ysum[3]);
       *reinterpret_cast<float4*>(pp + 4) = make_float4(ysum[4], ysum[5], ysum[6], ysum[7]);
     }
-    if constexpr (MODE == kModeState) {
-      float cs = 0.0f;
-#pragma unroll
-      for (int i = 0; i < kT; ++i) cs += dl[i];
-      dsum += (double)cs;
-    }
+    if constexpr (MODE == kModeState) dsum += (double)cs;
 
     // Stage chunk k + 1 into the other buffer (read last before the previous
     // barrier).  The register set it came from is free once its window's
     // last chunk is staged: refill it with the window two ahead.
-    if (k + 1 < nchunks) stage(buf ^ 1, k + 1, pre[SET][HALF], part_chunk && k + 2 == nchunks);
+    if (k + 1 < nplain) stage(buf ^ 1, k + 1, pre[SET][HALF], std::false_type{});
+    else stage(buf ^ 1, k + 1, pre[SET][HALF], std::true_type{});
     __syncthreads();  // partial outputs of chunk k and the tiles of chunk k + 1 are complete
     if constexpr (HALF == WIN - 1) issue(tb + ((k + 1) / WIN + 2) * WT, pre[SET]);
 
@@ -506,12 +544,16 @@ __global__ void __launch_bounds__(64 * W) s6_scan_kernel(ScanArgs a) {
       }
     }
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
   for (int64_t k = 0; k < nchunks; k += 2 * WIN) {
-    chunk(k, std::integral_constant<int, 0>{});
-    if (k + 1 < nchunks) chunk(k + 1, std::integral_constant<int, 1>{});
+    chunk(k, I0{});
+    chunk(k + 1, I1{});
     if constexpr (WIN == 2) {
-      if (k + 2 < nchunks) chunk(k + 2, std::integral_constant<int, 2>{});
-      if (k + 3 < nchunks) chunk(k + 3, std::integral_constant<int, 3>{});
+      chunk(k + 2, I2{});
+      chunk(k + 3, I3{});
     }
   }
 
