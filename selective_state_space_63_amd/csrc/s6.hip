@@ -619,10 +619,14 @@ struct StepArgs {
   int64_t batch, D, N;
 };
 
-// P lanes per channel, 4 states per lane.  V4: 16-byte state accesses
-// (N % 4 == 0 and h 16-byte aligned).
-template <typename In, bool GATE, int P, bool V4>
+// P lanes per channel, SPL states per lane (lane q: states q*SPL ...).
+// VEC: N == P * SPL and every row of h, A, B and C starts 16-byte aligned, so
+// all of them are read with 16-byte loads (h written back the same way).
+// The step's B and C rows are the same for every channel of a batch row and
+// stay in cache; h is streamed once in and once out.
+template <typename In, bool GATE, int P, int SPL, bool VEC>
 __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
+  static_assert(!VEC || (SPL * sizeof(In)) % 16 == 0, "16-byte rows of B and C");
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t ch = gid / P;
   const int q = (int)(gid % P);
@@ -636,46 +640,71 @@ __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
   const In* zp = static_cast<const In*>(a.z);
   const In* Bp = static_cast<const In*>(a.Bm);
   const In* Cp = static_cast<const In*>(a.Cm);
+  const int64_t n0 = (int64_t)q * SPL;
 
-  float hv[4] = {0.f, 0.f, 0.f, 0.f};
   float yp = 0.0f;
   float xt = 0.0f;
   if (valid) {
     const float dt = to_f32(dp[ch]);
     xt = to_f32(xp[ch]);
     const float u = dt * xt;
-    float* hrow = a.h + ch * N;
-    const int64_t n0 = (int64_t)q * 4;
-    if constexpr (V4) {
-      if (n0 < N) {
-        const float4 v = *reinterpret_cast<const float4*>(hrow + n0);
-        hv[0] = v.x; hv[1] = v.y; hv[2] = v.z; hv[3] = v.w;
+    float* hrow = a.h + ch * N + n0;
+    const float* arow = a.A + d * N + n0;
+    const In* brow = Bp + b * N + n0;
+    const In* crow = Cp + b * N + n0;
+    float hv[SPL], Av[SPL], Bv[SPL], Cv[SPL];
+    if constexpr (VEC) {
+#pragma unroll
+      for (int j = 0; j < SPL; j += 4) {
+        const float4 hh = *reinterpret_cast<const float4*>(hrow + j);
+        const float4 aa = *reinterpret_cast<const float4*>(arow + j);
+        hv[j] = hh.x; hv[j + 1] = hh.y; hv[j + 2] = hh.z; hv[j + 3] = hh.w;
+        Av[j] = aa.x; Av[j + 1] = aa.y; Av[j + 2] = aa.z; Av[j + 3] = aa.w;
+      }
+      constexpr int PER = 16 / (int)sizeof(In);  // elements per 16-byte load
+#pragma unroll
+      for (int j = 0; j < SPL; j += PER) {
+        const u32x4 bb = *reinterpret_cast<const u32x4*>(brow + j);
+        const u32x4 cc = *reinterpret_cast<const u32x4*>(crow + j);
+        const In* be = reinterpret_cast<const In*>(&bb);
+        const In* ce = reinterpret_cast<const In*>(&cc);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          Bv[j + k] = to_f32(be[k]);
+          Cv[j + k] = to_f32(ce[k]);
+        }
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n0 + j < N) hv[j] = hrow[n0 + j];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + j;
-      if (n < N) {
-        const float e = fast_exp2(dt * (a.A[d * N + n] * kLog2e));
-        hv[j] = __builtin_fmaf(e, hv[j], u * to_f32(Bp[b * N + n]));
-        yp = __builtin_fmaf(to_f32(Cp[b * N + n]), hv[j], yp);
+      for (int j = 0; j < SPL; ++j) {
+        const bool sv = n0 + j < N;
+        hv[j] = sv ? hrow[j] : 0.0f;
+        Av[j] = sv ? arow[j] : 0.0f;
+        Bv[j] = sv ? to_f32(brow[j]) : 0.0f;
+        Cv[j] = sv ? to_f32(crow[j]) : 0.0f;
       }
     }
-    if constexpr (V4) {
-      if (n0 < N) *reinterpret_cast<float4*>(hrow + n0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const float e = fast_exp2(dt * (Av[j] * kLog2e));
+      hv[j] = __builtin_fmaf(e, hv[j], u * Bv[j]);
+      yp = __builtin_fmaf(Cv[j], hv[j], yp);
+    }
+    if constexpr (VEC) {
+#pragma unroll
+      for (int j = 0; j < SPL; j += 4)
+        *reinterpret_cast<float4*>(hrow + j) = make_float4(hv[j], hv[j + 1], hv[j + 2], hv[j + 3]);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n0 + j < N) hrow[n0 + j] = hv[j];
+      for (int j = 0; j < SPL; ++j)
+        if (n0 + j < N) hrow[j] = hv[j];
     }
   }
   // reduce the P partial outputs of a channel (P consecutive lanes)
+  if constexpr (P > 1) {
 #pragma unroll
-  for (int off = P / 2; off > 0; off >>= 1) yp += __shfl_xor(yp, off, P);
+    for (int off = P / 2; off > 0; off >>= 1) yp += __shfl_xor(yp, off, P);
+  }
   if (valid && q == 0) {
     float yv = yp;
     if (a.Dskip) yv = __builtin_fmaf(a.Dskip[d], xt, yv);
@@ -901,25 +930,36 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
   return rc;
 }
 
-template <typename In, bool GATE, int P>
-int launch_step_t(const StepArgs& a, bool v4, hipStream_t st) {
+template <typename In, bool GATE, int P, int SPL>
+int launch_step_t(const StepArgs& a, bool vec, hipStream_t st) {
   const int64_t threads = a.batch * a.D * P;
   const int64_t blocks = (threads + 255) / 256;
-  if (v4)
-    hipLaunchKernelGGL((s6_step_kernel<In, GATE, P, true>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((s6_step_kernel<In, GATE, P, false>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  if constexpr ((SPL * sizeof(In)) % 16 == 0) {
+    if (vec) {
+      hipLaunchKernelGGL((s6_step_kernel<In, GATE, P, SPL, true>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+      S6_HIP(hipGetLastError(), "s6_step_kernel launch");
+      return S6_OK;
+    }
+  }
+  hipLaunchKernelGGL((s6_step_kernel<In, GATE, P, SPL, false>), dim3((unsigned)blocks), dim3(256), 0, st, a);
   S6_HIP(hipGetLastError(), "s6_step_kernel launch");
   return S6_OK;
 }
 
+// One lane per channel for dstate <= 16 (all states in registers, no
+// cross-lane reduction), two lanes for 17..32.
 template <typename In, bool GATE>
-int launch_step_g(const StepArgs& a, bool v4, hipStream_t st) {
-  const int64_t lanes = (a.N + 3) / 4;
-  if (lanes <= 1) return launch_step_t<In, GATE, 1>(a, v4, st);
-  if (lanes <= 2) return launch_step_t<In, GATE, 2>(a, v4, st);
-  if (lanes <= 4) return launch_step_t<In, GATE, 4>(a, v4, st);
-  return launch_step_t<In, GATE, 8>(a, v4, st);
+int launch_step_g(const StepArgs& a, hipStream_t st) {
+  const int64_t N = a.N;
+  const size_t esz = sizeof(In);
+  auto vec_ok = [&](int64_t P, int64_t SPL) {
+    return N == P * SPL && aligned(a.h, 16) && aligned(a.A, 16) && aligned(a.Bm, 16) && aligned(a.Cm, 16) &&
+           (N * (int64_t)esz) % 16 == 0 && (SPL * (int64_t)esz) % 16 == 0;
+  };
+  if (N <= 4) return launch_step_t<In, GATE, 1, 4>(a, vec_ok(1, 4), st);
+  if (N <= 8) return launch_step_t<In, GATE, 1, 8>(a, vec_ok(1, 8), st);
+  if (N <= 16) return launch_step_t<In, GATE, 1, 16>(a, vec_ok(1, 16), st);
+  return launch_step_t<In, GATE, 2, 16>(a, vec_ok(2, 16), st);
 }
 
 }  // namespace
@@ -973,11 +1013,10 @@ int s6_state_update(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, fl
   StepArgs a;
   a.h = h; a.x = x; a.delta = delta; a.z = z; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.y = y;
   a.batch = batch; a.D = dim; a.N = dstate;
-  const bool v4 = (dstate % 4 == 0) && aligned(h, 16);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_dtype == S6_BF16)
-    return z ? launch_step_g<uint16_t, true>(a, v4, st) : launch_step_g<uint16_t, false>(a, v4, st);
-  return z ? launch_step_g<float, true>(a, v4, st) : launch_step_g<float, false>(a, v4, st);
+    return z ? launch_step_g<uint16_t, true>(a, st) : launch_step_g<uint16_t, false>(a, st);
+  return z ? launch_step_g<float, true>(a, st) : launch_step_g<float, false>(a, st);
 }
 
 }  // extern "C"
