@@ -22,6 +22,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# VALU issue peak of MI355X without packed fp32: 256 CUs x 4 SIMDs x 16 lanes
+# x 2.4 GHz lane-operation slots per second.  A transcendental (v_exp_f32,
+# v_rcp_f32) takes two slots.
+VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 KERNEL_SRC = os.path.join(ROOT, "selective_state_space_63_amd", "csrc", "s6.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "s6_scan_kernel_m3b_traffic.md")
 
@@ -69,6 +73,16 @@ def scan_bytes(w, in_bytes, h0=False, h_last=True):
     return b
 
 
+def scan_valu_slots(w, skip=True):
+    """Algorithmic VALU lane-slots of one scan: per (token, channel, state)
+    the exponent argument (1), the exponential (2), the input term (1), the
+    state update (1) and the output term (1); per (token, channel) delta*x
+    (1), the skip term (1) and the SiLU gate (z*log2 e, exp, add, rcp, two
+    products: 8)."""
+    per = 6 * w.dstate + 1 + (1 if skip else 0) + (8 if w.gate else 0)
+    return w.batch * w.dim * w.seqlen * per
+
+
 def decode_step_bytes(batch, dim, N, in_bytes, gate=True):
     """One decode token: h read and written (fp32), x, delta (, z) in, y out
     (fp32) per channel; B, C per (batch, state); A and D once."""
@@ -76,10 +90,15 @@ def decode_step_bytes(batch, dim, N, in_bytes, gate=True):
     return batch * dim * per + 2 * batch * N * in_bytes + 4 * dim * N + 4 * dim
 
 
-def bench_scan(w, steps, warmup):
+def bench_scan(w, steps, warmup, flush=False):
+    """Times `steps` scans of workload w (after `warmup`).  flush: before each
+    timed scan, write a 512 MiB buffer so that no input is cache-resident,
+    and time each scan on its own."""
     import torch
     from selective_state_space_63_amd import s6, synth
     inp = synth.device_full(w)
+    if flush:
+        return inp, bench_scan_flushed(w, inp, steps, warmup), None
     y = torch.empty((w.batch, w.dim, w.seqlen), device="cuda", dtype=torch.float32)
     hl = torch.empty((w.batch, w.dim, w.dstate), device="cuda", dtype=torch.float32)
 
@@ -104,6 +123,38 @@ def bench_scan(w, steps, warmup):
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     ms = ev[0].elapsed_time(ev[steps]) / steps
     return inp, {"mean": ms, "median": per[len(per) // 2], "min": per[0]}, wall
+
+
+def bench_scan_flushed(w, inp, steps, warmup):
+    import torch
+    from selective_state_space_63_amd import s6
+    y = torch.empty((w.batch, w.dim, w.seqlen), device="cuda", dtype=torch.float32)
+    junk = torch.empty(512 << 20, device="cuda", dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    per = []
+    for i in range(warmup + steps):
+        junk.fill_(i & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        s6.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], D=inp["Dskip"], z=inp["z"], y=y)
+        e1.record(stream)
+        e1.synchronize()
+        if i >= warmup:
+            per.append(e0.elapsed_time(e1))
+    per.sort()
+    return {"mean": sum(per) / len(per), "median": per[len(per) // 2], "min": per[0]}
+
+
+def scan_line(name, w, tm, in_bytes, note, h_last):
+    byts = scan_bytes(w, in_bytes, h_last=h_last)
+    ms = tm["mean"]
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "ms_mean": round(ms, 4), "ms_median": round(tm["median"], 4),
+            "ms_min": round(tm["min"], 4), "GBps": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "token_channels_per_s": w.batch * w.dim * w.seqlen / (ms * 1e-3),
+            "valu_frac": round(scan_valu_slots(w) / (ms * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4),
+            "note": note}
 
 
 def bench_decode(steps_total, warmup):
@@ -139,10 +190,13 @@ def bench_decode(steps_total, warmup):
     ms = e0.elapsed_time(e1)
     upd = w.batch * w.dim * w.dstate * S
     byts = decode_step_bytes(w.batch, w.dim, w.dstate, 2) * S
+    gbs = byts / (ms * 1e-3) / 1e9
     return {
         "workload": w.name, "steps": S, "ms_total": round(ms, 3), "us_per_step": round(1e3 * ms / S, 2),
         "state_updates_per_s": upd / (ms * 1e-3), "token_steps_per_s": w.batch * S / (ms * 1e-3),
-        "effective_GBps": byts / (ms * 1e-3) / 1e9,
+        "effective_GBps": gbs,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)},
         "note": "plain launches, state resident in device memory (fits the 256 MB Infinity Cache)",
     }
 
@@ -247,6 +301,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the long-sequence and 130M-layer scan lines")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (byte-counter calibration)")
     args = ap.parse_args()
@@ -268,6 +324,8 @@ def main():
     print(f"[bench] scan {w.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
     inp, tm, wall = bench_scan(w, args.steps, args.warmup)
     ms = tm["mean"]
+    slots = scan_valu_slots(w)
+    tslots = slots / (ms * 1e-3) / 1e12
     byts = scan_bytes(w, in_bytes, h_last=True)
     gbs = byts / (ms * 1e-3) / 1e9
     tc = w.batch * w.dim * w.seqlen
@@ -291,14 +349,34 @@ def main():
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "token_channels_per_s": tc / (ms * 1e-3),
         "step_ms": {"mean": round(ms, 4), "median": round(tm["median"], 4), "min": round(tm["min"], 4)},
-        # one s6_scan_fwd = one launch of the scan kernel on this workload, so
-        # the per-launch duration is the per-step time measured on its stream
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+        # One s6_scan_fwd = one launch of the scan kernel on this workload, so
+        # the per-launch duration is the per-step time measured on its stream.
+        # The kernel is bound by VALU issue (the exponential and the FMAs of
+        # every (token, channel, state)), not by HBM: "achieved" is the
+        # method's VALU lane-slots per second against the VALU issue peak;
+        # the HBM side is given beside it.
+        "roofline": {"bound": "alu", "achieved": round(tslots, 2), "peak": VALU_PEAK_TSLOTS,
+                     "unit": "Tslot/s", "frac": round(tslots / VALU_PEAK_TSLOTS, 4),
+                     "valu_slots_per_launch": slots,
+                     "hbm_GBps": round(gbs, 1), "hbm_peak_GBps": HBM_PEAK_GBS,
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
     if not args.no_decode:
         print("[bench] decode", file=sys.stderr, flush=True)
         out["decode"] = bench_decode(args.decode_steps, args.warmup)
+    if not args.no_extra:
+        wl = synth.WORKLOADS["long"]
+        print(f"[bench] scan {wl.name}", file=sys.stderr, flush=True)
+        _, tl, _ = bench_scan(wl, 3, 1)
+        out["long"] = scan_line("long", wl, tl, 2, "sequence cut into segments + carry fold (two passes)", True)
+        torch.cuda.empty_cache()
+        wm = synth.WORKLOADS["m130"]
+        print(f"[bench] scan {wm.name} hot and cold", file=sys.stderr, flush=True)
+        _, th, _ = bench_scan(wm, 50, 5)
+        _, tc, _ = bench_scan(wm, 20, 2, flush=True)
+        out["m130_hot"] = scan_line("m130", wm, th, 2, "repeated; inputs stay in the 256 MB Infinity Cache", True)
+        out["m130_cold"] = scan_line("m130", wm, tc, 2, "a 512 MiB write between scans evicts the inputs", False)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inp)

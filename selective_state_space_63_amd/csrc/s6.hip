@@ -100,7 +100,7 @@ struct ScanArgs {
   float* hout;            // final states or null
   float* sumdelta;        // kModeState: per-segment sum of delta (S, batch, D) or null
   int64_t D, L, N;
-  int64_t seg_len;        // tokens per segment (multiple of kT); segment = blockIdx.z
+  int64_t seg_len;        // tokens per segment (multiple of 4 kT); segment = blockIdx.z
   int64_t hinit_stride;   // elements between segments in hinit (0: same for all)
   int64_t hout_stride;    // elements between segments in hout
   int64_t hout_last_only; // 1: only the last segment writes hout (at offset 0)
@@ -310,7 +310,9 @@ s6_scan_kernel(ScanArgs a) {
   }
   const bool fchv = d0 + fc < D;
   const float dsk = (MODE == kModeY && a.Dskip && fchv) ? a.Dskip[d0 + fc] : 0.0f;
-  double dsum = 0.0;
+  // Sum of delta over the segment (state mode), compensated (Neumaier):
+  // dsum + dcomp.  (A double accumulator here costs dozens of registers.)
+  float dsum = 0.0f, dcomp = 0.0f;
 
   // This thread's pieces: slot s holds piece tid + s * NTHR of every chunk.
   // Rows past the end of the block read the last valid row (their channels
@@ -489,10 +491,10 @@ s6_scan_kernel(ScanArgs a) {
       ysum[2 * g + 1] = ys[1];
       if constexpr (MODE == kModeState) cs += (dl[0] + dl[1]) + (dl[2] + dl[3]);
     }
-    // The chunk's state updates complete here.  (Without output terms nothing
-    // else ties them to the chunk, and the compiler would sink them past the
-    // barriers, keeping every chunk's inputs live at once.)
-    asm volatile("" : "+v"(h[0]), "+v"(h[1]));
+    // The chunk's state updates (and delta sum) complete here.  (Without
+    // output terms nothing else ties them to the chunk, and the compiler would
+    // sink them past the barriers, keeping every chunk's inputs live at once.)
+    asm volatile("" : "+v"(h[0]), "+v"(h[1]), "+v"(cs));
     float* pbuf = part + buf * (W * PART);
     if constexpr (MODE == kModeY) {
       // ysum[i] is this wave's sum for token 2i + r: part[buf][w][r][cl][i]
@@ -500,7 +502,11 @@ s6_scan_kernel(ScanArgs a) {
       *reinterpret_cast<float4*>(pp) = make_float4(ysum[0], ysum[1], ysum[2], ysum[3]);
       *reinterpret_cast<float4*>(pp + 4) = make_float4(ysum[4], ysum[5], ysum[6], ysum[7]);
     }
-    if constexpr (MODE == kModeState) dsum += (double)cs;
+    if constexpr (MODE == kModeState) {
+      const float t = dsum + cs;
+      dcomp += (fabsf(dsum) >= fabsf(cs)) ? (dsum - t) + cs : (cs - t) + dsum;
+      dsum = t;
+    }
 
     // Stage chunk k + 1 into the other buffer (read last before the previous
     // barrier).  The register set it came from is free once its window's
@@ -568,7 +574,7 @@ s6_scan_kernel(ScanArgs a) {
   }
   if constexpr (MODE == kModeState) {
     if (a.sumdelta && chv && w == 0 && r == 0)
-      a.sumdelta[seg * (int64_t)(gridDim.x / nblk) * D + b * D + d] = (float)dsum;
+      a.sumdelta[seg * (int64_t)(gridDim.x / nblk) * D + b * D + d] = dsum + dcomp;
   }
 }
 
@@ -751,13 +757,28 @@ struct Plan {
   int W;              // waves per workgroup (power of two, 4*W >= dstate)
   int64_t nblk;       // channel blocks per batch row
   int64_t segs;       // segments along L
-  int64_t seg_len;    // tokens per segment, multiple of kT
+  int64_t seg_len;    // tokens per segment, multiple of 4 kT
   bool vec;           // 16-byte staging and 8-byte stores
 };
 
-// Segments: when batch * channel blocks gives fewer than 640 workgroups
-// (2.5 per CU), cut L so that there are about 1280 (five per CU), each
-// segment holding at least 4 chunks.
+// Compute units of the current device (cached; 256 on MI355X).
+int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Segments: the scan kernel runs five waves per SIMD, i.e. 20 / W workgroups
+// per CU (two for W = 8).  When batch * channel blocks fills less than half
+// of those slots, L is cut into as many segments as keep the grid within
+// one round of slots (each segment at least 4 chunks, and a multiple of 64
+// tokens so the kernel's 4-chunk cycles have no phantom chunks).
 Plan make_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, size_t esz,
                const void* const* ptrs, int nptr) {
   Plan p;
@@ -765,16 +786,16 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, size_
   p.W = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
   p.nblk = (dim + kCW - 1) / kCW;
   const int64_t wgs = p.nblk * batch;
+  const int64_t slots = (int64_t)cu_count() * (p.W == 8 ? 2 : 20 / p.W);
   int64_t segs = 1;
-  if (wgs < 640) {
-    segs = (1280 + wgs - 1) / wgs;
+  if (2 * wgs <= slots) {
+    segs = slots / wgs;
     const int64_t max_segs = (seqlen + 4 * kT - 1) / (4 * kT);
     if (segs > max_segs) segs = max_segs;
     if (segs < 1) segs = 1;
   }
   int64_t seg_len = (seqlen + segs - 1) / segs;
-  seg_len = ((seg_len + kT - 1) / kT) * kT;
-  if (seg_len < kT) seg_len = kT;
+  seg_len = ((seg_len + 4 * kT - 1) / (4 * kT)) * (4 * kT);
   p.segs = (seqlen + seg_len - 1) / seg_len;
   if (p.segs < 1) p.segs = 1;
   p.seg_len = seg_len;
