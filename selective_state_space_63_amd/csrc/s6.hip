@@ -6,35 +6,40 @@
 //     h = exp(delta*A) * h + delta*B*x ;  y = (sum_n C*h + D*x) * SiLU(z)
 //
 // Design (gfx950, wave64):
-//  * The path is bound by the exponential (v_exp_f32 issues from the same
-//    VALU port as FMA at a quarter of its rate) and by HBM streaming, not by
-//    a dense contraction, so no MFMA is used.
-//  * Workgroup = 64 channels of one batch row x G waves; lane = channel,
-//    wave w = states [4w, 4w+4).  A, the state h and the per-lane partial
-//    output stay in VGPRs; the (batch, D, L, N) state is never written.
-//  * B and C of a token are the same for all 64 channels of a wave.  For 4
-//    tokens x 4 states they sit in one VGPR per tensor, replicated in each
-//    16-lane row (lane x of a row holds token x/4, state x%4), and every use
-//    reads them through a DPP row_newbcast operand folded into the multiply:
-//    no LDS traffic and no extra instruction.  They are loaded from the bf16
-//    or fp32 inputs one chunk ahead.
-//  * x, delta, z are staged per chunk of kT tokens into double-buffered,
-//    channel-major LDS tiles with coalesced row loads issued one chunk ahead;
-//    the token loop reads its lane's 16 deltas and x values in bulk, so it
-//    contains no memory waits.  Tokens past the end of the sequence are
-//    staged as delta = 0, which leaves the state unchanged, so every chunk
-//    runs the full unrolled loop.
-//  * Each wave writes its partial sum over its 4 states per token into LDS;
-//    after the chunk the G waves finalise the 64 x kT outputs (sum of G
-//    partials, skip term, gate), each lane 4 consecutive tokens of one
-//    channel, stored as 16-byte writes.  Two barriers per chunk.
-//  * Few long rows (too few workgroups to fill 256 CUs) are cut into
+//  * The scan is bound by VALU issue: per (token, channel, state) it needs an
+//    exponential (v_exp_f32, two issue slots) and four multiply/FMA slots,
+//    and packed fp32 math is not used.  There is no dense contraction, so no
+//    MFMA.  Everything below serves to keep the VALU busy with little else.
+//  * Workgroup = 32 channels of one batch row x W waves (W = 4 for N = 16).
+//    Lane l of wave w: channel (l >> 5) * 16 + (l & 15), states 4w + 2r and
+//    4w + 2r + 1 with r = (l >> 4) & 1.  For the 3B layer that is exactly 5
+//    waves per SIMD on 256 CUs.  A and the state stay in VGPRs; the
+//    (batch, D, L, N) state is never written.
+//  * B and C differ per state pair, i.e. per 16-lane row.  For a group of 4
+//    tokens a row keeps them in one VGPR (lane 4m + k: B of pair member m,
+//    token k; lane 8 + 4m + k: C), read through DPP row_newbcast operands of
+//    v_mul_f32_dpp / v_fmac_f32_dpp: no extra instruction per use.
+//  * The two state pairs of a channel sit in rows 2i and 2i + 1; one
+//    v_permlane16_swap plus an add combines their output terms for two
+//    tokens at once.  The W waves add theirs through LDS.
+//  * Inputs are staged per 16-token chunk: threads load 16-byte pieces of
+//    x, delta, z, B and C two 32-token windows ahead into registers (so each
+//    row is read in 64-byte runs), convert them to fp32 into double-buffered
+//    LDS tiles one chunk ahead (x, delta in a channel-major XOR-swizzled
+//    layout; B/C in the DPP layout), and each lane reads its channel's values
+//    per group of 4 tokens.  One barrier per chunk; after it, every lane
+//    finalises 2 tokens of one channel (sum of the W partial outputs, skip
+//    term, SiLU gate) and adjacent lanes store 64-byte runs of y.
+//  * Chunks past the end of a sequence are staged as delta = 0 (the state
+//    stays exactly unchanged) and store nothing, so the loop body has no
+//    conditional memory operations.
+//  * Few long rows (too few workgroups to fill the GPU) are cut into
 //    segments along L: pass 1 computes every segment's end state from zero
 //    and its summed delta, a tiny pass folds them into each segment's
 //    incoming state (associativity of the (a, b) pairs), and pass 2 runs the
 //    fused scan of every segment from its incoming state.
-//  * Decode: one lane per 4 states of a channel, h streamed in place with
-//    16-byte accesses, partial outputs reduced across the channel's lanes.
+//  * Decode: one lane per channel (dstate <= 16) with all its states in
+//    registers, h streamed in place with 16-byte accesses.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
