@@ -38,8 +38,10 @@
 //    and its summed delta, a tiny pass folds them into each segment's
 //    incoming state (associativity of the (a, b) pairs), and pass 2 runs the
 //    fused scan of every segment from its incoming state.
-//  * Decode: one lane per channel (dstate <= 16) with all its states in
-//    registers, h streamed in place with 16-byte accesses.
+//  * Decode: 4 states per lane (P = dstate / 4 adjacent lanes per channel,
+//    partial outputs added with DPP quad permutations), 4 batch rows per
+//    lane with all their loads issued first; h, A, B, C read and h written
+//    with 8/16-byte accesses that are contiguous across the lanes of a wave.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -630,97 +632,137 @@ struct StepArgs {
   int64_t batch, D, N;
 };
 
-// P lanes per channel, SPL states per lane (lane q: states q*SPL ...).
-// VEC: N == P * SPL and every row of h, A, B and C starts 16-byte aligned, so
-// all of them are read with 16-byte loads (h written back the same way).
-// The step's B and C rows are the same for every channel of a batch row and
-// stay in cache; h is streamed once in and once out.
-template <typename In, bool GATE, int P, int SPL, bool VEC>
+// P lanes per channel, SPL states per lane (lane q: states q*SPL ...), G
+// batch rows per lane (the same channel d of rows b0 .. b0+G-1, so the row of
+// A is read once).  All G rows' loads are issued before any arithmetic.
+// VEC: N == P * SPL and every row of h, A, B and C starts aligned, so h and A
+// are read with 16-byte loads (h written back the same way) and B, C with
+// 16- or 8-byte loads.  The step's B and C rows are the same for every
+// channel of a batch row and stay in cache; h is streamed once in and once
+// out.
+template <typename In, bool GATE, int P, int SPL, bool VEC, int G>
 __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
-  static_assert(!VEC || (SPL * sizeof(In)) % 16 == 0, "16-byte rows of B and C");
+  static_assert(!VEC || (SPL * sizeof(In)) % 8 == 0, "8- or 16-byte pieces of B and C");
+  static_assert(P == 1 || P == 2 || P == 4, "lanes per channel");
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t ch = gid / P;
+  const int64_t idx = gid / P;  // (batch group, channel)
   const int q = (int)(gid % P);
-  const int64_t pairs = a.batch * a.D;
-  const bool valid = ch < pairs;
-  const int64_t N = a.N;
-  const int64_t b = valid ? ch / a.D : 0;
-  const int64_t d = valid ? ch % a.D : 0;
+  const int64_t D = a.D, N = a.N;
+  const int64_t groups = (a.batch + G - 1) / G;
+  const bool valid = idx < groups * D;
+  const int64_t d = valid ? idx % D : 0;
+  const int64_t b0 = valid ? (idx / D) * G : 0;
   const In* xp = static_cast<const In*>(a.x);
   const In* dp = static_cast<const In*>(a.delta);
   const In* zp = static_cast<const In*>(a.z);
   const In* Bp = static_cast<const In*>(a.Bm);
   const In* Cp = static_cast<const In*>(a.Cm);
   const int64_t n0 = (int64_t)q * SPL;
+  using Piece = typename std::conditional<(SPL * sizeof(In)) % 16 == 0, u32x4, uint2>::type;
+  constexpr int PER = (int)(sizeof(Piece) / sizeof(In));  // B/C elements per load
+  constexpr int NP = VEC ? SPL / PER : 1;
 
-  float yp = 0.0f;
-  float xt = 0.0f;
-  if (valid) {
-    const float dt = to_f32(dp[ch]);
-    xt = to_f32(xp[ch]);
-    const float u = dt * xt;
-    float* hrow = a.h + ch * N + n0;
-    const float* arow = a.A + d * N + n0;
-    const In* brow = Bp + b * N + n0;
-    const In* crow = Cp + b * N + n0;
-    float hv[SPL], Av[SPL], Bv[SPL], Cv[SPL];
+  // the channel's row of A, scaled to base 2
+  float A2[SPL];
+  const float* arow = a.A + d * N + n0;
+  if constexpr (VEC) {
+#pragma unroll
+    for (int j = 0; j < SPL; j += 4) {
+      const float4 aa = *reinterpret_cast<const float4*>(arow + j);
+      A2[j] = aa.x * kLog2e; A2[j + 1] = aa.y * kLog2e; A2[j + 2] = aa.z * kLog2e; A2[j + 3] = aa.w * kLog2e;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) A2[j] = (valid && n0 + j < N) ? arow[j] * kLog2e : 0.0f;
+  }
+  const float dsk = (a.Dskip && valid) ? a.Dskip[d] : 0.0f;
+
+  // loads of all G rows
+  bool vb[G];
+  float hv[G][SPL], dt[G], xt[G];
+  Piece bp[G][NP], cp[G][NP];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int64_t b = b0 + g;
+    vb[g] = valid && b < a.batch;
+    const int64_t ch = vb[g] ? b * D + d : 0;  // invalid rows read row 0 and store nothing
+    const int64_t bb = vb[g] ? b : 0;
+    dt[g] = to_f32(dp[ch]);
+    xt[g] = to_f32(xp[ch]);
+    const float* hrow = a.h + ch * N + n0;
     if constexpr (VEC) {
 #pragma unroll
       for (int j = 0; j < SPL; j += 4) {
         const float4 hh = *reinterpret_cast<const float4*>(hrow + j);
-        const float4 aa = *reinterpret_cast<const float4*>(arow + j);
-        hv[j] = hh.x; hv[j + 1] = hh.y; hv[j + 2] = hh.z; hv[j + 3] = hh.w;
-        Av[j] = aa.x; Av[j + 1] = aa.y; Av[j + 2] = aa.z; Av[j + 3] = aa.w;
+        hv[g][j] = hh.x; hv[g][j + 1] = hh.y; hv[g][j + 2] = hh.z; hv[g][j + 3] = hh.w;
       }
-      constexpr int PER = 16 / (int)sizeof(In);  // elements per 16-byte load
 #pragma unroll
-      for (int j = 0; j < SPL; j += PER) {
-        const u32x4 bb = *reinterpret_cast<const u32x4*>(brow + j);
-        const u32x4 cc = *reinterpret_cast<const u32x4*>(crow + j);
-        const In* be = reinterpret_cast<const In*>(&bb);
-        const In* ce = reinterpret_cast<const In*>(&cc);
+      for (int k = 0; k < NP; ++k) {
+        bp[g][k] = *reinterpret_cast<const Piece*>(Bp + bb * N + n0 + k * PER);
+        cp[g][k] = *reinterpret_cast<const Piece*>(Cp + bb * N + n0 + k * PER);
+      }
+    } else {
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          Bv[j + k] = to_f32(be[k]);
-          Cv[j + k] = to_f32(ce[k]);
+      for (int j = 0; j < SPL; ++j) hv[g][j] = (vb[g] && n0 + j < N) ? hrow[j] : 0.0f;
+    }
+  }
+
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int64_t b = b0 + g;
+    const int64_t ch = vb[g] ? b * D + d : 0;
+    const int64_t bb = vb[g] ? b : 0;
+    float Bv[SPL], Cv[SPL];
+    if constexpr (VEC) {
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        const In* be = reinterpret_cast<const In*>(&bp[g][k]);
+        const In* ce = reinterpret_cast<const In*>(&cp[g][k]);
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+          Bv[k * PER + m] = to_f32(be[m]);
+          Cv[k * PER + m] = to_f32(ce[m]);
         }
       }
     } else {
 #pragma unroll
       for (int j = 0; j < SPL; ++j) {
-        const bool sv = n0 + j < N;
-        hv[j] = sv ? hrow[j] : 0.0f;
-        Av[j] = sv ? arow[j] : 0.0f;
-        Bv[j] = sv ? to_f32(brow[j]) : 0.0f;
-        Cv[j] = sv ? to_f32(crow[j]) : 0.0f;
+        const bool sv = vb[g] && n0 + j < N;
+        Bv[j] = sv ? to_f32(Bp[bb * N + n0 + j]) : 0.0f;
+        Cv[j] = sv ? to_f32(Cp[bb * N + n0 + j]) : 0.0f;
       }
     }
+    const float u = dt[g] * xt[g];
+    float yp = 0.0f;
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
-      const float e = fast_exp2(dt * (Av[j] * kLog2e));
-      hv[j] = __builtin_fmaf(e, hv[j], u * Bv[j]);
-      yp = __builtin_fmaf(Cv[j], hv[j], yp);
+      const float e = fast_exp2(dt[g] * A2[j]);
+      hv[g][j] = __builtin_fmaf(e, hv[g][j], u * Bv[j]);
+      yp = __builtin_fmaf(Cv[j], hv[g][j], yp);
     }
-    if constexpr (VEC) {
+    float* hrow = a.h + ch * N + n0;
+    if (vb[g]) {
+      if constexpr (VEC) {
 #pragma unroll
-      for (int j = 0; j < SPL; j += 4)
-        *reinterpret_cast<float4*>(hrow + j) = make_float4(hv[j], hv[j + 1], hv[j + 2], hv[j + 3]);
-    } else {
+        for (int j = 0; j < SPL; j += 4)
+          *reinterpret_cast<float4*>(hrow + j) = make_float4(hv[g][j], hv[g][j + 1], hv[g][j + 2], hv[g][j + 3]);
+      } else {
 #pragma unroll
-      for (int j = 0; j < SPL; ++j)
-        if (n0 + j < N) hrow[j] = hv[j];
+        for (int j = 0; j < SPL; ++j)
+          if (n0 + j < N) hrow[j] = hv[g][j];
+      }
     }
-  }
-  // reduce the P partial outputs of a channel (P consecutive lanes)
-  if constexpr (P > 1) {
-#pragma unroll
-    for (int off = P / 2; off > 0; off >>= 1) yp += __shfl_xor(yp, off, P);
-  }
-  if (valid && q == 0) {
-    float yv = yp;
-    if (a.Dskip) yv = __builtin_fmaf(a.Dskip[d], xt, yv);
-    if constexpr (GATE) yv *= silu(to_f32(zp[ch]));
-    a.y[ch] = yv;
+    // the P partial outputs of a channel sit in P consecutive lanes (P <= 4):
+    // add them with DPP quad permutations (lane ^ 1, then lane ^ 2)
+    if constexpr (P >= 2)
+      yp += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yp), 0xB1, 0xf, 0xf, false));
+    if constexpr (P >= 4)
+      yp += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yp), 0x4E, 0xf, 0xf, false));
+    if (vb[g] && q == 0) {
+      float yv = __builtin_fmaf(dsk, xt[g], yp);
+      if constexpr (GATE) yv *= silu(to_f32(zp[ch]));
+      a.y[ch] = yv;
+    }
   }
 }
 
@@ -956,36 +998,45 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
   return rc;
 }
 
-template <typename In, bool GATE, int P, int SPL>
+template <typename In, bool GATE, int P, int SPL, int G>
 int launch_step_t(const StepArgs& a, bool vec, hipStream_t st) {
-  const int64_t threads = a.batch * a.D * P;
+  const int64_t threads = ((a.batch + G - 1) / G) * a.D * P;
   const int64_t blocks = (threads + 255) / 256;
-  if constexpr ((SPL * sizeof(In)) % 16 == 0) {
+  if constexpr ((SPL * sizeof(In)) % 8 == 0) {
     if (vec) {
-      hipLaunchKernelGGL((s6_step_kernel<In, GATE, P, SPL, true>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((s6_step_kernel<In, GATE, P, SPL, true, G>), dim3((unsigned)blocks), dim3(256), 0, st, a);
       S6_HIP(hipGetLastError(), "s6_step_kernel launch");
       return S6_OK;
     }
   }
-  hipLaunchKernelGGL((s6_step_kernel<In, GATE, P, SPL, false>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((s6_step_kernel<In, GATE, P, SPL, false, G>), dim3((unsigned)blocks), dim3(256), 0, st, a);
   S6_HIP(hipGetLastError(), "s6_step_kernel launch");
   return S6_OK;
 }
 
-// One lane per channel for dstate <= 16 (all states in registers, no
-// cross-lane reduction), two lanes for 17..32.
+// Four batch rows per lane when that still leaves many lanes, else one.
+template <typename In, bool GATE, int P, int SPL>
+int launch_step_b(const StepArgs& a, bool vec, hipStream_t st) {
+  if (a.batch >= 4 && a.batch * a.D * P >= 4 * 65536) return launch_step_t<In, GATE, P, SPL, 4>(a, vec, st);
+  return launch_step_t<In, GATE, P, SPL, 1>(a, vec, st);
+}
+
+// Lanes per channel: 4 states per lane (P = 1, 2, 4 for dstate <= 4, 8,
+// 16), so the lanes of a wave read h and A in one contiguous run; 8 states
+// per lane over 4 lanes for 17..32.
 template <typename In, bool GATE>
 int launch_step_g(const StepArgs& a, hipStream_t st) {
   const int64_t N = a.N;
   const size_t esz = sizeof(In);
   auto vec_ok = [&](int64_t P, int64_t SPL) {
-    return N == P * SPL && aligned(a.h, 16) && aligned(a.A, 16) && aligned(a.Bm, 16) && aligned(a.Cm, 16) &&
-           (N * (int64_t)esz) % 16 == 0 && (SPL * (int64_t)esz) % 16 == 0;
+    const int64_t piece = (SPL * (int64_t)esz) % 16 == 0 ? 16 : 8;  // bytes of a B/C load
+    return N == P * SPL && aligned(a.h, 16) && aligned(a.A, 16) && aligned(a.Bm, piece) &&
+           aligned(a.Cm, piece) && (N * (int64_t)esz) % piece == 0 && (SPL * (int64_t)esz) % 8 == 0;
   };
-  if (N <= 4) return launch_step_t<In, GATE, 1, 4>(a, vec_ok(1, 4), st);
-  if (N <= 8) return launch_step_t<In, GATE, 1, 8>(a, vec_ok(1, 8), st);
-  if (N <= 16) return launch_step_t<In, GATE, 1, 16>(a, vec_ok(1, 16), st);
-  return launch_step_t<In, GATE, 2, 16>(a, vec_ok(2, 16), st);
+  if (N <= 4) return launch_step_b<In, GATE, 1, 4>(a, vec_ok(1, 4), st);
+  if (N <= 8) return launch_step_b<In, GATE, 2, 4>(a, vec_ok(2, 4), st);
+  if (N <= 16) return launch_step_b<In, GATE, 4, 4>(a, vec_ok(4, 4), st);
+  return launch_step_b<In, GATE, 4, 8>(a, vec_ok(4, 8), st);
 }
 
 }  // namespace

@@ -171,7 +171,8 @@ def test_last_state(torch_cuda, oracle, shape):
 @pytest.mark.parametrize("shape", [(3, 70, 16, synth.BF16, True), (2, 33, 5, synth.F32, True),
                                    (1, 17, 32, synth.BF16, False), (4, 9, 1, synth.F32, False),
                                    (2, 20, 8, synth.BF16, True), (2, 40, 4, synth.F32, True),
-                                   (1, 24, 12, synth.BF16, True)])
+                                   (1, 24, 12, synth.BF16, True),
+                                   (6, 22000, 16, synth.BF16, True)])  # 4 rows per lane, ragged batch
 def test_state_update_equals_scan(torch_cuda, oracle, shape):
     """S single-token steps from h0 against the oracle's step and against the
     scan of the same tokens."""
