@@ -198,10 +198,11 @@ def bench_decode(steps_total, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
+    h_eager = h.clone()
     upd = w.batch * w.dim * w.dstate * S
     byts = decode_step_bytes(w.batch, w.dim, w.dstate, 2) * S
     gbs = byts / (ms * 1e-3) / 1e9
-    return {
+    out = {
         "workload": w.name, "steps": S, "ms_total": round(ms, 3), "us_per_step": round(1e3 * ms / S, 2),
         "state_updates_per_s": upd / (ms * 1e-3), "token_steps_per_s": w.batch * S / (ms * 1e-3),
         "effective_GBps": gbs,
@@ -209,6 +210,29 @@ def bench_decode(steps_total, warmup):
                      "frac": round(gbs / HBM_PEAK_GBS, 4)},
         "note": "plain launches, state resident in device memory (fits the 256 MB Infinity Cache)",
     }
+    # The same S steps captured once in a HIP graph and replayed (the state
+    # is reset eagerly before each replay); each replay must reproduce the
+    # plain launches' final state bit for bit.
+    g = torch.cuda.CUDAGraph()
+    h.zero_()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run(S)
+    times = []
+    for _ in range(3):
+        h.zero_()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+        if not torch.equal(h, h_eager):
+            raise RuntimeError("decode graph replay differs from the plain launches")
+    gms = min(times)
+    out["graph"] = {"ms_total": round(gms, 3), "us_per_step": round(1e3 * gms / S, 2),
+                    "state_updates_per_s": upd / (gms * 1e-3), "replays_checked": len(times)}
+    return out
 
 
 def cpu_baseline(w, inp, budget_s=10.0):
