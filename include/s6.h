@@ -105,7 +105,8 @@ int s6_last_state(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
                   const float* h0, float* h_last, void* stream);
 
 /* One decode token for every (batch, channel): h is read, advanced by one
- * step and written back in place; y receives the token's output.
+ * step and written back in place; y receives the token's output.  batch*dim
+ * above 2^31 * 32 is rejected with S6_ERR_SHAPE (launch grid limit).
  *   h : required, in/out (batch, dim, dstate) fp32.
  *   x, delta, z : (batch, dim); Bm, Cm : (batch, dstate); Dskip and z nullable.
  *   y : required output (batch, dim) fp32. */

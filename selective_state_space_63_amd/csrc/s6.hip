@@ -1078,6 +1078,8 @@ int s6_state_update(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, fl
                     const void* Cm, const float* Dskip, const void* z, float* y, void* stream) {
   int rc = check_common(batch, dim, 1, dstate, in_dtype);
   if (rc) return rc;
+  // one thread per (batch, channel, 4 states) at most: the grid must fit
+  if (batch * dim > (int64_t)INT32_MAX * 256 / 8) return S6_ERR_SHAPE;
   if (batch == 0 || dim == 0) return S6_OK;
   if (!h || !x || !delta || !A || !Bm || !Cm || !y) return S6_ERR_NULL;
   const size_t esz = in_dtype == S6_BF16 ? 2 : 4;

@@ -114,6 +114,7 @@ def test_state_update_validation(lib, codes):
     assert f(2, 64, 16, 3, P, P, P, P, P, P, None, None, P, None) == codes["S6_ERR_DTYPE"]
     assert f(-2, 64, 16, 0, P, P, P, P, P, P, None, None, P, None) == codes["S6_ERR_SHAPE"]
     assert f(2, 0, 16, 0, P, P, P, P, P, P, None, None, P, None) == codes["S6_OK"]
+    assert f(1 << 20, 1 << 20, 16, 0, P, P, P, P, P, P, None, None, P, None) == codes["S6_ERR_SHAPE"]
 
 
 def test_binding_refuses_host_tensors():
