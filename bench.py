@@ -235,6 +235,48 @@ def bench_decode(steps_total, warmup):
     return out
 
 
+def bench_decode_hbm(steps=64, warmup=16, batch=1024):
+    """Decode steps on a state too large for the 256 MB Infinity Cache
+    (batch 1024, D 5120, N 16: 335 MB of fp32 state), so each step reads
+    and writes the state in HBM.  Plain launches, `steps` distinct tokens."""
+    import torch
+    from selective_state_space_63_amd import s6, synth
+    base = synth.WORKLOADS["decode"]
+    w = synth.custom(batch, base.dim, base.dstate, steps, seed=base.seed)
+    inp = synth.device_full(w)
+    x = inp["x"].permute(2, 0, 1).contiguous()
+    dl = inp["delta"].permute(2, 0, 1).contiguous()
+    z = inp["z"].permute(2, 0, 1).contiguous()
+    Bm = inp["Bm"].permute(2, 0, 1).contiguous()
+    Cm = inp["Cm"].permute(2, 0, 1).contiguous()
+    del inp["x"], inp["delta"], inp["z"]
+    h = torch.zeros((w.batch, w.dim, w.dstate), device="cuda", dtype=torch.float32)
+    y = torch.empty((w.batch, w.dim), device="cuda", dtype=torch.float32)
+
+    def run(n):
+        for s in range(n):
+            s6.state_update(h, x[s % steps], dl[s % steps], inp["A"], Bm[s % steps], Cm[s % steps],
+                            D=inp["Dskip"], z=z[s % steps], y=y)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    run(steps)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    gbs = decode_step_bytes(w.batch, w.dim, w.dstate, 2) * steps / (ms * 1e-3) / 1e9
+    return {"workload": f"decode_b{batch}_d{w.dim}_n{w.dstate}_s{steps}", "steps": steps,
+            "us_per_step": round(1e3 * ms / steps, 2),
+            "state_updates_per_s": w.batch * w.dim * w.dstate * steps / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "note": "plain launches; 335 MB of state, larger than the Infinity Cache"}
+
+
 def cpu_baseline(w, inp, budget_s=10.0):
     """The fp64 oracle (as it stands, OpenMP over channels) on whole batch
     rows of the same inputs, cycling over the rows until `budget_s` of oracle
@@ -400,6 +442,10 @@ def main():
     if not args.no_decode:
         print("[bench] decode", file=sys.stderr, flush=True)
         out["decode"] = bench_decode(args.decode_steps, args.warmup)
+        torch.cuda.empty_cache()
+        print("[bench] decode, batch 1024", file=sys.stderr, flush=True)
+        out["decode_b1024"] = bench_decode_hbm()
+        torch.cuda.empty_cache()
     if not args.no_extra:
         wl = synth.WORKLOADS["long"]
         print(f"[bench] scan {wl.name}", file=sys.stderr, flush=True)

@@ -43,6 +43,7 @@ def build_from_text(text: str) -> str:
 
 
 _P = ctypes.POINTER(ctypes.c_double)
+SOFTPLUS, ZOH_EXACT = 1, 2  # option bits of oracle_scan_ex / oracle_step_ex
 _I = ctypes.c_int64
 
 
@@ -58,6 +59,10 @@ class Oracle:
         self.lib.oracle_scan.restype = None
         self.lib.oracle_step.argtypes = [_I, _I, _I] + [_P] * 11
         self.lib.oracle_step.restype = None
+        self.lib.oracle_scan_ex.argtypes = [_I, _I, _I, _I, _P, _P, _P, ctypes.c_int] + [_P] * 10
+        self.lib.oracle_scan_ex.restype = None
+        self.lib.oracle_step_ex.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_int] + [_P] * 7
+        self.lib.oracle_step_ex.restype = None
         self.lib.oracle_num_threads.restype = ctypes.c_int
         self.path = path
 
@@ -73,10 +78,18 @@ class Oracle:
             raise ValueError(f"shape {arr.shape} != {tuple(shape)}")
         return arr, arr.ctypes.data_as(_P)
 
-    def scan(self, x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None):
+    @staticmethod
+    def _flags(softplus, zoh):
+        return (SOFTPLUS if softplus else 0) | (ZOH_EXACT if zoh else 0)
+
+    def scan(self, x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_bias=None,
+             softplus=False, zoh=False):
         """Full scan.  x, delta, z: (batch, D, L); Bm, Cm: (batch, N, L);
-        A: (D, N); Dskip: (D,); h0: (batch, D, N).  Returns a dict with y and
-        m (batch, D, L), h_last and H_last (batch, D, N), all fp64."""
+        A: (D, N); Dskip: (D,); h0: (batch, D, N); delta_bias: (D,).
+        softplus: the step is softplus(delta + delta_bias); zoh: exact
+        zero-order-hold input coefficient (exp(Delta A) - 1) / A.  Returns a
+        dict with y and m (batch, D, L), h_last and H_last (batch, D, N), all
+        fp64."""
         x = np.asarray(x)
         Bsz, D, L = x.shape
         N = np.asarray(A).shape[1]
@@ -94,12 +107,19 @@ class Oracle:
         hl = np.empty((Bsz, D, N))
         Hl = np.empty((Bsz, D, N))
         outs = [o.ctypes.data_as(_P) for o in (y, m, hl, Hl)]
-        self.lib.oracle_scan(Bsz, D, L, N, *args, *outs)
+        flags = self._flags(softplus, zoh)
+        if delta_bias is None and flags == 0:
+            self.lib.oracle_scan(Bsz, D, L, N, *args, *outs)
+        else:
+            bias, bptr = self._in(delta_bias, (D,))
+            self.lib.oracle_scan_ex(Bsz, D, L, N, args[0], args[1], bptr, flags, *args[2:], *outs)
         return {"y": y, "m": m, "h_last": hl, "H_last": Hl}
 
-    def step(self, h, H, x, delta, A, Bm, Cm, Dskip=None, z=None):
+    def step(self, h, H, x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None, softplus=False,
+             zoh=False):
         """One decode token.  h, H: (batch, D, N) fp64 arrays updated in place;
-        x, delta, z: (batch, D); Bm, Cm: (batch, N).  Returns (y, m)."""
+        x, delta, z: (batch, D); Bm, Cm: (batch, N); options as in scan.
+        Returns (y, m)."""
         if h.dtype != np.float64 or not h.flags.c_contiguous or H.dtype != np.float64:
             raise ValueError("h and H must be contiguous float64 arrays")
         Bsz, D, N = h.shape
@@ -112,8 +132,15 @@ class Oracle:
             args.append(ptr)
         y = np.empty((Bsz, D))
         m = np.empty((Bsz, D))
-        self.lib.oracle_step(Bsz, D, N, h.ctypes.data_as(_P), H.ctypes.data_as(_P), *args,
-                             y.ctypes.data_as(_P), m.ctypes.data_as(_P))
+        flags = self._flags(softplus, zoh)
+        if delta_bias is None and flags == 0:
+            self.lib.oracle_step(Bsz, D, N, h.ctypes.data_as(_P), H.ctypes.data_as(_P), *args,
+                                 y.ctypes.data_as(_P), m.ctypes.data_as(_P))
+        else:
+            bias, bptr = self._in(delta_bias, (D,))
+            self.lib.oracle_step_ex(Bsz, D, N, h.ctypes.data_as(_P), H.ctypes.data_as(_P), args[0],
+                                    args[1], bptr, flags, *args[2:], y.ctypes.data_as(_P),
+                                    m.ctypes.data_as(_P))
         return y, m
 
 

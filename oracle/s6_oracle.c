@@ -29,6 +29,17 @@
  *   A : (D, N)        Dskip : (D)        h0, h_last, H_last : (Bsz, D, N)
  *   decode step: x, delta, z, y, m : (Bsz, D); Bm, Cm : (Bsz, N)
  *
+ * Discretisation options (oracle_scan_ex, oracle_step_ex; bit flags):
+ *   ORACLE_DELTA_SOFTPLUS  the step is softplus(delta + delta_bias[d]) rather
+ *     than delta itself.  The pages make Delta learnable and input-dependent
+ *     (§3.2) but do not say how it is kept positive; softplus,
+ *     ln(1 + e^v), with a per-channel bias is the plain reading of the
+ *     Mamba layer this guide describes.
+ *   ORACLE_ZOH_EXACT  the input coefficient is the zero-order-hold integral
+ *     of exp(s A) over s in [0, Delta], i.e. (exp(Delta A) - 1) / A (its
+ *     limit at A = 0 is Delta), in place of Delta: the hold the pages name
+ *     in §2.3, applied to B as well as to A.
+ *
  * Besides y the oracle returns the magnitude m: the same recurrence run on
  * absolute values (|dA| H + |dBx|, then sum_n |C| H + |D x|, times |gate|).
  * m bounds |y| and is the scale of the componentwise error metric of the
@@ -54,6 +65,22 @@ int oracle_num_threads(void) {
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
+enum { ORACLE_DELTA_SOFTPLUS = 1, ORACLE_ZOH_EXACT = 2 };
+
+/* softplus(v) = ln(1 + e^v), written as max(v, 0) + ln(1 + e^-|v|) so that
+ * no exponential overflows (the two forms are equal for every v). */
+static double softplus(double v) { return (v > 0.0 ? v : 0.0) + log1p(exp(-fabs(v))); }
+
+/* The step Delta of pair (batch b, channel d) for a stored delta value. */
+static double step_of(double raw, const double* dbias, int64_t d, int flags) {
+  if (!(flags & ORACLE_DELTA_SOFTPLUS)) return raw;
+  return softplus(raw + (dbias ? dbias[d] : 0.0));
+}
+
+/* Zero-order-hold input coefficient: integral of exp(s a) ds over [0, dt],
+ * (exp(dt a) - 1) / a, which is dt when a = 0. */
+static double zoh_coef(double dt, double a) { return a != 0.0 ? expm1(dt * a) / a : dt; }
+
 /* One token of one (batch, channel) pair, all N states.
  * h, H   : the N states and their magnitudes, updated in place.
  * Ad     : A[d, 0..N-1].
@@ -61,11 +88,11 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
  * Returns the token's output before the gate; *mag gets its magnitude. */
 static double step_channel(int64_t N, double* h, double* H, const double* Ad, double dt, double xt,
                            const double* Bt, const double* Ct, int64_t bstride, double dskip,
-                           double* mag) {
+                           int zoh, double* mag) {
   double acc = 0.0, macc = 0.0;
   for (int64_t n = 0; n < N; ++n) {
     double a = exp(dt * Ad[n]);         /* zero-order-hold state transition */
-    double bx = dt * Bt[n * bstride] * xt; /* input term */
+    double bx = (zoh ? zoh_coef(dt, Ad[n]) : dt) * Bt[n * bstride] * xt; /* input term */
     h[n] = a * h[n] + bx;               /* update first ... */
     H[n] = fabs(a) * H[n] + fabs(bx);
     acc += Ct[n * bstride] * h[n];      /* ... then read the output from the new state */
@@ -78,11 +105,13 @@ static double step_channel(int64_t N, double* h, double* H, const double* Ad, do
 
 /* Whole sequence.  Dskip, z and h0 may be NULL (no skip, no gate, zero
  * initial state).  m, h_last and H_last may be NULL (not written).
+ * dbias (D) may be NULL (zero bias); flags: ORACLE_* above.
  * N must not exceed 256. */
-void oracle_scan(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x, const double* delta,
-                 const double* A, const double* Bm, const double* Cm, const double* Dskip,
-                 const double* z, const double* h0, double* y, double* m, double* h_last,
-                 double* H_last) {
+void oracle_scan_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x,
+                    const double* delta, const double* dbias, int flags, const double* A,
+                    const double* Bm, const double* Cm, const double* Dskip, const double* z,
+                    const double* h0, double* y, double* m, double* h_last, double* H_last) {
+  const int zoh = (flags & ORACLE_ZOH_EXACT) != 0;
   int64_t pairs = Bsz * D;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t p = 0; p < pairs; ++p) {
@@ -97,8 +126,9 @@ void oracle_scan(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x, 
     double dsk = Dskip ? Dskip[d] : 0.0;
     for (int64_t t = 0; t < L; ++t) {
       double mag;
-      double yt = step_channel(N, h, H, A + d * N, delta[p * L + t], x[p * L + t], Bb + t, Cb + t,
-                               L, dsk, &mag);
+      double dt = step_of(delta[p * L + t], dbias, d, flags);
+      double yt = step_channel(N, h, H, A + d * N, dt, x[p * L + t], Bb + t, Cb + t,
+                               L, dsk, zoh, &mag);
       if (z) {
         double g = silu(z[p * L + t]);
         yt *= g;
@@ -114,20 +144,30 @@ void oracle_scan(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x, 
   }
 }
 
+void oracle_scan(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x, const double* delta,
+                 const double* A, const double* Bm, const double* Cm, const double* Dskip,
+                 const double* z, const double* h0, double* y, double* m, double* h_last,
+                 double* H_last) {
+  oracle_scan_ex(Bsz, D, L, N, x, delta, NULL, 0, A, Bm, Cm, Dskip, z, h0, y, m, h_last, H_last);
+}
+
 /* One decode token for every (batch, channel) pair: h and its magnitude H are
  * updated in place, y and m receive the token's output.  Same arithmetic as
  * one iteration of the time loop above. */
-void oracle_step(int64_t Bsz, int64_t D, int64_t N, double* h, double* H, const double* x,
-                 const double* delta, const double* A, const double* Bm, const double* Cm,
-                 const double* Dskip, const double* z, double* y, double* m) {
+void oracle_step_ex(int64_t Bsz, int64_t D, int64_t N, double* h, double* H, const double* x,
+                    const double* delta, const double* dbias, int flags, const double* A,
+                    const double* Bm, const double* Cm, const double* Dskip, const double* z,
+                    double* y, double* m) {
+  const int zoh = (flags & ORACLE_ZOH_EXACT) != 0;
   int64_t pairs = Bsz * D;
 #pragma omp parallel for schedule(static)
   for (int64_t p = 0; p < pairs; ++p) {
     int64_t b = p / D, d = p % D;
     double dsk = Dskip ? Dskip[d] : 0.0;
     double mag;
-    double yt = step_channel(N, h + p * N, H + p * N, A + d * N, delta[p], x[p], Bm + b * N,
-                             Cm + b * N, 1, dsk, &mag);
+    double dt = step_of(delta[p], dbias, d, flags);
+    double yt = step_channel(N, h + p * N, H + p * N, A + d * N, dt, x[p], Bm + b * N,
+                             Cm + b * N, 1, dsk, zoh, &mag);
     if (z) {
       double g = silu(z[p]);
       yt *= g;
@@ -136,4 +176,10 @@ void oracle_step(int64_t Bsz, int64_t D, int64_t N, double* h, double* H, const 
     y[p] = yt;
     if (m) m[p] = mag;
   }
+}
+
+void oracle_step(int64_t Bsz, int64_t D, int64_t N, double* h, double* H, const double* x,
+                 const double* delta, const double* A, const double* Bm, const double* Cm,
+                 const double* Dskip, const double* z, double* y, double* m) {
+  oracle_step_ex(Bsz, D, N, h, H, x, delta, NULL, 0, A, Bm, Cm, Dskip, z, y, m);
 }

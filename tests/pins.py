@@ -333,6 +333,145 @@ def pin_magnitude_bounds(o):
     assert np.allclose(r["m"], r["y"], rtol=1e-14, atol=0)
 
 
+# ----------------------------------------------- discretisation options --
+def pin_softplus_hand(o):
+    """Step softplus(delta + bias[d]) with a per-channel bias (§3.2, §2.3):
+    three channels whose v = delta + bias are 0, ln 3 and -ln 3, worked by
+    hand in tests/golden/softplus_hand.txt.  Run as a scan and as decode
+    steps."""
+    g = _read_golden("softplus_hand.txt")
+    v = np.array(g["v"])
+    bias = np.array(g["bias"])
+    xv = np.array(g["x"])
+    L = xv.size
+    D = v.size
+    steps = np.array([math.log(2.0), math.log(4.0), math.log(4.0 / 3.0)])
+    want = np.array([g[f"ch{d} y_over_delta"] for d in range(D)]) * steps[:, None]
+    x = np.repeat(xv[None, None, :], D, axis=1)
+    raw = np.repeat((v - bias)[None, :, None], L, axis=2)
+    ones = np.ones((1, 1, L))
+    A = -np.ones((D, 1))
+    r = o.scan(x, raw, A, ones, ones, delta_bias=bias, softplus=True)
+    assert np.allclose(r["y"][0], want, rtol=1e-14, atol=1e-15), (r["y"], want)
+    h = np.zeros((1, D, 1))
+    H = np.zeros((1, D, 1))
+    for t in range(L):
+        y, _ = o.step(h, H, x[..., t], raw[..., t], A, ones[..., t], ones[..., t], delta_bias=bias,
+                      softplus=True)
+        assert np.allclose(y[0], want[:, t], rtol=1e-14, atol=1e-15), (t, y, want[:, t])
+
+
+def pin_softplus_limits(o):
+    """softplus(v) -> v for large v and -> e^v for very negative v: a scan
+    with v = 40 equals the plain scan with Delta = 40, and v = -40 the plain
+    scan with Delta = e^-40 (to 1e-15 of the magnitude)."""
+    p = _rand_problem(91, Bsz=1, D=2, L=12, N=3)
+    bias = np.array([0.75, -1.5])
+    for vv, dl in ((40.0, 40.0), (-40.0, math.exp(-40.0))):
+        raw = np.full_like(p["delta"], vv) - bias[None, :, None]
+        got = o.scan(**dict(p, delta=raw), delta_bias=bias, softplus=True)
+        ref = o.scan(**dict(p, delta=np.full_like(p["delta"], dl)))
+        assert np.max(np.abs(got["y"] - ref["y"]) / ref["m"]) < 1e-15, vv
+
+
+def pin_zoh_hand(o):
+    """Exact zero-order hold of the input term (§2.3): scalar, two-state and
+    A = 0 cases worked by hand in tests/golden/zoh_hand.txt; scan and decode
+    steps."""
+    g = _read_golden("zoh_hand.txt")
+    ln2 = math.log(2.0)
+    x = np.array([[g["x"]]])
+    L = x.shape[-1]
+    ones = np.ones((1, 1, L))
+    cases = [
+        (x, np.full_like(x, ln2), np.array([[-1.0]]), ones, ones, g["case1 y"]),
+        (np.array([[[1.0, 0.0, 0.0, 0.0]]]), np.full_like(x, ln2), np.array([[-1.0, -2.0]]),
+         np.ones((1, 2, L)), np.array([[[1.0] * L, [-1.0] * L]]), g["case2 y"]),
+        (x, np.full_like(x, 0.25), np.array([[0.0]]), ones, ones, g["case3 y"]),
+    ]
+    for xc, dl, A, Bm, Cm, want in cases:
+        r = o.scan(xc, dl, A, Bm, Cm, zoh=True)
+        assert np.allclose(r["y"][0, 0], want, rtol=1e-15, atol=1e-15), (r["y"], want)
+        N = A.shape[1]
+        h = np.zeros((1, 1, N))
+        H = np.zeros((1, 1, N))
+        for t in range(L):
+            y, _ = o.step(h, H, xc[..., t], dl[..., t], A, Bm[..., t], Cm[..., t], zoh=True)
+            assert abs(y[0, 0] - want[t]) <= 1e-15, (t, y, want[t])
+
+
+def pin_zoh_limits(o):
+    """Exact hold against its limits: |Delta A| -> 0 gives the plain step
+    Delta B (relative gap about |Delta A| / 2); Delta |A| -> infinity gives
+    the coefficient 1 / |A|, so one token from h = 0 leaves h = B x / |A|."""
+    p = _rand_problem(92, Bsz=1, D=2, L=20, N=3, h0=False, gate=False)
+    tiny = dict(p, A=-np.full_like(p["A"], 1e-9))
+    a = o.scan(**tiny, zoh=True)
+    b = o.scan(**tiny)
+    assert np.max(np.abs(a["y"] - b["y"]) / b["m"]) < 1e-9
+    A = -np.array([[2.0, 5.0, 0.5], [1.0, 4.0, 8.0]])
+    x = p["x"][..., :1]
+    Bm = p["Bm"][..., :1]
+    r = o.scan(x, np.full_like(x, 200.0), A, Bm, np.ones_like(Bm), zoh=True)
+    want = Bm[0, None, :, 0] * x[0, :, 0, None] / np.abs(A)
+    assert np.allclose(r["h_last"][0], want, rtol=1e-15, atol=0), (r["h_last"], want)
+
+
+def brute_force_options(p, dps=30):
+    """Materialised form with both options, in multi-digit arithmetic: the
+    step Delta = ln(1 + e^(delta + bias)) straight from the definition, and
+    the input coefficient as the hold integral of exp(s A) over [0, Delta]
+    by numerical quadrature (not the closed form).  Otherwise as
+    brute_force_y."""
+    import mpmath as mp
+    mp.mp.dps = dps
+    x, raw, A, Bm, Cm, bias = p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["delta_bias"]
+    Bsz, D, L = x.shape
+    N = A.shape[1]
+    out = np.zeros((Bsz, D, L))
+    for b in range(Bsz):
+        for d in range(D):
+            dl = [mp.log(1 + mp.exp(mp.mpf(float(raw[b, d, t])) + mp.mpf(float(bias[d])))) for t in range(L)]
+            cum = [mp.mpf(0)]
+            for t in range(L):
+                cum.append(cum[-1] + dl[t])
+            hold = [[mp.quad(lambda s, An=mp.mpf(float(A[d, n])): mp.exp(s * An), [0, dl[t]])
+                     for n in range(N)] for t in range(L)]
+            for t in range(L):
+                acc = mp.mpf(0)
+                for n in range(N):
+                    An = mp.mpf(float(A[d, n]))
+                    Ct = mp.mpf(float(Cm[b, n, t]))
+                    for s in range(t + 1):
+                        acc += Ct * mp.exp(An * (cum[t + 1] - cum[s + 1])) * hold[s][n] \
+                            * mp.mpf(float(Bm[b, n, s])) * mp.mpf(float(x[b, d, s]))
+                    if p.get("h0") is not None:
+                        acc += Ct * mp.exp(An * cum[t + 1]) * mp.mpf(float(p["h0"][b, d, n]))
+                if p.get("Dskip") is not None:
+                    acc += mp.mpf(float(p["Dskip"][d])) * mp.mpf(float(x[b, d, t]))
+                if p.get("z") is not None:
+                    zz = mp.mpf(float(p["z"][b, d, t]))
+                    acc *= zz / (1 + mp.exp(-zz))
+                out[b, d, t] = float(acc)
+    return out
+
+
+def pin_options_brute_force(o):
+    """Softplus step with bias and exact hold together, against the
+    quadrature-based materialised form, on tiny random problems with
+    time-varying delta, B, C, an initial state and a gate."""
+    for seed in (93, 94):
+        p = _rand_problem(seed, Bsz=1, D=2, L=10, N=3)
+        g = _rng(seed + 100)
+        p["delta"] = g.normal(-2.0, 1.5, size=p["delta"].shape)  # raw values, any sign
+        p["delta_bias"] = g.normal(0.0, 1.0, size=p["x"].shape[1])
+        r = o.scan(**p, softplus=True, zoh=True)
+        want = brute_force_options(p)
+        err = np.max(np.abs(r["y"] - want) / r["m"])
+        assert err < 1e-13, (seed, err)
+
+
 PINS = [pin_zero_step_hand, pin_scalar_hand, pin_lti_convolution, pin_step_response,
         pin_brute_force, pin_tree_scan, pin_split_resume, pin_linearity_and_permutation,
-        pin_gate_limits, pin_decode_equals_scan, pin_magnitude_bounds]
+        pin_gate_limits, pin_decode_equals_scan, pin_magnitude_bounds, pin_softplus_hand,
+        pin_softplus_limits, pin_zoh_hand, pin_zoh_limits, pin_options_brute_force]

@@ -21,17 +21,27 @@ MUTANTS = [
         ("acc += Ct[n * bstride] * h[n];      /* ... then read the output from the new state */",
          "acc += Ct[n * bstride] * hp_;")]),
     ("B_C_swapped", [
-        ("double bx = dt * Bt[n * bstride] * xt;", "double bx = dt * Ct[n * bstride] * xt;"),
+        ("* Bt[n * bstride] * xt;", "* Ct[n * bstride] * xt;"),
         ("acc += Ct[n * bstride] * h[n];      /*", "acc += Bt[n * bstride] * h[n];      /*")]),
     ("exp_sign", [("exp(dt * Ad[n])", "exp(-dt * Ad[n])")]),
-    ("dt_dropped_from_input", [("double bx = dt * Bt[n * bstride] * xt;",
-                                "double bx = Bt[n * bstride] * xt;")]),
+    ("dt_dropped_from_input", [("(zoh ? zoh_coef(dt, Ad[n]) : dt) * Bt",
+                                "(zoh ? zoh_coef(dt, Ad[n]) : 1.0) * Bt")]),
     ("gate_before_skip", [("        yt *= g;\n        mag *= fabs(g);\n      }\n      y[p * L + t] = yt;",
                            "        yt = (yt - dsk * x[p * L + t]) * g + dsk * x[p * L + t];\n"
                            "        mag *= fabs(g);\n      }\n      y[p * L + t] = yt;")]),
     ("h0_ignored", [("h[n] = h0 ? h0[p * N + n] : 0.0;", "h[n] = 0.0;")]),
-    ("exact_zoh_for_B", [("double bx = dt * Bt[n * bstride] * xt;",
-                          "double bx = (Ad[n] != 0.0 ? (a - 1.0) / Ad[n] : dt) * Bt[n * bstride] * xt;")]),
+    ("exact_zoh_for_B", [("(zoh ? zoh_coef(dt, Ad[n]) : dt) * Bt", "zoh_coef(dt, Ad[n]) * Bt")]),
+    ("zoh_never", [("(zoh ? zoh_coef(dt, Ad[n]) : dt) * Bt", "dt * Bt")]),
+    ("zoh_sign", [("return a != 0.0 ? expm1(dt * a) / a : dt;", "return a != 0.0 ? -expm1(dt * a) / a : dt;")]),
+    ("zoh_extra_step", [("return a != 0.0 ? expm1(dt * a) / a : dt;",
+                         "return a != 0.0 ? dt * expm1(dt * a) / a : dt;")]),
+    ("zoh_limit_at_zero", [("return a != 0.0 ? expm1(dt * a) / a : dt;", "return a != 0.0 ? expm1(dt * a) / a : 0.0;")]),
+    ("softplus_no_abs", [("log1p(exp(-fabs(v)))", "log1p(exp(-v))")]),
+    ("softplus_is_exp", [("return (v > 0.0 ? v : 0.0) + log1p(exp(-fabs(v)));", "return exp(v);")]),
+    ("softplus_bias_dropped", [("return softplus(raw + (dbias ? dbias[d] : 0.0));", "return softplus(raw);")]),
+    ("softplus_bias_channel", [("dbias ? dbias[d] : 0.0", "dbias ? dbias[0] : 0.0")]),
+    ("softplus_bias_after", [("return softplus(raw + (dbias ? dbias[d] : 0.0));",
+                              "return softplus(raw) + (dbias ? dbias[d] : 0.0);")]),
     ("delta_index_shift", [("delta[p * L + t]", "delta[p * L + (t > 0 ? t - 1 : 0)]")]),
     ("A_state_index", [("exp(dt * Ad[n])", "exp(dt * Ad[(n + 1) % N])")]),
     ("B_batch_index", [("const double* Bb = Bm + b * N * L;", "const double* Bb = Bm;")]),
