@@ -90,10 +90,12 @@ def decode_step_bytes(batch, dim, N, in_bytes, gate=True):
     return batch * dim * per + 2 * batch * N * in_bytes + 4 * dim * N + 4 * dim
 
 
-def bench_scan(w, steps, warmup, flush=False):
+def bench_scan(w, steps, warmup, flush=False, softplus=False, zoh=False):
     """Times `steps` scans of workload w (after `warmup`).  flush: before each
     timed scan, write a 512 MiB buffer so that no input is cache-resident,
-    and time each scan on its own."""
+    and time each scan on its own.  softplus / zoh: time the option kernels
+    (the stored delta is then the softplus argument, with a bias of -4 per
+    channel; the timing does not depend on the values)."""
     import torch
     from selective_state_space_63_amd import s6, synth
     inp = synth.device_full(w)
@@ -101,10 +103,14 @@ def bench_scan(w, steps, warmup, flush=False):
         return inp, bench_scan_flushed(w, inp, steps, warmup), None
     y = torch.empty((w.batch, w.dim, w.seqlen), device="cuda", dtype=torch.float32)
     hl = torch.empty((w.batch, w.dim, w.dstate), device="cuda", dtype=torch.float32)
+    opts = {}
+    if softplus or zoh:
+        opts = dict(delta_bias=torch.full((w.dim,), -4.0, device="cuda", dtype=torch.float32) if softplus else None,
+                    delta_softplus=softplus, zoh=zoh)
 
     def step():
         s6.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], D=inp["Dskip"], z=inp["z"],
-                    return_last_state=True, y=y, h_last=hl)
+                    return_last_state=True, y=y, h_last=hl, **opts)
 
     for _ in range(warmup):
         step()
@@ -458,6 +464,13 @@ def main():
         _, tc, _ = bench_scan(wm, 20, 2, flush=True)
         out["m130_hot"] = scan_line("m130", wm, th, 2, "repeated; inputs stay in the 256 MB Infinity Cache", True)
         out["m130_cold"] = scan_line("m130", wm, tc, 2, "a 512 MiB write between scans evicts the inputs", False)
+        torch.cuda.empty_cache()
+        print(f"[bench] scan {w.name} with the step options", file=sys.stderr, flush=True)
+        _, ts, _ = bench_scan(w, 50, 50, softplus=True)
+        out["softplus"] = scan_line("softplus", w, ts, in_bytes, "step softplus(delta + bias) in the kernel", True)
+        _, tz, _ = bench_scan(w, 50, 50, softplus=True, zoh=True)
+        out["softplus_zoh"] = scan_line("softplus_zoh", w, tz, in_bytes,
+                                        "softplus step and exact zero-order-hold input term", True)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

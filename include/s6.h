@@ -75,6 +75,11 @@ extern "C" {
 #define S6_ERR_UNSUPPORTED (-4) /* dstate outside 1..32 */
 #define S6_ERR_ALIGN (-5)       /* a pointer is not aligned to its element size */
 #define S6_ERR_HIP (-6)         /* a HIP call failed; s6_status_str gives the detail */
+#define S6_ERR_FLAGS (-7)       /* unknown bits in the flags of an _ex entry point */
+
+/* Options of the _ex entry points (bit flags). */
+#define S6_DELTA_SOFTPLUS 1 /* step = softplus(delta + delta_bias[d]) */
+#define S6_ZOH_EXACT 2      /* input term (exp(step*A) - 1) / A * B * x */
 
 /* Version of this ABI, major*10000 + minor*100 + patch. */
 int s6_version(void);
@@ -113,6 +118,35 @@ int s6_last_state(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
 int s6_state_update(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, float* h,
                     const void* x, const void* delta, const float* A, const void* Bm,
                     const void* Cm, const float* Dskip, const void* z, float* y, void* stream);
+
+/* The same three operations with a per-channel step bias and the
+ * discretisation options.  §3.2 of the guide makes Delta learned and
+ * input-dependent without saying how it stays positive, and §2.3 names the
+ * zero-order hold without its formula (the image is missing):
+ *   delta_bias : nullable (dim) fp32; the step is delta[b,d,t] + delta_bias[d].
+ *   S6_DELTA_SOFTPLUS : the step is softplus(delta + delta_bias[d]),
+ *       softplus(v) = ln(1 + e^v), computed in fp32 as the delta tile is
+ *       staged.
+ *   S6_ZOH_EXACT : the input term is held over the step as well as the
+ *       state: h[n] = exp(s*A[d,n]) * h[n] + (exp(s*A[d,n]) - 1) / A[d,n] *
+ *       Bm[b,n,t] * x[b,d,t] for the step s (s * Bm * x where A[d,n] = 0),
+ *       instead of s * Bm * x.
+ * flags = 0 and delta_bias = NULL give exactly s6_scan_fwd, s6_last_state
+ * and s6_state_update.  Other flag bits: S6_ERR_FLAGS.  delta_bias must be
+ * 4-byte aligned.  Everything else is as for the plain entry points. */
+int s6_scan_fwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                   const void* x, const void* delta, const float* delta_bias, int flags,
+                   const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                   const float* h0, float* y, float* h_last, void* stream);
+
+int s6_last_state_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                     const void* x, const void* delta, const float* delta_bias, int flags,
+                     const float* A, const void* Bm, const float* h0, float* h_last, void* stream);
+
+int s6_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, float* h,
+                       const void* x, const void* delta, const float* delta_bias, int flags,
+                       const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                       const void* z, float* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -85,9 +85,9 @@ class Oracle:
     def scan(self, x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_bias=None,
              softplus=False, zoh=False):
         """Full scan.  x, delta, z: (batch, D, L); Bm, Cm: (batch, N, L);
-        A: (D, N); Dskip: (D,); h0: (batch, D, N); delta_bias: (D,).
-        softplus: the step is softplus(delta + delta_bias); zoh: exact
-        zero-order-hold input coefficient (exp(Delta A) - 1) / A.  Returns a
+        A: (D, N); Dskip: (D,); h0: (batch, D, N); delta_bias: (D,), added
+        to delta.  softplus: the step is softplus(delta + delta_bias); zoh:
+        exact zero-order-hold input coefficient (exp(Delta A) - 1) / A.  Returns a
         dict with y and m (batch, D, L), h_last and H_last (batch, D, N), all
         fp64."""
         x = np.asarray(x)

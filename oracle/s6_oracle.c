@@ -29,12 +29,13 @@
  *   A : (D, N)        Dskip : (D)        h0, h_last, H_last : (Bsz, D, N)
  *   decode step: x, delta, z, y, m : (Bsz, D); Bm, Cm : (Bsz, N)
  *
- * Discretisation options (oracle_scan_ex, oracle_step_ex; bit flags):
- *   ORACLE_DELTA_SOFTPLUS  the step is softplus(delta + delta_bias[d]) rather
- *     than delta itself.  The pages make Delta learnable and input-dependent
- *     (§3.2) but do not say how it is kept positive; softplus,
- *     ln(1 + e^v), with a per-channel bias is the plain reading of the
- *     Mamba layer this guide describes.
+ Step bias and discretisation options (oracle_scan_ex, oracle_step_ex):
+ *   delta_bias (D), nullable: the step is delta + delta_bias[d].
+ *   ORACLE_DELTA_SOFTPLUS (bit flag): the step is softplus(delta + bias),
+ *     softplus(v) = ln(1 + e^v).  The pages make Delta learnable and
+ *     input-dependent (§3.2) but do not say how it is kept positive; a
+ *     per-channel bias and softplus are the plain reading of the Mamba layer
+ *     this guide describes.
  *   ORACLE_ZOH_EXACT  the input coefficient is the zero-order-hold integral
  *     of exp(s A) over s in [0, Delta], i.e. (exp(Delta A) - 1) / A (its
  *     limit at A = 0 is Delta), in place of Delta: the hold the pages name
@@ -71,10 +72,10 @@ enum { ORACLE_DELTA_SOFTPLUS = 1, ORACLE_ZOH_EXACT = 2 };
  * no exponential overflows (the two forms are equal for every v). */
 static double softplus(double v) { return (v > 0.0 ? v : 0.0) + log1p(exp(-fabs(v))); }
 
-/* The step Delta of pair (batch b, channel d) for a stored delta value. */
+/* The step Delta of channel d for a stored delta value. */
 static double step_of(double raw, const double* dbias, int64_t d, int flags) {
-  if (!(flags & ORACLE_DELTA_SOFTPLUS)) return raw;
-  return softplus(raw + (dbias ? dbias[d] : 0.0));
+  double v = dbias ? raw + dbias[d] : raw;
+  return (flags & ORACLE_DELTA_SOFTPLUS) ? softplus(v) : v;
 }
 
 /* Zero-order-hold input coefficient: integral of exp(s a) ds over [0, dt],
@@ -105,7 +106,7 @@ static double step_channel(int64_t N, double* h, double* H, const double* Ad, do
 
 /* Whole sequence.  Dskip, z and h0 may be NULL (no skip, no gate, zero
  * initial state).  m, h_last and H_last may be NULL (not written).
- * dbias (D) may be NULL (zero bias); flags: ORACLE_* above.
+ * dbias (D) may be NULL (no bias); flags: ORACLE_* above.
  * N must not exceed 256. */
 void oracle_scan_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x,
                     const double* delta, const double* dbias, int flags, const double* A,

@@ -56,6 +56,7 @@
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kCW = 32;            // channels per workgroup
 constexpr int kT = 16;             // tokens per chunk
 constexpr int kP = kT;             // LDS tile pitch in floats (channel-major [c][t], swizzled)
@@ -76,6 +77,29 @@ __device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcp
 
 // SiLU(z) = z / (1 + e^-z) = z * rcp(1 + 2^(-z*log2 e))
 __device__ __forceinline__ float silu(float z) { return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e)); }
+
+// softplus(v) = ln(1 + e^v) = max(v, 0) + ln(1 + w) with w = e^-|v| in (0, 1].
+// ln(1 + w) is taken as w ln(u) / (u - 1) with u = 1 + w as rounded (Kahan's
+// log1p): the rounding of u cancels between the two factors, so small w keep
+// full relative accuracy.  u == 1 (w below 2^-24) gives w itself.
+__device__ __forceinline__ float softplus_f(float v) {
+  const float w = fast_exp2(-fabsf(v) * kLog2e);
+  const float u = 1.0f + w;
+  const float l = w * (__builtin_amdgcn_logf(u) * kLn2) * fast_rcp(u - 1.0f);
+  return fmaxf(v, 0.0f) + (u == 1.0f ? w : l);
+}
+
+// Exact zero-order-hold input coefficient (e^(delta A) - 1) / A, the integral
+// of e^(s A) over s in [0, delta], given arg = delta A log2(e) and e = 2^arg
+// as computed for the state transition.  Taken as delta (e - 1) / ln(e) from
+// the rounded e itself (Kahan's expm1), so the coefficient keeps full relative
+// accuracy as delta A -> 0; e == 1 gives the limit delta.  Below 2^-64,
+// e - 1 = -1 in fp32 and log2(e) is taken as arg (no underflow to 0).
+__device__ __forceinline__ float zoh_coef(float dl, float arg, float e) {
+  const float lg = arg < -64.0f ? arg : __builtin_amdgcn_logf(e);
+  const float c = (e - 1.0f) * (dl * kLog2e) * fast_rcp(lg);
+  return e == 1.0f ? dl : c;
+}
 
 // Value of lane J of this lane's 16-lane row (DPP row_newbcast).  Used as an
 // operand of a multiply, the compiler folds it into v_mul_f32_dpp.
@@ -106,6 +130,10 @@ struct ScanArgs {
   float* y;               // kModeY output
   float* hout;            // final states or null
   float* sumdelta;        // kModeState: per-segment sum of delta (S, batch, D) or null
+  const float* dbias;     // (D) bias of the softplus step, or null (zero)
+  int softplus;           // step = softplus(delta + dbias[d])  (option kernels only; the
+                          // bias alone is added without it)
+  int zoh;                // exact zero-order-hold input coefficient (option kernels only)
   int64_t D, L, N;
   int64_t seg_len;        // tokens per segment (multiple of 4 kT); segment = blockIdx.z
   int64_t hinit_stride;   // elements between segments in hinit (0: same for all)
@@ -172,6 +200,23 @@ __device__ __forceinline__ void bcast_inputs(float bc, const float (&u)[4], floa
       : "v"(bc), "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]));
 }
 
+// Input terms with a coefficient per state: bx[t][m] = bc[lane 4m + t] * v[t][m].
+__device__ __forceinline__ void bcast_inputs2(float bc, const float (&v)[4][2], float (&bx)[4][2]) {
+  asm("s_nop 1\n\t"
+      "v_mul_f32_dpp %0, %8, %9 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %8, %10 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %2, %8, %11 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %3, %8, %12 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %4, %8, %13 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %5, %8, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %6, %8, %15 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %7, %8, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf"
+      : "=&v"(bx[0][0]), "=&v"(bx[0][1]), "=&v"(bx[1][0]), "=&v"(bx[1][1]), "=&v"(bx[2][0]),
+        "=&v"(bx[2][1]), "=&v"(bx[3][0]), "=&v"(bx[3][1])
+      : "v"(bc), "v"(v[0][0]), "v"(v[0][1]), "v"(v[1][0]), "v"(v[1][1]), "v"(v[2][0]), "v"(v[2][1]),
+        "v"(v[3][0]), "v"(v[3][1]));
+}
+
 // Output terms: p[t] = bc[lane 8 + t] * hs[t][0] + bc[lane 12 + t] * hs[t][1].
 __device__ __forceinline__ void bcast_outputs(float bc, const float (&hs)[4][2], float (&p)[4]) {
   asm("s_nop 1\n\t"
@@ -207,19 +252,33 @@ __device__ __forceinline__ float pair_rows(float even_tok, float odd_tok) {
 // so every result is consumed well after it is produced.  On return
 // ys[0], ys[1] hold the channel's output sums over this wave's 4 states for
 // tokens 2*0 + r and 2*1 + r of the group (r = row parity), i.e. the two
-// state pairs of the channel are added across rows.
-template <int MODE>
+// state pairs of the channel are added across rows.  EXT kernels take the
+// exact zero-order-hold input coefficient when `zoh` is set.
+template <int MODE, bool EXT>
 __device__ __forceinline__ void token_group(const float* dl, const float* xv, const float (&A2)[2],
-                                            float (&h)[2], float bc, float (&ys)[2]) {
-  float e[4][2], bx[4][2], u[4];
+                                            float (&h)[2], float bc, bool zoh, float (&ys)[2]) {
+  float e[4][2], bx[4][2], arg[4][2];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    e[t][0] = fast_exp2(dl[t] * A2[0]);
-    e[t][1] = fast_exp2(dl[t] * A2[1]);
+    arg[t][0] = dl[t] * A2[0];
+    arg[t][1] = dl[t] * A2[1];
+    e[t][0] = fast_exp2(arg[t][0]);
+    e[t][1] = fast_exp2(arg[t][1]);
   }
+  if (EXT && zoh) {
+    float v[4][2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) u[t] = dl[t] * xv[t];
-  bcast_inputs(bc, u, bx);
+    for (int t = 0; t < 4; ++t) {
+      v[t][0] = zoh_coef(dl[t], arg[t][0], e[t][0]) * xv[t];
+      v[t][1] = zoh_coef(dl[t], arg[t][1], e[t][1]) * xv[t];
+    }
+    bcast_inputs2(bc, v, bx);
+  } else {
+    float u[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) u[t] = dl[t] * xv[t];
+    bcast_inputs(bc, u, bx);
+  }
   float hs[4][2];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -251,8 +310,14 @@ __device__ __forceinline__ void token_group(const float* dl, const float* xv, co
 // is written with per-piece masking (delta = 0 past the end keeps the
 // state), and only a window that would cross the end of the rows clamps its
 // piece addresses.
-template <typename In, int VEC, bool GATE, int MODE, int W, int WIN>
-__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ? 5 : 1)))
+//
+// EXT kernels also take the step bias and discretisation options of ScanArgs:
+// the bias and softplus are applied to delta while it is staged (once per
+// element), the exact hold in the token groups, and the
+// kind of piece each wave stages rotates with the workgroup index so that
+// this extra work falls on every SIMD alike.
+template <typename In, int VEC, bool GATE, int MODE, int W, int WIN, bool EXT>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ? (EXT ? 4 : 5) : 1)))
 s6_scan_kernel(ScanArgs a) {
   constexpr int NTHR = 64 * W;
   constexpr int NTS = (MODE == kModeY && GATE) ? 3 : 2;  // staged tensors: x, delta (, z)
@@ -329,9 +394,15 @@ s6_scan_kernel(ScanArgs a) {
   int scol[SLOTS];       // first token of the piece within a chunk
   int srow[SLOTS];       // row within its tensor (channel or state)
   int skind[SLOTS];      // 0..NTS-1: x, delta, z; NTS + m: B (m = 0) or C (m = 1); -1: idle
+  float sbias[SLOTS];    // EXT: softplus bias of the piece's channel
+  const bool softplus = EXT && a.softplus;
+  const bool dstep = EXT && (a.softplus || a.dbias);  // delta is rewritten while staged
+  const bool zoh = EXT && a.zoh;
+  const int rot = EXT ? (int)(blockIdx.x % W) * 64 : 0;
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
-    int p = tid + s * NTHR;
+    int p = ((tid + rot) & (NTHR - 1)) + s * NTHR;
+    sbias[s] = 0.0f;
     const bool idle = p >= CP::kTotal;
     if (idle) p = 0;  // idle slot: loads piece 0, never writes
     if (p < CP::kTens) {
@@ -343,6 +414,7 @@ s6_scan_kernel(ScanArgs a) {
       srow[s] = row;
       scol[s] = (q - row * CP::PPC) * VEC;
       sptr[s] = src[k] + (row0 + rowc) * L + scol[s];
+      if (EXT && k == 1 && a.dbias) sbias[s] = a.dbias[d0 + rowc];
     } else {
       const int q = p - CP::kTens;
       const int m = q / (CP::kRowsBC * CP::PPC);
@@ -404,7 +476,25 @@ s6_scan_kernel(ScanArgs a) {
       if (skind[s] < 0) continue;
       const bool ok = !MASK || t0c + col < te;
       const In* e = reinterpret_cast<const In*>(&src_[s]);
-      if (skind[s] < 2) {
+      if (dstep && skind[s] == 1) {
+        // step = delta + bias, then softplus if asked; masked tokens stay 0
+        float* tile = tiles + (buf * 2 + 1) * TILE;
+        float v[VEC];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) v[k] = to_f32(e[k]) + sbias[s];
+        if (softplus) {
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) v[k] = softplus_f(v[k]);
+        }
+        if constexpr (VEC == 1) {
+          tile[tsw(srow[s], col >> 2) + (col & 3)] = ok ? v[0] : 0.0f;
+        } else {
+#pragma unroll
+          for (int k = 0; k < VEC; k += 4)
+            *reinterpret_cast<float4*>(tile + tsw(srow[s], (col + k) >> 2)) =
+                ok ? make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      } else if (skind[s] < 2) {
         float* tile = tiles + (buf * 2 + skind[s]) * TILE;
         if constexpr (VEC == 1) {
           tile[tsw(srow[s], col >> 2) + (col & 3)] = ok ? to_f32(e[0]) : 0.0f;
@@ -493,7 +583,7 @@ s6_scan_kernel(ScanArgs a) {
       const float xv[4] = {xx.x, xx.y, xx.z, xx.w};
       const float bc = bcs[buf * BCL::kFloats + BCL::pos(g, w, r, lane & 15)];
       float ys[2];
-      token_group<MODE>(dl, xv, A2, h, bc, ys);
+      token_group<MODE, EXT>(dl, xv, A2, h, bc, zoh, ys);
       ysum[2 * g] = ys[0];
       ysum[2 * g + 1] = ys[1];
       if constexpr (MODE == kModeState) cs += (dl[0] + dl[1]) + (dl[2] + dl[3]);
@@ -629,6 +719,9 @@ struct StepArgs {
   const void* Cm;
   const float* Dskip;
   float* y;
+  const float* dbias;  // (D) step bias or null
+  int softplus;        // step = softplus(delta + dbias[d])
+  int zoh;             // exact zero-order-hold input coefficient
   int64_t batch, D, N;
 };
 
@@ -640,7 +733,7 @@ struct StepArgs {
 // 16- or 8-byte loads.  The step's B and C rows are the same for every
 // channel of a batch row and stay in cache; h is streamed once in and once
 // out.
-template <typename In, bool GATE, int P, int SPL, bool VEC, int G>
+template <typename In, bool GATE, int P, int SPL, bool VEC, int G, bool EXT>
 __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
   static_assert(!VEC || (SPL * sizeof(In)) % 8 == 0, "8- or 16-byte pieces of B and C");
   static_assert(P == 1 || P == 2 || P == 4, "lanes per channel");
@@ -676,6 +769,7 @@ __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
     for (int j = 0; j < SPL; ++j) A2[j] = (valid && n0 + j < N) ? arow[j] * kLog2e : 0.0f;
   }
   const float dsk = (a.Dskip && valid) ? a.Dskip[d] : 0.0f;
+  const float dbias = (EXT && a.dbias && valid) ? a.dbias[d] : 0.0f;
 
   // loads of all G rows
   bool vb[G];
@@ -732,13 +826,27 @@ __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
         Cv[j] = sv ? to_f32(Cp[bb * N + n0 + j]) : 0.0f;
       }
     }
-    const float u = dt[g] * xt[g];
+    // the step: delta, plus the channel's bias, through softplus if asked
+    float dl = dt[g];
+    if (EXT && a.dbias) dl += dbias;
+    if (EXT && a.softplus) dl = softplus_f(dl);
     float yp = 0.0f;
+    if (EXT && a.zoh) {
 #pragma unroll
-    for (int j = 0; j < SPL; ++j) {
-      const float e = fast_exp2(dt[g] * A2[j]);
-      hv[g][j] = __builtin_fmaf(e, hv[g][j], u * Bv[j]);
-      yp = __builtin_fmaf(Cv[j], hv[g][j], yp);
+      for (int j = 0; j < SPL; ++j) {
+        const float arg = dl * A2[j];
+        const float e = fast_exp2(arg);
+        hv[g][j] = __builtin_fmaf(e, hv[g][j], (zoh_coef(dl, arg, e) * xt[g]) * Bv[j]);
+        yp = __builtin_fmaf(Cv[j], hv[g][j], yp);
+      }
+    } else {
+      const float u = dl * xt[g];
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        const float e = fast_exp2(dl * A2[j]);
+        hv[g][j] = __builtin_fmaf(e, hv[g][j], u * Bv[j]);
+        yp = __builtin_fmaf(Cv[j], hv[g][j], yp);
+      }
     }
     float* hrow = a.h + ch * N + n0;
     if (vb[g]) {
@@ -854,7 +962,7 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, size_
   return p;
 }
 
-template <typename In, int VEC, bool GATE, int MODE, int W>
+template <typename In, int VEC, bool GATE, int MODE, int W, bool EXT>
 int launch_scan_t(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, hipStream_t st) {
   // 64-byte row runs per load: two chunks per window for bf16 vectors with
   // enough threads to hold them, one chunk otherwise.
@@ -864,54 +972,65 @@ int launch_scan_t(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, 
   if (MODE == kModeY) lds += (size_t)2 * W * 2 * kCW * (kT / 2) * sizeof(float);  // partials
   lds += (size_t)2 * BCLayout<W>::kFloats * sizeof(float);                     // B/C
   dim3 grid((unsigned)(nblk * batch), 1u, (unsigned)segs);
-  hipLaunchKernelGGL((s6_scan_kernel<In, VEC, GATE, MODE, W, WIN>), grid, dim3(64 * W), lds, st, a);
+  hipLaunchKernelGGL((s6_scan_kernel<In, VEC, GATE, MODE, W, WIN, EXT>), grid, dim3(64 * W), lds, st, a);
   S6_HIP(hipGetLastError(), "s6_scan_kernel launch");
   return S6_OK;
 }
 
-template <typename In, int MODE, int W>
+template <typename In, int MODE, int W, bool EXT>
 int launch_scan_w(const ScanArgs& a, bool vec, bool gate, int64_t batch, int64_t nblk, int64_t segs,
                   hipStream_t st) {
   constexpr int kV = 16 / sizeof(In);
   if constexpr (MODE == kModeY) {
-    if (vec && gate) return launch_scan_t<In, kV, true, MODE, W>(a, batch, nblk, segs, st);
-    if (vec) return launch_scan_t<In, kV, false, MODE, W>(a, batch, nblk, segs, st);
-    if (gate) return launch_scan_t<In, 1, true, MODE, W>(a, batch, nblk, segs, st);
-    return launch_scan_t<In, 1, false, MODE, W>(a, batch, nblk, segs, st);
+    if (vec && gate) return launch_scan_t<In, kV, true, MODE, W, EXT>(a, batch, nblk, segs, st);
+    if (vec) return launch_scan_t<In, kV, false, MODE, W, EXT>(a, batch, nblk, segs, st);
+    if (gate) return launch_scan_t<In, 1, true, MODE, W, EXT>(a, batch, nblk, segs, st);
+    return launch_scan_t<In, 1, false, MODE, W, EXT>(a, batch, nblk, segs, st);
   } else {
-    if (vec) return launch_scan_t<In, kV, false, MODE, W>(a, batch, nblk, segs, st);
-    return launch_scan_t<In, 1, false, MODE, W>(a, batch, nblk, segs, st);
+    if (vec) return launch_scan_t<In, kV, false, MODE, W, EXT>(a, batch, nblk, segs, st);
+    return launch_scan_t<In, 1, false, MODE, W, EXT>(a, batch, nblk, segs, st);
   }
 }
 
-template <typename In, int MODE>
+template <typename In, int MODE, bool EXT>
 int launch_scan(const ScanArgs& a, int W, bool vec, bool gate, int64_t batch, int64_t nblk, int64_t segs,
                 hipStream_t st) {
   switch (W) {
-    case 1: return launch_scan_w<In, MODE, 1>(a, vec, gate, batch, nblk, segs, st);
-    case 2: return launch_scan_w<In, MODE, 2>(a, vec, gate, batch, nblk, segs, st);
-    case 4: return launch_scan_w<In, MODE, 4>(a, vec, gate, batch, nblk, segs, st);
-    default: return launch_scan_w<In, MODE, 8>(a, vec, gate, batch, nblk, segs, st);
+    case 1: return launch_scan_w<In, MODE, 1, EXT>(a, vec, gate, batch, nblk, segs, st);
+    case 2: return launch_scan_w<In, MODE, 2, EXT>(a, vec, gate, batch, nblk, segs, st);
+    case 4: return launch_scan_w<In, MODE, 4, EXT>(a, vec, gate, batch, nblk, segs, st);
+    default: return launch_scan_w<In, MODE, 8, EXT>(a, vec, gate, batch, nblk, segs, st);
   }
 }
 
+template <bool EXT>
+int launch_scan_e(int in_dtype, int mode, const ScanArgs& a, const Plan& p, bool gate, int64_t batch,
+                  int64_t segs, hipStream_t st) {
+  if (in_dtype == S6_BF16) {
+    return mode == kModeY ? launch_scan<uint16_t, kModeY, EXT>(a, p.W, p.vec, gate, batch, p.nblk, segs, st)
+                          : launch_scan<uint16_t, kModeState, EXT>(a, p.W, p.vec, gate, batch, p.nblk, segs, st);
+  }
+  return mode == kModeY ? launch_scan<float, kModeY, EXT>(a, p.W, p.vec, gate, batch, p.nblk, segs, st)
+                        : launch_scan<float, kModeState, EXT>(a, p.W, p.vec, gate, batch, p.nblk, segs, st);
+}
+
+// Kernels with the discretisation options only when an option is set, so
+// the plain path keeps its own code.
 int launch_scan_any(int in_dtype, int mode, const ScanArgs& a, const Plan& p, bool gate, int64_t batch,
                     int64_t segs, hipStream_t st) {
-  if (in_dtype == S6_BF16) {
-    return mode == kModeY ? launch_scan<uint16_t, kModeY>(a, p.W, p.vec, gate, batch, p.nblk, segs, st)
-                          : launch_scan<uint16_t, kModeState>(a, p.W, p.vec, gate, batch, p.nblk, segs, st);
-  }
-  return mode == kModeY ? launch_scan<float, kModeY>(a, p.W, p.vec, gate, batch, p.nblk, segs, st)
-                        : launch_scan<float, kModeState>(a, p.W, p.vec, gate, batch, p.nblk, segs, st);
+  if (a.softplus || a.zoh || a.dbias) return launch_scan_e<true>(in_dtype, mode, a, p, gate, batch, segs, st);
+  return launch_scan_e<false>(in_dtype, mode, a, p, gate, batch, segs, st);
 }
 
-// Shared implementation of s6_scan_fwd (want_y) and s6_last_state.
+// Shared implementation of s6_scan_fwd(_ex) (want_y) and s6_last_state(_ex).
 int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
-              const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
-              const float* Dskip, const void* z, const float* h0, float* y, float* h_last,
-              void* stream) {
+              const void* x, const void* delta, const float* dbias, int flags, const float* A,
+              const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
+              float* y, float* h_last, void* stream) {
   int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
   if (rc) return rc;
+  if (flags & ~(S6_DELTA_SOFTPLUS | S6_ZOH_EXACT)) return S6_ERR_FLAGS;
+  if (dbias && !aligned(dbias, 4)) return S6_ERR_ALIGN;
   const bool work = batch > 0 && dim > 0 && seqlen > 0;
   if (work && (!x || !delta || !A || !Bm || (want_y && (!Cm || !y)))) return S6_ERR_NULL;
   if (!want_y && !h_last) return S6_ERR_NULL;
@@ -945,6 +1064,9 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
   memset(&a, 0, sizeof(a));
   a.x = x; a.delta = delta; a.z = gate ? z : nullptr; a.Bm = Bm; a.Cm = want_y ? Cm : nullptr;
   a.A = A; a.Dskip = want_y ? Dskip : nullptr;
+  a.softplus = (flags & S6_DELTA_SOFTPLUS) != 0;
+  a.zoh = (flags & S6_ZOH_EXACT) != 0;
+  a.dbias = dbias;
   a.D = dim; a.L = seqlen; a.N = dstate; a.seg_len = p.seg_len;
 
   if (S == 1) {
@@ -998,27 +1120,34 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
   return rc;
 }
 
-template <typename In, bool GATE, int P, int SPL, int G>
+template <typename In, bool GATE, int P, int SPL, int G, bool EXT>
 int launch_step_t(const StepArgs& a, bool vec, hipStream_t st) {
   const int64_t threads = ((a.batch + G - 1) / G) * a.D * P;
   const int64_t blocks = (threads + 255) / 256;
   if constexpr ((SPL * sizeof(In)) % 8 == 0) {
     if (vec) {
-      hipLaunchKernelGGL((s6_step_kernel<In, GATE, P, SPL, true, G>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((s6_step_kernel<In, GATE, P, SPL, true, G, EXT>), dim3((unsigned)blocks), dim3(256), 0, st, a);
       S6_HIP(hipGetLastError(), "s6_step_kernel launch");
       return S6_OK;
     }
   }
-  hipLaunchKernelGGL((s6_step_kernel<In, GATE, P, SPL, false, G>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((s6_step_kernel<In, GATE, P, SPL, false, G, EXT>), dim3((unsigned)blocks), dim3(256), 0, st, a);
   S6_HIP(hipGetLastError(), "s6_step_kernel launch");
   return S6_OK;
 }
 
 // Four batch rows per lane when that still leaves many lanes, else one.
+// Kernels with the step options only when an option is set.
+template <typename In, bool GATE, int P, int SPL, int G>
+int launch_step_e(const StepArgs& a, bool vec, hipStream_t st) {
+  if (a.dbias || a.softplus || a.zoh) return launch_step_t<In, GATE, P, SPL, G, true>(a, vec, st);
+  return launch_step_t<In, GATE, P, SPL, G, false>(a, vec, st);
+}
+
 template <typename In, bool GATE, int P, int SPL>
 int launch_step_b(const StepArgs& a, bool vec, hipStream_t st) {
-  if (a.batch >= 4 && a.batch * a.D * P >= 4 * 65536) return launch_step_t<In, GATE, P, SPL, 4>(a, vec, st);
-  return launch_step_t<In, GATE, P, SPL, 1>(a, vec, st);
+  if (a.batch >= 4 && a.batch * a.D * P >= 4 * 65536) return launch_step_e<In, GATE, P, SPL, 4>(a, vec, st);
+  return launch_step_e<In, GATE, P, SPL, 1>(a, vec, st);
 }
 
 // Lanes per channel: 4 states per lane (P = 1, 2, 4 for dstate <= 4, 8,
@@ -1043,7 +1172,7 @@ int launch_step_g(const StepArgs& a, hipStream_t st) {
 
 extern "C" {
 
-int s6_version(void) { return 10000; }
+int s6_version(void) { return 10100; }
 
 const char* s6_status_str(int status) {
   switch (status) {
@@ -1053,6 +1182,7 @@ const char* s6_status_str(int status) {
     case S6_ERR_DTYPE: return "in_dtype must be S6_F32 or S6_BF16";
     case S6_ERR_UNSUPPORTED: return "dstate must be between 1 and 32";
     case S6_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    case S6_ERR_FLAGS: return "unknown option bits in flags";
     case S6_ERR_HIP: return g_err[0] ? g_err : "HIP error";
     default: return "unknown status";
   }
@@ -1062,22 +1192,39 @@ int s6_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
                 const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
                 const float* Dskip, const void* z, const float* h0, float* y, float* h_last,
                 void* stream) {
-  return scan_impl(true, batch, dim, seqlen, dstate, in_dtype, x, delta, A, Bm, Cm, Dskip, z, h0, y,
-                   h_last, stream);
+  return scan_impl(true, batch, dim, seqlen, dstate, in_dtype, x, delta, nullptr, 0, A, Bm, Cm, Dskip,
+                   z, h0, y, h_last, stream);
+}
+
+int s6_scan_fwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                   const void* x, const void* delta, const float* delta_bias, int flags,
+                   const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                   const float* h0, float* y, float* h_last, void* stream) {
+  return scan_impl(true, batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm,
+                   Dskip, z, h0, y, h_last, stream);
 }
 
 int s6_last_state(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                   const void* x, const void* delta, const float* A, const void* Bm,
                   const float* h0, float* h_last, void* stream) {
-  return scan_impl(false, batch, dim, seqlen, dstate, in_dtype, x, delta, A, Bm, nullptr, nullptr,
-                   nullptr, h0, nullptr, h_last, stream);
+  return scan_impl(false, batch, dim, seqlen, dstate, in_dtype, x, delta, nullptr, 0, A, Bm, nullptr,
+                   nullptr, nullptr, h0, nullptr, h_last, stream);
 }
 
-int s6_state_update(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, float* h,
-                    const void* x, const void* delta, const float* A, const void* Bm,
-                    const void* Cm, const float* Dskip, const void* z, float* y, void* stream) {
+int s6_last_state_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                     const void* x, const void* delta, const float* delta_bias, int flags,
+                     const float* A, const void* Bm, const float* h0, float* h_last, void* stream) {
+  return scan_impl(false, batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm,
+                   nullptr, nullptr, nullptr, h0, nullptr, h_last, stream);
+}
+
+int s6_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, float* h,
+                       const void* x, const void* delta, const float* delta_bias, int flags,
+                       const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                       const void* z, float* y, void* stream) {
   int rc = check_common(batch, dim, 1, dstate, in_dtype);
   if (rc) return rc;
+  if (flags & ~(S6_DELTA_SOFTPLUS | S6_ZOH_EXACT)) return S6_ERR_FLAGS;
   // one thread per (batch, channel, 4 states) at most: the grid must fit
   if (batch * dim > (int64_t)INT32_MAX * 256 / 8) return S6_ERR_SHAPE;
   if (batch == 0 || dim == 0) return S6_OK;
@@ -1086,16 +1233,26 @@ int s6_state_update(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, fl
   const void* ins[] = {x, delta, Bm, Cm, z};
   for (const void* p : ins)
     if (p && !aligned(p, esz)) return S6_ERR_ALIGN;
-  const void* f32s[] = {h, A, Dskip, y};
+  const void* f32s[] = {h, A, Dskip, y, delta_bias};
   for (const void* p : f32s)
     if (p && !aligned(p, 4)) return S6_ERR_ALIGN;
   StepArgs a;
   a.h = h; a.x = x; a.delta = delta; a.z = z; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.y = y;
+  a.dbias = delta_bias;
+  a.softplus = (flags & S6_DELTA_SOFTPLUS) != 0;
+  a.zoh = (flags & S6_ZOH_EXACT) != 0;
   a.batch = batch; a.D = dim; a.N = dstate;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_dtype == S6_BF16)
     return z ? launch_step_g<uint16_t, true>(a, st) : launch_step_g<uint16_t, false>(a, st);
   return z ? launch_step_g<float, true>(a, st) : launch_step_g<float, false>(a, st);
+}
+
+int s6_state_update(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, float* h,
+                    const void* x, const void* delta, const float* A, const void* Bm,
+                    const void* Cm, const float* Dskip, const void* z, float* y, void* stream) {
+  return s6_state_update_ex(batch, dim, dstate, in_dtype, h, x, delta, nullptr, 0, A, Bm, Cm, Dskip, z,
+                            y, stream);
 }
 
 }  // extern "C"

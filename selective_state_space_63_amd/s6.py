@@ -16,6 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libs6.so")
 
 S6_F32, S6_BF16 = 0, 1
+S6_DELTA_SOFTPLUS, S6_ZOH_EXACT = 1, 2  # option bits of the _ex entry points
 _DT = {torch.float32: S6_F32, torch.bfloat16: S6_BF16}
 
 _lib = None
@@ -41,6 +42,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.s6_last_state.argtypes = [i64, i64, i64, i64, i32] + [vp] * 7
     lib.s6_state_update.restype = i32
     lib.s6_state_update.argtypes = [i64, i64, i64, i32] + [vp] * 10
+    lib.s6_scan_fwd_ex.restype = i32
+    lib.s6_scan_fwd_ex.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32] + [vp] * 9
+    lib.s6_last_state_ex.restype = i32
+    lib.s6_last_state_ex.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32] + [vp] * 5
+    lib.s6_state_update_ex.restype = i32
+    lib.s6_state_update_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, i32] + [vp] * 7
     if path is None:
         _lib = lib
     return lib
@@ -82,12 +89,21 @@ def _opt(t, name, shape, dtype=None):
     return None if t is None else _req(t, name, shape, dtype)
 
 
+def _options(delta_bias, delta_softplus, zoh, dim):
+    """(use the _ex entry point, flags) for the step bias and options."""
+    _opt(delta_bias, "delta_bias", (dim,), torch.float32)
+    flags = (S6_DELTA_SOFTPLUS if delta_softplus else 0) | (S6_ZOH_EXACT if zoh else 0)
+    return delta_bias is not None or flags != 0, flags
+
+
 def scan_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, return_last_state=False, y=None,
-             h_last=None):
+             h_last=None, delta_bias=None, delta_softplus=False, zoh=False):
     """Fused selective scan.  x, delta, z: (batch, dim, L); Bm, Cm: (batch, N, L);
     A: (dim, N) fp32; D: (dim,) fp32; h0: (batch, dim, N) fp32.  Inputs x,
-    delta, Bm, Cm, z share one dtype (float32 or bfloat16).  Returns y
-    (batch, dim, L) fp32, and h_last (batch, dim, N) fp32 if requested."""
+    delta, Bm, Cm, z share one dtype (float32 or bfloat16).  Options: the
+    step is delta + delta_bias ((dim,) fp32), through softplus if
+    delta_softplus; zoh takes the exact zero-order-hold input term.  Returns
+    y (batch, dim, L) fp32, and h_last (batch, dim, N) fp32 if requested."""
     bsz, dim, L = x.shape
     N = A.shape[1]
     dt = x.dtype
@@ -107,15 +123,22 @@ def scan_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, return_last_state=Fal
     if return_last_state and h_last is None:
         h_last = torch.empty((bsz, dim, N), dtype=torch.float32, device=x.device)
     _opt(h_last, "h_last", (bsz, dim, N), torch.float32)
-    rc = load_library().s6_scan_fwd(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
-                                    _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last),
-                                    _stream())
+    ex, flags = _options(delta_bias, delta_softplus, zoh, dim)
+    if ex:
+        rc = load_library().s6_scan_fwd_ex(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(delta_bias),
+                                           flags, _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0),
+                                           _ptr(y), _ptr(h_last), _stream())
+    else:
+        rc = load_library().s6_scan_fwd(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
+                                        _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last),
+                                        _stream())
     _check(rc)
     return (y, h_last) if return_last_state else y
 
 
-def last_state(x, delta, A, Bm, h0=None, out=None):
-    """Final state of the recurrence (no output sequence): (batch, dim, N) fp32."""
+def last_state(x, delta, A, Bm, h0=None, out=None, delta_bias=None, delta_softplus=False, zoh=False):
+    """Final state of the recurrence (no output sequence): (batch, dim, N)
+    fp32.  Options as in scan_fwd."""
     bsz, dim, L = x.shape
     N = A.shape[1]
     dt = x.dtype
@@ -129,15 +152,23 @@ def last_state(x, delta, A, Bm, h0=None, out=None):
     if out is None:
         out = torch.empty((bsz, dim, N), dtype=torch.float32, device=x.device)
     _req(out, "out", (bsz, dim, N), torch.float32)
-    rc = load_library().s6_last_state(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
-                                      _ptr(h0), _ptr(out), _stream())
+    ex, flags = _options(delta_bias, delta_softplus, zoh, dim)
+    if ex:
+        rc = load_library().s6_last_state_ex(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta),
+                                             _ptr(delta_bias), flags, _ptr(A), _ptr(Bm), _ptr(h0),
+                                             _ptr(out), _stream())
+    else:
+        rc = load_library().s6_last_state(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
+                                          _ptr(h0), _ptr(out), _stream())
     _check(rc)
     return out
 
 
-def state_update(h, x, delta, A, Bm, Cm, D=None, z=None, y=None):
+def state_update(h, x, delta, A, Bm, Cm, D=None, z=None, y=None, delta_bias=None,
+                 delta_softplus=False, zoh=False):
     """One decode token: h (batch, dim, N) fp32 is advanced in place; x, delta,
-    z: (batch, dim); Bm, Cm: (batch, N).  Returns y (batch, dim) fp32."""
+    z: (batch, dim); Bm, Cm: (batch, N); options as in scan_fwd.  Returns y
+    (batch, dim) fp32."""
     bsz, dim, N = h.shape
     dt = x.dtype
     if dt not in _DT:
@@ -153,7 +184,13 @@ def state_update(h, x, delta, A, Bm, Cm, D=None, z=None, y=None):
     if y is None:
         y = torch.empty((bsz, dim), dtype=torch.float32, device=x.device)
     _req(y, "y", (bsz, dim), torch.float32)
-    rc = load_library().s6_state_update(bsz, dim, N, _DT[dt], _ptr(h), _ptr(x), _ptr(delta), _ptr(A),
-                                        _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(y), _stream())
+    ex, flags = _options(delta_bias, delta_softplus, zoh, dim)
+    if ex:
+        rc = load_library().s6_state_update_ex(bsz, dim, N, _DT[dt], _ptr(h), _ptr(x), _ptr(delta),
+                                               _ptr(delta_bias), flags, _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D),
+                                               _ptr(z), _ptr(y), _stream())
+    else:
+        rc = load_library().s6_state_update(bsz, dim, N, _DT[dt], _ptr(h), _ptr(x), _ptr(delta), _ptr(A),
+                                            _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(y), _stream())
     _check(rc)
     return y

@@ -47,8 +47,8 @@ def codes():
 
 
 def test_header_declares_the_entry_points():
-    assert header_functions() == ["s6_last_state", "s6_scan_fwd", "s6_state_update",
-                                  "s6_status_str", "s6_version"]
+    assert header_functions() == ["s6_last_state", "s6_last_state_ex", "s6_scan_fwd", "s6_scan_fwd_ex",
+                                  "s6_state_update", "s6_state_update_ex", "s6_status_str", "s6_version"]
 
 
 def test_every_declared_symbol_is_exported():
@@ -60,7 +60,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings(lib, codes):
-    assert lib.s6_version() == 10000
+    assert lib.s6_version() == 10100
     for name, v in codes.items():
         if name.startswith("S6_ERR_") or name == "S6_OK":
             s = lib.s6_status_str(v).decode()
@@ -115,6 +115,37 @@ def test_state_update_validation(lib, codes):
     assert f(-2, 64, 16, 0, P, P, P, P, P, P, None, None, P, None) == codes["S6_ERR_SHAPE"]
     assert f(2, 0, 16, 0, P, P, P, P, P, P, None, None, P, None) == codes["S6_OK"]
     assert f(1 << 20, 1 << 20, 16, 0, P, P, P, P, P, P, None, None, P, None) == codes["S6_ERR_SHAPE"]
+
+
+def test_option_entry_points_validation(lib, codes):
+    """The _ex entry points: unknown flag bits, a misaligned bias, and the
+    plain checks, all before any HIP call."""
+    SP, ZOH = codes["S6_DELTA_SOFTPLUS"], codes["S6_ZOH_EXACT"]
+    assert (SP, ZOH) == (1, 2)
+
+    def scan_ex(flags=SP | ZOH, bias=P, b=2, n=16, dt=1, x=P, y=P):
+        return lib.s6_scan_fwd_ex(b, 64, 32, n, dt, x, P, bias, flags, P, P, P, None, None, None, y, None,
+                                  None)
+
+    assert scan_ex(flags=4) == codes["S6_ERR_FLAGS"]
+    assert scan_ex(flags=-1) == codes["S6_ERR_FLAGS"]
+    assert scan_ex(bias=P_ODD) == codes["S6_ERR_ALIGN"]
+    assert scan_ex(n=0) == codes["S6_ERR_UNSUPPORTED"]
+    assert scan_ex(dt=5) == codes["S6_ERR_DTYPE"]
+    assert scan_ex(x=None) == codes["S6_ERR_NULL"]
+    assert scan_ex(y=None) == codes["S6_ERR_NULL"]
+    assert scan_ex(b=0) == codes["S6_OK"]
+    assert scan_ex(b=0, bias=None, flags=0) == codes["S6_OK"]
+    f = lib.s6_last_state_ex
+    assert f(2, 64, 32, 16, 1, P, P, P, 8, P, P, None, P, None) == codes["S6_ERR_FLAGS"]
+    assert f(2, 64, 32, 16, 1, P, P, P_ODD, 1, P, P, None, P, None) == codes["S6_ERR_ALIGN"]
+    assert f(2, 64, 32, 16, 1, P, P, P, 1, P, P, None, None, None) == codes["S6_ERR_NULL"]
+    assert f(0, 64, 32, 16, 1, P, P, P, 3, P, P, None, P, None) == codes["S6_OK"]
+    g = lib.s6_state_update_ex
+    assert g(2, 64, 16, 0, P, P, P, P, 16, P, P, P, None, None, P, None) == codes["S6_ERR_FLAGS"]
+    assert g(2, 64, 16, 0, P, P, P, P_ODD, 1, P, P, P, None, None, P, None) == codes["S6_ERR_ALIGN"]
+    assert g(2, 64, 16, 0, None, P, P, P, 1, P, P, P, None, None, P, None) == codes["S6_ERR_NULL"]
+    assert g(2, 0, 16, 0, P, P, P, P, 3, P, P, P, None, None, P, None) == codes["S6_OK"]
 
 
 def test_binding_refuses_host_tensors():

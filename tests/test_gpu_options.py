@@ -1,0 +1,175 @@
+"""Parity of the step bias and discretisation options (the _ex entry points)
+against the fp64 oracle: bias alone, softplus(delta + bias), the exact
+zero-order-hold input term, and softplus with the exact hold, for the scan,
+the final-state scan and decode steps.  Same error metric and bars as
+test_gpu_parity.py.
+
+Inputs of the softplus cases follow the workloads' own recipe for the step,
+computed here in the kernel instead of on the host: the stored delta is
+0.5 * N(0, 1) and the bias of channel d is ln(expm1(u_d)) with u_d
+log-uniform in [1e-3, 0.1], so softplus(delta + bias) is the workloads'
+Delta distribution.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import TOL, dev, host64, problem, scaled  # noqa: E402
+from selective_state_space_63_amd import synth  # noqa: E402
+
+MODES = ["bias", "softplus", "zoh", "all"]
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_63_amd import s6
+    s6.load_library()
+    return torch
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def options_problem(w, mode, with_h0=True):
+    """Device tensors and oracle inputs of workload w with the stored delta
+    and bias of `mode`; returns (dev, oracle inputs, binding options, oracle
+    options)."""
+    d, o = problem(w, with_h0)
+    g = np.random.default_rng(w.seed + 7)
+    bias = None
+    if mode in ("softplus", "all"):
+        u = np.exp(g.uniform(np.log(1e-3), np.log(0.1), size=w.dim))
+        bias = np.log(np.expm1(u)).astype(np.float32)
+        raw = synth.encode(0.5 * g.standard_normal((w.batch, w.dim, w.seqlen)), w.dtype)
+        d["delta"] = dev(raw, w.dtype)
+        o["delta"] = synth.decode(raw, w.dtype)
+    elif mode == "bias":
+        bias = (0.004 * (1 + np.arange(w.dim) % 3)).astype(np.float32)
+    softplus = mode in ("softplus", "all")
+    zoh = mode in ("zoh", "all")
+    kw = dict(delta_bias=None if bias is None else dev(bias, synth.F32), delta_softplus=softplus, zoh=zoh)
+    okw = dict(delta_bias=None if bias is None else bias.astype(np.float64), softplus=softplus, zoh=zoh)
+    return d, o, kw, okw
+
+
+SHAPES = [
+    # batch, dim, N, L, dtype, gate
+    (1, 16, 4, 256, synth.F32, False),      # the fp32 workload's shape
+    (2, 65, 16, 100, synth.BF16, True),     # ragged channels, scalar path
+    (2, 96, 16, 40, synth.BF16, True),      # vector path of the bf16 layers
+    (1, 64, 16, 4096, synth.BF16, True),    # sequence cut into segments
+    (1, 63, 5, 65, synth.F32, True),        # dstate 5
+    (2, 40, 32, 48, synth.BF16, True),      # largest dstate
+    (3, 130, 16, 64, synth.F32, True),      # fp32 vector path
+]
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b{}_d{}_n{}_l{}_{}_{}".format(*s))
+def test_scan_options(torch_cuda, oracle, shape, mode):
+    from selective_state_space_63_amd import s6
+    b, dm, n, L, dt, gate = shape
+    w = synth.custom(b, dm, n, L, dt, gate, seed=3000 + L + dm)
+    _say(f"[case] scan options {mode} {w.name}")
+    d, o, kw, okw = options_problem(w, mode)
+    y, hl = s6.scan_fwd(d["x"], d["delta"], d["A"], d["Bm"], d["Cm"], D=d["D"], z=d["z"], h0=d["h0"],
+                        return_last_state=True, **kw)
+    torch_cuda.cuda.synchronize()
+    r = oracle.scan(**o, **okw)
+    ey = scaled(host64(y), r["y"], r["m"])
+    eh = scaled(host64(hl), r["h_last"], r["H_last"])
+    assert ey <= TOL[dt], (mode, "y", ey)
+    assert eh <= TOL[dt], (mode, "h_last", eh)
+
+
+def test_scan_options_m130_full(torch_cuda, oracle):
+    """Every output of the Mamba-130M-shaped layer with softplus and the
+    exact hold."""
+    from selective_state_space_63_amd import s6
+    w = synth.WORKLOADS["m130"]
+    _say(f"[case] scan options all {w.name}")
+    d, o, kw, okw = options_problem(w, "all", with_h0=False)
+    y = s6.scan_fwd(d["x"], d["delta"], d["A"], d["Bm"], d["Cm"], D=d["D"], z=d["z"], **kw)
+    torch_cuda.cuda.synchronize()
+    r = oracle.scan(**o, **okw)
+    assert scaled(host64(y), r["y"], r["m"]) <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("mode", ["softplus", "all", "zoh"])
+@pytest.mark.parametrize("shape", [(2, 65, 16, 100, synth.BF16), (1, 256, 16, 20000, synth.BF16),
+                                   (1, 30, 5, 37, synth.F32)])
+def test_last_state_options(torch_cuda, oracle, shape, mode):
+    from selective_state_space_63_amd import s6
+    b, dm, n, L, dt = shape
+    w = synth.custom(b, dm, n, L, dt, False, seed=3100 + L)
+    _say(f"[case] last_state options {mode} {w.name}")
+    d, o, kw, okw = options_problem(w, mode)
+    hl = s6.last_state(d["x"], d["delta"], d["A"], d["Bm"], h0=d["h0"], **kw)
+    torch_cuda.cuda.synchronize()
+    r = oracle.scan(**o, **okw)
+    assert scaled(host64(hl), r["h_last"], r["H_last"]) <= TOL[dt]
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", [(3, 70, 16, synth.BF16, True), (2, 33, 5, synth.F32, True),
+                                   (6, 22000, 16, synth.BF16, True)])
+def test_state_update_options(torch_cuda, oracle, shape, mode):
+    """S decode steps with the options against the oracle's scan of the same
+    tokens."""
+    import torch
+    from selective_state_space_63_amd import s6
+    b, dm, n, dt, gate = shape
+    S = 8
+    w = synth.custom(b, dm, n, S, dt, gate, seed=3200 + dm)
+    _say(f"[case] decode options {mode} {w.name}")
+    d, o, kw, okw = options_problem(w, mode)
+    h = d["h0"].clone()
+    ys = []
+    for s in range(S):
+        sl = lambda t: None if t is None else t[..., s].contiguous()  # noqa: E731
+        ys.append(s6.state_update(h, sl(d["x"]), sl(d["delta"]), d["A"], sl(d["Bm"]), sl(d["Cm"]),
+                                  D=d["D"], z=sl(d["z"]), **kw))
+    torch.cuda.synchronize()
+    r = oracle.scan(**o, **okw)
+    y = np.stack([host64(v) for v in ys], axis=-1)
+    assert scaled(y, r["y"], r["m"]) <= TOL[dt]
+    assert scaled(host64(h), r["h_last"], r["H_last"]) <= TOL[dt]
+
+
+def test_no_options_equal_plain_entry_points(torch_cuda):
+    """flags 0 and no bias through the _ex entry points give the plain entry
+    points' results bit for bit."""
+    import ctypes
+    import torch
+    from selective_state_space_63_amd import s6
+    lib = s6.load_library()
+    w = synth.custom(2, 96, 16, 40, synth.BF16, True, seed=3300)
+    _say(f"[case] options off {w.name}")
+    d, _ = problem(w, True)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    f = dict(device="cuda", dtype=torch.float32)
+    y1, y2 = torch.empty((2, 96, 40), **f), torch.empty((2, 96, 40), **f)
+    h1, h2 = torch.empty((2, 96, 16), **f), torch.empty((2, 96, 16), **f)
+    args = (P(d["A"]), P(d["Bm"]), P(d["Cm"]), P(d["D"]), P(d["z"]), P(d["h0"]))
+    assert lib.s6_scan_fwd(2, 96, 40, 16, 1, P(d["x"]), P(d["delta"]), *args, P(y1), P(h1), st) == 0
+    assert lib.s6_scan_fwd_ex(2, 96, 40, 16, 1, P(d["x"]), P(d["delta"]), None, 0, *args, P(y2), P(h2), st) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    hs1, hs2 = d["h0"].clone(), d["h0"].clone()
+    tok = {k: d[k][..., 0].contiguous() for k in ("x", "delta", "Bm", "Cm", "z")}  # kept alive
+    ins = (tok["x"], tok["delta"])
+    rest = (P(d["A"]), P(tok["Bm"]), P(tok["Cm"]), P(d["D"]), P(tok["z"]))
+    ya, yb = torch.empty((2, 96), **f), torch.empty((2, 96), **f)
+    assert lib.s6_state_update(2, 96, 16, 1, P(hs1), P(ins[0]), P(ins[1]), *rest, P(ya), st) == 0
+    assert lib.s6_state_update_ex(2, 96, 16, 1, P(hs2), P(ins[0]), P(ins[1]), None, 0, *rest, P(yb), st) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(hs1, hs2) and torch.equal(ya, yb)

@@ -38,10 +38,11 @@ MUTANTS = [
     ("zoh_limit_at_zero", [("return a != 0.0 ? expm1(dt * a) / a : dt;", "return a != 0.0 ? expm1(dt * a) / a : 0.0;")]),
     ("softplus_no_abs", [("log1p(exp(-fabs(v)))", "log1p(exp(-v))")]),
     ("softplus_is_exp", [("return (v > 0.0 ? v : 0.0) + log1p(exp(-fabs(v)));", "return exp(v);")]),
-    ("softplus_bias_dropped", [("return softplus(raw + (dbias ? dbias[d] : 0.0));", "return softplus(raw);")]),
-    ("softplus_bias_channel", [("dbias ? dbias[d] : 0.0", "dbias ? dbias[0] : 0.0")]),
-    ("softplus_bias_after", [("return softplus(raw + (dbias ? dbias[d] : 0.0));",
-                              "return softplus(raw) + (dbias ? dbias[d] : 0.0);")]),
+    ("bias_dropped", [("double v = dbias ? raw + dbias[d] : raw;", "double v = raw;")]),
+    ("bias_channel", [("raw + dbias[d]", "raw + dbias[0]")]),
+    ("bias_after_softplus", [("double v = dbias ? raw + dbias[d] : raw;\n  return (flags & ORACLE_DELTA_SOFTPLUS) ? softplus(v) : v;",
+                              "return ((flags & ORACLE_DELTA_SOFTPLUS) ? softplus(raw) : raw) + (dbias ? dbias[d] : 0.0);")]),
+    ("softplus_always", [("return (flags & ORACLE_DELTA_SOFTPLUS) ? softplus(v) : v;", "return softplus(v);")]),
     ("delta_index_shift", [("delta[p * L + t]", "delta[p * L + (t > 0 ? t - 1 : 0)]")]),
     ("A_state_index", [("exp(dt * Ad[n])", "exp(dt * Ad[(n + 1) % N])")]),
     ("B_batch_index", [("const double* Bb = Bm + b * N * L;", "const double* Bb = Bm;")]),
