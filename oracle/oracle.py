@@ -63,6 +63,8 @@ class Oracle:
         self.lib.oracle_scan_ex.restype = None
         self.lib.oracle_step_ex.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_int] + [_P] * 7
         self.lib.oracle_step_ex.restype = None
+        self.lib.oracle_scan_bwd.argtypes = [_I, _I, _I, _I] + [_P] * 26
+        self.lib.oracle_scan_bwd.restype = ctypes.c_int
         self.lib.oracle_num_threads.restype = ctypes.c_int
         self.path = path
 
@@ -142,6 +144,37 @@ class Oracle:
                                     args[1], bptr, flags, *args[2:], y.ctypes.data_as(_P),
                                     m.ctypes.data_as(_P))
         return y, m
+
+
+    def scan_bwd(self, x, delta, A, Bm, Cm, dy, Dskip=None, z=None, h0=None, dh_last=None):
+        """Gradients of <dy, y> + <dh_last, h_last> for the plain scan.
+        Returns a dict: dx, ddelta, dz (batch, D, L); dA (D, N); dBm, dCm
+        (batch, N, L); dDskip (D,); dh0 (batch, D, N); and for each the
+        magnitude under the key prefixed with "m" (mdx, mddelta, ...).  dz is
+        zero without a gate."""
+        x = np.asarray(x)
+        Bsz, D, L = x.shape
+        N = np.asarray(A).shape[1]
+        if N > 256:
+            raise ValueError("oracle supports N <= 256")
+        keep = []
+        args = []
+        for a, shp in ((x, (Bsz, D, L)), (delta, (Bsz, D, L)), (A, (D, N)), (Bm, (Bsz, N, L)),
+                       (Cm, (Bsz, N, L)), (Dskip, (D,)), (z, (Bsz, D, L)), (h0, (Bsz, D, N)),
+                       (dy, (Bsz, D, L)), (dh_last, (Bsz, D, N))):
+            arr, ptr = self._in(a, shp)
+            keep.append(arr)
+            args.append(ptr)
+        shapes = {"dx": (Bsz, D, L), "ddelta": (Bsz, D, L), "dA": (D, N), "dBm": (Bsz, N, L),
+                  "dCm": (Bsz, N, L), "dDskip": (D,), "dz": (Bsz, D, L), "dh0": (Bsz, D, N)}
+        out = {k: np.empty(v) for k, v in shapes.items()}
+        out.update({"m" + k: np.empty(v) for k, v in shapes.items()})
+        order = ["dx", "ddelta", "dA", "dBm", "dCm", "dDskip", "dz", "dh0"]
+        ptrs = [out[k].ctypes.data_as(_P) for k in order] + [out["m" + k].ctypes.data_as(_P) for k in order]
+        rc = self.lib.oracle_scan_bwd(Bsz, D, L, N, *args, *ptrs)
+        if rc != 0:
+            raise MemoryError("oracle_scan_bwd: out of memory")
+        return out
 
 
 _default = None

@@ -51,6 +51,7 @@
  */
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <stdint.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -183,4 +184,167 @@ void oracle_step(int64_t Bsz, int64_t D, int64_t N, double* h, double* H, const 
                  const double* delta, const double* A, const double* Bm, const double* Cm,
                  const double* Dskip, const double* z, double* y, double* m) {
   oracle_step_ex(Bsz, D, N, h, H, x, delta, NULL, 0, A, Bm, Cm, Dskip, z, y, m);
+}
+
+/* ---------------------------------------------------------------- backward --
+ * Gradients of the scan for the loss  <dy, y> + <dh_last, h_last>  (reverse
+ * mode; plain step, no options).  The state is recomputed from the inputs
+ * (the pages' guide, §3.4, notes that the fused scan recomputes the states in
+ * the backward pass instead of storing them).  With a_t[n] = exp(Delta_t
+ * A[n]), g_t = SiLU(z_t) (1 without a gate), yc_t = sum_n C_t[n] h_t[n] +
+ * D x_t (the output before the gate) and dyc_t = dy_t g_t:
+ *
+ *   lambda_t[n] = dL/dh_t[n] = dyc_t C_t[n] + a_{t+1}[n] lambda_{t+1}[n],
+ *                 lambda_{L-1}[n] = dyc_{L-1} C_{L-1}[n] + dh_last[n]
+ *   dx_t     = dyc_t D + sum_n lambda_t[n] Delta_t B_t[n]
+ *   ddelta_t = sum_n lambda_t[n] (A[n] a_t[n] h_{t-1}[n] + B_t[n] x_t)
+ *   dA[d,n]  = sum_{b,t} lambda_t[n] Delta_t a_t[n] h_{t-1}[n]
+ *   dB[b,n,t] = sum_d lambda_t[n] Delta_t x_t      dC[b,n,t] = sum_d dyc_t h_t[n]
+ *   dD[d]    = sum_{b,t} dyc_t x_t                 dh0[n] = a_0[n] lambda_0[n]
+ *   dz_t     = dy_t yc_t SiLU'(z_t),  SiLU'(z) = s (1 + z (1 - s)), s = 1/(1+e^-z)
+ * with h_{-1} = h0 (or 0).  Each output also gets its magnitude: the same
+ * sums over the absolute values of every factor (states and adjoints
+ * replaced by their magnitude recurrences), the scale of the componentwise
+ * error metric.
+ *
+ * Order of evaluation: batch rows in parallel; within a row the channels in
+ * order d = 0 .. D-1, so dB and dC are summed over d in a fixed order; dA and
+ * dD are summed over rows b = 0 .. Bsz-1 after the parallel loop.
+ * Nullable: Dskip, z, h0, dh_last (inputs); dDskip, dz, dh0 (outputs); every
+ * magnitude output.  Work memory: 4 L N doubles per batch row. */
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+int oracle_scan_bwd(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x,
+                    const double* delta, const double* A, const double* Bm, const double* Cm,
+                    const double* Dskip, const double* z, const double* h0, const double* dy,
+                    const double* dh_last, double* dx, double* ddelta, double* dA, double* dBm,
+                    double* dCm, double* dDskip, double* dz, double* dh0, double* mdx,
+                    double* mddelta, double* mdA, double* mdB, double* mdC, double* mdD,
+                    double* mdz, double* mdh0) {
+  double* dA_b = (double*)calloc((size_t)(Bsz * D * N), sizeof(double));
+  double* mdA_b = (double*)calloc((size_t)(Bsz * D * N), sizeof(double));
+  double* dD_b = (double*)calloc((size_t)(Bsz * D), sizeof(double));
+  double* mdD_b = (double*)calloc((size_t)(Bsz * D), sizeof(double));
+  int fail = !dA_b || !mdA_b || !dD_b || !mdD_b;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t b = 0; b < Bsz; ++b) {
+    if (fail) continue;
+    /* states h_t and magnitudes H_t, t = -1 .. L-1 (row t+1) */
+    double* hs = (double*)malloc((size_t)((L + 1) * N) * sizeof(double));
+    double* Hs = (double*)malloc((size_t)((L + 1) * N) * sizeof(double));
+    double lam[256], Lam[256];
+    if (!hs || !Hs) {
+      free(hs);
+      free(Hs);
+#pragma omp atomic write
+      fail = 1;
+      continue;
+    }
+    const double* Bb = Bm + b * N * L;
+    const double* Cb = Cm + b * N * L;
+    for (int64_t i = 0; i < N * L; ++i) {
+      dBm[b * N * L + i] = 0.0;
+      dCm[b * N * L + i] = 0.0;
+      if (mdB) mdB[b * N * L + i] = 0.0;
+      if (mdC) mdC[b * N * L + i] = 0.0;
+    }
+    for (int64_t d = 0; d < D; ++d) {
+      const int64_t p = b * D + d;
+      const double* Ad = A + d * N;
+      const double dsk = Dskip ? Dskip[d] : 0.0;
+      /* forward: the states of every token */
+      for (int64_t n = 0; n < N; ++n) {
+        hs[n] = h0 ? h0[p * N + n] : 0.0;
+        Hs[n] = fabs(hs[n]);
+      }
+      for (int64_t t = 0; t < L; ++t) {
+        const double dt = delta[p * L + t], xt = x[p * L + t];
+        for (int64_t n = 0; n < N; ++n) {
+          const double a = exp(dt * Ad[n]);
+          const double bx = dt * Bb[n * L + t] * xt;
+          hs[(t + 1) * N + n] = a * hs[t * N + n] + bx;
+          Hs[(t + 1) * N + n] = a * Hs[t * N + n] + fabs(bx);
+        }
+      }
+      /* reverse: adjoints from the last token back */
+      for (int64_t n = 0; n < N; ++n) {
+        lam[n] = dh_last ? dh_last[p * N + n] : 0.0; /* a_{t+1} lambda_{t+1} carried in */
+        Lam[n] = fabs(lam[n]);
+      }
+      for (int64_t t = L - 1; t >= 0; --t) {
+        const double dt = delta[p * L + t], xt = x[p * L + t];
+        const double g = z ? silu(z[p * L + t]) : 1.0;
+        const double dyc = dy[p * L + t] * g;
+        double gx = 0.0, mgx = 0.0, gd = 0.0, mgd = 0.0, yc = 0.0, myc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          const double a = exp(dt * Ad[n]);
+          const double Bt = Bb[n * L + t], Ct = Cb[n * L + t];
+          const double l = dyc * Ct + lam[n]; /* lambda_t */
+          const double ml = fabs(dyc * Ct) + Lam[n];
+          const double hp = hs[t * N + n], Hp = Hs[t * N + n]; /* h_{t-1} */
+          const double ht = hs[(t + 1) * N + n], Ht = Hs[(t + 1) * N + n];
+          gx += l * dt * Bt;
+          mgx += ml * fabs(dt * Bt);
+          gd += l * (Ad[n] * a * hp + Bt * xt);
+          mgd += ml * (fabs(Ad[n] * a) * Hp + fabs(Bt * xt));
+          dA_b[p * N + n] += l * dt * a * hp;
+          mdA_b[p * N + n] += ml * fabs(dt * a) * Hp;
+          dBm[b * N * L + n * L + t] += l * dt * xt;
+          dCm[b * N * L + n * L + t] += dyc * ht;
+          if (mdB) mdB[b * N * L + n * L + t] += ml * fabs(dt * xt);
+          if (mdC) mdC[b * N * L + n * L + t] += fabs(dyc) * Ht;
+          yc += Ct * ht;
+          myc += fabs(Ct) * Ht;
+          lam[n] = a * l; /* carried to token t - 1 */
+          Lam[n] = a * ml;
+        }
+        yc += dsk * xt;
+        myc += fabs(dsk * xt);
+        dx[p * L + t] = dyc * dsk + gx;
+        ddelta[p * L + t] = gd;
+        if (mdx) mdx[p * L + t] = fabs(dyc * dsk) + mgx;
+        if (mddelta) mddelta[p * L + t] = mgd;
+        dD_b[p] += dyc * xt;
+        mdD_b[p] += fabs(dyc * xt);
+        if (dz) {
+          double zz = z ? z[p * L + t] : 0.0;
+          double s = sigmoid(zz);
+          double dsilu = s * (1.0 + zz * (1.0 - s));
+          dz[p * L + t] = z ? dy[p * L + t] * yc * dsilu : 0.0;
+          if (mdz) mdz[p * L + t] = z ? fabs(dy[p * L + t] * dsilu) * myc : 0.0;
+        }
+      }
+      for (int64_t n = 0; n < N; ++n) {
+        if (dh0) dh0[p * N + n] = lam[n];
+        if (mdh0) mdh0[p * N + n] = Lam[n];
+      }
+    }
+    free(hs);
+    free(Hs);
+  }
+  if (!fail) {
+    for (int64_t i = 0; i < D * N; ++i) {
+      double s = 0.0, ms = 0.0;
+      for (int64_t b = 0; b < Bsz; ++b) {
+        s += dA_b[b * D * N + i];
+        ms += mdA_b[b * D * N + i];
+      }
+      dA[i] = s;
+      if (mdA) mdA[i] = ms;
+    }
+    for (int64_t d = 0; d < D; ++d) {
+      double s = 0.0, ms = 0.0;
+      for (int64_t b = 0; b < Bsz; ++b) {
+        s += dD_b[b * D + d];
+        ms += mdD_b[b * D + d];
+      }
+      if (dDskip) dDskip[d] = s;
+      if (mdD) mdD[d] = ms;
+    }
+  }
+  free(dA_b);
+  free(mdA_b);
+  free(dD_b);
+  free(mdD_b);
+  return fail ? -1 : 0;
 }

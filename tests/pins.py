@@ -471,7 +471,178 @@ def pin_options_brute_force(o):
         assert err < 1e-13, (seed, err)
 
 
+# --------------------------------------------------------------- backward --
+BWD_INPUTS = (("x", "dx"), ("delta", "ddelta"), ("A", "dA"), ("Bm", "dBm"), ("Cm", "dCm"),
+              ("Dskip", "dDskip"), ("z", "dz"), ("h0", "dh0"))
+
+
+def _bwd_problem(seed, **kw):
+    p = _rand_problem(seed, **kw)
+    g = _rng(seed + 500)
+    dy = g.standard_normal(p["x"].shape)
+    dhl = g.standard_normal(p["h0"].shape) if p.get("h0") is not None else None
+    return p, dy, dhl
+
+
+def _bwd(o, p, dy, dhl):
+    return o.scan_bwd(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], dy, Dskip=p.get("Dskip"), z=p.get("z"),
+                      h0=p.get("h0"), dh_last=dhl)
+
+
+def brute_force_loss(p, dy, dhl, dps=50):
+    """<dy, y> + <dh_last, h_last> in multi-digit arithmetic from the
+    materialised form (exponentials of sums of Delta, as in brute_force_y),
+    returned as an mpmath number."""
+    import mpmath as mp
+    mp.mp.dps = dps
+    f = lambda v: mp.mpf(v) if not isinstance(v, mp.mpf) else v  # noqa: E731
+    x, dl, A, Bm, Cm = p["x"], p["delta"], p["A"], p["Bm"], p["Cm"]
+    Bsz, D, L = x.shape
+    N = A.shape[1]
+    total = mp.mpf(0)
+    for b in range(Bsz):
+        for d in range(D):
+            cum = [mp.mpf(0)]
+            for t in range(L):
+                cum.append(cum[-1] + f(dl[b, d, t]))
+            for t in range(L + 1):  # t = L: the final state
+                for n in range(N):
+                    An = f(A[d, n])
+                    last = t == L
+                    tt = L - 1 if last else t
+                    hn = mp.mpf(0)
+                    for s in range(tt + 1):
+                        hn += mp.exp(An * (cum[tt + 1] - cum[s + 1])) * f(dl[b, d, s]) * f(Bm[b, n, s]) * f(x[b, d, s])
+                    if p.get("h0") is not None:
+                        hn += mp.exp(An * cum[tt + 1]) * f(p["h0"][b, d, n])
+                    if last:
+                        if dhl is not None:
+                            total += f(dhl[b, d, n]) * hn
+                    else:
+                        yc_n = f(Cm[b, n, t]) * hn
+                        g = mp.mpf(1)
+                        if p.get("z") is not None:
+                            zz = f(p["z"][b, d, t])
+                            g = zz / (1 + mp.exp(-zz))
+                        total += f(dy[b, d, t]) * yc_n * g
+            if p.get("Dskip") is not None:
+                for t in range(L):
+                    g = mp.mpf(1)
+                    if p.get("z") is not None:
+                        zz = f(p["z"][b, d, t])
+                        g = zz / (1 + mp.exp(-zz))
+                    total += f(dy[b, d, t]) * f(p["Dskip"][d]) * f(x[b, d, t]) * g
+    return total
+
+
+def pin_bwd_directional_brute_force(o):
+    """Every gradient of the backward oracle against a directional derivative
+    of the 50-digit materialised loss by central differences (step 1e-15,
+    truncation far below fp64): an evaluation that shares neither the
+    recurrence nor the adjoint formulas (§3.3, §3.4 recomputation)."""
+    import mpmath as mp
+    p, dy, dhl = _bwd_problem(101, Bsz=2, D=2, L=7, N=3)
+    r = _bwd(o, p, dy, dhl)
+    g = _rng(102)
+    eps = mp.mpf("1e-15")
+    for key, gk in BWD_INPUTS:
+        v = g.standard_normal(p[key].shape)
+        mp.mp.dps = 50
+        qp = dict(p)
+        qm = dict(p)
+        qp[key] = np.array([mp.mpf(float(a)) + eps * mp.mpf(float(b)) for a, b in
+                            zip(p[key].ravel(), v.ravel())], dtype=object).reshape(p[key].shape)
+        qm[key] = np.array([mp.mpf(float(a)) - eps * mp.mpf(float(b)) for a, b in
+                            zip(p[key].ravel(), v.ravel())], dtype=object).reshape(p[key].shape)
+        fd = (brute_force_loss(qp, dy, dhl) - brute_force_loss(qm, dy, dhl)) / (2 * eps)
+        an = float(np.sum(r[gk] * v))
+        scale = float(np.sum(r["m" + gk] * np.abs(v)))
+        assert abs(float(fd) - an) <= 1e-13 * scale, (key, float(fd), an, scale)
+
+
+def pin_bwd_elementwise_fd(o):
+    """Every element of every gradient against a central difference of the
+    forward oracle (step 1e-6, fp64) on a tiny problem: catches a wrong index
+    or layout that a directional check could average out."""
+    p, dy, dhl = _bwd_problem(103, Bsz=2, D=2, L=5, N=2)
+    r = _bwd(o, p, dy, dhl)
+
+    def loss(q):
+        f = o.scan(**q)
+        return np.sum(dy * f["y"]) + np.sum(dhl * f["h_last"])
+
+    eps = 1e-6
+    for key, gk in BWD_INPUTS:
+        fd = np.zeros(p[key].shape)
+        for idx in np.ndindex(p[key].shape):
+            qp = dict(p)
+            qm = dict(p)
+            qp[key] = p[key].copy()
+            qm[key] = p[key].copy()
+            qp[key][idx] += eps
+            qm[key][idx] -= eps
+            fd[idx] = (loss(qp) - loss(qm)) / (2 * eps)
+        err = np.abs(fd - r[gk]) / np.maximum(r["m" + gk], 1e-300)
+        assert np.all(err < 1e-6), (key, np.max(err))
+
+
+def pin_bwd_linear_in_cotangent(o):
+    """The gradients are linear in (dy, dh_last) for fixed inputs."""
+    p, dy, dhl = _bwd_problem(104, Bsz=1, D=3, L=9, N=3)
+    g = _rng(105)
+    dy2 = g.standard_normal(dy.shape)
+    dhl2 = g.standard_normal(dhl.shape)
+    r1 = _bwd(o, p, dy, dhl)
+    r2 = _bwd(o, p, dy2, dhl2)
+    r3 = _bwd(o, p, 1.5 * dy - 0.5 * dy2, 1.5 * dhl - 0.5 * dhl2)
+    for _, gk in BWD_INPUTS:
+        want = 1.5 * r1[gk] - 0.5 * r2[gk]
+        scale = 1.5 * r1["m" + gk] + 0.5 * r2["m" + gk]
+        assert np.all(np.abs(r3[gk] - want) <= 1e-13 * scale + 1e-300), gk
+
+
+def pin_bwd_no_input_coupling(o):
+    """B = 0 and h0 = 0: the state stays 0 and y = D x SiLU(z), so
+    dx = dy SiLU(z) D, dD = sum dy SiLU(z) x, dz = dy D x SiLU'(z), and the
+    gradients of delta, A and C vanish.  The adjoint is then the
+    anti-causal sum lambda_t = sum_{s >= t} exp(A sum_{u=t+1..s} Delta_u)
+    dyc_s C_s, evaluated directly (exponentials of sums), which gives
+    dB = sum_d lambda Delta x and dh0 = exp(A Delta_0) lambda_0."""
+    p, dy, _ = _bwd_problem(106, Bsz=2, D=2, L=6, N=3, h0=False)
+    p["Bm"] = np.zeros_like(p["Bm"])
+    r = _bwd(o, p, dy, None)
+    zz = p["z"]
+    s = 1.0 / (1.0 + np.exp(-zz))
+    g = zz * s
+    dsilu = s * (1.0 + zz * (1.0 - s))
+    Dk = p["Dskip"][None, :, None]
+    assert np.allclose(r["dx"], dy * g * Dk, rtol=1e-14, atol=0)
+    assert np.allclose(r["dDskip"], np.sum(dy * g * p["x"], axis=(0, 2)), rtol=1e-13, atol=0)
+    assert np.allclose(r["dz"], dy * Dk * p["x"] * dsilu, rtol=1e-14, atol=0)
+    for gk in ("ddelta", "dA", "dCm"):
+        assert np.all(r[gk] == 0.0), gk
+    Bsz, D, L = p["x"].shape
+    N = p["A"].shape[1]
+    dB = np.zeros((Bsz, N, L))
+    dh0 = np.zeros((Bsz, D, N))
+    for b in range(Bsz):
+        for d in range(D):
+            dl = p["delta"][b, d]
+            cum = np.concatenate([[0.0], np.cumsum(dl)])
+            dyc = dy[b, d] * g[b, d]
+            for n in range(N):
+                An = p["A"][d, n]
+                lam = np.array([sum(math.exp(An * (cum[s_ + 1] - cum[t + 1])) * dyc[s_] * p["Cm"][b, n, s_]
+                                    for s_ in range(t, L)) for t in range(L)])
+                dB[b, n] += lam * dl * p["x"][b, d]
+                dh0[b, d, n] = math.exp(An * dl[0]) * lam[0]
+    assert np.all(np.abs(r["dBm"] - dB) <= 1e-13 * r["mdBm"]), np.max(np.abs(r["dBm"] - dB))
+    assert np.all(np.abs(r["dh0"] - dh0) <= 1e-13 * r["mdh0"]), np.max(np.abs(r["dh0"] - dh0))
+
+
 PINS = [pin_zero_step_hand, pin_scalar_hand, pin_lti_convolution, pin_step_response,
         pin_brute_force, pin_tree_scan, pin_split_resume, pin_linearity_and_permutation,
         pin_gate_limits, pin_decode_equals_scan, pin_magnitude_bounds, pin_softplus_hand,
-        pin_softplus_limits, pin_zoh_hand, pin_zoh_limits, pin_options_brute_force]
+        pin_softplus_limits, pin_zoh_hand, pin_zoh_limits, pin_options_brute_force,
+        pin_bwd_directional_brute_force, pin_bwd_elementwise_fd, pin_bwd_linear_in_cotangent,
+        pin_bwd_no_input_coupling]

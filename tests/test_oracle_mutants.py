@@ -23,7 +23,7 @@ MUTANTS = [
     ("B_C_swapped", [
         ("* Bt[n * bstride] * xt;", "* Ct[n * bstride] * xt;"),
         ("acc += Ct[n * bstride] * h[n];      /*", "acc += Bt[n * bstride] * h[n];      /*")]),
-    ("exp_sign", [("exp(dt * Ad[n])", "exp(-dt * Ad[n])")]),
+    ("exp_sign", [("double a = exp(dt * Ad[n]);         /*", "double a = exp(-dt * Ad[n]);         /*")]),
     ("dt_dropped_from_input", [("(zoh ? zoh_coef(dt, Ad[n]) : dt) * Bt",
                                 "(zoh ? zoh_coef(dt, Ad[n]) : 1.0) * Bt")]),
     ("gate_before_skip", [("        yt *= g;\n        mag *= fabs(g);\n      }\n      y[p * L + t] = yt;",
@@ -43,9 +43,25 @@ MUTANTS = [
     ("bias_after_softplus", [("double v = dbias ? raw + dbias[d] : raw;\n  return (flags & ORACLE_DELTA_SOFTPLUS) ? softplus(v) : v;",
                               "return ((flags & ORACLE_DELTA_SOFTPLUS) ? softplus(raw) : raw) + (dbias ? dbias[d] : 0.0);")]),
     ("softplus_always", [("return (flags & ORACLE_DELTA_SOFTPLUS) ? softplus(v) : v;", "return softplus(v);")]),
-    ("delta_index_shift", [("delta[p * L + t]", "delta[p * L + (t > 0 ? t - 1 : 0)]")]),
-    ("A_state_index", [("exp(dt * Ad[n])", "exp(dt * Ad[(n + 1) % N])")]),
-    ("B_batch_index", [("const double* Bb = Bm + b * N * L;", "const double* Bb = Bm;")]),
+    # backward
+    ("bwd_decay_same_step", [("const double l = dyc * Ct + lam[n];", "const double l = a * (dyc * Ct + lam[n]);")]),
+    ("bwd_carry_without_decay", [("lam[n] = a * l; /* carried", "lam[n] = l; /* carried")]),
+    ("bwd_ddelta_no_input_term", [("gd += l * (Ad[n] * a * hp + Bt * xt);", "gd += l * (Ad[n] * a * hp);")]),
+    ("bwd_ddelta_new_state", [("gd += l * (Ad[n] * a * hp + Bt * xt);", "gd += l * (Ad[n] * a * ht + Bt * xt);")]),
+    ("bwd_dA_no_step", [("dA_b[p * N + n] += l * dt * a * hp;", "dA_b[p * N + n] += l * a * hp;")]),
+    ("bwd_dB_no_x", [("dBm[b * N * L + n * L + t] += l * dt * xt;", "dBm[b * N * L + n * L + t] += l * dt;")]),
+    ("bwd_dC_prev_state", [("dCm[b * N * L + n * L + t] += dyc * ht;", "dCm[b * N * L + n * L + t] += dyc * hp;")]),
+    ("bwd_dz_silu_not_derivative", [("dz[p * L + t] = z ? dy[p * L + t] * yc * dsilu : 0.0;",
+                                     "dz[p * L + t] = z ? dy[p * L + t] * yc * g : 0.0;")]),
+    ("bwd_gate_ignored", [("const double dyc = dy[p * L + t] * g;", "const double dyc = dy[p * L + t];")]),
+    ("bwd_dh_last_ignored", [("lam[n] = dh_last ? dh_last[p * N + n] : 0.0;", "lam[n] = 0.0;")]),
+    ("bwd_dx_no_skip", [("dx[p * L + t] = dyc * dsk + gx;", "dx[p * L + t] = gx;")]),
+    ("bwd_dD_ungated", [("dD_b[p] += dyc * xt;", "dD_b[p] += dy[p * L + t] * xt;")]),
+    ("bwd_dx_B_of_next_state", [("gx += l * dt * Bt;", "gx += l * dt * Bb[((n + 1) % N) * L + t];")]),
+    ("delta_index_shift", [("step_of(delta[p * L + t],", "step_of(delta[p * L + (t > 0 ? t - 1 : 0)],")]),
+    ("A_state_index", [("double a = exp(dt * Ad[n]);         /*", "double a = exp(dt * Ad[(n + 1) % N]);         /*")]),
+    ("B_batch_index", [("const double* Bb = Bm + b * N * L;\n    const double* Cb = Cm + b * N * L;\n    double dsk",
+                        "const double* Bb = Bm;\n    const double* Cb = Cm + b * N * L;\n    double dsk")]),
     ("BC_layout_transposed", [("Bb + t, Cb + t,\n                               L,",
                                "Bb + t * N, Cb + t * N,\n                               1,")]),
     ("skip_channel_index", [("double dsk = Dskip ? Dskip[d] : 0.0;\n    for (int64_t t",
