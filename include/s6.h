@@ -148,6 +148,32 @@ int s6_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, int in_dtype,
                        const float* A, const void* Bm, const void* Cm, const float* Dskip,
                        const void* z, float* y, void* stream);
 
+/* Gradients of the scan (reverse mode) for the loss <dy, y> + <dh_last,
+ * h_last>, plain step (no options), same inputs as s6_scan_fwd.  The guide's
+ * §3.4 notes that the fused scan recomputes the states in the backward pass
+ * rather than storing them: the states entering every 64-token segment are
+ * recomputed by a state-only pass and the carry fold, and each segment's
+ * states again in registers while the adjoint
+ *   lambda_t[n] = dy_t SiLU(z_t) Cm[b,n,t] + exp(delta_{t+1} A[d,n]) lambda_{t+1}[n]
+ * runs from the last token back.  All gradients are fp32 and overwrite their
+ * buffers:
+ *   dy      : required (batch, dim, seqlen) fp32.   dh_last : nullable (zero).
+ *   dx, ddelta : required (batch, dim, seqlen).     dz : nullable; written only
+ *            when z is given.
+ *   dA : required (dim, dstate).  dBm, dCm : required (batch, dstate, seqlen).
+ *   dDskip : nullable (dim).   dh0 : nullable (batch, dim, dstate), the
+ *            gradient of the initial state (h0 itself may be NULL = zero).
+ * Sums over channels (dBm, dCm), over batch rows and tokens (dA, dDskip) are
+ * taken in a fixed order: repeated calls give identical bits.  Workspace from
+ * the stream-ordered allocator (hipMallocAsync), released on the stream before
+ * returning: about 2*(dim/32)*batch*dstate*seqlen + 2*batch*dim*dstate*seqlen/64
+ * floats. */
+int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
+                const float* Dskip, const void* z, const float* h0, const float* dy,
+                const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm, float* dCm,
+                float* dDskip, float* dz, float* dh0, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -311,7 +311,9 @@ int oracle_scan_bwd(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* 
           double s = sigmoid(zz);
           double dsilu = s * (1.0 + zz * (1.0 - s));
           dz[p * L + t] = z ? dy[p * L + t] * yc * dsilu : 0.0;
-          if (mdz) mdz[p * L + t] = z ? fabs(dy[p * L + t] * dsilu) * myc : 0.0;
+          /* magnitude of SiLU'(z) = s + z s (1 - s): the sum of its two terms' absolute values */
+          double mdsilu = s + fabs(zz) * s * (1.0 - s);
+          if (mdz) mdz[p * L + t] = z ? fabs(dy[p * L + t]) * mdsilu * myc : 0.0;
         }
       }
       for (int64_t n = 0; n < N; ++n) {

@@ -874,6 +874,331 @@ __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- backward --
+// Reverse-mode gradients of the scan for the loss <dy, y> + <dh_last, h_last>
+// (plain step).  The states are recomputed, never stored per token: a
+// state-only pass and the carry fold give the state entering every segment of
+// kBwdSeg tokens (the same kernels as a segmented forward scan); this kernel
+// then walks the segments of a (batch row, 32-channel block) from the last to
+// the first.  Per segment it stages the inputs in LDS, recomputes the states
+// at the four chunk starts, and per 16-token chunk (last first) recomputes
+// the chunk's states and transitions in registers and runs the adjoint
+// lambda_t = dyc_t C_t + a_{t+1} lambda_{t+1} backwards through it.
+//
+// Lane l of wave w: channel c = 4w + (l >> 4) of the block, states
+// (l & 15) * SPL + j.  Sums over states (for dx, ddelta and the pre-gate
+// output) are taken across the 16 lanes of a row with DPP rotations; sums
+// over channels (dB, dC) across the 4 rows of a wave with permlane swaps,
+// across the 8 waves in LDS, and across channel blocks by a second kernel
+// from per-block partials (a fixed order: results are bitwise repeatable).
+constexpr int kBwdSeg = 64;    // tokens per recomputation segment
+
+// Waves per workgroup (4 channels each): 8 with one state per lane, 4 with
+// two (the LDS of a workgroup stays under 64 KB).
+template <int SPL>
+constexpr int bwd_waves() { return SPL == 1 ? 8 : 4; }
+
+template <int SPL>
+constexpr size_t bwd_lds_bytes(bool) {
+  return sizeof(float) * ((size_t)4 * (4 * bwd_waves<SPL>()) * kBwdSeg + (size_t)2 * 16 * SPL * kBwdSeg +
+                          (size_t)bwd_waves<SPL>() * 2 * 16 * 16 * SPL);
+}
+
+struct BwdArgs {
+  const void* x;
+  const void* delta;
+  const void* z;          // null: no gate
+  const void* Bm;
+  const void* Cm;
+  const float* A;
+  const float* Dskip;     // nullable
+  const float* dy;        // (batch, D, L)
+  const float* dh_last;   // nullable
+  const float* hin;       // (S, batch*D*N): state entering each segment
+  float* dx;              // (batch, D, L)
+  float* ddelta;          // (batch, D, L)
+  float* dz;              // (batch, D, L), gate only
+  float* dA_part;         // (batch, D, N): sums over t of one batch row
+  float* dD_part;         // (batch, D)
+  float* dB_part;         // (nblk, batch, N, L)
+  float* dC_part;         // (nblk, batch, N, L)
+  float* dh0;             // nullable (batch, D, N)
+  int64_t batch, D, L, N, nseg;
+};
+
+// Sum over the 16 lanes of a row, in every lane (DPP row rotations).
+__device__ __forceinline__ float row_sum16(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false));
+  return v;
+}
+
+// Sums over the 4 rows (channels) of a wave for 4 tokens at once: v[k] is
+// this lane's value of token k; the result in row r is the 4-row sum of
+// token row_tok(r) = 0, 2, 1, 3 (v_permlane32_swap pairs rows 0,1 with 2,3
+// for two tokens, v_permlane16_swap then rows 0 with 1 and 2 with 3).
+__device__ __forceinline__ int row_tok(int r) { return ((r & 1) << 1) | (r >> 1); }
+__device__ __forceinline__ float rows_sum4(const float (&v)[4]) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v[0]),
+                                                  __builtin_bit_cast(unsigned, v[1]), false, false);
+  const auto q = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v[2]),
+                                                  __builtin_bit_cast(unsigned, v[3]), false, false);
+  const float w01 = __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
+  const float w23 = __builtin_bit_cast(float, (unsigned)q[0]) + __builtin_bit_cast(float, (unsigned)q[1]);
+  const auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, w01),
+                                                  __builtin_bit_cast(unsigned, w23), false, false);
+  return __builtin_bit_cast(float, (unsigned)s[0]) + __builtin_bit_cast(float, (unsigned)s[1]);
+}
+
+template <typename In, bool GATE, int SPL>
+__global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a) {
+  constexpr int WB = bwd_waves<SPL>();
+  constexpr int NTHR = 64 * WB;
+  constexpr int CW = 4 * WB;         // channels per workgroup
+  constexpr int NS = 16 * SPL;       // state slots per channel
+  constexpr int KS = kBwdSeg;
+  extern __shared__ float4 lds4[];
+  float* lds = reinterpret_cast<float*>(lds4);
+  float* sx = lds;                   // [CW][KS] x
+  float* sdl = sx + CW * KS;         // [CW][KS] delta
+  float* sdyc = sdl + CW * KS;       // [CW][KS] dy * SiLU(z)
+  float* sq = sdyc + CW * KS;        // [CW][KS] dy * SiLU'(z)
+  float* sB = sq + CW * KS;          // [NS][KS]
+  float* sC = sB + NS * KS;          // [NS][KS]
+  float* red = sC + NS * KS;         // [waves][2][16][NS]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int row = lane >> 4;
+  const int nl = lane & 15;
+  const int c = 4 * w + row;
+  const int64_t D = a.D, L = a.L, N = a.N;
+  const int64_t nblk = (D + CW - 1) / CW;
+  const int64_t blk = blockIdx.x % nblk;
+  const int64_t b = blockIdx.x / nblk;
+  const int64_t d0 = blk * CW;
+  const int64_t rows_valid = D - d0 < CW ? D - d0 : CW;
+  const int64_t d = d0 + c;
+  const bool chv = c < rows_valid;
+  const In* xp = static_cast<const In*>(a.x);
+  const In* dp = static_cast<const In*>(a.delta);
+  const In* zp = static_cast<const In*>(a.z);
+  const In* Bp = static_cast<const In*>(a.Bm);
+  const In* Cp = static_cast<const In*>(a.Cm);
+  const float dsk = (a.Dskip && chv) ? a.Dskip[d] : 0.0f;
+
+  float A2[SPL], An[SPL], mu[SPL], dA[SPL];
+  bool sv[SPL];
+#pragma unroll
+  for (int j = 0; j < SPL; ++j) {
+    const int64_t n = (int64_t)nl * SPL + j;
+    sv[j] = chv && n < N;
+    An[j] = sv[j] ? a.A[d * N + n] : 0.0f;
+    A2[j] = An[j] * kLog2e;
+    mu[j] = (sv[j] && a.dh_last) ? a.dh_last[(b * D + d) * N + n] : 0.0f;  // a_{t+1} lambda_{t+1}
+    dA[j] = 0.0f;
+  }
+  float dD = 0.0f;
+
+  for (int64_t s = a.nseg - 1; s >= 0; --s) {
+    const int64_t tb = s * KS;
+    const int64_t tl = L - tb < KS ? L - tb : KS;  // valid tokens of the segment
+    __syncthreads();  // the previous segment's reads of the staged inputs are done
+    for (int i = tid; i < CW * KS; i += NTHR) {
+      const int cc = i / KS, t = i % KS;
+      const bool ok = cc < rows_valid && t < tl;
+      const int64_t off = (b * D + d0 + (cc < rows_valid ? cc : 0)) * L + tb + (t < tl ? t : 0);
+      float xv = 0.0f, dl = 0.0f, dyc = 0.0f, q = 0.0f;
+      if (ok) {
+        xv = to_f32(xp[off]);
+        dl = to_f32(dp[off]);
+        const float g = a.dy[off];
+        if constexpr (GATE) {
+          const float zz = to_f32(zp[off]);
+          const float sg = fast_rcp(1.0f + fast_exp2(-zz * kLog2e));
+          dyc = g * (zz * sg);
+          q = g * (sg * (1.0f + zz * (1.0f - sg)));
+        } else {
+          dyc = g;
+        }
+      }
+      sx[i] = xv;
+      sdl[i] = dl;
+      sdyc[i] = dyc;
+      sq[i] = q;
+    }
+    for (int i = tid; i < NS * KS; i += NTHR) {
+      const int n = i / KS, t = i % KS;
+      const bool ok = n < N && t < tl;
+      const int64_t off = (b * N + (n < N ? n : 0)) * L + tb + (t < tl ? t : 0);
+      sB[i] = ok ? to_f32(Bp[off]) : 0.0f;
+      sC[i] = ok ? to_f32(Cp[off]) : 0.0f;
+    }
+    __syncthreads();
+
+    // states at the four chunk starts of the segment
+    float hc[4][SPL];
+    {
+      float h[SPL];
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        const int64_t n = (int64_t)nl * SPL + j;
+        h[j] = sv[j] ? a.hin[s * a.batch * D * N + (b * D + d) * N + n] : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) hc[k][j] = h[j];
+        for (int i = 0; i < 16; ++i) {
+          const int t = 16 * k + i;
+          const float dl = sdl[c * KS + t];
+          const float u = dl * sx[c * KS + t];
+#pragma unroll
+          for (int j = 0; j < SPL; ++j)
+            h[j] = __builtin_fmaf(fast_exp2(dl * A2[j]), h[j], u * sB[(nl * SPL + j) * KS + t]);
+        }
+      }
+    }
+
+    for (int k = 3; k >= 0; --k) {
+      // the chunk's transitions and states: hist[j][i] = h before token i
+      float ea[SPL][16], hist[SPL][17];
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) hist[j][0] = hc[k][j];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = 16 * k + i;
+        const float dl = sdl[c * KS + t];
+        const float u = dl * sx[c * KS + t];
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+          ea[j][i] = fast_exp2(dl * A2[j]);
+          hist[j][i + 1] = __builtin_fmaf(ea[j][i], hist[j][i], u * sB[(nl * SPL + j) * KS + t]);
+        }
+      }
+      // adjoint, last token first; lane nl keeps the row sums of token nl
+      float k1 = 0.0f, k2 = 0.0f, k3 = 0.0f;
+#pragma unroll
+      for (int g4 = 3; g4 >= 0; --g4) {
+        float pb[SPL][4], pc[SPL][4];
+#pragma unroll
+        for (int ii = 3; ii >= 0; --ii) {
+          const int i = 4 * g4 + ii;
+          const int t = 16 * k + i;
+          const float dl = sdl[c * KS + t];
+          const float xv = sx[c * KS + t];
+          const float dyc = sdyc[c * KS + t];
+          float s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+          for (int j = 0; j < SPL; ++j) {
+            const float Bv = sB[(nl * SPL + j) * KS + t];
+            const float Cv = sC[(nl * SPL + j) * KS + t];
+            const float lam = __builtin_fmaf(dyc, Cv, mu[j]);
+            mu[j] = ea[j][i] * lam;
+            const float r = lam * (ea[j][i] * hist[j][i]);
+            s1 = __builtin_fmaf(lam, Bv, s1);
+            s2 = __builtin_fmaf(An[j], r, s2);
+            s3 = __builtin_fmaf(Cv, hist[j][i + 1], s3);
+            dA[j] = __builtin_fmaf(dl, r, dA[j]);
+            pb[j][ii] = lam * (dl * xv);
+            pc[j][ii] = dyc * hist[j][i + 1];
+          }
+          dD = __builtin_fmaf(dyc, xv, dD);
+          s1 = row_sum16(s1);
+          s2 = row_sum16(s2);
+          if constexpr (GATE) s3 = row_sum16(s3);
+          if (nl == i) { k1 = s1; k2 = s2; k3 = s3; }
+        }
+        // channel sums of the 4 tokens over the wave's rows, then to LDS
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+          const int tok = 4 * g4 + row_tok(row);
+          red[((w * 2 + 0) * 16 + tok) * NS + nl * SPL + j] = rows_sum4(pb[j]);
+          red[((w * 2 + 1) * 16 + tok) * NS + nl * SPL + j] = rows_sum4(pc[j]);
+        }
+      }
+      // outputs of token nl of the chunk for this lane's channel
+      {
+        const int t = 16 * k + nl;
+        const int64_t tt = tb + t;
+        if (chv && tt < L) {
+          const float dl = sdl[c * KS + t];
+          const float xv = sx[c * KS + t];
+          const float dyc = sdyc[c * KS + t];
+          const int64_t off = (b * D + d) * L + tt;
+          a.dx[off] = __builtin_fmaf(dyc, dsk, dl * k1);
+          a.ddelta[off] = __builtin_fmaf(xv, k1, k2);
+          if (GATE && a.dz) a.dz[off] = __builtin_fmaf(dsk, xv, k3) * sq[c * KS + t];
+        }
+      }
+      __syncthreads();  // every wave's channel sums of the chunk are in LDS
+      for (int e = tid; e < 2 * 16 * NS; e += NTHR) {
+        const int kind = e / (16 * NS);
+        const int tok = (e / NS) % 16;
+        const int n = e % NS;
+        float sum = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < WB; ++ww) sum += red[((ww * 2 + kind) * 16 + tok) * NS + n];
+        const int64_t tt = tb + 16 * k + tok;
+        if (n < N && tt < L) {
+          float* dst = kind ? a.dC_part : a.dB_part;
+          dst[((blk * a.batch + b) * N + n) * L + tt] = sum;
+        }
+      }
+      __syncthreads();  // red is free again
+    }
+  }
+  if (chv) {
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const int64_t n = (int64_t)nl * SPL + j;
+      if (n < N) {
+        a.dA_part[(b * D + d) * N + n] = dA[j];
+        if (a.dh0) a.dh0[(b * D + d) * N + n] = mu[j];
+      }
+    }
+    if (nl == 0) a.dD_part[b * D + d] = dD;
+  }
+}
+
+// dB and dC: sums of the per-block partials over the channel blocks, in order.
+__global__ void s6_bwd_reduce_bc(const float* __restrict__ part, float* __restrict__ out, int64_t nblk,
+                                 int64_t total) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float s = 0.0f;
+    for (int64_t k = 0; k < nblk; ++k) s += part[k * total + i];
+    out[i] = s;
+  }
+}
+
+// dA (D, N) and dD (D): sums over batch rows, in order.
+__global__ void s6_bwd_reduce_rows(const float* __restrict__ dA_part, const float* __restrict__ dD_part,
+                                   float* __restrict__ dA, float* __restrict__ dD, int64_t batch, int64_t D,
+                                   int64_t N) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < D * N) {
+    float s = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) s += dA_part[b * D * N + i];
+    dA[i] = s;
+  }
+  if (dD && i < D) {
+    float s = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) s += dD_part[b * D + i];
+    dD[i] = s;
+  }
+}
+
+// out[i] = v (a fill that a captured graph can hold, unlike a memset node).
+__global__ void s6_fill(float* __restrict__ out, float v, int64_t total) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = v;
+}
+
 // ------------------------------------------------------------------- host --
 thread_local char g_err[256];
 
@@ -1168,6 +1493,31 @@ int launch_step_g(const StepArgs& a, hipStream_t st) {
   return launch_step_b<In, GATE, 4, 8>(a, vec_ok(4, 8), st);
 }
 
+template <typename In, bool GATE, int SPL>
+int launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+  constexpr int CW = 4 * bwd_waves<SPL>();
+  const int64_t nblk = (a.D + CW - 1) / CW;
+  hipLaunchKernelGGL((s6_bwd_kernel<In, GATE, SPL>), dim3((unsigned)(nblk * a.batch)), dim3(64 * bwd_waves<SPL>()),
+                     bwd_lds_bytes<SPL>(GATE), st, a);
+  S6_HIP(hipGetLastError(), "s6_bwd_kernel launch");
+  return S6_OK;
+}
+
+template <typename In>
+int launch_bwd(const BwdArgs& a, bool gate, hipStream_t st) {
+  if (a.N <= 16) return gate ? launch_bwd_t<In, true, 1>(a, st) : launch_bwd_t<In, false, 1>(a, st);
+  return gate ? launch_bwd_t<In, true, 2>(a, st) : launch_bwd_t<In, false, 2>(a, st);
+}
+
+int bwd_channels_per_block(int64_t dstate) { return dstate <= 16 ? 4 * bwd_waves<1>() : 4 * bwd_waves<2>(); }
+
+void fill(float* p, float v, int64_t n, hipStream_t st) {
+  if (!p || n <= 0) return;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(s6_fill, dim3((unsigned)blocks), dim3(256), 0, st, p, v, n);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1253,6 +1603,116 @@ int s6_state_update(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, fl
                     const void* Cm, const float* Dskip, const void* z, float* y, void* stream) {
   return s6_state_update_ex(batch, dim, dstate, in_dtype, h, x, delta, nullptr, 0, A, Bm, Cm, Dskip, z,
                             y, stream);
+}
+
+int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
+                const float* Dskip, const void* z, const float* h0, const float* dy,
+                const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm, float* dCm,
+                float* dDskip, float* dz, float* dh0, void* stream) {
+  int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
+  if (rc) return rc;
+  const bool work = batch > 0 && dim > 0 && seqlen > 0;
+  if (dim > 0 && !dA) return S6_ERR_NULL;
+  if (work && (!x || !delta || !A || !Bm || !Cm || !dy || !dx || !ddelta || !dBm || !dCm))
+    return S6_ERR_NULL;
+  const size_t esz = in_dtype == S6_BF16 ? 2 : 4;
+  const void* ins[] = {x, delta, Bm, Cm, z};
+  for (const void* p : ins)
+    if (p && !aligned(p, esz)) return S6_ERR_ALIGN;
+  const void* f32s[] = {A, Dskip, h0, dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0};
+  for (const void* p : f32s)
+    if (p && !aligned(p, 4)) return S6_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dim == 0) return S6_OK;
+  const int64_t nstate = batch * dim * dstate;
+  if (!work) {
+    // no tokens or no rows: the parameter gradients are zero and dh0 = dh_last
+    fill(dA, 0.0f, dim * dstate, st);
+    fill(dDskip, 0.0f, dim, st);
+    if (dh0 && nstate > 0) {
+      int64_t blocks = (nstate + 255) / 256;
+      if (blocks > 65536) blocks = 65536;
+      hipLaunchKernelGGL(s6_copy_state, dim3((unsigned)blocks), dim3(256), 0, st, dh_last, dh0, nstate);
+    }
+    S6_HIP(hipGetLastError(), "s6_scan_bwd fill");
+    return S6_OK;
+  }
+
+  // workspace: segment states (pass 1, fold), per-row and per-block partials
+  const int64_t S = (seqlen + kBwdSeg - 1) / kBwdSeg;
+  const int64_t nagg = S - 1;
+  const int64_t cw = bwd_channels_per_block(dstate);
+  const int64_t nblkb = (dim + cw - 1) / cw;
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const size_t agg_b = (size_t)(nagg > 0 ? nagg : 0) * nstate * sizeof(float);
+  const size_t sd_b = (size_t)(nagg > 0 ? nagg : 0) * batch * dim * sizeof(float);
+  const size_t hin_b = (size_t)S * nstate * sizeof(float);
+  const size_t dap_b = (size_t)nstate * sizeof(float);
+  const size_t ddp_b = (size_t)batch * dim * sizeof(float);
+  const size_t bc_b = (size_t)nblkb * batch * dstate * seqlen * sizeof(float);
+  const size_t total = up(agg_b) + up(sd_b) + up(hin_b) + up(dap_b) + up(ddp_b) + 2 * up(bc_b);
+  void* ws = nullptr;
+  S6_HIP(hipMallocAsync(&ws, total, st), "hipMallocAsync(backward workspace)");
+  char* wp = static_cast<char*>(ws);
+  float* agg = reinterpret_cast<float*>(wp);
+  wp += up(agg_b);
+  float* sd = reinterpret_cast<float*>(wp);
+  wp += up(sd_b);
+  float* hin = reinterpret_cast<float*>(wp);
+  wp += up(hin_b);
+  float* dap = reinterpret_cast<float*>(wp);
+  wp += up(dap_b);
+  float* ddp = reinterpret_cast<float*>(wp);
+  wp += up(ddp_b);
+  float* dbp = reinterpret_cast<float*>(wp);
+  wp += up(bc_b);
+  float* dcp = reinterpret_cast<float*>(wp);
+
+  // pass 1: end state (from zero) and summed delta of every segment but the last
+  if (nagg > 0) {
+    const void* vecptrs[] = {x, delta, Bm};
+    Plan p = make_plan(batch, dim, seqlen, dstate, esz, vecptrs, 3);
+    ScanArgs g;
+    memset(&g, 0, sizeof(g));
+    g.x = x; g.delta = delta; g.Bm = Bm; g.A = A;
+    g.hout = agg; g.hout_stride = nstate; g.sumdelta = sd;
+    g.D = dim; g.L = seqlen; g.N = dstate; g.seg_len = kBwdSeg;
+    rc = launch_scan_any(in_dtype, kModeState, g, p, false, batch, nagg, st);
+  }
+  // the state entering every segment
+  if (rc == S6_OK) {
+    const int64_t blocks = (nstate + 255) / 256;
+    hipLaunchKernelGGL(s6_fold_carries, dim3((unsigned)blocks), dim3(256), 0, st, A, h0, agg, sd, hin,
+                       nullptr, batch, dim, dstate, S, nagg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) rc = hip_fail(e, "s6_fold_carries launch");
+  }
+  if (rc == S6_OK) {
+    BwdArgs b;
+    memset(&b, 0, sizeof(b));
+    b.x = x; b.delta = delta; b.z = z; b.Bm = Bm; b.Cm = Cm; b.A = A; b.Dskip = Dskip;
+    b.dy = dy; b.dh_last = dh_last; b.hin = hin;
+    b.dx = dx; b.ddelta = ddelta; b.dz = dz; b.dA_part = dap; b.dD_part = ddp;
+    b.dB_part = dbp; b.dC_part = dcp; b.dh0 = dh0;
+    b.batch = batch; b.D = dim; b.L = seqlen; b.N = dstate; b.nseg = S;
+    rc = in_dtype == S6_BF16 ? launch_bwd<uint16_t>(b, z != nullptr, st) : launch_bwd<float>(b, z != nullptr, st);
+  }
+  if (rc == S6_OK) {
+    const int64_t tot = batch * dstate * seqlen;
+    int64_t blocks = (tot + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3((unsigned)blocks), dim3(256), 0, st, dbp, dBm, nblkb, tot);
+    hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3((unsigned)blocks), dim3(256), 0, st, dcp, dCm, nblkb, tot);
+    const int64_t rows = dim * dstate;
+    hipLaunchKernelGGL(s6_bwd_reduce_rows, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, dap, ddp, dA,
+                       dDskip, batch, dim, dstate);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) rc = hip_fail(e, "s6_bwd reduction launch");
+  }
+  hipError_t e = hipFreeAsync(ws, st);
+  if (rc == S6_OK && e != hipSuccess) rc = hip_fail(e, "hipFreeAsync(backward workspace)");
+  return rc;
 }
 
 }  // extern "C"

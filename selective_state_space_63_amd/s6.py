@@ -48,6 +48,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.s6_last_state_ex.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32] + [vp] * 5
     lib.s6_state_update_ex.restype = i32
     lib.s6_state_update_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, i32] + [vp] * 7
+    lib.s6_scan_bwd.restype = i32
+    lib.s6_scan_bwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 19
     if path is None:
         _lib = lib
     return lib
@@ -194,3 +196,40 @@ def state_update(h, x, delta, A, Bm, Cm, D=None, z=None, y=None, delta_bias=None
                                             _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(y), _stream())
     _check(rc)
     return y
+
+
+def scan_bwd(x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_last=None):
+    """Gradients of <dy, y> + <dh_last, h_last> for scan_fwd with the same
+    inputs (plain step).  dy: (batch, dim, L) fp32; dh_last: (batch, dim, N)
+    fp32 or None.  Returns a dict of fp32 tensors: dx, ddelta (batch, dim, L),
+    dA (dim, N), dBm, dCm (batch, N, L), dh0 (batch, dim, N), and dD (dim,)
+    when D is given, dz (batch, dim, L) when z is given."""
+    bsz, dim, L = x.shape
+    N = A.shape[1]
+    dt = x.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported input dtype {dt}")
+    _req(x, "x", (bsz, dim, L), dt)
+    _req(delta, "delta", (bsz, dim, L), dt)
+    _req(A, "A", (dim, N), torch.float32)
+    _req(Bm, "Bm", (bsz, N, L), dt)
+    _req(Cm, "Cm", (bsz, N, L), dt)
+    _opt(D, "D", (dim,), torch.float32)
+    _opt(z, "z", (bsz, dim, L), dt)
+    _opt(h0, "h0", (bsz, dim, N), torch.float32)
+    _req(dy, "dy", (bsz, dim, L), torch.float32)
+    _opt(dh_last, "dh_last", (bsz, dim, N), torch.float32)
+    f = dict(dtype=torch.float32, device=x.device)
+    g = {"dx": torch.empty((bsz, dim, L), **f), "ddelta": torch.empty((bsz, dim, L), **f),
+         "dA": torch.empty((dim, N), **f), "dBm": torch.empty((bsz, N, L), **f),
+         "dCm": torch.empty((bsz, N, L), **f), "dh0": torch.empty((bsz, dim, N), **f)}
+    if D is not None:
+        g["dD"] = torch.empty((dim,), **f)
+    if z is not None:
+        g["dz"] = torch.empty((bsz, dim, L), **f)
+    rc = load_library().s6_scan_bwd(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+                                    _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(g["dx"]),
+                                    _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dBm"]), _ptr(g["dCm"]),
+                                    _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g["dh0"]), _stream())
+    _check(rc)
+    return g

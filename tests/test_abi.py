@@ -47,7 +47,7 @@ def codes():
 
 
 def test_header_declares_the_entry_points():
-    assert header_functions() == ["s6_last_state", "s6_last_state_ex", "s6_scan_fwd", "s6_scan_fwd_ex",
+    assert header_functions() == ["s6_last_state", "s6_last_state_ex", "s6_scan_bwd", "s6_scan_fwd", "s6_scan_fwd_ex",
                                   "s6_state_update", "s6_state_update_ex", "s6_status_str", "s6_version"]
 
 
@@ -146,6 +146,25 @@ def test_option_entry_points_validation(lib, codes):
     assert g(2, 64, 16, 0, P, P, P, P_ODD, 1, P, P, P, None, None, P, None) == codes["S6_ERR_ALIGN"]
     assert g(2, 64, 16, 0, None, P, P, P, 1, P, P, P, None, None, P, None) == codes["S6_ERR_NULL"]
     assert g(2, 0, 16, 0, P, P, P, P, 3, P, P, P, None, None, P, None) == codes["S6_OK"]
+
+
+def test_backward_validation(lib, codes):
+    f = lib.s6_scan_bwd
+
+    def bwd(b=2, d=64, L=32, n=16, dt=1, x=P, dy=P, dA=P, dB=P, dz=None, dh0=None):
+        return f(b, d, L, n, dt, x, P, P, P, P, None, None, None, dy, None, P, P, dA, dB, P, None, dz, dh0, None)
+
+    assert bwd(dt=3) == codes["S6_ERR_DTYPE"]
+    assert bwd(n=0) == codes["S6_ERR_UNSUPPORTED"]
+    assert bwd(n=33) == codes["S6_ERR_UNSUPPORTED"]
+    assert bwd(L=-1) == codes["S6_ERR_SHAPE"]
+    assert bwd(x=None) == codes["S6_ERR_NULL"]
+    assert bwd(dy=None) == codes["S6_ERR_NULL"]
+    assert bwd(dA=None) == codes["S6_ERR_NULL"]
+    assert bwd(dB=None) == codes["S6_ERR_NULL"]
+    assert bwd(dz=P_ODD) == codes["S6_ERR_ALIGN"]
+    assert bwd(dh0=P_ODD) == codes["S6_ERR_ALIGN"]
+    assert bwd(d=0, dA=None) == codes["S6_OK"]  # no channels: nothing to write
 
 
 def test_binding_refuses_host_tensors():

@@ -1,0 +1,123 @@
+"""Parity of the backward (s6_scan_bwd, §8(f) row f1) against the fp64
+oracle's reverse-mode gradients.  Error metric: per element
+|gpu - oracle| / m with m the oracle's magnitude of that gradient element
+(the same sums over absolute values); bars 1e-5 (fp32 inputs) and 2e-3
+(bf16 inputs), as for the forward.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import TOL, dev, host64, problem, scaled  # noqa: E402
+from selective_state_space_63_amd import synth  # noqa: E402
+
+GRADS = [("dx", "dx"), ("ddelta", "ddelta"), ("dA", "dA"), ("dBm", "dBm"), ("dCm", "dCm"),
+         ("dD", "dDskip"), ("dz", "dz"), ("dh0", "dh0")]
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_63_amd import s6
+    s6.load_library()
+    return torch
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _cotangents(w, seed=7):
+    g = np.random.default_rng(seed)
+    dy = g.standard_normal((w.batch, w.dim, w.seqlen)).astype(np.float32)
+    dhl = g.standard_normal((w.batch, w.dim, w.dstate)).astype(np.float32)
+    return dy, dhl
+
+
+def _check_bwd(oracle, w, with_h0=True, with_dhl=True, use_D=True):
+    from selective_state_space_63_amd import s6
+    d, o = problem(w, with_h0)
+    if not use_D:
+        d["D"] = None
+        o["Dskip"] = None
+    dy, dhl = _cotangents(w)
+    dhl = dhl if with_dhl else None
+    g = s6.scan_bwd(d["x"], d["delta"], d["A"], d["Bm"], d["Cm"], dev(dy, synth.F32), D=d["D"], z=d["z"],
+                    h0=d["h0"], dh_last=None if dhl is None else dev(dhl, synth.F32))
+    import torch
+    torch.cuda.synchronize()
+    r = oracle.scan_bwd(o["x"], o["delta"], o["A"], o["Bm"], o["Cm"], dy.astype(np.float64), Dskip=o["Dskip"],
+                        z=o["z"], h0=o["h0"], dh_last=None if dhl is None else dhl.astype(np.float64))
+    tol = TOL[w.dtype]
+    errs = {}
+    for gk, ok in GRADS:
+        if gk not in g:
+            continue
+        errs[gk] = scaled(host64(g[gk]), r[ok], r["m" + ok])
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, (w.name, bad, errs)
+    return errs
+
+
+SHAPES = [
+    # batch, dim, N, L, dtype, gate
+    (1, 16, 4, 256, synth.F32, False),      # the fp32 workload's shape
+    (2, 65, 16, 100, synth.BF16, True),     # ragged channel block, partial segment
+    (1, 64, 16, 200, synth.BF16, True),     # several segments, ragged tail
+    (2, 40, 32, 48, synth.BF16, True),      # two states per lane
+    (1, 63, 5, 65, synth.F32, True),        # dstate 5, one token past a segment
+    (3, 33, 16, 129, synth.F32, True),
+    (1, 1, 1, 1, synth.F32, False),
+    (2, 7, 3, 17, synth.BF16, False),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b{}_d{}_n{}_l{}_{}_{}".format(*s))
+def test_backward_small(torch_cuda, oracle, shape):
+    b, dm, n, L, dt, gate = shape
+    w = synth.custom(b, dm, n, L, dt, gate, seed=4000 + L + dm)
+    _say(f"[case] backward {w.name}")
+    _check_bwd(oracle, w)
+
+
+def test_backward_without_optional_inputs(torch_cuda, oracle):
+    w = synth.custom(2, 50, 16, 80, synth.BF16, True, seed=4100)
+    _say(f"[case] backward, no h0 / dh_last / D {w.name}")
+    _check_bwd(oracle, w, with_h0=False, with_dhl=False, use_D=False)
+
+
+def test_backward_repeatable(torch_cuda):
+    import torch
+    from selective_state_space_63_amd import s6
+    w = synth.custom(2, 70, 16, 150, synth.BF16, True, seed=4200)
+    _say(f"[case] backward repeat {w.name}")
+    d, _ = problem(w, True)
+    dy, dhl = _cotangents(w)
+    args = (d["x"], d["delta"], d["A"], d["Bm"], d["Cm"], dev(dy, synth.F32))
+    kw = dict(D=d["D"], z=d["z"], h0=d["h0"], dh_last=dev(dhl, synth.F32))
+    g1 = s6.scan_bwd(*args, **kw)
+    g2 = s6.scan_bwd(*args, **kw)
+    torch.cuda.synchronize()
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+
+
+def test_backward_empty(torch_cuda):
+    import torch
+    from selective_state_space_63_amd import s6
+    _say("[case] backward empty")
+    f = dict(device="cuda", dtype=torch.float32)
+    x = torch.empty((2, 3, 0), **f)
+    A = -torch.ones((3, 4), **f)
+    Bm = torch.empty((2, 4, 0), **f)
+    dhl = torch.randn((2, 3, 4), **f)
+    g = s6.scan_bwd(x, x, A, Bm, Bm, x, D=torch.ones(3, **f), dh_last=dhl)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(g["dA"]) == 0 and torch.count_nonzero(g["dD"]) == 0
+    assert torch.equal(g["dh0"], dhl)
