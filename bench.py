@@ -83,6 +83,58 @@ def scan_valu_slots(w, skip=True):
     return w.batch * w.dim * w.seqlen * per
 
 
+def bwd_bytes(w, in_bytes):
+    """Algorithmic bytes of one backward: x, delta, z and dy (fp32) in, dx,
+    ddelta, dz (fp32) out per token-channel; B, C in and dB, dC (fp32) out
+    per (batch, state, token); A, D and their gradients once."""
+    T = w.batch * w.dim * w.seqlen
+    b = T * (3 * in_bytes + 4 + 3 * 4)
+    b += w.batch * w.dstate * w.seqlen * (2 * in_bytes + 2 * 4)
+    b += 2 * (4 * w.dim * w.dstate + 4 * w.dim)
+    return b
+
+
+def bwd_valu_slots(w):
+    """Algorithmic VALU lane-slots of one backward with the states recomputed
+    once: per (token, channel, state) the forward recurrence (exponent
+    argument, exponential, input term, update: 5 slots), the adjoint update
+    and its carry (2), and the products for dx, ddelta (3), dA, dB and dC (1
+    each): 13; per (token, channel) delta*x, the gate and its derivative and
+    the dx, ddelta, dz, dD terms: 16."""
+    return w.batch * w.dim * w.seqlen * (13 * w.dstate + 16)
+
+
+def bench_backward(w, steps=10, warmup=3):
+    """Times s6_scan_bwd on workload w (dy random, no dh_last)."""
+    import torch
+    from selective_state_space_63_amd import s6, synth
+    inp = synth.device_full(w)
+    dy = torch.randn((w.batch, w.dim, w.seqlen), device="cuda", dtype=torch.float32)
+
+    def step():
+        s6.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], dy, D=inp["Dskip"], z=inp["z"])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    in_bytes = 2 if w.dtype == synth.BF16 else 4
+    gbs = bwd_bytes(w, in_bytes) / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "ms_mean": round(ms, 4), "GBps": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "token_channels_per_s": w.batch * w.dim * w.seqlen / (ms * 1e-3),
+            "valu_frac": round(bwd_valu_slots(w) / (ms * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4),
+            "note": "s6_scan_bwd: checkpoint pass + reverse adjoint kernel + reductions; all gradients fp32"}
+
+
 def decode_step_bytes(batch, dim, N, in_bytes, gate=True):
     """One decode token: h read and written (fp32), x, delta (, z) in, y out
     (fp32) per channel; B, C per (batch, state); A and D once."""
@@ -464,6 +516,9 @@ def main():
         _, tc, _ = bench_scan(wm, 20, 2, flush=True)
         out["m130_hot"] = scan_line("m130", wm, th, 2, "repeated; inputs stay in the 256 MB Infinity Cache", True)
         out["m130_cold"] = scan_line("m130", wm, tc, 2, "a 512 MiB write between scans evicts the inputs", False)
+        torch.cuda.empty_cache()
+        print(f"[bench] backward {w.name}", file=sys.stderr, flush=True)
+        out["backward"] = bench_backward(w)
         torch.cuda.empty_cache()
         print(f"[bench] scan {w.name} with the step options", file=sys.stderr, flush=True)
         _, ts, _ = bench_scan(w, 50, 50, softplus=True)

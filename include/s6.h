@@ -166,7 +166,7 @@ int s6_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, int in_dtype,
  * Sums over channels (dBm, dCm), over batch rows and tokens (dA, dDskip) are
  * taken in a fixed order: repeated calls give identical bits.  Workspace from
  * the stream-ordered allocator (hipMallocAsync), released on the stream before
- * returning: about 2*(dim/32)*batch*dstate*seqlen + 2*batch*dim*dstate*seqlen/64
+ * returning: about 2*(dim/16)*batch*dstate*seqlen + 2*batch*dim*dstate*seqlen/64
  * floats. */
 int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                 const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,

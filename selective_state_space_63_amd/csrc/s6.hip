@@ -879,7 +879,7 @@ __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
 // (plain step).  The states are recomputed, never stored per token: a
 // state-only pass and the carry fold give the state entering every segment of
 // kBwdSeg tokens (the same kernels as a segmented forward scan); this kernel
-// then walks the segments of a (batch row, 32-channel block) from the last to
+// then walks the segments of a (batch row, 16-channel block) from the last to
 // the first.  Per segment it stages the inputs in LDS, recomputes the states
 // at the four chunk starts, and per 16-token chunk (last first) recomputes
 // the chunk's states and transitions in registers and runs the adjoint
@@ -889,14 +889,15 @@ __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
 // (l & 15) * SPL + j.  Sums over states (for dx, ddelta and the pre-gate
 // output) are taken across the 16 lanes of a row with DPP rotations; sums
 // over channels (dB, dC) across the 4 rows of a wave with permlane swaps,
-// across the 8 waves in LDS, and across channel blocks by a second kernel
+// across the 4 waves in LDS, and across channel blocks by a second kernel
 // from per-block partials (a fixed order: results are bitwise repeatable).
 constexpr int kBwdSeg = 64;    // tokens per recomputation segment
 
-// Waves per workgroup (4 channels each): 8 with one state per lane, 4 with
-// two (the LDS of a workgroup stays under 64 KB).
+// Waves per workgroup (4 channels each).  The kernel needs 150-190 VGPRs,
+// i.e. two waves per SIMD: two 4-wave workgroups per CU, whose barriers fall
+// at different times, run faster than one 8-wave workgroup.
 template <int SPL>
-constexpr int bwd_waves() { return SPL == 1 ? 8 : 4; }
+constexpr int bwd_waves() { return 4; }
 
 template <int SPL>
 constexpr size_t bwd_lds_bytes(bool) {
@@ -1052,65 +1053,109 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
       for (int k = 0; k < 4; ++k) {
 #pragma unroll
         for (int j = 0; j < SPL; ++j) hc[k][j] = h[j];
-        for (int i = 0; i < 16; ++i) {
-          const int t = 16 * k + i;
-          const float dl = sdl[c * KS + t];
-          const float u = dl * sx[c * KS + t];
+        for (int g = 0; g < 4; ++g) {
+          // one group of 4 tokens at a time: the compiler would otherwise
+          // hoist every LDS read of the segment and run out of registers
+          __builtin_amdgcn_sched_barrier(0);
+          const int t = 16 * k + 4 * g;
+          const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KS + t);
+          const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KS + t);
+          const float dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+          const float u[4] = {dl4.x * x4.x, dl4.y * x4.y, dl4.z * x4.z, dl4.w * x4.w};
 #pragma unroll
-          for (int j = 0; j < SPL; ++j)
-            h[j] = __builtin_fmaf(fast_exp2(dl * A2[j]), h[j], u * sB[(nl * SPL + j) * KS + t]);
+          for (int j = 0; j < SPL; ++j) {
+            const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KS + t);
+            const float Bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h[j] = __builtin_fmaf(fast_exp2(dl[i] * A2[j]), h[j], u[i] * Bv[i]);
+          }
         }
       }
     }
 
     for (int k = 3; k >= 0; --k) {
-      // the chunk's transitions and states: hist[j][i] = h before token i
-      float ea[SPL][16], hist[SPL][17];
+      // the chunk's states: hist[j][i] = h before token i (the transitions
+      // are recomputed in the adjoint loop: keeping them costs 16 registers
+      // per state, which halves the waves per SIMD)
+      float hist[SPL][17];
 #pragma unroll
       for (int j = 0; j < SPL; ++j) hist[j][0] = hc[k][j];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = 16 * k + i;
-        const float dl = sdl[c * KS + t];
-        const float u = dl * sx[c * KS + t];
+      for (int g = 0; g < 4; ++g) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int t = 16 * k + 4 * g;
+        const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KS + t);
+        const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KS + t);
+        const float dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+        const float u[4] = {dl4.x * x4.x, dl4.y * x4.y, dl4.z * x4.z, dl4.w * x4.w};
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
-          ea[j][i] = fast_exp2(dl * A2[j]);
-          hist[j][i + 1] = __builtin_fmaf(ea[j][i], hist[j][i], u * sB[(nl * SPL + j) * KS + t]);
+          const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KS + t);
+          const float Bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            hist[j][4 * g + i + 1] = __builtin_fmaf(fast_exp2(dl[i] * A2[j]), hist[j][4 * g + i], u[i] * Bv[i]);
         }
       }
       // adjoint, last token first; lane nl keeps the row sums of token nl
       float k1 = 0.0f, k2 = 0.0f, k3 = 0.0f;
 #pragma unroll
       for (int g4 = 3; g4 >= 0; --g4) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int t4 = 16 * k + 4 * g4;
+        const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KS + t4);
+        const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KS + t4);
+        const float4 y4 = *reinterpret_cast<const float4*>(sdyc + c * KS + t4);
+        const float dlv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+        const float xvv[4] = {x4.x, x4.y, x4.z, x4.w};
+        const float dycv[4] = {y4.x, y4.y, y4.z, y4.w};
+        float Bv[SPL][4], Cv[SPL][4];
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+          const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KS + t4);
+          const float4 c4 = *reinterpret_cast<const float4*>(sC + (nl * SPL + j) * KS + t4);
+          Bv[j][0] = b4.x; Bv[j][1] = b4.y; Bv[j][2] = b4.z; Bv[j][3] = b4.w;
+          Cv[j][0] = c4.x; Cv[j][1] = c4.y; Cv[j][2] = c4.z; Cv[j][3] = c4.w;
+        }
         float pb[SPL][4], pc[SPL][4];
+        float s1[4], s2[4], s3[4];
 #pragma unroll
         for (int ii = 3; ii >= 0; --ii) {
           const int i = 4 * g4 + ii;
-          const int t = 16 * k + i;
-          const float dl = sdl[c * KS + t];
-          const float xv = sx[c * KS + t];
-          const float dyc = sdyc[c * KS + t];
-          float s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+          const float dl = dlv[ii], xv = xvv[ii], dyc = dycv[ii];
+          s1[ii] = 0.0f;
+          s2[ii] = 0.0f;
+          s3[ii] = 0.0f;
 #pragma unroll
           for (int j = 0; j < SPL; ++j) {
-            const float Bv = sB[(nl * SPL + j) * KS + t];
-            const float Cv = sC[(nl * SPL + j) * KS + t];
-            const float lam = __builtin_fmaf(dyc, Cv, mu[j]);
-            mu[j] = ea[j][i] * lam;
-            const float r = lam * (ea[j][i] * hist[j][i]);
-            s1 = __builtin_fmaf(lam, Bv, s1);
-            s2 = __builtin_fmaf(An[j], r, s2);
-            s3 = __builtin_fmaf(Cv, hist[j][i + 1], s3);
+            const float ea = fast_exp2(dl * A2[j]);
+            const float lam = __builtin_fmaf(dyc, Cv[j][ii], mu[j]);
+            mu[j] = ea * lam;
+            const float r = lam * (ea * hist[j][i]);
+            s1[ii] = __builtin_fmaf(lam, Bv[j][ii], s1[ii]);
+            s2[ii] = __builtin_fmaf(An[j], r, s2[ii]);
+            s3[ii] = __builtin_fmaf(Cv[j][ii], hist[j][i + 1], s3[ii]);
             dA[j] = __builtin_fmaf(dl, r, dA[j]);
             pb[j][ii] = lam * (dl * xv);
             pc[j][ii] = dyc * hist[j][i + 1];
           }
           dD = __builtin_fmaf(dyc, xv, dD);
-          s1 = row_sum16(s1);
-          s2 = row_sum16(s2);
-          if constexpr (GATE) s3 = row_sum16(s3);
-          if (nl == i) { k1 = s1; k2 = s2; k3 = s3; }
+        }
+        // the running sums are updated here (left alone, the compiler defers
+        // them to the end of the chunk and keeps all their operands live)
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) asm volatile("" : "+v"(dA[j]), "+v"(mu[j]));
+        asm volatile("" : "+v"(dD));
+        // sums over the row's states for the 4 tokens (independent chains)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          s1[ii] = row_sum16(s1[ii]);
+          s2[ii] = row_sum16(s2[ii]);
+          if constexpr (GATE) s3[ii] = row_sum16(s3[ii]);
+          const bool mine = nl == 4 * g4 + ii;
+          k1 = mine ? s1[ii] : k1;
+          k2 = mine ? s2[ii] : k2;
+          k3 = mine ? s3[ii] : k3;
         }
         // channel sums of the 4 tokens over the wave's rows, then to LDS
 #pragma unroll
