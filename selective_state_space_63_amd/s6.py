@@ -233,3 +233,25 @@ def scan_bwd(x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_last=None):
                                     _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g["dh0"]), _stream())
     _check(rc)
     return g
+
+
+class SelectiveScan(torch.autograd.Function):
+    """scan_fwd with its gradients from scan_bwd, for training with torch
+    autograd: y = SelectiveScan.apply(x, delta, A, Bm, Cm, D, z, h0).  D, z
+    and h0 may be None.  The forward keeps only its inputs; the backward
+    recomputes the states (plain step)."""
+
+    @staticmethod
+    def forward(ctx, x, delta, A, Bm, Cm, D=None, z=None, h0=None):
+        y = scan_fwd(x, delta, A, Bm, Cm, D=D, z=z, h0=h0)
+        ctx.save_for_backward(x, delta, A, Bm, Cm, D, z, h0)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, delta, A, Bm, Cm, D, z, h0 = ctx.saved_tensors
+        g = scan_bwd(x, delta, A, Bm, Cm, dy.contiguous().to(torch.float32), D=D, z=z, h0=h0)
+        cast = lambda t, like: None if t is None else t.to(like.dtype)  # noqa: E731
+        return (cast(g["dx"], x), cast(g["ddelta"], delta), g["dA"], cast(g["dBm"], Bm), cast(g["dCm"], Cm),
+                g.get("dD"), cast(g.get("dz"), x) if z is not None else None,
+                g["dh0"] if h0 is not None else None)
