@@ -887,7 +887,8 @@ __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
 //
 // Lane l of wave w: channel c = 4w + (l >> 4) of the block, states
 // (l & 15) * SPL + j.  Sums over states (for dx, ddelta and the pre-gate
-// output) are taken across the 16 lanes of a row with DPP rotations; sums
+// output) are taken across the 16 lanes of a row with a DPP butterfly that
+// leaves token l's sums in lane l; sums
 // over channels (dB, dC) across the 4 rows of a wave with permlane swaps,
 // across the 4 waves in LDS, and across channel blocks by a second kernel
 // from per-block partials (a fixed order: results are bitwise repeatable).
@@ -927,13 +928,26 @@ struct BwdArgs {
   int64_t batch, D, L, N, nseg;
 };
 
-// Sum over the 16 lanes of a row, in every lane (DPP row rotations).
-__device__ __forceinline__ float row_sum16(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false));
-  return v;
+// Sums over the 16 lanes of a row of 16 per-token values, leaving token l's
+// sum in lane l of the row: a butterfly over the lane partners l^8 (row
+// rotation by 8), l^7 (half-row mirror), l^2 and l^1 (quad permutations).  At
+// each step a lane keeps the half of its values whose token index has the
+// lane's bit (8, 4, 2, 1), and adds its partner's copy of that half; the
+// partner shares the bits already used, so both hold the same tokens.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int nl) {
+  const bool b3 = nl & 8, b2 = nl & 4, b1 = nl & 2, b0 = nl & 1;
+  float a8[8], a4[4], a2[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a8[j] = (b3 ? v[j + 8] : v[j]) + dpp_f<0x128>(b3 ? v[j] : v[j + 8]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a4[j] = (b2 ? a8[j + 4] : a8[j]) + dpp_f<0x141>(b2 ? a8[j] : a8[j + 4]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) a2[j] = (b1 ? a4[j + 2] : a4[j]) + dpp_f<0x4E>(b1 ? a4[j] : a4[j + 2]);
+  return (b0 ? a2[1] : a2[0]) + dpp_f<0xB1>(b0 ? a2[0] : a2[1]);
 }
 
 // Sums over the 4 rows (channels) of a wave for 4 tokens at once: v[k] is
@@ -1098,7 +1112,7 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
         }
       }
       // adjoint, last token first; lane nl keeps the row sums of token nl
-      float k1 = 0.0f, k2 = 0.0f, k3 = 0.0f;
+      float s1[16], s2[16], s3[16];  // this lane's terms of the state sums, per token
 #pragma unroll
       for (int g4 = 3; g4 >= 0; --g4) {
         __builtin_amdgcn_sched_barrier(0);
@@ -1118,23 +1132,22 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
           Cv[j][0] = c4.x; Cv[j][1] = c4.y; Cv[j][2] = c4.z; Cv[j][3] = c4.w;
         }
         float pb[SPL][4], pc[SPL][4];
-        float s1[4], s2[4], s3[4];
 #pragma unroll
         for (int ii = 3; ii >= 0; --ii) {
           const int i = 4 * g4 + ii;
           const float dl = dlv[ii], xv = xvv[ii], dyc = dycv[ii];
-          s1[ii] = 0.0f;
-          s2[ii] = 0.0f;
-          s3[ii] = 0.0f;
+          s1[i] = 0.0f;
+          s2[i] = 0.0f;
+          s3[i] = 0.0f;
 #pragma unroll
           for (int j = 0; j < SPL; ++j) {
             const float ea = fast_exp2(dl * A2[j]);
             const float lam = __builtin_fmaf(dyc, Cv[j][ii], mu[j]);
             mu[j] = ea * lam;
             const float r = lam * (ea * hist[j][i]);
-            s1[ii] = __builtin_fmaf(lam, Bv[j][ii], s1[ii]);
-            s2[ii] = __builtin_fmaf(An[j], r, s2[ii]);
-            s3[ii] = __builtin_fmaf(Cv[j][ii], hist[j][i + 1], s3[ii]);
+            s1[i] = __builtin_fmaf(lam, Bv[j][ii], s1[i]);
+            s2[i] = __builtin_fmaf(An[j], r, s2[i]);
+            s3[i] = __builtin_fmaf(Cv[j][ii], hist[j][i + 1], s3[i]);
             dA[j] = __builtin_fmaf(dl, r, dA[j]);
             pb[j][ii] = lam * (dl * xv);
             pc[j][ii] = dyc * hist[j][i + 1];
@@ -1146,17 +1159,6 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
 #pragma unroll
         for (int j = 0; j < SPL; ++j) asm volatile("" : "+v"(dA[j]), "+v"(mu[j]));
         asm volatile("" : "+v"(dD));
-        // sums over the row's states for the 4 tokens (independent chains)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          s1[ii] = row_sum16(s1[ii]);
-          s2[ii] = row_sum16(s2[ii]);
-          if constexpr (GATE) s3[ii] = row_sum16(s3[ii]);
-          const bool mine = nl == 4 * g4 + ii;
-          k1 = mine ? s1[ii] : k1;
-          k2 = mine ? s2[ii] : k2;
-          k3 = mine ? s3[ii] : k3;
-        }
         // channel sums of the 4 tokens over the wave's rows, then to LDS
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
@@ -1165,6 +1167,10 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
           red[((w * 2 + 1) * 16 + tok) * NS + nl * SPL + j] = rows_sum4(pc[j]);
         }
       }
+      // sums over the row's states: lane nl gets those of token nl
+      const float k1 = row_reduce_scatter16(s1, nl);
+      const float k2 = row_reduce_scatter16(s2, nl);
+      const float k3 = GATE ? row_reduce_scatter16(s3, nl) : 0.0f;
       // outputs of token nl of the chunk for this lane's channel
       {
         const int t = 16 * k + nl;
