@@ -378,6 +378,57 @@ def cpu_baseline(w, inp, budget_s=10.0):
             "token_channels_per_s": done_tc / spent}
 
 
+def cpu_backward_baseline(w, inp, channels=256):
+    """The oracle's backward (fp64; its threads run over batch rows) on every
+    batch row of the first `channels` channels of the same inputs, with a
+    random dy: token-channels per second."""
+    import numpy as np
+    import torch
+    from oracle.oracle import Oracle
+    o = Oracle()
+
+    def h64(t):
+        return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+    c = min(channels, w.dim)
+    x = h64(inp["x"][:, :c])
+    dl = h64(inp["delta"][:, :c])
+    z = h64(inp["z"][:, :c])
+    dy = np.random.default_rng(0).standard_normal(x.shape)
+    t0 = time.perf_counter()
+    o.scan_bwd(x, dl, h64(inp["A"][:c]), h64(inp["Bm"]), h64(inp["Cm"]), dy, Dskip=h64(inp["Dskip"][:c]), z=z)
+    spent = time.perf_counter() - t0
+    return {"token_channels_per_s": w.batch * c * w.seqlen / spent, "cores": min(o.num_threads(), w.batch),
+            "kind": "oracle", "seconds": round(spent, 2),
+            "sample": f"all {w.batch} batch rows, the first {c} of {w.dim} channels"}
+
+
+def cpu_options_baseline(w, inp, budget_s=3.0):
+    """The oracle's scan with the softplus step and the exact hold, on whole
+    batch rows of the same inputs until `budget_s` is spent."""
+    import numpy as np
+    import torch
+    from oracle.oracle import Oracle
+    o = Oracle()
+
+    def h64(t):
+        return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+    A, Dk = h64(inp["A"]), h64(inp["Dskip"])
+    bias = np.full(w.dim, -4.0)
+    spent, rows = 0.0, 0
+    while spent < budget_s or rows == 0:
+        b = rows % w.batch
+        args = dict(x=h64(inp["x"][b:b + 1]), delta=h64(inp["delta"][b:b + 1]), A=A, Bm=h64(inp["Bm"][b:b + 1]),
+                    Cm=h64(inp["Cm"][b:b + 1]), Dskip=Dk, z=h64(inp["z"][b:b + 1]))
+        t0 = time.perf_counter()
+        o.scan(**args, delta_bias=bias, softplus=True, zoh=True)
+        spent += time.perf_counter() - t0
+        rows += 1
+    return {"token_channels_per_s": rows * w.dim * w.seqlen / spent, "cores": o.num_threads(), "kind": "oracle",
+            "sample": f"{rows} batch rows ({w.dim} channels x {w.seqlen} tokens each), {spent:.2f} s"}
+
+
 def cpu_decode_baseline(w, budget_s=3.0):
     """The oracle's single-token step (fp64) on the decode workload's shape,
     repeated until `budget_s` is spent: state-element updates per second."""
@@ -532,6 +583,10 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, inp)
         if "decode" in out:
             out["decode"]["cpu_baseline"] = cpu_decode_baseline(synth.WORKLOADS["decode"])
+        if "backward" in out:
+            out["backward"]["cpu_baseline"] = cpu_backward_baseline(w, inp)
+        if "softplus_zoh" in out:
+            out["softplus_zoh"]["cpu_baseline"] = cpu_options_baseline(w, inp)
     print(json.dumps(out), flush=True)
 
 

@@ -920,12 +920,17 @@ struct BwdArgs {
   float* dx;              // (batch, D, L)
   float* ddelta;          // (batch, D, L)
   float* dz;              // (batch, D, L), gate only
-  float* dA_part;         // (batch, D, N): sums over t of one batch row
-  float* dD_part;         // (batch, D)
+  float* dA_part;         // (G, batch, D, N): sums over the tokens of one batch row and part
+  float* dD_part;         // (G, batch, D)
   float* dB_part;         // (nblk, batch, N, L)
   float* dC_part;         // (nblk, batch, N, L)
   float* dh0;             // nullable (batch, D, N)
+  const float* mu_in;     // (G, batch*D*N): adjoint carry entering each part from the right, or
+                          // null (one part: the carry is dh_last)
+  float* carry_M;         // (G, batch*D*N): carry leaving each part from a zero carry-in
+  float* carry_SD;        // (G, batch*D): summed delta of each part
   int64_t batch, D, L, N, nseg;
+  int64_t seg_per_part;   // segments per part (the sequence is cut into G parts, blockIdx.y)
 };
 
 // Sums over the 16 lanes of a row of 16 per-token values, leaving token l's
@@ -1005,6 +1010,12 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
   const In* Cp = static_cast<const In*>(a.Cm);
   const float dsk = (a.Dskip && chv) ? a.Dskip[d] : 0.0f;
 
+  // this workgroup's part of the sequence: segments [s_begin, s_end)
+  const int64_t part = blockIdx.y;
+  const int64_t nstate = a.batch * D * N;
+  const int64_t s_begin = part * a.seg_per_part;
+  const int64_t s_end = s_begin + a.seg_per_part < a.nseg ? s_begin + a.seg_per_part : a.nseg;
+
   float A2[SPL], An[SPL], mu[SPL], dA[SPL];
   bool sv[SPL];
 #pragma unroll
@@ -1013,12 +1024,15 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
     sv[j] = chv && n < N;
     An[j] = sv[j] ? a.A[d * N + n] : 0.0f;
     A2[j] = An[j] * kLog2e;
-    mu[j] = (sv[j] && a.dh_last) ? a.dh_last[(b * D + d) * N + n] : 0.0f;  // a_{t+1} lambda_{t+1}
+    // a_{t+1} lambda_{t+1} entering the part's last token
+    mu[j] = !sv[j] ? 0.0f
+            : a.mu_in ? a.mu_in[part * nstate + (b * D + d) * N + n]
+            : a.dh_last ? a.dh_last[(b * D + d) * N + n] : 0.0f;
     dA[j] = 0.0f;
   }
   float dD = 0.0f;
 
-  for (int64_t s = a.nseg - 1; s >= 0; --s) {
+  for (int64_t s = s_end - 1; s >= s_begin; --s) {
     const int64_t tb = s * KS;
     const int64_t tl = L - tb < KS ? L - tb : KS;  // valid tokens of the segment
     __syncthreads();  // the previous segment's reads of the staged inputs are done
@@ -1207,11 +1221,123 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
     for (int j = 0; j < SPL; ++j) {
       const int64_t n = (int64_t)nl * SPL + j;
       if (n < N) {
-        a.dA_part[(b * D + d) * N + n] = dA[j];
-        if (a.dh0) a.dh0[(b * D + d) * N + n] = mu[j];
+        a.dA_part[part * nstate + (b * D + d) * N + n] = dA[j];
+        if (a.dh0 && part == 0) a.dh0[(b * D + d) * N + n] = mu[j];
       }
     }
-    if (nl == 0) a.dD_part[b * D + d] = dD;
+    if (nl == 0) a.dD_part[part * a.batch * D + b * D + d] = dD;
+  }
+}
+
+// Adjoint carries of the parts of a long sequence: for part g = blockIdx.y + 1
+// (the first part's carry is never needed), the carry a_t lambda_t that
+// leaves its first token when zero enters its last one, mu <- a_t (dyc_t C_t
+// + mu) from the last token back, and the part's summed delta (compensated),
+// from which exp(A sum delta) carries the right neighbour's carry through.
+template <typename In, bool GATE, int SPL>
+__global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_carry_kernel(BwdArgs a) {
+  constexpr int WB = bwd_waves<SPL>();
+  constexpr int NTHR = 64 * WB;
+  constexpr int CW = 4 * WB;
+  constexpr int NS = 16 * SPL;
+  constexpr int KS = kBwdSeg;
+  extern __shared__ float4 lds4[];
+  float* sdl = reinterpret_cast<float*>(lds4);  // [CW][KS]
+  float* sdyc = sdl + CW * KS;                  // [CW][KS]
+  float* sC = sdyc + CW * KS;                   // [NS][KS]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int nl = lane & 15;
+  const int c = 4 * (tid >> 6) + (lane >> 4);
+  const int64_t D = a.D, L = a.L, N = a.N;
+  const int64_t nblk = (D + CW - 1) / CW;
+  const int64_t b = blockIdx.x / nblk;
+  const int64_t d0 = (blockIdx.x % nblk) * CW;
+  const int64_t rows_valid = D - d0 < CW ? D - d0 : CW;
+  const int64_t d = d0 + c;
+  const bool chv = c < rows_valid;
+  const int64_t part = blockIdx.y + 1;
+  const int64_t nstate = a.batch * D * N;
+  const int64_t s_begin = part * a.seg_per_part;
+  const int64_t s_end = s_begin + a.seg_per_part < a.nseg ? s_begin + a.seg_per_part : a.nseg;
+  const In* dp = static_cast<const In*>(a.delta);
+  const In* zp = static_cast<const In*>(a.z);
+  const In* Cp = static_cast<const In*>(a.Cm);
+
+  float A2[SPL], mu[SPL];
+#pragma unroll
+  for (int j = 0; j < SPL; ++j) {
+    const int64_t n = (int64_t)nl * SPL + j;
+    A2[j] = (chv && n < N) ? a.A[d * N + n] * kLog2e : 0.0f;
+    mu[j] = 0.0f;
+  }
+  float dsum = 0.0f, dcomp = 0.0f;
+  for (int64_t s = s_end - 1; s >= s_begin; --s) {
+    const int64_t tb = s * KS;
+    const int64_t tl = L - tb < KS ? L - tb : KS;
+    __syncthreads();
+    for (int i = tid; i < CW * KS; i += NTHR) {
+      const int cc = i / KS, t = i % KS;
+      const bool ok = cc < rows_valid && t < tl;
+      const int64_t off = (b * D + d0 + (cc < rows_valid ? cc : 0)) * L + tb + (t < tl ? t : 0);
+      float dl = 0.0f, dyc = 0.0f;
+      if (ok) {
+        dl = to_f32(dp[off]);
+        dyc = a.dy[off];
+        if constexpr (GATE) {
+          const float zz = to_f32(zp[off]);
+          dyc *= zz * fast_rcp(1.0f + fast_exp2(-zz * kLog2e));
+        }
+      }
+      sdl[i] = dl;
+      sdyc[i] = dyc;
+    }
+    for (int i = tid; i < NS * KS; i += NTHR) {
+      const int n = i / KS, t = i % KS;
+      const bool ok = n < N && t < tl;
+      sC[i] = ok ? to_f32(Cp[(b * N + (n < N ? n : 0)) * L + tb + (t < tl ? t : 0)]) : 0.0f;
+    }
+    __syncthreads();
+    float cs = 0.0f;
+    for (int t = KS - 1; t >= 0; --t) {
+      const float dlt = sdl[c * KS + t];
+      const float dyct = sdyc[c * KS + t];
+#pragma unroll
+      for (int j = 0; j < SPL; ++j)
+        mu[j] = fast_exp2(dlt * A2[j]) * __builtin_fmaf(dyct, sC[(nl * SPL + j) * KS + t], mu[j]);
+      cs += dlt;
+    }
+    const float tsum = dsum + cs;
+    dcomp += (fabsf(dsum) >= fabsf(cs)) ? (dsum - tsum) + cs : (cs - tsum) + dsum;
+    dsum = tsum;
+  }
+  if (chv) {
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const int64_t n = (int64_t)nl * SPL + j;
+      if (n < N) a.carry_M[part * nstate + (b * D + d) * N + n] = mu[j];
+    }
+    if (nl == 0) a.carry_SD[part * a.batch * D + b * D + d] = dsum + dcomp;
+  }
+}
+
+// Carries entering each part from the right: mu_in[G-1] = dh_last (or 0),
+// mu_in[g-1] = carry_M[g] + exp(A * carry_SD[g]) * mu_in[g].
+__global__ void s6_bwd_fold(const float* __restrict__ A, const float* __restrict__ dh_last,
+                            const float* __restrict__ M, const float* __restrict__ SD, float* __restrict__ mu_in,
+                            int64_t batch, int64_t D, int64_t N, int64_t G) {
+  const int64_t total = batch * D * N;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t n = i % N;
+  const int64_t bd = i / N;
+  const float A2 = A[(bd % D) * N + n] * kLog2e;
+  float mu = dh_last ? dh_last[i] : 0.0f;
+  mu_in[(G - 1) * total + i] = mu;
+  for (int64_t g = G - 1; g >= 1; --g) {
+    mu = __builtin_fmaf(fast_exp2(A2 * SD[g * batch * D + bd]), mu, M[g * total + i]);
+    mu_in[(g - 1) * total + i] = mu;
   }
 }
 
@@ -1544,20 +1670,30 @@ int launch_step_g(const StepArgs& a, hipStream_t st) {
   return launch_step_b<In, GATE, 4, 8>(a, vec_ok(4, 8), st);
 }
 
+// carry: the part-carry kernel (parts 1 .. G-1) instead of the main kernel.
 template <typename In, bool GATE, int SPL>
-int launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+int launch_bwd_t(const BwdArgs& a, int64_t parts, bool carry, hipStream_t st) {
   constexpr int CW = 4 * bwd_waves<SPL>();
   const int64_t nblk = (a.D + CW - 1) / CW;
-  hipLaunchKernelGGL((s6_bwd_kernel<In, GATE, SPL>), dim3((unsigned)(nblk * a.batch)), dim3(64 * bwd_waves<SPL>()),
-                     bwd_lds_bytes<SPL>(GATE), st, a);
-  S6_HIP(hipGetLastError(), "s6_bwd_kernel launch");
+  const dim3 block(64 * bwd_waves<SPL>());
+  if (carry) {
+    const size_t lds = sizeof(float) * ((size_t)2 * CW * kBwdSeg + (size_t)16 * SPL * kBwdSeg);
+    hipLaunchKernelGGL((s6_bwd_carry_kernel<In, GATE, SPL>), dim3((unsigned)(nblk * a.batch), (unsigned)(parts - 1)),
+                       block, lds, st, a);
+    S6_HIP(hipGetLastError(), "s6_bwd_carry_kernel launch");
+  } else {
+    hipLaunchKernelGGL((s6_bwd_kernel<In, GATE, SPL>), dim3((unsigned)(nblk * a.batch), (unsigned)parts), block,
+                       bwd_lds_bytes<SPL>(GATE), st, a);
+    S6_HIP(hipGetLastError(), "s6_bwd_kernel launch");
+  }
   return S6_OK;
 }
 
 template <typename In>
-int launch_bwd(const BwdArgs& a, bool gate, hipStream_t st) {
-  if (a.N <= 16) return gate ? launch_bwd_t<In, true, 1>(a, st) : launch_bwd_t<In, false, 1>(a, st);
-  return gate ? launch_bwd_t<In, true, 2>(a, st) : launch_bwd_t<In, false, 2>(a, st);
+int launch_bwd(const BwdArgs& a, bool gate, int64_t parts, bool carry, hipStream_t st) {
+  if (a.N <= 16)
+    return gate ? launch_bwd_t<In, true, 1>(a, parts, carry, st) : launch_bwd_t<In, false, 1>(a, parts, carry, st);
+  return gate ? launch_bwd_t<In, true, 2>(a, parts, carry, st) : launch_bwd_t<In, false, 2>(a, parts, carry, st);
 }
 
 int bwd_channels_per_block(int64_t dstate) { return dstate <= 16 ? 4 * bwd_waves<1>() : 4 * bwd_waves<2>(); }
@@ -1695,14 +1831,30 @@ int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
   const int64_t nagg = S - 1;
   const int64_t cw = bwd_channels_per_block(dstate);
   const int64_t nblkb = (dim + cw - 1) / cw;
+  // Parts: when the (row, channel block) workgroups fill less than half of
+  // the workgroup slots (few long rows), the sequence is cut into parts run
+  // side by side; the adjoint carry entering each part from the right comes
+  // from a carry pass and a fold.
+  int64_t G = 1;
+  {
+    const int64_t wgs = nblkb * batch;
+    const int64_t slots = (int64_t)cu_count() * (dstate <= 16 ? 4 : 3);
+    if (2 * wgs <= slots) G = slots / wgs < S ? slots / wgs : S;
+    if (G < 1) G = 1;
+  }
+  const int64_t spp = (S + G - 1) / G;  // segments per part
+  G = (S + spp - 1) / spp;
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
   const size_t agg_b = (size_t)(nagg > 0 ? nagg : 0) * nstate * sizeof(float);
   const size_t sd_b = (size_t)(nagg > 0 ? nagg : 0) * batch * dim * sizeof(float);
   const size_t hin_b = (size_t)S * nstate * sizeof(float);
-  const size_t dap_b = (size_t)nstate * sizeof(float);
-  const size_t ddp_b = (size_t)batch * dim * sizeof(float);
+  const size_t dap_b = (size_t)G * nstate * sizeof(float);
+  const size_t ddp_b = (size_t)G * batch * dim * sizeof(float);
   const size_t bc_b = (size_t)nblkb * batch * dstate * seqlen * sizeof(float);
-  const size_t total = up(agg_b) + up(sd_b) + up(hin_b) + up(dap_b) + up(ddp_b) + 2 * up(bc_b);
+  const size_t mu_b = G > 1 ? (size_t)G * nstate * sizeof(float) : 0;     // carries: M and mu_in
+  const size_t csd_b = G > 1 ? (size_t)G * batch * dim * sizeof(float) : 0;
+  const size_t total = up(agg_b) + up(sd_b) + up(hin_b) + up(dap_b) + up(ddp_b) + 2 * up(bc_b) + 2 * up(mu_b) +
+                       up(csd_b);
   void* ws = nullptr;
   S6_HIP(hipMallocAsync(&ws, total, st), "hipMallocAsync(backward workspace)");
   char* wp = static_cast<char*>(ws);
@@ -1719,6 +1871,12 @@ int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
   float* dbp = reinterpret_cast<float*>(wp);
   wp += up(bc_b);
   float* dcp = reinterpret_cast<float*>(wp);
+  wp += up(bc_b);
+  float* cM = reinterpret_cast<float*>(wp);
+  wp += up(mu_b);
+  float* muin = reinterpret_cast<float*>(wp);
+  wp += up(mu_b);
+  float* cSD = reinterpret_cast<float*>(wp);
 
   // pass 1: end state (from zero) and summed delta of every segment but the last
   if (nagg > 0) {
@@ -1746,8 +1904,22 @@ int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
     b.dy = dy; b.dh_last = dh_last; b.hin = hin;
     b.dx = dx; b.ddelta = ddelta; b.dz = dz; b.dA_part = dap; b.dD_part = ddp;
     b.dB_part = dbp; b.dC_part = dcp; b.dh0 = dh0;
-    b.batch = batch; b.D = dim; b.L = seqlen; b.N = dstate; b.nseg = S;
-    rc = in_dtype == S6_BF16 ? launch_bwd<uint16_t>(b, z != nullptr, st) : launch_bwd<float>(b, z != nullptr, st);
+    b.batch = batch; b.D = dim; b.L = seqlen; b.N = dstate; b.nseg = S; b.seg_per_part = spp;
+    const bool gate = z != nullptr;
+    if (G > 1) {
+      b.carry_M = cM;
+      b.carry_SD = cSD;
+      rc = in_dtype == S6_BF16 ? launch_bwd<uint16_t>(b, gate, G, true, st) : launch_bwd<float>(b, gate, G, true, st);
+      if (rc == S6_OK) {
+        hipLaunchKernelGGL(s6_bwd_fold, dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0, st, A, dh_last, cM, cSD,
+                           muin, batch, dim, dstate, G);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) rc = hip_fail(e, "s6_bwd_fold launch");
+      }
+      b.mu_in = muin;
+    }
+    if (rc == S6_OK)
+      rc = in_dtype == S6_BF16 ? launch_bwd<uint16_t>(b, gate, G, false, st) : launch_bwd<float>(b, gate, G, false, st);
   }
   if (rc == S6_OK) {
     const int64_t tot = batch * dstate * seqlen;
@@ -1757,7 +1929,7 @@ int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
     hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3((unsigned)blocks), dim3(256), 0, st, dcp, dCm, nblkb, tot);
     const int64_t rows = dim * dstate;
     hipLaunchKernelGGL(s6_bwd_reduce_rows, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, dap, ddp, dA,
-                       dDskip, batch, dim, dstate);
+                       dDskip, G * batch, dim, dstate);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) rc = hip_fail(e, "s6_bwd reduction launch");
   }

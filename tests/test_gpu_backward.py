@@ -75,6 +75,8 @@ SHAPES = [
     (3, 33, 16, 129, synth.F32, True),
     (1, 1, 1, 1, synth.F32, False),
     (2, 7, 3, 17, synth.BF16, False),
+    (1, 32, 16, 20000, synth.BF16, True),   # long rows: the sequence runs in parts with carries
+    (1, 20, 24, 3000, synth.F32, True),     # parts, two states per lane
 ]
 
 
