@@ -571,6 +571,10 @@ def main():
         print(f"[bench] backward {w.name}", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(w)
         torch.cuda.empty_cache()
+        print(f"[bench] backward {wl.name}", file=sys.stderr, flush=True)
+        out["backward_long"] = bench_backward(wl, steps=3, warmup=2)
+        out["backward_long"]["note"] = "sequence run in parts with adjoint carries (carry pass + fold)"
+        torch.cuda.empty_cache()
         print(f"[bench] scan {w.name} with the step options", file=sys.stderr, flush=True)
         _, ts, _ = bench_scan(w, 50, 50, softplus=True)
         out["softplus"] = scan_line("softplus", w, ts, in_bytes, "step softplus(delta + bias) in the kernel", True)
