@@ -65,6 +65,8 @@ class Oracle:
         self.lib.oracle_step_ex.restype = None
         self.lib.oracle_scan_bwd.argtypes = [_I, _I, _I, _I] + [_P] * 26
         self.lib.oracle_scan_bwd.restype = ctypes.c_int
+        self.lib.oracle_scan_bwd_ex.argtypes = [_I, _I, _I, _I, _P, _P, _P, ctypes.c_int] + [_P] * 26
+        self.lib.oracle_scan_bwd_ex.restype = ctypes.c_int
         self.lib.oracle_num_threads.restype = ctypes.c_int
         self.path = path
 
@@ -146,12 +148,14 @@ class Oracle:
         return y, m
 
 
-    def scan_bwd(self, x, delta, A, Bm, Cm, dy, Dskip=None, z=None, h0=None, dh_last=None):
-        """Gradients of <dy, y> + <dh_last, h_last> for the plain scan.
-        Returns a dict: dx, ddelta, dz (batch, D, L); dA (D, N); dBm, dCm
-        (batch, N, L); dDskip (D,); dh0 (batch, D, N); and for each the
-        magnitude under the key prefixed with "m" (mdx, mddelta, ...).  dz is
-        zero without a gate."""
+    def scan_bwd(self, x, delta, A, Bm, Cm, dy, Dskip=None, z=None, h0=None, dh_last=None,
+                 delta_bias=None, softplus=False):
+        """Gradients of <dy, y> + <dh_last, h_last> for the scan (with the
+        step bias and softplus of scan(), not the exact hold).  Returns a
+        dict: dx, ddelta (of the stored delta), dz (batch, D, L); dA (D, N);
+        dBm, dCm (batch, N, L); dDskip (D,); dh0 (batch, D, N); ddelta_bias
+        (D,); and for each the magnitude under the key prefixed with "m"
+        (mdx, mddelta, ...).  dz is zero without a gate."""
         x = np.asarray(x)
         Bsz, D, L = x.shape
         N = np.asarray(A).shape[1]
@@ -166,12 +170,17 @@ class Oracle:
             keep.append(arr)
             args.append(ptr)
         shapes = {"dx": (Bsz, D, L), "ddelta": (Bsz, D, L), "dA": (D, N), "dBm": (Bsz, N, L),
-                  "dCm": (Bsz, N, L), "dDskip": (D,), "dz": (Bsz, D, L), "dh0": (Bsz, D, N)}
+                  "dCm": (Bsz, N, L), "dDskip": (D,), "dz": (Bsz, D, L), "dh0": (Bsz, D, N),
+                  "ddelta_bias": (D,)}
         out = {k: np.empty(v) for k, v in shapes.items()}
         out.update({"m" + k: np.empty(v) for k, v in shapes.items()})
-        order = ["dx", "ddelta", "dA", "dBm", "dCm", "dDskip", "dz", "dh0"]
+        order = ["dx", "ddelta", "dA", "dBm", "dCm", "dDskip", "dz", "dh0", "ddelta_bias"]
         ptrs = [out[k].ctypes.data_as(_P) for k in order] + [out["m" + k].ctypes.data_as(_P) for k in order]
-        rc = self.lib.oracle_scan_bwd(Bsz, D, L, N, *args, *ptrs)
+        bias, bptr = self._in(delta_bias, (D,))
+        rc = self.lib.oracle_scan_bwd_ex(Bsz, D, L, N, args[0], args[1], bptr, self._flags(softplus, False),
+                                         *args[2:], *ptrs)
+        if rc == -2:
+            raise ValueError("oracle_scan_bwd: unsupported option")
         if rc != 0:
             raise MemoryError("oracle_scan_bwd: out of memory")
         return out

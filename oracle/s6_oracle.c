@@ -211,21 +211,32 @@ void oracle_step(int64_t Bsz, int64_t D, int64_t N, double* h, double* H, const 
  * order d = 0 .. D-1, so dB and dC are summed over d in a fixed order; dA and
  * dD are summed over rows b = 0 .. Bsz-1 after the parallel loop.
  * Nullable: Dskip, z, h0, dh_last (inputs); dDskip, dz, dh0 (outputs); every
- * magnitude output.  Work memory: 4 L N doubles per batch row. */
+ * magnitude output.  Work memory: 4 L N doubles per batch row.
+ *
+ * oracle_scan_bwd_ex also takes the step bias and ORACLE_DELTA_SOFTPLUS of
+ * oracle_scan_ex (not the exact hold: -2): the step is Delta = v or
+ * softplus(v), v = delta + bias[d], so ddelta above becomes the gradient of
+ * the stored delta, ddelta * dDelta/dv with dsoftplus/dv = 1/(1 + e^-v), and
+ * dbias[d] = sum over b, t of that (ddbias, nullable). */
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 
-int oracle_scan_bwd(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x,
-                    const double* delta, const double* A, const double* Bm, const double* Cm,
-                    const double* Dskip, const double* z, const double* h0, const double* dy,
-                    const double* dh_last, double* dx, double* ddelta, double* dA, double* dBm,
-                    double* dCm, double* dDskip, double* dz, double* dh0, double* mdx,
-                    double* mddelta, double* mdA, double* mdB, double* mdC, double* mdD,
-                    double* mdz, double* mdh0) {
+int oracle_scan_bwd_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x,
+                       const double* delta, const double* dbias, int flags, const double* A,
+                       const double* Bm, const double* Cm, const double* Dskip, const double* z,
+                       const double* h0, const double* dy, const double* dh_last, double* dx,
+                       double* ddelta, double* dA, double* dBm, double* dCm, double* dDskip,
+                       double* dz, double* dh0, double* ddbias, double* mdx, double* mddelta,
+                       double* mdA, double* mdB, double* mdC, double* mdD, double* mdz, double* mdh0,
+                       double* mddbias) {
+  if (flags & ~ORACLE_DELTA_SOFTPLUS) return -2;
+  const int sp = (flags & ORACLE_DELTA_SOFTPLUS) != 0;
   double* dA_b = (double*)calloc((size_t)(Bsz * D * N), sizeof(double));
   double* mdA_b = (double*)calloc((size_t)(Bsz * D * N), sizeof(double));
   double* dD_b = (double*)calloc((size_t)(Bsz * D), sizeof(double));
   double* mdD_b = (double*)calloc((size_t)(Bsz * D), sizeof(double));
-  int fail = !dA_b || !mdA_b || !dD_b || !mdD_b;
+  double* db_b = (double*)calloc((size_t)(Bsz * D), sizeof(double));
+  double* mdb_b = (double*)calloc((size_t)(Bsz * D), sizeof(double));
+  int fail = !dA_b || !mdA_b || !dD_b || !mdD_b || !db_b || !mdb_b;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t b = 0; b < Bsz; ++b) {
     if (fail) continue;
@@ -258,7 +269,7 @@ int oracle_scan_bwd(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* 
         Hs[n] = fabs(hs[n]);
       }
       for (int64_t t = 0; t < L; ++t) {
-        const double dt = delta[p * L + t], xt = x[p * L + t];
+        const double dt = step_of(delta[p * L + t], dbias, d, flags), xt = x[p * L + t];
         for (int64_t n = 0; n < N; ++n) {
           const double a = exp(dt * Ad[n]);
           const double bx = dt * Bb[n * L + t] * xt;
@@ -272,7 +283,7 @@ int oracle_scan_bwd(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* 
         Lam[n] = fabs(lam[n]);
       }
       for (int64_t t = L - 1; t >= 0; --t) {
-        const double dt = delta[p * L + t], xt = x[p * L + t];
+        const double dt = step_of(delta[p * L + t], dbias, d, flags), xt = x[p * L + t];
         const double g = z ? silu(z[p * L + t]) : 1.0;
         const double dyc = dy[p * L + t] * g;
         double gx = 0.0, mgx = 0.0, gd = 0.0, mgd = 0.0, yc = 0.0, myc = 0.0;
@@ -300,10 +311,15 @@ int oracle_scan_bwd(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* 
         }
         yc += dsk * xt;
         myc += fabs(dsk * xt);
+        /* chain rule through the step: dDelta/d(stored delta) */
+        const double v = dbias ? delta[p * L + t] + dbias[d] : delta[p * L + t];
+        const double js = sp ? sigmoid(v) : 1.0;
         dx[p * L + t] = dyc * dsk + gx;
-        ddelta[p * L + t] = gd;
+        ddelta[p * L + t] = gd * js;
         if (mdx) mdx[p * L + t] = fabs(dyc * dsk) + mgx;
-        if (mddelta) mddelta[p * L + t] = mgd;
+        if (mddelta) mddelta[p * L + t] = mgd * js;
+        db_b[p] += gd * js;
+        mdb_b[p] += mgd * js;
         dD_b[p] += dyc * xt;
         mdD_b[p] += fabs(dyc * xt);
         if (dz) {
@@ -335,18 +351,36 @@ int oracle_scan_bwd(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* 
       if (mdA) mdA[i] = ms;
     }
     for (int64_t d = 0; d < D; ++d) {
-      double s = 0.0, ms = 0.0;
+      double s = 0.0, ms = 0.0, sb = 0.0, msb = 0.0;
       for (int64_t b = 0; b < Bsz; ++b) {
         s += dD_b[b * D + d];
         ms += mdD_b[b * D + d];
+        sb += db_b[b * D + d];
+        msb += mdb_b[b * D + d];
       }
       if (dDskip) dDskip[d] = s;
       if (mdD) mdD[d] = ms;
+      if (ddbias) ddbias[d] = sb;
+      if (mddbias) mddbias[d] = msb;
     }
   }
   free(dA_b);
   free(mdA_b);
   free(dD_b);
   free(mdD_b);
+  free(db_b);
+  free(mdb_b);
   return fail ? -1 : 0;
+}
+
+int oracle_scan_bwd(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x,
+                    const double* delta, const double* A, const double* Bm, const double* Cm,
+                    const double* Dskip, const double* z, const double* h0, const double* dy,
+                    const double* dh_last, double* dx, double* ddelta, double* dA, double* dBm,
+                    double* dCm, double* dDskip, double* dz, double* dh0, double* mdx,
+                    double* mddelta, double* mdA, double* mdB, double* mdC, double* mdD,
+                    double* mdz, double* mdh0) {
+  return oracle_scan_bwd_ex(Bsz, D, L, N, x, delta, NULL, 0, A, Bm, Cm, Dskip, z, h0, dy, dh_last, dx,
+                            ddelta, dA, dBm, dCm, dDskip, dz, dh0, NULL, mdx, mddelta, mdA, mdB, mdC,
+                            mdD, mdz, mdh0, NULL);
 }

@@ -489,16 +489,21 @@ def _bwd(o, p, dy, dhl):
                       h0=p.get("h0"), dh_last=dhl)
 
 
-def brute_force_loss(p, dy, dhl, dps=50):
+def brute_force_loss(p, dy, dhl, dps=50, bias=None, softplus=False):
     """<dy, y> + <dh_last, h_last> in multi-digit arithmetic from the
     materialised form (exponentials of sums of Delta, as in brute_force_y),
-    returned as an mpmath number."""
+    returned as an mpmath number.  With bias / softplus the step is
+    delta + bias[d], or ln(1 + e^(delta + bias[d])) from the definition."""
     import mpmath as mp
     mp.mp.dps = dps
     f = lambda v: mp.mpf(v) if not isinstance(v, mp.mpf) else v  # noqa: E731
-    x, dl, A, Bm, Cm = p["x"], p["delta"], p["A"], p["Bm"], p["Cm"]
+    x, A, Bm, Cm = p["x"], p["A"], p["Bm"], p["Cm"]
     Bsz, D, L = x.shape
     N = A.shape[1]
+    dl = np.empty(p["delta"].shape, dtype=object)
+    for idx in np.ndindex(dl.shape):
+        v = f(p["delta"][idx]) + (f(bias[idx[1]]) if bias is not None else 0)
+        dl[idx] = mp.log(1 + mp.exp(v)) if softplus else v
     total = mp.mpf(0)
     for b in range(Bsz):
         for d in range(D):
@@ -640,9 +645,75 @@ def pin_bwd_no_input_coupling(o):
     assert np.all(np.abs(r["dh0"] - dh0) <= 1e-13 * r["mdh0"]), np.max(np.abs(r["dh0"] - dh0))
 
 
+def pin_bwd_options_directional_brute_force(o):
+    """The backward with a step bias and softplus against a directional
+    derivative of the 50-digit materialised loss whose step is
+    ln(1 + e^(delta + bias)) from the definition: the gradients of the
+    stored delta and of the bias (and of every other input)."""
+    import mpmath as mp
+    p, dy, dhl = _bwd_problem(107, Bsz=2, D=2, L=6, N=3)
+    g = _rng(108)
+    p["delta"] = g.normal(-1.5, 1.0, size=p["delta"].shape)
+    bias = g.normal(0.0, 0.7, size=p["x"].shape[1])
+    r = o.scan_bwd(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], dy, Dskip=p["Dskip"], z=p["z"], h0=p["h0"],
+                   dh_last=dhl, delta_bias=bias, softplus=True)
+    eps = mp.mpf("1e-15")
+    for key, gk in BWD_INPUTS + (("bias", "ddelta_bias"),):
+        base = bias if key == "bias" else p[key]
+        v = g.standard_normal(base.shape)
+        mp.mp.dps = 50
+        plus = np.array([mp.mpf(float(a)) + eps * mp.mpf(float(c)) for a, c in zip(base.ravel(), v.ravel())],
+                        dtype=object).reshape(base.shape)
+        minus = np.array([mp.mpf(float(a)) - eps * mp.mpf(float(c)) for a, c in zip(base.ravel(), v.ravel())],
+                         dtype=object).reshape(base.shape)
+        if key == "bias":
+            fp = brute_force_loss(p, dy, dhl, bias=plus, softplus=True)
+            fm = brute_force_loss(p, dy, dhl, bias=minus, softplus=True)
+        else:
+            fp = brute_force_loss(dict(p, **{key: plus}), dy, dhl, bias=bias, softplus=True)
+            fm = brute_force_loss(dict(p, **{key: minus}), dy, dhl, bias=bias, softplus=True)
+        fd = (fp - fm) / (2 * eps)
+        an = float(np.sum(r[gk] * v))
+        scale = float(np.sum(r["m" + gk] * np.abs(v)))
+        assert abs(float(fd) - an) <= 1e-13 * scale, (key, float(fd), an, scale)
+
+
+def pin_bwd_options_elementwise_fd(o):
+    """Every element of the gradients of the stored delta and of the bias
+    against central differences of the forward oracle with the same options
+    (bias alone, and bias with softplus)."""
+    p, dy, dhl = _bwd_problem(109, Bsz=2, D=2, L=5, N=2)
+    g = _rng(110)
+    p["delta"] = g.normal(-1.0, 1.0, size=p["delta"].shape)
+    bias = g.normal(0.5, 0.5, size=p["x"].shape[1])
+    for softplus in (False, True):
+        q = dict(p)
+        if not softplus:
+            q["delta"] = np.abs(p["delta"]) * 0.2  # keep the step positive without softplus
+        r = o.scan_bwd(q["x"], q["delta"], q["A"], q["Bm"], q["Cm"], dy, Dskip=q["Dskip"], z=q["z"], h0=q["h0"],
+                       dh_last=dhl, delta_bias=bias, softplus=softplus)
+
+        def loss(dl, bs):
+            f = o.scan(**dict(q, delta=dl), delta_bias=bs, softplus=softplus)
+            return np.sum(dy * f["y"]) + np.sum(dhl * f["h_last"])
+
+        eps = 1e-6
+        for key, gk in (("delta", "ddelta"), ("bias", "ddelta_bias")):
+            base = q["delta"] if key == "delta" else bias
+            fd = np.zeros(base.shape)
+            for idx in np.ndindex(base.shape):
+                bp, bm = base.copy(), base.copy()
+                bp[idx] += eps
+                bm[idx] -= eps
+                fd[idx] = ((loss(bp, bias) - loss(bm, bias)) if key == "delta"
+                           else (loss(q["delta"], bp) - loss(q["delta"], bm))) / (2 * eps)
+            err = np.abs(fd - r[gk]) / np.maximum(r["m" + gk], 1e-300)
+            assert np.all(err < 1e-6), (softplus, key, np.max(err))
+
+
 PINS = [pin_zero_step_hand, pin_scalar_hand, pin_lti_convolution, pin_step_response,
         pin_brute_force, pin_tree_scan, pin_split_resume, pin_linearity_and_permutation,
         pin_gate_limits, pin_decode_equals_scan, pin_magnitude_bounds, pin_softplus_hand,
         pin_softplus_limits, pin_zoh_hand, pin_zoh_limits, pin_options_brute_force,
         pin_bwd_directional_brute_force, pin_bwd_elementwise_fd, pin_bwd_linear_in_cotangent,
-        pin_bwd_no_input_coupling]
+        pin_bwd_no_input_coupling, pin_bwd_options_directional_brute_force, pin_bwd_options_elementwise_fd]

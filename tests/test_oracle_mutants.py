@@ -58,7 +58,14 @@ MUTANTS = [
     ("bwd_dx_no_skip", [("dx[p * L + t] = dyc * dsk + gx;", "dx[p * L + t] = gx;")]),
     ("bwd_dD_ungated", [("dD_b[p] += dyc * xt;", "dD_b[p] += dy[p * L + t] * xt;")]),
     ("bwd_dx_B_of_next_state", [("gx += l * dt * Bt;", "gx += l * dt * Bb[((n + 1) % N) * L + t];")]),
-    ("delta_index_shift", [("step_of(delta[p * L + t],", "step_of(delta[p * L + (t > 0 ? t - 1 : 0)],")]),
+    ("bwd_softplus_chain_missing", [("const double js = sp ? sigmoid(v) : 1.0;", "const double js = 1.0;")]),
+    ("bwd_softplus_chain_of_step", [("const double js = sp ? sigmoid(v) : 1.0;", "const double js = sp ? sigmoid(dt) : 1.0;")]),
+    ("bwd_bias_grad_dropped", [("db_b[p] += gd * js;", "db_b[p] += 0.0 * gd * js;")]),
+    ("bwd_reverse_step_without_options", [
+        ("const double dt = step_of(delta[p * L + t], dbias, d, flags), xt = x[p * L + t];\n        const double g",
+         "const double dt = delta[p * L + t], xt = x[p * L + t];\n        const double g")]),
+    ("delta_index_shift", [("double dt = step_of(delta[p * L + t], dbias, d, flags);",
+                            "double dt = step_of(delta[p * L + (t > 0 ? t - 1 : 0)], dbias, d, flags);")]),
     ("A_state_index", [("double a = exp(dt * Ad[n]);         /*", "double a = exp(dt * Ad[(n + 1) % N]);         /*")]),
     ("B_batch_index", [("const double* Bb = Bm + b * N * L;\n    const double* Cb = Cm + b * N * L;\n    double dsk",
                         "const double* Bb = Bm;\n    const double* Cb = Cm + b * N * L;\n    double dsk")]),
