@@ -104,15 +104,19 @@ def bwd_valu_slots(w):
     return w.batch * w.dim * w.seqlen * (13 * w.dstate + 16)
 
 
-def bench_backward(w, steps=10, warmup=3):
-    """Times s6_scan_bwd on workload w (dy random, no dh_last)."""
+def bench_backward(w, steps=10, warmup=3, softplus=False):
+    """Times s6_scan_bwd on workload w (dy random, no dh_last); softplus:
+    with the softplus step and a bias of -4 per channel."""
     import torch
     from selective_state_space_63_amd import s6, synth
     inp = synth.device_full(w)
     dy = torch.randn((w.batch, w.dim, w.seqlen), device="cuda", dtype=torch.float32)
+    opts = {}
+    if softplus:
+        opts = dict(delta_bias=torch.full((w.dim,), -4.0, device="cuda", dtype=torch.float32), delta_softplus=True)
 
     def step():
-        s6.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], dy, D=inp["Dskip"], z=inp["z"])
+        s6.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], dy, D=inp["Dskip"], z=inp["z"], **opts)
 
     for _ in range(warmup):
         step()
@@ -570,6 +574,9 @@ def main():
         torch.cuda.empty_cache()
         print(f"[bench] backward {w.name}", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(w)
+        torch.cuda.empty_cache()
+        out["backward_softplus"] = bench_backward(w, softplus=True)
+        out["backward_softplus"]["note"] = "s6_scan_bwd_ex with the softplus step and a bias (gradient of the bias too)"
         torch.cuda.empty_cache()
         print(f"[bench] backward {wl.name}", file=sys.stderr, flush=True)
         out["backward_long"] = bench_backward(wl, steps=3, warmup=2)

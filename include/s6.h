@@ -174,6 +174,18 @@ int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
                 const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm, float* dCm,
                 float* dDskip, float* dz, float* dh0, void* stream);
 
+/* s6_scan_bwd with the step bias and S6_DELTA_SOFTPLUS of s6_scan_fwd_ex
+ * (S6_ZOH_EXACT: S6_ERR_UNSUPPORTED; other bits: S6_ERR_FLAGS).  ddelta is
+ * then the gradient of the stored delta (the step's gradient times
+ * dstep/dv, v = delta + delta_bias[d], 1/(1 + e^-v) under softplus), and
+ * ddelta_bias (nullable, (dim) fp32) receives its sum over batch rows and
+ * tokens.  flags = 0 with both bias pointers NULL is s6_scan_bwd. */
+int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                   const void* x, const void* delta, const float* delta_bias, int flags, const float* A,
+                   const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
+                   const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
+                   float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -901,9 +901,21 @@ template <int SPL>
 constexpr int bwd_waves() { return 4; }
 
 template <int SPL>
-constexpr size_t bwd_lds_bytes(bool) {
-  return sizeof(float) * ((size_t)4 * (4 * bwd_waves<SPL>()) * kBwdSeg + (size_t)2 * 16 * SPL * kBwdSeg +
+constexpr size_t bwd_lds_bytes(bool sp) {
+  return sizeof(float) * ((size_t)(sp ? 5 : 4) * (4 * bwd_waves<SPL>()) * kBwdSeg + (size_t)2 * 16 * SPL * kBwdSeg +
                           (size_t)bwd_waves<SPL>() * 2 * 16 * 16 * SPL);
+}
+
+// Step of a stored delta value under the step options (SP kernels): v =
+// delta + bias, then softplus(v) if asked; *js receives dstep/dv.
+__device__ __forceinline__ float bwd_step(float raw, float bias, bool softplus, float* js) {
+  const float v = raw + bias;
+  if (!softplus) {
+    *js = 1.0f;
+    return v;
+  }
+  *js = fast_rcp(1.0f + fast_exp2(-v * kLog2e));
+  return softplus_f(v);
 }
 
 struct BwdArgs {
@@ -929,6 +941,9 @@ struct BwdArgs {
                           // null (one part: the carry is dh_last)
   float* carry_M;         // (G, batch*D*N): carry leaving each part from a zero carry-in
   float* carry_SD;        // (G, batch*D): summed delta of each part
+  const float* dbias;     // SP kernels: (D) step bias or null
+  int softplus;           // SP kernels: step = softplus(delta + dbias)
+  float* ddbias_part;     // SP kernels: (G, batch, D) gradient of the bias, or null
   int64_t batch, D, L, N, nseg;
   int64_t seg_per_part;   // segments per part (the sequence is cut into G parts, blockIdx.y)
 };
@@ -972,7 +987,9 @@ __device__ __forceinline__ float rows_sum4(const float (&v)[4]) {
   return __builtin_bit_cast(float, (unsigned)s[0]) + __builtin_bit_cast(float, (unsigned)s[1]);
 }
 
-template <typename In, bool GATE, int SPL>
+// SP: the step bias / softplus options (the gradient of the stored delta
+// gets the factor dstep/dv; the bias gradient is summed per channel).
+template <typename In, bool GATE, int SPL, bool SP>
 __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a) {
   constexpr int WB = bwd_waves<SPL>();
   constexpr int NTHR = 64 * WB;
@@ -988,6 +1005,7 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
   float* sB = sq + CW * KS;          // [NS][KS]
   float* sC = sB + NS * KS;          // [NS][KS]
   float* red = sC + NS * KS;         // [waves][2][16][NS]
+  float* sjs = red + WB * 2 * 16 * NS;  // SP: [CW][KS] dstep/dv
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1030,7 +1048,7 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
             : a.dh_last ? a.dh_last[(b * D + d) * N + n] : 0.0f;
     dA[j] = 0.0f;
   }
-  float dD = 0.0f;
+  float dD = 0.0f, dbias = 0.0f;
 
   for (int64_t s = s_end - 1; s >= s_begin; --s) {
     const int64_t tb = s * KS;
@@ -1040,10 +1058,11 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
       const int cc = i / KS, t = i % KS;
       const bool ok = cc < rows_valid && t < tl;
       const int64_t off = (b * D + d0 + (cc < rows_valid ? cc : 0)) * L + tb + (t < tl ? t : 0);
-      float xv = 0.0f, dl = 0.0f, dyc = 0.0f, q = 0.0f;
+      float xv = 0.0f, dl = 0.0f, dyc = 0.0f, q = 0.0f, js = 0.0f;
       if (ok) {
         xv = to_f32(xp[off]);
         dl = to_f32(dp[off]);
+        if constexpr (SP) dl = bwd_step(dl, a.dbias ? a.dbias[d0 + cc] : 0.0f, a.softplus, &js);
         const float g = a.dy[off];
         if constexpr (GATE) {
           const float zz = to_f32(zp[off]);
@@ -1058,6 +1077,7 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
       sdl[i] = dl;
       sdyc[i] = dyc;
       sq[i] = q;
+      if constexpr (SP) sjs[i] = js;
     }
     for (int i = tid; i < NS * KS; i += NTHR) {
       const int n = i / KS, t = i % KS;
@@ -1195,7 +1215,12 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
           const float dyc = sdyc[c * KS + t];
           const int64_t off = (b * D + d) * L + tt;
           a.dx[off] = __builtin_fmaf(dyc, dsk, dl * k1);
-          a.ddelta[off] = __builtin_fmaf(xv, k1, k2);
+          float gd = __builtin_fmaf(xv, k1, k2);
+          if constexpr (SP) {
+            gd *= sjs[c * KS + t];
+            dbias += gd;
+          }
+          a.ddelta[off] = gd;
           if (GATE && a.dz) a.dz[off] = __builtin_fmaf(dsk, xv, k3) * sq[c * KS + t];
         }
       }
@@ -1227,6 +1252,14 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
     }
     if (nl == 0) a.dD_part[part * a.batch * D + b * D + d] = dD;
   }
+  if constexpr (SP) {
+    // the channel's bias gradient: lane nl summed the tokens it wrote
+    dbias += dpp_f<0x128>(dbias);
+    dbias += dpp_f<0x124>(dbias);
+    dbias += dpp_f<0x122>(dbias);
+    dbias += dpp_f<0x121>(dbias);
+    if (chv && nl == 0 && a.ddbias_part) a.ddbias_part[part * a.batch * D + b * D + d] = dbias;
+  }
 }
 
 // Adjoint carries of the parts of a long sequence: for part g = blockIdx.y + 1
@@ -1234,7 +1267,7 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
 // leaves its first token when zero enters its last one, mu <- a_t (dyc_t C_t
 // + mu) from the last token back, and the part's summed delta (compensated),
 // from which exp(A sum delta) carries the right neighbour's carry through.
-template <typename In, bool GATE, int SPL>
+template <typename In, bool GATE, int SPL, bool SP>
 __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_carry_kernel(BwdArgs a) {
   constexpr int WB = bwd_waves<SPL>();
   constexpr int NTHR = 64 * WB;
@@ -1284,6 +1317,10 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_carry_kernel(Bwd
       float dl = 0.0f, dyc = 0.0f;
       if (ok) {
         dl = to_f32(dp[off]);
+        if constexpr (SP) {
+          float js;
+          dl = bwd_step(dl, a.dbias ? a.dbias[d0 + cc] : 0.0f, a.softplus, &js);
+        }
         dyc = a.dy[off];
         if constexpr (GATE) {
           const float zz = to_f32(zp[off]);
@@ -1354,7 +1391,8 @@ __global__ void s6_bwd_reduce_bc(const float* __restrict__ part, float* __restri
 
 // dA (D, N) and dD (D): sums over batch rows, in order.
 __global__ void s6_bwd_reduce_rows(const float* __restrict__ dA_part, const float* __restrict__ dD_part,
-                                   float* __restrict__ dA, float* __restrict__ dD, int64_t batch, int64_t D,
+                                   const float* __restrict__ db_part, float* __restrict__ dA,
+                                   float* __restrict__ dD, float* __restrict__ db, int64_t batch, int64_t D,
                                    int64_t N) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < D * N) {
@@ -1366,6 +1404,11 @@ __global__ void s6_bwd_reduce_rows(const float* __restrict__ dA_part, const floa
     float s = 0.0f;
     for (int64_t b = 0; b < batch; ++b) s += dD_part[b * D + i];
     dD[i] = s;
+  }
+  if (db && i < D) {
+    float s = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) s += db_part[b * D + i];
+    db[i] = s;
   }
 }
 
@@ -1671,29 +1714,36 @@ int launch_step_g(const StepArgs& a, hipStream_t st) {
 }
 
 // carry: the part-carry kernel (parts 1 .. G-1) instead of the main kernel.
-template <typename In, bool GATE, int SPL>
+template <typename In, bool GATE, int SPL, bool SP>
 int launch_bwd_t(const BwdArgs& a, int64_t parts, bool carry, hipStream_t st) {
   constexpr int CW = 4 * bwd_waves<SPL>();
   const int64_t nblk = (a.D + CW - 1) / CW;
   const dim3 block(64 * bwd_waves<SPL>());
   if (carry) {
     const size_t lds = sizeof(float) * ((size_t)2 * CW * kBwdSeg + (size_t)16 * SPL * kBwdSeg);
-    hipLaunchKernelGGL((s6_bwd_carry_kernel<In, GATE, SPL>), dim3((unsigned)(nblk * a.batch), (unsigned)(parts - 1)),
-                       block, lds, st, a);
+    hipLaunchKernelGGL((s6_bwd_carry_kernel<In, GATE, SPL, SP>),
+                       dim3((unsigned)(nblk * a.batch), (unsigned)(parts - 1)), block, lds, st, a);
     S6_HIP(hipGetLastError(), "s6_bwd_carry_kernel launch");
   } else {
-    hipLaunchKernelGGL((s6_bwd_kernel<In, GATE, SPL>), dim3((unsigned)(nblk * a.batch), (unsigned)parts), block,
-                       bwd_lds_bytes<SPL>(GATE), st, a);
+    hipLaunchKernelGGL((s6_bwd_kernel<In, GATE, SPL, SP>), dim3((unsigned)(nblk * a.batch), (unsigned)parts), block,
+                       bwd_lds_bytes<SPL>(SP), st, a);
     S6_HIP(hipGetLastError(), "s6_bwd_kernel launch");
   }
   return S6_OK;
 }
 
+template <typename In, int SPL, bool SP>
+int launch_bwd_g(const BwdArgs& a, bool gate, int64_t parts, bool carry, hipStream_t st) {
+  return gate ? launch_bwd_t<In, true, SPL, SP>(a, parts, carry, st)
+              : launch_bwd_t<In, false, SPL, SP>(a, parts, carry, st);
+}
+
 template <typename In>
 int launch_bwd(const BwdArgs& a, bool gate, int64_t parts, bool carry, hipStream_t st) {
+  const bool sp = a.dbias || a.softplus || a.ddbias_part;
   if (a.N <= 16)
-    return gate ? launch_bwd_t<In, true, 1>(a, parts, carry, st) : launch_bwd_t<In, false, 1>(a, parts, carry, st);
-  return gate ? launch_bwd_t<In, true, 2>(a, parts, carry, st) : launch_bwd_t<In, false, 2>(a, parts, carry, st);
+    return sp ? launch_bwd_g<In, 1, true>(a, gate, parts, carry, st) : launch_bwd_g<In, 1, false>(a, gate, parts, carry, st);
+  return sp ? launch_bwd_g<In, 2, true>(a, gate, parts, carry, st) : launch_bwd_g<In, 2, false>(a, gate, parts, carry, st);
 }
 
 int bwd_channels_per_block(int64_t dstate) { return dstate <= 16 ? 4 * bwd_waves<1>() : 4 * bwd_waves<2>(); }
@@ -1792,13 +1842,16 @@ int s6_state_update(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, fl
                             y, stream);
 }
 
-int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
-                const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
-                const float* Dskip, const void* z, const float* h0, const float* dy,
-                const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm, float* dCm,
-                float* dDskip, float* dz, float* dh0, void* stream) {
+int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                   const void* x, const void* delta, const float* delta_bias, int flags, const float* A,
+                   const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
+                   const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
+                   float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* stream) {
   int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
   if (rc) return rc;
+  if (flags & ~(S6_DELTA_SOFTPLUS | S6_ZOH_EXACT)) return S6_ERR_FLAGS;
+  if (flags & S6_ZOH_EXACT) return S6_ERR_UNSUPPORTED;
+  const bool softplus = (flags & S6_DELTA_SOFTPLUS) != 0;
   const bool work = batch > 0 && dim > 0 && seqlen > 0;
   if (dim > 0 && !dA) return S6_ERR_NULL;
   if (work && (!x || !delta || !A || !Bm || !Cm || !dy || !dx || !ddelta || !dBm || !dCm))
@@ -1807,7 +1860,8 @@ int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
   const void* ins[] = {x, delta, Bm, Cm, z};
   for (const void* p : ins)
     if (p && !aligned(p, esz)) return S6_ERR_ALIGN;
-  const void* f32s[] = {A, Dskip, h0, dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0};
+  const void* f32s[] = {A, Dskip, h0, dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, delta_bias,
+                        ddelta_bias};
   for (const void* p : f32s)
     if (p && !aligned(p, 4)) return S6_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -1817,6 +1871,7 @@ int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
     // no tokens or no rows: the parameter gradients are zero and dh0 = dh_last
     fill(dA, 0.0f, dim * dstate, st);
     fill(dDskip, 0.0f, dim, st);
+    fill(ddelta_bias, 0.0f, dim, st);
     if (dh0 && nstate > 0) {
       int64_t blocks = (nstate + 255) / 256;
       if (blocks > 65536) blocks = 65536;
@@ -1853,7 +1908,7 @@ int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
   const size_t bc_b = (size_t)nblkb * batch * dstate * seqlen * sizeof(float);
   const size_t mu_b = G > 1 ? (size_t)G * nstate * sizeof(float) : 0;     // carries: M and mu_in
   const size_t csd_b = G > 1 ? (size_t)G * batch * dim * sizeof(float) : 0;
-  const size_t total = up(agg_b) + up(sd_b) + up(hin_b) + up(dap_b) + up(ddp_b) + 2 * up(bc_b) + 2 * up(mu_b) +
+  const size_t total = up(agg_b) + up(sd_b) + up(hin_b) + up(dap_b) + 2 * up(ddp_b) + 2 * up(bc_b) + 2 * up(mu_b) +
                        up(csd_b);
   void* ws = nullptr;
   S6_HIP(hipMallocAsync(&ws, total, st), "hipMallocAsync(backward workspace)");
@@ -1868,7 +1923,9 @@ int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
   wp += up(dap_b);
   float* ddp = reinterpret_cast<float*>(wp);
   wp += up(ddp_b);
-  float* dbp = reinterpret_cast<float*>(wp);
+  float* dbp = reinterpret_cast<float*>(wp);  // bias gradient per part and row
+  wp += up(ddp_b);
+  float* dBp = reinterpret_cast<float*>(wp);
   wp += up(bc_b);
   float* dcp = reinterpret_cast<float*>(wp);
   wp += up(bc_b);
@@ -1886,6 +1943,7 @@ int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
     memset(&g, 0, sizeof(g));
     g.x = x; g.delta = delta; g.Bm = Bm; g.A = A;
     g.hout = agg; g.hout_stride = nstate; g.sumdelta = sd;
+    g.dbias = delta_bias; g.softplus = softplus;
     g.D = dim; g.L = seqlen; g.N = dstate; g.seg_len = kBwdSeg;
     rc = launch_scan_any(in_dtype, kModeState, g, p, false, batch, nagg, st);
   }
@@ -1903,7 +1961,8 @@ int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
     b.x = x; b.delta = delta; b.z = z; b.Bm = Bm; b.Cm = Cm; b.A = A; b.Dskip = Dskip;
     b.dy = dy; b.dh_last = dh_last; b.hin = hin;
     b.dx = dx; b.ddelta = ddelta; b.dz = dz; b.dA_part = dap; b.dD_part = ddp;
-    b.dB_part = dbp; b.dC_part = dcp; b.dh0 = dh0;
+    b.dB_part = dBp; b.dC_part = dcp; b.dh0 = dh0;
+    b.dbias = delta_bias; b.softplus = softplus; b.ddbias_part = ddelta_bias ? dbp : nullptr;
     b.batch = batch; b.D = dim; b.L = seqlen; b.N = dstate; b.nseg = S; b.seg_per_part = spp;
     const bool gate = z != nullptr;
     if (G > 1) {
@@ -1925,17 +1984,26 @@ int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
     const int64_t tot = batch * dstate * seqlen;
     int64_t blocks = (tot + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3((unsigned)blocks), dim3(256), 0, st, dbp, dBm, nblkb, tot);
+    hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3((unsigned)blocks), dim3(256), 0, st, dBp, dBm, nblkb, tot);
     hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3((unsigned)blocks), dim3(256), 0, st, dcp, dCm, nblkb, tot);
     const int64_t rows = dim * dstate;
-    hipLaunchKernelGGL(s6_bwd_reduce_rows, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, dap, ddp, dA,
-                       dDskip, G * batch, dim, dstate);
+    hipLaunchKernelGGL(s6_bwd_reduce_rows, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, dap, ddp, dbp,
+                       dA, dDskip, ddelta_bias, G * batch, dim, dstate);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) rc = hip_fail(e, "s6_bwd reduction launch");
   }
   hipError_t e = hipFreeAsync(ws, st);
   if (rc == S6_OK && e != hipSuccess) rc = hip_fail(e, "hipFreeAsync(backward workspace)");
   return rc;
+}
+
+int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
+                const float* Dskip, const void* z, const float* h0, const float* dy,
+                const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm, float* dCm,
+                float* dDskip, float* dz, float* dh0, void* stream) {
+  return s6_scan_bwd_ex(batch, dim, seqlen, dstate, in_dtype, x, delta, nullptr, 0, A, Bm, Cm, Dskip, z, h0, dy,
+                        dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, nullptr, stream);
 }
 
 }  // extern "C"

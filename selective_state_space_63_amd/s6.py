@@ -50,6 +50,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.s6_state_update_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, i32] + [vp] * 7
     lib.s6_scan_bwd.restype = i32
     lib.s6_scan_bwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 19
+    lib.s6_scan_bwd_ex.restype = i32
+    lib.s6_scan_bwd_ex.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32] + [vp] * 18
     if path is None:
         _lib = lib
     return lib
@@ -198,12 +200,14 @@ def state_update(h, x, delta, A, Bm, Cm, D=None, z=None, y=None, delta_bias=None
     return y
 
 
-def scan_bwd(x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_last=None):
+def scan_bwd(x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_last=None, delta_bias=None,
+             delta_softplus=False):
     """Gradients of <dy, y> + <dh_last, h_last> for scan_fwd with the same
-    inputs (plain step).  dy: (batch, dim, L) fp32; dh_last: (batch, dim, N)
-    fp32 or None.  Returns a dict of fp32 tensors: dx, ddelta (batch, dim, L),
-    dA (dim, N), dBm, dCm (batch, N, L), dh0 (batch, dim, N), and dD (dim,)
-    when D is given, dz (batch, dim, L) when z is given."""
+    inputs and step options (not zoh).  dy: (batch, dim, L) fp32; dh_last:
+    (batch, dim, N) fp32 or None.  Returns a dict of fp32 tensors: dx, ddelta
+    (of the stored delta; batch, dim, L), dA (dim, N), dBm, dCm (batch, N, L),
+    dh0 (batch, dim, N), and dD (dim,) when D is given, dz (batch, dim, L)
+    when z is given, ddelta_bias (dim,) when delta_bias is given."""
     bsz, dim, L = x.shape
     N = A.shape[1]
     dt = x.dtype
@@ -227,31 +231,42 @@ def scan_bwd(x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_last=None):
         g["dD"] = torch.empty((dim,), **f)
     if z is not None:
         g["dz"] = torch.empty((bsz, dim, L), **f)
-    rc = load_library().s6_scan_bwd(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
-                                    _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(g["dx"]),
-                                    _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dBm"]), _ptr(g["dCm"]),
-                                    _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g["dh0"]), _stream())
+    ex, flags = _options(delta_bias, delta_softplus, False, dim)
+    if ex:
+        g["ddelta_bias"] = torch.empty((dim,), **f)
+        rc = load_library().s6_scan_bwd_ex(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(delta_bias), flags,
+                                           _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy),
+                                           _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                                           _ptr(g["dBm"]), _ptr(g["dCm"]), _ptr(g.get("dD")), _ptr(g.get("dz")),
+                                           _ptr(g["dh0"]), _ptr(g["ddelta_bias"]), _stream())
+    else:
+        rc = load_library().s6_scan_bwd(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+                                        _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(g["dx"]),
+                                        _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dBm"]), _ptr(g["dCm"]),
+                                        _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g["dh0"]), _stream())
     _check(rc)
     return g
 
 
 class SelectiveScan(torch.autograd.Function):
     """scan_fwd with its gradients from scan_bwd, for training with torch
-    autograd: y = SelectiveScan.apply(x, delta, A, Bm, Cm, D, z, h0).  D, z
-    and h0 may be None.  The forward keeps only its inputs; the backward
-    recomputes the states (plain step)."""
+    autograd: y = SelectiveScan.apply(x, delta, A, Bm, Cm, D, z, h0,
+    delta_bias, delta_softplus).  D, z, h0 and delta_bias may be None.  The
+    forward keeps only its inputs; the backward recomputes the states."""
 
     @staticmethod
-    def forward(ctx, x, delta, A, Bm, Cm, D=None, z=None, h0=None):
-        y = scan_fwd(x, delta, A, Bm, Cm, D=D, z=z, h0=h0)
-        ctx.save_for_backward(x, delta, A, Bm, Cm, D, z, h0)
+    def forward(ctx, x, delta, A, Bm, Cm, D=None, z=None, h0=None, delta_bias=None, delta_softplus=False):
+        y = scan_fwd(x, delta, A, Bm, Cm, D=D, z=z, h0=h0, delta_bias=delta_bias, delta_softplus=delta_softplus)
+        ctx.save_for_backward(x, delta, A, Bm, Cm, D, z, h0, delta_bias)
+        ctx.delta_softplus = delta_softplus
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        x, delta, A, Bm, Cm, D, z, h0 = ctx.saved_tensors
-        g = scan_bwd(x, delta, A, Bm, Cm, dy.contiguous().to(torch.float32), D=D, z=z, h0=h0)
+        x, delta, A, Bm, Cm, D, z, h0, delta_bias = ctx.saved_tensors
+        g = scan_bwd(x, delta, A, Bm, Cm, dy.contiguous().to(torch.float32), D=D, z=z, h0=h0,
+                     delta_bias=delta_bias, delta_softplus=ctx.delta_softplus)
         cast = lambda t, like: None if t is None else t.to(like.dtype)  # noqa: E731
         return (cast(g["dx"], x), cast(g["ddelta"], delta), g["dA"], cast(g["dBm"], Bm), cast(g["dCm"], Cm),
                 g.get("dD"), cast(g.get("dz"), x) if z is not None else None,
-                g["dh0"] if h0 is not None else None)
+                g["dh0"] if h0 is not None else None, g.get("ddelta_bias"), None)

@@ -47,7 +47,7 @@ def codes():
 
 
 def test_header_declares_the_entry_points():
-    assert header_functions() == ["s6_last_state", "s6_last_state_ex", "s6_scan_bwd", "s6_scan_fwd", "s6_scan_fwd_ex",
+    assert header_functions() == ["s6_last_state", "s6_last_state_ex", "s6_scan_bwd", "s6_scan_bwd_ex", "s6_scan_fwd", "s6_scan_fwd_ex",
                                   "s6_state_update", "s6_state_update_ex", "s6_status_str", "s6_version"]
 
 
@@ -165,6 +165,17 @@ def test_backward_validation(lib, codes):
     assert bwd(dz=P_ODD) == codes["S6_ERR_ALIGN"]
     assert bwd(dh0=P_ODD) == codes["S6_ERR_ALIGN"]
     assert bwd(d=0, dA=None) == codes["S6_OK"]  # no channels: nothing to write
+    g = lib.s6_scan_bwd_ex
+
+    def bwd_ex(flags=1, bias=P, dbias=P):
+        return g(2, 64, 32, 16, 1, P, P, bias, flags, P, P, P, None, None, None, P, None, P, P, P, P, P, None, None,
+                 None, dbias, None)
+
+    assert bwd_ex(flags=2) == codes["S6_ERR_UNSUPPORTED"]  # exact hold: forward only
+    assert bwd_ex(flags=3) == codes["S6_ERR_UNSUPPORTED"]
+    assert bwd_ex(flags=8) == codes["S6_ERR_FLAGS"]
+    assert bwd_ex(bias=P_ODD) == codes["S6_ERR_ALIGN"]
+    assert bwd_ex(dbias=P_ODD) == codes["S6_ERR_ALIGN"]
 
 
 def test_binding_refuses_host_tensors():
