@@ -893,6 +893,11 @@ __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
 // across the 4 waves in LDS, and across channel blocks by a second kernel
 // from per-block partials (a fixed order: results are bitwise repeatable).
 constexpr int kBwdSeg = 64;    // tokens per recomputation segment
+// Pitch (floats) of the staged [row][token] tiles.  With a pitch of 64 the
+// 16 states of a channel (float4 reads of B and C, one row each) and the 4
+// channels of a wave would all fall on the same LDS banks; 4 more floats put
+// consecutive rows 4 banks apart, so 16 lanes' 16-byte reads cover all 64.
+constexpr int kBwdPitch = kBwdSeg + 4;
 
 // Waves per workgroup (4 channels each).  The kernel needs 150-190 VGPRs,
 // i.e. two waves per SIMD: two 4-wave workgroups per CU, whose barriers fall
@@ -902,7 +907,7 @@ constexpr int bwd_waves() { return 4; }
 
 template <int SPL>
 constexpr size_t bwd_lds_bytes(bool sp) {
-  return sizeof(float) * ((size_t)(sp ? 5 : 4) * (4 * bwd_waves<SPL>()) * kBwdSeg + (size_t)2 * 16 * SPL * kBwdSeg +
+  return sizeof(float) * ((size_t)(sp ? 5 : 4) * (4 * bwd_waves<SPL>()) * kBwdPitch + (size_t)2 * 16 * SPL * kBwdPitch +
                           (size_t)bwd_waves<SPL>() * 2 * 16 * 16 * SPL);
 }
 
@@ -996,16 +1001,17 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
   constexpr int CW = 4 * WB;         // channels per workgroup
   constexpr int NS = 16 * SPL;       // state slots per channel
   constexpr int KS = kBwdSeg;
+  constexpr int KP = kBwdPitch;  // LDS row pitch: rows 4 banks apart
   extern __shared__ float4 lds4[];
   float* lds = reinterpret_cast<float*>(lds4);
   float* sx = lds;                   // [CW][KS] x
-  float* sdl = sx + CW * KS;         // [CW][KS] delta
-  float* sdyc = sdl + CW * KS;       // [CW][KS] dy * SiLU(z)
-  float* sq = sdyc + CW * KS;        // [CW][KS] dy * SiLU'(z)
-  float* sB = sq + CW * KS;          // [NS][KS]
-  float* sC = sB + NS * KS;          // [NS][KS]
-  float* red = sC + NS * KS;         // [waves][2][16][NS]
-  float* sjs = red + WB * 2 * 16 * NS;  // SP: [CW][KS] dstep/dv
+  float* sdl = sx + CW * KP;         // [CW][KP] delta
+  float* sdyc = sdl + CW * KP;       // [CW][KP] dy * SiLU(z)
+  float* sq = sdyc + CW * KP;        // [CW][KP] dy * SiLU'(z)
+  float* sB = sq + CW * KP;          // [NS][KP]
+  float* sC = sB + NS * KP;          // [NS][KP]
+  float* red = sC + NS * KP;         // [waves][2][16][NS]
+  float* sjs = red + WB * 2 * 16 * NS;  // SP: [CW][KP] dstep/dv
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1073,18 +1079,19 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
           dyc = g;
         }
       }
-      sx[i] = xv;
-      sdl[i] = dl;
-      sdyc[i] = dyc;
-      sq[i] = q;
-      if constexpr (SP) sjs[i] = js;
+      const int li = cc * KP + t;
+      sx[li] = xv;
+      sdl[li] = dl;
+      sdyc[li] = dyc;
+      sq[li] = q;
+      if constexpr (SP) sjs[li] = js;
     }
     for (int i = tid; i < NS * KS; i += NTHR) {
       const int n = i / KS, t = i % KS;
       const bool ok = n < N && t < tl;
       const int64_t off = (b * N + (n < N ? n : 0)) * L + tb + (t < tl ? t : 0);
-      sB[i] = ok ? to_f32(Bp[off]) : 0.0f;
-      sC[i] = ok ? to_f32(Cp[off]) : 0.0f;
+      sB[n * KP + t] = ok ? to_f32(Bp[off]) : 0.0f;
+      sC[n * KP + t] = ok ? to_f32(Cp[off]) : 0.0f;
     }
     __syncthreads();
 
@@ -1106,13 +1113,13 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
           // hoist every LDS read of the segment and run out of registers
           __builtin_amdgcn_sched_barrier(0);
           const int t = 16 * k + 4 * g;
-          const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KS + t);
-          const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KS + t);
+          const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KP + t);
+          const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KP + t);
           const float dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
           const float u[4] = {dl4.x * x4.x, dl4.y * x4.y, dl4.z * x4.z, dl4.w * x4.w};
 #pragma unroll
           for (int j = 0; j < SPL; ++j) {
-            const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KS + t);
+            const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KP + t);
             const float Bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) h[j] = __builtin_fmaf(fast_exp2(dl[i] * A2[j]), h[j], u[i] * Bv[i]);
@@ -1132,13 +1139,13 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
       for (int g = 0; g < 4; ++g) {
         __builtin_amdgcn_sched_barrier(0);
         const int t = 16 * k + 4 * g;
-        const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KS + t);
-        const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KS + t);
+        const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KP + t);
+        const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KP + t);
         const float dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
         const float u[4] = {dl4.x * x4.x, dl4.y * x4.y, dl4.z * x4.z, dl4.w * x4.w};
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
-          const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KS + t);
+          const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KP + t);
           const float Bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -1151,17 +1158,17 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
       for (int g4 = 3; g4 >= 0; --g4) {
         __builtin_amdgcn_sched_barrier(0);
         const int t4 = 16 * k + 4 * g4;
-        const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KS + t4);
-        const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KS + t4);
-        const float4 y4 = *reinterpret_cast<const float4*>(sdyc + c * KS + t4);
+        const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KP + t4);
+        const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KP + t4);
+        const float4 y4 = *reinterpret_cast<const float4*>(sdyc + c * KP + t4);
         const float dlv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
         const float xvv[4] = {x4.x, x4.y, x4.z, x4.w};
         const float dycv[4] = {y4.x, y4.y, y4.z, y4.w};
         float Bv[SPL][4], Cv[SPL][4];
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
-          const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KS + t4);
-          const float4 c4 = *reinterpret_cast<const float4*>(sC + (nl * SPL + j) * KS + t4);
+          const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KP + t4);
+          const float4 c4 = *reinterpret_cast<const float4*>(sC + (nl * SPL + j) * KP + t4);
           Bv[j][0] = b4.x; Bv[j][1] = b4.y; Bv[j][2] = b4.z; Bv[j][3] = b4.w;
           Cv[j][0] = c4.x; Cv[j][1] = c4.y; Cv[j][2] = c4.z; Cv[j][3] = c4.w;
         }
@@ -1210,18 +1217,18 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
         const int t = 16 * k + nl;
         const int64_t tt = tb + t;
         if (chv && tt < L) {
-          const float dl = sdl[c * KS + t];
-          const float xv = sx[c * KS + t];
-          const float dyc = sdyc[c * KS + t];
+          const float dl = sdl[c * KP + t];
+          const float xv = sx[c * KP + t];
+          const float dyc = sdyc[c * KP + t];
           const int64_t off = (b * D + d) * L + tt;
           a.dx[off] = __builtin_fmaf(dyc, dsk, dl * k1);
           float gd = __builtin_fmaf(xv, k1, k2);
           if constexpr (SP) {
-            gd *= sjs[c * KS + t];
+            gd *= sjs[c * KP + t];
             dbias += gd;
           }
           a.ddelta[off] = gd;
-          if (GATE && a.dz) a.dz[off] = __builtin_fmaf(dsk, xv, k3) * sq[c * KS + t];
+          if (GATE && a.dz) a.dz[off] = __builtin_fmaf(dsk, xv, k3) * sq[c * KP + t];
         }
       }
       __syncthreads();  // every wave's channel sums of the chunk are in LDS
@@ -1274,10 +1281,11 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_carry_kernel(Bwd
   constexpr int CW = 4 * WB;
   constexpr int NS = 16 * SPL;
   constexpr int KS = kBwdSeg;
+  constexpr int KP = kBwdPitch;  // LDS row pitch: rows 4 banks apart
   extern __shared__ float4 lds4[];
-  float* sdl = reinterpret_cast<float*>(lds4);  // [CW][KS]
-  float* sdyc = sdl + CW * KS;                  // [CW][KS]
-  float* sC = sdyc + CW * KS;                   // [NS][KS]
+  float* sdl = reinterpret_cast<float*>(lds4);  // [CW][KP]
+  float* sdyc = sdl + CW * KP;                  // [CW][KP]
+  float* sC = sdyc + CW * KP;                   // [NS][KP]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1327,22 +1335,22 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_carry_kernel(Bwd
           dyc *= zz * fast_rcp(1.0f + fast_exp2(-zz * kLog2e));
         }
       }
-      sdl[i] = dl;
-      sdyc[i] = dyc;
+      sdl[cc * KP + t] = dl;
+      sdyc[cc * KP + t] = dyc;
     }
     for (int i = tid; i < NS * KS; i += NTHR) {
       const int n = i / KS, t = i % KS;
       const bool ok = n < N && t < tl;
-      sC[i] = ok ? to_f32(Cp[(b * N + (n < N ? n : 0)) * L + tb + (t < tl ? t : 0)]) : 0.0f;
+      sC[n * KP + t] = ok ? to_f32(Cp[(b * N + (n < N ? n : 0)) * L + tb + (t < tl ? t : 0)]) : 0.0f;
     }
     __syncthreads();
     float cs = 0.0f;
     for (int t = KS - 1; t >= 0; --t) {
-      const float dlt = sdl[c * KS + t];
-      const float dyct = sdyc[c * KS + t];
+      const float dlt = sdl[c * KP + t];
+      const float dyct = sdyc[c * KP + t];
 #pragma unroll
       for (int j = 0; j < SPL; ++j)
-        mu[j] = fast_exp2(dlt * A2[j]) * __builtin_fmaf(dyct, sC[(nl * SPL + j) * KS + t], mu[j]);
+        mu[j] = fast_exp2(dlt * A2[j]) * __builtin_fmaf(dyct, sC[(nl * SPL + j) * KP + t], mu[j]);
       cs += dlt;
     }
     const float tsum = dsum + cs;
@@ -1720,7 +1728,7 @@ int launch_bwd_t(const BwdArgs& a, int64_t parts, bool carry, hipStream_t st) {
   const int64_t nblk = (a.D + CW - 1) / CW;
   const dim3 block(64 * bwd_waves<SPL>());
   if (carry) {
-    const size_t lds = sizeof(float) * ((size_t)2 * CW * kBwdSeg + (size_t)16 * SPL * kBwdSeg);
+    const size_t lds = sizeof(float) * ((size_t)2 * CW * kBwdPitch + (size_t)16 * SPL * kBwdPitch);
     hipLaunchKernelGGL((s6_bwd_carry_kernel<In, GATE, SPL, SP>),
                        dim3((unsigned)(nblk * a.batch), (unsigned)(parts - 1)), block, lds, st, a);
     S6_HIP(hipGetLastError(), "s6_bwd_carry_kernel launch");
