@@ -1129,10 +1129,8 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
     }
 
     for (int k = 3; k >= 0; --k) {
-      // the chunk's states: hist[j][i] = h before token i (the transitions
-      // are recomputed in the adjoint loop: keeping them costs 16 registers
-      // per state, which halves the waves per SIMD)
-      float hist[SPL][17];
+      // the chunk's transitions ea and states: hist[j][i] = h before token i
+      float ea[SPL][16], hist[SPL][17];
 #pragma unroll
       for (int j = 0; j < SPL; ++j) hist[j][0] = hc[k][j];
 #pragma unroll
@@ -1148,8 +1146,10 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
           const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KP + t);
           const float Bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            hist[j][4 * g + i + 1] = __builtin_fmaf(fast_exp2(dl[i] * A2[j]), hist[j][4 * g + i], u[i] * Bv[i]);
+          for (int i = 0; i < 4; ++i) {
+            ea[j][4 * g + i] = fast_exp2(dl[i] * A2[j]);
+            hist[j][4 * g + i + 1] = __builtin_fmaf(ea[j][4 * g + i], hist[j][4 * g + i], u[i] * Bv[i]);
+          }
         }
       }
       // adjoint, last token first; lane nl keeps the row sums of token nl
@@ -1182,10 +1182,9 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
           s3[i] = 0.0f;
 #pragma unroll
           for (int j = 0; j < SPL; ++j) {
-            const float ea = fast_exp2(dl * A2[j]);
             const float lam = __builtin_fmaf(dyc, Cv[j][ii], mu[j]);
-            mu[j] = ea * lam;
-            const float r = lam * (ea * hist[j][i]);
+            mu[j] = ea[j][i] * lam;
+            const float r = lam * (ea[j][i] * hist[j][i]);
             s1[i] = __builtin_fmaf(lam, Bv[j][ii], s1[i]);
             s2[i] = __builtin_fmaf(An[j], r, s2[i]);
             s3[i] = __builtin_fmaf(Cv[j][ii], hist[j][i + 1], s3[i]);
@@ -1386,14 +1385,26 @@ __global__ void s6_bwd_fold(const float* __restrict__ A, const float* __restrict
   }
 }
 
-// dB and dC: sums of the per-block partials over the channel blocks, in order.
+// dB and dC: sums of the per-block partials over the channel blocks.  Four
+// running sums (blocks k = 4m + j go to sum j), added at the end in a fixed
+// order: the loads of four blocks are in flight at once, and the result does
+// not depend on the launch shape.
 __global__ void s6_bwd_reduce_bc(const float* __restrict__ part, float* __restrict__ out, int64_t nblk,
                                  int64_t total) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    float s = 0.0f;
-    for (int64_t k = 0; k < nblk; ++k) s += part[k * total + i];
-    out[i] = s;
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    int64_t k = 0;
+    for (; k + 4 <= nblk; k += 4) {
+      s0 += part[k * total + i];
+      s1 += part[(k + 1) * total + i];
+      s2 += part[(k + 2) * total + i];
+      s3 += part[(k + 3) * total + i];
+    }
+    if (k < nblk) s0 += part[k * total + i];
+    if (k + 1 < nblk) s1 += part[(k + 1) * total + i];
+    if (k + 2 < nblk) s2 += part[(k + 2) * total + i];
+    out[i] = (s0 + s1) + (s2 + s3);
   }
 }
 
