@@ -26,14 +26,18 @@ HBM_PEAK_GBS = 8000.0
 # x 2.4 GHz lane-operation slots per second.  A transcendental (v_exp_f32,
 # v_rcp_f32) takes two slots.
 VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
-KERNEL_SRC = os.path.join(ROOT, "selective_state_space_63_amd", "csrc", "s6.hip")
+# The sources of the scan kernel (the counters in TRAFFIC_FILE hold for them).
+KERNEL_SRC = [os.path.join(ROOT, "selective_state_space_63_amd", "csrc", f) for f in ("scan.hip", "s6_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "s6_scan_kernel_m3b_traffic.md")
 
 
-def source_digest(path=KERNEL_SRC):
+def source_digest(paths=KERNEL_SRC):
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(path=TRAFFIC_FILE):

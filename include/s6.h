@@ -72,7 +72,7 @@ extern "C" {
 #define S6_ERR_NULL (-1)        /* a required pointer is NULL */
 #define S6_ERR_SHAPE (-2)       /* a size is negative or the element count overflows */
 #define S6_ERR_DTYPE (-3)       /* in_dtype is not S6_F32 or S6_BF16 */
-#define S6_ERR_UNSUPPORTED (-4) /* dstate outside 1..32 */
+#define S6_ERR_UNSUPPORTED (-4) /* dstate outside 1..32, or an option the entry point lacks */
 #define S6_ERR_ALIGN (-5)       /* a pointer is not aligned to its element size */
 #define S6_ERR_HIP (-6)         /* a HIP call failed; s6_status_str gives the detail */
 #define S6_ERR_FLAGS (-7)       /* unknown bits in the flags of an _ex entry point */

@@ -1,0 +1,759 @@
+// bwd.hip -- gradients of the scan (s6_scan_bwd and its _ex form) with the
+// states recomputed.
+#include "s6_internal.h"
+
+namespace s6i {
+
+namespace {
+
+// Reverse-mode gradients of the scan for the loss <dy, y> + <dh_last, h_last>
+// (plain step).  The states are recomputed, never stored per token: a
+// state-only pass and the carry fold give the state entering every segment of
+// kBwdSeg tokens (the same kernels as a segmented forward scan); this kernel
+// then walks the segments of a (batch row, 16-channel block) from the last to
+// the first.  Per segment it stages the inputs in LDS, recomputes the states
+// at the four chunk starts, and per 16-token chunk (last first) recomputes
+// the chunk's states and transitions in registers and runs the adjoint
+// lambda_t = dyc_t C_t + a_{t+1} lambda_{t+1} backwards through it.
+//
+// Lane l of wave w: channel c = 4w + (l >> 4) of the block, states
+// (l & 15) * SPL + j.  Sums over states (for dx, ddelta and the pre-gate
+// output) are taken across the 16 lanes of a row with a DPP butterfly that
+// leaves token l's sums in lane l; sums
+// over channels (dB, dC) across the 4 rows of a wave with permlane swaps,
+// across the 4 waves in LDS, and across channel blocks by a second kernel
+// from per-block partials (a fixed order: results are bitwise repeatable).
+constexpr int kBwdSeg = 64;    // tokens per recomputation segment
+// Pitch (floats) of the staged [row][token] tiles.  With a pitch of 64 the
+// 16 states of a channel (float4 reads of B and C, one row each) and the 4
+// channels of a wave would all fall on the same LDS banks; 4 more floats put
+// consecutive rows 4 banks apart, so 16 lanes' 16-byte reads cover all 64.
+constexpr int kBwdPitch = kBwdSeg + 4;
+
+// Waves per workgroup (4 channels each).  The kernel needs 150-190 VGPRs,
+// i.e. two waves per SIMD: two 4-wave workgroups per CU, whose barriers fall
+// at different times, run faster than one 8-wave workgroup.
+template <int SPL>
+constexpr int bwd_waves() { return 4; }
+
+template <int SPL>
+constexpr size_t bwd_lds_bytes(bool sp) {
+  return sizeof(float) * ((size_t)(sp ? 5 : 4) * (4 * bwd_waves<SPL>()) * kBwdPitch + (size_t)2 * 16 * SPL * kBwdPitch +
+                          (size_t)bwd_waves<SPL>() * 2 * 16 * 16 * SPL);
+}
+
+// Step of a stored delta value under the step options (SP kernels): v =
+// delta + bias, then softplus(v) if asked; *js receives dstep/dv.
+__device__ __forceinline__ float bwd_step(float raw, float bias, bool softplus, float* js) {
+  const float v = raw + bias;
+  if (!softplus) {
+    *js = 1.0f;
+    return v;
+  }
+  *js = fast_rcp(1.0f + fast_exp2(-v * kLog2e));
+  return softplus_f(v);
+}
+
+struct BwdArgs {
+  const void* x;
+  const void* delta;
+  const void* z;          // null: no gate
+  const void* Bm;
+  const void* Cm;
+  const float* A;
+  const float* Dskip;     // nullable
+  const float* dy;        // (batch, D, L)
+  const float* dh_last;   // nullable
+  const float* hin;       // (S, batch*D*N): state entering each segment
+  float* dx;              // (batch, D, L)
+  float* ddelta;          // (batch, D, L)
+  float* dz;              // (batch, D, L), gate only
+  float* dA_part;         // (G, batch, D, N): sums over the tokens of one batch row and part
+  float* dD_part;         // (G, batch, D)
+  float* dB_part;         // (nblk, batch, N, L)
+  float* dC_part;         // (nblk, batch, N, L)
+  float* dh0;             // nullable (batch, D, N)
+  const float* mu_in;     // (G, batch*D*N): adjoint carry entering each part from the right, or
+                          // null (one part: the carry is dh_last)
+  float* carry_M;         // (G, batch*D*N): carry leaving each part from a zero carry-in
+  float* carry_SD;        // (G, batch*D): summed delta of each part
+  const float* dbias;     // SP kernels: (D) step bias or null
+  int softplus;           // SP kernels: step = softplus(delta + dbias)
+  float* ddbias_part;     // SP kernels: (G, batch, D) gradient of the bias, or null
+  int64_t batch, D, L, N, nseg;
+  int64_t seg_per_part;   // segments per part (the sequence is cut into G parts, blockIdx.y)
+};
+
+// Sums over the 16 lanes of a row of 16 per-token values, leaving token l's
+// sum in lane l of the row: a butterfly over the lane partners l^8 (row
+// rotation by 8), l^7 (half-row mirror), l^2 and l^1 (quad permutations).  At
+// each step a lane keeps the half of its values whose token index has the
+// lane's bit (8, 4, 2, 1), and adds its partner's copy of that half; the
+// partner shares the bits already used, so both hold the same tokens.
+__device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int nl) {
+  const bool b3 = nl & 8, b2 = nl & 4, b1 = nl & 2, b0 = nl & 1;
+  float a8[8], a4[4], a2[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a8[j] = (b3 ? v[j + 8] : v[j]) + dpp_f<0x128>(b3 ? v[j] : v[j + 8]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a4[j] = (b2 ? a8[j + 4] : a8[j]) + dpp_f<0x141>(b2 ? a8[j] : a8[j + 4]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) a2[j] = (b1 ? a4[j + 2] : a4[j]) + dpp_f<0x4E>(b1 ? a4[j] : a4[j + 2]);
+  return (b0 ? a2[1] : a2[0]) + dpp_f<0xB1>(b0 ? a2[0] : a2[1]);
+}
+
+// Sums over the 4 rows (channels) of a wave for 4 tokens at once: v[k] is
+// this lane's value of token k; the result in row r is the 4-row sum of
+// token row_tok(r) = 0, 2, 1, 3 (v_permlane32_swap pairs rows 0,1 with 2,3
+// for two tokens, v_permlane16_swap then rows 0 with 1 and 2 with 3).
+__device__ __forceinline__ int row_tok(int r) { return ((r & 1) << 1) | (r >> 1); }
+__device__ __forceinline__ float rows_sum4(const float (&v)[4]) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v[0]),
+                                                  __builtin_bit_cast(unsigned, v[1]), false, false);
+  const auto q = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v[2]),
+                                                  __builtin_bit_cast(unsigned, v[3]), false, false);
+  const float w01 = __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
+  const float w23 = __builtin_bit_cast(float, (unsigned)q[0]) + __builtin_bit_cast(float, (unsigned)q[1]);
+  const auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, w01),
+                                                  __builtin_bit_cast(unsigned, w23), false, false);
+  return __builtin_bit_cast(float, (unsigned)s[0]) + __builtin_bit_cast(float, (unsigned)s[1]);
+}
+
+// SP: the step bias / softplus options (the gradient of the stored delta
+// gets the factor dstep/dv; the bias gradient is summed per channel).
+template <typename In, bool GATE, int SPL, bool SP>
+__global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a) {
+  constexpr int WB = bwd_waves<SPL>();
+  constexpr int NTHR = 64 * WB;
+  constexpr int CW = 4 * WB;         // channels per workgroup
+  constexpr int NS = 16 * SPL;       // state slots per channel
+  constexpr int KS = kBwdSeg;
+  constexpr int KP = kBwdPitch;  // LDS row pitch: rows 4 banks apart
+  extern __shared__ float4 lds4[];
+  float* lds = reinterpret_cast<float*>(lds4);
+  float* sx = lds;                   // [CW][KS] x
+  float* sdl = sx + CW * KP;         // [CW][KP] delta
+  float* sdyc = sdl + CW * KP;       // [CW][KP] dy * SiLU(z)
+  float* sq = sdyc + CW * KP;        // [CW][KP] dy * SiLU'(z)
+  float* sB = sq + CW * KP;          // [NS][KP]
+  float* sC = sB + NS * KP;          // [NS][KP]
+  float* red = sC + NS * KP;         // [waves][2][16][NS]
+  float* sjs = red + WB * 2 * 16 * NS;  // SP: [CW][KP] dstep/dv
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int row = lane >> 4;
+  const int nl = lane & 15;
+  const int c = 4 * w + row;
+  const int64_t D = a.D, L = a.L, N = a.N;
+  const int64_t nblk = (D + CW - 1) / CW;
+  const int64_t blk = blockIdx.x % nblk;
+  const int64_t b = blockIdx.x / nblk;
+  const int64_t d0 = blk * CW;
+  const int64_t rows_valid = D - d0 < CW ? D - d0 : CW;
+  const int64_t d = d0 + c;
+  const bool chv = c < rows_valid;
+  const In* xp = static_cast<const In*>(a.x);
+  const In* dp = static_cast<const In*>(a.delta);
+  const In* zp = static_cast<const In*>(a.z);
+  const In* Bp = static_cast<const In*>(a.Bm);
+  const In* Cp = static_cast<const In*>(a.Cm);
+  const float dsk = (a.Dskip && chv) ? a.Dskip[d] : 0.0f;
+
+  // this workgroup's part of the sequence: segments [s_begin, s_end)
+  const int64_t part = blockIdx.y;
+  const int64_t nstate = a.batch * D * N;
+  const int64_t s_begin = part * a.seg_per_part;
+  const int64_t s_end = s_begin + a.seg_per_part < a.nseg ? s_begin + a.seg_per_part : a.nseg;
+
+  float A2[SPL], An[SPL], mu[SPL], dA[SPL];
+  bool sv[SPL];
+#pragma unroll
+  for (int j = 0; j < SPL; ++j) {
+    const int64_t n = (int64_t)nl * SPL + j;
+    sv[j] = chv && n < N;
+    An[j] = sv[j] ? a.A[d * N + n] : 0.0f;
+    A2[j] = An[j] * kLog2e;
+    // a_{t+1} lambda_{t+1} entering the part's last token
+    mu[j] = !sv[j] ? 0.0f
+            : a.mu_in ? a.mu_in[part * nstate + (b * D + d) * N + n]
+            : a.dh_last ? a.dh_last[(b * D + d) * N + n] : 0.0f;
+    dA[j] = 0.0f;
+  }
+  float dD = 0.0f, dbias = 0.0f;
+
+  for (int64_t s = s_end - 1; s >= s_begin; --s) {
+    const int64_t tb = s * KS;
+    const int64_t tl = L - tb < KS ? L - tb : KS;  // valid tokens of the segment
+    __syncthreads();  // the previous segment's reads of the staged inputs are done
+    for (int i = tid; i < CW * KS; i += NTHR) {
+      const int cc = i / KS, t = i % KS;
+      const bool ok = cc < rows_valid && t < tl;
+      const int64_t off = (b * D + d0 + (cc < rows_valid ? cc : 0)) * L + tb + (t < tl ? t : 0);
+      float xv = 0.0f, dl = 0.0f, dyc = 0.0f, q = 0.0f, js = 0.0f;
+      if (ok) {
+        xv = to_f32(xp[off]);
+        dl = to_f32(dp[off]);
+        if constexpr (SP) dl = bwd_step(dl, a.dbias ? a.dbias[d0 + cc] : 0.0f, a.softplus, &js);
+        const float g = a.dy[off];
+        if constexpr (GATE) {
+          const float zz = to_f32(zp[off]);
+          const float sg = fast_rcp(1.0f + fast_exp2(-zz * kLog2e));
+          dyc = g * (zz * sg);
+          q = g * (sg * (1.0f + zz * (1.0f - sg)));
+        } else {
+          dyc = g;
+        }
+      }
+      const int li = cc * KP + t;
+      sx[li] = xv;
+      sdl[li] = dl;
+      sdyc[li] = dyc;
+      sq[li] = q;
+      if constexpr (SP) sjs[li] = js;
+    }
+    for (int i = tid; i < NS * KS; i += NTHR) {
+      const int n = i / KS, t = i % KS;
+      const bool ok = n < N && t < tl;
+      const int64_t off = (b * N + (n < N ? n : 0)) * L + tb + (t < tl ? t : 0);
+      sB[n * KP + t] = ok ? to_f32(Bp[off]) : 0.0f;
+      sC[n * KP + t] = ok ? to_f32(Cp[off]) : 0.0f;
+    }
+    __syncthreads();
+
+    // states at the four chunk starts of the segment
+    float hc[4][SPL];
+    {
+      float h[SPL];
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        const int64_t n = (int64_t)nl * SPL + j;
+        h[j] = sv[j] ? a.hin[s * a.batch * D * N + (b * D + d) * N + n] : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) hc[k][j] = h[j];
+        for (int g = 0; g < 4; ++g) {
+          // one group of 4 tokens at a time: the compiler would otherwise
+          // hoist every LDS read of the segment and run out of registers
+          __builtin_amdgcn_sched_barrier(0);
+          const int t = 16 * k + 4 * g;
+          const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KP + t);
+          const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KP + t);
+          const float dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+          const float u[4] = {dl4.x * x4.x, dl4.y * x4.y, dl4.z * x4.z, dl4.w * x4.w};
+#pragma unroll
+          for (int j = 0; j < SPL; ++j) {
+            const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KP + t);
+            const float Bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h[j] = __builtin_fmaf(fast_exp2(dl[i] * A2[j]), h[j], u[i] * Bv[i]);
+          }
+        }
+      }
+    }
+
+    for (int k = 3; k >= 0; --k) {
+      // the chunk's transitions ea and states: hist[j][i] = h before token i
+      float ea[SPL][16], hist[SPL][17];
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) hist[j][0] = hc[k][j];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int t = 16 * k + 4 * g;
+        const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KP + t);
+        const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KP + t);
+        const float dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+        const float u[4] = {dl4.x * x4.x, dl4.y * x4.y, dl4.z * x4.z, dl4.w * x4.w};
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+          const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KP + t);
+          const float Bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ea[j][4 * g + i] = fast_exp2(dl[i] * A2[j]);
+            hist[j][4 * g + i + 1] = __builtin_fmaf(ea[j][4 * g + i], hist[j][4 * g + i], u[i] * Bv[i]);
+          }
+        }
+      }
+      // adjoint, last token first; lane nl keeps the row sums of token nl
+      float s1[16], s2[16], s3[16];  // this lane's terms of the state sums, per token
+#pragma unroll
+      for (int g4 = 3; g4 >= 0; --g4) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int t4 = 16 * k + 4 * g4;
+        const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KP + t4);
+        const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KP + t4);
+        const float4 y4 = *reinterpret_cast<const float4*>(sdyc + c * KP + t4);
+        const float dlv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+        const float xvv[4] = {x4.x, x4.y, x4.z, x4.w};
+        const float dycv[4] = {y4.x, y4.y, y4.z, y4.w};
+        float Bv[SPL][4], Cv[SPL][4];
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+          const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KP + t4);
+          const float4 c4 = *reinterpret_cast<const float4*>(sC + (nl * SPL + j) * KP + t4);
+          Bv[j][0] = b4.x; Bv[j][1] = b4.y; Bv[j][2] = b4.z; Bv[j][3] = b4.w;
+          Cv[j][0] = c4.x; Cv[j][1] = c4.y; Cv[j][2] = c4.z; Cv[j][3] = c4.w;
+        }
+        float pb[SPL][4], pc[SPL][4];
+#pragma unroll
+        for (int ii = 3; ii >= 0; --ii) {
+          const int i = 4 * g4 + ii;
+          const float dl = dlv[ii], xv = xvv[ii], dyc = dycv[ii];
+          s1[i] = 0.0f;
+          s2[i] = 0.0f;
+          s3[i] = 0.0f;
+#pragma unroll
+          for (int j = 0; j < SPL; ++j) {
+            const float lam = __builtin_fmaf(dyc, Cv[j][ii], mu[j]);
+            mu[j] = ea[j][i] * lam;
+            const float r = lam * (ea[j][i] * hist[j][i]);
+            s1[i] = __builtin_fmaf(lam, Bv[j][ii], s1[i]);
+            s2[i] = __builtin_fmaf(An[j], r, s2[i]);
+            s3[i] = __builtin_fmaf(Cv[j][ii], hist[j][i + 1], s3[i]);
+            dA[j] = __builtin_fmaf(dl, r, dA[j]);
+            pb[j][ii] = lam * (dl * xv);
+            pc[j][ii] = dyc * hist[j][i + 1];
+          }
+          dD = __builtin_fmaf(dyc, xv, dD);
+        }
+        // the running sums are updated here (left alone, the compiler defers
+        // them to the end of the chunk and keeps all their operands live)
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) asm volatile("" : "+v"(dA[j]), "+v"(mu[j]));
+        asm volatile("" : "+v"(dD));
+        // channel sums of the 4 tokens over the wave's rows, then to LDS
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+          const int tok = 4 * g4 + row_tok(row);
+          red[((w * 2 + 0) * 16 + tok) * NS + nl * SPL + j] = rows_sum4(pb[j]);
+          red[((w * 2 + 1) * 16 + tok) * NS + nl * SPL + j] = rows_sum4(pc[j]);
+        }
+      }
+      // sums over the row's states: lane nl gets those of token nl
+      const float k1 = row_reduce_scatter16(s1, nl);
+      const float k2 = row_reduce_scatter16(s2, nl);
+      const float k3 = GATE ? row_reduce_scatter16(s3, nl) : 0.0f;
+      // outputs of token nl of the chunk for this lane's channel
+      {
+        const int t = 16 * k + nl;
+        const int64_t tt = tb + t;
+        if (chv && tt < L) {
+          const float dl = sdl[c * KP + t];
+          const float xv = sx[c * KP + t];
+          const float dyc = sdyc[c * KP + t];
+          const int64_t off = (b * D + d) * L + tt;
+          a.dx[off] = __builtin_fmaf(dyc, dsk, dl * k1);
+          float gd = __builtin_fmaf(xv, k1, k2);
+          if constexpr (SP) {
+            gd *= sjs[c * KP + t];
+            dbias += gd;
+          }
+          a.ddelta[off] = gd;
+          if (GATE && a.dz) a.dz[off] = __builtin_fmaf(dsk, xv, k3) * sq[c * KP + t];
+        }
+      }
+      __syncthreads();  // every wave's channel sums of the chunk are in LDS
+      for (int e = tid; e < 2 * 16 * NS; e += NTHR) {
+        const int kind = e / (16 * NS);
+        const int tok = (e / NS) % 16;
+        const int n = e % NS;
+        float sum = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < WB; ++ww) sum += red[((ww * 2 + kind) * 16 + tok) * NS + n];
+        const int64_t tt = tb + 16 * k + tok;
+        if (n < N && tt < L) {
+          float* dst = kind ? a.dC_part : a.dB_part;
+          dst[((blk * a.batch + b) * N + n) * L + tt] = sum;
+        }
+      }
+      __syncthreads();  // red is free again
+    }
+  }
+  if (chv) {
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const int64_t n = (int64_t)nl * SPL + j;
+      if (n < N) {
+        a.dA_part[part * nstate + (b * D + d) * N + n] = dA[j];
+        if (a.dh0 && part == 0) a.dh0[(b * D + d) * N + n] = mu[j];
+      }
+    }
+    if (nl == 0) a.dD_part[part * a.batch * D + b * D + d] = dD;
+  }
+  if constexpr (SP) {
+    // the channel's bias gradient: lane nl summed the tokens it wrote
+    dbias += dpp_f<0x128>(dbias);
+    dbias += dpp_f<0x124>(dbias);
+    dbias += dpp_f<0x122>(dbias);
+    dbias += dpp_f<0x121>(dbias);
+    if (chv && nl == 0 && a.ddbias_part) a.ddbias_part[part * a.batch * D + b * D + d] = dbias;
+  }
+}
+
+// Adjoint carries of the parts of a long sequence: for part g = blockIdx.y + 1
+// (the first part's carry is never needed), the carry a_t lambda_t that
+// leaves its first token when zero enters its last one, mu <- a_t (dyc_t C_t
+// + mu) from the last token back, and the part's summed delta (compensated),
+// from which exp(A sum delta) carries the right neighbour's carry through.
+template <typename In, bool GATE, int SPL, bool SP>
+__global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_carry_kernel(BwdArgs a) {
+  constexpr int WB = bwd_waves<SPL>();
+  constexpr int NTHR = 64 * WB;
+  constexpr int CW = 4 * WB;
+  constexpr int NS = 16 * SPL;
+  constexpr int KS = kBwdSeg;
+  constexpr int KP = kBwdPitch;  // LDS row pitch: rows 4 banks apart
+  extern __shared__ float4 lds4[];
+  float* sdl = reinterpret_cast<float*>(lds4);  // [CW][KP]
+  float* sdyc = sdl + CW * KP;                  // [CW][KP]
+  float* sC = sdyc + CW * KP;                   // [NS][KP]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int nl = lane & 15;
+  const int c = 4 * (tid >> 6) + (lane >> 4);
+  const int64_t D = a.D, L = a.L, N = a.N;
+  const int64_t nblk = (D + CW - 1) / CW;
+  const int64_t b = blockIdx.x / nblk;
+  const int64_t d0 = (blockIdx.x % nblk) * CW;
+  const int64_t rows_valid = D - d0 < CW ? D - d0 : CW;
+  const int64_t d = d0 + c;
+  const bool chv = c < rows_valid;
+  const int64_t part = blockIdx.y + 1;
+  const int64_t nstate = a.batch * D * N;
+  const int64_t s_begin = part * a.seg_per_part;
+  const int64_t s_end = s_begin + a.seg_per_part < a.nseg ? s_begin + a.seg_per_part : a.nseg;
+  const In* dp = static_cast<const In*>(a.delta);
+  const In* zp = static_cast<const In*>(a.z);
+  const In* Cp = static_cast<const In*>(a.Cm);
+
+  float A2[SPL], mu[SPL];
+#pragma unroll
+  for (int j = 0; j < SPL; ++j) {
+    const int64_t n = (int64_t)nl * SPL + j;
+    A2[j] = (chv && n < N) ? a.A[d * N + n] * kLog2e : 0.0f;
+    mu[j] = 0.0f;
+  }
+  float dsum = 0.0f, dcomp = 0.0f;
+  for (int64_t s = s_end - 1; s >= s_begin; --s) {
+    const int64_t tb = s * KS;
+    const int64_t tl = L - tb < KS ? L - tb : KS;
+    __syncthreads();
+    for (int i = tid; i < CW * KS; i += NTHR) {
+      const int cc = i / KS, t = i % KS;
+      const bool ok = cc < rows_valid && t < tl;
+      const int64_t off = (b * D + d0 + (cc < rows_valid ? cc : 0)) * L + tb + (t < tl ? t : 0);
+      float dl = 0.0f, dyc = 0.0f;
+      if (ok) {
+        dl = to_f32(dp[off]);
+        if constexpr (SP) {
+          float js;
+          dl = bwd_step(dl, a.dbias ? a.dbias[d0 + cc] : 0.0f, a.softplus, &js);
+        }
+        dyc = a.dy[off];
+        if constexpr (GATE) {
+          const float zz = to_f32(zp[off]);
+          dyc *= zz * fast_rcp(1.0f + fast_exp2(-zz * kLog2e));
+        }
+      }
+      sdl[cc * KP + t] = dl;
+      sdyc[cc * KP + t] = dyc;
+    }
+    for (int i = tid; i < NS * KS; i += NTHR) {
+      const int n = i / KS, t = i % KS;
+      const bool ok = n < N && t < tl;
+      sC[n * KP + t] = ok ? to_f32(Cp[(b * N + (n < N ? n : 0)) * L + tb + (t < tl ? t : 0)]) : 0.0f;
+    }
+    __syncthreads();
+    float cs = 0.0f;
+    for (int t = KS - 1; t >= 0; --t) {
+      const float dlt = sdl[c * KP + t];
+      const float dyct = sdyc[c * KP + t];
+#pragma unroll
+      for (int j = 0; j < SPL; ++j)
+        mu[j] = fast_exp2(dlt * A2[j]) * __builtin_fmaf(dyct, sC[(nl * SPL + j) * KP + t], mu[j]);
+      cs += dlt;
+    }
+    const float tsum = dsum + cs;
+    dcomp += (fabsf(dsum) >= fabsf(cs)) ? (dsum - tsum) + cs : (cs - tsum) + dsum;
+    dsum = tsum;
+  }
+  if (chv) {
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const int64_t n = (int64_t)nl * SPL + j;
+      if (n < N) a.carry_M[part * nstate + (b * D + d) * N + n] = mu[j];
+    }
+    if (nl == 0) a.carry_SD[part * a.batch * D + b * D + d] = dsum + dcomp;
+  }
+}
+
+// Carries entering each part from the right: mu_in[G-1] = dh_last (or 0),
+// mu_in[g-1] = carry_M[g] + exp(A * carry_SD[g]) * mu_in[g].
+__global__ void s6_bwd_fold(const float* __restrict__ A, const float* __restrict__ dh_last,
+                            const float* __restrict__ M, const float* __restrict__ SD, float* __restrict__ mu_in,
+                            int64_t batch, int64_t D, int64_t N, int64_t G) {
+  const int64_t total = batch * D * N;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t n = i % N;
+  const int64_t bd = i / N;
+  const float A2 = A[(bd % D) * N + n] * kLog2e;
+  float mu = dh_last ? dh_last[i] : 0.0f;
+  mu_in[(G - 1) * total + i] = mu;
+  for (int64_t g = G - 1; g >= 1; --g) {
+    mu = __builtin_fmaf(fast_exp2(A2 * SD[g * batch * D + bd]), mu, M[g * total + i]);
+    mu_in[(g - 1) * total + i] = mu;
+  }
+}
+
+// dB and dC: sums of the per-block partials over the channel blocks.  Four
+// running sums (blocks k = 4m + j go to sum j), added at the end in a fixed
+// order: the loads of four blocks are in flight at once, and the result does
+// not depend on the launch shape.
+__global__ void s6_bwd_reduce_bc(const float* __restrict__ part, float* __restrict__ out, int64_t nblk,
+                                 int64_t total) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    int64_t k = 0;
+    for (; k + 4 <= nblk; k += 4) {
+      s0 += part[k * total + i];
+      s1 += part[(k + 1) * total + i];
+      s2 += part[(k + 2) * total + i];
+      s3 += part[(k + 3) * total + i];
+    }
+    if (k < nblk) s0 += part[k * total + i];
+    if (k + 1 < nblk) s1 += part[(k + 1) * total + i];
+    if (k + 2 < nblk) s2 += part[(k + 2) * total + i];
+    out[i] = (s0 + s1) + (s2 + s3);
+  }
+}
+
+// dA (D, N) and dD (D): sums over batch rows, in order.
+__global__ void s6_bwd_reduce_rows(const float* __restrict__ dA_part, const float* __restrict__ dD_part,
+                                   const float* __restrict__ db_part, float* __restrict__ dA,
+                                   float* __restrict__ dD, float* __restrict__ db, int64_t batch, int64_t D,
+                                   int64_t N) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < D * N) {
+    float s = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) s += dA_part[b * D * N + i];
+    dA[i] = s;
+  }
+  if (dD && i < D) {
+    float s = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) s += dD_part[b * D + i];
+    dD[i] = s;
+  }
+  if (db && i < D) {
+    float s = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) s += db_part[b * D + i];
+    db[i] = s;
+  }
+}
+
+// carry: the part-carry kernel (parts 1 .. G-1) instead of the main kernel.
+template <typename In, bool GATE, int SPL, bool SP>
+int launch_bwd_t(const BwdArgs& a, int64_t parts, bool carry, hipStream_t st) {
+  constexpr int CW = 4 * bwd_waves<SPL>();
+  const int64_t nblk = (a.D + CW - 1) / CW;
+  const dim3 block(64 * bwd_waves<SPL>());
+  if (carry) {
+    const size_t lds = sizeof(float) * ((size_t)2 * CW * kBwdPitch + (size_t)16 * SPL * kBwdPitch);
+    hipLaunchKernelGGL((s6_bwd_carry_kernel<In, GATE, SPL, SP>),
+                       dim3((unsigned)(nblk * a.batch), (unsigned)(parts - 1)), block, lds, st, a);
+    S6_HIP(hipGetLastError(), "s6_bwd_carry_kernel launch");
+  } else {
+    hipLaunchKernelGGL((s6_bwd_kernel<In, GATE, SPL, SP>), dim3((unsigned)(nblk * a.batch), (unsigned)parts), block,
+                       bwd_lds_bytes<SPL>(SP), st, a);
+    S6_HIP(hipGetLastError(), "s6_bwd_kernel launch");
+  }
+  return S6_OK;
+}
+
+template <typename In, int SPL, bool SP>
+int launch_bwd_g(const BwdArgs& a, bool gate, int64_t parts, bool carry, hipStream_t st) {
+  return gate ? launch_bwd_t<In, true, SPL, SP>(a, parts, carry, st)
+              : launch_bwd_t<In, false, SPL, SP>(a, parts, carry, st);
+}
+
+template <typename In>
+int launch_bwd(const BwdArgs& a, bool gate, int64_t parts, bool carry, hipStream_t st) {
+  const bool sp = a.dbias || a.softplus || a.ddbias_part;
+  if (a.N <= 16)
+    return sp ? launch_bwd_g<In, 1, true>(a, gate, parts, carry, st) : launch_bwd_g<In, 1, false>(a, gate, parts, carry, st);
+  return sp ? launch_bwd_g<In, 2, true>(a, gate, parts, carry, st) : launch_bwd_g<In, 2, false>(a, gate, parts, carry, st);
+}
+
+int bwd_channels_per_block(int64_t dstate) { return dstate <= 16 ? 4 * bwd_waves<1>() : 4 * bwd_waves<2>(); }
+
+}  // namespace
+
+}  // namespace s6i
+
+using namespace s6i;
+
+extern "C" {
+
+int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                   const void* x, const void* delta, const float* delta_bias, int flags, const float* A,
+                   const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
+                   const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
+                   float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* stream) {
+  int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
+  if (rc) return rc;
+  if (flags & ~(S6_DELTA_SOFTPLUS | S6_ZOH_EXACT)) return S6_ERR_FLAGS;
+  if (flags & S6_ZOH_EXACT) return S6_ERR_UNSUPPORTED;
+  const bool softplus = (flags & S6_DELTA_SOFTPLUS) != 0;
+  const bool work = batch > 0 && dim > 0 && seqlen > 0;
+  if (dim > 0 && !dA) return S6_ERR_NULL;
+  if (work && (!x || !delta || !A || !Bm || !Cm || !dy || !dx || !ddelta || !dBm || !dCm))
+    return S6_ERR_NULL;
+  const size_t esz = in_dtype == S6_BF16 ? 2 : 4;
+  const void* ins[] = {x, delta, Bm, Cm, z};
+  for (const void* p : ins)
+    if (p && !aligned(p, esz)) return S6_ERR_ALIGN;
+  const void* f32s[] = {A, Dskip, h0, dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, delta_bias,
+                        ddelta_bias};
+  for (const void* p : f32s)
+    if (p && !aligned(p, 4)) return S6_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dim == 0) return S6_OK;
+  const int64_t nstate = batch * dim * dstate;
+  if (!work) {
+    // no tokens or no rows: the parameter gradients are zero and dh0 = dh_last
+    fill(dA, 0.0f, dim * dstate, st);
+    fill(dDskip, 0.0f, dim, st);
+    fill(ddelta_bias, 0.0f, dim, st);
+    S6_HIP(hipGetLastError(), "s6_scan_bwd fill");
+    return dh0 ? launch_copy_state(dh_last, dh0, nstate, st) : S6_OK;
+  }
+
+  // workspace: segment states (pass 1, fold), per-row and per-block partials
+  const int64_t S = (seqlen + kBwdSeg - 1) / kBwdSeg;
+  const int64_t nagg = S - 1;
+  const int64_t cw = bwd_channels_per_block(dstate);
+  const int64_t nblkb = (dim + cw - 1) / cw;
+  // Parts: when the (row, channel block) workgroups fill less than half of
+  // the workgroup slots (few long rows), the sequence is cut into parts run
+  // side by side; the adjoint carry entering each part from the right comes
+  // from a carry pass and a fold.
+  int64_t G = 1;
+  {
+    const int64_t wgs = nblkb * batch;
+    const int64_t slots = (int64_t)cu_count() * (dstate <= 16 ? 4 : 3);
+    if (2 * wgs <= slots) G = slots / wgs < S ? slots / wgs : S;
+    if (G < 1) G = 1;
+  }
+  const int64_t spp = (S + G - 1) / G;  // segments per part
+  G = (S + spp - 1) / spp;
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const size_t agg_b = (size_t)(nagg > 0 ? nagg : 0) * nstate * sizeof(float);
+  const size_t sd_b = (size_t)(nagg > 0 ? nagg : 0) * batch * dim * sizeof(float);
+  const size_t hin_b = (size_t)S * nstate * sizeof(float);
+  const size_t dap_b = (size_t)G * nstate * sizeof(float);
+  const size_t ddp_b = (size_t)G * batch * dim * sizeof(float);
+  const size_t bc_b = (size_t)nblkb * batch * dstate * seqlen * sizeof(float);
+  const size_t mu_b = G > 1 ? (size_t)G * nstate * sizeof(float) : 0;     // carries: M and mu_in
+  const size_t csd_b = G > 1 ? (size_t)G * batch * dim * sizeof(float) : 0;
+  const size_t total = up(agg_b) + up(sd_b) + up(hin_b) + up(dap_b) + 2 * up(ddp_b) + 2 * up(bc_b) + 2 * up(mu_b) +
+                       up(csd_b);
+  void* ws = nullptr;
+  S6_HIP(hipMallocAsync(&ws, total, st), "hipMallocAsync(backward workspace)");
+  char* wp = static_cast<char*>(ws);
+  float* agg = reinterpret_cast<float*>(wp);
+  wp += up(agg_b);
+  float* sd = reinterpret_cast<float*>(wp);
+  wp += up(sd_b);
+  float* hin = reinterpret_cast<float*>(wp);
+  wp += up(hin_b);
+  float* dap = reinterpret_cast<float*>(wp);
+  wp += up(dap_b);
+  float* ddp = reinterpret_cast<float*>(wp);
+  wp += up(ddp_b);
+  float* dbp = reinterpret_cast<float*>(wp);  // bias gradient per part and row
+  wp += up(ddp_b);
+  float* dBp = reinterpret_cast<float*>(wp);
+  wp += up(bc_b);
+  float* dcp = reinterpret_cast<float*>(wp);
+  wp += up(bc_b);
+  float* cM = reinterpret_cast<float*>(wp);
+  wp += up(mu_b);
+  float* muin = reinterpret_cast<float*>(wp);
+  wp += up(mu_b);
+  float* cSD = reinterpret_cast<float*>(wp);
+
+  // pass 1: end state (from zero) and summed delta of every segment but the last
+  if (nagg > 0) {
+    const void* vecptrs[] = {x, delta, Bm};
+    Plan p = make_plan(batch, dim, seqlen, dstate, esz, vecptrs, 3);
+    ScanArgs g;
+    memset(&g, 0, sizeof(g));
+    g.x = x; g.delta = delta; g.Bm = Bm; g.A = A;
+    g.hout = agg; g.hout_stride = nstate; g.sumdelta = sd;
+    g.dbias = delta_bias; g.softplus = softplus;
+    g.D = dim; g.L = seqlen; g.N = dstate; g.seg_len = kBwdSeg;
+    rc = launch_scan_any(in_dtype, kModeState, g, p, false, batch, nagg, st);
+  }
+  // the state entering every segment
+  if (rc == S6_OK) {
+    rc = launch_fold_carries(A, h0, agg, sd, hin, nullptr, batch, dim, dstate, S, nagg, st);
+  }
+  if (rc == S6_OK) {
+    BwdArgs b;
+    memset(&b, 0, sizeof(b));
+    b.x = x; b.delta = delta; b.z = z; b.Bm = Bm; b.Cm = Cm; b.A = A; b.Dskip = Dskip;
+    b.dy = dy; b.dh_last = dh_last; b.hin = hin;
+    b.dx = dx; b.ddelta = ddelta; b.dz = dz; b.dA_part = dap; b.dD_part = ddp;
+    b.dB_part = dBp; b.dC_part = dcp; b.dh0 = dh0;
+    b.dbias = delta_bias; b.softplus = softplus; b.ddbias_part = ddelta_bias ? dbp : nullptr;
+    b.batch = batch; b.D = dim; b.L = seqlen; b.N = dstate; b.nseg = S; b.seg_per_part = spp;
+    const bool gate = z != nullptr;
+    if (G > 1) {
+      b.carry_M = cM;
+      b.carry_SD = cSD;
+      rc = in_dtype == S6_BF16 ? launch_bwd<uint16_t>(b, gate, G, true, st) : launch_bwd<float>(b, gate, G, true, st);
+      if (rc == S6_OK) {
+        hipLaunchKernelGGL(s6_bwd_fold, dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0, st, A, dh_last, cM, cSD,
+                           muin, batch, dim, dstate, G);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) rc = hip_fail(e, "s6_bwd_fold launch");
+      }
+      b.mu_in = muin;
+    }
+    if (rc == S6_OK)
+      rc = in_dtype == S6_BF16 ? launch_bwd<uint16_t>(b, gate, G, false, st) : launch_bwd<float>(b, gate, G, false, st);
+  }
+  if (rc == S6_OK) {
+    const int64_t tot = batch * dstate * seqlen;
+    int64_t blocks = (tot + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3((unsigned)blocks), dim3(256), 0, st, dBp, dBm, nblkb, tot);
+    hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3((unsigned)blocks), dim3(256), 0, st, dcp, dCm, nblkb, tot);
+    const int64_t rows = dim * dstate;
+    hipLaunchKernelGGL(s6_bwd_reduce_rows, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, dap, ddp, dbp,
+                       dA, dDskip, ddelta_bias, G * batch, dim, dstate);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) rc = hip_fail(e, "s6_bwd reduction launch");
+  }
+  hipError_t e = hipFreeAsync(ws, st);
+  if (rc == S6_OK && e != hipSuccess) rc = hip_fail(e, "hipFreeAsync(backward workspace)");
+  return rc;
+}
+
+int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
+                const float* Dskip, const void* z, const float* h0, const float* dy,
+                const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm, float* dCm,
+                float* dDskip, float* dz, float* dh0, void* stream) {
+  return s6_scan_bwd_ex(batch, dim, seqlen, dstate, in_dtype, x, delta, nullptr, 0, A, Bm, Cm, Dskip, z, h0, dy,
+                        dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, nullptr, stream);
+}
+
+}  // extern "C"
