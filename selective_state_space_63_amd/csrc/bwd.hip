@@ -640,6 +640,7 @@ int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, i
   const int64_t nagg = S - 1;
   const int64_t cw = bwd_channels_per_block(dstate);
   const int64_t nblkb = (dim + cw - 1) / cw;
+  if (nblkb * batch > INT32_MAX) return S6_ERR_SHAPE;  // grid size
   // Parts: when the (row, channel block) workgroups fill less than half of
   // the workgroup slots (few long rows), the sequence is cut into parts run
   // side by side; the adjoint carry entering each part from the right comes
