@@ -500,6 +500,8 @@ def main():
                     help="skip the long-sequence and 130M-layer scan lines")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (byte-counter calibration)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time s6_scan_bwd on the workload (one JSON line; for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the scan has no cross-GPU step); got --gpus {args.gpus}",
@@ -516,6 +518,9 @@ def main():
     s6.load_library()
     w = synth.WORKLOADS[args.workload]
     in_bytes = 2 if w.dtype == synth.BF16 else 4
+    if args.backward_only:
+        print(json.dumps({"backward": bench_backward(w, steps=args.steps, warmup=args.warmup)}), flush=True)
+        return
     print(f"[bench] scan {w.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
     inp, tm, wall = bench_scan(w, args.steps, args.warmup)
     ms = tm["mean"]
