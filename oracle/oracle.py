@@ -67,6 +67,12 @@ class Oracle:
         self.lib.oracle_scan_bwd.restype = ctypes.c_int
         self.lib.oracle_scan_bwd_ex.argtypes = [_I, _I, _I, _I, _P, _P, _P, ctypes.c_int] + [_P] * 26
         self.lib.oracle_scan_bwd_ex.restype = ctypes.c_int
+        self.lib.oracle_scan_xm.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, ctypes.c_int] + [_P] * 10
+        self.lib.oracle_scan_xm.restype = None
+        self.lib.oracle_step_xm.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.c_int] + [_P] * 7
+        self.lib.oracle_step_xm.restype = None
+        self.lib.oracle_conv_silu.argtypes = [_I, _I, _I, _I] + [_P] * 6
+        self.lib.oracle_conv_silu.restype = ctypes.c_int
         self.lib.oracle_num_threads.restype = ctypes.c_int
         self.path = path
 
@@ -87,13 +93,14 @@ class Oracle:
         return (SOFTPLUS if softplus else 0) | (ZOH_EXACT if zoh else 0)
 
     def scan(self, x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_bias=None,
-             softplus=False, zoh=False):
+             softplus=False, zoh=False, xmag=None):
         """Full scan.  x, delta, z: (batch, D, L); Bm, Cm: (batch, N, L);
         A: (D, N); Dskip: (D,); h0: (batch, D, N); delta_bias: (D,), added
         to delta.  softplus: the step is softplus(delta + delta_bias); zoh:
-        exact zero-order-hold input coefficient (exp(Delta A) - 1) / A.  Returns a
-        dict with y and m (batch, D, L), h_last and H_last (batch, D, N), all
-        fp64."""
+        exact zero-order-hold input coefficient (exp(Delta A) - 1) / A.
+        xmag: (batch, D, L) magnitudes taken for x in m (|x| when None; the
+        xm of conv_silu when x is its output).  Returns a dict with y and m
+        (batch, D, L), h_last and H_last (batch, D, N), all fp64."""
         x = np.asarray(x)
         Bsz, D, L = x.shape
         N = np.asarray(A).shape[1]
@@ -112,7 +119,11 @@ class Oracle:
         Hl = np.empty((Bsz, D, N))
         outs = [o.ctypes.data_as(_P) for o in (y, m, hl, Hl)]
         flags = self._flags(softplus, zoh)
-        if delta_bias is None and flags == 0:
+        if xmag is not None:
+            xm, xptr = self._in(xmag, (Bsz, D, L))
+            bias, bptr = self._in(delta_bias, (D,))
+            self.lib.oracle_scan_xm(Bsz, D, L, N, args[0], xptr, args[1], bptr, flags, *args[2:], *outs)
+        elif delta_bias is None and flags == 0:
             self.lib.oracle_scan(Bsz, D, L, N, *args, *outs)
         else:
             bias, bptr = self._in(delta_bias, (D,))
@@ -120,10 +131,10 @@ class Oracle:
         return {"y": y, "m": m, "h_last": hl, "H_last": Hl}
 
     def step(self, h, H, x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None, softplus=False,
-             zoh=False):
+             zoh=False, xmag=None):
         """One decode token.  h, H: (batch, D, N) fp64 arrays updated in place;
-        x, delta, z: (batch, D); Bm, Cm: (batch, N); options as in scan.
-        Returns (y, m)."""
+        x, delta, z: (batch, D); Bm, Cm: (batch, N); options and xmag as in
+        scan.  Returns (y, m)."""
         if h.dtype != np.float64 or not h.flags.c_contiguous or H.dtype != np.float64:
             raise ValueError("h and H must be contiguous float64 arrays")
         Bsz, D, N = h.shape
@@ -137,7 +148,13 @@ class Oracle:
         y = np.empty((Bsz, D))
         m = np.empty((Bsz, D))
         flags = self._flags(softplus, zoh)
-        if delta_bias is None and flags == 0:
+        if xmag is not None:
+            xm, xptr = self._in(xmag, (Bsz, D))
+            bias, bptr = self._in(delta_bias, (D,))
+            self.lib.oracle_step_xm(Bsz, D, N, h.ctypes.data_as(_P), H.ctypes.data_as(_P), args[0], xptr,
+                                    args[1], bptr, flags, *args[2:], y.ctypes.data_as(_P),
+                                    m.ctypes.data_as(_P))
+        elif delta_bias is None and flags == 0:
             self.lib.oracle_step(Bsz, D, N, h.ctypes.data_as(_P), H.ctypes.data_as(_P), *args,
                                  y.ctypes.data_as(_P), m.ctypes.data_as(_P))
         else:
@@ -147,6 +164,27 @@ class Oracle:
                                     m.ctypes.data_as(_P))
         return y, m
 
+    def conv_silu(self, x, w, bias=None, state=None):
+        """The convolution front: x' = SiLU(bias[d] + sum_k w[d, k]
+        x_{t-K+1+k}) along the tokens of each (batch, channel) row, inputs
+        before the sequence from state (batch, D, K-1) (oldest first) or 0.
+        x: (batch, D, L); w: (D, K); bias: (D,).  Returns (x', xm), both
+        (batch, D, L) fp64; xm is the magnitude the error metric takes for
+        x' (pass it to scan / step as xmag)."""
+        x = np.asarray(x)
+        Bsz, D, L = x.shape
+        K = np.asarray(w).shape[1]
+        xa, xp = self._in(x, (Bsz, D, L))
+        wa, wp = self._in(w, (D, K))
+        ba, bp = self._in(bias, (D,))
+        sa, sp = self._in(state, (Bsz, D, K - 1)) if state is not None else (None, None)
+        xo = np.empty((Bsz, D, L))
+        xm = np.empty((Bsz, D, L))
+        rc = self.lib.oracle_conv_silu(Bsz, D, L, K, xp, wp, bp, sp, xo.ctypes.data_as(_P),
+                                       xm.ctypes.data_as(_P))
+        if rc != 0:
+            raise ValueError("conv_silu: width must be >= 1")
+        return xo, xm
 
     def scan_bwd(self, x, delta, A, Bm, Cm, dy, Dskip=None, z=None, h0=None, dh_last=None,
                  delta_bias=None, softplus=False):

@@ -87,32 +87,38 @@ static double zoh_coef(double dt, double a) { return a != 0.0 ? expm1(dt * a) / 
  * h, H   : the N states and their magnitudes, updated in place.
  * Ad     : A[d, 0..N-1].
  * Bt, Ct : B and C of this token; state n is at Bt[n * bstride].
+ * xm     : the magnitude taken for the input x_t in H and *mag: |x_t| for a
+ *          plain input, the convolution front's magnitude for its output.
  * Returns the token's output before the gate; *mag gets its magnitude. */
 static double step_channel(int64_t N, double* h, double* H, const double* Ad, double dt, double xt,
                            const double* Bt, const double* Ct, int64_t bstride, double dskip,
-                           int zoh, double* mag) {
+                           int zoh, double xm, double* mag) {
   double acc = 0.0, macc = 0.0;
   for (int64_t n = 0; n < N; ++n) {
     double a = exp(dt * Ad[n]);         /* zero-order-hold state transition */
-    double bx = (zoh ? zoh_coef(dt, Ad[n]) : dt) * Bt[n * bstride] * xt; /* input term */
+    double cb = (zoh ? zoh_coef(dt, Ad[n]) : dt) * Bt[n * bstride];
+    double bx = cb * xt;                /* input term */
     h[n] = a * h[n] + bx;               /* update first ... */
-    H[n] = fabs(a) * H[n] + fabs(bx);
+    H[n] = fabs(a) * H[n] + fabs(cb) * xm;
     acc += Ct[n * bstride] * h[n];      /* ... then read the output from the new state */
     macc += fabs(Ct[n * bstride]) * H[n];
   }
   double skip = dskip * xt;
-  *mag = macc + fabs(skip);
+  *mag = macc + fabs(dskip) * xm;
   return acc + skip;
 }
 
 /* Whole sequence.  Dskip, z and h0 may be NULL (no skip, no gate, zero
  * initial state).  m, h_last and H_last may be NULL (not written).
  * dbias (D) may be NULL (no bias); flags: ORACLE_* above.
+ * xmag (Bsz, D, L) may be NULL: the magnitudes taken for x (|x| when NULL;
+ * oracle_conv_silu's xm when x is the convolution front's output).
  * N must not exceed 256. */
-void oracle_scan_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x,
-                    const double* delta, const double* dbias, int flags, const double* A,
-                    const double* Bm, const double* Cm, const double* Dskip, const double* z,
-                    const double* h0, double* y, double* m, double* h_last, double* H_last) {
+void oracle_scan_xm(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x,
+                    const double* xmag, const double* delta, const double* dbias, int flags,
+                    const double* A, const double* Bm, const double* Cm, const double* Dskip,
+                    const double* z, const double* h0, double* y, double* m, double* h_last,
+                    double* H_last) {
   const int zoh = (flags & ORACLE_ZOH_EXACT) != 0;
   int64_t pairs = Bsz * D;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -129,8 +135,9 @@ void oracle_scan_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* 
     for (int64_t t = 0; t < L; ++t) {
       double mag;
       double dt = step_of(delta[p * L + t], dbias, d, flags);
+      double xm = xmag ? xmag[p * L + t] : fabs(x[p * L + t]);
       double yt = step_channel(N, h, H, A + d * N, dt, x[p * L + t], Bb + t, Cb + t,
-                               L, dsk, zoh, &mag);
+                               L, dsk, zoh, xm, &mag);
       if (z) {
         double g = silu(z[p * L + t]);
         yt *= g;
@@ -146,6 +153,14 @@ void oracle_scan_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* 
   }
 }
 
+void oracle_scan_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x,
+                    const double* delta, const double* dbias, int flags, const double* A,
+                    const double* Bm, const double* Cm, const double* Dskip, const double* z,
+                    const double* h0, double* y, double* m, double* h_last, double* H_last) {
+  oracle_scan_xm(Bsz, D, L, N, x, NULL, delta, dbias, flags, A, Bm, Cm, Dskip, z, h0, y, m,
+                 h_last, H_last);
+}
+
 void oracle_scan(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x, const double* delta,
                  const double* A, const double* Bm, const double* Cm, const double* Dskip,
                  const double* z, const double* h0, double* y, double* m, double* h_last,
@@ -156,10 +171,10 @@ void oracle_scan(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x, 
 /* One decode token for every (batch, channel) pair: h and its magnitude H are
  * updated in place, y and m receive the token's output.  Same arithmetic as
  * one iteration of the time loop above. */
-void oracle_step_ex(int64_t Bsz, int64_t D, int64_t N, double* h, double* H, const double* x,
-                    const double* delta, const double* dbias, int flags, const double* A,
-                    const double* Bm, const double* Cm, const double* Dskip, const double* z,
-                    double* y, double* m) {
+void oracle_step_xm(int64_t Bsz, int64_t D, int64_t N, double* h, double* H, const double* x,
+                    const double* xmag, const double* delta, const double* dbias, int flags,
+                    const double* A, const double* Bm, const double* Cm, const double* Dskip,
+                    const double* z, double* y, double* m) {
   const int zoh = (flags & ORACLE_ZOH_EXACT) != 0;
   int64_t pairs = Bsz * D;
 #pragma omp parallel for schedule(static)
@@ -168,8 +183,9 @@ void oracle_step_ex(int64_t Bsz, int64_t D, int64_t N, double* h, double* H, con
     double dsk = Dskip ? Dskip[d] : 0.0;
     double mag;
     double dt = step_of(delta[p], dbias, d, flags);
+    double xm = xmag ? xmag[p] : fabs(x[p]);
     double yt = step_channel(N, h + p * N, H + p * N, A + d * N, dt, x[p], Bm + b * N,
-                             Cm + b * N, 1, dsk, zoh, &mag);
+                             Cm + b * N, 1, dsk, zoh, xm, &mag);
     if (z) {
       double g = silu(z[p]);
       yt *= g;
@@ -180,10 +196,57 @@ void oracle_step_ex(int64_t Bsz, int64_t D, int64_t N, double* h, double* H, con
   }
 }
 
+void oracle_step_ex(int64_t Bsz, int64_t D, int64_t N, double* h, double* H, const double* x,
+                    const double* delta, const double* dbias, int flags, const double* A,
+                    const double* Bm, const double* Cm, const double* Dskip, const double* z,
+                    double* y, double* m) {
+  oracle_step_xm(Bsz, D, N, h, H, x, NULL, delta, dbias, flags, A, Bm, Cm, Dskip, z, y, m);
+}
+
 void oracle_step(int64_t Bsz, int64_t D, int64_t N, double* h, double* H, const double* x,
                  const double* delta, const double* A, const double* Bm, const double* Cm,
                  const double* Dskip, const double* z, double* y, double* m) {
   oracle_step_ex(Bsz, D, N, h, H, x, delta, NULL, 0, A, Bm, Cm, Dskip, z, y, m);
+}
+
+/* ------------------------------------------------------ convolution front --
+ * The guide's Mamba block (§3.5 "Mamba Block") applies a convolution to the
+ * expanded input before the selective SSM, so that tokens are not handled
+ * independently.  The pages give neither its width nor its activation.
+ * Reading: per channel d a causal filter of width K with weights w[d, k]
+ * and a bias, followed by SiLU, the input the scan then takes as x:
+ *   xc_t = bias[d] + sum_{k=0}^{K-1} w[d, k] x_{t-K+1+k},   x'_t = SiLU(xc_t),
+ * where x_s for s < 0 is state[b, d, K-1+s] (the K-1 inputs before the
+ * sequence, oldest first) or 0 when state is NULL.  bias may be NULL (0).
+ * Layouts: x, xo, xm (Bsz, D, L); w (D, K); bias (D); state (Bsz, D, K-1).
+ * xm receives the magnitude the error metric takes for x'_t:
+ *   |x'_t| + |SiLU'(xc_t)| (|bias[d]| + sum_k |w[d, k] x_{t-K+1+k}|),
+ * |x'| plus the first-order effect of a rounding of each term of the
+ * convolution's sum, SiLU'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z).
+ * Returns -1 when K < 1, else 0. */
+int oracle_conv_silu(int64_t Bsz, int64_t D, int64_t L, int64_t K, const double* x,
+                     const double* w, const double* bias, const double* state, double* xo,
+                     double* xm) {
+  if (K < 1) return -1;
+  int64_t pairs = Bsz * D;
+#pragma omp parallel for schedule(static)
+  for (int64_t p = 0; p < pairs; ++p) {
+    int64_t d = p % D;
+    double b0 = bias ? bias[d] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+      double acc = b0, mag = fabs(b0);
+      for (int64_t k = 0; k < K; ++k) {
+        int64_t s = t - (K - 1) + k;  /* token of tap k */
+        double xs = s >= 0 ? x[p * L + s] : (state ? state[p * (K - 1) + (K - 1) + s] : 0.0);
+        acc += w[d * K + k] * xs;
+        mag += fabs(w[d * K + k] * xs);
+      }
+      double sg = 1.0 / (1.0 + exp(-acc));
+      xo[p * L + t] = acc * sg;
+      if (xm) xm[p * L + t] = fabs(acc * sg) + fabs(sg * (1.0 + acc * (1.0 - sg))) * mag;
+    }
+  }
+  return 0;
 }
 
 /* ---------------------------------------------------------------- backward --

@@ -711,9 +711,133 @@ def pin_bwd_options_elementwise_fd(o):
             assert np.all(err < 1e-6), (softplus, key, np.max(err))
 
 
+# ------------------------------------------------------ convolution front --
+def _conv_problem(seed, Bsz=2, D=3, L=30, K=4, bias=True, state=True):
+    g = _rng(seed)
+    return dict(x=g.standard_normal((Bsz, D, L)), w=g.standard_normal((D, K)) * 0.6,
+                bias=g.standard_normal(D) if bias else None,
+                state=g.standard_normal((Bsz, D, K - 1)) if state and K > 1 else None)
+
+
+def pin_conv_hand(o):
+    """The convolution front on a hand-worked channel (tests/golden/
+    conv_hand.txt; §3.5 "Mamba Block"): taps, their order, the bias and the
+    inputs taken from the state before the sequence."""
+    g = _read_golden("conv_hand.txt")
+    x = np.array(g["x"])[None, None, :]
+    w = np.array(g["w"])[None, :]
+    bias = np.array(g["bias"])
+    state = np.array(g["state"])[None, None, :]
+    for key, st in (("xc_state", state), ("xc_nostate", None)):
+        xo, _ = o.conv_silu(x, w, bias, st)
+        want = _silu(np.array(g[key]))
+        assert np.allclose(xo[0, 0], want, rtol=1e-15, atol=0), (key, xo[0, 0], want)
+
+
+def pin_conv_numpy(o):
+    """Against numpy's convolution (a library routine): x' = SiLU(bias +
+    (x_ext * reversed w)), x_ext = state ++ x, every width 1..4, with and
+    without bias and state."""
+    for K in (1, 2, 3, 4):
+        for seed, kw in ((90 + K, dict(bias=True, state=True)), (95 + K, dict(bias=False, state=False))):
+            p = _conv_problem(seed, K=K, **kw)
+            xo, _ = o.conv_silu(**p)
+            Bsz, D, L = p["x"].shape
+            st = p["state"] if p["state"] is not None else np.zeros((Bsz, D, K - 1))
+            full = np.concatenate([st, p["x"]], axis=-1)
+            for b in range(Bsz):
+                for d in range(D):
+                    c = np.convolve(full[b, d], p["w"][d][::-1], mode="valid")
+                    if p["bias"] is not None:
+                        c = c + p["bias"][d]
+                    assert np.allclose(xo[b, d], _silu(c), rtol=1e-13, atol=1e-15), (K, b, d)
+
+
+def pin_conv_split_resume(o):
+    """A sequence cut in two: the second part with the last K-1 inputs of
+    the first as its state gives the same output as the whole sequence."""
+    p = _conv_problem(101, L=37, K=4)
+    whole, _ = o.conv_silu(**p)
+    for cut in (1, 2, 3, 17):
+        a, _ = o.conv_silu(p["x"][..., :cut], p["w"], p["bias"], p["state"])
+        ext = np.concatenate([p["state"], p["x"][..., :cut]], axis=-1)[..., -3:]
+        b, _ = o.conv_silu(p["x"][..., cut:], p["w"], p["bias"], ext)
+        assert np.allclose(np.concatenate([a, b], axis=-1), whole, rtol=0, atol=0), cut
+
+
+def pin_conv_magnitude(o):
+    """xm bounds the first-order effect of relative perturbations of size
+    eps of every term of the convolution's sum (and of x' itself), and is
+    >= |x'|; the scan's magnitude is linear in the x magnitudes it is given
+    (with no initial state), so doubling xmag doubles m."""
+    p = _conv_problem(111, Bsz=1, D=2, L=25, K=4)
+    xo, xm = o.conv_silu(**p)
+    assert np.all(xm >= np.abs(xo))
+    g = _rng(112)
+    eps = 1e-7
+    K = p["w"].shape[1]
+    full = np.concatenate([p["state"], p["x"]], axis=-1)
+    worst = 0.0
+    for trial in range(20):
+        for d in range(2):
+            for t in range(25):
+                terms = p["w"][d] * full[0, d, t:t + K]
+                pert = np.concatenate([[p["bias"][d]], terms])
+                pert = pert * (1 + eps * g.choice([-1.0, 1.0], size=pert.size))
+                c = pert.sum()
+                dev = abs(_silu(c) * (1 + eps * g.choice([-1.0, 1.0])) - xo[0, d, t])
+                worst = max(worst, dev / (eps * xm[0, d, t]))
+    assert worst <= 1.0 + 1e-3, worst
+    # tight somewhere: the bound is not loose by a large factor everywhere
+    assert worst >= 0.2, worst
+    q = _rand_problem(113, Bsz=1, D=2, L=20, N=3, h0=False)
+    r1 = o.scan(**q)
+    r2 = o.scan(**q, xmag=2 * np.abs(q["x"]))
+    assert np.allclose(r2["m"], 2 * r1["m"], rtol=1e-14, atol=0)
+    assert np.array_equal(r2["y"], r1["y"])
+
+
+def _mp_conv_silu(p, dps=50):
+    import mpmath as mp
+    mp.mp.dps = dps
+    x, w = p["x"], p["w"]
+    Bsz, D, L = x.shape
+    K = w.shape[1]
+    out = np.zeros(x.shape)
+    for b in range(Bsz):
+        for d in range(D):
+            for t in range(L):
+                acc = mp.mpf(float(p["bias"][d])) if p["bias"] is not None else mp.mpf(0)
+                for k in range(K):
+                    s = t - (K - 1) + k
+                    if s >= 0:
+                        xs = float(x[b, d, s])
+                    elif p["state"] is not None:
+                        xs = float(p["state"][b, d, K - 1 + s])
+                    else:
+                        xs = 0.0
+                    acc += mp.mpf(float(w[d, k])) * mp.mpf(xs)
+                out[b, d, t] = float(acc / (1 + mp.exp(-acc)))
+    return out
+
+
+def pin_conv_scan_brute_force(o):
+    """The scan of the convolution front's output against the 50-digit
+    materialised form fed with a 50-digit convolution front."""
+    p = _rand_problem(121, Bsz=1, D=2, L=16, N=3)
+    c = _conv_problem(122, Bsz=1, D=2, L=16, K=4)
+    xo, xm = o.conv_silu(**c)
+    r = o.scan(**dict(p, x=xo), xmag=xm)
+    want = brute_force_y(dict(p, x=_mp_conv_silu(c)))
+    err = np.max(np.abs(r["y"] - want) / r["m"])
+    assert err < 1e-13, err
+
+
 PINS = [pin_zero_step_hand, pin_scalar_hand, pin_lti_convolution, pin_step_response,
         pin_brute_force, pin_tree_scan, pin_split_resume, pin_linearity_and_permutation,
         pin_gate_limits, pin_decode_equals_scan, pin_magnitude_bounds, pin_softplus_hand,
         pin_softplus_limits, pin_zoh_hand, pin_zoh_limits, pin_options_brute_force,
         pin_bwd_directional_brute_force, pin_bwd_elementwise_fd, pin_bwd_linear_in_cotangent,
-        pin_bwd_no_input_coupling, pin_bwd_options_directional_brute_force, pin_bwd_options_elementwise_fd]
+        pin_bwd_no_input_coupling, pin_bwd_options_directional_brute_force, pin_bwd_options_elementwise_fd,
+        pin_conv_hand, pin_conv_numpy, pin_conv_split_resume, pin_conv_magnitude,
+        pin_conv_scan_brute_force]

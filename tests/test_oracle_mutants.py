@@ -21,7 +21,7 @@ MUTANTS = [
         ("acc += Ct[n * bstride] * h[n];      /* ... then read the output from the new state */",
          "acc += Ct[n * bstride] * hp_;")]),
     ("B_C_swapped", [
-        ("* Bt[n * bstride] * xt;", "* Ct[n * bstride] * xt;"),
+        ("* Bt[n * bstride];", "* Ct[n * bstride];"),
         ("acc += Ct[n * bstride] * h[n];      /*", "acc += Bt[n * bstride] * h[n];      /*")]),
     ("exp_sign", [("double a = exp(dt * Ad[n]);         /*", "double a = exp(-dt * Ad[n]);         /*")]),
     ("dt_dropped_from_input", [("(zoh ? zoh_coef(dt, Ad[n]) : dt) * Bt",
@@ -75,7 +75,18 @@ MUTANTS = [
                              "double dsk = Dskip ? Dskip[0] : 0.0;\n    for (int64_t t")]),
     ("sigmoid_sign", [("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));")]),
     ("input_decayed_same_step", [("h[n] = a * h[n] + bx;", "h[n] = a * (h[n] + bx);")]),
-    ("magnitude_drops_input", [("H[n] = fabs(a) * H[n] + fabs(bx);", "H[n] = fabs(a) * H[n];")]),
+    ("magnitude_drops_input", [("H[n] = fabs(a) * H[n] + fabs(cb) * xm;", "H[n] = fabs(a) * H[n];")]),
+    # convolution front
+    ("conv_tap_shift", [("int64_t s = t - (K - 1) + k;", "int64_t s = t - K + k;")]),
+    ("conv_taps_reversed", [("acc += w[d * K + k] * xs;", "acc += w[d * K + (K - 1 - k)] * xs;")]),
+    ("conv_weight_channel", [("acc += w[d * K + k] * xs;", "acc += w[k] * xs;")]),
+    ("conv_state_ignored", [("(state ? state[p * (K - 1) + (K - 1) + s] : 0.0)", "0.0")]),
+    ("conv_state_order", [("state[p * (K - 1) + (K - 1) + s]", "state[p * (K - 1) - 1 - s]")]),
+    ("conv_bias_dropped", [("double b0 = bias ? bias[d] : 0.0;", "double b0 = 0.0;")]),
+    ("conv_no_silu", [("xo[p * L + t] = acc * sg;", "xo[p * L + t] = acc;")]),
+    ("scan_xmag_ignored", [("double xm = xmag ? xmag[p * L + t] : fabs(x[p * L + t]);",
+                           "double xm = fabs(x[p * L + t]);")]),
+    ("conv_magnitude_no_sum", [("fabs(sg * (1.0 + acc * (1.0 - sg))) * mag;", "0.0 * mag;")]),
 ]
 
 
