@@ -77,13 +77,15 @@ def scan_bytes(w, in_bytes, h0=False, h_last=True):
     return b
 
 
-def scan_valu_slots(w, skip=True):
+def scan_valu_slots(w, skip=True, conv_k=0):
     """Algorithmic VALU lane-slots of one scan: per (token, channel, state)
     the exponent argument (1), the exponential (2), the input term (1), the
     state update (1) and the output term (1); per (token, channel) delta*x
     (1), the skip term (1) and the SiLU gate (z*log2 e, exp, add, rcp, two
-    products: 8)."""
-    per = 6 * w.dstate + 1 + (1 if skip else 0) + (8 if w.gate else 0)
+    products: 8).  With the convolution front of width conv_k, per (token,
+    channel) its conv_k multiply-adds and SiLU (x*log2 e, exp, add, rcp,
+    product: 7)."""
+    per = 6 * w.dstate + 1 + (1 if skip else 0) + (8 if w.gate else 0) + ((conv_k + 7) if conv_k else 0)
     return w.batch * w.dim * w.seqlen * per
 
 
@@ -150,12 +152,14 @@ def decode_step_bytes(batch, dim, N, in_bytes, gate=True):
     return batch * dim * per + 2 * batch * N * in_bytes + 4 * dim * N + 4 * dim
 
 
-def bench_scan(w, steps, warmup, flush=False, softplus=False, zoh=False):
+def bench_scan(w, steps, warmup, flush=False, softplus=False, zoh=False, conv_k=0):
     """Times `steps` scans of workload w (after `warmup`).  flush: before each
     timed scan, write a 512 MiB buffer so that no input is cache-resident,
     and time each scan on its own.  softplus / zoh: time the option kernels
     (the stored delta is then the softplus argument, with a bias of -4 per
-    channel; the timing does not depend on the values)."""
+    channel; the timing does not depend on the values).  conv_k: the scan
+    with the convolution front of that width (synth.conv_params filter and
+    bias, no state)."""
     import torch
     from selective_state_space_63_amd import s6, synth
     inp = synth.device_full(w)
@@ -168,9 +172,17 @@ def bench_scan(w, steps, warmup, flush=False, softplus=False, zoh=False):
         opts = dict(delta_bias=torch.full((w.dim,), -4.0, device="cuda", dtype=torch.float32) if softplus else None,
                     delta_softplus=softplus, zoh=zoh)
 
-    def step():
-        s6.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], D=inp["Dskip"], z=inp["z"],
-                    return_last_state=True, y=y, h_last=hl, **opts)
+    if conv_k:
+        cw, cb = synth.conv_params(w.dim, conv_k, w.seed)
+        cw, cb = torch.from_numpy(cw).cuda(), torch.from_numpy(cb).cuda()
+
+        def step():
+            s6.conv_scan_fwd(inp["x"], cw, inp["delta"], inp["A"], inp["Bm"], inp["Cm"], conv_bias=cb,
+                             D=inp["Dskip"], z=inp["z"], return_last_state=True, y=y, h_last=hl, **opts)
+    else:
+        def step():
+            s6.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], D=inp["Dskip"], z=inp["z"],
+                        return_last_state=True, y=y, h_last=hl, **opts)
 
     for _ in range(warmup):
         step()
@@ -222,14 +234,14 @@ def bench_scan_flushed(w, inp, steps, warmup):
     return {"mean": sum(per) / len(per), "median": per[len(per) // 2], "min": per[0]}
 
 
-def scan_line(name, w, tm, in_bytes, note, h_last):
+def scan_line(name, w, tm, in_bytes, note, h_last, conv_k=0):
     byts = scan_bytes(w, in_bytes, h_last=h_last)
     ms = tm["mean"]
     gbs = byts / (ms * 1e-3) / 1e9
     return {"workload": w.name, "ms_mean": round(ms, 4), "ms_median": round(tm["median"], 4),
             "ms_min": round(tm["min"], 4), "GBps": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "token_channels_per_s": w.batch * w.dim * w.seqlen / (ms * 1e-3),
-            "valu_frac": round(scan_valu_slots(w) / (ms * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4),
+            "valu_frac": round(scan_valu_slots(w, conv_k=conv_k) / (ms * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4),
             "note": note}
 
 
@@ -437,6 +449,33 @@ def cpu_options_baseline(w, inp, budget_s=3.0):
             "sample": f"{rows} batch rows ({w.dim} channels x {w.seqlen} tokens each), {spent:.2f} s"}
 
 
+def cpu_conv_baseline(w, inp, conv_k, budget_s=3.0):
+    """The oracle's convolution front and scan on whole batch rows of the
+    same inputs until `budget_s` is spent."""
+    import numpy as np
+    import torch
+    from oracle.oracle import Oracle
+    from selective_state_space_63_amd import synth
+    o = Oracle()
+
+    def h64(t):
+        return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+    A, Dk = h64(inp["A"]), h64(inp["Dskip"])
+    cw, cb = synth.conv_params(w.dim, conv_k, w.seed)
+    spent, rows = 0.0, 0
+    while spent < budget_s or rows == 0:
+        b = rows % w.batch
+        t0 = time.perf_counter()
+        xo, xm = o.conv_silu(h64(inp["x"][b:b + 1]), cw, cb)
+        o.scan(x=xo, delta=h64(inp["delta"][b:b + 1]), A=A, Bm=h64(inp["Bm"][b:b + 1]), Cm=h64(inp["Cm"][b:b + 1]),
+               Dskip=Dk, z=h64(inp["z"][b:b + 1]), xmag=xm)
+        spent += time.perf_counter() - t0
+        rows += 1
+    return {"token_channels_per_s": rows * w.dim * w.seqlen / spent, "cores": o.num_threads(), "kind": "oracle",
+            "sample": f"{rows} batch rows ({w.dim} channels x {w.seqlen} tokens each), {spent:.2f} s"}
+
+
 def cpu_decode_baseline(w, budget_s=3.0):
     """The oracle's single-token step (fp64) on the decode workload's shape,
     repeated until `budget_s` is spent: state-element updates per second."""
@@ -598,6 +637,11 @@ def main():
         out["softplus_zoh"] = scan_line("softplus_zoh", w, tz, in_bytes,
                                         "softplus step and exact zero-order-hold input term", True)
         torch.cuda.empty_cache()
+        print(f"[bench] scan {w.name} with the convolution front", file=sys.stderr, flush=True)
+        _, tcv, _ = bench_scan(w, 50, 50, conv_k=4)
+        out["conv"] = scan_line("conv", w, tcv, in_bytes, "convolution front (width 4, bias, SiLU) fused into the "
+                                "staging of x; the filtered input is never written", True, conv_k=4)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inp)
@@ -607,6 +651,8 @@ def main():
             out["backward"]["cpu_baseline"] = cpu_backward_baseline(w, inp)
         if "softplus_zoh" in out:
             out["softplus_zoh"]["cpu_baseline"] = cpu_options_baseline(w, inp)
+        if "conv" in out:
+            out["conv"]["cpu_baseline"] = cpu_conv_baseline(w, inp, 4)
     print(json.dumps(out), flush=True)
 
 

@@ -72,7 +72,7 @@ extern "C" {
 #define S6_ERR_NULL (-1)        /* a required pointer is NULL */
 #define S6_ERR_SHAPE (-2)       /* a size is negative or the element count overflows */
 #define S6_ERR_DTYPE (-3)       /* in_dtype is not S6_F32 or S6_BF16 */
-#define S6_ERR_UNSUPPORTED (-4) /* dstate outside 1..32, or an option the entry point lacks */
+#define S6_ERR_UNSUPPORTED (-4) /* dstate outside 1..32, a filter width outside 1..4, or an option the entry point lacks */
 #define S6_ERR_ALIGN (-5)       /* a pointer is not aligned to its element size */
 #define S6_ERR_HIP (-6)         /* a HIP call failed; s6_status_str gives the detail */
 #define S6_ERR_FLAGS (-7)       /* unknown bits in the flags of an _ex entry point */
@@ -147,6 +147,44 @@ int s6_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, int in_dtype,
                        const void* x, const void* delta, const float* delta_bias, int flags,
                        const float* A, const void* Bm, const void* Cm, const float* Dskip,
                        const void* z, float* y, void* stream);
+
+/* The scan with the convolution front of the Mamba block.  §3.5 of the
+ * guide ("Mamba Block") applies a convolution to the expanded input before
+ * the selective SSM, so that tokens are not handled independently; it gives
+ * neither the width nor an activation.  Here: per channel a causal filter of
+ * conv_width taps and a bias, then SiLU, and the scan (with its skip term)
+ * takes the result as its input x:
+ *   x'[b,d,t] = SiLU(conv_bias[d] + sum_{k<K} conv_w[d,k] * x[b,d,t-K+1+k]),
+ * K = conv_width, where inputs before token 0 are conv_state[b,d,K-1+s] for
+ * s = -(K-1) .. -1 (oldest first), or 0 when conv_state is NULL.  The
+ * filtered input is computed in fp32 as x is staged and never written.
+ *   conv_w     : required (dim, conv_width) fp32.  conv_width: 1..4, else
+ *                S6_ERR_UNSUPPORTED.
+ *   conv_bias  : nullable (dim) fp32.   conv_state : nullable (batch, dim,
+ *                conv_width - 1) fp32.  All three 4-byte aligned.
+ * The last conv_width - 1 inputs of a sequence (the state of its
+ * continuation) are x itself: the caller keeps them.  Everything else is as
+ * for s6_scan_fwd_ex (step bias, S6_DELTA_SOFTPLUS, S6_ZOH_EXACT). */
+int s6_conv_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                     const void* x, const float* conv_w, const float* conv_bias, int conv_width,
+                     const float* conv_state, const void* delta, const float* delta_bias, int flags,
+                     const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                     const float* h0, float* y, float* h_last, void* stream);
+
+/* One decode token with the convolution front of s6_conv_scan_fwd: the
+ * filter runs over the conv_width - 1 kept inputs and this token's x, the
+ * scan step takes SiLU of the result as its input, and the kept inputs move
+ * on by one (the oldest dropped, x appended):
+ *   conv_state : (batch, dim, conv_width - 1) fp32, in/out, oldest first;
+ *                required when conv_width > 1.
+ * A sequence scanned by s6_conv_scan_fwd continues here with conv_state =
+ * its last conv_width - 1 inputs and h = its h_last.  Everything else is as
+ * for s6_state_update_ex. */
+int s6_conv_state_update(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, float* h,
+                         float* conv_state, const void* x, const float* conv_w, const float* conv_bias,
+                         int conv_width, const void* delta, const float* delta_bias, int flags,
+                         const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                         const void* z, float* y, void* stream);
 
 /* Gradients of the scan (reverse mode) for the loss <dy, y> + <dh_last,
  * h_last>, plain step (no options), same inputs as s6_scan_fwd.  The guide's

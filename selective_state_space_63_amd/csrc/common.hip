@@ -65,7 +65,7 @@ using namespace s6i;
 
 extern "C" {
 
-int s6_version(void) { return 10100; }
+int s6_version(void) { return 10200; }
 
 const char* s6_status_str(int status) {
   switch (status) {
@@ -73,7 +73,7 @@ const char* s6_status_str(int status) {
     case S6_ERR_NULL: return "a required pointer is NULL";
     case S6_ERR_SHAPE: return "invalid size (negative, or the element count overflows)";
     case S6_ERR_DTYPE: return "in_dtype must be S6_F32 or S6_BF16";
-    case S6_ERR_UNSUPPORTED: return "unsupported: dstate outside 1..32, or an option this entry point lacks";
+    case S6_ERR_UNSUPPORTED: return "unsupported: dstate outside 1..32, filter width outside 1..4, or an option this entry point lacks";
     case S6_ERR_ALIGN: return "a pointer is not aligned to its element size";
     case S6_ERR_FLAGS: return "unknown option bits in flags";
     case S6_ERR_HIP: return g_err[0] ? g_err : "HIP error";

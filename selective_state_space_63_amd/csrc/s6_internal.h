@@ -32,6 +32,7 @@ constexpr int kCW = 32;            // channels per workgroup
 constexpr int kT = 16;             // tokens per chunk
 constexpr int kP = kT;             // LDS tile pitch in floats (channel-major [c][t], swizzled)
 constexpr int kMaxN = 32;          // largest dstate supported
+constexpr int kMaxConv = 4;        // widest filter of the convolution front
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
@@ -113,6 +114,12 @@ struct ScanArgs {
   int softplus;           // step = softplus(delta + dbias[d])  (option kernels only; the
                           // bias alone is added without it)
   int zoh;                // exact zero-order-hold input coefficient (option kernels only)
+  const float* conv_w;    // (D, conv_k) causal filter of the convolution front, or null
+                          // (option kernels only; x is then SiLU(conv_b + filter * x))
+  const float* conv_b;    // (D) its bias, or null (zero)
+  const float* conv_state;  // (batch, D, conv_k - 1) inputs before token 0, oldest first,
+                            // or null (zero)
+  int conv_k;             // filter width, 1..kMaxConv
   int64_t D, L, N;
   int64_t seg_len;        // tokens per segment (multiple of 4 kT); segment = blockIdx.z
   int64_t hinit_stride;   // elements between segments in hinit (0: same for all)

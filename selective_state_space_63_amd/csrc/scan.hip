@@ -30,6 +30,12 @@
 //  * Chunks past the end of a sequence are staged as delta = 0 (the state
 //    stays exactly unchanged) and store nothing, so the loop body has no
 //    conditional memory operations.
+//  * The convolution front (option kernels): the threads that stage x
+//    pieces replace them by SiLU(bias + causal filter * x) before writing
+//    the tile, so the scan, the skip term and the state-only passes all see
+//    the filtered input and it never goes to memory.  The three inputs
+//    before a piece come from the neighbouring lane's piece (DPP), or from
+//    the previous chunk's last piece, which its lane keeps in registers.
 //  * Few long rows (too few workgroups to fill the GPU) are cut into
 //    segments along L: pass 1 computes every segment's end state from zero
 //    and its summed delta, a tiny pass folds them into each segment's
@@ -213,7 +219,8 @@ __device__ __forceinline__ void token_group(const float* dl, const float* xv, co
 //
 // EXT kernels also take the step bias and discretisation options of ScanArgs:
 // the bias and softplus are applied to delta while it is staged (once per
-// element), the exact hold in the token groups, and the
+// element), the convolution front to x the same way, the exact hold in the
+// token groups, and the
 // kind of piece each wave stages rotates with the workgroup index so that
 // this extra work falls on every SIMD alike.
 template <typename In, int VEC, bool GATE, int MODE, int W, int WIN, bool EXT>
@@ -329,6 +336,40 @@ s6_scan_kernel(ScanArgs a) {
     if (idle) skind[s] = -1;
   }
 
+  // Convolution front: per slot the filter taps newest first (cwr[j] weighs
+  // the input j tokens back; taps past the width are 0), the bias, and the
+  // inputs carried over from the previous chunk: elements VEC-3 .. VEC-1 of
+  // this lane's piece (only the last piece of a row passes them on), or the
+  // single element (VEC == 1).  Before the segment's first chunk they are
+  // the inputs before it: x itself, or conv_state / 0 before token 0.
+  const bool conv = EXT && a.conv_w != nullptr;
+  constexpr int NCAR = VEC == 1 ? 1 : 3;
+  float cwr[SLOTS][kMaxConv], cbias[SLOTS], carry[SLOTS][NCAR];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+#pragma unroll
+    for (int j = 0; j < kMaxConv; ++j) cwr[s][j] = 0.0f;
+    cbias[s] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NCAR; ++j) carry[s][j] = 0.0f;
+    if (conv && skind[s] == 0) {
+      const int K = a.conv_k;
+      const int64_t rowc = srow[s] < rows_valid ? srow[s] : rows_valid - 1;
+      const int64_t ch = d0 + rowc;
+      for (int j = 0; j < K; ++j) cwr[s][j] = a.conv_w[ch * K + (K - 1 - j)];
+      if (a.conv_b) cbias[s] = a.conv_b[ch];
+#pragma unroll
+      for (int j = 0; j < NCAR; ++j) {
+        const int64_t u = tb - kT + scol[s] + (VEC == 1 ? 0 : VEC - 3 + j);  // token of the carried input
+        if (u >= 0) {
+          carry[s][j] = to_f32(sptr[s][u - scol[s]]);
+        } else if (a.conv_state && u >= -(int64_t)(K - 1)) {
+          carry[s][j] = a.conv_state[(b * D + ch) * (K - 1) + (K - 1) + u];
+        }
+      }
+    }
+  }
+
   // B/C slots of states >= N are never written: clear both buffers once.
   if (N < 4 * W) {
     for (int i = tid; i < 2 * BCL::kFloats; i += NTHR) bcs[i] = 0.0f;
@@ -373,9 +414,50 @@ s6_scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
       const int col = scol[s];
+      const In* e = reinterpret_cast<const In*>(&src_[s]);
+      // Convolution front (all lanes take part in the exchange; x lanes use it).
+      float xf[VEC];
+      if (conv) {
+        float cur[VEC], prev[3];  // prev[i]: the input 3 - i tokens before the piece
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) cur[k] = to_f32(e[k]);
+        if constexpr (VEC == 1) {
+          // the 16 pieces of a row are the 16 lanes of a DPP row: lane q
+          // reads lane q - i (rotating; lanes 16 - i .. 15 send the previous
+          // chunk's element)
+          const int q = lane & 15;
+          prev[2] = dpp_f<0x121>(q >= 15 ? carry[s][0] : cur[0]);
+          prev[1] = dpp_f<0x122>(q >= 14 ? carry[s][0] : cur[0]);
+          prev[0] = dpp_f<0x123>(q >= 13 ? carry[s][0] : cur[0]);
+          carry[s][0] = cur[0];
+        } else {
+          // the PPC pieces of a row sit in PPC adjacent lanes; piece q reads
+          // piece q - 1, the first piece the last one (which sends the
+          // previous chunk's inputs)
+          static_assert(CP::PPC == 2 || CP::PPC == 4, "pieces per row");
+          constexpr int CTRL = CP::PPC == 2 ? 0xB1 : 0x93;  // quad_perm [1,0,3,2] / [3,0,1,2]
+          const bool lastp = col == (CP::PPC - 1) * VEC;
+#pragma unroll
+          for (int j = 0; j < 3; ++j) {
+            prev[j] = dpp_f<CTRL>(lastp ? carry[s][j] : cur[VEC - 3 + j]);
+            carry[s][j] = cur[VEC - 3 + j];
+          }
+        }
+        if (skind[s] == 0) {
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) {
+            float acc = cbias[s];
+#pragma unroll
+            for (int j = 0; j < kMaxConv; ++j) {
+              const float v = k - j >= 0 ? cur[k - j] : prev[3 + k - j];
+              acc = __builtin_fmaf(cwr[s][j], v, acc);
+            }
+            xf[k] = silu(acc);
+          }
+        }
+      }
       if (skind[s] < 0) continue;
       const bool ok = !MASK || t0c + col < te;
-      const In* e = reinterpret_cast<const In*>(&src_[s]);
       if (dstep && skind[s] == 1) {
         // step = delta + bias, then softplus if asked; masked tokens stay 0
         float* tile = tiles + (buf * 2 + 1) * TILE;
@@ -393,6 +475,16 @@ s6_scan_kernel(ScanArgs a) {
           for (int k = 0; k < VEC; k += 4)
             *reinterpret_cast<float4*>(tile + tsw(srow[s], (col + k) >> 2)) =
                 ok ? make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      } else if (conv && skind[s] == 0) {
+        float* tile = tiles + buf * 2 * TILE;
+        if constexpr (VEC == 1) {
+          tile[tsw(srow[s], col >> 2) + (col & 3)] = ok ? xf[0] : 0.0f;
+        } else {
+#pragma unroll
+          for (int k = 0; k < VEC; k += 4)
+            *reinterpret_cast<float4*>(tile + tsw(srow[s], (col + k) >> 2)) =
+                ok ? make_float4(xf[k], xf[k + 1], xf[k + 2], xf[k + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
       } else if (skind[s] < 2) {
         float* tile = tiles + (buf * 2 + skind[s]) * TILE;
@@ -695,11 +787,11 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, size_
   return p;
 }
 
-// Kernels with the discretisation options only when an option is set, so
-// the plain path keeps its own code.
+// Kernels with the discretisation options and the convolution front only
+// when one is set, so the plain path keeps its own code.
 int launch_scan_any(int in_dtype, int mode, const ScanArgs& a, const Plan& p, bool gate, int64_t batch,
                     int64_t segs, hipStream_t st) {
-  if (a.softplus || a.zoh || a.dbias) return launch_scan_e<true>(in_dtype, mode, a, p, gate, batch, segs, st);
+  if (a.softplus || a.zoh || a.dbias || a.conv_w) return launch_scan_e<true>(in_dtype, mode, a, p, gate, batch, segs, st);
   return launch_scan_e<false>(in_dtype, mode, a, p, gate, batch, segs, st);
 }
 
@@ -724,15 +816,32 @@ int launch_copy_state(const float* src, float* dst, int64_t n, hipStream_t st) {
 
 namespace {
 
-// Shared implementation of s6_scan_fwd(_ex) (want_y) and s6_last_state(_ex).
+// The convolution front of s6_conv_scan_fwd: filter (D, width), bias,
+// state before token 0; all null for the plain scan.
+struct ConvFront {
+  const float* w = nullptr;
+  const float* bias = nullptr;
+  const float* state = nullptr;
+  int width = 0;
+};
+
+// Shared implementation of s6_scan_fwd(_ex), s6_conv_scan_fwd (want_y) and
+// s6_last_state(_ex).
 int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
               const void* x, const void* delta, const float* dbias, int flags, const float* A,
               const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
-              float* y, float* h_last, void* stream) {
+              float* y, float* h_last, void* stream, const ConvFront& cf = ConvFront()) {
   int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
   if (rc) return rc;
   if (flags & ~(S6_DELTA_SOFTPLUS | S6_ZOH_EXACT)) return S6_ERR_FLAGS;
   if (dbias && !aligned(dbias, 4)) return S6_ERR_ALIGN;
+  if (cf.w || cf.width) {
+    if (cf.width < 1 || cf.width > kMaxConv) return S6_ERR_UNSUPPORTED;
+    if (!cf.w) return S6_ERR_NULL;
+    const void* cps[] = {cf.w, cf.bias, cf.state};
+    for (const void* p : cps)
+      if (p && !aligned(p, 4)) return S6_ERR_ALIGN;
+  }
   const bool work = batch > 0 && dim > 0 && seqlen > 0;
   if (work && (!x || !delta || !A || !Bm || (want_y && (!Cm || !y)))) return S6_ERR_NULL;
   if (!want_y && !h_last) return S6_ERR_NULL;
@@ -769,6 +878,7 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
   a.softplus = (flags & S6_DELTA_SOFTPLUS) != 0;
   a.zoh = (flags & S6_ZOH_EXACT) != 0;
   a.dbias = dbias;
+  a.conv_w = cf.w; a.conv_b = cf.bias; a.conv_state = cf.state; a.conv_k = cf.width;
   a.D = dim; a.L = seqlen; a.N = dstate; a.seg_len = p.seg_len;
 
   if (S == 1) {
@@ -844,6 +954,21 @@ int s6_scan_fwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, i
                    const float* h0, float* y, float* h_last, void* stream) {
   return scan_impl(true, batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm,
                    Dskip, z, h0, y, h_last, stream);
+}
+
+int s6_conv_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                     const void* x, const float* conv_w, const float* conv_bias, int conv_width,
+                     const float* conv_state, const void* delta, const float* delta_bias, int flags,
+                     const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                     const float* h0, float* y, float* h_last, void* stream) {
+  ConvFront cf;
+  cf.w = conv_w;
+  cf.bias = conv_bias;
+  cf.state = conv_state;
+  cf.width = conv_width;
+  if (!conv_w && conv_width == 0) return S6_ERR_NULL;
+  return scan_impl(true, batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm,
+                   Dskip, z, h0, y, h_last, stream, cf);
 }
 
 int s6_last_state(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,

@@ -6,6 +6,9 @@
 // with all their loads issued first; h, A, B, C read and h written with
 // 8/16-byte accesses that are contiguous across the lanes of a wave.  The
 // step is HBM-bound (or Infinity-Cache-bound when the state fits there).
+// s6_conv_state_update also runs the convolution front on the token: the
+// filter over the kept inputs and the new one, then SiLU, and shifts the
+// kept inputs by one.
 #include "s6_internal.h"
 
 namespace s6i {
@@ -25,6 +28,10 @@ struct StepArgs {
   const float* dbias;  // (D) step bias or null
   int softplus;        // step = softplus(delta + dbias[d])
   int zoh;             // exact zero-order-hold input coefficient
+  const float* conv_w; // (D, conv_k) filter of the convolution front, or null
+  const float* conv_b; // (D) its bias, or null
+  float* conv_state;   // (batch, D, conv_k - 1) last inputs, oldest first; in/out
+  int conv_k;
   int64_t batch, D, N;
 };
 
@@ -129,6 +136,26 @@ __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
         Cv[j] = sv ? to_f32(Cp[bb * N + n0 + j]) : 0.0f;
       }
     }
+    // convolution front: the filter over the kept inputs and this token's,
+    // then SiLU; the first lane of the channel shifts the kept inputs (every
+    // lane's loads of them complete before, as the filter consumes them)
+    if (EXT && a.conv_w) {
+      const int K = a.conv_k;
+      const float* cw = a.conv_w + d * K;
+      float* cs = a.conv_state + ch * (K - 1);
+      float keep[kMaxConv];
+      float acc = (a.conv_b && valid) ? a.conv_b[d] : 0.0f;
+      for (int k = 0; k < K - 1; ++k) {
+        keep[k] = cs[k];
+        acc = __builtin_fmaf(cw[k], keep[k], acc);
+      }
+      acc = __builtin_fmaf(cw[K - 1], xt[g], acc);
+      if (vb[g] && q == 0 && K > 1) {
+        for (int k = 0; k + 1 < K - 1; ++k) cs[k] = keep[k + 1];
+        cs[K - 2] = xt[g];
+      }
+      xt[g] = silu(acc);
+    }
     // the step: delta, plus the channel's bias, through softplus if asked
     float dl = dt[g];
     if (EXT && a.dbias) dl += dbias;
@@ -197,7 +224,7 @@ int launch_step_t(const StepArgs& a, bool vec, hipStream_t st) {
 // Kernels with the step options only when an option is set.
 template <typename In, bool GATE, int P, int SPL, int G>
 int launch_step_e(const StepArgs& a, bool vec, hipStream_t st) {
-  if (a.dbias || a.softplus || a.zoh) return launch_step_t<In, GATE, P, SPL, G, true>(a, vec, st);
+  if (a.dbias || a.softplus || a.zoh || a.conv_w) return launch_step_t<In, GATE, P, SPL, G, true>(a, vec, st);
   return launch_step_t<In, GATE, P, SPL, G, false>(a, vec, st);
 }
 
@@ -231,15 +258,23 @@ int launch_step_g(const StepArgs& a, hipStream_t st) {
 
 using namespace s6i;
 
-extern "C" {
+namespace {
 
-int s6_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, float* h,
-                       const void* x, const void* delta, const float* delta_bias, int flags,
-                       const float* A, const void* Bm, const void* Cm, const float* Dskip,
-                       const void* z, float* y, void* stream) {
+int state_update_impl(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, float* h,
+                      const void* x, const void* delta, const float* delta_bias, int flags,
+                      const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                      const void* z, float* y, void* stream, const float* conv_w = nullptr,
+                      const float* conv_b = nullptr, float* conv_state = nullptr, int conv_k = 0) {
   int rc = check_common(batch, dim, 1, dstate, in_dtype);
   if (rc) return rc;
   if (flags & ~(S6_DELTA_SOFTPLUS | S6_ZOH_EXACT)) return S6_ERR_FLAGS;
+  if (conv_w || conv_k) {
+    if (conv_k < 1 || conv_k > kMaxConv) return S6_ERR_UNSUPPORTED;
+    if (!conv_w || (conv_k > 1 && !conv_state)) return S6_ERR_NULL;
+    const void* cps[] = {conv_w, conv_b, conv_state};
+    for (const void* p : cps)
+      if (p && !aligned(p, 4)) return S6_ERR_ALIGN;
+  }
   // one thread per (batch, channel, 4 states) at most: the grid must fit
   if (batch * dim > (int64_t)INT32_MAX * 256 / 8) return S6_ERR_SHAPE;
   if (batch == 0 || dim == 0) return S6_OK;
@@ -256,11 +291,34 @@ int s6_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, int in_dtype,
   a.dbias = delta_bias;
   a.softplus = (flags & S6_DELTA_SOFTPLUS) != 0;
   a.zoh = (flags & S6_ZOH_EXACT) != 0;
+  a.conv_w = conv_w; a.conv_b = conv_b; a.conv_state = conv_state; a.conv_k = conv_k;
   a.batch = batch; a.D = dim; a.N = dstate;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_dtype == S6_BF16)
     return z ? launch_step_g<uint16_t, true>(a, st) : launch_step_g<uint16_t, false>(a, st);
   return z ? launch_step_g<float, true>(a, st) : launch_step_g<float, false>(a, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int s6_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, float* h,
+                       const void* x, const void* delta, const float* delta_bias, int flags,
+                       const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                       const void* z, float* y, void* stream) {
+  return state_update_impl(batch, dim, dstate, in_dtype, h, x, delta, delta_bias, flags, A, Bm, Cm, Dskip,
+                           z, y, stream);
+}
+
+int s6_conv_state_update(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, float* h,
+                         float* conv_state, const void* x, const float* conv_w, const float* conv_bias,
+                         int conv_width, const void* delta, const float* delta_bias, int flags,
+                         const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                         const void* z, float* y, void* stream) {
+  if (!conv_w && conv_width == 0) return S6_ERR_NULL;
+  return state_update_impl(batch, dim, dstate, in_dtype, h, x, delta, delta_bias, flags, A, Bm, Cm, Dskip,
+                           z, y, stream, conv_w, conv_bias, conv_state, conv_width);
 }
 
 int s6_state_update(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, float* h,

@@ -48,6 +48,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.s6_last_state_ex.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32] + [vp] * 5
     lib.s6_state_update_ex.restype = i32
     lib.s6_state_update_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, i32] + [vp] * 7
+    lib.s6_conv_scan_fwd.restype = i32
+    lib.s6_conv_scan_fwd.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32, vp, vp, vp, i32] + [vp] * 9
+    lib.s6_conv_state_update.restype = i32
+    lib.s6_conv_state_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32] + [vp] * 7
     lib.s6_scan_bwd.restype = i32
     lib.s6_scan_bwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 19
     lib.s6_scan_bwd_ex.restype = i32
@@ -196,6 +200,84 @@ def state_update(h, x, delta, A, Bm, Cm, D=None, z=None, y=None, delta_bias=None
     else:
         rc = load_library().s6_state_update(bsz, dim, N, _DT[dt], _ptr(h), _ptr(x), _ptr(delta), _ptr(A),
                                             _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(y), _stream())
+    _check(rc)
+    return y
+
+
+def _conv_args(conv_w, conv_bias, dim):
+    if conv_w is None or conv_w.dim() != 2 or conv_w.shape[0] != dim:
+        raise ValueError("conv_w must be a (dim, width) tensor")
+    width = int(conv_w.shape[1])
+    _req(conv_w, "conv_w", (dim, width), torch.float32)
+    _opt(conv_bias, "conv_bias", (dim,), torch.float32)
+    return width
+
+
+def conv_scan_fwd(x, conv_w, delta, A, Bm, Cm, conv_bias=None, conv_state=None, D=None, z=None, h0=None,
+                  return_last_state=False, y=None, h_last=None, delta_bias=None, delta_softplus=False,
+                  zoh=False):
+    """scan_fwd with the convolution front: the scan's input is
+    SiLU(conv_bias + causal filter conv_w (dim, width <= 4) over x), inputs
+    before token 0 from conv_state (batch, dim, width - 1) fp32 or zero.
+    Other arguments and the result as in scan_fwd."""
+    bsz, dim, L = x.shape
+    N = A.shape[1]
+    dt = x.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported input dtype {dt}")
+    width = _conv_args(conv_w, conv_bias, dim)
+    _opt(conv_state, "conv_state", (bsz, dim, width - 1), torch.float32)
+    _req(x, "x", (bsz, dim, L), dt)
+    _req(delta, "delta", (bsz, dim, L), dt)
+    _req(A, "A", (dim, N), torch.float32)
+    _req(Bm, "Bm", (bsz, N, L), dt)
+    _req(Cm, "Cm", (bsz, N, L), dt)
+    _opt(D, "D", (dim,), torch.float32)
+    _opt(z, "z", (bsz, dim, L), dt)
+    _opt(h0, "h0", (bsz, dim, N), torch.float32)
+    if y is None:
+        y = torch.empty((bsz, dim, L), dtype=torch.float32, device=x.device)
+    _req(y, "y", (bsz, dim, L), torch.float32)
+    if return_last_state and h_last is None:
+        h_last = torch.empty((bsz, dim, N), dtype=torch.float32, device=x.device)
+    _opt(h_last, "h_last", (bsz, dim, N), torch.float32)
+    _, flags = _options(delta_bias, delta_softplus, zoh, dim)
+    rc = load_library().s6_conv_scan_fwd(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(conv_w), _ptr(conv_bias), width,
+                                         _ptr(conv_state), _ptr(delta), _ptr(delta_bias), flags, _ptr(A),
+                                         _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last),
+                                         _stream())
+    _check(rc)
+    return (y, h_last) if return_last_state else y
+
+
+def conv_state_update(h, conv_state, x, conv_w, delta, A, Bm, Cm, conv_bias=None, D=None, z=None, y=None,
+                      delta_bias=None, delta_softplus=False, zoh=False):
+    """state_update with the convolution front: conv_state (batch, dim,
+    width - 1) fp32 holds the last inputs (oldest first) and is shifted in
+    place; h is advanced in place.  Returns y (batch, dim) fp32."""
+    bsz, dim, N = h.shape
+    dt = x.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported input dtype {dt}")
+    width = _conv_args(conv_w, conv_bias, dim)
+    if width > 1:
+        _req(conv_state, "conv_state", (bsz, dim, width - 1), torch.float32)
+    _req(h, "h", (bsz, dim, N), torch.float32)
+    _req(x, "x", (bsz, dim), dt)
+    _req(delta, "delta", (bsz, dim), dt)
+    _req(A, "A", (dim, N), torch.float32)
+    _req(Bm, "Bm", (bsz, N), dt)
+    _req(Cm, "Cm", (bsz, N), dt)
+    _opt(D, "D", (dim,), torch.float32)
+    _opt(z, "z", (bsz, dim), dt)
+    if y is None:
+        y = torch.empty((bsz, dim), dtype=torch.float32, device=x.device)
+    _req(y, "y", (bsz, dim), torch.float32)
+    _, flags = _options(delta_bias, delta_softplus, zoh, dim)
+    rc = load_library().s6_conv_state_update(bsz, dim, N, _DT[dt], _ptr(h), _ptr(conv_state), _ptr(x),
+                                             _ptr(conv_w), _ptr(conv_bias), width, _ptr(delta), _ptr(delta_bias),
+                                             flags, _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(y),
+                                             _stream())
     _check(rc)
     return y
 

@@ -204,6 +204,17 @@ def full(w: Workload, threads: int | None = None) -> dict:
     return prm
 
 
+def conv_params(dim: int, width: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """Filter (dim, width) and bias (dim,) of the convolution front, fp32:
+    both Uniform[-1/sqrt(width), 1/sqrt(width)] (the usual initialisation of
+    a per-channel convolution with fan-in `width`).  Stream [seed, 1 << 20]."""
+    g = np.random.default_rng([seed, 1 << 20])
+    lim = 1.0 / math.sqrt(width)
+    w = g.uniform(-lim, lim, size=(dim, width)).astype(np.float32)
+    bias = g.uniform(-lim, lim, size=dim).astype(np.float32)
+    return w, bias
+
+
 # ------------------------------------------------------- device generation --
 def device_full(w: Workload, device="cuda", pair_chunk: int | None = None) -> dict:
     """The whole workload generated directly in device memory with torch's

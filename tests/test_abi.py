@@ -47,7 +47,8 @@ def codes():
 
 
 def test_header_declares_the_entry_points():
-    assert header_functions() == ["s6_last_state", "s6_last_state_ex", "s6_scan_bwd", "s6_scan_bwd_ex", "s6_scan_fwd", "s6_scan_fwd_ex",
+    assert header_functions() == ["s6_conv_scan_fwd", "s6_conv_state_update", "s6_last_state", "s6_last_state_ex",
+                                  "s6_scan_bwd", "s6_scan_bwd_ex", "s6_scan_fwd", "s6_scan_fwd_ex",
                                   "s6_state_update", "s6_state_update_ex", "s6_status_str", "s6_version"]
 
 
@@ -60,7 +61,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings(lib, codes):
-    assert lib.s6_version() == 10100
+    assert lib.s6_version() == 10200
     for name, v in codes.items():
         if name.startswith("S6_ERR_") or name == "S6_OK":
             s = lib.s6_status_str(v).decode()
@@ -146,6 +147,42 @@ def test_option_entry_points_validation(lib, codes):
     assert g(2, 64, 16, 0, P, P, P, P_ODD, 1, P, P, P, None, None, P, None) == codes["S6_ERR_ALIGN"]
     assert g(2, 64, 16, 0, None, P, P, P, 1, P, P, P, None, None, P, None) == codes["S6_ERR_NULL"]
     assert g(2, 0, 16, 0, P, P, P, P, 3, P, P, P, None, None, P, None) == codes["S6_OK"]
+
+
+def test_conv_entry_points_validation(lib, codes):
+    """The convolution front's checks: width 1..4, a filter, a state for
+    decode widths above 1, alignment, then the plain checks."""
+    def scan(w=P, width=4, bias=None, state=None, flags=0, b=2, x=P, y=P):
+        return lib.s6_conv_scan_fwd(b, 64, 32, 16, 1, x, w, bias, width, state, P, None, flags, P, P, P, None, None,
+                                    None, y, None, None)
+
+    assert scan(width=0) == codes["S6_ERR_UNSUPPORTED"]
+    assert scan(width=5) == codes["S6_ERR_UNSUPPORTED"]
+    assert scan(width=-1) == codes["S6_ERR_UNSUPPORTED"]
+    assert scan(w=None) == codes["S6_ERR_NULL"]
+    assert scan(w=None, width=0) == codes["S6_ERR_NULL"]
+    assert scan(w=P_ODD) == codes["S6_ERR_ALIGN"]
+    assert scan(bias=P_ODD) == codes["S6_ERR_ALIGN"]
+    assert scan(state=P_ODD) == codes["S6_ERR_ALIGN"]
+    assert scan(flags=4) == codes["S6_ERR_FLAGS"]
+    assert scan(x=None) == codes["S6_ERR_NULL"]
+    assert scan(y=None) == codes["S6_ERR_NULL"]
+    assert scan(b=0) == codes["S6_OK"]
+    assert scan(b=0, width=1, state=None) == codes["S6_OK"]
+
+    def step(w=P, width=4, state=P, bias=None, b=2, h=P):
+        return lib.s6_conv_state_update(b, 64, 16, 1, h, state, P, w, bias, width, P, None, 0, P, P, P, None, None,
+                                        P, None)
+
+    assert step(width=5) == codes["S6_ERR_UNSUPPORTED"]
+    assert step(width=0) == codes["S6_ERR_UNSUPPORTED"]
+    assert step(w=None, width=0) == codes["S6_ERR_NULL"]
+    assert step(state=None) == codes["S6_ERR_NULL"]
+    assert step(state=P_ODD) == codes["S6_ERR_ALIGN"]
+    assert step(bias=P_ODD) == codes["S6_ERR_ALIGN"]
+    assert step(h=None) == codes["S6_ERR_NULL"]
+    assert step(b=0) == codes["S6_OK"]
+    assert step(b=0, width=1, state=None) == codes["S6_OK"]
 
 
 def test_backward_validation(lib, codes):

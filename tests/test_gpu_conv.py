@@ -1,0 +1,209 @@
+"""Parity of the convolution front (s6_conv_scan_fwd, s6_conv_state_update)
+against the fp64 oracle: the oracle's conv_silu gives the filtered input and
+its magnitude, and the oracle's scan / step run on them.  Same error metric
+and bars as test_gpu_parity.py.
+
+Cases: every width 1..4; with and without bias and state; the vector and
+scalar staging paths (bf16 and fp32, ragged channels and lengths), a long
+row cut into segments (the segments' first inputs come from the previous
+segment's tokens), the state-only pass, the step options together with the
+front; decode steps against the scan, and a scan continued by decode steps.
+
+Filter and bias: synth.conv_params (Uniform[-1/sqrt(K), 1/sqrt(K)]); state:
+N(0, 1) fp32.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import TOL, dev, host64, problem, scaled  # noqa: E402
+from selective_state_space_63_amd import synth  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_63_amd import s6
+    s6.load_library()
+    return torch
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def conv_inputs(w, K, with_bias=True, with_state=True, seed=0):
+    cw, cb = synth.conv_params(w.dim, K, w.seed + seed)
+    g = np.random.default_rng(w.seed + 17 + seed)
+    st = g.standard_normal((w.batch, w.dim, K - 1)).astype(np.float32) if with_state and K > 1 else None
+    return cw, (cb if with_bias else None), st
+
+
+SHAPES = [
+    # batch, dim, N, L, dtype, gate
+    (1, 16, 4, 256, synth.F32, False),      # the fp32 workload's shape
+    (2, 65, 16, 100, synth.BF16, True),     # ragged channels, scalar path
+    (2, 96, 16, 40, synth.BF16, True),      # vector path of the bf16 layers
+    (1, 64, 16, 4096, synth.BF16, True),    # sequence cut into segments
+    (1, 63, 5, 67, synth.F32, True),        # dstate 5, scalar path
+    (2, 40, 32, 48, synth.BF16, True),      # largest dstate
+    (3, 130, 16, 64, synth.F32, True),      # fp32 vector path
+]
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b{}_d{}_n{}_l{}_{}_{}".format(*s))
+def test_conv_scan(torch_cuda, oracle, shape, K):
+    from selective_state_space_63_amd import s6
+    b, dm, n, L, dt, gate = shape
+    w = synth.custom(b, dm, n, L, dt, gate, seed=4000 + L + dm)
+    _say(f"[case] conv scan K={K} {w.name}")
+    d, o = problem(w, True)
+    cw, cb, st = conv_inputs(w, K, with_bias=(K % 2 == 0), with_state=(K != 3))
+    y, hl = s6.conv_scan_fwd(d["x"], dev(cw, synth.F32), d["delta"], d["A"], d["Bm"], d["Cm"],
+                             conv_bias=dev(cb, synth.F32), conv_state=dev(st, synth.F32), D=d["D"], z=d["z"],
+                             h0=d["h0"], return_last_state=True)
+    torch_cuda.cuda.synchronize()
+    xo, xm = oracle.conv_silu(o["x"], cw, cb, st)
+    r = oracle.scan(**dict(o, x=xo), xmag=xm)
+    ey = scaled(host64(y), r["y"], r["m"])
+    eh = scaled(host64(hl), r["h_last"], r["H_last"])
+    assert ey <= TOL[dt], ("y", ey)
+    assert eh <= TOL[dt], ("h_last", eh)
+
+
+@pytest.mark.parametrize("shape", [(2, 65, 16, 100, synth.BF16), (1, 256, 16, 20000, synth.BF16),
+                                   (2, 96, 16, 40, synth.F32)])
+def test_conv_scan_with_step_options(torch_cuda, oracle, shape):
+    """The front together with softplus(delta + bias) and the exact hold."""
+    from selective_state_space_63_amd import s6
+    b, dm, n, L, dt = shape
+    w = synth.custom(b, dm, n, L, dt, True, seed=4100 + L)
+    _say(f"[case] conv scan + options {w.name}")
+    d, o = problem(w, False)
+    g = np.random.default_rng(w.seed + 3)
+    bias = np.log(np.expm1(np.exp(g.uniform(np.log(1e-3), np.log(0.1), size=w.dim)))).astype(np.float32)
+    raw = synth.encode(0.5 * g.standard_normal((w.batch, w.dim, w.seqlen)), w.dtype)
+    d["delta"] = dev(raw, w.dtype)
+    o["delta"] = synth.decode(raw, w.dtype)
+    cw, cb, st = conv_inputs(w, 4)
+    y, hl = s6.conv_scan_fwd(d["x"], dev(cw, synth.F32), d["delta"], d["A"], d["Bm"], d["Cm"],
+                             conv_bias=dev(cb, synth.F32), conv_state=dev(st, synth.F32), D=d["D"], z=d["z"],
+                             return_last_state=True, delta_bias=dev(bias, synth.F32), delta_softplus=True,
+                             zoh=True)
+    torch_cuda.cuda.synchronize()
+    xo, xm = oracle.conv_silu(o["x"], cw, cb, st)
+    r = oracle.scan(**dict(o, x=xo), xmag=xm, delta_bias=bias.astype(np.float64), softplus=True, zoh=True)
+    assert scaled(host64(y), r["y"], r["m"]) <= TOL[dt]
+    assert scaled(host64(hl), r["h_last"], r["H_last"]) <= TOL[dt]
+
+
+@pytest.mark.parametrize("K", [1, 4])
+@pytest.mark.parametrize("shape", [(3, 70, 16, synth.BF16, True), (2, 33, 5, synth.F32, True),
+                                   (6, 22000, 16, synth.BF16, True)])
+def test_conv_decode_steps(torch_cuda, oracle, shape, K):
+    """S decode steps with the front against the oracle's scan of the same
+    tokens; the kept inputs end as the last K-1 inputs."""
+    import torch
+    from selective_state_space_63_amd import s6
+    b, dm, n, dt, gate = shape
+    S = 8
+    w = synth.custom(b, dm, n, S, dt, gate, seed=4200 + dm)
+    _say(f"[case] conv decode K={K} {w.name}")
+    d, o = problem(w, True)
+    cw, cb, st = conv_inputs(w, K)
+    h = d["h0"].clone()
+    cs = dev(st, synth.F32).clone() if st is not None else None
+    cwd, cbd = dev(cw, synth.F32), dev(cb, synth.F32)
+    ys = []
+    tok = {k: [d[k][..., s].contiguous() for s in range(S)] for k in ("x", "delta", "Bm", "Cm", "z")}
+    for s in range(S):
+        ys.append(s6.conv_state_update(h, cs, tok["x"][s], cwd, tok["delta"][s], d["A"], tok["Bm"][s],
+                                       tok["Cm"][s], conv_bias=cbd, D=d["D"], z=tok["z"][s]))
+    torch.cuda.synchronize()
+    xo, xm = oracle.conv_silu(o["x"], cw, cb, st)
+    r = oracle.scan(**dict(o, x=xo), xmag=xm)
+    y = np.stack([host64(v) for v in ys], axis=-1)
+    assert scaled(y, r["y"], r["m"]) <= TOL[dt]
+    assert scaled(host64(h), r["h_last"], r["H_last"]) <= TOL[dt]
+    if K > 1:
+        assert np.array_equal(host64(cs), o["x"][..., S - (K - 1):])
+
+
+def test_conv_scan_then_decode(torch_cuda, oracle):
+    """A prefix scanned with the front, continued by decode steps from its
+    final state and its last three inputs: the whole sequence's outputs."""
+    import torch
+    from selective_state_space_63_amd import s6
+    P, S = 56, 6
+    w = synth.custom(2, 96, 16, P + S, synth.BF16, True, seed=4300)
+    _say(f"[case] conv scan then decode {w.name}")
+    d, o = problem(w, False)
+    cw, cb, _ = conv_inputs(w, 4, with_state=False)
+    cwd, cbd = dev(cw, synth.F32), dev(cb, synth.F32)
+    pre = {k: d[k][..., :P].contiguous() for k in ("x", "delta", "Bm", "Cm", "z")}
+    y0, h = s6.conv_scan_fwd(pre["x"], cwd, pre["delta"], d["A"], pre["Bm"], pre["Cm"], conv_bias=cbd, D=d["D"],
+                             z=pre["z"], return_last_state=True)
+    cs = d["x"][..., P - 3:P].to(torch.float32).contiguous()
+    ys = []
+    for s in range(P, P + S):
+        t = {k: d[k][..., s].contiguous() for k in ("x", "delta", "Bm", "Cm", "z")}
+        ys.append(s6.conv_state_update(h, cs, t["x"], cwd, t["delta"], d["A"], t["Bm"], t["Cm"], conv_bias=cbd,
+                                       D=d["D"], z=t["z"]))
+    torch.cuda.synchronize()
+    xo, xm = oracle.conv_silu(o["x"], cw, cb, None)
+    r = oracle.scan(**dict(o, x=xo), xmag=xm)
+    y = np.concatenate([host64(y0), np.stack([host64(v) for v in ys], axis=-1)], axis=-1)
+    assert scaled(y, r["y"], r["m"]) <= TOL[w.dtype]
+    assert scaled(host64(h), r["h_last"], r["H_last"]) <= TOL[w.dtype]
+
+
+def test_conv_width_one_identity_filter_is_silu_input(torch_cuda):
+    """Width 1, weight 1, no bias: the front is SiLU(x), so the result equals
+    the plain scan of SiLU(x) computed on the device."""
+    import torch
+    from selective_state_space_63_amd import s6
+    w = synth.custom(2, 96, 16, 64, synth.F32, True, seed=4400)
+    _say(f"[case] conv identity {w.name}")
+    d, _ = problem(w, False)
+    ones = torch.ones((w.dim, 1), device="cuda", dtype=torch.float32)
+    y1 = s6.conv_scan_fwd(d["x"], ones, d["delta"], d["A"], d["Bm"], d["Cm"], D=d["D"], z=d["z"])
+    y2 = s6.scan_fwd(torch.nn.functional.silu(d["x"]), d["delta"], d["A"], d["Bm"], d["Cm"], D=d["D"], z=d["z"])
+    torch.cuda.synchronize()
+    assert torch.allclose(y1, y2, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("name", ["m3b", "long"])
+def test_conv_workload_sampled(torch_cuda, oracle, name):
+    """The full-size workloads with the front (width 4 and its bias, as
+    bench.py times the 3B layer), sampled (batch, channel) rows over their
+    whole length against the oracle's front and scan of those rows."""
+    from selective_state_space_63_amd import s6
+    w = synth.WORKLOADS[name]
+    _say(f"[case] conv workload {w.name}")
+    inp = synth.device_full(w)
+    cw, cb = synth.conv_params(w.dim, 4, w.seed)
+    y, hl = s6.conv_scan_fwd(inp["x"], dev(cw, synth.F32), inp["delta"], inp["A"], inp["Bm"], inp["Cm"],
+                             conv_bias=dev(cb, synth.F32), D=inp["Dskip"], z=inp["z"], return_last_state=True)
+    torch_cuda.cuda.synchronize()
+    g = np.random.default_rng(21)
+    ds = sorted(set([0, 31, 32, 63, 64, w.dim - 1] + [int(v) for v in g.choice(w.dim, size=10, replace=False)]))
+    idx = np.array(ds)
+    bs = sorted(set([0, w.batch - 1]))
+    worst = 0.0
+    for b in bs:
+        xo, xm = oracle.conv_silu(host64(inp["x"][b:b + 1, idx]), cw[idx], cb[idx])
+        r = oracle.scan(x=xo, delta=host64(inp["delta"][b:b + 1, idx]), A=host64(inp["A"][idx]),
+                        Bm=host64(inp["Bm"][b:b + 1]), Cm=host64(inp["Cm"][b:b + 1]), Dskip=host64(inp["Dskip"][idx]),
+                        z=host64(inp["z"][b:b + 1, idx]), xmag=xm)
+        ey = scaled(host64(y[b, idx]), r["y"][0], r["m"][0])
+        eh = scaled(host64(hl[b, idx]), r["h_last"][0], r["H_last"][0])
+        worst = max(worst, ey, eh)
+        assert ey <= TOL[w.dtype] and eh <= TOL[w.dtype], (b, ey, eh)
+    _say(f"[result] conv {w.name} max scaled error {worst:.3e}")
