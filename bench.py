@@ -27,7 +27,8 @@ HBM_PEAK_GBS = 8000.0
 # v_rcp_f32) takes two slots.
 VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 # The sources of the scan kernel (the counters in TRAFFIC_FILE hold for them).
-KERNEL_SRC = [os.path.join(ROOT, "selective_state_space_63_amd", "csrc", f) for f in ("scan.hip", "s6_internal.h")]
+KERNEL_SRC = [os.path.join(ROOT, "selective_state_space_63_amd", "csrc", f)
+              for f in ("scan.hip", "scan_kernel.h", "s6_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "s6_scan_kernel_m3b_traffic.md")
 
 

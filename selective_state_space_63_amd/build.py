@@ -15,8 +15,9 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = [os.path.join(CSRC, f) for f in ("scan.hip", "step.hip", "bwd.hip", "common.hip")]
-HEADERS = [os.path.join(CSRC, "s6_internal.h"), os.path.join(ROOT, "include", "s6.h")]
+SOURCES = [os.path.join(CSRC, f) for f in ("scan.hip", "scan_ext.hip", "step.hip", "bwd.hip", "common.hip")]
+HEADERS = [os.path.join(CSRC, "s6_internal.h"), os.path.join(CSRC, "scan_kernel.h"),
+           os.path.join(ROOT, "include", "s6.h")]
 LIB = os.path.join(PKG, "libs6.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed FP32 instructions are switched off: hipcc would otherwise pair

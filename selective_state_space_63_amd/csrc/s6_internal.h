@@ -7,9 +7,10 @@
 // State Space Models详解" §2.2-§2.4 and §3.2-§3.4).  Per (batch, channel,
 // state):  h = exp(delta*A) * h + delta*B*x ;  y = (sum_n C*h + D*x) * SiLU(z)
 //
-// Files: scan.hip (fused scan, final-state scan, segments and carries),
-// step.hip (decode step), bwd.hip (gradients), common.hip (checks, errors,
-// version).
+// Files: scan_kernel.h (the fused scan kernel), scan.hip (its plain
+// instantiations, final-state scan, segments and carries, entry points),
+// scan_ext.hip (option kernels), step.hip (decode step), bwd.hip
+// (gradients), common.hip (checks, errors, version).
 #ifndef S6_INTERNAL_H_
 #define S6_INTERNAL_H_
 
@@ -144,9 +145,15 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, size_
                const void* const* ptrs, int nptr);
 
 // One launch of the scan kernel (mode kModeY or kModeState) over `segs`
-// segments; the option kernels when a.softplus, a.zoh or a.dbias is set.
+// segments; the option kernels when a.softplus, a.zoh, a.dbias or a.conv_w
+// is set.
 int launch_scan_any(int in_dtype, int mode, const ScanArgs& a, const Plan& p, bool gate, int64_t batch,
                     int64_t segs, hipStream_t st);
+
+// The option kernels (scan_ext.hip): step bias, softplus, exact hold,
+// convolution front.
+int launch_scan_options(int in_dtype, int mode, const ScanArgs& a, const Plan& p, bool gate, int64_t batch,
+                        int64_t segs, hipStream_t st);
 
 // The carry fold over segments: hin[s] (nullable) receives the state entering
 // segment s, hlast (nullable) the state after the last of `nagg` aggregates.
