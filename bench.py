@@ -111,9 +111,11 @@ def bwd_valu_slots(w):
     return w.batch * w.dim * w.seqlen * (13 * w.dstate + 16)
 
 
-def bench_backward(w, steps=10, warmup=3, softplus=False):
+def bench_backward(w, steps=10, warmup=3, softplus=False, ckpt=False):
     """Times s6_scan_bwd on workload w (dy random, no dh_last); softplus:
-    with the softplus step and a bias of -4 per channel."""
+    with the softplus step and a bias of -4 per channel; ckpt: from the
+    checkpoints of one forward with checkpoints (s6_scan_bwd_ckpt), not
+    timed here."""
     import torch
     from selective_state_space_63_amd import s6, synth
     inp = synth.device_full(w)
@@ -121,6 +123,12 @@ def bench_backward(w, steps=10, warmup=3, softplus=False):
     opts = {}
     if softplus:
         opts = dict(delta_bias=torch.full((w.dim,), -4.0, device="cuda", dtype=torch.float32), delta_softplus=True)
+
+    if ckpt:
+        ck = torch.empty(s6.ckpt_shape(w.batch, w.dim, w.seqlen, w.dstate), device="cuda", dtype=torch.float32)
+        s6.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], D=inp["Dskip"], z=inp["z"], ckpt=ck,
+                    **opts)
+        opts = dict(opts, ckpt=ck)
 
     def step():
         s6.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], dy, D=inp["Dskip"], z=inp["z"], **opts)
@@ -153,14 +161,15 @@ def decode_step_bytes(batch, dim, N, in_bytes, gate=True):
     return batch * dim * per + 2 * batch * N * in_bytes + 4 * dim * N + 4 * dim
 
 
-def bench_scan(w, steps, warmup, flush=False, softplus=False, zoh=False, conv_k=0):
+def bench_scan(w, steps, warmup, flush=False, softplus=False, zoh=False, conv_k=0, ckpt=False):
     """Times `steps` scans of workload w (after `warmup`).  flush: before each
     timed scan, write a 512 MiB buffer so that no input is cache-resident,
     and time each scan on its own.  softplus / zoh: time the option kernels
     (the stored delta is then the softplus argument, with a bias of -4 per
     channel; the timing does not depend on the values).  conv_k: the scan
     with the convolution front of that width (synth.conv_params filter and
-    bias, no state)."""
+    bias, no state).  ckpt: the scan that also writes the checkpoints for
+    the backward (s6_scan_fwd_ckpt)."""
     import torch
     from selective_state_space_63_amd import s6, synth
     inp = synth.device_full(w)
@@ -173,6 +182,9 @@ def bench_scan(w, steps, warmup, flush=False, softplus=False, zoh=False, conv_k=
         opts = dict(delta_bias=torch.full((w.dim,), -4.0, device="cuda", dtype=torch.float32) if softplus else None,
                     delta_softplus=softplus, zoh=zoh)
 
+    if ckpt:
+        opts["ckpt"] = torch.empty(s6.ckpt_shape(w.batch, w.dim, w.seqlen, w.dstate), device="cuda",
+                                   dtype=torch.float32)
     if conv_k:
         cw, cb = synth.conv_params(w.dim, conv_k, w.seed)
         cw, cb = torch.from_numpy(cw).cuda(), torch.from_numpy(cb).cuda()
@@ -630,6 +642,18 @@ def main():
         print(f"[bench] backward {wl.name}", file=sys.stderr, flush=True)
         out["backward_long"] = bench_backward(wl, steps=3, warmup=2)
         out["backward_long"]["note"] = "sequence run in parts with adjoint carries (carry pass + fold)"
+        torch.cuda.empty_cache()
+        print(f"[bench] training step {w.name} (forward with checkpoints + backward from them)", file=sys.stderr,
+              flush=True)
+        _, tfc, _ = bench_scan(w, 50, 50, ckpt=True)
+        bck = bench_backward(w, ckpt=True)
+        out["training"] = {"workload": w.name, "fwd_ckpt_ms": round(tfc["mean"], 4), "bwd_ckpt_ms": bck["ms_mean"],
+                           "step_ms": round(tfc["mean"] + bck["ms_mean"], 4),
+                           "recompute_step_ms": round(ms + out["backward"]["ms_mean"], 4),
+                           "bwd_ckpt_valu_frac": bck["valu_frac"],
+                           "note": "s6_scan_fwd_ckpt (also writes the state entering every 64-token block) + "
+                                   "s6_scan_bwd_ckpt (starts from them: no checkpoint pass); recompute_step_ms = "
+                                   "s6_scan_fwd + s6_scan_bwd"}
         torch.cuda.empty_cache()
         print(f"[bench] scan {w.name} with the step options", file=sys.stderr, flush=True)
         _, ts, _ = bench_scan(w, 50, 50, softplus=True)

@@ -224,6 +224,32 @@ int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, i
                    const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
                    float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* stream);
 
+/* Checkpoints for training: the forward saves the state entering every
+ * S6_CKPT_TOKENS-token block, and the backward starts from them instead of
+ * recomputing them.  The pages' guide (§3.4) has the fused scan recompute the
+ * intermediate states in the backward pass rather than read them from slow
+ * memory; these two entry points keep one state in S6_CKPT_TOKENS from the
+ * forward pass (1/64 of the states: 4 * batch * dim * dstate bytes per 64
+ * tokens) and still recompute everything inside a block.
+ *   ckpt : (ceil(seqlen / S6_CKPT_TOKENS), batch, dim, dstate) fp32; block s
+ *          holds the state before token S6_CKPT_TOKENS * s (block 0: h0, or
+ *          0).  Written by s6_scan_fwd_ckpt, read by s6_scan_bwd_ckpt;
+ *          required (S6_ERR_NULL) when there is any work.  4-byte aligned.
+ * s6_scan_fwd_ckpt is s6_scan_fwd_ex plus the checkpoints.  s6_scan_bwd_ckpt
+ * is s6_scan_bwd_ex with ckpt in place of h0 (the same inputs and options as
+ * the forward that wrote it). */
+#define S6_CKPT_TOKENS 64
+int s6_scan_fwd_ckpt(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                     const void* x, const void* delta, const float* delta_bias, int flags,
+                     const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                     const float* h0, float* y, float* h_last, float* ckpt, void* stream);
+
+int s6_scan_bwd_ckpt(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                     const void* x, const void* delta, const float* delta_bias, int flags, const float* A,
+                     const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* ckpt,
+                     const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
+                     float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

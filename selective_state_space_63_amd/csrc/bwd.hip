@@ -38,7 +38,8 @@ constexpr int bwd_waves() { return 4; }
 
 template <int SPL>
 constexpr size_t bwd_lds_bytes(bool sp) {
-  return sizeof(float) * ((size_t)(sp ? 5 : 4) * (4 * bwd_waves<SPL>()) * kBwdPitch + (size_t)2 * 16 * SPL * kBwdPitch +
+  // tiles x, delta, dyc, dy SiLU'(z), then delta * x (plain) or dstep/dv (SP)
+  return sizeof(float) * ((size_t)5 * (4 * bwd_waves<SPL>()) * kBwdPitch + (size_t)2 * 16 * SPL * kBwdPitch +
                           (size_t)bwd_waves<SPL>() * 2 * 16 * 16 * SPL);
 }
 
@@ -135,10 +136,11 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
   float* sdl = sx + CW * KP;         // [CW][KP] delta
   float* sdyc = sdl + CW * KP;       // [CW][KP] dy * SiLU(z)
   float* sq = sdyc + CW * KP;        // [CW][KP] dy * SiLU'(z)
-  float* sB = sq + CW * KP;          // [NS][KP]
+  float* su = sq + CW * KP;          // [CW][KP] plain: delta * x; SP: dstep/dv
+  float* sB = su + CW * KP;          // [NS][KP]
   float* sC = sB + NS * KP;          // [NS][KP]
   float* red = sC + NS * KP;         // [waves][2][16][NS]
-  float* sjs = red + WB * 2 * 16 * NS;  // SP: [CW][KP] dstep/dv
+  float* sjs = su;                   // SP: the fifth tile holds dstep/dv (delta * x is formed on use)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -183,6 +185,17 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
   }
   float dD = 0.0f, dbias = 0.0f;
 
+  // delta * x of 4 tokens of this lane's channel from LDS (formed from delta
+  // and x in SP kernels, whose fifth tile holds dstep/dv instead)
+  auto load_u4 = [&](int t, const float4& dl4) {
+    if constexpr (SP) {
+      const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KP + t);
+      return make_float4(dl4.x * x4.x, dl4.y * x4.y, dl4.z * x4.z, dl4.w * x4.w);
+    } else {
+      return *reinterpret_cast<const float4*>(su + c * KP + t);
+    }
+  };
+
   for (int64_t s = s_end - 1; s >= s_begin; --s) {
     const int64_t tb = s * KS;
     const int64_t tl = L - tb < KS ? L - tb : KS;  // valid tokens of the segment
@@ -212,6 +225,7 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
       sdyc[li] = dyc;
       sq[li] = q;
       if constexpr (SP) sjs[li] = js;
+      else su[li] = dl * xv;
     }
     for (int i = tid; i < NS * KS; i += NTHR) {
       const int n = i / KS, t = i % KS;
@@ -241,9 +255,9 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
           __builtin_amdgcn_sched_barrier(0);
           const int t = 16 * k + 4 * g;
           const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KP + t);
-          const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KP + t);
+          const float4 u4 = load_u4(t, dl4);
           const float dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
-          const float u[4] = {dl4.x * x4.x, dl4.y * x4.y, dl4.z * x4.z, dl4.w * x4.w};
+          const float u[4] = {u4.x, u4.y, u4.z, u4.w};
 #pragma unroll
           for (int j = 0; j < SPL; ++j) {
             const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KP + t);
@@ -265,9 +279,9 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
         __builtin_amdgcn_sched_barrier(0);
         const int t = 16 * k + 4 * g;
         const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KP + t);
-        const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KP + t);
+        const float4 u4 = load_u4(t, dl4);
         const float dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
-        const float u[4] = {dl4.x * x4.x, dl4.y * x4.y, dl4.z * x4.z, dl4.w * x4.w};
+        const float u[4] = {u4.x, u4.y, u4.z, u4.w};
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
           const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KP + t);
@@ -286,10 +300,10 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
         __builtin_amdgcn_sched_barrier(0);
         const int t4 = 16 * k + 4 * g4;
         const float4 dl4 = *reinterpret_cast<const float4*>(sdl + c * KP + t4);
-        const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KP + t4);
+        const float4 u4 = load_u4(t4, dl4);
         const float4 y4 = *reinterpret_cast<const float4*>(sdyc + c * KP + t4);
         const float dlv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
-        const float xvv[4] = {x4.x, x4.y, x4.z, x4.w};
+        const float uv[4] = {u4.x, u4.y, u4.z, u4.w};
         const float dycv[4] = {y4.x, y4.y, y4.z, y4.w};
         float Bv[SPL][4], Cv[SPL][4];
 #pragma unroll
@@ -303,7 +317,7 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
 #pragma unroll
         for (int ii = 3; ii >= 0; --ii) {
           const int i = 4 * g4 + ii;
-          const float dl = dlv[ii], xv = xvv[ii], dyc = dycv[ii];
+          const float dl = dlv[ii], uu = uv[ii], dyc = dycv[ii];
           s1[i] = 0.0f;
           s2[i] = 0.0f;
           s3[i] = 0.0f;
@@ -316,16 +330,14 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
             s2[i] = __builtin_fmaf(An[j], r, s2[i]);
             s3[i] = __builtin_fmaf(Cv[j][ii], hist[j][i + 1], s3[i]);
             dA[j] = __builtin_fmaf(dl, r, dA[j]);
-            pb[j][ii] = lam * (dl * xv);
+            pb[j][ii] = lam * uu;
             pc[j][ii] = dyc * hist[j][i + 1];
           }
-          dD = __builtin_fmaf(dyc, xv, dD);
         }
         // the running sums are updated here (left alone, the compiler defers
         // them to the end of the chunk and keeps all their operands live)
 #pragma unroll
         for (int j = 0; j < SPL; ++j) asm volatile("" : "+v"(dA[j]), "+v"(mu[j]));
-        asm volatile("" : "+v"(dD));
         // channel sums of the 4 tokens over the wave's rows, then to LDS
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
@@ -347,6 +359,7 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
           const float xv = sx[c * KP + t];
           const float dyc = sdyc[c * KP + t];
           const int64_t off = (b * D + d) * L + tt;
+          dD = __builtin_fmaf(dyc, xv, dD);  // lane nl: the tokens nl mod 16
           a.dx[off] = __builtin_fmaf(dyc, dsk, dl * k1);
           float gd = __builtin_fmaf(xv, k1, k2);
           if constexpr (SP) {
@@ -374,6 +387,11 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
       __syncthreads();  // red is free again
     }
   }
+  // the channel's dD: lane nl summed the tokens it wrote
+  dD += dpp_f<0x128>(dD);
+  dD += dpp_f<0x124>(dD);
+  dD += dpp_f<0x122>(dD);
+  dD += dpp_f<0x121>(dD);
   if (chv) {
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
@@ -599,13 +617,18 @@ int bwd_channels_per_block(int64_t dstate) { return dstate <= 16 ? 4 * bwd_waves
 
 using namespace s6i;
 
-extern "C" {
+namespace {
 
-int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
-                   const void* x, const void* delta, const float* delta_bias, int flags, const float* A,
-                   const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
-                   const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
-                   float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* stream) {
+// s6_scan_bwd_ex, and s6_scan_bwd_ckpt when ckpt (the states entering every
+// kCkpt-token block, from s6_scan_fwd_ckpt) is given: the checkpoint pass is
+// then skipped.
+int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                  const void* x, const void* delta, const float* delta_bias, int flags, const float* A,
+                  const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
+                  const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
+                  float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, const float* ckpt,
+                  void* stream) {
+  static_assert(kBwdSeg == kCkpt, "backward segments are the checkpoint blocks");
   int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
   if (rc) return rc;
   if (flags & ~(S6_DELTA_SOFTPLUS | S6_ZOH_EXACT)) return S6_ERR_FLAGS;
@@ -620,7 +643,7 @@ int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, i
   for (const void* p : ins)
     if (p && !aligned(p, esz)) return S6_ERR_ALIGN;
   const void* f32s[] = {A, Dskip, h0, dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, delta_bias,
-                        ddelta_bias};
+                        ddelta_bias, ckpt};
   for (const void* p : f32s)
     if (p && !aligned(p, 4)) return S6_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -655,9 +678,9 @@ int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, i
   const int64_t spp = (S + G - 1) / G;  // segments per part
   G = (S + spp - 1) / spp;
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-  const size_t agg_b = (size_t)(nagg > 0 ? nagg : 0) * nstate * sizeof(float);
-  const size_t sd_b = (size_t)(nagg > 0 ? nagg : 0) * batch * dim * sizeof(float);
-  const size_t hin_b = (size_t)S * nstate * sizeof(float);
+  const size_t agg_b = ckpt ? 0 : (size_t)(nagg > 0 ? nagg : 0) * nstate * sizeof(float);
+  const size_t sd_b = ckpt ? 0 : (size_t)(nagg > 0 ? nagg : 0) * batch * dim * sizeof(float);
+  const size_t hin_b = ckpt ? 0 : (size_t)S * nstate * sizeof(float);
   const size_t dap_b = (size_t)G * nstate * sizeof(float);
   const size_t ddp_b = (size_t)G * batch * dim * sizeof(float);
   const size_t bc_b = (size_t)nblkb * batch * dstate * seqlen * sizeof(float);
@@ -672,7 +695,7 @@ int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, i
   wp += up(agg_b);
   float* sd = reinterpret_cast<float*>(wp);
   wp += up(sd_b);
-  float* hin = reinterpret_cast<float*>(wp);
+  const float* hin = ckpt ? ckpt : reinterpret_cast<float*>(wp);
   wp += up(hin_b);
   float* dap = reinterpret_cast<float*>(wp);
   wp += up(dap_b);
@@ -691,7 +714,7 @@ int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, i
   float* cSD = reinterpret_cast<float*>(wp);
 
   // pass 1: end state (from zero) and summed delta of every segment but the last
-  if (nagg > 0) {
+  if (nagg > 0 && !ckpt) {
     const void* vecptrs[] = {x, delta, Bm};
     Plan p = make_plan(batch, dim, seqlen, dstate, esz, vecptrs, 3);
     ScanArgs g;
@@ -703,8 +726,8 @@ int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, i
     rc = launch_scan_any(in_dtype, kModeState, g, p, false, batch, nagg, st);
   }
   // the state entering every segment
-  if (rc == S6_OK) {
-    rc = launch_fold_carries(A, h0, agg, sd, hin, nullptr, batch, dim, dstate, S, nagg, st);
+  if (rc == S6_OK && !ckpt) {
+    rc = launch_fold_carries(A, h0, agg, sd, const_cast<float*>(hin), nullptr, batch, dim, dstate, S, nagg, st);
   }
   if (rc == S6_OK) {
     BwdArgs b;
@@ -746,6 +769,29 @@ int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, i
   hipError_t e = hipFreeAsync(ws, st);
   if (rc == S6_OK && e != hipSuccess) rc = hip_fail(e, "hipFreeAsync(backward workspace)");
   return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                   const void* x, const void* delta, const float* delta_bias, int flags, const float* A,
+                   const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
+                   const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
+                   float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* stream) {
+  return scan_bwd_impl(batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm, Dskip, z, h0,
+                       dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, ddelta_bias, nullptr, stream);
+}
+
+int s6_scan_bwd_ckpt(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                     const void* x, const void* delta, const float* delta_bias, int flags, const float* A,
+                     const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* ckpt,
+                     const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
+                     float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* stream) {
+  if (!ckpt && batch > 0 && dim > 0 && seqlen > 0) return S6_ERR_NULL;
+  return scan_bwd_impl(batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm, Dskip, z,
+                       nullptr, dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, ddelta_bias, ckpt, stream);
 }
 
 int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,

@@ -34,6 +34,7 @@ constexpr int kT = 16;             // tokens per chunk
 constexpr int kP = kT;             // LDS tile pitch in floats (channel-major [c][t], swizzled)
 constexpr int kMaxN = 32;          // largest dstate supported
 constexpr int kMaxConv = 4;        // widest filter of the convolution front
+constexpr int kCkpt = 64;          // tokens per checkpoint block (S6_CKPT_TOKENS)
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
@@ -126,6 +127,8 @@ struct ScanArgs {
   int64_t hinit_stride;   // elements between segments in hinit (0: same for all)
   int64_t hout_stride;    // elements between segments in hout
   int64_t hout_last_only; // 1: only the last segment writes hout (at offset 0)
+  float* ckpt;            // kModeY: the state entering every kCkpt-token block,
+                          // (ceil(L / kCkpt), batch, D, N), or null
 };
 
 struct Plan {

@@ -120,7 +120,8 @@ struct ConvFront {
 int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
               const void* x, const void* delta, const float* dbias, int flags, const float* A,
               const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
-              float* y, float* h_last, void* stream, const ConvFront& cf = ConvFront()) {
+              float* y, float* h_last, void* stream, const ConvFront& cf = ConvFront(),
+              float* ckpt = nullptr) {
   int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
   if (rc) return rc;
   if (flags & ~(S6_DELTA_SOFTPLUS | S6_ZOH_EXACT)) return S6_ERR_FLAGS;
@@ -139,7 +140,7 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
   const void* ins[] = {x, delta, Bm, Cm, z};
   for (const void* p : ins)
     if (p && !aligned(p, esz)) return S6_ERR_ALIGN;
-  const void* f32s[] = {A, Dskip, h0, y, h_last};
+  const void* f32s[] = {A, Dskip, h0, y, h_last, ckpt};
   for (const void* p : f32s)
     if (p && !aligned(p, 4)) return S6_ERR_ALIGN;
 
@@ -170,6 +171,7 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
   a.dbias = dbias;
   a.conv_w = cf.w; a.conv_b = cf.bias; a.conv_state = cf.state; a.conv_k = cf.width;
   a.D = dim; a.L = seqlen; a.N = dstate; a.seg_len = p.seg_len;
+  a.ckpt = want_y ? ckpt : nullptr;
 
   if (S == 1) {
     a.hinit = h0;
@@ -194,7 +196,7 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
 
   // pass 1: end states of the first nagg segments from a zero state
   ScanArgs g = a;
-  g.z = nullptr; g.Cm = nullptr; g.Dskip = nullptr;
+  g.z = nullptr; g.Cm = nullptr; g.Dskip = nullptr; g.ckpt = nullptr;
   g.hinit = nullptr;
   g.hout = agg;
   g.hout_stride = nstate;
@@ -259,6 +261,15 @@ int s6_conv_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
   if (!conv_w && conv_width == 0) return S6_ERR_NULL;
   return scan_impl(true, batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm,
                    Dskip, z, h0, y, h_last, stream, cf);
+}
+
+int s6_scan_fwd_ckpt(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                     const void* x, const void* delta, const float* delta_bias, int flags,
+                     const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                     const float* h0, float* y, float* h_last, float* ckpt, void* stream) {
+  if (!ckpt && batch > 0 && dim > 0 && seqlen > 0) return S6_ERR_NULL;
+  return scan_impl(true, batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm,
+                   Dskip, z, h0, y, h_last, stream, ConvFront(), ckpt);
 }
 
 int s6_last_state(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,

@@ -228,7 +228,7 @@ __device__ __forceinline__ void token_group(const float* dl, const float* xv, co
 // token groups, and the
 // kind of piece each wave stages rotates with the workgroup index so that
 // this extra work falls on every SIMD alike.
-template <typename In, int VEC, bool GATE, int MODE, int W, int WIN, int EXT>
+template <typename In, int VEC, bool GATE, int MODE, int W, int WIN, int EXT, bool CK>
 __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ? (EXT ? 4 : 5) : 1)))
 s6_scan_kernel(ScanArgs a) {
   constexpr int NTHR = 64 * W;
@@ -294,6 +294,26 @@ s6_scan_kernel(ScanArgs a) {
   }
   const bool fchv = d0 + fc < D;
   const float dsk = (MODE == kModeY && a.Dskip && fchv) ? a.Dskip[d0 + fc] : 0.0f;
+  // Checkpoints (fused pass): the state entering every kCkpt-token block of
+  // this segment, the first one being the segment's incoming state.
+  // (The offsets are rebuilt from the thread index here, inside the rarely
+  // taken branch: values kept from outside would hold registers through the
+  // whole chunk loop.)
+  auto write_ckpt = [&](int64_t tok) {
+    const int64_t nst = (int64_t)(gridDim.x / nblk) * D * N;
+    float* base = a.ckpt + (tok / kCkpt) * nst + (b * D + d0) * N;  // uniform
+    const int ln = (int)threadIdx.x & 63;
+    const int c = ((ln >> 5) << 4) | (ln & 15);
+    const int n0 = ((int)threadIdx.x >> 6) * 4 + 2 * ((ln >> 4) & 1);
+    if (c < rows_valid) {
+      if (n0 < N) base[c * N + n0] = h[0];
+      if (n0 + 1 < N) base[c * N + n0 + 1] = h[1];
+    }
+  };
+  // Plain kernels write checkpoints only in their CK instantiations (the
+  // write in the chunk loop costs registers); option kernels check a.ckpt.
+  constexpr bool kCk = MODE == kModeY && (CK || EXT != 0);
+  if (kCk && a.ckpt && tb < te) write_ckpt(tb);
   // Sum of delta over the segment (state mode), compensated (Neumaier):
   // dsum + dcomp.  (A double accumulator here costs dozens of registers.)
   float dsum = 0.0f, dcomp = 0.0f;
@@ -589,6 +609,14 @@ s6_scan_kernel(ScanArgs a) {
     // output terms nothing else ties them to the chunk, and the compiler would
     // sink them past the barriers, keeping every chunk's inputs live at once.)
     asm volatile("" : "+v"(h[0]), "+v"(h[1]), "+v"(cs));
+    if constexpr (kCk) {
+      // A block ends with this chunk: segments start at multiples of kCkpt
+      // tokens, so with 4-chunk cycles only the cycle's last chunk can end one.
+      if constexpr (2 * WIN != 4 || P == 3) {
+        const int64_t tn = t0 + kT;  // tokens done after this chunk
+        if (a.ckpt && tn % kCkpt == 0 && tn < te) write_ckpt(tn);
+      }
+    }
     float* pbuf = part + buf * (W * PART);
     if constexpr (MODE == kModeY) {
       // ysum[i] is this wave's sum for token 2i + r: part[buf][w][r][cl][i]
@@ -672,7 +700,7 @@ s6_scan_kernel(ScanArgs a) {
   }
 }
 
-template <typename In, int VEC, bool GATE, int MODE, int W, int EXT>
+template <typename In, int VEC, bool GATE, int MODE, int W, int EXT, bool CK>
 int launch_scan_t(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, hipStream_t st) {
   // 64-byte row runs per load: two chunks per window for bf16 vectors with
   // enough threads to hold them, one chunk otherwise.
@@ -682,9 +710,19 @@ int launch_scan_t(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, 
   if (MODE == kModeY) lds += (size_t)2 * W * 2 * kCW * (kT / 2) * sizeof(float);  // partials
   lds += (size_t)2 * BCLayout<W>::kFloats * sizeof(float);                     // B/C
   dim3 grid((unsigned)(nblk * batch), 1u, (unsigned)segs);
-  hipLaunchKernelGGL((s6_scan_kernel<In, VEC, GATE, MODE, W, WIN, EXT>), grid, dim3(64 * W), lds, st, a);
+  hipLaunchKernelGGL((s6_scan_kernel<In, VEC, GATE, MODE, W, WIN, EXT, CK>), grid, dim3(64 * W), lds, st, a);
   S6_HIP(hipGetLastError(), "s6_scan_kernel launch");
   return S6_OK;
+}
+
+// The checkpoint-writing instantiation of a plain fused kernel when a.ckpt
+// is set (option kernels write them whenever it is set).
+template <typename In, int VEC, bool GATE, int MODE, int W, int EXT>
+int launch_scan_c(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, hipStream_t st) {
+  if constexpr (MODE == kModeY && EXT == 0) {
+    if (a.ckpt) return launch_scan_t<In, VEC, GATE, MODE, W, EXT, true>(a, batch, nblk, segs, st);
+  }
+  return launch_scan_t<In, VEC, GATE, MODE, W, EXT, false>(a, batch, nblk, segs, st);
 }
 
 template <typename In, int MODE, int W, int EXT>
@@ -692,13 +730,13 @@ int launch_scan_w(const ScanArgs& a, bool vec, bool gate, int64_t batch, int64_t
                   hipStream_t st) {
   constexpr int kV = 16 / sizeof(In);
   if constexpr (MODE == kModeY) {
-    if (vec && gate) return launch_scan_t<In, kV, true, MODE, W, EXT>(a, batch, nblk, segs, st);
-    if (vec) return launch_scan_t<In, kV, false, MODE, W, EXT>(a, batch, nblk, segs, st);
-    if (gate) return launch_scan_t<In, 1, true, MODE, W, EXT>(a, batch, nblk, segs, st);
-    return launch_scan_t<In, 1, false, MODE, W, EXT>(a, batch, nblk, segs, st);
+    if (vec && gate) return launch_scan_c<In, kV, true, MODE, W, EXT>(a, batch, nblk, segs, st);
+    if (vec) return launch_scan_c<In, kV, false, MODE, W, EXT>(a, batch, nblk, segs, st);
+    if (gate) return launch_scan_c<In, 1, true, MODE, W, EXT>(a, batch, nblk, segs, st);
+    return launch_scan_c<In, 1, false, MODE, W, EXT>(a, batch, nblk, segs, st);
   } else {
-    if (vec) return launch_scan_t<In, kV, false, MODE, W, EXT>(a, batch, nblk, segs, st);
-    return launch_scan_t<In, 1, false, MODE, W, EXT>(a, batch, nblk, segs, st);
+    if (vec) return launch_scan_c<In, kV, false, MODE, W, EXT>(a, batch, nblk, segs, st);
+    return launch_scan_c<In, 1, false, MODE, W, EXT>(a, batch, nblk, segs, st);
   }
 }
 

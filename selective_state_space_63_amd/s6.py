@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libs6.so")
 
 S6_F32, S6_BF16 = 0, 1
 S6_DELTA_SOFTPLUS, S6_ZOH_EXACT = 1, 2  # option bits of the _ex entry points
+S6_CKPT_TOKENS = 64  # tokens per checkpoint block (s6_scan_fwd_ckpt / s6_scan_bwd_ckpt)
 _DT = {torch.float32: S6_F32, torch.bfloat16: S6_BF16}
 
 _lib = None
@@ -52,6 +53,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.s6_conv_scan_fwd.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32, vp, vp, vp, i32] + [vp] * 9
     lib.s6_conv_state_update.restype = i32
     lib.s6_conv_state_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32] + [vp] * 7
+    lib.s6_scan_fwd_ckpt.restype = i32
+    lib.s6_scan_fwd_ckpt.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32] + [vp] * 10
+    lib.s6_scan_bwd_ckpt.restype = i32
+    lib.s6_scan_bwd_ckpt.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32] + [vp] * 18
     lib.s6_scan_bwd.restype = i32
     lib.s6_scan_bwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 19
     lib.s6_scan_bwd_ex.restype = i32
@@ -104,14 +109,22 @@ def _options(delta_bias, delta_softplus, zoh, dim):
     return delta_bias is not None or flags != 0, flags
 
 
+def ckpt_shape(bsz, dim, L, N):
+    """Shape of the checkpoints of a scan: the state entering every
+    S6_CKPT_TOKENS-token block."""
+    return ((L + S6_CKPT_TOKENS - 1) // S6_CKPT_TOKENS, bsz, dim, N)
+
+
 def scan_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, return_last_state=False, y=None,
-             h_last=None, delta_bias=None, delta_softplus=False, zoh=False):
+             h_last=None, delta_bias=None, delta_softplus=False, zoh=False, ckpt=None):
     """Fused selective scan.  x, delta, z: (batch, dim, L); Bm, Cm: (batch, N, L);
     A: (dim, N) fp32; D: (dim,) fp32; h0: (batch, dim, N) fp32.  Inputs x,
     delta, Bm, Cm, z share one dtype (float32 or bfloat16).  Options: the
     step is delta + delta_bias ((dim,) fp32), through softplus if
-    delta_softplus; zoh takes the exact zero-order-hold input term.  Returns
-    y (batch, dim, L) fp32, and h_last (batch, dim, N) fp32 if requested."""
+    delta_softplus; zoh takes the exact zero-order-hold input term.  ckpt:
+    an fp32 tensor of ckpt_shape(...) that receives the state entering every
+    64-token block (for scan_bwd).  Returns y (batch, dim, L) fp32, and h_last
+    (batch, dim, N) fp32 if requested."""
     bsz, dim, L = x.shape
     N = A.shape[1]
     dt = x.dtype
@@ -132,7 +145,12 @@ def scan_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, return_last_state=Fal
         h_last = torch.empty((bsz, dim, N), dtype=torch.float32, device=x.device)
     _opt(h_last, "h_last", (bsz, dim, N), torch.float32)
     ex, flags = _options(delta_bias, delta_softplus, zoh, dim)
-    if ex:
+    if ckpt is not None:
+        _req(ckpt, "ckpt", ckpt_shape(bsz, dim, L, N), torch.float32)
+        rc = load_library().s6_scan_fwd_ckpt(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(delta_bias),
+                                             flags, _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0),
+                                             _ptr(y), _ptr(h_last), _ptr(ckpt), _stream())
+    elif ex:
         rc = load_library().s6_scan_fwd_ex(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(delta_bias),
                                            flags, _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0),
                                            _ptr(y), _ptr(h_last), _stream())
@@ -283,10 +301,12 @@ def conv_state_update(h, conv_state, x, conv_w, delta, A, Bm, Cm, conv_bias=None
 
 
 def scan_bwd(x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_last=None, delta_bias=None,
-             delta_softplus=False):
+             delta_softplus=False, ckpt=None):
     """Gradients of <dy, y> + <dh_last, h_last> for scan_fwd with the same
     inputs and step options (not zoh).  dy: (batch, dim, L) fp32; dh_last:
-    (batch, dim, N) fp32 or None.  Returns a dict of fp32 tensors: dx, ddelta
+    (batch, dim, N) fp32 or None.  ckpt: the checkpoints scan_fwd wrote for
+    these inputs (then h0 is not read and the states entering the blocks are
+    not recomputed).  Returns a dict of fp32 tensors: dx, ddelta
     (of the stored delta; batch, dim, L), dA (dim, N), dBm, dCm (batch, N, L),
     dh0 (batch, dim, N), and dD (dim,) when D is given, dz (batch, dim, L)
     when z is given, ddelta_bias (dim,) when delta_bias is given."""
@@ -316,6 +336,14 @@ def scan_bwd(x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_last=None, del
     ex, flags = _options(delta_bias, delta_softplus, False, dim)
     if ex:
         g["ddelta_bias"] = torch.empty((dim,), **f)
+    if ckpt is not None:
+        _req(ckpt, "ckpt", ckpt_shape(bsz, dim, L, N), torch.float32)
+        rc = load_library().s6_scan_bwd_ckpt(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(delta_bias), flags,
+                                             _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(ckpt), _ptr(dy),
+                                             _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                                             _ptr(g["dBm"]), _ptr(g["dCm"]), _ptr(g.get("dD")), _ptr(g.get("dz")),
+                                             _ptr(g["dh0"]), _ptr(g.get("ddelta_bias")), _stream())
+    elif ex:
         rc = load_library().s6_scan_bwd_ex(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(delta_bias), flags,
                                            _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy),
                                            _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
@@ -334,20 +362,25 @@ class SelectiveScan(torch.autograd.Function):
     """scan_fwd with its gradients from scan_bwd, for training with torch
     autograd: y = SelectiveScan.apply(x, delta, A, Bm, Cm, D, z, h0,
     delta_bias, delta_softplus).  D, z, h0 and delta_bias may be None.  The
-    forward keeps only its inputs; the backward recomputes the states."""
+    forward keeps its inputs and the state entering every 64-token block
+    (1/64 of the states); the backward recomputes the states inside the
+    blocks."""
 
     @staticmethod
     def forward(ctx, x, delta, A, Bm, Cm, D=None, z=None, h0=None, delta_bias=None, delta_softplus=False):
-        y = scan_fwd(x, delta, A, Bm, Cm, D=D, z=z, h0=h0, delta_bias=delta_bias, delta_softplus=delta_softplus)
-        ctx.save_for_backward(x, delta, A, Bm, Cm, D, z, h0, delta_bias)
+        bsz, dim, L = x.shape
+        ck = torch.empty(ckpt_shape(bsz, dim, L, A.shape[1]), dtype=torch.float32, device=x.device)
+        y = scan_fwd(x, delta, A, Bm, Cm, D=D, z=z, h0=h0, delta_bias=delta_bias, delta_softplus=delta_softplus,
+                     ckpt=ck)
+        ctx.save_for_backward(x, delta, A, Bm, Cm, D, z, h0, delta_bias, ck)
         ctx.delta_softplus = delta_softplus
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        x, delta, A, Bm, Cm, D, z, h0, delta_bias = ctx.saved_tensors
+        x, delta, A, Bm, Cm, D, z, h0, delta_bias, ck = ctx.saved_tensors
         g = scan_bwd(x, delta, A, Bm, Cm, dy.contiguous().to(torch.float32), D=D, z=z, h0=h0,
-                     delta_bias=delta_bias, delta_softplus=ctx.delta_softplus)
+                     delta_bias=delta_bias, delta_softplus=ctx.delta_softplus, ckpt=ck)
         cast = lambda t, like: None if t is None else t.to(like.dtype)  # noqa: E731
         return (cast(g["dx"], x), cast(g["ddelta"], delta), g["dA"], cast(g["dBm"], Bm), cast(g["dCm"], Cm),
                 g.get("dD"), cast(g.get("dz"), x) if z is not None else None,

@@ -48,8 +48,9 @@ def codes():
 
 def test_header_declares_the_entry_points():
     assert header_functions() == ["s6_conv_scan_fwd", "s6_conv_state_update", "s6_last_state", "s6_last_state_ex",
-                                  "s6_scan_bwd", "s6_scan_bwd_ex", "s6_scan_fwd", "s6_scan_fwd_ex",
-                                  "s6_state_update", "s6_state_update_ex", "s6_status_str", "s6_version"]
+                                  "s6_scan_bwd", "s6_scan_bwd_ckpt", "s6_scan_bwd_ex", "s6_scan_fwd",
+                                  "s6_scan_fwd_ckpt", "s6_scan_fwd_ex", "s6_state_update", "s6_state_update_ex",
+                                  "s6_status_str", "s6_version"]
 
 
 def test_every_declared_symbol_is_exported():
@@ -183,6 +184,30 @@ def test_conv_entry_points_validation(lib, codes):
     assert step(h=None) == codes["S6_ERR_NULL"]
     assert step(b=0) == codes["S6_OK"]
     assert step(b=0, width=1, state=None) == codes["S6_OK"]
+
+
+def test_checkpoint_entry_points_validation(lib, codes):
+    """Checkpoints are required when there is work, 4-byte aligned; the
+    other checks are those of the _ex entry points."""
+    assert codes["S6_CKPT_TOKENS"] == 64
+
+    def fwd(ck=P, b=2, L=32, flags=0):
+        return lib.s6_scan_fwd_ckpt(b, 64, L, 16, 1, P, P, None, flags, P, P, P, None, None, None, P, None, ck, None)
+
+    assert fwd(ck=None) == codes["S6_ERR_NULL"]
+    assert fwd(ck=P_ODD) == codes["S6_ERR_ALIGN"]
+    assert fwd(flags=8) == codes["S6_ERR_FLAGS"]
+    assert fwd(ck=None, b=0) == codes["S6_OK"]
+    assert fwd(ck=None, L=0, b=0) == codes["S6_OK"]
+
+    def bwd(ck=P, flags=0, b=2):
+        return lib.s6_scan_bwd_ckpt(b, 64, 32, 16, 1, P, P, None, flags, P, P, P, None, None, ck, P, None, P, P, P, P,
+                                    P, None, None, None, None, None)
+
+    assert bwd(ck=None) == codes["S6_ERR_NULL"]
+    assert bwd(ck=P_ODD) == codes["S6_ERR_ALIGN"]
+    assert bwd(flags=2) == codes["S6_ERR_UNSUPPORTED"]
+    assert bwd(flags=8) == codes["S6_ERR_FLAGS"]
 
 
 def test_backward_validation(lib, codes):

@@ -40,9 +40,11 @@ def _cotangents(w, seed=7):
     return dy, dhl
 
 
-def _check_bwd(oracle, w, with_h0=True, with_dhl=True, use_D=True, mode=None):
+def _check_bwd(oracle, w, with_h0=True, with_dhl=True, use_D=True, mode=None, ckpt=False):
     """mode: None (plain step), "bias" or "softplus" (softplus(delta + bias),
-    with the stored delta 0.5 * N(0, 1) and the workloads' per-channel bias)."""
+    with the stored delta 0.5 * N(0, 1) and the workloads' per-channel bias).
+    ckpt: run the forward with checkpoints first and the backward from them
+    (s6_scan_fwd_ckpt, s6_scan_bwd_ckpt)."""
     from selective_state_space_63_amd import s6
     d, o = problem(w, with_h0)
     if not use_D:
@@ -63,9 +65,13 @@ def _check_bwd(oracle, w, with_h0=True, with_dhl=True, use_D=True, mode=None):
         okw = dict(delta_bias=bias.astype(np.float64), softplus=mode == "softplus")
     dy, dhl = _cotangents(w)
     dhl = dhl if with_dhl else None
-    g = s6.scan_bwd(d["x"], d["delta"], d["A"], d["Bm"], d["Cm"], dev(dy, synth.F32), D=d["D"], z=d["z"],
-                    h0=d["h0"], dh_last=None if dhl is None else dev(dhl, synth.F32), **kw)
     import torch
+    if ckpt:
+        ck = torch.empty(s6.ckpt_shape(w.batch, w.dim, w.seqlen, w.dstate), device="cuda", dtype=torch.float32)
+        s6.scan_fwd(d["x"], d["delta"], d["A"], d["Bm"], d["Cm"], D=d["D"], z=d["z"], h0=d["h0"], ckpt=ck, **kw)
+        kw = dict(kw, ckpt=ck)
+    g = s6.scan_bwd(d["x"], d["delta"], d["A"], d["Bm"], d["Cm"], dev(dy, synth.F32), D=d["D"], z=d["z"],
+                    h0=None if ckpt else d["h0"], dh_last=None if dhl is None else dev(dhl, synth.F32), **kw)
     torch.cuda.synchronize()
     r = oracle.scan_bwd(o["x"], o["delta"], o["A"], o["Bm"], o["Cm"], dy.astype(np.float64), Dskip=o["Dskip"],
                         z=o["z"], h0=o["h0"], dh_last=None if dhl is None else dhl.astype(np.float64), **okw)
@@ -113,6 +119,64 @@ def test_backward_step_options(torch_cuda, oracle, shape, mode):
     w = synth.custom(b, dm, n, L, dt, gate, seed=4400 + L + dm)
     _say(f"[case] backward {mode} {w.name}")
     _check_bwd(oracle, w, mode=mode)
+
+
+@pytest.mark.parametrize("shape", [s for s in SHAPES if s[3] >= 48] + [(1, 64, 16, 64, synth.BF16, True)],
+                         ids=lambda s: "b{}_d{}_n{}_l{}_{}_{}".format(*s))
+def test_backward_from_checkpoints(torch_cuda, oracle, shape):
+    """The forward writes the state entering every 64-token block, the
+    backward starts from those (no checkpoint pass): same gradients."""
+    b, dm, n, L, dt, gate = shape
+    w = synth.custom(b, dm, n, L, dt, gate, seed=4000 + L + dm)
+    _say(f"[case] backward from checkpoints {w.name}")
+    _check_bwd(oracle, w, ckpt=True)
+
+
+@pytest.mark.parametrize("shape", [(2, 65, 16, 100, synth.BF16, True), (1, 32, 16, 5000, synth.BF16, True),
+                                   (3, 33, 16, 129, synth.F32, True)],
+                         ids=lambda s: "b{}_d{}_n{}_l{}_{}_{}".format(*s))
+def test_backward_from_checkpoints_softplus(torch_cuda, oracle, shape):
+    b, dm, n, L, dt, gate = shape
+    w = synth.custom(b, dm, n, L, dt, gate, seed=4400 + L + dm)
+    _say(f"[case] backward from checkpoints softplus {w.name}")
+    _check_bwd(oracle, w, mode="softplus", ckpt=True)
+
+
+@pytest.mark.parametrize("mode", [None, "softplus"])
+@pytest.mark.parametrize("shape", [(1, 16, 4, 256, synth.F32, False), (2, 65, 16, 100, synth.BF16, True),
+                                   (1, 64, 16, 4096, synth.BF16, True), (1, 63, 5, 200, synth.F32, True),
+                                   (2, 96, 16, 128, synth.BF16, True)],
+                         ids=lambda s: "b{}_d{}_n{}_l{}_{}_{}".format(*s))
+def test_forward_checkpoints(torch_cuda, oracle, shape, mode):
+    """The checkpoints are the states before tokens 0, 64, 128, ...
+    (against the oracle's final state of each prefix), and y / h_last do not
+    change when they are written."""
+    import torch
+    from selective_state_space_63_amd import s6
+    b, dm, n, L, dt, gate = shape
+    w = synth.custom(b, dm, n, L, dt, gate, seed=4700 + L + dm)
+    _say(f"[case] forward checkpoints {mode} {w.name}")
+    d, o = problem(w, True)
+    kw, okw = {}, {}
+    if mode == "softplus":
+        bias = np.full(w.dim, -2.0, dtype=np.float32)
+        kw = dict(delta_bias=dev(bias, synth.F32), delta_softplus=True)
+        okw = dict(delta_bias=bias.astype(np.float64), softplus=True)
+    ck = torch.full(s6.ckpt_shape(w.batch, w.dim, w.seqlen, w.dstate), float("nan"), device="cuda")
+    y1, h1 = s6.scan_fwd(d["x"], d["delta"], d["A"], d["Bm"], d["Cm"], D=d["D"], z=d["z"], h0=d["h0"],
+                         return_last_state=True, ckpt=ck, **kw)
+    y2, h2 = s6.scan_fwd(d["x"], d["delta"], d["A"], d["Bm"], d["Cm"], D=d["D"], z=d["z"], h0=d["h0"],
+                         return_last_state=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    got = host64(ck)
+    assert np.array_equal(got[0], o["h0"].astype(np.float64))
+    for s in range(1, got.shape[0]):
+        T = 64 * s
+        pre = {k: (v[..., :T] if k in ("x", "delta", "Bm", "Cm", "z") and v is not None else v) for k, v in o.items()}
+        r = oracle.scan(**pre, **okw)
+        e = scaled(got[s], r["h_last"], r["H_last"])
+        assert e <= TOL[dt], (s, e)
 
 
 def test_backward_without_optional_inputs(torch_cuda, oracle):

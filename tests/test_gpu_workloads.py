@@ -93,7 +93,8 @@ def test_decode_workload_sampled(torch_cuda, oracle):
     print(f"[result] {w.name} max scaled error {worst:.3e}", flush=True)
 
 
-def test_backward_m3b_row(torch_cuda, oracle):
+@pytest.mark.parametrize("ckpt", [False, True], ids=["recompute", "checkpoints"])
+def test_backward_m3b_row(torch_cuda, oracle, ckpt):
     """s6_scan_bwd on the whole 3B layer (as bench.py runs it); batch row 5
     of every per-row gradient (dx, ddelta, dz, dB, dC, dh0) against the
     oracle's backward of that row alone."""
@@ -104,7 +105,12 @@ def test_backward_m3b_row(torch_cuda, oracle):
     gen = torch_cuda.Generator(device="cuda")
     gen.manual_seed(5)
     dy = torch_cuda.randn((w.batch, w.dim, w.seqlen), device="cuda", generator=gen)
-    g = s6.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], dy, D=inp["Dskip"], z=inp["z"])
+    kw = {}
+    if ckpt:  # the forward as bench.py's training line runs it, then the backward from its checkpoints
+        ck = torch_cuda.empty(s6.ckpt_shape(w.batch, w.dim, w.seqlen, w.dstate), device="cuda")
+        s6.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], D=inp["Dskip"], z=inp["z"], ckpt=ck)
+        kw["ckpt"] = ck
+    g = s6.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], dy, D=inp["Dskip"], z=inp["z"], **kw)
     torch_cuda.cuda.synchronize()
     b = 5
     r = oracle.scan_bwd(host64(inp["x"][b:b + 1]), host64(inp["delta"][b:b + 1]), host64(inp["A"]),
