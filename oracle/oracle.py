@@ -187,9 +187,9 @@ class Oracle:
         return xo, xm
 
     def scan_bwd(self, x, delta, A, Bm, Cm, dy, Dskip=None, z=None, h0=None, dh_last=None,
-                 delta_bias=None, softplus=False):
+                 delta_bias=None, softplus=False, zoh=False):
         """Gradients of <dy, y> + <dh_last, h_last> for the scan (with the
-        step bias and softplus of scan(), not the exact hold).  Returns a
+        step bias, softplus and exact hold of scan()).  Returns a
         dict: dx, ddelta (of the stored delta), dz (batch, D, L); dA (D, N);
         dBm, dCm (batch, N, L); dDskip (D,); dh0 (batch, D, N); ddelta_bias
         (D,); and for each the magnitude under the key prefixed with "m"
@@ -215,7 +215,7 @@ class Oracle:
         order = ["dx", "ddelta", "dA", "dBm", "dCm", "dDskip", "dz", "dh0", "ddelta_bias"]
         ptrs = [out[k].ctypes.data_as(_P) for k in order] + [out["m" + k].ctypes.data_as(_P) for k in order]
         bias, bptr = self._in(delta_bias, (D,))
-        rc = self.lib.oracle_scan_bwd_ex(Bsz, D, L, N, args[0], args[1], bptr, self._flags(softplus, False),
+        rc = self.lib.oracle_scan_bwd_ex(Bsz, D, L, N, args[0], args[1], bptr, self._flags(softplus, zoh),
                                          *args[2:], *ptrs)
         if rc == -2:
             raise ValueError("oracle_scan_bwd: unsupported option")

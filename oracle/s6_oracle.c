@@ -276,12 +276,30 @@ int oracle_conv_silu(int64_t Bsz, int64_t D, int64_t L, int64_t K, const double*
  * Nullable: Dskip, z, h0, dh_last (inputs); dDskip, dz, dh0 (outputs); every
  * magnitude output.  Work memory: 4 L N doubles per batch row.
  *
- * oracle_scan_bwd_ex also takes the step bias and ORACLE_DELTA_SOFTPLUS of
- * oracle_scan_ex (not the exact hold: -2): the step is Delta = v or
- * softplus(v), v = delta + bias[d], so ddelta above becomes the gradient of
- * the stored delta, ddelta * dDelta/dv with dsoftplus/dv = 1/(1 + e^-v), and
- * dbias[d] = sum over b, t of that (ddbias, nullable). */
+ * oracle_scan_bwd_ex also takes the options of oracle_scan_ex.  The step is
+ * Delta = v or softplus(v), v = delta + bias[d], so ddelta above becomes the
+ * gradient of the stored delta, ddelta * dDelta/dv with dsoftplus/dv =
+ * 1/(1 + e^-v), and dbias[d] = sum over b, t of that (ddbias, nullable).
+ * With ORACLE_ZOH_EXACT the input term is c(Delta, A[n]) B x with the hold's
+ * coefficient c = (e^{Delta A} - 1) / A in place of Delta, so in the sums
+ * above Delta B (dx) and Delta x (dB) take c, the input part of ddelta takes
+ * dc/dDelta = e^{Delta A} = a, and dA gains lambda B x dc/dA. */
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* dc/dA of the hold's coefficient c(dt, a) = (e^{dt a} - 1) / a:
+ * (dt a e^{dt a} - (e^{dt a} - 1)) / a^2 = dt^2 q(dt a) with
+ * q(u) = (u e^u - (e^u - 1)) / u^2 = sum_{k>=0} (k+1) u^k / (k+2)!, q(0) = 1/2.
+ * The difference cancels for small |u|, so there the series (7 terms: the
+ * next one is below 1e-18 for |u| < 1e-2) is summed instead. */
+static double zoh_dcoef_da(double dt, double a) {
+  const double u = dt * a;
+  double q;
+  if (fabs(u) < 1e-2)
+    q = 1.0 / 2 + u * (1.0 / 3 + u * (1.0 / 8 + u * (1.0 / 30 + u * (1.0 / 144 + u * (1.0 / 840 + u / 5760)))));
+  else
+    q = (u * exp(u) - expm1(u)) / (u * u);
+  return dt * dt * q;
+}
 
 int oracle_scan_bwd_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x,
                        const double* delta, const double* dbias, int flags, const double* A,
@@ -291,8 +309,9 @@ int oracle_scan_bwd_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const doubl
                        double* dz, double* dh0, double* ddbias, double* mdx, double* mddelta,
                        double* mdA, double* mdB, double* mdC, double* mdD, double* mdz, double* mdh0,
                        double* mddbias) {
-  if (flags & ~ORACLE_DELTA_SOFTPLUS) return -2;
+  if (flags & ~(ORACLE_DELTA_SOFTPLUS | ORACLE_ZOH_EXACT)) return -2;
   const int sp = (flags & ORACLE_DELTA_SOFTPLUS) != 0;
+  const int zoh = (flags & ORACLE_ZOH_EXACT) != 0;
   double* dA_b = (double*)calloc((size_t)(Bsz * D * N), sizeof(double));
   double* mdA_b = (double*)calloc((size_t)(Bsz * D * N), sizeof(double));
   double* dD_b = (double*)calloc((size_t)(Bsz * D), sizeof(double));
@@ -335,7 +354,7 @@ int oracle_scan_bwd_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const doubl
         const double dt = step_of(delta[p * L + t], dbias, d, flags), xt = x[p * L + t];
         for (int64_t n = 0; n < N; ++n) {
           const double a = exp(dt * Ad[n]);
-          const double bx = dt * Bb[n * L + t] * xt;
+          const double bx = (zoh ? zoh_coef(dt, Ad[n]) : dt) * Bb[n * L + t] * xt;
           hs[(t + 1) * N + n] = a * hs[t * N + n] + bx;
           Hs[(t + 1) * N + n] = a * Hs[t * N + n] + fabs(bx);
         }
@@ -357,15 +376,19 @@ int oracle_scan_bwd_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const doubl
           const double ml = fabs(dyc * Ct) + Lam[n];
           const double hp = hs[t * N + n], Hp = Hs[t * N + n]; /* h_{t-1} */
           const double ht = hs[(t + 1) * N + n], Ht = Hs[(t + 1) * N + n];
-          gx += l * dt * Bt;
-          mgx += ml * fabs(dt * Bt);
-          gd += l * (Ad[n] * a * hp + Bt * xt);
-          mgd += ml * (fabs(Ad[n] * a) * Hp + fabs(Bt * xt));
-          dA_b[p * N + n] += l * dt * a * hp;
-          mdA_b[p * N + n] += ml * fabs(dt * a) * Hp;
-          dBm[b * N * L + n * L + t] += l * dt * xt;
+          /* the input coefficient and its derivatives in the step and in A */
+          const double cf = zoh ? zoh_coef(dt, Ad[n]) : dt;
+          const double cfd = zoh ? a : 1.0;
+          const double cfa = zoh ? zoh_dcoef_da(dt, Ad[n]) : 0.0;
+          gx += l * cf * Bt;
+          mgx += ml * fabs(cf * Bt);
+          gd += l * (Ad[n] * a * hp + cfd * Bt * xt);
+          mgd += ml * (fabs(Ad[n] * a) * Hp + fabs(cfd * Bt * xt));
+          dA_b[p * N + n] += l * dt * a * hp + l * cfa * Bt * xt;
+          mdA_b[p * N + n] += ml * fabs(dt * a) * Hp + ml * fabs(cfa * Bt * xt);
+          dBm[b * N * L + n * L + t] += l * cf * xt;
           dCm[b * N * L + n * L + t] += dyc * ht;
-          if (mdB) mdB[b * N * L + n * L + t] += ml * fabs(dt * xt);
+          if (mdB) mdB[b * N * L + n * L + t] += ml * fabs(cf * xt);
           if (mdC) mdC[b * N * L + n * L + t] += fabs(dyc) * Ht;
           yc += Ct * ht;
           myc += fabs(Ct) * Ht;

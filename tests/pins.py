@@ -489,11 +489,13 @@ def _bwd(o, p, dy, dhl):
                       h0=p.get("h0"), dh_last=dhl)
 
 
-def brute_force_loss(p, dy, dhl, dps=50, bias=None, softplus=False):
+def brute_force_loss(p, dy, dhl, dps=50, bias=None, softplus=False, zoh=False):
     """<dy, y> + <dh_last, h_last> in multi-digit arithmetic from the
     materialised form (exponentials of sums of Delta, as in brute_force_y),
     returned as an mpmath number.  With bias / softplus the step is
-    delta + bias[d], or ln(1 + e^(delta + bias[d])) from the definition."""
+    delta + bias[d], or ln(1 + e^(delta + bias[d])) from the definition;
+    zoh: token s enters with the hold's integral of e^(rA) over r in
+    [0, Delta_s], (e^(Delta_s A) - 1) / A, in place of Delta_s."""
     import mpmath as mp
     mp.mp.dps = dps
     f = lambda v: mp.mpf(v) if not isinstance(v, mp.mpf) else v  # noqa: E731
@@ -517,7 +519,9 @@ def brute_force_loss(p, dy, dhl, dps=50, bias=None, softplus=False):
                     tt = L - 1 if last else t
                     hn = mp.mpf(0)
                     for s in range(tt + 1):
-                        hn += mp.exp(An * (cum[tt + 1] - cum[s + 1])) * f(dl[b, d, s]) * f(Bm[b, n, s]) * f(x[b, d, s])
+                        cs = (mp.expm1(An * f(dl[b, d, s])) / An if An != 0 else f(dl[b, d, s])) if zoh \
+                            else f(dl[b, d, s])
+                        hn += mp.exp(An * (cum[tt + 1] - cum[s + 1])) * cs * f(Bm[b, n, s]) * f(x[b, d, s])
                     if p.get("h0") is not None:
                         hn += mp.exp(An * cum[tt + 1]) * f(p["h0"][b, d, n])
                     if last:
@@ -711,6 +715,99 @@ def pin_bwd_options_elementwise_fd(o):
             assert np.all(err < 1e-6), (softplus, key, np.max(err))
 
 
+def pin_bwd_zoh_directional_brute_force(o):
+    """The backward with the exact hold (and softplus with a bias) against a
+    directional derivative of the 50-digit materialised loss whose input
+    coefficient is (e^(Delta A) - 1) / A: every gradient, including dA
+    (through the coefficient) and the stored delta."""
+    import mpmath as mp
+    p, dy, dhl = _bwd_problem(131, Bsz=2, D=2, L=6, N=3)
+    g = _rng(132)
+    p["delta"] = g.normal(-1.5, 1.0, size=p["delta"].shape)
+    bias = g.normal(0.0, 0.7, size=p["x"].shape[1])
+    r = o.scan_bwd(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], dy, Dskip=p["Dskip"], z=p["z"], h0=p["h0"],
+                   dh_last=dhl, delta_bias=bias, softplus=True, zoh=True)
+    eps = mp.mpf("1e-15")
+    for key, gk in BWD_INPUTS + (("bias", "ddelta_bias"),):
+        base = bias if key == "bias" else p[key]
+        v = g.standard_normal(base.shape)
+        mp.mp.dps = 50
+        plus = np.array([mp.mpf(float(a)) + eps * mp.mpf(float(c)) for a, c in zip(base.ravel(), v.ravel())],
+                        dtype=object).reshape(base.shape)
+        minus = np.array([mp.mpf(float(a)) - eps * mp.mpf(float(c)) for a, c in zip(base.ravel(), v.ravel())],
+                         dtype=object).reshape(base.shape)
+        if key == "bias":
+            fp = brute_force_loss(p, dy, dhl, bias=plus, softplus=True, zoh=True)
+            fm = brute_force_loss(p, dy, dhl, bias=minus, softplus=True, zoh=True)
+        else:
+            fp = brute_force_loss(dict(p, **{key: plus}), dy, dhl, bias=bias, softplus=True, zoh=True)
+            fm = brute_force_loss(dict(p, **{key: minus}), dy, dhl, bias=bias, softplus=True, zoh=True)
+        fd = (fp - fm) / (2 * eps)
+        an = float(np.sum(r[gk] * v))
+        scale = float(np.sum(r["m" + gk] * np.abs(v)))
+        assert abs(float(fd) - an) <= 1e-13 * scale, (key, float(fd), an, scale)
+
+
+def pin_bwd_zoh_elementwise_fd(o):
+    """Every element of the gradients of delta and of A with the exact hold
+    against central differences of the forward oracle, with steps from 1e-4
+    to 0.1 so that Delta A spans both evaluations of dc/dA (its series below
+    |Delta A| = 1e-2 and the closed form above)."""
+    p, dy, dhl = _bwd_problem(133, Bsz=2, D=2, L=5, N=3)
+    g = _rng(134)
+    p["delta"] = np.exp(g.uniform(np.log(1e-4), np.log(0.1), size=p["delta"].shape))
+    r = o.scan_bwd(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], dy, Dskip=p["Dskip"], z=p["z"], h0=p["h0"],
+                   dh_last=dhl, zoh=True)
+    u = np.abs(p["delta"][:, :, :, None] * p["A"][None, :, None, :])
+    assert u.min() < 1e-2 < u.max()
+
+    def loss(q):
+        f = o.scan(**q, zoh=True)
+        return np.sum(dy * f["y"]) + np.sum(dhl * f["h_last"])
+
+    for key, gk, eps in (("delta", "ddelta", 1e-9), ("A", "dA", 1e-7)):
+        base = p[key]
+        fd = np.zeros(base.shape)
+        for idx in np.ndindex(base.shape):
+            bp, bm = base.copy(), base.copy()
+            bp[idx] += eps
+            bm[idx] -= eps
+            fd[idx] = (loss(dict(p, **{key: bp})) - loss(dict(p, **{key: bm}))) / (2 * eps)
+        err = np.abs(fd - r[gk]) / np.maximum(r["m" + gk], 1e-300)
+        assert np.all(err < 1e-5), (key, np.max(err))
+
+
+def pin_bwd_zoh_single_token(o):
+    """One token from a zero state, loss <dh_last, h_last> = sum_n
+    dh_n c(Delta, A_n) B_n x: the gradients are closed forms in the hold's
+    coefficient c(Delta, A) = (e^(Delta A) - 1) / A and its derivatives,
+    taken here in 50-digit arithmetic (dc/dA by mpmath's numerical
+    differentiation) for Delta A from -1e-5 to -3, across the oracle's switch
+    between the series and the closed form of dc/dA."""
+    import mpmath as mp
+    mp.mp.dps = 50
+    A = -np.array([[1e-5, 3e-4, 2e-3, 9e-3, 1.1e-2, 0.05, 0.4, 3.0]])
+    N = A.shape[1]
+    g = _rng(135)
+    dt, x = 1.0, 0.75
+    Bm = g.standard_normal((1, N, 1))
+    dhl = g.standard_normal((1, 1, N))
+    r = o.scan_bwd(np.array([[[x]]]), np.array([[[dt]]]), A, Bm, np.zeros((1, N, 1)), np.zeros((1, 1, 1)),
+                   dh_last=dhl, zoh=True)
+
+    def c(a, d=mp.mpf(dt)):
+        return mp.expm1(d * a) / a
+
+    dA_want = np.array([float(dhl[0, 0, n] * Bm[0, n, 0] * x * mp.diff(c, mp.mpf(A[0, n]))) for n in range(N)])
+    assert np.allclose(r["dA"][0], dA_want, rtol=1e-13, atol=0), (r["dA"][0], dA_want)
+    ddt_want = sum(float(dhl[0, 0, n] * Bm[0, n, 0] * x * mp.exp(dt * mp.mpf(A[0, n]))) for n in range(N))
+    assert abs(r["ddelta"][0, 0, 0] - ddt_want) <= 1e-13 * r["mddelta"][0, 0, 0]
+    dx_want = sum(float(dhl[0, 0, n] * Bm[0, n, 0] * c(mp.mpf(A[0, n]))) for n in range(N))
+    assert abs(r["dx"][0, 0, 0] - dx_want) <= 1e-13 * r["mdx"][0, 0, 0]
+    dB_want = np.array([float(dhl[0, 0, n] * x * c(mp.mpf(A[0, n]))) for n in range(N)])
+    assert np.allclose(r["dBm"][0, :, 0], dB_want, rtol=1e-13, atol=0)
+
+
 # ------------------------------------------------------ convolution front --
 def _conv_problem(seed, Bsz=2, D=3, L=30, K=4, bias=True, state=True):
     g = _rng(seed)
@@ -839,5 +936,6 @@ PINS = [pin_zero_step_hand, pin_scalar_hand, pin_lti_convolution, pin_step_respo
         pin_softplus_limits, pin_zoh_hand, pin_zoh_limits, pin_options_brute_force,
         pin_bwd_directional_brute_force, pin_bwd_elementwise_fd, pin_bwd_linear_in_cotangent,
         pin_bwd_no_input_coupling, pin_bwd_options_directional_brute_force, pin_bwd_options_elementwise_fd,
+        pin_bwd_zoh_directional_brute_force, pin_bwd_zoh_elementwise_fd, pin_bwd_zoh_single_token,
         pin_conv_hand, pin_conv_numpy, pin_conv_split_resume, pin_conv_magnitude,
         pin_conv_scan_brute_force]

@@ -46,10 +46,11 @@ MUTANTS = [
     # backward
     ("bwd_decay_same_step", [("const double l = dyc * Ct + lam[n];", "const double l = a * (dyc * Ct + lam[n]);")]),
     ("bwd_carry_without_decay", [("lam[n] = a * l; /* carried", "lam[n] = l; /* carried")]),
-    ("bwd_ddelta_no_input_term", [("gd += l * (Ad[n] * a * hp + Bt * xt);", "gd += l * (Ad[n] * a * hp);")]),
-    ("bwd_ddelta_new_state", [("gd += l * (Ad[n] * a * hp + Bt * xt);", "gd += l * (Ad[n] * a * ht + Bt * xt);")]),
-    ("bwd_dA_no_step", [("dA_b[p * N + n] += l * dt * a * hp;", "dA_b[p * N + n] += l * a * hp;")]),
-    ("bwd_dB_no_x", [("dBm[b * N * L + n * L + t] += l * dt * xt;", "dBm[b * N * L + n * L + t] += l * dt;")]),
+    ("bwd_ddelta_no_input_term", [("gd += l * (Ad[n] * a * hp + cfd * Bt * xt);", "gd += l * (Ad[n] * a * hp);")]),
+    ("bwd_ddelta_new_state", [("gd += l * (Ad[n] * a * hp + cfd * Bt * xt);", "gd += l * (Ad[n] * a * ht + cfd * Bt * xt);")]),
+    ("bwd_dA_no_step", [("dA_b[p * N + n] += l * dt * a * hp + l * cfa * Bt * xt;",
+                         "dA_b[p * N + n] += l * a * hp + l * cfa * Bt * xt;")]),
+    ("bwd_dB_no_x", [("dBm[b * N * L + n * L + t] += l * cf * xt;", "dBm[b * N * L + n * L + t] += l * cf;")]),
     ("bwd_dC_prev_state", [("dCm[b * N * L + n * L + t] += dyc * ht;", "dCm[b * N * L + n * L + t] += dyc * hp;")]),
     ("bwd_dz_silu_not_derivative", [("dz[p * L + t] = z ? dy[p * L + t] * yc * dsilu : 0.0;",
                                      "dz[p * L + t] = z ? dy[p * L + t] * yc * g : 0.0;")]),
@@ -57,7 +58,15 @@ MUTANTS = [
     ("bwd_dh_last_ignored", [("lam[n] = dh_last ? dh_last[p * N + n] : 0.0;", "lam[n] = 0.0;")]),
     ("bwd_dx_no_skip", [("dx[p * L + t] = dyc * dsk + gx;", "dx[p * L + t] = gx;")]),
     ("bwd_dD_ungated", [("dD_b[p] += dyc * xt;", "dD_b[p] += dy[p * L + t] * xt;")]),
-    ("bwd_dx_B_of_next_state", [("gx += l * dt * Bt;", "gx += l * dt * Bb[((n + 1) % N) * L + t];")]),
+    ("bwd_dx_B_of_next_state", [("gx += l * cf * Bt;", "gx += l * cf * Bb[((n + 1) % N) * L + t];")]),
+    # backward of the exact hold
+    ("bwd_zoh_coef_is_step", [("const double cf = zoh ? zoh_coef(dt, Ad[n]) : dt;", "const double cf = dt;")]),
+    ("bwd_zoh_dstep_is_one", [("const double cfd = zoh ? a : 1.0;", "const double cfd = 1.0;")]),
+    ("bwd_zoh_no_dA_term", [("const double cfa = zoh ? zoh_dcoef_da(dt, Ad[n]) : 0.0;", "const double cfa = 0.0;")]),
+    ("bwd_zoh_dA_sign", [("q = (u * exp(u) - expm1(u)) / (u * u);", "q = (expm1(u) - u * exp(u)) / (u * u);")]),
+    ("bwd_zoh_series_term", [("(1.0 / 3 + u * (1.0 / 8", "(1.0 / 6 + u * (1.0 / 8")]),
+    ("bwd_zoh_forward_plain", [("const double bx = (zoh ? zoh_coef(dt, Ad[n]) : dt) * Bb[n * L + t] * xt;",
+                                "const double bx = dt * Bb[n * L + t] * xt;")]),
     ("bwd_softplus_chain_missing", [("const double js = sp ? sigmoid(v) : 1.0;", "const double js = 1.0;")]),
     ("bwd_softplus_chain_of_step", [("const double js = sp ? sigmoid(v) : 1.0;", "const double js = sp ? sigmoid(dt) : 1.0;")]),
     ("bwd_bias_grad_dropped", [("db_b[p] += gd * js;", "db_b[p] += 0.0 * gd * js;")]),
