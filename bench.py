@@ -111,7 +111,7 @@ def bwd_valu_slots(w):
     return w.batch * w.dim * w.seqlen * (13 * w.dstate + 16)
 
 
-def bench_backward(w, steps=10, warmup=3, softplus=False, ckpt=False):
+def bench_backward(w, steps=10, warmup=3, softplus=False, ckpt=False, zoh=False):
     """Times s6_scan_bwd on workload w (dy random, no dh_last); softplus:
     with the softplus step and a bias of -4 per channel; ckpt: from the
     checkpoints of one forward with checkpoints (s6_scan_bwd_ckpt), not
@@ -123,6 +123,8 @@ def bench_backward(w, steps=10, warmup=3, softplus=False, ckpt=False):
     opts = {}
     if softplus:
         opts = dict(delta_bias=torch.full((w.dim,), -4.0, device="cuda", dtype=torch.float32), delta_softplus=True)
+    if zoh:
+        opts["zoh"] = True
 
     if ckpt:
         ck = torch.empty(s6.ckpt_shape(w.batch, w.dim, w.seqlen, w.dstate), device="cuda", dtype=torch.float32)
@@ -638,6 +640,9 @@ def main():
         torch.cuda.empty_cache()
         out["backward_softplus"] = bench_backward(w, softplus=True)
         out["backward_softplus"]["note"] = "s6_scan_bwd_ex with the softplus step and a bias (gradient of the bias too)"
+        torch.cuda.empty_cache()
+        out["backward_softplus_zoh"] = bench_backward(w, softplus=True, zoh=True)
+        out["backward_softplus_zoh"]["note"] = "s6_scan_bwd_ex with the softplus step, a bias and the exact hold"
         torch.cuda.empty_cache()
         print(f"[bench] backward {wl.name}", file=sys.stderr, flush=True)
         out["backward_long"] = bench_backward(wl, steps=3, warmup=2)

@@ -212,12 +212,15 @@ int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
                 const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm, float* dCm,
                 float* dDskip, float* dz, float* dh0, void* stream);
 
-/* s6_scan_bwd with the step bias and S6_DELTA_SOFTPLUS of s6_scan_fwd_ex
- * (S6_ZOH_EXACT: S6_ERR_UNSUPPORTED; other bits: S6_ERR_FLAGS).  ddelta is
- * then the gradient of the stored delta (the step's gradient times
- * dstep/dv, v = delta + delta_bias[d], 1/(1 + e^-v) under softplus), and
- * ddelta_bias (nullable, (dim) fp32) receives its sum over batch rows and
- * tokens.  flags = 0 with both bias pointers NULL is s6_scan_bwd. */
+/* s6_scan_bwd with the step bias and the options of s6_scan_fwd_ex (other
+ * flag bits: S6_ERR_FLAGS).  ddelta is then the gradient of the stored delta
+ * (the step's gradient times dstep/dv, v = delta + delta_bias[d],
+ * 1/(1 + e^-v) under softplus), and ddelta_bias (nullable, (dim) fp32)
+ * receives its sum over batch rows and tokens.  With S6_ZOH_EXACT the input
+ * term's coefficient c = (exp(s*A) - 1) / A enters the gradients: dx and dBm
+ * take c where the plain step has s, ddelta's input part takes dc/ds =
+ * exp(s*A), and dA gains the term of dc/dA (a series where |s*A| < 1/2).
+ * flags = 0 with both bias pointers NULL is s6_scan_bwd. */
 int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                    const void* x, const void* delta, const float* delta_bias, int flags, const float* A,
                    const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,

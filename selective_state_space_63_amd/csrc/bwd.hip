@@ -55,6 +55,28 @@ __device__ __forceinline__ float bwd_step(float raw, float bias, bool softplus, 
   return softplus_f(v);
 }
 
+// Input factor of one state's input term under the exact hold: c x with the
+// hold's coefficient c (zoh_coef) from the transition e = 2^arg the caller
+// computed; x is the token's input.
+__device__ __forceinline__ float zoh_input(float dl, float x, float arg, float e) { return zoh_coef(dl, arg, e) * x; }
+
+// dc/dA of the hold's coefficient c = (e^u - 1) / A, u = dl A (e = e^u):
+// (u e^u - (e^u - 1)) / A^2 = dl^2 q(u) with q(u) = sum_{k>=0} (k+1) u^k /
+// (k+2)!.  The difference cancels for small |u|, so below |u| = 1/2 the
+// series is summed (8 terms: the next is below 1e-8 relative); q(0) = 1/2.
+__device__ __forceinline__ float zoh_dcoef_da(float dl, float u, float e) {
+  float qs = 1.0f / 45360;
+  qs = __builtin_fmaf(qs, u, 1.0f / 5760);
+  qs = __builtin_fmaf(qs, u, 1.0f / 840);
+  qs = __builtin_fmaf(qs, u, 1.0f / 144);
+  qs = __builtin_fmaf(qs, u, 1.0f / 30);
+  qs = __builtin_fmaf(qs, u, 1.0f / 8);
+  qs = __builtin_fmaf(qs, u, 1.0f / 3);
+  qs = __builtin_fmaf(qs, u, 0.5f);
+  const float qd = __builtin_fmaf(u, e, 1.0f - e) * fast_rcp(u * u);
+  return dl * dl * (fabsf(u) < 0.5f ? qs : qd);
+}
+
 struct BwdArgs {
   const void* x;
   const void* delta;
@@ -80,6 +102,7 @@ struct BwdArgs {
   float* carry_SD;        // (G, batch*D): summed delta of each part
   const float* dbias;     // SP kernels: (D) step bias or null
   int softplus;           // SP kernels: step = softplus(delta + dbias)
+  int zoh;                // exact zero-order-hold input coefficient (OPT 2 kernels)
   float* ddbias_part;     // SP kernels: (G, batch, D) gradient of the bias, or null
   int64_t batch, D, L, N, nseg;
   int64_t seg_per_part;   // segments per part (the sequence is cut into G parts, blockIdx.y)
@@ -122,8 +145,14 @@ __device__ __forceinline__ float rows_sum4(const float (&v)[4]) {
 
 // SP: the step bias / softplus options (the gradient of the stored delta
 // gets the factor dstep/dv; the bias gradient is summed per channel).
-template <typename In, bool GATE, int SPL, bool SP>
+// OPT: 0 plain; 1 step bias / softplus; 2 those and the exact hold, whose
+// input coefficient c = (e^{delta A} - 1) / A replaces delta in the input
+// term: dx and dB take c, the input part of ddelta takes dc/ddelta = e^{delta
+// A}, and dA gains lambda B x dc/dA.
+template <typename In, bool GATE, int SPL, int OPT>
 __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a) {
+  constexpr bool SP = OPT >= 1;
+  constexpr bool ZOH = OPT == 2;
   constexpr int WB = bwd_waves<SPL>();
   constexpr int NTHR = 64 * WB;
   constexpr int CW = 4 * WB;         // channels per workgroup
@@ -186,9 +215,12 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
   float dD = 0.0f, dbias = 0.0f;
 
   // delta * x of 4 tokens of this lane's channel from LDS (formed from delta
-  // and x in SP kernels, whose fifth tile holds dstep/dv instead)
+  // and x in SP kernels, whose fifth tile holds dstep/dv instead; x itself
+  // in the exact-hold kernels)
   auto load_u4 = [&](int t, const float4& dl4) {
-    if constexpr (SP) {
+    if constexpr (ZOH) {
+      return *reinterpret_cast<const float4*>(sx + c * KP + t);  // x: the coefficient is per state
+    } else if constexpr (SP) {
       const float4 x4 = *reinterpret_cast<const float4*>(sx + c * KP + t);
       return make_float4(dl4.x * x4.x, dl4.y * x4.y, dl4.z * x4.z, dl4.w * x4.w);
     } else {
@@ -263,7 +295,12 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
             const float4 b4 = *reinterpret_cast<const float4*>(sB + (nl * SPL + j) * KP + t);
             const float Bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) h[j] = __builtin_fmaf(fast_exp2(dl[i] * A2[j]), h[j], u[i] * Bv[i]);
+            for (int i = 0; i < 4; ++i) {
+              const float arg = dl[i] * A2[j];
+              const float e = fast_exp2(arg);
+              const float in = ZOH ? zoh_input(dl[i], u[i], arg, e) : u[i];
+              h[j] = __builtin_fmaf(e, h[j], in * Bv[i]);
+            }
           }
         }
       }
@@ -288,8 +325,10 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
           const float Bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            ea[j][4 * g + i] = fast_exp2(dl[i] * A2[j]);
-            hist[j][4 * g + i + 1] = __builtin_fmaf(ea[j][4 * g + i], hist[j][4 * g + i], u[i] * Bv[i]);
+            const float arg = dl[i] * A2[j];
+            ea[j][4 * g + i] = fast_exp2(arg);
+            const float in = ZOH ? zoh_input(dl[i], u[i], arg, ea[j][4 * g + i]) : u[i];
+            hist[j][4 * g + i + 1] = __builtin_fmaf(ea[j][4 * g + i], hist[j][4 * g + i], in * Bv[i]);
           }
         }
       }
@@ -326,12 +365,26 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
             const float lam = __builtin_fmaf(dyc, Cv[j][ii], mu[j]);
             mu[j] = ea[j][i] * lam;
             const float r = lam * (ea[j][i] * hist[j][i]);
-            s1[i] = __builtin_fmaf(lam, Bv[j][ii], s1[i]);
-            s2[i] = __builtin_fmaf(An[j], r, s2[i]);
             s3[i] = __builtin_fmaf(Cv[j][ii], hist[j][i + 1], s3[i]);
-            dA[j] = __builtin_fmaf(dl, r, dA[j]);
-            pb[j][ii] = lam * uu;
             pc[j][ii] = dyc * hist[j][i + 1];
+            if constexpr (ZOH) {
+              // uu is x here: dx sums lambda c B, ddelta lambda (A a h + a B x),
+              // dA lambda (delta a h + B x dc/dA), dB lambda c x
+              const float arg = dl * A2[j];
+              const float cf = zoh_coef(dl, arg, ea[j][i]);
+              const float lb = lam * Bv[j][ii];
+              s1[i] = __builtin_fmaf(lb, cf, s1[i]);
+              s2[i] = __builtin_fmaf(An[j], r, s2[i]);
+              s2[i] = __builtin_fmaf(lb * ea[j][i], uu, s2[i]);
+              dA[j] = __builtin_fmaf(dl, r, dA[j]);
+              dA[j] = __builtin_fmaf(lb * uu, zoh_dcoef_da(dl, arg * kLn2, ea[j][i]), dA[j]);
+              pb[j][ii] = (lam * cf) * uu;
+            } else {
+              s1[i] = __builtin_fmaf(lam, Bv[j][ii], s1[i]);
+              s2[i] = __builtin_fmaf(An[j], r, s2[i]);
+              dA[j] = __builtin_fmaf(dl, r, dA[j]);
+              pb[j][ii] = lam * uu;
+            }
           }
         }
         // the running sums are updated here (left alone, the compiler defers
@@ -360,8 +413,9 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
           const float dyc = sdyc[c * KP + t];
           const int64_t off = (b * D + d) * L + tt;
           dD = __builtin_fmaf(dyc, xv, dD);  // lane nl: the tokens nl mod 16
-          a.dx[off] = __builtin_fmaf(dyc, dsk, dl * k1);
-          float gd = __builtin_fmaf(xv, k1, k2);
+          // (the exact hold's sums already carry the coefficient and x)
+          a.dx[off] = __builtin_fmaf(dyc, dsk, ZOH ? k1 : dl * k1);
+          float gd = ZOH ? k2 : __builtin_fmaf(xv, k1, k2);
           if constexpr (SP) {
             gd *= sjs[c * KP + t];
             dbias += gd;
@@ -577,36 +631,39 @@ __global__ void s6_bwd_reduce_rows(const float* __restrict__ dA_part, const floa
 }
 
 // carry: the part-carry kernel (parts 1 .. G-1) instead of the main kernel.
-template <typename In, bool GATE, int SPL, bool SP>
+template <typename In, bool GATE, int SPL, int OPT>
 int launch_bwd_t(const BwdArgs& a, int64_t parts, bool carry, hipStream_t st) {
   constexpr int CW = 4 * bwd_waves<SPL>();
   const int64_t nblk = (a.D + CW - 1) / CW;
   const dim3 block(64 * bwd_waves<SPL>());
   if (carry) {
     const size_t lds = sizeof(float) * ((size_t)2 * CW * kBwdPitch + (size_t)16 * SPL * kBwdPitch);
-    hipLaunchKernelGGL((s6_bwd_carry_kernel<In, GATE, SPL, SP>),
+    hipLaunchKernelGGL((s6_bwd_carry_kernel<In, GATE, SPL, (OPT >= 1)>),
                        dim3((unsigned)(nblk * a.batch), (unsigned)(parts - 1)), block, lds, st, a);
     S6_HIP(hipGetLastError(), "s6_bwd_carry_kernel launch");
   } else {
-    hipLaunchKernelGGL((s6_bwd_kernel<In, GATE, SPL, SP>), dim3((unsigned)(nblk * a.batch), (unsigned)parts), block,
-                       bwd_lds_bytes<SPL>(SP), st, a);
+    hipLaunchKernelGGL((s6_bwd_kernel<In, GATE, SPL, OPT>), dim3((unsigned)(nblk * a.batch), (unsigned)parts), block,
+                       bwd_lds_bytes<SPL>(OPT >= 1), st, a);
     S6_HIP(hipGetLastError(), "s6_bwd_kernel launch");
   }
   return S6_OK;
 }
 
-template <typename In, int SPL, bool SP>
+template <typename In, int SPL, int OPT>
 int launch_bwd_g(const BwdArgs& a, bool gate, int64_t parts, bool carry, hipStream_t st) {
-  return gate ? launch_bwd_t<In, true, SPL, SP>(a, parts, carry, st)
-              : launch_bwd_t<In, false, SPL, SP>(a, parts, carry, st);
+  return gate ? launch_bwd_t<In, true, SPL, OPT>(a, parts, carry, st)
+              : launch_bwd_t<In, false, SPL, OPT>(a, parts, carry, st);
 }
 
 template <typename In>
 int launch_bwd(const BwdArgs& a, bool gate, int64_t parts, bool carry, hipStream_t st) {
-  const bool sp = a.dbias || a.softplus || a.ddbias_part;
-  if (a.N <= 16)
-    return sp ? launch_bwd_g<In, 1, true>(a, gate, parts, carry, st) : launch_bwd_g<In, 1, false>(a, gate, parts, carry, st);
-  return sp ? launch_bwd_g<In, 2, true>(a, gate, parts, carry, st) : launch_bwd_g<In, 2, false>(a, gate, parts, carry, st);
+  const int opt = a.zoh ? 2 : (a.dbias || a.softplus || a.ddbias_part) ? 1 : 0;
+  if (a.N <= 16) {
+    if (opt == 2) return launch_bwd_g<In, 1, 2>(a, gate, parts, carry, st);
+    return opt ? launch_bwd_g<In, 1, 1>(a, gate, parts, carry, st) : launch_bwd_g<In, 1, 0>(a, gate, parts, carry, st);
+  }
+  if (opt == 2) return launch_bwd_g<In, 2, 2>(a, gate, parts, carry, st);
+  return opt ? launch_bwd_g<In, 2, 1>(a, gate, parts, carry, st) : launch_bwd_g<In, 2, 0>(a, gate, parts, carry, st);
 }
 
 int bwd_channels_per_block(int64_t dstate) { return dstate <= 16 ? 4 * bwd_waves<1>() : 4 * bwd_waves<2>(); }
@@ -632,8 +689,8 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
   int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
   if (rc) return rc;
   if (flags & ~(S6_DELTA_SOFTPLUS | S6_ZOH_EXACT)) return S6_ERR_FLAGS;
-  if (flags & S6_ZOH_EXACT) return S6_ERR_UNSUPPORTED;
   const bool softplus = (flags & S6_DELTA_SOFTPLUS) != 0;
+  const bool zoh = (flags & S6_ZOH_EXACT) != 0;
   const bool work = batch > 0 && dim > 0 && seqlen > 0;
   if (dim > 0 && !dA) return S6_ERR_NULL;
   if (work && (!x || !delta || !A || !Bm || !Cm || !dy || !dx || !ddelta || !dBm || !dCm))
@@ -721,7 +778,7 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
     memset(&g, 0, sizeof(g));
     g.x = x; g.delta = delta; g.Bm = Bm; g.A = A;
     g.hout = agg; g.hout_stride = nstate; g.sumdelta = sd;
-    g.dbias = delta_bias; g.softplus = softplus;
+    g.dbias = delta_bias; g.softplus = softplus; g.zoh = zoh;
     g.D = dim; g.L = seqlen; g.N = dstate; g.seg_len = kBwdSeg;
     rc = launch_scan_any(in_dtype, kModeState, g, p, false, batch, nagg, st);
   }
@@ -736,7 +793,7 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
     b.dy = dy; b.dh_last = dh_last; b.hin = hin;
     b.dx = dx; b.ddelta = ddelta; b.dz = dz; b.dA_part = dap; b.dD_part = ddp;
     b.dB_part = dBp; b.dC_part = dcp; b.dh0 = dh0;
-    b.dbias = delta_bias; b.softplus = softplus; b.ddbias_part = ddelta_bias ? dbp : nullptr;
+    b.dbias = delta_bias; b.softplus = softplus; b.zoh = zoh; b.ddbias_part = ddelta_bias ? dbp : nullptr;
     b.batch = batch; b.D = dim; b.L = seqlen; b.N = dstate; b.nseg = S; b.seg_per_part = spp;
     const bool gate = z != nullptr;
     if (G > 1) {

@@ -301,9 +301,9 @@ def conv_state_update(h, conv_state, x, conv_w, delta, A, Bm, Cm, conv_bias=None
 
 
 def scan_bwd(x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_last=None, delta_bias=None,
-             delta_softplus=False, ckpt=None):
+             delta_softplus=False, ckpt=None, zoh=False):
     """Gradients of <dy, y> + <dh_last, h_last> for scan_fwd with the same
-    inputs and step options (not zoh).  dy: (batch, dim, L) fp32; dh_last:
+    inputs and step options (delta_bias, delta_softplus, zoh).  dy: (batch, dim, L) fp32; dh_last:
     (batch, dim, N) fp32 or None.  ckpt: the checkpoints scan_fwd wrote for
     these inputs (then h0 is not read and the states entering the blocks are
     not recomputed).  Returns a dict of fp32 tensors: dx, ddelta
@@ -333,8 +333,8 @@ def scan_bwd(x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_last=None, del
         g["dD"] = torch.empty((dim,), **f)
     if z is not None:
         g["dz"] = torch.empty((bsz, dim, L), **f)
-    ex, flags = _options(delta_bias, delta_softplus, False, dim)
-    if ex:
+    ex, flags = _options(delta_bias, delta_softplus, zoh, dim)
+    if delta_bias is not None:
         g["ddelta_bias"] = torch.empty((dim,), **f)
     if ckpt is not None:
         _req(ckpt, "ckpt", ckpt_shape(bsz, dim, L, N), torch.float32)
@@ -348,7 +348,7 @@ def scan_bwd(x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_last=None, del
                                            _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy),
                                            _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
                                            _ptr(g["dBm"]), _ptr(g["dCm"]), _ptr(g.get("dD")), _ptr(g.get("dz")),
-                                           _ptr(g["dh0"]), _ptr(g["ddelta_bias"]), _stream())
+                                           _ptr(g["dh0"]), _ptr(g.get("ddelta_bias")), _stream())
     else:
         rc = load_library().s6_scan_bwd(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
                                         _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(g["dx"]),
@@ -361,27 +361,29 @@ def scan_bwd(x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_last=None, del
 class SelectiveScan(torch.autograd.Function):
     """scan_fwd with its gradients from scan_bwd, for training with torch
     autograd: y = SelectiveScan.apply(x, delta, A, Bm, Cm, D, z, h0,
-    delta_bias, delta_softplus).  D, z, h0 and delta_bias may be None.  The
+    delta_bias, delta_softplus, zoh).  D, z, h0 and delta_bias may be None.  The
     forward keeps its inputs and the state entering every 64-token block
     (1/64 of the states); the backward recomputes the states inside the
     blocks."""
 
     @staticmethod
-    def forward(ctx, x, delta, A, Bm, Cm, D=None, z=None, h0=None, delta_bias=None, delta_softplus=False):
+    def forward(ctx, x, delta, A, Bm, Cm, D=None, z=None, h0=None, delta_bias=None, delta_softplus=False,
+                zoh=False):
         bsz, dim, L = x.shape
         ck = torch.empty(ckpt_shape(bsz, dim, L, A.shape[1]), dtype=torch.float32, device=x.device)
         y = scan_fwd(x, delta, A, Bm, Cm, D=D, z=z, h0=h0, delta_bias=delta_bias, delta_softplus=delta_softplus,
-                     ckpt=ck)
+                     zoh=zoh, ckpt=ck)
         ctx.save_for_backward(x, delta, A, Bm, Cm, D, z, h0, delta_bias, ck)
         ctx.delta_softplus = delta_softplus
+        ctx.zoh = zoh
         return y
 
     @staticmethod
     def backward(ctx, dy):
         x, delta, A, Bm, Cm, D, z, h0, delta_bias, ck = ctx.saved_tensors
         g = scan_bwd(x, delta, A, Bm, Cm, dy.contiguous().to(torch.float32), D=D, z=z, h0=h0,
-                     delta_bias=delta_bias, delta_softplus=ctx.delta_softplus, ckpt=ck)
+                     delta_bias=delta_bias, delta_softplus=ctx.delta_softplus, ckpt=ck, zoh=ctx.zoh)
         cast = lambda t, like: None if t is None else t.to(like.dtype)  # noqa: E731
         return (cast(g["dx"], x), cast(g["ddelta"], delta), g["dA"], cast(g["dBm"], Bm), cast(g["dCm"], Cm),
                 g.get("dD"), cast(g.get("dz"), x) if z is not None else None,
-                g["dh0"] if h0 is not None else None, g.get("ddelta_bias"), None)
+                g["dh0"] if h0 is not None else None, g.get("ddelta_bias"), None, None)

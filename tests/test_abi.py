@@ -206,7 +206,6 @@ def test_checkpoint_entry_points_validation(lib, codes):
 
     assert bwd(ck=None) == codes["S6_ERR_NULL"]
     assert bwd(ck=P_ODD) == codes["S6_ERR_ALIGN"]
-    assert bwd(flags=2) == codes["S6_ERR_UNSUPPORTED"]
     assert bwd(flags=8) == codes["S6_ERR_FLAGS"]
 
 
@@ -229,12 +228,13 @@ def test_backward_validation(lib, codes):
     assert bwd(d=0, dA=None) == codes["S6_OK"]  # no channels: nothing to write
     g = lib.s6_scan_bwd_ex
 
-    def bwd_ex(flags=1, bias=P, dbias=P):
-        return g(2, 64, 32, 16, 1, P, P, bias, flags, P, P, P, None, None, None, P, None, P, P, P, P, P, None, None,
+    def bwd_ex(flags=1, bias=P, dbias=P, d=64):
+        return g(2, d, 32, 16, 1, P, P, bias, flags, P, P, P, None, None, None, P, None, P, P, P, P, P, None, None,
                  None, dbias, None)
 
-    assert bwd_ex(flags=2) == codes["S6_ERR_UNSUPPORTED"]  # exact hold: forward only
-    assert bwd_ex(flags=3) == codes["S6_ERR_UNSUPPORTED"]
+    # (dim 0: the checks pass and nothing is launched on these placeholder pointers)
+    assert bwd_ex(flags=2, d=0) == codes["S6_OK"]  # the exact hold has a backward
+    assert bwd_ex(flags=3, d=0) == codes["S6_OK"]
     assert bwd_ex(flags=8) == codes["S6_ERR_FLAGS"]
     assert bwd_ex(bias=P_ODD) == codes["S6_ERR_ALIGN"]
     assert bwd_ex(dbias=P_ODD) == codes["S6_ERR_ALIGN"]

@@ -42,7 +42,8 @@ def _cotangents(w, seed=7):
 
 def _check_bwd(oracle, w, with_h0=True, with_dhl=True, use_D=True, mode=None, ckpt=False):
     """mode: None (plain step), "bias" or "softplus" (softplus(delta + bias),
-    with the stored delta 0.5 * N(0, 1) and the workloads' per-channel bias).
+    with the stored delta 0.5 * N(0, 1) and the workloads' per-channel bias),
+    "zoh" (the exact hold) or "softplus_zoh" (both).
     ckpt: run the forward with checkpoints first and the backward from them
     (s6_scan_fwd_ckpt, s6_scan_bwd_ckpt)."""
     from selective_state_space_63_amd import s6
@@ -51,9 +52,12 @@ def _check_bwd(oracle, w, with_h0=True, with_dhl=True, use_D=True, mode=None, ck
         d["D"] = None
         o["Dskip"] = None
     kw, okw = {}, {}
-    if mode is not None:
+    zoh = mode is not None and mode.endswith("zoh")
+    if mode == "zoh":
+        kw, okw = dict(zoh=True), dict(zoh=True)
+    elif mode is not None:
         g0 = np.random.default_rng(w.seed + 9)
-        if mode == "softplus":
+        if mode.startswith("softplus"):
             u = np.exp(g0.uniform(np.log(1e-3), np.log(0.1), size=w.dim))
             bias = np.log(np.expm1(u)).astype(np.float32)
             raw = synth.encode(0.5 * g0.standard_normal((w.batch, w.dim, w.seqlen)), w.dtype)
@@ -61,8 +65,9 @@ def _check_bwd(oracle, w, with_h0=True, with_dhl=True, use_D=True, mode=None, ck
             o["delta"] = synth.decode(raw, w.dtype)
         else:
             bias = (0.004 * (1 + np.arange(w.dim) % 3)).astype(np.float32)
-        kw = dict(delta_bias=dev(bias, synth.F32), delta_softplus=mode == "softplus")
-        okw = dict(delta_bias=bias.astype(np.float64), softplus=mode == "softplus")
+        sp = mode.startswith("softplus")
+        kw = dict(delta_bias=dev(bias, synth.F32), delta_softplus=sp, zoh=zoh)
+        okw = dict(delta_bias=bias.astype(np.float64), softplus=sp, zoh=zoh)
     dy, dhl = _cotangents(w)
     dhl = dhl if with_dhl else None
     import torch
@@ -109,10 +114,10 @@ def test_backward_small(torch_cuda, oracle, shape):
     _check_bwd(oracle, w)
 
 
-@pytest.mark.parametrize("mode", ["bias", "softplus"])
+@pytest.mark.parametrize("mode", ["bias", "softplus", "zoh", "softplus_zoh"])
 @pytest.mark.parametrize("shape", [(1, 16, 4, 256, synth.F32, False), (2, 65, 16, 100, synth.BF16, True),
                                    (1, 32, 16, 5000, synth.BF16, True), (2, 40, 32, 48, synth.BF16, True),
-                                   (3, 33, 16, 129, synth.F32, True)],
+                                   (3, 33, 16, 129, synth.F32, True), (1, 63, 5, 65, synth.F32, True)],
                          ids=lambda s: "b{}_d{}_n{}_l{}_{}_{}".format(*s))
 def test_backward_step_options(torch_cuda, oracle, shape, mode):
     b, dm, n, L, dt, gate = shape
@@ -221,6 +226,12 @@ def test_backward_m130_full(torch_cuda, oracle):
     w = synth.WORKLOADS["m130"]
     _say(f"[case] backward {w.name}")
     _check_bwd(oracle, w, with_h0=False, with_dhl=False)
+
+
+def test_backward_zoh_from_checkpoints(torch_cuda, oracle):
+    w = synth.custom(2, 65, 16, 300, synth.BF16, True, seed=4500)
+    _say(f"[case] backward softplus + exact hold from checkpoints {w.name}")
+    _check_bwd(oracle, w, mode="softplus_zoh", ckpt=True)
 
 
 def test_autograd_function(torch_cuda, oracle):
