@@ -35,6 +35,17 @@ struct StepArgs {
   int64_t batch, D, N;
 };
 
+// Value of lane g of this lane's quad (DPP quad broadcast; g is a constant
+// once the caller's loop is unrolled).
+__device__ __forceinline__ float quad_bcast(float v, int g) {
+  switch (g) {
+    case 0: return dpp_f<0x00>(v);
+    case 1: return dpp_f<0x55>(v);
+    case 2: return dpp_f<0xAA>(v);
+    default: return dpp_f<0xFF>(v);
+  }
+}
+
 // P lanes per channel, SPL states per lane (lane q: states q*SPL ...), G
 // batch rows per lane (the same channel d of rows b0 .. b0+G-1, so the row of
 // A is read once).  All G rows' loads are issued before any arithmetic.
@@ -81,6 +92,20 @@ __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
   const float dsk = (a.Dskip && valid) ? a.Dskip[d] : 0.0f;
   const float dbias = (EXT && a.dbias && valid) ? a.dbias[d] : 0.0f;
 
+  // With as many rows as lanes per channel (P = G = 4), lane q loads row
+  // b0 + q's x, delta (and z) and the quad shares them by DPP broadcasts: one
+  // 2-byte load per tensor instead of four, which matters when the step's
+  // inputs come cold from HBM.
+  constexpr bool QS = P == 4 && G == 4;
+  float xq = 0.0f, dq = 0.0f, zq = 0.0f;
+  if constexpr (QS) {
+    const int64_t bq = b0 + q;
+    const int64_t chq = (valid && bq < a.batch) ? bq * D + d : 0;
+    dq = to_f32(dp[chq]);
+    xq = to_f32(xp[chq]);
+    if constexpr (GATE) zq = to_f32(zp[chq]);
+  }
+
   // loads of all G rows
   bool vb[G];
   float hv[G][SPL], dt[G], xt[G];
@@ -91,8 +116,13 @@ __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
     vb[g] = valid && b < a.batch;
     const int64_t ch = vb[g] ? b * D + d : 0;  // invalid rows read row 0 and store nothing
     const int64_t bb = vb[g] ? b : 0;
-    dt[g] = to_f32(dp[ch]);
-    xt[g] = to_f32(xp[ch]);
+    if constexpr (QS) {
+      dt[g] = quad_bcast(dq, g);
+      xt[g] = quad_bcast(xq, g);
+    } else {
+      dt[g] = to_f32(dp[ch]);
+      xt[g] = to_f32(xp[ch]);
+    }
     const float* hrow = a.h + ch * N + n0;
     if constexpr (VEC) {
 #pragma unroll
@@ -196,9 +226,10 @@ __global__ void __launch_bounds__(256) s6_step_kernel(StepArgs a) {
       yp += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yp), 0xB1, 0xf, 0xf, false));
     if constexpr (P >= 4)
       yp += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yp), 0x4E, 0xf, 0xf, false));
+    const float zg = (GATE && QS) ? quad_bcast(zq, g) : 0.0f;
     if (vb[g] && q == 0) {
       float yv = __builtin_fmaf(dsk, xt[g], yp);
-      if constexpr (GATE) yv *= silu(to_f32(zp[ch]));
+      if constexpr (GATE) yv *= silu(QS ? zg : to_f32(zp[ch]));
       a.y[ch] = yv;
     }
   }
