@@ -73,6 +73,10 @@ class Oracle:
         self.lib.oracle_step_xm.restype = None
         self.lib.oracle_conv_silu.argtypes = [_I, _I, _I, _I] + [_P] * 6
         self.lib.oracle_conv_silu.restype = ctypes.c_int
+        self.lib.oracle_conv_silu_bwd.argtypes = [_I, _I, _I, _I] + [_P] * 14
+        self.lib.oracle_conv_silu_bwd.restype = ctypes.c_int
+        self.lib.oracle_scan_bwd_xm.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, ctypes.c_int] + [_P] * 26
+        self.lib.oracle_scan_bwd_xm.restype = ctypes.c_int
         self.lib.oracle_num_threads.restype = ctypes.c_int
         self.path = path
 
@@ -186,10 +190,36 @@ class Oracle:
             raise ValueError("conv_silu: width must be >= 1")
         return xo, xm
 
+    def conv_silu_bwd(self, x, w, dxo, mdxo=None, bias=None, state=None):
+        """Gradients through the convolution front from dxo, the gradient
+        with respect to its output (and mdxo, that gradient's magnitude).
+        Returns a dict: dx (batch, D, L), dw (D, K), dbias (D,), dstate
+        (batch, D, K-1), and their magnitudes under the keys prefixed with
+        "m"."""
+        x = np.asarray(x)
+        Bsz, D, L = x.shape
+        K = np.asarray(w).shape[1]
+        keep = []
+        ptrs = []
+        for a, shp in ((x, (Bsz, D, L)), (w, (D, K)), (bias, (D,)), (state, (Bsz, D, K - 1)),
+                       (dxo, (Bsz, D, L)), (mdxo, (Bsz, D, L))):
+            arr, ptr = self._in(a, shp) if a is not None else (None, None)
+            keep.append(arr)
+            ptrs.append(ptr)
+        shapes = {"dx": (Bsz, D, L), "dw": (D, K), "dbias": (D,), "dstate": (Bsz, D, K - 1)}
+        out = {k: np.empty(v) for k, v in shapes.items()}
+        out.update({"m" + k: np.empty(v) for k, v in shapes.items()})
+        order = ["dx", "dw", "dbias", "dstate"]
+        optr = [out[k].ctypes.data_as(_P) for k in order] + [out["m" + k].ctypes.data_as(_P) for k in order]
+        rc = self.lib.oracle_conv_silu_bwd(Bsz, D, L, K, *ptrs, *optr)
+        if rc != 0:
+            raise ValueError(f"conv_silu_bwd failed ({rc})")
+        return out
+
     def scan_bwd(self, x, delta, A, Bm, Cm, dy, Dskip=None, z=None, h0=None, dh_last=None,
-                 delta_bias=None, softplus=False, zoh=False):
+                 delta_bias=None, softplus=False, zoh=False, xmag=None):
         """Gradients of <dy, y> + <dh_last, h_last> for the scan (with the
-        step bias, softplus and exact hold of scan()).  Returns a
+        step bias, softplus and exact hold of scan(); xmag as in scan).  Returns a
         dict: dx, ddelta (of the stored delta), dz (batch, D, L); dA (D, N);
         dBm, dCm (batch, N, L); dDskip (D,); dh0 (batch, D, N); ddelta_bias
         (D,); and for each the magnitude under the key prefixed with "m"
@@ -215,7 +245,8 @@ class Oracle:
         order = ["dx", "ddelta", "dA", "dBm", "dCm", "dDskip", "dz", "dh0", "ddelta_bias"]
         ptrs = [out[k].ctypes.data_as(_P) for k in order] + [out["m" + k].ctypes.data_as(_P) for k in order]
         bias, bptr = self._in(delta_bias, (D,))
-        rc = self.lib.oracle_scan_bwd_ex(Bsz, D, L, N, args[0], args[1], bptr, self._flags(softplus, zoh),
+        xm, xptr = self._in(xmag, (Bsz, D, L))
+        rc = self.lib.oracle_scan_bwd_xm(Bsz, D, L, N, args[0], xptr, args[1], bptr, self._flags(softplus, zoh),
                                          *args[2:], *ptrs)
         if rc == -2:
             raise ValueError("oracle_scan_bwd: unsupported option")

@@ -224,6 +224,29 @@ void oracle_step(int64_t Bsz, int64_t D, int64_t N, double* h, double* H, const 
  * |x'| plus the first-order effect of a rounding of each term of the
  * convolution's sum, SiLU'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z).
  * Returns -1 when K < 1, else 0. */
+/* Input of the filter at token s of pair p: x itself, or before token 0 the
+ * state (oldest first), or 0 without one. */
+static double conv_input(int64_t p, int64_t s, int64_t L, int64_t K, const double* x,
+                         const double* state) {
+  return s >= 0 ? x[p * L + s] : (state ? state[p * (K - 1) + (K - 1) + s] : 0.0);
+}
+
+/* The filter's output xc_t of pair p (channel d) before SiLU; *mag receives
+ * |bias| + sum_k |w x|. */
+static double conv_pre(int64_t p, int64_t d, int64_t t, int64_t L, int64_t K, const double* x,
+                       const double* w, const double* bias, const double* state, double* mag) {
+  double b0 = bias ? bias[d] : 0.0;
+  double acc = b0, m = fabs(b0);
+  for (int64_t k = 0; k < K; ++k) {
+    int64_t s = t - (K - 1) + k;  /* token of tap k */
+    double xs = conv_input(p, s, L, K, x, state);
+    acc += w[d * K + k] * xs;
+    m += fabs(w[d * K + k] * xs);
+  }
+  *mag = m;
+  return acc;
+}
+
 int oracle_conv_silu(int64_t Bsz, int64_t D, int64_t L, int64_t K, const double* x,
                      const double* w, const double* bias, const double* state, double* xo,
                      double* xm) {
@@ -232,20 +255,100 @@ int oracle_conv_silu(int64_t Bsz, int64_t D, int64_t L, int64_t K, const double*
 #pragma omp parallel for schedule(static)
   for (int64_t p = 0; p < pairs; ++p) {
     int64_t d = p % D;
-    double b0 = bias ? bias[d] : 0.0;
     for (int64_t t = 0; t < L; ++t) {
-      double acc = b0, mag = fabs(b0);
-      for (int64_t k = 0; k < K; ++k) {
-        int64_t s = t - (K - 1) + k;  /* token of tap k */
-        double xs = s >= 0 ? x[p * L + s] : (state ? state[p * (K - 1) + (K - 1) + s] : 0.0);
-        acc += w[d * K + k] * xs;
-        mag += fabs(w[d * K + k] * xs);
-      }
+      double mag;
+      double acc = conv_pre(p, d, t, L, K, x, w, bias, state, &mag);
       double sg = 1.0 / (1.0 + exp(-acc));
       xo[p * L + t] = acc * sg;
       if (xm) xm[p * L + t] = fabs(acc * sg) + fabs(sg * (1.0 + acc * (1.0 - sg))) * mag;
     }
   }
+  return 0;
+}
+
+/* Gradients through the convolution front, given the gradient dxo of the
+ * loss with respect to its output x' (the scan backward's dx when the scan
+ * ran on x') and that gradient's magnitude mdxo.  With xc_t the filter's
+ * output before SiLU and dxc_t = dxo_t SiLU'(xc_t):
+ *   dx_s      = sum_k w[d,k] dxc_{s+K-1-k}          (tokens s = 0 .. L-1)
+ *   dstate_s  = the same sum for s = -(K-1) .. -1   (at [b, d, K-1+s])
+ *   dw[d,k]   = sum_{b,t} dxc_t x_{t-K+1+k}         dbias[d] = sum_{b,t} dxc_t
+ * where x_s for s < 0 comes from state (or is 0), and terms with
+ * s+K-1-k >= L are absent.  SiLU'(z) = s (1 + z (1 - s)); SiLU''(z) =
+ * s (1 - s) (2 + z (1 - 2 s)).  Magnitudes: mdxc_t = mdxo_t |SiLU'(xc_t)| +
+ * |dxo_t| |SiLU''(xc_t)| (|bias| + sum_k |w x|) (the second term: a
+ * rounding of the filter's sum moves SiLU'), then the same sums over
+ * absolute values.  dstate, dbias and every magnitude output are nullable;
+ * dw and dbias are summed over rows in order b = 0 .. Bsz-1.  Returns -1
+ * when K < 1, -3 when out of memory. */
+int oracle_conv_silu_bwd(int64_t Bsz, int64_t D, int64_t L, int64_t K, const double* x,
+                         const double* w, const double* bias, const double* state,
+                         const double* dxo, const double* mdxo, double* dx, double* dw,
+                         double* dbias, double* dstate, double* mdx, double* mdw, double* mdbias,
+                         double* mdstate) {
+  if (K < 1) return -1;
+  const int64_t pairs = Bsz * D;
+  double* dxc = (double*)malloc((size_t)(pairs * L) * sizeof(double));
+  double* mdxc = (double*)malloc((size_t)(pairs * L) * sizeof(double));
+  if (!dxc || !mdxc) {
+    free(dxc);
+    free(mdxc);
+    return -3;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t p = 0; p < pairs; ++p) {
+    const int64_t d = p % D;
+    for (int64_t t = 0; t < L; ++t) {
+      double mag;
+      const double acc = conv_pre(p, d, t, L, K, x, w, bias, state, &mag);
+      const double sg = 1.0 / (1.0 + exp(-acc));
+      const double d1 = sg * (1.0 + acc * (1.0 - sg));
+      const double d2 = sg * (1.0 - sg) * (2.0 + acc * (1.0 - 2.0 * sg));
+      dxc[p * L + t] = dxo[p * L + t] * d1;
+      mdxc[p * L + t] = (mdxo ? mdxo[p * L + t] : fabs(dxo[p * L + t])) * fabs(d1) +
+                        fabs(dxo[p * L + t]) * fabs(d2) * mag;
+    }
+    /* token s (s >= -(K-1)) feeds outputs t = s + K - 1 - k through tap k */
+    for (int64_t s = -(K - 1); s < L; ++s) {
+      double g = 0.0, mg = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t t = s + K - 1 - k;
+        if (t < 0 || t >= L) continue;
+        g += w[d * K + k] * dxc[p * L + t];
+        mg += fabs(w[d * K + k]) * mdxc[p * L + t];
+      }
+      if (s >= 0) {
+        dx[p * L + s] = g;
+        if (mdx) mdx[p * L + s] = mg;
+      } else {
+        if (dstate) dstate[p * (K - 1) + (K - 1) + s] = g;
+        if (mdstate) mdstate[p * (K - 1) + (K - 1) + s] = mg;
+      }
+    }
+  }
+  for (int64_t d = 0; d < D; ++d) {
+    for (int64_t k = 0; k <= K; ++k) { /* k == K: the bias */
+      double g = 0.0, mg = 0.0;
+      for (int64_t b = 0; b < Bsz; ++b) {
+        const int64_t p = b * D + d;
+        for (int64_t t = 0; t < L; ++t) {
+          double xs = 1.0;
+          if (k < K) xs = conv_input(p, t + k - (K - 1), L, K, x, state);
+          g += dxc[p * L + t] * xs;
+          mg += mdxc[p * L + t] * fabs(xs);
+        }
+      }
+      if (k < K) {
+        dw[d * K + k] = g;
+        if (mdw) mdw[d * K + k] = mg;
+      } else {
+        if (dbias) dbias[d] = g;
+        if (mdbias) mdbias[d] = mg;
+      }
+    }
+  }
+  free(dxc);
+  free(mdxc);
   return 0;
 }
 
@@ -301,8 +404,9 @@ static double zoh_dcoef_da(double dt, double a) {
   return dt * dt * q;
 }
 
-int oracle_scan_bwd_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x,
-                       const double* delta, const double* dbias, int flags, const double* A,
+int oracle_scan_bwd_xm(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x,
+                       const double* xmag, const double* delta, const double* dbias, int flags,
+                       const double* A,
                        const double* Bm, const double* Cm, const double* Dskip, const double* z,
                        const double* h0, const double* dy, const double* dh_last, double* dx,
                        double* ddelta, double* dA, double* dBm, double* dCm, double* dDskip,
@@ -352,11 +456,12 @@ int oracle_scan_bwd_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const doubl
       }
       for (int64_t t = 0; t < L; ++t) {
         const double dt = step_of(delta[p * L + t], dbias, d, flags), xt = x[p * L + t];
+        const double xm = xmag ? xmag[p * L + t] : fabs(xt);
         for (int64_t n = 0; n < N; ++n) {
           const double a = exp(dt * Ad[n]);
-          const double bx = (zoh ? zoh_coef(dt, Ad[n]) : dt) * Bb[n * L + t] * xt;
-          hs[(t + 1) * N + n] = a * hs[t * N + n] + bx;
-          Hs[(t + 1) * N + n] = a * Hs[t * N + n] + fabs(bx);
+          const double cb = (zoh ? zoh_coef(dt, Ad[n]) : dt) * Bb[n * L + t];
+          hs[(t + 1) * N + n] = a * hs[t * N + n] + cb * xt;
+          Hs[(t + 1) * N + n] = a * Hs[t * N + n] + fabs(cb) * xm;
         }
       }
       /* reverse: adjoints from the last token back */
@@ -366,6 +471,7 @@ int oracle_scan_bwd_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const doubl
       }
       for (int64_t t = L - 1; t >= 0; --t) {
         const double dt = step_of(delta[p * L + t], dbias, d, flags), xt = x[p * L + t];
+        const double xm = xmag ? xmag[p * L + t] : fabs(xt);
         const double g = z ? silu(z[p * L + t]) : 1.0;
         const double dyc = dy[p * L + t] * g;
         double gx = 0.0, mgx = 0.0, gd = 0.0, mgd = 0.0, yc = 0.0, myc = 0.0;
@@ -383,12 +489,12 @@ int oracle_scan_bwd_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const doubl
           gx += l * cf * Bt;
           mgx += ml * fabs(cf * Bt);
           gd += l * (Ad[n] * a * hp + cfd * Bt * xt);
-          mgd += ml * (fabs(Ad[n] * a) * Hp + fabs(cfd * Bt * xt));
+          mgd += ml * (fabs(Ad[n] * a) * Hp + fabs(cfd * Bt) * xm);
           dA_b[p * N + n] += l * dt * a * hp + l * cfa * Bt * xt;
-          mdA_b[p * N + n] += ml * fabs(dt * a) * Hp + ml * fabs(cfa * Bt * xt);
+          mdA_b[p * N + n] += ml * fabs(dt * a) * Hp + ml * fabs(cfa * Bt) * xm;
           dBm[b * N * L + n * L + t] += l * cf * xt;
           dCm[b * N * L + n * L + t] += dyc * ht;
-          if (mdB) mdB[b * N * L + n * L + t] += ml * fabs(cf * xt);
+          if (mdB) mdB[b * N * L + n * L + t] += ml * fabs(cf) * xm;
           if (mdC) mdC[b * N * L + n * L + t] += fabs(dyc) * Ht;
           yc += Ct * ht;
           myc += fabs(Ct) * Ht;
@@ -396,7 +502,7 @@ int oracle_scan_bwd_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const doubl
           Lam[n] = a * ml;
         }
         yc += dsk * xt;
-        myc += fabs(dsk * xt);
+        myc += fabs(dsk) * xm;
         /* chain rule through the step: dDelta/d(stored delta) */
         const double v = dbias ? delta[p * L + t] + dbias[d] : delta[p * L + t];
         const double js = sp ? sigmoid(v) : 1.0;
@@ -407,7 +513,7 @@ int oracle_scan_bwd_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const doubl
         db_b[p] += gd * js;
         mdb_b[p] += mgd * js;
         dD_b[p] += dyc * xt;
-        mdD_b[p] += fabs(dyc * xt);
+        mdD_b[p] += fabs(dyc) * xm;
         if (dz) {
           double zz = z ? z[p * L + t] : 0.0;
           double s = sigmoid(zz);
@@ -457,6 +563,19 @@ int oracle_scan_bwd_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const doubl
   free(db_b);
   free(mdb_b);
   return fail ? -1 : 0;
+}
+
+int oracle_scan_bwd_ex(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x,
+                       const double* delta, const double* dbias, int flags, const double* A,
+                       const double* Bm, const double* Cm, const double* Dskip, const double* z,
+                       const double* h0, const double* dy, const double* dh_last, double* dx,
+                       double* ddelta, double* dA, double* dBm, double* dCm, double* dDskip,
+                       double* dz, double* dh0, double* ddbias, double* mdx, double* mddelta,
+                       double* mdA, double* mdB, double* mdC, double* mdD, double* mdz, double* mdh0,
+                       double* mddbias) {
+  return oracle_scan_bwd_xm(Bsz, D, L, N, x, NULL, delta, dbias, flags, A, Bm, Cm, Dskip, z, h0, dy,
+                            dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, ddbias, mdx, mddelta,
+                            mdA, mdB, mdC, mdD, mdz, mdh0, mddbias);
 }
 
 int oracle_scan_bwd(int64_t Bsz, int64_t D, int64_t L, int64_t N, const double* x,

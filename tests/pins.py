@@ -930,6 +930,114 @@ def pin_conv_scan_brute_force(o):
     assert err < 1e-13, err
 
 
+
+def _conv_chain_loss(o, p, c, dy, dhl):
+    xo, _ = o.conv_silu(**c)
+    f = o.scan(**dict(p, x=xo))
+    return np.sum(dy * f["y"]) + np.sum(dhl * f["h_last"])
+
+
+def _conv_chain_grads(o, p, c, dy, dhl):
+    xo, xm = o.conv_silu(**c)
+    r = o.scan_bwd(xo, p["delta"], p["A"], p["Bm"], p["Cm"], dy, Dskip=p["Dskip"], z=p["z"], h0=p["h0"],
+                   dh_last=dhl, xmag=xm)
+    cb = o.conv_silu_bwd(c["x"], c["w"], r["dx"], mdxo=r["mdx"], bias=c["bias"], state=c["state"])
+    return r, cb
+
+
+def pin_conv_bwd_chain_fd(o):
+    """Gradients through the convolution front and the scan (the oracle's
+    scan backward on the front's output, then the front's backward) against
+    central differences of the composed forward oracle, for every element of
+    x, the filter, the bias and the state."""
+    p, dy, dhl = _bwd_problem(141, Bsz=2, D=2, L=9, N=3)
+    c = _conv_problem(142, Bsz=2, D=2, L=9, K=3)
+    c["x"] = p["x"]
+    r, cb = _conv_chain_grads(o, p, c, dy, dhl)
+    eps = 1e-6
+    for key, gk in (("x", "dx"), ("w", "dw"), ("bias", "dbias"), ("state", "dstate")):
+        base = c[key]
+        fd = np.zeros(base.shape)
+        for idx in np.ndindex(base.shape):
+            bp, bm = base.copy(), base.copy()
+            bp[idx] += eps
+            bm[idx] -= eps
+            fd[idx] = (_conv_chain_loss(o, p, dict(c, **{key: bp}), dy, dhl)
+                       - _conv_chain_loss(o, p, dict(c, **{key: bm}), dy, dhl)) / (2 * eps)
+        err = np.abs(fd - cb[gk]) / np.maximum(cb["m" + gk], 1e-300)
+        assert np.all(err < 1e-6), (key, np.max(err))
+
+
+def pin_conv_bwd_numpy(o):
+    """The front's backward against numpy routines: with dxc = dxo SiLU'(xc)
+    (xc by numpy's convolution), dx and the state's gradient are the full
+    correlation of dxc with the filter, dw the correlation of x (with the
+    state before it) with dxc, dbias the sum of dxc; widths 1..4."""
+    for K in (1, 2, 3, 4):
+        c = _conv_problem(150 + K, Bsz=2, D=3, L=11, K=K)
+        g = _rng(160 + K)
+        dxo = g.standard_normal(c["x"].shape)
+        cb = o.conv_silu_bwd(c["x"], c["w"], dxo, bias=c["bias"], state=c["state"])
+        Bsz, D, L = c["x"].shape
+        st = c["state"] if c["state"] is not None else np.zeros((Bsz, D, K - 1))
+        for b in range(Bsz):
+            for d in range(D):
+                full = np.concatenate([st[b, d], c["x"][b, d]])
+                xc = np.convolve(full, c["w"][d][::-1], mode="valid") + c["bias"][d]
+                s = 1.0 / (1.0 + np.exp(-xc))
+                dxc = dxo[b, d] * s * (1.0 + xc * (1.0 - s))
+                back = np.convolve(dxc, c["w"][d], mode="full")  # gradient of every input of `full`
+                assert np.allclose(cb["dx"][b, d], back[K - 1:], rtol=1e-12, atol=1e-14)
+                if K > 1:
+                    assert np.allclose(cb["dstate"][b, d], back[:K - 1], rtol=1e-12, atol=1e-14)
+        for d in range(D):
+            dw = np.zeros(K)
+            db = 0.0
+            for b in range(Bsz):
+                full = np.concatenate([st[b, d], c["x"][b, d]])
+                xc = np.convolve(full, c["w"][d][::-1], mode="valid") + c["bias"][d]
+                s = 1.0 / (1.0 + np.exp(-xc))
+                dxc = dxo[b, d] * s * (1.0 + xc * (1.0 - s))
+                dw += np.correlate(full, dxc, mode="valid")
+                db += dxc.sum()
+            assert np.allclose(cb["dw"][d], dw, rtol=1e-12, atol=1e-14), (K, d)
+            assert np.isclose(cb["dbias"][d], db, rtol=1e-12, atol=1e-14)
+
+
+def pin_conv_bwd_magnitude(o):
+    """Width 1 and weight 1 make dx = dxc: its magnitude minus mdxo |SiLU'|
+    bounds (and is within 5x of) the change of dxc under relative
+    perturbations of size eps of the filter's terms; with the backward's
+    magnitudes m(2|x'|) for the scan, dB's and dD's magnitudes double."""
+    g = _rng(171)
+    x = g.standard_normal((1, 2, 30)) * 2
+    w = np.ones((2, 1))
+    bias = g.standard_normal(2)
+    dxo = g.standard_normal(x.shape)
+    cb = o.conv_silu_bwd(x, w, dxo, mdxo=np.abs(dxo), bias=bias)
+    xc = x + bias[None, :, None]
+    s = 1.0 / (1.0 + np.exp(-xc))
+    first = np.abs(dxo) * np.abs(s * (1.0 + xc * (1.0 - s)))
+    second = cb["mdx"] - first
+    eps = 1e-7
+    worst = np.zeros(x.shape)
+    for trial in range(40):
+        tx = x * (1 + eps * g.choice([-1.0, 1.0], size=x.shape))
+        tb = bias * (1 + eps * g.choice([-1.0, 1.0], size=bias.shape))
+        pert = o.conv_silu_bwd(tx, w, dxo, bias=tb)["dx"]
+        worst = np.maximum(worst, np.abs(pert - cb["dx"]) / eps)
+    assert np.all(worst <= second * (1 + 1e-3) + 1e-12)
+    assert np.max(worst / np.maximum(second, 1e-300)) >= 0.2
+    q = _rand_problem(172, Bsz=1, D=2, L=15, N=3, h0=False)
+    dy = g.standard_normal(q["x"].shape)
+    r1 = o.scan_bwd(q["x"], q["delta"], q["A"], q["Bm"], q["Cm"], dy, Dskip=q["Dskip"], z=q["z"])
+    r2 = o.scan_bwd(q["x"], q["delta"], q["A"], q["Bm"], q["Cm"], dy, Dskip=q["Dskip"], z=q["z"],
+                    xmag=2 * np.abs(q["x"]))
+    assert np.allclose(r2["mdBm"], 2 * r1["mdBm"], rtol=1e-14, atol=0)
+    assert np.allclose(r2["mdDskip"], 2 * r1["mdDskip"], rtol=1e-14, atol=0)
+    assert np.array_equal(r2["dBm"], r1["dBm"])
+
+
 PINS = [pin_zero_step_hand, pin_scalar_hand, pin_lti_convolution, pin_step_response,
         pin_brute_force, pin_tree_scan, pin_split_resume, pin_linearity_and_permutation,
         pin_gate_limits, pin_decode_equals_scan, pin_magnitude_bounds, pin_softplus_hand,
@@ -938,4 +1046,4 @@ PINS = [pin_zero_step_hand, pin_scalar_hand, pin_lti_convolution, pin_step_respo
         pin_bwd_no_input_coupling, pin_bwd_options_directional_brute_force, pin_bwd_options_elementwise_fd,
         pin_bwd_zoh_directional_brute_force, pin_bwd_zoh_elementwise_fd, pin_bwd_zoh_single_token,
         pin_conv_hand, pin_conv_numpy, pin_conv_split_resume, pin_conv_magnitude,
-        pin_conv_scan_brute_force]
+        pin_conv_scan_brute_force, pin_conv_bwd_chain_fd, pin_conv_bwd_numpy, pin_conv_bwd_magnitude]

@@ -65,14 +65,16 @@ MUTANTS = [
     ("bwd_zoh_no_dA_term", [("const double cfa = zoh ? zoh_dcoef_da(dt, Ad[n]) : 0.0;", "const double cfa = 0.0;")]),
     ("bwd_zoh_dA_sign", [("q = (u * exp(u) - expm1(u)) / (u * u);", "q = (expm1(u) - u * exp(u)) / (u * u);")]),
     ("bwd_zoh_series_term", [("(1.0 / 3 + u * (1.0 / 8", "(1.0 / 6 + u * (1.0 / 8")]),
-    ("bwd_zoh_forward_plain", [("const double bx = (zoh ? zoh_coef(dt, Ad[n]) : dt) * Bb[n * L + t] * xt;",
-                                "const double bx = dt * Bb[n * L + t] * xt;")]),
+    ("bwd_zoh_forward_plain", [("const double cb = (zoh ? zoh_coef(dt, Ad[n]) : dt) * Bb[n * L + t];",
+                                "const double cb = dt * Bb[n * L + t];")]),
     ("bwd_softplus_chain_missing", [("const double js = sp ? sigmoid(v) : 1.0;", "const double js = 1.0;")]),
     ("bwd_softplus_chain_of_step", [("const double js = sp ? sigmoid(v) : 1.0;", "const double js = sp ? sigmoid(dt) : 1.0;")]),
     ("bwd_bias_grad_dropped", [("db_b[p] += gd * js;", "db_b[p] += 0.0 * gd * js;")]),
     ("bwd_reverse_step_without_options", [
-        ("const double dt = step_of(delta[p * L + t], dbias, d, flags), xt = x[p * L + t];\n        const double g",
-         "const double dt = delta[p * L + t], xt = x[p * L + t];\n        const double g")]),
+        ("const double dt = step_of(delta[p * L + t], dbias, d, flags), xt = x[p * L + t];\n"
+         "        const double xm = xmag ? xmag[p * L + t] : fabs(xt);\n        const double g",
+         "const double dt = delta[p * L + t], xt = x[p * L + t];\n"
+         "        const double xm = xmag ? xmag[p * L + t] : fabs(xt);\n        const double g")]),
     ("delta_index_shift", [("double dt = step_of(delta[p * L + t], dbias, d, flags);",
                             "double dt = step_of(delta[p * L + (t > 0 ? t - 1 : 0)], dbias, d, flags);")]),
     ("A_state_index", [("double a = exp(dt * Ad[n]);         /*", "double a = exp(dt * Ad[(n + 1) % N]);         /*")]),
@@ -86,15 +88,24 @@ MUTANTS = [
     ("input_decayed_same_step", [("h[n] = a * h[n] + bx;", "h[n] = a * (h[n] + bx);")]),
     ("magnitude_drops_input", [("H[n] = fabs(a) * H[n] + fabs(cb) * xm;", "H[n] = fabs(a) * H[n];")]),
     # convolution front
-    ("conv_tap_shift", [("int64_t s = t - (K - 1) + k;", "int64_t s = t - K + k;")]),
+    ("conv_tap_shift", [("int64_t s = t - (K - 1) + k;  /* token of tap k */", "int64_t s = t - K + k;")]),
     ("conv_taps_reversed", [("acc += w[d * K + k] * xs;", "acc += w[d * K + (K - 1 - k)] * xs;")]),
     ("conv_weight_channel", [("acc += w[d * K + k] * xs;", "acc += w[k] * xs;")]),
     ("conv_state_ignored", [("(state ? state[p * (K - 1) + (K - 1) + s] : 0.0)", "0.0")]),
-    ("conv_state_order", [("state[p * (K - 1) + (K - 1) + s]", "state[p * (K - 1) - 1 - s]")]),
+    ("conv_state_order", [("? state[p * (K - 1) + (K - 1) + s]", "? state[p * (K - 1) - 1 - s]")]),
     ("conv_bias_dropped", [("double b0 = bias ? bias[d] : 0.0;", "double b0 = 0.0;")]),
     ("conv_no_silu", [("xo[p * L + t] = acc * sg;", "xo[p * L + t] = acc;")]),
     ("scan_xmag_ignored", [("double xm = xmag ? xmag[p * L + t] : fabs(x[p * L + t]);",
                            "double xm = fabs(x[p * L + t]);")]),
+    ("conv_bwd_taps_reversed", [("        g += w[d * K + k] * dxc[p * L + t];", "        g += w[d * K + (K - 1 - k)] * dxc[p * L + t];")]),
+    ("conv_bwd_silu_prime", [("const double d1 = sg * (1.0 + acc * (1.0 - sg));", "const double d1 = sg;")]),
+    ("conv_bwd_dw_shift", [("xs = conv_input(p, t + k - (K - 1), L, K, x, state);",
+                            "xs = conv_input(p, t + k - K, L, K, x, state);")]),
+    ("conv_bwd_state_index", [("if (dstate) dstate[p * (K - 1) + (K - 1) + s] = g;", "if (dstate) dstate[p * (K - 1) - 1 - s] = g;")]),
+    ("conv_bwd_bias_grad", [("          double xs = 1.0;\n", "          double xs = 0.0;\n")]),
+    ("conv_bwd_no_second_derivative", [("fabs(dxo[p * L + t]) * fabs(d2) * mag;", "0.0 * mag;")]),
+    ("scan_bwd_xmag_ignored", [("        const double xm = xmag ? xmag[p * L + t] : fabs(xt);\n        const double g",
+                                "        const double xm = fabs(xt);\n        const double g")]),
     ("conv_magnitude_no_sum", [("fabs(sg * (1.0 + acc * (1.0 - sg))) * mag;", "0.0 * mag;")]),
 ]
 
