@@ -111,7 +111,7 @@ def bwd_valu_slots(w):
     return w.batch * w.dim * w.seqlen * (13 * w.dstate + 16)
 
 
-def bench_backward(w, steps=10, warmup=3, softplus=False, ckpt=False, zoh=False):
+def bench_backward(w, steps=10, warmup=3, softplus=False, ckpt=False, zoh=False, conv_k=0):
     """Times s6_scan_bwd on workload w (dy random, no dh_last); softplus:
     with the softplus step and a bias of -4 per channel; ckpt: from the
     checkpoints of one forward with checkpoints (s6_scan_bwd_ckpt), not
@@ -134,6 +134,14 @@ def bench_backward(w, steps=10, warmup=3, softplus=False, ckpt=False, zoh=False)
 
     def step():
         s6.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], dy, D=inp["Dskip"], z=inp["z"], **opts)
+
+    if conv_k:
+        cw, cb = synth.conv_params(w.dim, conv_k, w.seed)
+        cw, cb = torch.from_numpy(cw).cuda(), torch.from_numpy(cb).cuda()
+
+        def step():  # noqa: F811
+            s6.conv_scan_bwd(inp["x"], cw, inp["delta"], inp["A"], inp["Bm"], inp["Cm"], dy, conv_bias=cb,
+                             D=inp["Dskip"], z=inp["z"], **opts)
 
     for _ in range(warmup):
         step()
@@ -643,6 +651,10 @@ def main():
         torch.cuda.empty_cache()
         out["backward_softplus_zoh"] = bench_backward(w, softplus=True, zoh=True)
         out["backward_softplus_zoh"]["note"] = "s6_scan_bwd_ex with the softplus step, a bias and the exact hold"
+        torch.cuda.empty_cache()
+        out["backward_conv"] = bench_backward(w, conv_k=4)
+        out["backward_conv"]["note"] = ("s6_conv_scan_bwd: the scan's backward on the recomputed filtered input, then "
+                                        "the convolution front's backward (filter, bias and input gradients)")
         torch.cuda.empty_cache()
         print(f"[bench] backward {wl.name}", file=sys.stderr, flush=True)
         out["backward_long"] = bench_backward(wl, steps=3, warmup=2)

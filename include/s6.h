@@ -227,6 +227,29 @@ int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, i
                    const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
                    float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* stream);
 
+/* Gradients of s6_conv_scan_fwd: the scan's gradients as from s6_scan_bwd_ex
+ * (with the same step options), taken on the filtered input x', then carried
+ * back through SiLU and the filter:
+ *   dxc_t = dx'_t SiLU'(xc_t)        (xc: the filter's output before SiLU)
+ *   dx[b,d,s]         = sum_k conv_w[d,k] dxc_{s+K-1-k}  (terms past the end absent)
+ *   dconv_state[b,d,K-1+s] = the same sum for s = -(K-1) .. -1
+ *   dconv_w[d,k]      = sum_{b,t} dxc_t x_{t-K+1+k} (inputs before token 0 from
+ *                       conv_state, or 0)
+ *   dconv_bias[d]     = sum_{b,t} dxc_t
+ * x' is recomputed as the forward computes it (never stored).  dconv_w is
+ * required (dim, conv_width); dconv_bias (dim) and dconv_state (batch, dim,
+ * conv_width - 1) are nullable; every other argument as for s6_scan_bwd_ex
+ * and s6_conv_scan_fwd, except that S6_ZOH_EXACT is not taken here
+ * (S6_ERR_UNSUPPORTED).  Sums over rows and tokens are taken in a fixed
+ * order: repeated calls give identical bits. */
+int s6_conv_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                     const void* x, const float* conv_w, const float* conv_bias, int conv_width,
+                     const float* conv_state, const void* delta, const float* delta_bias, int flags,
+                     const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                     const float* h0, const float* dy, const float* dh_last, float* dx, float* ddelta,
+                     float* dA, float* dBm, float* dCm, float* dDskip, float* dz, float* dh0,
+                     float* ddelta_bias, float* dconv_w, float* dconv_bias, float* dconv_state, void* stream);
+
 /* Checkpoints for training: the forward saves the state entering every
  * S6_CKPT_TOKENS-token block, and the backward starts from them instead of
  * recomputing them.  The pages' guide (§3.4) has the fused scan recompute the

@@ -103,6 +103,10 @@ struct BwdArgs {
   const float* dbias;     // SP kernels: (D) step bias or null
   int softplus;           // SP kernels: step = softplus(delta + dbias)
   int zoh;                // exact zero-order-hold input coefficient (OPT 2 kernels)
+  const float* conv_w;    // SP kernels: the convolution front (as in ScanArgs), or null
+  const float* conv_b;
+  const float* conv_state;
+  int conv_k;
   float* ddbias_part;     // SP kernels: (G, batch, D) gradient of the bias, or null
   int64_t batch, D, L, N, nseg;
   int64_t seg_per_part;   // segments per part (the sequence is cut into G parts, blockIdx.y)
@@ -145,7 +149,8 @@ __device__ __forceinline__ float rows_sum4(const float (&v)[4]) {
 
 // SP: the step bias / softplus options (the gradient of the stored delta
 // gets the factor dstep/dv; the bias gradient is summed per channel).
-// OPT: 0 plain; 1 step bias / softplus; 2 those and the exact hold, whose
+// OPT: 0 plain; 1 step bias / softplus; 3 those and the convolution front;
+// 2 bias / softplus and the exact hold, whose
 // input coefficient c = (e^{delta A} - 1) / A replaces delta in the input
 // term: dx and dB take c, the input part of ddelta takes dc/ddelta = e^{delta
 // A}, and dA gains lambda B x dc/dA.
@@ -153,6 +158,7 @@ template <typename In, bool GATE, int SPL, int OPT>
 __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a) {
   constexpr bool SP = OPT >= 1;
   constexpr bool ZOH = OPT == 2;
+  constexpr bool CONV = OPT == 3;  // the convolution front (its own kernels: it costs registers)
   constexpr int WB = bwd_waves<SPL>();
   constexpr int NTHR = 64 * WB;
   constexpr int CW = 4 * WB;         // channels per workgroup
@@ -267,6 +273,50 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>()) s6_bwd_kernel(BwdArgs a
       sC[n * KP + t] = ok ? to_f32(Cp[off]) : 0.0f;
     }
     __syncthreads();
+    if constexpr (CONV) {
+      // The convolution front's output x' replaces the staged x, as the
+      // forward computes it: 4 consecutive tokens of one channel per thread
+      // from the 3 + 4 raw inputs around them (the 3 before the segment from
+      // memory), read before any thread overwrites its tokens.
+      static_assert(CW * KS == 4 * NTHR, "one group of 4 tokens per thread");
+      const int fcc = tid / (KS / 4), ft4 = (tid % (KS / 4)) * 4;
+      const int K = a.conv_k;
+      float xin[4 + kMaxConv - 1];  // raw inputs at ft4 - (kMaxConv - 1) .. ft4 + 3
+#pragma unroll
+      for (int i = 0; i < 4 + kMaxConv - 1; ++i) {
+        const int t = ft4 - (kMaxConv - 1) + i;
+        float v = 0.0f;
+        if (t >= 0) {
+          v = sx[fcc * KP + t];
+        } else if (fcc < rows_valid) {
+          const int64_t sg = tb + t, rw = b * D + d0 + fcc;
+          if (sg >= 0) v = to_f32(xp[rw * L + sg]);
+          else if (sg >= -(int64_t)(K - 1) && a.conv_state) v = a.conv_state[rw * (K - 1) + (K - 1) + sg];
+        }
+        xin[i] = v;
+      }
+      __syncthreads();  // every raw input is read
+      float xo[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (fcc < rows_valid) {
+        const int64_t ch = d0 + fcc;
+        float wk[kMaxConv];
+#pragma unroll
+        for (int k = 0; k < kMaxConv; ++k) wk[k] = k < K ? a.conv_w[ch * K + k] : 0.0f;
+        const float cbias = a.conv_b ? a.conv_b[ch] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (ft4 + u < tl) {
+            float acc = cbias;
+#pragma unroll
+            for (int j = 0; j < kMaxConv; ++j)
+              if (j < K) acc = __builtin_fmaf(wk[K - 1 - j], xin[(kMaxConv - 1) + u - j], acc);
+            xo[u] = silu(acc);
+          }
+        }
+      }
+      *reinterpret_cast<float4*>(sx + fcc * KP + ft4) = make_float4(xo[0], xo[1], xo[2], xo[3]);
+      __syncthreads();
+    }
 
     // states at the four chunk starts of the segment
     float hc[4][SPL];
@@ -630,6 +680,139 @@ __global__ void s6_bwd_reduce_rows(const float* __restrict__ dA_part, const floa
   }
 }
 
+// Backward through the convolution front.  dxo: the gradient with respect
+// to its output x' (the adjoint kernel's dx when the scan ran on x').  A
+// block of 256 threads covers 2048 tokens of one (batch, channel) row
+// (blockIdx.x = row * nlb + block); thread tid takes tokens tid, tid + 256,
+// ... of the block, so every load is contiguous across the threads.  Each
+// thread recomputes the filter's output xc and dxc = dxo * SiLU'(xc) for its
+// tokens into LDS (the first K - 1 threads also the tokens just past the
+// block), then writes dx_s = sum_k w_k dxc_{s+K-1-k}; the block sums
+// dxc_t x_{t-K+1+k} (filter) and dxc_t (bias) in a fixed tree into
+// part[(b * nlb + block) * D + ch][k]; the row's first block also writes the
+// state's gradient (the same sum for s < 0).
+constexpr int kConvTok = 8;  // tokens per thread
+template <typename In>
+__global__ void __launch_bounds__(256) s6_conv_bwd_kernel(const In* __restrict__ xp, const float* __restrict__ cw,
+                                                          const float* __restrict__ cb,
+                                                          const float* __restrict__ cstate, int K,
+                                                          const float* __restrict__ dxo, float* __restrict__ dx,
+                                                          float* __restrict__ dstate, float* __restrict__ part,
+                                                          int64_t batch, int64_t D, int64_t L, int64_t nlb) {
+  constexpr int TB = 256 * kConvTok;  // tokens per block
+  constexpr int H = kMaxConv - 1;       // halo
+  __shared__ float sdxc[TB + H];
+  __shared__ float sxin[TB + 2 * H];    // inputs at tb0 - H .. tb0 + TB + H - 1
+  __shared__ float red[256 * (kMaxConv + 1)];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x / nlb;
+  const int64_t lb = blockIdx.x % nlb;
+  const int64_t ch = row % D;
+  const int64_t b = row / D;
+  const int64_t tb0 = lb * TB;
+  float wk[kMaxConv];
+#pragma unroll
+  for (int k = 0; k < kMaxConv; ++k) wk[k] = k < K ? cw[ch * K + k] : 0.0f;
+  const float bias = cb ? cb[ch] : 0.0f;
+  for (int i = tid; i < TB + 2 * H; i += 256) {
+    const int64_t sg = tb0 - H + i;
+    float v = 0.0f;
+    if (sg >= 0 && sg < L) v = to_f32(xp[row * L + sg]);
+    else if (sg < 0 && sg >= -(int64_t)(K - 1) && cstate) v = cstate[row * (K - 1) + (K - 1) + sg];
+    sxin[i] = v;
+  }
+  __syncthreads();
+  auto x_at = [&](int64_t s) -> float { return sxin[s - tb0 + H]; };
+  // dxc of token t (0 past the end); xs[j] receives the input j tokens back
+  auto dxc_at = [&](int64_t t, float (&xs)[kMaxConv]) -> float {
+#pragma unroll
+    for (int j = 0; j < kMaxConv; ++j) xs[j] = 0.0f;
+    if (t >= L) return 0.0f;
+    float acc = bias;
+#pragma unroll
+    for (int j = 0; j < kMaxConv; ++j) {
+      if (j < K) {
+        xs[j] = x_at(t - j);
+        acc = __builtin_fmaf(wk[K - 1 - j], xs[j], acc);
+      }
+    }
+    const float sg = fast_rcp(1.0f + fast_exp2(-acc * kLog2e));
+    return dxo[row * L + t] * (sg * __builtin_fmaf(acc, 1.0f - sg, 1.0f));
+  };
+  float pk[kMaxConv + 1];
+#pragma unroll
+  for (int k = 0; k <= kMaxConv; ++k) pk[k] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kConvTok; ++i) {
+    float xs[kMaxConv];
+    const float v = dxc_at(tb0 + i * 256 + tid, xs);
+    sdxc[i * 256 + tid] = v;
+    pk[kMaxConv] += v;
+    // tap k reads the input K - 1 - k tokens back
+#pragma unroll
+    for (int k = 0; k < kMaxConv; ++k)
+      if (k < K) pk[k] = __builtin_fmaf(v, xs[K - 1 - k], pk[k]);
+  }
+  if (tid < K - 1) {
+    float xs[kMaxConv];
+    sdxc[TB + tid] = dxc_at(tb0 + TB + tid, xs);
+  }
+  __syncthreads();
+  // input gradients: token s feeds outputs s + K - 1 - k through tap k
+#pragma unroll
+  for (int i = 0; i < kConvTok; ++i) {
+    const int li = i * 256 + tid;
+    const int64_t s = tb0 + li;
+    if (s < L) {
+      float g = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kMaxConv; ++k)
+        if (k < K) g = __builtin_fmaf(wk[k], sdxc[li + K - 1 - k], g);
+      dx[row * L + s] = g;
+    }
+  }
+  if (dstate && lb == 0 && tid == 0) {
+    for (int s = -(K - 1); s < 0; ++s) {
+      float g = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        const int t = s + K - 1 - k;
+        if (t >= 0) g = __builtin_fmaf(wk[k], sdxc[t], g);
+      }
+      dstate[row * (K - 1) + (K - 1) + s] = g;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k <= kMaxConv; ++k) red[k * 256 + tid] = pk[k];
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) {
+#pragma unroll
+      for (int k = 0; k <= kMaxConv; ++k) red[k * 256 + tid] += red[k * 256 + tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid <= kMaxConv && (tid < K || tid == kMaxConv))
+    part[((b * nlb + lb) * D + ch) * (kMaxConv + 1) + tid] = red[tid * 256];
+}
+
+// The filter's and bias's gradients: sums of the per-block partials over
+// batch rows and blocks, in order.
+__global__ void s6_conv_bwd_reduce(const float* __restrict__ part, float* __restrict__ dw, float* __restrict__ db,
+                                   int K, int64_t rows_blocks, int64_t D) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (channel, tap or bias)
+  if (i >= D * (kMaxConv + 1)) return;
+  const int64_t ch = i / (kMaxConv + 1);
+  const int k = (int)(i % (kMaxConv + 1));
+  if (k >= K && k != kMaxConv) return;
+  float sum = 0.0f;
+  for (int64_t r = 0; r < rows_blocks; ++r) sum += part[(r * D + ch) * (kMaxConv + 1) + k];
+  if (k == kMaxConv) {
+    if (db) db[ch] = sum;
+  } else {
+    dw[ch * K + k] = sum;
+  }
+}
+
 // carry: the part-carry kernel (parts 1 .. G-1) instead of the main kernel.
 template <typename In, bool GATE, int SPL, int OPT>
 int launch_bwd_t(const BwdArgs& a, int64_t parts, bool carry, hipStream_t st) {
@@ -657,11 +840,13 @@ int launch_bwd_g(const BwdArgs& a, bool gate, int64_t parts, bool carry, hipStre
 
 template <typename In>
 int launch_bwd(const BwdArgs& a, bool gate, int64_t parts, bool carry, hipStream_t st) {
-  const int opt = a.zoh ? 2 : (a.dbias || a.softplus || a.ddbias_part) ? 1 : 0;
+  const int opt = a.conv_w ? 3 : a.zoh ? 2 : (a.dbias || a.softplus || a.ddbias_part) ? 1 : 0;
   if (a.N <= 16) {
+    if (opt == 3) return launch_bwd_g<In, 1, 3>(a, gate, parts, carry, st);
     if (opt == 2) return launch_bwd_g<In, 1, 2>(a, gate, parts, carry, st);
     return opt ? launch_bwd_g<In, 1, 1>(a, gate, parts, carry, st) : launch_bwd_g<In, 1, 0>(a, gate, parts, carry, st);
   }
+  if (opt == 3) return launch_bwd_g<In, 2, 3>(a, gate, parts, carry, st);
   if (opt == 2) return launch_bwd_g<In, 2, 2>(a, gate, parts, carry, st);
   return opt ? launch_bwd_g<In, 2, 1>(a, gate, parts, carry, st) : launch_bwd_g<In, 2, 0>(a, gate, parts, carry, st);
 }
@@ -676,22 +861,42 @@ using namespace s6i;
 
 namespace {
 
+// The convolution front of s6_conv_scan_bwd and its gradient outputs.
+struct ConvGrad {
+  const float* w = nullptr;
+  const float* bias = nullptr;
+  const float* state = nullptr;
+  int width = 0;
+  float* dw = nullptr;
+  float* dbias = nullptr;
+  float* dstate = nullptr;
+};
+
 // s6_scan_bwd_ex, and s6_scan_bwd_ckpt when ckpt (the states entering every
 // kCkpt-token block, from s6_scan_fwd_ckpt) is given: the checkpoint pass is
-// then skipped.
+// then skipped; s6_conv_scan_bwd with a convolution front (cg.w).
 int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                   const void* x, const void* delta, const float* delta_bias, int flags, const float* A,
                   const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
                   const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
                   float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, const float* ckpt,
-                  void* stream) {
+                  void* stream, const ConvGrad& cg = ConvGrad()) {
   static_assert(kBwdSeg == kCkpt, "backward segments are the checkpoint blocks");
+  const bool conv = cg.w != nullptr || cg.width != 0;
   int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
   if (rc) return rc;
   if (flags & ~(S6_DELTA_SOFTPLUS | S6_ZOH_EXACT)) return S6_ERR_FLAGS;
   const bool softplus = (flags & S6_DELTA_SOFTPLUS) != 0;
   const bool zoh = (flags & S6_ZOH_EXACT) != 0;
   const bool work = batch > 0 && dim > 0 && seqlen > 0;
+  if (conv) {
+    if (cg.width < 1 || cg.width > kMaxConv) return S6_ERR_UNSUPPORTED;
+    if (zoh) return S6_ERR_UNSUPPORTED;  // the front's kernels have no exact hold
+    if (!cg.w || (dim > 0 && !cg.dw)) return S6_ERR_NULL;
+    const void* cps[] = {cg.w, cg.bias, cg.state, cg.dw, cg.dbias, cg.dstate};
+    for (const void* p : cps)
+      if (p && !aligned(p, 4)) return S6_ERR_ALIGN;
+  }
   if (dim > 0 && !dA) return S6_ERR_NULL;
   if (work && (!x || !delta || !A || !Bm || !Cm || !dy || !dx || !ddelta || !dBm || !dCm))
     return S6_ERR_NULL;
@@ -711,6 +916,11 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
     fill(dA, 0.0f, dim * dstate, st);
     fill(dDskip, 0.0f, dim, st);
     fill(ddelta_bias, 0.0f, dim, st);
+    if (conv) {
+      fill(cg.dw, 0.0f, dim * cg.width, st);
+      fill(cg.dbias, 0.0f, dim, st);
+      fill(cg.dstate, 0.0f, batch * dim * (cg.width - 1), st);
+    }
     S6_HIP(hipGetLastError(), "s6_scan_bwd fill");
     return dh0 ? launch_copy_state(dh_last, dh0, nstate, st) : S6_OK;
   }
@@ -743,8 +953,14 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
   const size_t bc_b = (size_t)nblkb * batch * dstate * seqlen * sizeof(float);
   const size_t mu_b = G > 1 ? (size_t)G * nstate * sizeof(float) : 0;     // carries: M and mu_in
   const size_t csd_b = G > 1 ? (size_t)G * batch * dim * sizeof(float) : 0;
+  // convolution front: the gradient of its output x' (the adjoint kernel's
+  // dx) and the per-block partials of the filter's and bias's gradients
+  const int64_t nlb = (seqlen + 256 * kConvTok - 1) / (256 * kConvTok);
+  const size_t dxo_b = conv ? (size_t)batch * dim * seqlen * sizeof(float) : 0;
+  const size_t cpart_b = conv ? (size_t)batch * nlb * dim * (kMaxConv + 1) * sizeof(float) : 0;
+  if (conv && (double)batch * dim * nlb > (double)INT32_MAX) return S6_ERR_SHAPE;
   const size_t total = up(agg_b) + up(sd_b) + up(hin_b) + up(dap_b) + 2 * up(ddp_b) + 2 * up(bc_b) + 2 * up(mu_b) +
-                       up(csd_b);
+                       up(csd_b) + up(dxo_b) + up(cpart_b);
   void* ws = nullptr;
   S6_HIP(hipMallocAsync(&ws, total, st), "hipMallocAsync(backward workspace)");
   char* wp = static_cast<char*>(ws);
@@ -769,6 +985,10 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
   float* muin = reinterpret_cast<float*>(wp);
   wp += up(mu_b);
   float* cSD = reinterpret_cast<float*>(wp);
+  wp += up(csd_b);
+  float* dxo = conv ? reinterpret_cast<float*>(wp) : nullptr;
+  wp += up(dxo_b);
+  float* cpart = reinterpret_cast<float*>(wp);
 
   // pass 1: end state (from zero) and summed delta of every segment but the last
   if (nagg > 0 && !ckpt) {
@@ -779,6 +999,7 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
     g.x = x; g.delta = delta; g.Bm = Bm; g.A = A;
     g.hout = agg; g.hout_stride = nstate; g.sumdelta = sd;
     g.dbias = delta_bias; g.softplus = softplus; g.zoh = zoh;
+    g.conv_w = cg.w; g.conv_b = cg.bias; g.conv_state = cg.state; g.conv_k = cg.width;
     g.D = dim; g.L = seqlen; g.N = dstate; g.seg_len = kBwdSeg;
     rc = launch_scan_any(in_dtype, kModeState, g, p, false, batch, nagg, st);
   }
@@ -791,7 +1012,8 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
     memset(&b, 0, sizeof(b));
     b.x = x; b.delta = delta; b.z = z; b.Bm = Bm; b.Cm = Cm; b.A = A; b.Dskip = Dskip;
     b.dy = dy; b.dh_last = dh_last; b.hin = hin;
-    b.dx = dx; b.ddelta = ddelta; b.dz = dz; b.dA_part = dap; b.dD_part = ddp;
+    b.dx = conv ? dxo : dx; b.ddelta = ddelta; b.dz = dz; b.dA_part = dap; b.dD_part = ddp;
+    b.conv_w = cg.w; b.conv_b = cg.bias; b.conv_state = cg.state; b.conv_k = cg.width;
     b.dB_part = dBp; b.dC_part = dcp; b.dh0 = dh0;
     b.dbias = delta_bias; b.softplus = softplus; b.zoh = zoh; b.ddbias_part = ddelta_bias ? dbp : nullptr;
     b.batch = batch; b.D = dim; b.L = seqlen; b.N = dstate; b.nseg = S; b.seg_per_part = spp;
@@ -823,6 +1045,20 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) rc = hip_fail(e, "s6_bwd reduction launch");
   }
+  if (rc == S6_OK && conv) {
+    const dim3 grid((unsigned)(batch * dim * nlb));
+    if (in_dtype == S6_BF16)
+      hipLaunchKernelGGL(s6_conv_bwd_kernel<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x), cg.w,
+                         cg.bias, cg.state, cg.width, dxo, dx, cg.dstate, cpart, batch, dim, seqlen, nlb);
+    else
+      hipLaunchKernelGGL(s6_conv_bwd_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(x), cg.w,
+                         cg.bias, cg.state, cg.width, dxo, dx, cg.dstate, cpart, batch, dim, seqlen, nlb);
+    const int64_t n = dim * (kMaxConv + 1);
+    hipLaunchKernelGGL(s6_conv_bwd_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cpart, cg.dw,
+                       cg.dbias, cg.width, batch * nlb, dim);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) rc = hip_fail(e, "s6_conv_bwd launch");
+  }
   hipError_t e = hipFreeAsync(ws, st);
   if (rc == S6_OK && e != hipSuccess) rc = hip_fail(e, "hipFreeAsync(backward workspace)");
   return rc;
@@ -849,6 +1085,26 @@ int s6_scan_bwd_ckpt(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
   if (!ckpt && batch > 0 && dim > 0 && seqlen > 0) return S6_ERR_NULL;
   return scan_bwd_impl(batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm, Dskip, z,
                        nullptr, dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, ddelta_bias, ckpt, stream);
+}
+
+int s6_conv_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                     const void* x, const float* conv_w, const float* conv_bias, int conv_width,
+                     const float* conv_state, const void* delta, const float* delta_bias, int flags,
+                     const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                     const float* h0, const float* dy, const float* dh_last, float* dx, float* ddelta,
+                     float* dA, float* dBm, float* dCm, float* dDskip, float* dz, float* dh0,
+                     float* ddelta_bias, float* dconv_w, float* dconv_bias, float* dconv_state, void* stream) {
+  if (!conv_w && conv_width == 0) return S6_ERR_NULL;
+  ConvGrad cg;
+  cg.w = conv_w;
+  cg.bias = conv_bias;
+  cg.state = conv_state;
+  cg.width = conv_width;
+  cg.dw = dconv_w;
+  cg.dbias = dconv_bias;
+  cg.dstate = dconv_state;
+  return scan_bwd_impl(batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm, Dskip, z, h0,
+                       dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, ddelta_bias, nullptr, stream, cg);
 }
 
 int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,

@@ -57,6 +57,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.s6_scan_fwd_ckpt.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32] + [vp] * 10
     lib.s6_scan_bwd_ckpt.restype = i32
     lib.s6_scan_bwd_ckpt.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32] + [vp] * 18
+    lib.s6_conv_scan_bwd.restype = i32
+    lib.s6_conv_scan_bwd.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32, vp, vp, vp, i32] + [vp] * 21
     lib.s6_scan_bwd.restype = i32
     lib.s6_scan_bwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 19
     lib.s6_scan_bwd_ex.restype = i32
@@ -354,6 +356,56 @@ def scan_bwd(x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_last=None, del
                                         _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(g["dx"]),
                                         _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dBm"]), _ptr(g["dCm"]),
                                         _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g["dh0"]), _stream())
+    _check(rc)
+    return g
+
+
+def conv_scan_bwd(x, conv_w, delta, A, Bm, Cm, dy, conv_bias=None, conv_state=None, D=None, z=None, h0=None,
+                  dh_last=None, delta_bias=None, delta_softplus=False, zoh=False):
+    """Gradients of <dy, y> + <dh_last, h_last> for conv_scan_fwd with the
+    same inputs and options.  Returns the dict of scan_bwd (dx is the
+    gradient of the raw x) plus dconv_w (dim, width), and dconv_bias /
+    dconv_state when conv_bias / conv_state are given."""
+    bsz, dim, L = x.shape
+    N = A.shape[1]
+    dt = x.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported input dtype {dt}")
+    width = _conv_args(conv_w, conv_bias, dim)
+    _opt(conv_state, "conv_state", (bsz, dim, width - 1), torch.float32)
+    _req(x, "x", (bsz, dim, L), dt)
+    _req(delta, "delta", (bsz, dim, L), dt)
+    _req(A, "A", (dim, N), torch.float32)
+    _req(Bm, "Bm", (bsz, N, L), dt)
+    _req(Cm, "Cm", (bsz, N, L), dt)
+    _opt(D, "D", (dim,), torch.float32)
+    _opt(z, "z", (bsz, dim, L), dt)
+    _opt(h0, "h0", (bsz, dim, N), torch.float32)
+    _req(dy, "dy", (bsz, dim, L), torch.float32)
+    _opt(dh_last, "dh_last", (bsz, dim, N), torch.float32)
+    f = dict(dtype=torch.float32, device=x.device)
+    g = {"dx": torch.empty((bsz, dim, L), **f), "ddelta": torch.empty((bsz, dim, L), **f),
+         "dA": torch.empty((dim, N), **f), "dBm": torch.empty((bsz, N, L), **f),
+         "dCm": torch.empty((bsz, N, L), **f), "dh0": torch.empty((bsz, dim, N), **f),
+         "dconv_w": torch.empty((dim, width), **f)}
+    if D is not None:
+        g["dD"] = torch.empty((dim,), **f)
+    if z is not None:
+        g["dz"] = torch.empty((bsz, dim, L), **f)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty((dim,), **f)
+    if conv_bias is not None:
+        g["dconv_bias"] = torch.empty((dim,), **f)
+    if conv_state is not None:
+        g["dconv_state"] = torch.empty((bsz, dim, width - 1), **f)
+    _, flags = _options(delta_bias, delta_softplus, zoh, dim)
+    rc = load_library().s6_conv_scan_bwd(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(conv_w), _ptr(conv_bias), width,
+                                         _ptr(conv_state), _ptr(delta), _ptr(delta_bias), flags, _ptr(A), _ptr(Bm),
+                                         _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(g["dx"]),
+                                         _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dBm"]), _ptr(g["dCm"]),
+                                         _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g["dh0"]),
+                                         _ptr(g.get("ddelta_bias")), _ptr(g["dconv_w"]), _ptr(g.get("dconv_bias")),
+                                         _ptr(g.get("dconv_state")), _stream())
     _check(rc)
     return g
 

@@ -47,7 +47,8 @@ def codes():
 
 
 def test_header_declares_the_entry_points():
-    assert header_functions() == ["s6_conv_scan_fwd", "s6_conv_state_update", "s6_last_state", "s6_last_state_ex",
+    assert header_functions() == ["s6_conv_scan_bwd", "s6_conv_scan_fwd", "s6_conv_state_update", "s6_last_state",
+                                  "s6_last_state_ex",
                                   "s6_scan_bwd", "s6_scan_bwd_ckpt", "s6_scan_bwd_ex", "s6_scan_fwd",
                                   "s6_scan_fwd_ckpt", "s6_scan_fwd_ex", "s6_state_update", "s6_state_update_ex",
                                   "s6_status_str", "s6_version"]
@@ -184,6 +185,19 @@ def test_conv_entry_points_validation(lib, codes):
     assert step(h=None) == codes["S6_ERR_NULL"]
     assert step(b=0) == codes["S6_OK"]
     assert step(b=0, width=1, state=None) == codes["S6_OK"]
+
+    def bwd(w=P, width=4, dw=P, d=64, flags=0, bias=None):
+        return lib.s6_conv_scan_bwd(2, d, 32, 16, 1, P, w, bias, width, None, P, None, flags, P, P, P, None, None,
+                                    None, P, None, P, P, P, P, P, None, None, None, None, dw, None, None, None)
+
+    assert bwd(width=5) == codes["S6_ERR_UNSUPPORTED"]
+    assert bwd(w=None) == codes["S6_ERR_NULL"]
+    assert bwd(w=None, width=0) == codes["S6_ERR_NULL"]
+    assert bwd(dw=None) == codes["S6_ERR_NULL"]
+    assert bwd(bias=P_ODD) == codes["S6_ERR_ALIGN"]
+    assert bwd(flags=8) == codes["S6_ERR_FLAGS"]
+    assert bwd(flags=2) == codes["S6_ERR_UNSUPPORTED"]  # no exact hold with the front
+    assert bwd(d=0, dw=None) == codes["S6_OK"]  # no channels: nothing to write
 
 
 def test_checkpoint_entry_points_validation(lib, codes):
