@@ -54,7 +54,9 @@
  *     (few long rows), s6_scan_fwd and s6_last_state split the sequence into
  *     segments and take the per-segment carries from the stream-ordered
  *     allocator (hipMallocAsync), releasing them on the same stream before
- *     returning; otherwise, and in s6_state_update, nothing is allocated.
+ *     returning; otherwise, and in the decode steps, nothing is allocated.
+ *     The backward entry points take their workspace (segment states,
+ *     partial sums) from the same allocator in the same way.
  */
 #ifndef S6_H_
 #define S6_H_

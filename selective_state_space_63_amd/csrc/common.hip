@@ -65,7 +65,7 @@ using namespace s6i;
 
 extern "C" {
 
-int s6_version(void) { return 10200; }
+int s6_version(void) { return 10300; }
 
 const char* s6_status_str(int status) {
   switch (status) {

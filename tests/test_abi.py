@@ -63,7 +63,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings(lib, codes):
-    assert lib.s6_version() == 10200
+    assert lib.s6_version() == 10300
     for name, v in codes.items():
         if name.startswith("S6_ERR_") or name == "S6_OK":
             s = lib.s6_status_str(v).decode()
