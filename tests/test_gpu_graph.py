@@ -51,3 +51,36 @@ def test_decode_graph_replays(torch_cuda):
         torch.cuda.synchronize()
         assert torch.equal(h, h_ref), rep
         assert torch.equal(y, y_ref), rep
+
+
+def test_scan_graph_replays(torch_cuda):
+    """The fused scan (with final state and training checkpoints) captured in
+    a HIP graph: it allocates nothing when the rows fill the GPU, so the
+    capture holds just its kernel; every replay equals the eager call bit for
+    bit."""
+    import torch
+    from selective_state_space_63_amd import s6
+    w = synth.custom(8, 2600, 16, 256, synth.BF16, True, seed=32)  # 656 row blocks: not cut into segments
+    d, _ = problem(w, True)
+    y = torch.empty((w.batch, w.dim, w.seqlen), device="cuda", dtype=torch.float32)
+    hl = torch.empty((w.batch, w.dim, w.dstate), device="cuda", dtype=torch.float32)
+    ck = torch.empty(s6.ckpt_shape(w.batch, w.dim, w.seqlen, w.dstate), device="cuda", dtype=torch.float32)
+
+    def run():
+        s6.scan_fwd(d["x"], d["delta"], d["A"], d["Bm"], d["Cm"], D=d["D"], z=d["z"], h0=d["h0"], y=y, h_last=hl,
+                    return_last_state=True, ckpt=ck)
+
+    run()
+    torch.cuda.synchronize()
+    refs = (y.clone(), hl.clone(), ck.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        for t in (y, hl, ck):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, r in zip((y, hl, ck), refs):
+            assert torch.equal(t, r), rep
