@@ -29,7 +29,7 @@
  *   A : (D, N)        Dskip : (D)        h0, h_last, H_last : (Bsz, D, N)
  *   decode step: x, delta, z, y, m : (Bsz, D); Bm, Cm : (Bsz, N)
  *
- Step bias and discretisation options (oracle_scan_ex, oracle_step_ex):
+ * Step bias and discretisation options (oracle_scan_ex, oracle_step_ex):
  *   delta_bias (D), nullable: the step is delta + delta_bias[d].
  *   ORACLE_DELTA_SOFTPLUS (bit flag): the step is softplus(delta + bias),
  *     softplus(v) = ln(1 + e^v).  The pages make Delta learnable and
