@@ -9,7 +9,8 @@
 //
 // Files: scan_kernel.h (the fused scan kernel), scan.hip (its plain
 // instantiations, final-state scan, segments and carries, entry points),
-// scan_ext.hip (option kernels), step.hip (decode step), bwd.hip
+// scan_ext.hip, scan_conv.hip, scan_hold.hip (option kernels: step bias
+// and softplus; convolution front; exact hold), step.hip (decode step), bwd.hip
 // (gradients), common.hip (checks, errors, version).
 #ifndef S6_INTERNAL_H_
 #define S6_INTERNAL_H_
@@ -153,10 +154,16 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, size_
 int launch_scan_any(int in_dtype, int mode, const ScanArgs& a, const Plan& p, bool gate, int64_t batch,
                     int64_t segs, hipStream_t st);
 
-// The option kernels (scan_ext.hip): step bias, softplus, exact hold,
-// convolution front.
+// The option kernels: step bias, softplus, exact hold, convolution front
+// (dispatch in scan_ext.hip).  Three levels, each compiled in a file of its
+// own: the step bias and softplus (scan_ext.hip), those and the convolution
+// front (scan_conv.hip), all of them and the exact hold (scan_hold.hip).
 int launch_scan_options(int in_dtype, int mode, const ScanArgs& a, const Plan& p, bool gate, int64_t batch,
                         int64_t segs, hipStream_t st);
+int launch_scan_conv(int in_dtype, int mode, const ScanArgs& a, const Plan& p, bool gate, int64_t batch,
+                     int64_t segs, hipStream_t st);
+int launch_scan_hold(int in_dtype, int mode, const ScanArgs& a, const Plan& p, bool gate, int64_t batch,
+                     int64_t segs, hipStream_t st);
 
 // The carry fold over segments: hin[s] (nullable) receives the state entering
 // segment s, hlast (nullable) the state after the last of `nagg` aggregates.

@@ -2,7 +2,7 @@
 // _ex forms and s6_conv_scan_fwd): launch planning, the segment carry fold,
 // the plain kernels.  The kernel itself is in scan_kernel.h; the kernels with
 // the step options and the convolution front are instantiated in
-// scan_ext.hip.
+// scan_ext.hip, scan_conv.hip and scan_hold.hip.
 #include "scan_kernel.h"
 
 namespace s6i {

@@ -1,7 +1,7 @@
 // scan_kernel.h -- the fused selective-scan kernel template and its launch
 // helpers, shared by scan.hip (plain kernels and the host side) and
-// scan_ext.hip (the kernels with the step options and the convolution
-// front).  Internal to libs6.
+// scan_ext.hip, scan_conv.hip, scan_hold.hip (the kernels with the step
+// options and the convolution front).  Internal to libs6.
 //
 //
 // Design (gfx950, wave64):
@@ -229,7 +229,8 @@ __device__ __forceinline__ void token_group(const float* dl, const float* xv, co
 // kind of piece each wave stages rotates with the workgroup index so that
 // this extra work falls on every SIMD alike.
 template <typename In, int VEC, bool GATE, int MODE, int W, int WIN, int EXT, bool CK>
-__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ? (EXT ? 4 : 5) : 1)))
+__global__ void __launch_bounds__(64 * W)
+    __attribute__((amdgpu_waves_per_eu(W == 4 ? ((EXT == 0 || (EXT == 1 && VEC > 1 && !CK)) ? 5 : 4) : 1)))
 s6_scan_kernel(ScanArgs a) {
   constexpr int NTHR = 64 * W;
   constexpr int NTS = (MODE == kModeY && GATE) ? 3 : 2;  // staged tensors: x, delta (, z)
@@ -310,9 +311,10 @@ s6_scan_kernel(ScanArgs a) {
       if (n0 + 1 < N) base[c * N + n0 + 1] = h[1];
     }
   };
-  // Plain kernels write checkpoints only in their CK instantiations (the
-  // write in the chunk loop costs registers); option kernels check a.ckpt.
-  constexpr bool kCk = MODE == kModeY && (CK || EXT != 0);
+  // The plain and step-bias kernels write checkpoints only in their CK
+  // instantiations (the write in the chunk loop costs registers); the
+  // exact-hold and convolution kernels check a.ckpt.
+  constexpr bool kCk = MODE == kModeY && (CK || EXT >= 2);
   if (kCk && a.ckpt && tb < te) write_ckpt(tb);
   // Sum of delta over the segment (state mode), compensated (Neumaier):
   // dsum + dcomp.  (A double accumulator here costs dozens of registers.)
@@ -367,7 +369,7 @@ s6_scan_kernel(ScanArgs a) {
   // this lane's piece (only the last piece of a row passes them on), or the
   // single element (VEC == 1).  Before the segment's first chunk they are
   // the inputs before it: x itself, or conv_state / 0 before token 0.
-  const bool conv = EXT && a.conv_w != nullptr;
+  const bool conv = EXT >= 2 && a.conv_w != nullptr;
   constexpr int NCAR = VEC == 1 ? 1 : 3;
   float cwr[SLOTS][kMaxConv], cbias[SLOTS], carry[SLOTS][NCAR];
 #pragma unroll
@@ -719,7 +721,7 @@ int launch_scan_t(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, 
 // is set (option kernels write them whenever it is set).
 template <typename In, int VEC, bool GATE, int MODE, int W, int EXT>
 int launch_scan_c(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, hipStream_t st) {
-  if constexpr (MODE == kModeY && EXT == 0) {
+  if constexpr (MODE == kModeY && EXT <= 1) {
     if (a.ckpt) return launch_scan_t<In, VEC, GATE, MODE, W, EXT, true>(a, batch, nblk, segs, st);
   }
   return launch_scan_t<In, VEC, GATE, MODE, W, EXT, false>(a, batch, nblk, segs, st);
@@ -751,8 +753,9 @@ int launch_scan(const ScanArgs& a, int W, bool vec, bool gate, int64_t batch, in
   }
 }
 
-// EXT: 0 the plain kernels; 1 the step bias, softplus and the convolution
-// front; 2 those and the exact hold (which needs more registers).
+// EXT: 0 the plain kernels; 1 the step bias and softplus (few enough
+// registers for five waves per SIMD); 3 those and the convolution front; 2
+// all of them and the exact hold.  Each level costs registers.
 template <int EXT>
 int launch_scan_e(int in_dtype, int mode, const ScanArgs& a, const Plan& p, bool gate, int64_t batch,
                   int64_t segs, hipStream_t st) {
