@@ -222,12 +222,12 @@ __device__ __forceinline__ void token_group(const float* dl, const float* xv, co
 // state), and only a window that would cross the end of the rows clamps its
 // piece addresses.
 //
-// EXT kernels also take the step bias and discretisation options of ScanArgs:
-// the bias and softplus are applied to delta while it is staged (once per
-// element), the convolution front to x the same way, the exact hold in the
-// token groups, and the
-// kind of piece each wave stages rotates with the workgroup index so that
-// this extra work falls on every SIMD alike.
+// EXT kernels also take the step bias and discretisation options of ScanArgs
+// (EXT 1: bias and softplus; 3: and the convolution front; 2: and the exact
+// hold): the bias and softplus are applied to delta while it is staged (once
+// per element), the convolution front to x the same way, the exact hold in
+// the token groups, and the kind of piece each wave stages rotates with the
+// workgroup index so that this extra work falls on every SIMD alike.
 template <typename In, int VEC, bool GATE, int MODE, int W, int WIN, int EXT, bool CK>
 __global__ void __launch_bounds__(64 * W)
     __attribute__((amdgpu_waves_per_eu(W == 4 ? ((EXT == 0 || (EXT == 1 && VEC > 1 && !CK)) ? 5 : 4) : 1)))
@@ -717,8 +717,9 @@ int launch_scan_t(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, 
   return S6_OK;
 }
 
-// The checkpoint-writing instantiation of a plain fused kernel when a.ckpt
-// is set (option kernels write them whenever it is set).
+// The checkpoint-writing instantiation of a plain or step-bias fused kernel
+// when a.ckpt is set (the convolution and exact-hold kernels write them
+// whenever it is set).
 template <typename In, int VEC, bool GATE, int MODE, int W, int EXT>
 int launch_scan_c(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, hipStream_t st) {
   if constexpr (MODE == kModeY && EXT <= 1) {
