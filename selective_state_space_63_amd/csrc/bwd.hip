@@ -118,13 +118,39 @@ struct BwdArgs {
 // each step a lane keeps the half of its values whose token index has the
 // lane's bit (8, 4, 2, 1), and adds its partner's copy of that half; the
 // partner shares the bits already used, so both hold the same tokens.
+//
+// Lane bits 3 and 2 are bank bits (a bank is 4 lanes of a row), so the first
+// two steps need no selects: out[j] = hi[j] + partner's hi[j] is written in
+// every lane, then lo[j] + partner's lo[j] over it in the banks whose bit is
+// 0 (a DPP add with a bank mask leaves the other banks' value in place).
+// The sums are the same additions as with selects, bit for bit.
+#define S6_BANKED_PAIR_SUMS4(CTRL, BANKS)                                                        \
+  asm("s_nop 1\n\t"                                                                            \
+      "v_add_f32_dpp %0, %4, %4 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                       \
+      "v_add_f32_dpp %1, %5, %5 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                       \
+      "v_add_f32_dpp %2, %6, %6 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                       \
+      "v_add_f32_dpp %3, %7, %7 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                       \
+      "v_add_f32_dpp %0, %8, %8 " CTRL " row_mask:0xf bank_mask:" BANKS "\n\t"                 \
+      "v_add_f32_dpp %1, %9, %9 " CTRL " row_mask:0xf bank_mask:" BANKS "\n\t"                 \
+      "v_add_f32_dpp %2, %10, %10 " CTRL " row_mask:0xf bank_mask:" BANKS "\n\t"               \
+      "v_add_f32_dpp %3, %11, %11 " CTRL " row_mask:0xf bank_mask:" BANKS                        \
+      : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])                              \
+      : "v"(hi[0]), "v"(hi[1]), "v"(hi[2]), "v"(hi[3]), "v"(lo[0]), "v"(lo[1]), "v"(lo[2]), "v"(lo[3]))
+// partner l^8 (row rotation by 8); bit 3 is clear in banks 0 and 1
+__device__ __forceinline__ void pair_sums4_l8(const float* lo, const float* hi, float* out) {
+  S6_BANKED_PAIR_SUMS4("row_ror:8", "0x3");
+}
+// partner l^7 (half-row mirror); bit 2 is clear in banks 0 and 2
+__device__ __forceinline__ void pair_sums4_l7(const float* lo, const float* hi, float* out) {
+  S6_BANKED_PAIR_SUMS4("row_half_mirror", "0x5");
+}
+#undef S6_BANKED_PAIR_SUMS4
 __device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int nl) {
-  const bool b3 = nl & 8, b2 = nl & 4, b1 = nl & 2, b0 = nl & 1;
+  const bool b1 = nl & 2, b0 = nl & 1;
   float a8[8], a4[4], a2[2];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) a8[j] = (b3 ? v[j + 8] : v[j]) + dpp_f<0x128>(b3 ? v[j] : v[j + 8]);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) a4[j] = (b2 ? a8[j + 4] : a8[j]) + dpp_f<0x141>(b2 ? a8[j] : a8[j + 4]);
+  pair_sums4_l8(v, v + 8, a8);
+  pair_sums4_l8(v + 4, v + 12, a8 + 4);
+  pair_sums4_l7(a8, a8 + 4, a4);
 #pragma unroll
   for (int j = 0; j < 2; ++j) a2[j] = (b1 ? a4[j + 2] : a4[j]) + dpp_f<0x4E>(b1 ? a4[j] : a4[j + 2]);
   return (b0 ? a2[1] : a2[0]) + dpp_f<0xB1>(b0 ? a2[0] : a2[1]);
