@@ -594,6 +594,8 @@ def main():
                     help="only run a plain device copy of this many MiB (byte-counter calibration)")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time s6_scan_bwd on the workload (one JSON line; for profiling)")
+    ap.add_argument("--conv-k", type=int, default=0,
+                    help="with --backward-only: time s6_conv_scan_bwd with a filter of this width")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the scan has no cross-GPU step); got --gpus {args.gpus}",
@@ -611,7 +613,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     in_bytes = 2 if w.dtype == synth.BF16 else 4
     if args.backward_only:
-        print(json.dumps({"backward": bench_backward(w, steps=args.steps, warmup=args.warmup)}), flush=True)
+        print(json.dumps({"backward": bench_backward(w, steps=args.steps, warmup=args.warmup, conv_k=args.conv_k)}),
+              flush=True)
         return
     print(f"[bench] scan {w.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
     inp, tm, wall = bench_scan(w, args.steps, args.warmup)
