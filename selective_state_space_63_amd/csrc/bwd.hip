@@ -718,7 +718,8 @@ __global__ void s6_bwd_reduce_rows(const float* __restrict__ dA_part, const floa
 // thread recomputes the filter's output xc and dxc = dxo * SiLU'(xc) for its
 // tokens into LDS (the first K - 1 threads also the tokens just past the
 // block), then writes dx_s = sum_k w_k dxc_{s+K-1-k}; the block sums
-// dxc_t x_{t-K+1+k} (filter) and dxc_t (bias) in a fixed tree into
+// dxc_t x_{t-K+1+k} (filter) and dxc_t (bias) in a fixed order (DPP sums
+// over the 16 lanes of a row, then the 16 row sums one after another) into
 // part[(b * nlb + block) * D + ch][k]; the row's first block also writes the
 // state's gradient (the same sum for s < 0).
 constexpr int kConvTok = 8;  // tokens per thread
@@ -733,7 +734,7 @@ __global__ void __launch_bounds__(256) s6_conv_bwd_kernel(const In* __restrict__
   constexpr int H = kMaxConv - 1;       // halo
   __shared__ float sdxc[TB + H];
   __shared__ float sxin[TB + 2 * H];    // inputs at tb0 - H .. tb0 + TB + H - 1
-  __shared__ float red[256 * (kMaxConv + 1)];
+  __shared__ float red[16 * (kMaxConv + 1)];
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x / nlb;
   const int64_t lb = blockIdx.x % nlb;
@@ -811,18 +812,23 @@ __global__ void __launch_bounds__(256) s6_conv_bwd_kernel(const In* __restrict__
       dstate[row * (K - 1) + (K - 1) + s] = g;
     }
   }
+  // Sums over the 16 lanes of each row (DPP: partners l^1, l^2, the half-row
+  // mirror, rotation by 8), then the 16 row sums of the block in order.
 #pragma unroll
-  for (int k = 0; k <= kMaxConv; ++k) red[k * 256 + tid] = pk[k];
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) {
-#pragma unroll
-      for (int k = 0; k <= kMaxConv; ++k) red[k * 256 + tid] += red[k * 256 + tid + w];
-    }
-    __syncthreads();
+  for (int k = 0; k <= kMaxConv; ++k) {
+    float v = pk[k];
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x128>(v);
+    if ((tid & 15) == 0) red[k * 16 + (tid >> 4)] = v;
   }
-  if (tid <= kMaxConv && (tid < K || tid == kMaxConv))
-    part[((b * nlb + lb) * D + ch) * (kMaxConv + 1) + tid] = red[tid * 256];
+  __syncthreads();
+  if (tid <= kMaxConv && (tid < K || tid == kMaxConv)) {
+    float acc = 0.0f;
+    for (int r = 0; r < 16; ++r) acc += red[tid * 16 + r];
+    part[((b * nlb + lb) * D + ch) * (kMaxConv + 1) + tid] = acc;
+  }
 }
 
 // The filter's and bias's gradients: sums of the per-block partials over
