@@ -302,12 +302,30 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>())
       sB[n * KP + t] = ok ? to_f32(Bp[off]) : 0.0f;
       sC[n * KP + t] = ok ? to_f32(Cp[off]) : 0.0f;
     }
+    if constexpr (CONV) {
+      // the raw inputs of the kMaxConv - 1 tokens before the segment (from
+      // the previous segment, or the front's state before token 0) go to the
+      // row's padding slots KS .. KS + kMaxConv - 2, loaded with the rest
+      static_assert(KP - KS >= kMaxConv - 1, "halo fits the row padding");
+      if (tid < CW * (kMaxConv - 1)) {
+        const int hc = tid / (kMaxConv - 1), hj = tid % (kMaxConv - 1);
+        const int64_t sg = tb - (kMaxConv - 1) + hj;
+        const int K = a.conv_k;
+        float v = 0.0f;
+        if (hc < rows_valid) {
+          const int64_t rw = b * D + d0 + hc;
+          if (sg >= 0) v = to_f32(xp[rw * L + sg]);
+          else if (sg >= -(int64_t)(K - 1) && a.conv_state) v = a.conv_state[rw * (K - 1) + (K - 1) + sg];
+        }
+        sx[hc * KP + KS + hj] = v;
+      }
+    }
     __syncthreads();
     if constexpr (CONV) {
       // The convolution front's output x' replaces the staged x, as the
       // forward computes it: 4 consecutive tokens of one channel per thread
       // from the 3 + 4 raw inputs around them (the 3 before the segment from
-      // memory), read before any thread overwrites its tokens.
+      // the row's padding slots), read before any thread overwrites its tokens.
       static_assert(CW * KS == 4 * NTHR, "one group of 4 tokens per thread");
       const int fcc = tid / (KS / 4), ft4 = (tid % (KS / 4)) * 4;
       const int K = a.conv_k;
@@ -315,15 +333,7 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>())
 #pragma unroll
       for (int i = 0; i < 4 + kMaxConv - 1; ++i) {
         const int t = ft4 - (kMaxConv - 1) + i;
-        float v = 0.0f;
-        if (t >= 0) {
-          v = sx[fcc * KP + t];
-        } else if (fcc < rows_valid) {
-          const int64_t sg = tb + t, rw = b * D + d0 + fcc;
-          if (sg >= 0) v = to_f32(xp[rw * L + sg]);
-          else if (sg >= -(int64_t)(K - 1) && a.conv_state) v = a.conv_state[rw * (K - 1) + (K - 1) + sg];
-        }
-        xin[i] = v;
+        xin[i] = sx[fcc * KP + (t >= 0 ? t : KS + (kMaxConv - 1) + t)];
       }
       __syncthreads();  // every raw input is read
       float xo[4] = {0.0f, 0.0f, 0.0f, 0.0f};
