@@ -267,6 +267,18 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>())
   for (int64_t s = s_end - 1; s >= s_begin; --s) {
     const int64_t tb = s * KS;
     const int64_t tl = L - tb < KS ? L - tb : KS;  // valid tokens of the segment
+    // the state entering the segment: loaded before the staging, so that its
+    // latency is not exposed after the barrier, where registers allow (the
+    // kernels held to 128 VGPRs load it after the staging)
+    float hseg[SPL];
+    auto load_hseg = [&]() {
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        const int64_t n = (int64_t)nl * SPL + j;
+        hseg[j] = sv[j] ? a.hin[s * a.batch * D * N + (b * D + d) * N + n] : 0.0f;
+      }
+    };
+    if constexpr (OPT < 2) load_hseg();
     __syncthreads();  // the previous segment's reads of the staged inputs are done
     for (int i = tid; i < CW * KS; i += NTHR) {
       const int cc = i / KS, t = i % KS;
@@ -361,12 +373,10 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>())
     // states at the four chunk starts of the segment
     float hc[4][SPL];
     {
+      if constexpr (OPT >= 2) load_hseg();
       float h[SPL];
 #pragma unroll
-      for (int j = 0; j < SPL; ++j) {
-        const int64_t n = (int64_t)nl * SPL + j;
-        h[j] = sv[j] ? a.hin[s * a.batch * D * N + (b * D + d) * N + n] : 0.0f;
-      }
+      for (int j = 0; j < SPL; ++j) h[j] = hseg[j];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
 #pragma unroll
