@@ -30,9 +30,10 @@ constexpr int kBwdSeg = 64;    // tokens per recomputation segment
 // consecutive rows 4 banks apart, so 16 lanes' 16-byte reads cover all 64.
 constexpr int kBwdPitch = kBwdSeg + 4;
 
-// Waves per workgroup (4 channels each).  The kernel needs 150-190 VGPRs,
-// i.e. two waves per SIMD: two 4-wave workgroups per CU, whose barriers fall
-// at different times, run faster than one 8-wave workgroup.
+// Waves per workgroup (4 channels each).  With one state per lane the
+// kernels take 103-128 VGPRs (four waves per SIMD), with two (N > 16) about
+// 180 (two waves per SIMD).  Several 4-wave workgroups per CU, whose barriers
+// fall at different times, run faster than fewer 8-wave ones.
 template <int SPL>
 constexpr int bwd_waves() { return 4; }
 
