@@ -3,6 +3,11 @@ import sys
 
 import pytest
 
+# Under pytest-xdist every worker would start one OpenMP thread per core in
+# the oracle, and their spin-waits oversubscribe the host: one thread each.
+if os.environ.get("PYTEST_XDIST_WORKER"):
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)

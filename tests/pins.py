@@ -1038,6 +1038,88 @@ def pin_conv_bwd_magnitude(o):
     assert np.array_equal(r2["dBm"], r1["dBm"])
 
 
+# ---------------------------------------------- magnitudes of the backward --
+BWD_GRADS = ("dx", "ddelta", "dA", "dBm", "dCm", "dDskip", "dz", "dh0", "ddelta_bias")
+
+
+def _sign_uniform_bwd(seed, Bsz=2, D=3, L=24, N=4):
+    """A backward problem on which every factor of every gradient's sum is
+    >= 0: positive x, B, C, D, h0, dy, dh_last and step; z > 0 (SiLU and
+    SiLU' positive there); A > 0 (transitions e^(Delta A) > 0, and the
+    A-terms of dDelta and dA positive).  The hold's coefficient and its
+    derivatives in Delta and A are positive for every A."""
+    g = _rng(seed)
+    return dict(
+        x=g.uniform(0.1, 1.5, (Bsz, D, L)), delta=g.uniform(0.01, 0.3, (Bsz, D, L)),
+        A=g.uniform(0.05, 0.6, (D, N)), Bm=g.uniform(0.1, 1.5, (Bsz, N, L)),
+        Cm=g.uniform(0.1, 1.5, (Bsz, N, L)), Dskip=g.uniform(0.1, 1.5, D),
+        z=g.uniform(0.05, 3.0, (Bsz, D, L)), h0=g.uniform(0.1, 1.5, (Bsz, D, N)),
+        dy=g.uniform(0.1, 1.5, (Bsz, D, L)), dh_last=g.uniform(0.1, 1.5, (Bsz, D, N)),
+        delta_bias=g.uniform(-0.5, 0.5, D))
+
+
+def pin_bwd_magnitudes(o):
+    """Every magnitude the backward returns is the same sum as its gradient
+    over the absolute value of every factor.  So (a) where every factor is
+    >= 0 it equals the gradient itself, element by element -- with the
+    plain step, with the bias and softplus, with the exact hold and with
+    x magnitudes |x| passed in explicitly; and (b) on random inputs it is
+    never below |gradient|.  A magnitude scaled by any constant other than
+    1 fails (a); a dropped term fails (a) or (b).  These magnitudes are the
+    scale of every gradient comparison, so they are pinned here rather than
+    through the comparisons that divide by them."""
+    base = _sign_uniform_bwd(191)
+    cases = [dict(), dict(delta_bias=base["delta_bias"], softplus=True), dict(zoh=True),
+             dict(delta_bias=base["delta_bias"], softplus=True, zoh=True), dict(xmag=np.abs(base["x"]))]
+    for opt in cases:
+        r = o.scan_bwd(base["x"], base["delta"], base["A"], base["Bm"], base["Cm"], base["dy"],
+                       Dskip=base["Dskip"], z=base["z"], h0=base["h0"], dh_last=base["dh_last"], **opt)
+        for k in BWD_GRADS:
+            if k == "ddelta_bias" and "delta_bias" not in opt:
+                continue
+            assert np.all(r[k] > 0), (k, opt.keys())
+            assert np.allclose(r["m" + k], r[k], rtol=1e-13, atol=0), (k, list(opt.keys()),
+                                                                       np.max(np.abs(r["m" + k] / r[k] - 1)))
+    p, dy, dhl = _bwd_problem(192, Bsz=2, D=3, L=30, N=4)
+    g = _rng(193)
+    bias = g.standard_normal(3) * 0.5
+    for opt in (dict(), dict(delta_bias=bias, softplus=True), dict(zoh=True)):
+        r = o.scan_bwd(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], dy, Dskip=p["Dskip"], z=p["z"],
+                       h0=p["h0"], dh_last=dhl, **opt)
+        for k in BWD_GRADS:
+            if k == "ddelta_bias" and "delta_bias" not in opt:
+                continue
+            assert np.all(r["m" + k] >= np.abs(r[k]) * (1 - 1e-13)), (k, list(opt.keys()))
+            # not a trivial bound: on random signs the sums cancel, but not by orders of magnitude
+            assert np.max(np.abs(r[k]) / r["m" + k]) > 0.05, (k, list(opt.keys()))
+
+
+def pin_conv_bwd_magnitude_bracket(o):
+    """The front's backward magnitudes (input, filter, bias, state) on inputs
+    where every factor is >= 0 and the filter's output xc lies in (0, 0.3]:
+    there they are the gradient itself plus the second-derivative term
+    |dxo| |SiLU''(xc)| (|bias| + sum |w x|), which adds at most 30% (on
+    that range |SiLU''| <= 0.5, SiLU' >= 0.5 and the sum of terms is xc
+    itself).  So gradient <= magnitude <= 1.3 gradient element by element;
+    a magnitude off by a constant factor fails one side."""
+    g = _rng(194)
+    Bsz, D, L, K = 2, 3, 20, 4
+    x = g.uniform(0.0, 0.1, (Bsz, D, L))
+    w = g.uniform(0.05, 0.5, (D, K))
+    bias = g.uniform(0.0, 0.05, D)
+    state = g.uniform(0.0, 0.1, (Bsz, D, K - 1))
+    dxo = g.uniform(0.1, 1.5, (Bsz, D, L))
+    xo, _ = o.conv_silu(x, w, bias, state)
+    full = np.concatenate([state, x], axis=-1)
+    xc = bias[None, :, None] + sum(w[None, :, k, None] * full[..., k:k + L] for k in range(K))
+    assert np.all(xc > 0) and np.all(xc <= 0.3)
+    cb = o.conv_silu_bwd(x, w, dxo, mdxo=dxo, bias=bias, state=state)
+    for k in ("dx", "dw", "dbias", "dstate"):
+        assert np.all(cb[k] > 0), k
+        assert np.all(cb["m" + k] >= cb[k] * (1 - 1e-14)), k
+        assert np.all(cb["m" + k] <= 1.3 * cb[k]), (k, np.max(cb["m" + k] / cb[k]))
+
+
 PINS = [pin_zero_step_hand, pin_scalar_hand, pin_lti_convolution, pin_step_response,
         pin_brute_force, pin_tree_scan, pin_split_resume, pin_linearity_and_permutation,
         pin_gate_limits, pin_decode_equals_scan, pin_magnitude_bounds, pin_softplus_hand,
@@ -1046,4 +1128,5 @@ PINS = [pin_zero_step_hand, pin_scalar_hand, pin_lti_convolution, pin_step_respo
         pin_bwd_no_input_coupling, pin_bwd_options_directional_brute_force, pin_bwd_options_elementwise_fd,
         pin_bwd_zoh_directional_brute_force, pin_bwd_zoh_elementwise_fd, pin_bwd_zoh_single_token,
         pin_conv_hand, pin_conv_numpy, pin_conv_split_resume, pin_conv_magnitude,
-        pin_conv_scan_brute_force, pin_conv_bwd_chain_fd, pin_conv_bwd_numpy, pin_conv_bwd_magnitude]
+        pin_conv_scan_brute_force, pin_conv_bwd_chain_fd, pin_conv_bwd_numpy, pin_conv_bwd_magnitude,
+        pin_bwd_magnitudes, pin_conv_bwd_magnitude_bracket]
