@@ -178,7 +178,7 @@ def decode_step_bytes(batch, dim, N, in_bytes, gate=True):
     return batch * dim * per + 2 * batch * N * in_bytes + 4 * dim * N + 4 * dim
 
 
-def bench_scan(w, steps, warmup, flush=False, softplus=False, zoh=False, conv_k=0, ckpt=False):
+def bench_scan(w, steps, warmup, flush=False, softplus=False, zoh=False, conv_k=0, ckpt=False, keep_out=False):
     """Times `steps` scans of workload w (after `warmup`).  flush: before each
     timed scan, write a 512 MiB buffer so that no input is cache-resident,
     and time each scan on its own.  softplus / zoh: time the option kernels
@@ -186,7 +186,8 @@ def bench_scan(w, steps, warmup, flush=False, softplus=False, zoh=False, conv_k=
     channel; the timing does not depend on the values).  conv_k: the scan
     with the convolution front of that width (synth.conv_params filter and
     bias, no state).  ckpt: the scan that also writes the checkpoints for
-    the backward (s6_scan_fwd_ckpt)."""
+    the backward (s6_scan_fwd_ckpt).  keep_out: the outputs of the last
+    timed scan are returned in the input dict as "y_out" and "h_last_out"."""
     import torch
     from selective_state_space_63_amd import s6, synth
     inp = synth.device_full(w)
@@ -240,6 +241,8 @@ def bench_scan(w, steps, warmup, flush=False, softplus=False, zoh=False, conv_k=
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n))
+    if keep_out:
+        inp["y_out"], inp["h_last_out"] = y, hl
     return inp, {"mean": ms, "median": per[len(per) // 2], "min": per[0]}, wall
 
 
@@ -385,15 +388,37 @@ def bench_decode_hbm(steps=64, warmup=16, batch=1024):
             "note": "plain launches; 335 MB of state, larger than the Infinity Cache"}
 
 
+def error_report(got, ref, mag):
+    """The three error figures of a parity comparison: the componentwise
+    |got - ref| / m with the oracle's magnitude m (the gated figure), the
+    plain max relative error over elements with |ref| >= 1e-3 max|ref|, and
+    the normwise max|got - ref| / max|ref|."""
+    import numpy as np
+    from oracle.oracle import relative_error, scaled_error
+    ref = np.asarray(ref)
+    big = float(np.max(np.abs(ref))) if ref.size else 0.0
+    norm = float(np.max(np.abs(np.asarray(got, dtype=np.float64) - ref)) / big) if big > 0 else 0.0
+    return {"scaled": scaled_error(got, ref, mag), "relative": relative_error(got, ref), "normwise": norm}
+
+
+def _merge_err(acc, e):
+    return {k: max(acc.get(k, 0.0), v) for k, v in e.items()}
+
+
 def cpu_baseline(w, inp, budget_s=10.0):
     """The fp64 oracle (as it stands, OpenMP over channels) on whole batch
     rows of the same inputs, cycling over the rows until `budget_s` of oracle
     time is spent (at least one row).  The inputs are copied to the host
-    outside the timed region."""
+    outside the timed region.  When the GPU's outputs of the timed scan are
+    in `inp` ("y_out", "h_last_out"), every batch row the oracle computed is
+    also compared with them (after its timing): the returned dict's
+    "max_err" holds the error figures of error_report over those rows."""
     import numpy as np
     import torch
     from oracle.oracle import Oracle
     o = Oracle()
+    errs = {"y": {}, "h_last": {}}
+    checked = set()
 
     def h64(t):
         return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
@@ -411,10 +436,15 @@ def cpu_baseline(w, inp, budget_s=10.0):
                               Bm=h64(inp["Bm"][b:b + 1]), Cm=h64(inp["Cm"][b:b + 1]), Dskip=Dk,
                               z=h64(inp["z"][b:b + 1]))
         t0 = time.perf_counter()
-        o.scan(**rows_in[b])
+        r = o.scan(**rows_in[b])
         spent += time.perf_counter() - t0
         done_tc += w.dim * w.seqlen
         rows += 1
+        if "y_out" in inp and b not in checked:
+            checked.add(b)
+            errs["y"] = _merge_err(errs["y"], error_report(h64(inp["y_out"][b:b + 1]), r["y"], r["m"]))
+            errs["h_last"] = _merge_err(errs["h_last"], error_report(h64(inp["h_last_out"][b:b + 1]), r["h_last"],
+                                                                     r["H_last"]))
     gbs = scan_bytes(w, 2) * (rows / w.batch) / spent / 1e9
     cpu = "unknown"
     try:
@@ -422,10 +452,50 @@ def cpu_baseline(w, inp, budget_s=10.0):
             cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
     except OSError:
         pass
-    return {"value": gbs, "unit": "GB/s", "cores": o.num_threads(), "kind": "oracle",
-            "sample": f"{rows} batch rows of the same workload ({w.dim} channels x {w.seqlen} tokens each, "
-                      f"cycling over its {w.batch} rows), {spent:.2f} s of oracle time on {cpu}",
-            "token_channels_per_s": done_tc / spent}
+    out = {"value": gbs, "unit": "GB/s", "cores": o.num_threads(), "kind": "oracle",
+           "sample": f"{rows} batch rows of the same workload ({w.dim} channels x {w.seqlen} tokens each, "
+                     f"cycling over its {w.batch} rows), {spent:.2f} s of oracle time on {cpu}",
+           "token_channels_per_s": done_tc / spent}
+    if checked:
+        out["max_err"] = {"rows_compared": f"{len(checked)} of {w.batch} batch rows, every channel and token",
+                          "tolerance_scaled": 2e-3 if w.dtype == "bf16" else 1e-5, **errs}
+    return out
+
+
+def cpu_long_baseline(w, inp, budget_s=10.0, block=64):
+    """The oracle on blocks of `block` whole channels (every token) of the
+    long-sequence workload, until `budget_s` of oracle time is spent:
+    token-channels per second and the bytes-equivalent rate.  The GPU's y of
+    the same channels (inp["y_out"], when kept) is compared after timing."""
+    import numpy as np
+    import torch
+    from oracle.oracle import Oracle
+    o = Oracle()
+
+    def h64(t):
+        return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+    spent, chans = 0.0, 0
+    err = {}
+    Bm, Cm = h64(inp["Bm"]), h64(inp["Cm"])
+    while (spent < budget_s or chans == 0) and chans < w.dim:
+        c0, c1 = chans, min(w.dim, chans + block)
+        args = dict(x=h64(inp["x"][:, c0:c1]), delta=h64(inp["delta"][:, c0:c1]), A=h64(inp["A"][c0:c1]), Bm=Bm,
+                    Cm=Cm, Dskip=h64(inp["Dskip"][c0:c1]), z=h64(inp["z"][:, c0:c1]))
+        t0 = time.perf_counter()
+        r = o.scan(**args)
+        spent += time.perf_counter() - t0
+        chans = c1
+        if "y_out" in inp:
+            err = _merge_err(err, error_report(h64(inp["y_out"][:, c0:c1]), r["y"], r["m"]))
+    tc = w.batch * chans * w.seqlen
+    out = {"value": scan_bytes(w, 2) * chans / w.dim / spent / 1e9, "unit": "GB/s",
+           "token_channels_per_s": tc / spent, "cores": o.num_threads(), "kind": "oracle",
+           "sample": f"the first {chans} of {w.dim} channels, all {w.seqlen} tokens, in blocks of {block}; "
+                     f"{spent:.2f} s of oracle time"}
+    if err:
+        out["max_err_y"] = err
+    return out
 
 
 def cpu_backward_baseline(w, inp, channels=256):
@@ -506,29 +576,54 @@ def cpu_conv_baseline(w, inp, conv_k, budget_s=3.0):
             "sample": f"{rows} batch rows ({w.dim} channels x {w.seqlen} tokens each), {spent:.2f} s"}
 
 
-def cpu_decode_baseline(w, budget_s=3.0):
-    """The oracle's single-token step (fp64) on the decode workload's shape,
-    repeated until `budget_s` is spent: state-element updates per second."""
+def cpu_decode_baseline(w, budget_s=10.0):
+    """The oracle's single-token step (fp64) over the decode workload's own
+    steps (the same seeded inputs as the timed decode, from h = 0), step
+    after step until `budget_s` is spent: state-element updates per second.
+    The per-step inputs are copied to the host outside the timed region."""
     import numpy as np
+    import torch
     from oracle.oracle import Oracle
+    from selective_state_space_63_amd import synth
     o = Oracle()
-    rng = np.random.default_rng(0)
+    inp = synth.device_full(w)
+
+    def h64(t):
+        return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
     B, D, N = w.batch, w.dim, w.dstate
-    A = -np.tile(np.arange(1, N + 1, dtype=np.float64), (D, 1))
+    A, Dk = h64(inp["A"]), h64(inp["Dskip"])
     h = np.zeros((B, D, N))
     H = np.zeros((B, D, N))
-    args = dict(x=rng.standard_normal((B, D)), delta=np.full((B, D), 0.01), A=A,
-                Bm=rng.standard_normal((B, N)), Cm=rng.standard_normal((B, N)),
-                Dskip=rng.standard_normal(D), z=rng.standard_normal((B, D)))
     steps = 0
     spent = 0.0
-    while spent < budget_s or steps == 0:
+    while (spent < budget_s or steps == 0) and steps < w.seqlen:
+        s = steps
+        args = dict(x=h64(inp["x"][..., s]), delta=h64(inp["delta"][..., s]), A=A, Bm=h64(inp["Bm"][..., s]),
+                    Cm=h64(inp["Cm"][..., s]), Dskip=Dk, z=h64(inp["z"][..., s]))
         t0 = time.perf_counter()
         o.step(h, H, **args)
         spent += time.perf_counter() - t0
         steps += 1
+    del inp
+    torch.cuda.empty_cache()
     return {"state_updates_per_s": B * D * N * steps / spent, "steps": steps, "seconds": round(spent, 2),
-            "cores": o.num_threads(), "kind": "oracle"}
+            "cores": o.num_threads(), "kind": "oracle",
+            "sample": f"the first {steps} of the workload's {w.seqlen} decode steps (same inputs, from h = 0)"}
+
+
+def versions():
+    """Library ABI, torch and ROCm versions of this run."""
+    import torch
+    from selective_state_space_63_amd import s6
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"libs6_abi": s6.load_library().s6_version(), "torch": torch.__version__, "hip": torch.version.hip,
+            "rocm": rocm}
 
 
 def copy_rate(mib=1024, steps=10):
@@ -617,7 +712,7 @@ def main():
               flush=True)
         return
     print(f"[bench] scan {w.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
-    inp, tm, wall = bench_scan(w, args.steps, args.warmup)
+    inp, tm, wall = bench_scan(w, args.steps, args.warmup, keep_out=True)
     ms = tm["mean"]
     slots = scan_valu_slots(w)
     tslots = slots / (ms * 1e-3) / 1e12
@@ -651,13 +746,18 @@ def main():
         # every (token, channel, state)), not by HBM: "achieved" is the
         # method's VALU lane-slots per second against the VALU issue peak;
         # the HBM side is given beside it.
+        # The achieved figure is the method's algorithmic bytes over the
+        # kernel's mean launch time, against the HBM peak.  The kernel's own
+        # limit is VALU issue (N exponentials and FMAs per token-channel):
+        # its fraction of the VALU issue peak is given beside it.
         "copy_GBps": round(cp_gbs, 1),
         "frac_of_copy": round(gbs / cp_gbs, 4),
-        "roofline": {"bound": "alu", "achieved": round(tslots, 2), "peak": VALU_PEAK_TSLOTS,
-                     "unit": "Tslot/s", "frac": round(tslots / VALU_PEAK_TSLOTS, 4),
-                     "valu_slots_per_launch": slots,
-                     "hbm_GBps": round(gbs, 1), "hbm_peak_GBps": HBM_PEAK_GBS,
-                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": byts,
+                     "valu": {"achieved_Tslot_s": round(tslots, 2), "peak_Tslot_s": VALU_PEAK_TSLOTS,
+                              "frac": round(tslots / VALU_PEAK_TSLOTS, 4), "slots_per_launch": slots}},
+        "versions": versions(),
     }
     if not args.no_decode:
         print("[bench] decode", file=sys.stderr, flush=True)
@@ -669,8 +769,12 @@ def main():
     if not args.no_extra:
         wl = synth.WORKLOADS["long"]
         print(f"[bench] scan {wl.name}", file=sys.stderr, flush=True)
-        _, tl, _ = bench_scan(wl, 5, 2)
+        inp_long, tl, _ = bench_scan(wl, 5, 2, keep_out=True)
         out["long"] = scan_line("long", wl, tl, 2, "sequence cut into segments + carry fold (two passes)", True)
+        if not args.no_cpu_baseline:
+            print("[bench] cpu baseline of the long sequence (oracle)", file=sys.stderr, flush=True)
+            out["long"]["cpu_baseline"] = cpu_long_baseline(wl, inp_long)
+        del inp_long
         torch.cuda.empty_cache()
         wm = synth.WORKLOADS["m130"]
         print(f"[bench] scan {wm.name} hot and cold", file=sys.stderr, flush=True)
@@ -723,6 +827,8 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inp)
+        if "max_err" in out["cpu_baseline"]:
+            out["max_err"] = out["cpu_baseline"].pop("max_err")
         if "decode" in out:
             out["decode"]["cpu_baseline"] = cpu_decode_baseline(synth.WORKLOADS["decode"])
         if "backward" in out:

@@ -50,17 +50,24 @@
  *     before any HIP call, so a rejected call has no side effect.  Values are
  *     not checked: NaN/Inf propagate.  Accuracy is specified for A <= 0 and
  *     delta >= 0 (decaying states).
- *   Memory: when there are too few (batch, channel) blocks to fill the GPU
- *     (few long rows), s6_scan_fwd and s6_last_state split the sequence into
- *     segments and take the per-segment carries from the stream-ordered
- *     allocator (hipMallocAsync), releasing them on the same stream before
- *     returning; otherwise, and in the decode steps, nothing is allocated.
- *     The backward entry points take their workspace (segment states,
- *     partial sums) from the same allocator in the same way.
+ *   Memory: the library allocates nothing and keeps no state between calls.
+ *     Entry points that may need scratch memory take a caller-owned device
+ *     workspace (void* workspace, size_t workspace_bytes), 256-byte aligned,
+ *     of at least the size the matching *_workspace_size query returns for
+ *     the same sizes on the same device (0 when none is needed; NULL is then
+ *     accepted).  The forward and final-state scans need one only when there
+ *     are too few (batch, channel) blocks to fill the GPU and the sequence is
+ *     cut into segments (per-segment carries); the backward always does
+ *     (segment states, partial sums).  A call only enqueues work that uses the
+ *     workspace: it must stay allocated, and not be used by other work, until
+ *     that work has run on the stream.  Too small or NULL when needed:
+ *     S6_ERR_WORKSPACE, before any work is enqueued.  Its contents on entry
+ *     do not matter and are left undefined.
  */
 #ifndef S6_H_
 #define S6_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -78,6 +85,7 @@ extern "C" {
 #define S6_ERR_ALIGN (-5)       /* a pointer is not aligned to its element size */
 #define S6_ERR_HIP (-6)         /* a HIP call failed; s6_status_str gives the detail */
 #define S6_ERR_FLAGS (-7)       /* unknown bits in the flags of an _ex entry point */
+#define S6_ERR_WORKSPACE (-8)   /* the workspace is NULL or smaller than its *_workspace_size */
 
 /* Options of the _ex entry points (bit flags). */
 #define S6_DELTA_SOFTPLUS 1 /* step = softplus(delta + delta_bias[d]) */
@@ -98,18 +106,31 @@ const char* s6_status_str(int status);
  *   h0    : nullable (zero initial state).
  *   y     : required output (batch, dim, seqlen) fp32.
  *   h_last: nullable output (batch, dim, dstate) fp32, the state after the
- *           last token. */
+ *           last token.
+ *   workspace, workspace_bytes: see Memory above; the size is
+ *           s6_scan_fwd_workspace_size for the same sizes (it serves the
+ *           _ex, _ckpt and convolution-front forms as well). */
 int s6_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                 const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
                 const float* Dskip, const void* z, const float* h0, float* y, float* h_last,
-                void* stream);
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace size in bytes (*bytes) of the forward scans (s6_scan_fwd,
+ * s6_scan_fwd_ex, s6_scan_fwd_ckpt, s6_conv_scan_fwd) and of the final-state
+ * scans (s6_last_state, s6_last_state_ex) for these sizes on the current
+ * device.  Checks the sizes as the entry points do; bytes: required. */
+int s6_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                               size_t* bytes);
+int s6_last_state_workspace_size(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                                 size_t* bytes);
 
 /* Final state only (prefill -> decode hand-off, or a sequence shard's
  * carry): the recurrence of s6_scan_fwd without C, D, z or y.
- *   h0 : nullable.   h_last : required output (batch, dim, dstate) fp32. */
+ *   h0 : nullable.   h_last : required output (batch, dim, dstate) fp32.
+ *   workspace: s6_last_state_workspace_size bytes. */
 int s6_last_state(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                   const void* x, const void* delta, const float* A, const void* Bm,
-                  const float* h0, float* h_last, void* stream);
+                  const float* h0, float* h_last, void* workspace, size_t workspace_bytes, void* stream);
 
 /* One decode token for every (batch, channel): h is read, advanced by one
  * step and written back in place; y receives the token's output.  batch*dim
@@ -139,11 +160,13 @@ int s6_state_update(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, fl
 int s6_scan_fwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                    const void* x, const void* delta, const float* delta_bias, int flags,
                    const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
-                   const float* h0, float* y, float* h_last, void* stream);
+                   const float* h0, float* y, float* h_last, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 int s6_last_state_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                      const void* x, const void* delta, const float* delta_bias, int flags,
-                     const float* A, const void* Bm, const float* h0, float* h_last, void* stream);
+                     const float* A, const void* Bm, const float* h0, float* h_last, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 int s6_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, int in_dtype, float* h,
                        const void* x, const void* delta, const float* delta_bias, int flags,
@@ -171,7 +194,8 @@ int s6_conv_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
                      const void* x, const float* conv_w, const float* conv_bias, int conv_width,
                      const float* conv_state, const void* delta, const float* delta_bias, int flags,
                      const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
-                     const float* h0, float* y, float* h_last, void* stream);
+                     const float* h0, float* y, float* h_last, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /* One decode token with the convolution front of s6_conv_scan_fwd: the
  * filter runs over the conv_width - 1 kept inputs and this token's x, the
@@ -204,15 +228,25 @@ int s6_conv_state_update(int64_t batch, int64_t dim, int64_t dstate, int in_dtyp
  *   dDskip : nullable (dim).   dh0 : nullable (batch, dim, dstate), the
  *            gradient of the initial state (h0 itself may be NULL = zero).
  * Sums over channels (dBm, dCm), over batch rows and tokens (dA, dDskip) are
- * taken in a fixed order: repeated calls give identical bits.  Workspace from
- * the stream-ordered allocator (hipMallocAsync), released on the stream before
- * returning: about 2*(dim/16)*batch*dstate*seqlen + 2*batch*dim*dstate*seqlen/64
- * floats. */
+ * taken in a fixed order: repeated calls give identical bits.
+ *   workspace: s6_scan_bwd_workspace_size(..., conv_width = 0, from_ckpt =
+ *            0, ...) bytes (see Memory above). */
 int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                 const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
                 const float* Dskip, const void* z, const float* h0, const float* dy,
                 const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm, float* dCm,
-                float* dDskip, float* dz, float* dh0, void* stream);
+                float* dDskip, float* dz, float* dh0, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace size in bytes (*bytes) of the backward entry points on the
+ * current device: conv_width = 0 for s6_scan_bwd, s6_scan_bwd_ex and
+ * s6_scan_bwd_ckpt, the filter width for s6_conv_scan_bwd; from_ckpt != 0
+ * for s6_scan_bwd_ckpt (it needs no room for the recomputed segment
+ * states).  Its largest parts are the per-16-channel-block partial sums of
+ * dBm and dCm (2 * ceil(dim/16) * batch * dstate * seqlen floats) and, without
+ * checkpoints, the state entering every 64-token segment (batch * dim *
+ * dstate * ceil(seqlen/64) floats). */
+int s6_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                               int conv_width, int from_ckpt, size_t* bytes);
 
 /* s6_scan_bwd with the step bias and the options of s6_scan_fwd_ex (other
  * flag bits: S6_ERR_FLAGS).  ddelta is then the gradient of the stored delta
@@ -227,7 +261,8 @@ int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, i
                    const void* x, const void* delta, const float* delta_bias, int flags, const float* A,
                    const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
                    const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
-                   float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* stream);
+                   float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /* Gradients of s6_conv_scan_fwd: the scan's gradients as from s6_scan_bwd_ex
  * (with the same step options), taken on the filtered input x', then carried
@@ -250,7 +285,8 @@ int s6_conv_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
                      const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
                      const float* h0, const float* dy, const float* dh_last, float* dx, float* ddelta,
                      float* dA, float* dBm, float* dCm, float* dDskip, float* dz, float* dh0,
-                     float* ddelta_bias, float* dconv_w, float* dconv_bias, float* dconv_state, void* stream);
+                     float* ddelta_bias, float* dconv_w, float* dconv_bias, float* dconv_state, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /* Checkpoints for training: the forward saves the state entering every
  * S6_CKPT_TOKENS-token block, and the backward starts from them instead of
@@ -270,13 +306,15 @@ int s6_conv_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
 int s6_scan_fwd_ckpt(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                      const void* x, const void* delta, const float* delta_bias, int flags,
                      const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
-                     const float* h0, float* y, float* h_last, float* ckpt, void* stream);
+                     const float* h0, float* y, float* h_last, float* ckpt, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 int s6_scan_bwd_ckpt(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                      const void* x, const void* delta, const float* delta_bias, int flags, const float* A,
                      const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* ckpt,
                      const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
-                     float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* stream);
+                     float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -910,6 +910,66 @@ int launch_bwd(const BwdArgs& a, bool gate, int64_t parts, bool carry, hipStream
 
 int bwd_channels_per_block(int64_t dstate) { return dstate <= 16 ? 4 * bwd_waves<1>() : 4 * bwd_waves<2>(); }
 
+// The backward's launch geometry and the byte offsets (256-aligned) of its
+// buffers in the caller's workspace.
+struct BwdWs {
+  int64_t S, nblkb, G, spp, nlb;  // segments, channel blocks, parts, segments per part, front blocks
+  size_t agg, sd, hin;            // checkpoint pass: segment end states, summed deltas, incoming states
+  size_t dap, ddp, dbp;           // per (part, row) partials of dA, dD and the bias gradient
+  size_t dBp, dCp;                // per channel-block partials of dB and dC
+  size_t cM, muin, cSD;           // parts: adjoint carries and summed deltas
+  size_t dxo, cpart;              // convolution front: gradient of x', filter/bias partials
+  size_t total;                   // 0: the grid limits are exceeded
+};
+
+BwdWs bwd_ws_layout(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, bool ckpt, bool conv) {
+  BwdWs w;
+  memset(&w, 0, sizeof(w));
+  w.S = (seqlen + kBwdSeg - 1) / kBwdSeg;
+  const int64_t nagg = w.S - 1;
+  const int64_t cw = bwd_channels_per_block(dstate);
+  w.nblkb = (dim + cw - 1) / cw;
+  if (w.nblkb * batch > INT32_MAX) return w;  // grid size
+  // Parts: when the (row, channel block) workgroups fill less than half of
+  // the workgroup slots (few long rows), the sequence is cut into parts run
+  // side by side; the adjoint carry entering each part from the right comes
+  // from a carry pass and a fold.
+  int64_t G = 1;
+  {
+    const int64_t wgs = w.nblkb * batch;
+    const int64_t slots = (int64_t)cu_count() * (dstate <= 16 ? 4 : 3);
+    if (2 * wgs <= slots) G = slots / wgs < w.S ? slots / wgs : w.S;
+    if (G < 1) G = 1;
+  }
+  w.spp = (w.S + G - 1) / G;
+  w.G = (w.S + w.spp - 1) / w.spp;
+  w.nlb = (seqlen + 256 * kConvTok - 1) / (256 * kConvTok);
+  if (conv && (double)batch * dim * w.nlb > (double)INT32_MAX) return w;
+  const int64_t nstate = batch * dim * dstate;
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += up(bytes);
+    return o;
+  };
+  w.agg = take(ckpt ? 0 : (size_t)(nagg > 0 ? nagg : 0) * nstate * sizeof(float));
+  w.sd = take(ckpt ? 0 : (size_t)(nagg > 0 ? nagg : 0) * batch * dim * sizeof(float));
+  w.hin = take(ckpt ? 0 : (size_t)w.S * nstate * sizeof(float));
+  w.dap = take((size_t)w.G * nstate * sizeof(float));
+  w.ddp = take((size_t)w.G * batch * dim * sizeof(float));
+  w.dbp = take((size_t)w.G * batch * dim * sizeof(float));
+  w.dBp = take((size_t)w.nblkb * batch * dstate * seqlen * sizeof(float));
+  w.dCp = take((size_t)w.nblkb * batch * dstate * seqlen * sizeof(float));
+  w.cM = take(w.G > 1 ? (size_t)w.G * nstate * sizeof(float) : 0);
+  w.muin = take(w.G > 1 ? (size_t)w.G * nstate * sizeof(float) : 0);
+  w.cSD = take(w.G > 1 ? (size_t)w.G * batch * dim * sizeof(float) : 0);
+  w.dxo = take(conv ? (size_t)batch * dim * seqlen * sizeof(float) : 0);
+  w.cpart = take(conv ? (size_t)batch * w.nlb * dim * (kMaxConv + 1) * sizeof(float) : 0);
+  w.total = off;
+  return w;
+}
+
 }  // namespace
 
 }  // namespace s6i
@@ -937,7 +997,7 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
                   const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
                   const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
                   float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, const float* ckpt,
-                  void* stream, const ConvGrad& cg = ConvGrad()) {
+                  void* workspace, size_t workspace_bytes, void* stream, const ConvGrad& cg = ConvGrad()) {
   static_assert(kBwdSeg == kCkpt, "backward segments are the checkpoint blocks");
   const bool conv = cg.w != nullptr || cg.width != 0;
   int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
@@ -982,70 +1042,25 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
     return dh0 ? launch_copy_state(dh_last, dh0, nstate, st) : S6_OK;
   }
 
-  // workspace: segment states (pass 1, fold), per-row and per-block partials
-  const int64_t S = (seqlen + kBwdSeg - 1) / kBwdSeg;
-  const int64_t nagg = S - 1;
-  const int64_t cw = bwd_channels_per_block(dstate);
-  const int64_t nblkb = (dim + cw - 1) / cw;
-  if (nblkb * batch > INT32_MAX) return S6_ERR_SHAPE;  // grid size
-  // Parts: when the (row, channel block) workgroups fill less than half of
-  // the workgroup slots (few long rows), the sequence is cut into parts run
-  // side by side; the adjoint carry entering each part from the right comes
-  // from a carry pass and a fold.
-  int64_t G = 1;
-  {
-    const int64_t wgs = nblkb * batch;
-    const int64_t slots = (int64_t)cu_count() * (dstate <= 16 ? 4 : 3);
-    if (2 * wgs <= slots) G = slots / wgs < S ? slots / wgs : S;
-    if (G < 1) G = 1;
-  }
-  const int64_t spp = (S + G - 1) / G;  // segments per part
-  G = (S + spp - 1) / spp;
-  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-  const size_t agg_b = ckpt ? 0 : (size_t)(nagg > 0 ? nagg : 0) * nstate * sizeof(float);
-  const size_t sd_b = ckpt ? 0 : (size_t)(nagg > 0 ? nagg : 0) * batch * dim * sizeof(float);
-  const size_t hin_b = ckpt ? 0 : (size_t)S * nstate * sizeof(float);
-  const size_t dap_b = (size_t)G * nstate * sizeof(float);
-  const size_t ddp_b = (size_t)G * batch * dim * sizeof(float);
-  const size_t bc_b = (size_t)nblkb * batch * dstate * seqlen * sizeof(float);
-  const size_t mu_b = G > 1 ? (size_t)G * nstate * sizeof(float) : 0;     // carries: M and mu_in
-  const size_t csd_b = G > 1 ? (size_t)G * batch * dim * sizeof(float) : 0;
-  // convolution front: the gradient of its output x' (the adjoint kernel's
-  // dx) and the per-block partials of the filter's and bias's gradients
-  const int64_t nlb = (seqlen + 256 * kConvTok - 1) / (256 * kConvTok);
-  const size_t dxo_b = conv ? (size_t)batch * dim * seqlen * sizeof(float) : 0;
-  const size_t cpart_b = conv ? (size_t)batch * nlb * dim * (kMaxConv + 1) * sizeof(float) : 0;
-  if (conv && (double)batch * dim * nlb > (double)INT32_MAX) return S6_ERR_SHAPE;
-  const size_t total = up(agg_b) + up(sd_b) + up(hin_b) + up(dap_b) + 2 * up(ddp_b) + 2 * up(bc_b) + 2 * up(mu_b) +
-                       up(csd_b) + up(dxo_b) + up(cpart_b);
-  void* ws = nullptr;
-  S6_HIP(hipMallocAsync(&ws, total, st), "hipMallocAsync(backward workspace)");
-  char* wp = static_cast<char*>(ws);
-  float* agg = reinterpret_cast<float*>(wp);
-  wp += up(agg_b);
-  float* sd = reinterpret_cast<float*>(wp);
-  wp += up(sd_b);
-  const float* hin = ckpt ? ckpt : reinterpret_cast<float*>(wp);
-  wp += up(hin_b);
-  float* dap = reinterpret_cast<float*>(wp);
-  wp += up(dap_b);
-  float* ddp = reinterpret_cast<float*>(wp);
-  wp += up(ddp_b);
-  float* dbp = reinterpret_cast<float*>(wp);  // bias gradient per part and row
-  wp += up(ddp_b);
-  float* dBp = reinterpret_cast<float*>(wp);
-  wp += up(bc_b);
-  float* dcp = reinterpret_cast<float*>(wp);
-  wp += up(bc_b);
-  float* cM = reinterpret_cast<float*>(wp);
-  wp += up(mu_b);
-  float* muin = reinterpret_cast<float*>(wp);
-  wp += up(mu_b);
-  float* cSD = reinterpret_cast<float*>(wp);
-  wp += up(csd_b);
-  float* dxo = conv ? reinterpret_cast<float*>(wp) : nullptr;
-  wp += up(dxo_b);
-  float* cpart = reinterpret_cast<float*>(wp);
+  const BwdWs w = bwd_ws_layout(batch, dim, seqlen, dstate, ckpt != nullptr, conv);
+  if (w.total == 0) return S6_ERR_SHAPE;  // grid limits
+  if (!workspace || workspace_bytes < w.total) return S6_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return S6_ERR_ALIGN;
+  const int64_t S = w.S, nagg = S - 1, nblkb = w.nblkb, G = w.G, spp = w.spp, nlb = w.nlb;
+  char* wp = static_cast<char*>(workspace);
+  float* agg = reinterpret_cast<float*>(wp + w.agg);
+  float* sd = reinterpret_cast<float*>(wp + w.sd);
+  const float* hin = ckpt ? ckpt : reinterpret_cast<float*>(wp + w.hin);
+  float* dap = reinterpret_cast<float*>(wp + w.dap);
+  float* ddp = reinterpret_cast<float*>(wp + w.ddp);
+  float* dbp = reinterpret_cast<float*>(wp + w.dbp);  // bias gradient per part and row
+  float* dBp = reinterpret_cast<float*>(wp + w.dBp);
+  float* dcp = reinterpret_cast<float*>(wp + w.dCp);
+  float* cM = reinterpret_cast<float*>(wp + w.cM);
+  float* muin = reinterpret_cast<float*>(wp + w.muin);
+  float* cSD = reinterpret_cast<float*>(wp + w.cSD);
+  float* dxo = conv ? reinterpret_cast<float*>(wp + w.dxo) : nullptr;
+  float* cpart = reinterpret_cast<float*>(wp + w.cpart);
 
   // pass 1: end state (from zero) and summed delta of every segment but the last
   if (nagg > 0 && !ckpt) {
@@ -1116,8 +1131,6 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) rc = hip_fail(e, "s6_conv_bwd launch");
   }
-  hipError_t e = hipFreeAsync(ws, st);
-  if (rc == S6_OK && e != hipSuccess) rc = hip_fail(e, "hipFreeAsync(backward workspace)");
   return rc;
 }
 
@@ -1129,19 +1142,23 @@ int s6_scan_bwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, i
                    const void* x, const void* delta, const float* delta_bias, int flags, const float* A,
                    const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
                    const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
-                   float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* stream) {
+                   float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   return scan_bwd_impl(batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm, Dskip, z, h0,
-                       dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, ddelta_bias, nullptr, stream);
+                       dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, ddelta_bias, nullptr, workspace,
+                       workspace_bytes, stream);
 }
 
 int s6_scan_bwd_ckpt(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                      const void* x, const void* delta, const float* delta_bias, int flags, const float* A,
                      const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* ckpt,
                      const float* dy, const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm,
-                     float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* stream) {
+                     float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   if (!ckpt && batch > 0 && dim > 0 && seqlen > 0) return S6_ERR_NULL;
   return scan_bwd_impl(batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm, Dskip, z,
-                       nullptr, dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, ddelta_bias, ckpt, stream);
+                       nullptr, dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, ddelta_bias, ckpt, workspace,
+                       workspace_bytes, stream);
 }
 
 int s6_conv_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
@@ -1150,7 +1167,8 @@ int s6_conv_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
                      const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
                      const float* h0, const float* dy, const float* dh_last, float* dx, float* ddelta,
                      float* dA, float* dBm, float* dCm, float* dDskip, float* dz, float* dh0,
-                     float* ddelta_bias, float* dconv_w, float* dconv_bias, float* dconv_state, void* stream) {
+                     float* ddelta_bias, float* dconv_w, float* dconv_bias, float* dconv_state, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   if (!conv_w && conv_width == 0) return S6_ERR_NULL;
   ConvGrad cg;
   cg.w = conv_w;
@@ -1161,16 +1179,32 @@ int s6_conv_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
   cg.dbias = dconv_bias;
   cg.dstate = dconv_state;
   return scan_bwd_impl(batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm, Dskip, z, h0,
-                       dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, ddelta_bias, nullptr, stream, cg);
+                       dy, dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, ddelta_bias, nullptr, workspace,
+                       workspace_bytes, stream, cg);
 }
 
 int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                 const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
                 const float* Dskip, const void* z, const float* h0, const float* dy,
                 const float* dh_last, float* dx, float* ddelta, float* dA, float* dBm, float* dCm,
-                float* dDskip, float* dz, float* dh0, void* stream) {
+                float* dDskip, float* dz, float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
   return s6_scan_bwd_ex(batch, dim, seqlen, dstate, in_dtype, x, delta, nullptr, 0, A, Bm, Cm, Dskip, z, h0, dy,
-                        dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, nullptr, stream);
+                        dh_last, dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, nullptr, workspace, workspace_bytes,
+                        stream);
+}
+
+int s6_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                               int conv_width, int from_ckpt, size_t* bytes) {
+  if (!bytes) return S6_ERR_NULL;
+  int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
+  if (rc) return rc;
+  if (conv_width < 0 || conv_width > kMaxConv) return S6_ERR_UNSUPPORTED;
+  *bytes = 0;
+  if (batch == 0 || dim == 0 || seqlen == 0) return S6_OK;
+  const BwdWs w = bwd_ws_layout(batch, dim, seqlen, dstate, from_ckpt != 0, conv_width > 0);
+  if (w.total == 0) return S6_ERR_SHAPE;
+  *bytes = w.total;
+  return S6_OK;
 }
 
 }  // extern "C"

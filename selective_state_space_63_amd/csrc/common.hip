@@ -41,15 +41,10 @@ int check_common(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int
 }
 
 int cu_count() {
-  static int cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] <= 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
 }
 
 void fill(float* p, float v, int64_t n, hipStream_t st) {
@@ -65,7 +60,7 @@ using namespace s6i;
 
 extern "C" {
 
-int s6_version(void) { return 10300; }
+int s6_version(void) { return 20000; }
 
 const char* s6_status_str(int status) {
   switch (status) {
@@ -76,6 +71,7 @@ const char* s6_status_str(int status) {
     case S6_ERR_UNSUPPORTED: return "unsupported: dstate outside 1..32, filter width outside 1..4, or an option this entry point lacks";
     case S6_ERR_ALIGN: return "a pointer is not aligned to its element size";
     case S6_ERR_FLAGS: return "unknown option bits in flags";
+    case S6_ERR_WORKSPACE: return "the call needs a workspace: none given, or smaller than its *_workspace_size";
     case S6_ERR_HIP: return g_err[0] ? g_err : "HIP error";
     default: return "unknown status";
   }

@@ -140,13 +140,24 @@ struct Plan {
   bool vec;           // 16-byte staging and 8-byte stores
 };
 
-// Compute units of the current device (cached; 256 on MI355X).
+// Compute units of the current device (256 on MI355X; 256 when no device
+// can be queried).
 int cu_count();
 
 // Launch plan of a scan: waves per workgroup, channel blocks, segments, and
 // whether the 16-byte load path applies (every pointer in ptrs aligned).
 Plan make_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, size_t esz,
                const void* const* ptrs, int nptr);
+
+// Byte offsets of a segmented scan's buffers in the caller's workspace, and
+// its size (all zero when the plan has one segment).
+struct ScanWs {
+  size_t agg;    // segment end states from a zero state (nagg, batch, D, N)
+  size_t sd;     // summed delta of those segments (nagg, batch, D)
+  size_t hin;    // state entering every segment (S, batch, D, N), fused pass only
+  size_t total;
+};
+ScanWs scan_ws_layout(bool want_y, const Plan& p, int64_t batch, int64_t dim, int64_t dstate);
 
 // One launch of the scan kernel (mode kModeY or kModeState) over `segs`
 // segments; the option kernels when a.softplus, a.zoh, a.dbias or a.conv_w

@@ -77,6 +77,22 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, size_
   return p;
 }
 
+// Offsets (bytes, 256-aligned) of the segmented scan's buffers in the
+// workspace: segment end states (nagg, batch, D, N), summed deltas (nagg,
+// batch, D) and, for the fused pass, incoming states (S, batch, D, N).
+ScanWs scan_ws_layout(bool want_y, const Plan& p, int64_t batch, int64_t dim, int64_t dstate) {
+  ScanWs w{0, 0, 0, 0};
+  if (p.segs <= 1) return w;
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const int64_t nstate = batch * dim * dstate;
+  const int64_t nagg = want_y ? p.segs - 1 : p.segs;
+  w.agg = 0;
+  w.sd = up((size_t)nagg * nstate * sizeof(float));
+  w.hin = w.sd + up((size_t)nagg * batch * dim * sizeof(float));
+  w.total = w.hin + (want_y ? up((size_t)p.segs * nstate * sizeof(float)) : 0);
+  return w;
+}
+
 // Kernels with the discretisation options and the convolution front only
 // when one is set, so the plain path keeps its own code.
 int launch_scan_any(int in_dtype, int mode, const ScanArgs& a, const Plan& p, bool gate, int64_t batch,
@@ -120,8 +136,8 @@ struct ConvFront {
 int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
               const void* x, const void* delta, const float* dbias, int flags, const float* A,
               const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
-              float* y, float* h_last, void* stream, const ConvFront& cf = ConvFront(),
-              float* ckpt = nullptr) {
+              float* y, float* h_last, void* workspace, size_t workspace_bytes, void* stream,
+              const ConvFront& cf = ConvFront(), float* ckpt = nullptr) {
   int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
   if (rc) return rc;
   if (flags & ~(S6_DELTA_SOFTPLUS | S6_ZOH_EXACT)) return S6_ERR_FLAGS;
@@ -161,6 +177,9 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
   const Plan p = make_plan(batch, dim, seqlen, dstate, esz, vecptrs, 6);
   const bool gate = want_y && z != nullptr;
   const int64_t S = p.segs;
+  const ScanWs wl = scan_ws_layout(want_y, p, batch, dim, dstate);
+  if (wl.total > 0 && (!workspace || workspace_bytes < wl.total)) return S6_ERR_WORKSPACE;
+  if (wl.total > 0 && !aligned(workspace, 256)) return S6_ERR_ALIGN;
 
   ScanArgs a;
   memset(&a, 0, sizeof(a));
@@ -181,18 +200,13 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
     return launch_scan_any(in_dtype, want_y ? kModeY : kModeState, a, p, gate, batch, 1, st);
   }
 
-  // Segmented: workspace for segment end states, summed deltas and carries.
+  // Segmented: the caller's workspace holds the segment end states, summed
+  // deltas and incoming states.
   const int64_t nagg = want_y ? S - 1 : S;
-  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-  const size_t agg_bytes = (size_t)nagg * nstate * sizeof(float);
-  const size_t sd_bytes = (size_t)nagg * batch * dim * sizeof(float);
-  const size_t hin_bytes = want_y ? (size_t)S * nstate * sizeof(float) : 0;
-  void* ws = nullptr;
-  S6_HIP(hipMallocAsync(&ws, up(agg_bytes) + up(sd_bytes) + up(hin_bytes), st), "hipMallocAsync(workspace)");
-  char* wp = static_cast<char*>(ws);
-  float* agg = reinterpret_cast<float*>(wp);
-  float* sd = reinterpret_cast<float*>(wp + up(agg_bytes));
-  float* hin = reinterpret_cast<float*>(wp + up(agg_bytes) + up(sd_bytes));
+  char* wp = static_cast<char*>(workspace);
+  float* agg = reinterpret_cast<float*>(wp + wl.agg);
+  float* sd = reinterpret_cast<float*>(wp + wl.sd);
+  float* hin = reinterpret_cast<float*>(wp + wl.hin);
 
   // pass 1: end states of the first nagg segments from a zero state
   ScanArgs g = a;
@@ -219,9 +233,20 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
     m.y = y;
     rc = launch_scan_any(in_dtype, kModeY, m, p, gate, batch, S, st);
   }
-  hipError_t e = hipFreeAsync(ws, st);
-  if (rc == S6_OK && e != hipSuccess) rc = hip_fail(e, "hipFreeAsync(workspace)");
   return rc;
+}
+
+// Workspace of the forward (want_y) or the final-state scan.
+int scan_ws_query(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                  size_t* bytes) {
+  if (!bytes) return S6_ERR_NULL;
+  int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
+  if (rc) return rc;
+  *bytes = 0;
+  if (batch == 0 || dim == 0 || seqlen == 0) return S6_OK;
+  const Plan p = make_plan(batch, dim, seqlen, dstate, in_dtype == S6_BF16 ? 2 : 4, nullptr, 0);
+  *bytes = scan_ws_layout(want_y, p, batch, dim, dstate).total;
+  return S6_OK;
 }
 
 }  // namespace
@@ -235,24 +260,26 @@ extern "C" {
 int s6_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                 const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
                 const float* Dskip, const void* z, const float* h0, float* y, float* h_last,
-                void* stream) {
+                void* workspace, size_t workspace_bytes, void* stream) {
   return scan_impl(true, batch, dim, seqlen, dstate, in_dtype, x, delta, nullptr, 0, A, Bm, Cm, Dskip,
-                   z, h0, y, h_last, stream);
+                   z, h0, y, h_last, workspace, workspace_bytes, stream);
 }
 
 int s6_scan_fwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                    const void* x, const void* delta, const float* delta_bias, int flags,
                    const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
-                   const float* h0, float* y, float* h_last, void* stream) {
+                   const float* h0, float* y, float* h_last, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   return scan_impl(true, batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm,
-                   Dskip, z, h0, y, h_last, stream);
+                   Dskip, z, h0, y, h_last, workspace, workspace_bytes, stream);
 }
 
 int s6_conv_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                      const void* x, const float* conv_w, const float* conv_bias, int conv_width,
                      const float* conv_state, const void* delta, const float* delta_bias, int flags,
                      const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
-                     const float* h0, float* y, float* h_last, void* stream) {
+                     const float* h0, float* y, float* h_last, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   ConvFront cf;
   cf.w = conv_w;
   cf.bias = conv_bias;
@@ -260,30 +287,42 @@ int s6_conv_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
   cf.width = conv_width;
   if (!conv_w && conv_width == 0) return S6_ERR_NULL;
   return scan_impl(true, batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm,
-                   Dskip, z, h0, y, h_last, stream, cf);
+                   Dskip, z, h0, y, h_last, workspace, workspace_bytes, stream, cf);
 }
 
 int s6_scan_fwd_ckpt(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                      const void* x, const void* delta, const float* delta_bias, int flags,
                      const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
-                     const float* h0, float* y, float* h_last, float* ckpt, void* stream) {
+                     const float* h0, float* y, float* h_last, float* ckpt, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   if (!ckpt && batch > 0 && dim > 0 && seqlen > 0) return S6_ERR_NULL;
   return scan_impl(true, batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm, Cm,
-                   Dskip, z, h0, y, h_last, stream, ConvFront(), ckpt);
+                   Dskip, z, h0, y, h_last, workspace, workspace_bytes, stream, ConvFront(), ckpt);
 }
 
 int s6_last_state(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                   const void* x, const void* delta, const float* A, const void* Bm,
-                  const float* h0, float* h_last, void* stream) {
+                  const float* h0, float* h_last, void* workspace, size_t workspace_bytes, void* stream) {
   return scan_impl(false, batch, dim, seqlen, dstate, in_dtype, x, delta, nullptr, 0, A, Bm, nullptr,
-                   nullptr, nullptr, h0, nullptr, h_last, stream);
+                   nullptr, nullptr, h0, nullptr, h_last, workspace, workspace_bytes, stream);
 }
 
 int s6_last_state_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                      const void* x, const void* delta, const float* delta_bias, int flags,
-                     const float* A, const void* Bm, const float* h0, float* h_last, void* stream) {
+                     const float* A, const void* Bm, const float* h0, float* h_last, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   return scan_impl(false, batch, dim, seqlen, dstate, in_dtype, x, delta, delta_bias, flags, A, Bm,
-                   nullptr, nullptr, nullptr, h0, nullptr, h_last, stream);
+                   nullptr, nullptr, nullptr, h0, nullptr, h_last, workspace, workspace_bytes, stream);
+}
+
+int s6_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                               size_t* bytes) {
+  return scan_ws_query(true, batch, dim, seqlen, dstate, in_dtype, bytes);
+}
+
+int s6_last_state_workspace_size(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                                 size_t* bytes) {
+  return scan_ws_query(false, batch, dim, seqlen, dstate, in_dtype, bytes);
 }
 
 }  // extern "C"

@@ -44,6 +44,26 @@ def problem(w: synth.Workload, with_h0: bool, seed_h0: int = 5):
     return d, o
 
 
+# Every comparison made through scaled(): (test, scaled, relative, normwise,
+# elements).  conftest.py prints them at the end of the session.
+ERRORS: list[tuple] = []
+
+
 def scaled(got, ref, mag):
-    from oracle.oracle import scaled_error
-    return scaled_error(got, ref, mag)
+    """The gated error |got - ref| / m (m: the oracle's magnitude; the bars
+    of TOL), recorded together with the plain max relative error over
+    elements with |ref| >= 1e-3 max|ref| and the normwise error
+    max|got - ref| / max|ref|, which are reported, not gated."""
+    import os
+
+    from oracle.oracle import relative_error, scaled_error
+    e = scaled_error(got, ref, mag)
+    ref = np.asarray(ref, dtype=np.float64)
+    big = float(np.max(np.abs(ref))) if ref.size else 0.0
+    got64 = np.asarray(got, dtype=np.float64)
+    norm = float(np.max(np.abs(got64 - ref)) / big) if big > 0 and np.all(np.isfinite(got64)) else (
+        0.0 if big == 0 else float("inf"))
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    ERRORS.append((test, e, relative_error(got, ref) if np.all(np.isfinite(got64)) else float("inf"), norm,
+                   int(ref.size)))
+    return e

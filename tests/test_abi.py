@@ -48,10 +48,10 @@ def codes():
 
 def test_header_declares_the_entry_points():
     assert header_functions() == ["s6_conv_scan_bwd", "s6_conv_scan_fwd", "s6_conv_state_update", "s6_last_state",
-                                  "s6_last_state_ex",
-                                  "s6_scan_bwd", "s6_scan_bwd_ckpt", "s6_scan_bwd_ex", "s6_scan_fwd",
-                                  "s6_scan_fwd_ckpt", "s6_scan_fwd_ex", "s6_state_update", "s6_state_update_ex",
-                                  "s6_status_str", "s6_version"]
+                                  "s6_last_state_ex", "s6_last_state_workspace_size",
+                                  "s6_scan_bwd", "s6_scan_bwd_ckpt", "s6_scan_bwd_ex", "s6_scan_bwd_workspace_size",
+                                  "s6_scan_fwd", "s6_scan_fwd_ckpt", "s6_scan_fwd_ex", "s6_scan_fwd_workspace_size",
+                                  "s6_state_update", "s6_state_update_ex", "s6_status_str", "s6_version"]
 
 
 def test_every_declared_symbol_is_exported():
@@ -63,7 +63,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings(lib, codes):
-    assert lib.s6_version() == 10300
+    assert lib.s6_version() == 20000
     for name, v in codes.items():
         if name.startswith("S6_ERR_") or name == "S6_OK":
             s = lib.s6_status_str(v).decode()
@@ -78,7 +78,7 @@ P_ODD = ctypes.c_void_p((1 << 20) + 2)
 
 
 def scan(lib, b=2, d=64, L=32, n=16, dt=0, x=P, y=P, A=P, z=None, hl=None):
-    return lib.s6_scan_fwd(b, d, L, n, dt, x, P, A, P, P, None, z, None, y, hl, None)
+    return lib.s6_scan_fwd(b, d, L, n, dt, x, P, A, P, P, None, z, None, y, hl, None, 0, None)
 
 
 def test_scan_validation(lib, codes):
@@ -102,11 +102,11 @@ def test_scan_validation(lib, codes):
 
 def test_last_state_validation(lib, codes):
     f = lib.s6_last_state
-    assert f(2, 64, 32, 16, 0, P, P, P, P, None, None, None) == codes["S6_ERR_NULL"]  # no h_last
-    assert f(2, 64, 32, 40, 0, P, P, P, P, None, P, None) == codes["S6_ERR_UNSUPPORTED"]
-    assert f(2, 64, 32, 16, 7, P, P, P, P, None, P, None) == codes["S6_ERR_DTYPE"]
-    assert f(2, 64, 32, 16, 0, None, P, P, P, None, P, None) == codes["S6_ERR_NULL"]
-    assert f(0, 64, 32, 16, 0, P, P, P, P, None, P, None) == codes["S6_OK"]
+    assert f(2, 64, 32, 16, 0, P, P, P, P, None, None, None, 0, None) == codes["S6_ERR_NULL"]  # no h_last
+    assert f(2, 64, 32, 40, 0, P, P, P, P, None, P, None, 0, None) == codes["S6_ERR_UNSUPPORTED"]
+    assert f(2, 64, 32, 16, 7, P, P, P, P, None, P, None, 0, None) == codes["S6_ERR_DTYPE"]
+    assert f(2, 64, 32, 16, 0, None, P, P, P, None, P, None, 0, None) == codes["S6_ERR_NULL"]
+    assert f(0, 64, 32, 16, 0, P, P, P, P, None, P, None, 0, None) == codes["S6_OK"]
 
 
 def test_state_update_validation(lib, codes):
@@ -128,7 +128,7 @@ def test_option_entry_points_validation(lib, codes):
 
     def scan_ex(flags=SP | ZOH, bias=P, b=2, n=16, dt=1, x=P, y=P):
         return lib.s6_scan_fwd_ex(b, 64, 32, n, dt, x, P, bias, flags, P, P, P, None, None, None, y, None,
-                                  None)
+                                  None, 0, None)
 
     assert scan_ex(flags=4) == codes["S6_ERR_FLAGS"]
     assert scan_ex(flags=-1) == codes["S6_ERR_FLAGS"]
@@ -140,10 +140,10 @@ def test_option_entry_points_validation(lib, codes):
     assert scan_ex(b=0) == codes["S6_OK"]
     assert scan_ex(b=0, bias=None, flags=0) == codes["S6_OK"]
     f = lib.s6_last_state_ex
-    assert f(2, 64, 32, 16, 1, P, P, P, 8, P, P, None, P, None) == codes["S6_ERR_FLAGS"]
-    assert f(2, 64, 32, 16, 1, P, P, P_ODD, 1, P, P, None, P, None) == codes["S6_ERR_ALIGN"]
-    assert f(2, 64, 32, 16, 1, P, P, P, 1, P, P, None, None, None) == codes["S6_ERR_NULL"]
-    assert f(0, 64, 32, 16, 1, P, P, P, 3, P, P, None, P, None) == codes["S6_OK"]
+    assert f(2, 64, 32, 16, 1, P, P, P, 8, P, P, None, P, None, 0, None) == codes["S6_ERR_FLAGS"]
+    assert f(2, 64, 32, 16, 1, P, P, P_ODD, 1, P, P, None, P, None, 0, None) == codes["S6_ERR_ALIGN"]
+    assert f(2, 64, 32, 16, 1, P, P, P, 1, P, P, None, None, None, 0, None) == codes["S6_ERR_NULL"]
+    assert f(0, 64, 32, 16, 1, P, P, P, 3, P, P, None, P, None, 0, None) == codes["S6_OK"]
     g = lib.s6_state_update_ex
     assert g(2, 64, 16, 0, P, P, P, P, 16, P, P, P, None, None, P, None) == codes["S6_ERR_FLAGS"]
     assert g(2, 64, 16, 0, P, P, P, P_ODD, 1, P, P, P, None, None, P, None) == codes["S6_ERR_ALIGN"]
@@ -156,7 +156,7 @@ def test_conv_entry_points_validation(lib, codes):
     decode widths above 1, alignment, then the plain checks."""
     def scan(w=P, width=4, bias=None, state=None, flags=0, b=2, x=P, y=P):
         return lib.s6_conv_scan_fwd(b, 64, 32, 16, 1, x, w, bias, width, state, P, None, flags, P, P, P, None, None,
-                                    None, y, None, None)
+                                    None, y, None, None, 0, None)
 
     assert scan(width=0) == codes["S6_ERR_UNSUPPORTED"]
     assert scan(width=5) == codes["S6_ERR_UNSUPPORTED"]
@@ -188,7 +188,8 @@ def test_conv_entry_points_validation(lib, codes):
 
     def bwd(w=P, width=4, dw=P, d=64, flags=0, bias=None):
         return lib.s6_conv_scan_bwd(2, d, 32, 16, 1, P, w, bias, width, None, P, None, flags, P, P, P, None, None,
-                                    None, P, None, P, P, P, P, P, None, None, None, None, dw, None, None, None)
+                                    None, P, None, P, P, P, P, P, None, None, None, None, dw, None, None, None, 0,
+                                    None)
 
     assert bwd(width=5) == codes["S6_ERR_UNSUPPORTED"]
     assert bwd(w=None) == codes["S6_ERR_NULL"]
@@ -206,7 +207,8 @@ def test_checkpoint_entry_points_validation(lib, codes):
     assert codes["S6_CKPT_TOKENS"] == 64
 
     def fwd(ck=P, b=2, L=32, flags=0):
-        return lib.s6_scan_fwd_ckpt(b, 64, L, 16, 1, P, P, None, flags, P, P, P, None, None, None, P, None, ck, None)
+        return lib.s6_scan_fwd_ckpt(b, 64, L, 16, 1, P, P, None, flags, P, P, P, None, None, None, P, None, ck, None,
+                                    0, None)
 
     assert fwd(ck=None) == codes["S6_ERR_NULL"]
     assert fwd(ck=P_ODD) == codes["S6_ERR_ALIGN"]
@@ -216,7 +218,7 @@ def test_checkpoint_entry_points_validation(lib, codes):
 
     def bwd(ck=P, flags=0, b=2):
         return lib.s6_scan_bwd_ckpt(b, 64, 32, 16, 1, P, P, None, flags, P, P, P, None, None, ck, P, None, P, P, P, P,
-                                    P, None, None, None, None, None)
+                                    P, None, None, None, None, None, 0, None)
 
     assert bwd(ck=None) == codes["S6_ERR_NULL"]
     assert bwd(ck=P_ODD) == codes["S6_ERR_ALIGN"]
@@ -227,7 +229,8 @@ def test_backward_validation(lib, codes):
     f = lib.s6_scan_bwd
 
     def bwd(b=2, d=64, L=32, n=16, dt=1, x=P, dy=P, dA=P, dB=P, dz=None, dh0=None):
-        return f(b, d, L, n, dt, x, P, P, P, P, None, None, None, dy, None, P, P, dA, dB, P, None, dz, dh0, None)
+        return f(b, d, L, n, dt, x, P, P, P, P, None, None, None, dy, None, P, P, dA, dB, P, None, dz, dh0, None, 0,
+                 None)
 
     assert bwd(dt=3) == codes["S6_ERR_DTYPE"]
     assert bwd(n=0) == codes["S6_ERR_UNSUPPORTED"]
@@ -244,7 +247,7 @@ def test_backward_validation(lib, codes):
 
     def bwd_ex(flags=1, bias=P, dbias=P, d=64):
         return g(2, d, 32, 16, 1, P, P, bias, flags, P, P, P, None, None, None, P, None, P, P, P, P, P, None, None,
-                 None, dbias, None)
+                 None, dbias, None, 0, None)
 
     # (dim 0: the checks pass and nothing is launched on these placeholder pointers)
     assert bwd_ex(flags=2, d=0) == codes["S6_OK"]  # the exact hold has a backward
@@ -266,3 +269,78 @@ def test_binding_fails_loudly_without_library(tmp_path):
     from selective_state_space_63_amd import s6
     with pytest.raises(FileNotFoundError):
         s6.load_library(str(tmp_path / "missing.so"))
+
+
+def _size(fn, *args):
+    out = ctypes.c_size_t(12345)
+    rc = fn(*args, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_workspace_size_queries(lib, codes):
+    """Sizes from the launch plan on a 256-CU device (the count the library
+    assumes when no device can be queried, and MI355X's): no workspace when
+    the (row, 32-channel block) workgroups fill the GPU; for few long rows
+    the segment carries.  The 1M-token sequence (1 x 1536 channels, 16
+    states): 48 blocks, 5 workgroups of 4 waves per CU -> 26 segments of
+    40384 tokens; 25 end states and summed deltas, 26 incoming states."""
+    ok = codes["S6_OK"]
+    assert _size(lib.s6_scan_fwd_workspace_size, 8, 5120, 2048, 16, 1) == (ok, 0)
+    nstate = 1536 * 16 * 4
+    want = 25 * nstate + 25 * 1536 * 4 + 26 * nstate
+    assert _size(lib.s6_scan_fwd_workspace_size, 1, 1536, 1 << 20, 16, 1) == (ok, want)
+    assert _size(lib.s6_last_state_workspace_size, 1, 1536, 1 << 20, 16, 1) == (ok, 26 * nstate + 26 * 1536 * 4)
+    assert _size(lib.s6_scan_fwd_workspace_size, 0, 1536, 1 << 20, 16, 1) == (ok, 0)
+    assert _size(lib.s6_scan_fwd_workspace_size, 1, 1536, 0, 16, 1) == (ok, 0)
+    assert _size(lib.s6_scan_fwd_workspace_size, 1, 64, 4096, 40, 1)[0] == codes["S6_ERR_UNSUPPORTED"]
+    assert _size(lib.s6_scan_fwd_workspace_size, 1, 64, 4096, 16, 9)[0] == codes["S6_ERR_DTYPE"]
+    assert lib.s6_scan_fwd_workspace_size(1, 64, 4096, 16, 1, None) == codes["S6_ERR_NULL"]
+    # backward of the 3B layer (one part, 32 segments of 64 tokens): 31
+    # segment end states and summed deltas, 32 incoming states, the per-row
+    # partials of dA, dD and the bias gradient, and the per-16-channel-block
+    # dB/dC partials, which dominate
+    rc, full = _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 2048, 16, 1, 0, 0)
+    assert rc == ok
+    st = 8 * 5120 * 16 * 4
+    bc = (5120 // 16) * 8 * 16 * 2048 * 4
+    assert full == 31 * st + 31 * 8 * 5120 * 4 + 32 * st + st + 2 * 8 * 5120 * 4 + 2 * bc
+    rc, ck = _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 2048, 16, 1, 0, 1)
+    assert rc == ok and ck == full - (31 * st + 31 * 8 * 5120 * 4 + 32 * st)
+    rc, conv = _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 2048, 16, 1, 4, 0)
+    assert rc == ok and conv == full + 8 * 5120 * 2048 * 4 + 8 * 1 * 5120 * 5 * 4
+    assert _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 2048, 16, 1, 5, 0)[0] == codes["S6_ERR_UNSUPPORTED"]
+    assert _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 0, 16, 1, 0, 0) == (ok, 0)
+
+
+def test_workspace_required(lib, codes):
+    """A call that needs a workspace fails with S6_ERR_WORKSPACE (NULL or
+    too small) or S6_ERR_ALIGN (not 256-byte aligned) before any HIP call;
+    one that needs none accepts NULL (checked above with batch or dim 0)."""
+    rc, need = _size(lib.s6_scan_fwd_workspace_size, 1, 64, 4096, 16, 1)
+    assert rc == codes["S6_OK"] and need > 0  # 2 blocks: cut into segments
+
+    def fwd(ws, nbytes):
+        return lib.s6_scan_fwd(1, 64, 4096, 16, 1, P, P, P, P, P, None, None, None, P, None, ws, nbytes, None)
+
+    assert fwd(None, 0) == codes["S6_ERR_WORKSPACE"]
+    assert fwd(None, need) == codes["S6_ERR_WORKSPACE"]
+    assert fwd(P, need - 1) == codes["S6_ERR_WORKSPACE"]
+    assert fwd(ctypes.c_void_p((1 << 20) + 128), need) == codes["S6_ERR_ALIGN"]
+    f = lib.s6_last_state
+    assert f(1, 64, 4096, 16, 1, P, P, P, P, None, P, None, 0, None) == codes["S6_ERR_WORKSPACE"]
+    g = lib.s6_scan_bwd
+    assert g(2, 64, 32, 16, 1, P, P, P, P, P, None, None, None, P, None, P, P, P, P, P, None, None, None,
+             None, 0, None) == codes["S6_ERR_WORKSPACE"]
+    rc, bneed = _size(lib.s6_scan_bwd_workspace_size, 2, 64, 32, 16, 1, 0, 0)
+    assert rc == codes["S6_OK"] and bneed > 0
+    assert g(2, 64, 32, 16, 1, P, P, P, P, P, None, None, None, P, None, P, P, P, P, P, None, None, None,
+             P, bneed - 4, None) == codes["S6_ERR_WORKSPACE"]
+
+
+def test_library_source_allocates_nothing():
+    """No device allocation or release anywhere in the library's sources."""
+    import glob
+    for f in glob.glob(os.path.join(ROOT, "selective_state_space_63_amd", "csrc", "*")):
+        text = open(f).read()
+        for word in ("hipMalloc", "hipFree", "hipHostMalloc", "hipMallocAsync"):
+            assert word not in text, (f, word)

@@ -1,5 +1,5 @@
-"""Decode steps captured in a HIP graph (through torch's graph capture on the
-stream the binding launches on): every replay, with eager work and
+"""Decode steps, scans and backwards captured in a HIP graph (through torch's
+graph capture on the stream the binding launches on): every replay, with eager work and
 synchronisation between replays, must equal the plain launches bit for bit."""
 import pytest
 
@@ -84,3 +84,80 @@ def test_scan_graph_replays(torch_cuda):
         torch.cuda.synchronize()
         for t, r in zip((y, hl, ck), refs):
             assert torch.equal(t, r), rep
+
+
+def _replay_check(torch, g, outs, refs, reps=3):
+    """Replays g `reps` times with eager work (clearing the outputs, an
+    unrelated product) and synchronisation between replays; every replay
+    must reproduce refs bit for bit."""
+    for rep in range(reps):
+        for t in outs:
+            t.fill_(float("nan"))
+        junk = torch.randn(256, 256, device="cuda") @ torch.randn(256, 256, device="cuda")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        del junk
+        for t, r in zip(outs, refs):
+            assert torch.equal(t, r), rep
+
+
+def test_segmented_scan_graph_replays(torch_cuda):
+    """A scan of one long row of 1536 channels (48 channel blocks: the
+    sequence is cut into segments whose carries live in the caller's
+    workspace, here allocated by the binding inside the capture) and its
+    final-state-only form, captured and replayed."""
+    import torch
+    from selective_state_space_63_amd import s6
+    w = synth.custom(1, 1536, 16, 65536, synth.BF16, True, seed=33)
+    assert s6.workspace_size("scan_fwd", w.batch, w.dim, w.seqlen, w.dstate) > 0
+    print(f"[case] segmented scan graph {w.name}", flush=True)
+    d = synth.device_full(w)
+    h0 = torch.randn((w.batch, w.dim, w.dstate), device="cuda", dtype=torch.float32)
+    y = torch.empty((w.batch, w.dim, w.seqlen), device="cuda", dtype=torch.float32)
+    hl = torch.empty((w.batch, w.dim, w.dstate), device="cuda", dtype=torch.float32)
+    hs = torch.empty_like(hl)
+
+    def run():
+        s6.scan_fwd(d["x"], d["delta"], d["A"], d["Bm"], d["Cm"], D=d["Dskip"], z=d["z"], h0=h0, y=y, h_last=hl,
+                    return_last_state=True)
+        s6.last_state(d["x"], d["delta"], d["A"], d["Bm"], h0=h0, out=hs)
+
+    run()
+    torch.cuda.synchronize()
+    refs = (y.clone(), hl.clone(), hs.clone())
+    assert torch.equal(hl, hs)  # same segments, same fold
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    _replay_check(torch, g, (y, hl, hs), refs)
+
+
+@pytest.mark.parametrize("shape", [(2, 256, 1024), (1, 64, 8192)], ids=["rows", "parts"])
+def test_backward_graph_replays(torch_cuda, shape):
+    """The backward (checkpoint pass, adjoint kernel, fixed-order reductions;
+    with few long rows also the carry pass and fold over parts) captured with
+    its workspace and replayed: every gradient equal to the eager call bit
+    for bit."""
+    import torch
+    from selective_state_space_63_amd import s6
+    bsz, dim, L = shape
+    w = synth.custom(bsz, dim, 16, L, synth.BF16, True, seed=34)
+    print(f"[case] backward graph {w.name}", flush=True)
+    d, _ = problem(w, True)
+    dy = torch.randn((bsz, dim, L), device="cuda", dtype=torch.float32)
+    dhl = torch.randn((bsz, dim, 16), device="cuda", dtype=torch.float32)
+    res = {}
+
+    def run():
+        res.update(s6.scan_bwd(d["x"], d["delta"], d["A"], d["Bm"], d["Cm"], dy, D=d["D"], z=d["z"], h0=d["h0"],
+                               dh_last=dhl))
+
+    run()
+    torch.cuda.synchronize()
+    keys = sorted(res)
+    refs = tuple(res[k].clone() for k in keys)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    _replay_check(torch, g, tuple(res[k] for k in keys), refs)

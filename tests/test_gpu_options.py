@@ -160,8 +160,11 @@ def test_no_options_equal_plain_entry_points(torch_cuda):
     y1, y2 = torch.empty((2, 96, 40), **f), torch.empty((2, 96, 40), **f)
     h1, h2 = torch.empty((2, 96, 16), **f), torch.empty((2, 96, 16), **f)
     args = (P(d["A"]), P(d["Bm"]), P(d["Cm"]), P(d["D"]), P(d["z"]), P(d["h0"]))
-    assert lib.s6_scan_fwd(2, 96, 40, 16, 1, P(d["x"]), P(d["delta"]), *args, P(y1), P(h1), st) == 0
-    assert lib.s6_scan_fwd_ex(2, 96, 40, 16, 1, P(d["x"]), P(d["delta"]), None, 0, *args, P(y2), P(h2), st) == 0
+    # 40 tokens: one segment, so no workspace
+    assert s6.workspace_size("scan_fwd", 2, 96, 40, 16) == 0
+    assert lib.s6_scan_fwd(2, 96, 40, 16, 1, P(d["x"]), P(d["delta"]), *args, P(y1), P(h1), None, 0, st) == 0
+    assert lib.s6_scan_fwd_ex(2, 96, 40, 16, 1, P(d["x"]), P(d["delta"]), None, 0, *args, P(y2), P(h2), None, 0,
+                              st) == 0
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
     hs1, hs2 = d["h0"].clone(), d["h0"].clone()
