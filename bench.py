@@ -246,6 +246,89 @@ def bench_scan(w, steps, warmup, flush=False, softplus=False, zoh=False, conv_k=
     return inp, {"mean": ms, "median": per[len(per) // 2], "min": per[0]}, wall
 
 
+def ssd_mfma_flops(w):
+    """Matrix-core flops one s6_ssd_scan_fwd issues (bf16 inputs): per
+    16-token chunk and 16-channel tile, ten 16x16x16 products (two
+    transposes of B and C by the identity, the Gram matrix, tril(G) V as
+    three products of two-part operands, C H and B^T V as two each), 2 *
+    16^3 flops each."""
+    tiles = w.batch * ((w.dim + 15) // 16) * ((w.seqlen + 15) // 16)
+    return tiles * 10 * 2 * 16 ** 3
+
+
+def bench_ssd(w, steps, warmup):
+    """Times s6_ssd_scan_fwd (the scalar-A chunked matrix-form scan) on
+    workload w with the final state, inputs resident on the device."""
+    import torch
+    from selective_state_space_63_amd import s6, synth
+    inp = synth.device_full(w)
+    a = synth.scalar_a_device(w)
+    y = torch.empty((w.batch, w.dim, w.seqlen), device="cuda", dtype=torch.float32)
+    hl = torch.empty((w.batch, w.dim, w.dstate), device="cuda", dtype=torch.float32)
+
+    def step():
+        s6.ssd_scan_fwd(inp["x"], inp["delta"], a, inp["Bm"], inp["Cm"], D=inp["Dskip"], z=inp["z"],
+                        return_last_state=True, y=y, h_last=hl)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    in_bytes = 2 if w.dtype == synth.BF16 else 4
+    # A is one value per channel here: 4 D bytes instead of 4 D N
+    byts = scan_bytes(w, in_bytes, h_last=True) - 4 * w.dim * (w.dstate - 1)
+    gbs = byts / (ms * 1e-3) / 1e9
+    fl = ssd_mfma_flops(w)
+    inp["y_out"], inp["h_last_out"], inp["a"] = y, hl, a
+    return inp, {"workload": w.name, "ms_mean": round(ms, 4), "GBps": round(gbs, 1),
+                 "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                 "token_channels_per_s": w.batch * w.dim * w.seqlen / (ms * 1e-3),
+                 "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": byts,
+                              "mfma": {"flops_per_launch": fl, "achieved_TFLOPs": round(fl / (ms * 1e-3) / 1e12, 1),
+                                       "peak_bf16_TFLOPs": 2500.0,
+                                       "frac": round(fl / (ms * 1e-3) / 1e12 / 2500.0, 4)}},
+                 "note": "s6_ssd_scan_fwd: one A value per channel, chunked matrix form on the matrix cores"}
+
+
+def cpu_ssd_baseline(w, inp, budget_s=3.0):
+    """The oracle's scan with A[d, n] = a_d on whole batch rows of the same
+    inputs until `budget_s` is spent; the GPU's outputs of those rows are
+    compared after timing (max_err)."""
+    import numpy as np
+    import torch
+    from oracle.oracle import Oracle
+    o = Oracle()
+
+    def h64(t):
+        return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+    A2 = np.repeat(h64(inp["a"])[:, None], w.dstate, axis=1)
+    Dk = h64(inp["Dskip"])
+    spent, rows, err = 0.0, 0, {}
+    while spent < budget_s or rows == 0:
+        b = rows % w.batch
+        args = dict(x=h64(inp["x"][b:b + 1]), delta=h64(inp["delta"][b:b + 1]), A=A2, Bm=h64(inp["Bm"][b:b + 1]),
+                    Cm=h64(inp["Cm"][b:b + 1]), Dskip=Dk, z=h64(inp["z"][b:b + 1]))
+        t0 = time.perf_counter()
+        r = o.scan(**args)
+        spent += time.perf_counter() - t0
+        if rows < w.batch:
+            err = _merge_err(err, error_report(h64(inp["y_out"][b:b + 1]), r["y"], r["m"]))
+        rows += 1
+    return {"token_channels_per_s": rows * w.dim * w.seqlen / spent, "cores": o.num_threads(), "kind": "oracle",
+            "sample": f"{rows} batch rows ({w.dim} channels x {w.seqlen} tokens each), {spent:.2f} s",
+            "max_err_y": err}
+
+
 def bench_scan_flushed(w, inp, steps, warmup):
     import torch
     from selective_state_space_63_amd import s6
@@ -626,7 +709,7 @@ def versions():
             "rocm": rocm}
 
 
-def copy_rate(mib=1024, steps=10):
+def copy_rate(mib=1024, steps=40):
     """GB/s (read + written) of a plain 1 GiB device copy (torch's elementwise
     negation): the practical HBM ceiling beside the 8 TB/s peak."""
     import torch
@@ -691,6 +774,8 @@ def main():
                     help="only time s6_scan_bwd on the workload (one JSON line; for profiling)")
     ap.add_argument("--conv-k", type=int, default=0,
                     help="with --backward-only: time s6_conv_scan_bwd with a filter of this width")
+    ap.add_argument("--ssd-only", action="store_true",
+                    help="only time s6_ssd_scan_fwd on the scalar-A workload (one JSON line; for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the scan has no cross-GPU step); got --gpus {args.gpus}",
@@ -707,10 +792,18 @@ def main():
     s6.load_library()
     w = synth.WORKLOADS[args.workload]
     in_bytes = 2 if w.dtype == synth.BF16 else 4
+    if args.ssd_only:
+        _, line = bench_ssd(synth.WORKLOADS["ssd3b"], args.steps, args.warmup)
+        print(json.dumps({"ssd": line}), flush=True)
+        return
     if args.backward_only:
         print(json.dumps({"backward": bench_backward(w, steps=args.steps, warmup=args.warmup, conv_k=args.conv_k)}),
               flush=True)
         return
+    # The plain 1 GiB copy (the practical HBM ceiling reported beside the
+    # peak) runs first: its ~0.1 s of load also brings the GPU clock up from
+    # idle, which a short warm-up of the scan alone does not.
+    cp_gbs = copy_rate()
     print(f"[bench] scan {w.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
     inp, tm, wall = bench_scan(w, args.steps, args.warmup, keep_out=True)
     ms = tm["mean"]
@@ -720,7 +813,6 @@ def main():
     gbs = byts / (ms * 1e-3) / 1e9
     tc = w.batch * w.dim * w.seqlen
     traffic = measured_traffic() if w.name == synth.WORKLOADS["m3b"].name else None
-    cp_gbs = copy_rate()  # the practical HBM ceiling, measured in the same run
     out = {
         "metric": "selective-scan fwd GB/s and % of HBM peak; decode state-updates/s",
         "value": round(gbs, 1),
@@ -818,6 +910,13 @@ def main():
         _, tz, _ = bench_scan(w, 50, 50, softplus=True, zoh=True)
         out["softplus_zoh"] = scan_line("softplus_zoh", w, tz, in_bytes,
                                         "softplus step and exact zero-order-hold input term", True)
+        torch.cuda.empty_cache()
+        ws = synth.WORKLOADS["ssd3b"]
+        print(f"[bench] scalar-A matrix-form scan {ws.name}", file=sys.stderr, flush=True)
+        inp_ssd, out["ssd"] = bench_ssd(ws, 50, 20)
+        if not args.no_cpu_baseline:
+            out["ssd"]["cpu_baseline"] = cpu_ssd_baseline(ws, inp_ssd)
+        del inp_ssd
         torch.cuda.empty_cache()
         print(f"[bench] scan {w.name} with the convolution front", file=sys.stderr, flush=True)
         _, tcv, _ = bench_scan(w, 50, 50, conv_k=4)

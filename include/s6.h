@@ -316,6 +316,31 @@ int s6_scan_bwd_ckpt(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
                      float* dCm, float* dDskip, float* dz, float* dh0, float* ddelta_bias, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* The scan with one A value per channel, A[d, n] = a_d for every state n,
+ * computed in chunked matrix form on the matrix cores.  The paper-list page's
+ * Mamba-2 abstract (structured state space duality) observes that a scan with
+ * such an A is a structured semiseparable matrix whose blocks are matrix
+ * products; the result is the recurrence of s6_scan_fwd (the guide's §2.3,
+ * §2.4, §3.2) with A[d, n] = A[d]:
+ *   h[n] = exp(delta[b,d,t] * A[d]) * h[n] + delta[b,d,t] * Bm[b,n,t] * x[b,d,t]
+ *   y[b,d,t] = (sum_n Cm[b,n,t] * h[n] + Dskip[d] * x[b,d,t]) * SiLU(z[b,d,t])
+ * evaluated per 16-token chunk as products with the Gram matrix of B and C
+ * (shared by every channel of a batch row) and two exponentials per token
+ * and channel.  With bf16 inputs the fp32 operands enter the bf16 matrix
+ * cores as two bf16 parts each (about 2^-16 relative per product); with
+ * fp32 inputs the products are fp32.
+ *   A : (dim) fp32, one value per channel (accuracy specified for A <= 0).
+ *   dstate : 1..16 (else S6_ERR_UNSUPPORTED).
+ *   Everything else (layouts, nullable Dskip, z, h0, h_last; errors; stream)
+ *   as for s6_scan_fwd.  workspace: s6_ssd_scan_fwd_workspace_size bytes
+ *   (currently 0 for every size: one pass over the sequence). */
+int s6_ssd_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                    const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
+                    const float* Dskip, const void* z, const float* h0, float* y, float* h_last,
+                    void* workspace, size_t workspace_bytes, void* stream);
+int s6_ssd_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                                   size_t* bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, f) for f in ("scan.hip", "scan_ext.hip", "scan_conv.hip", "scan_hold.hip",
-                                                    "step.hip", "bwd.hip", "common.hip")]
+                                                    "step.hip", "bwd.hip", "ssd.hip", "common.hip")]
 HEADERS = [os.path.join(CSRC, "s6_internal.h"), os.path.join(CSRC, "scan_kernel.h"),
            os.path.join(ROOT, "include", "s6.h")]
 LIB = os.path.join(PKG, "libs6.so")

@@ -70,6 +70,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         getattr(lib, q).argtypes = [i64, i64, i64, i64, i32, szp]
     lib.s6_scan_bwd_workspace_size.restype = i32
     lib.s6_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i32, i32, i32, szp]
+    lib.s6_ssd_scan_fwd.restype = i32
+    lib.s6_ssd_scan_fwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 10 + ws
+    lib.s6_ssd_scan_fwd_workspace_size.restype = i32
+    lib.s6_ssd_scan_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i32, szp]
     if path is None:
         _lib = lib
     return lib
@@ -96,13 +100,16 @@ def _stream():
 def workspace_size(op: str, bsz: int, dim: int, L: int, N: int, dtype=torch.bfloat16, conv_width: int = 0,
                    from_ckpt: bool = False) -> int:
     """Bytes of device workspace the entry points of `op` ("scan_fwd",
-    "last_state" or "scan_bwd") need for these sizes on the current device."""
+    "last_state", "ssd_scan_fwd" or "scan_bwd") need for these sizes on the
+    current device."""
     lib = load_library()
     out = ctypes.c_size_t(0)
     if op == "scan_fwd":
         rc = lib.s6_scan_fwd_workspace_size(bsz, dim, L, N, _DT[dtype], ctypes.byref(out))
     elif op == "last_state":
         rc = lib.s6_last_state_workspace_size(bsz, dim, L, N, _DT[dtype], ctypes.byref(out))
+    elif op == "ssd_scan_fwd":
+        rc = lib.s6_ssd_scan_fwd_workspace_size(bsz, dim, L, N, _DT[dtype], ctypes.byref(out))
     elif op == "scan_bwd":
         rc = lib.s6_scan_bwd_workspace_size(bsz, dim, L, N, _DT[dtype], conv_width, int(bool(from_ckpt)),
                                             ctypes.byref(out))
@@ -200,6 +207,37 @@ def scan_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, return_last_state=Fal
         rc = load_library().s6_scan_fwd(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
                                         _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last),
                                         wsp, wsn, _stream())
+    del keep
+    _check(rc)
+    return (y, h_last) if return_last_state else y
+
+
+def ssd_scan_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, return_last_state=False, y=None, h_last=None):
+    """The scan with one A value per channel (A: (dim,) fp32, A[d, n] = A[d]
+    for every state), in chunked matrix form on the matrix cores; N <= 16.
+    Other arguments and the result as in scan_fwd (no step options)."""
+    bsz, dim, L = x.shape
+    N = Bm.shape[1]
+    dt = x.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported input dtype {dt}")
+    _req(x, "x", (bsz, dim, L), dt)
+    _req(delta, "delta", (bsz, dim, L), dt)
+    _req(A, "A", (dim,), torch.float32)
+    _req(Bm, "Bm", (bsz, N, L), dt)
+    _req(Cm, "Cm", (bsz, N, L), dt)
+    _opt(D, "D", (dim,), torch.float32)
+    _opt(z, "z", (bsz, dim, L), dt)
+    _opt(h0, "h0", (bsz, dim, N), torch.float32)
+    if y is None:
+        y = torch.empty((bsz, dim, L), dtype=torch.float32, device=x.device)
+    _req(y, "y", (bsz, dim, L), torch.float32)
+    if return_last_state and h_last is None:
+        h_last = torch.empty((bsz, dim, N), dtype=torch.float32, device=x.device)
+    _opt(h_last, "h_last", (bsz, dim, N), torch.float32)
+    keep, wsp, wsn = _workspace("ssd_scan_fwd", x, bsz, dim, L, N)
+    rc = load_library().s6_ssd_scan_fwd(bsz, dim, L, N, _DT[dt], _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+                                        _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last), wsp, wsn, _stream())
     del keep
     _check(rc)
     return (y, h_last) if return_last_state else y

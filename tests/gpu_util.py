@@ -49,9 +49,15 @@ def problem(w: synth.Workload, with_h0: bool, seed_h0: int = 5):
 ERRORS: list[tuple] = []
 
 
-def scaled(got, ref, mag):
+# Regression guard: the measured scaled errors of the scans, decode steps and
+# backwards are at most about 1.1e-6 (fp32 state; every path, every test);
+# 1e-5 catches a tenfold loss of accuracy long before the bars of TOL.
+GUARD = 1e-5
+
+
+def scaled(got, ref, mag, guard=GUARD):
     """The gated error |got - ref| / m (m: the oracle's magnitude; the bars
-    of TOL), recorded together with the plain max relative error over
+    of TOL; it must also stay within `guard`), recorded together with the plain max relative error over
     elements with |ref| >= 1e-3 max|ref| and the normwise error
     max|got - ref| / max|ref|, which are reported, not gated."""
     import os
@@ -66,4 +72,5 @@ def scaled(got, ref, mag):
     test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
     ERRORS.append((test, e, relative_error(got, ref) if np.all(np.isfinite(got64)) else float("inf"), norm,
                    int(ref.size)))
+    assert e <= guard, f"scaled error {e:.3e} above the regression guard {guard:.0e}"
     return e

@@ -1120,6 +1120,63 @@ def pin_conv_bwd_magnitude_bracket(o):
         assert np.all(cb["m" + k] <= 1.3 * cb[k]), (k, np.max(cb["m" + k] / cb[k]))
 
 
+# ---------------------------------------------- scalar A: the matrix form --
+def semiseparable_scalar_a(p):
+    """The scan with one A value per channel (A[d, n] = a_d), evaluated as a
+    matrix: per batch row the Gram matrix G[t, s] = sum_n C_t[n] B_s[n] of
+    the shared B and C (L x L, one numpy product), and per channel the
+    lower-triangular (semiseparable) mask M[t, s] = exp(a_d (cum_t - cum_s))
+    for s <= t from the cumulative step cum_t = sum_{u <= t} Delta_u, so
+    y = (G o M) (Delta x) + exp(a_d cum_t) C_t . h0 + D x, then the gate;
+    the final state sum_s exp(a_d (cum_L - cum_s)) Delta_s x_s B_s +
+    exp(a_d cum_L) h0.  The structured-matrix view of the Mamba-2 abstract
+    on the paper-list page, written out densely in fp64."""
+    x, dl, A, Bm, Cm = p["x"], p["delta"], p["A"], p["Bm"], p["Cm"]
+    Bsz, D, L = x.shape
+    y = np.empty((Bsz, D, L))
+    hl = np.empty((Bsz, D, Bm.shape[1]))
+    tri = np.tril(np.ones((L, L), dtype=bool))
+    for b in range(Bsz):
+        G = Cm[b].T @ Bm[b]  # (L, L)
+        for d in range(D):
+            a = A[d, 0]
+            cum = np.cumsum(dl[b, d])
+            M = np.where(tri, np.exp(a * np.subtract.outer(cum, cum)), 0.0)
+            v = dl[b, d] * x[b, d]
+            yy = (G * M) @ v
+            if p.get("h0") is not None:
+                yy += np.exp(a * cum) * (Cm[b].T @ p["h0"][b, d])
+            if p.get("Dskip") is not None:
+                yy += p["Dskip"][d] * x[b, d]
+            if p.get("z") is not None:
+                yy *= _silu(p["z"][b, d])
+            y[b, d] = yy
+            h = Bm[b] @ (np.exp(a * (cum[-1] - cum)) * v)
+            if p.get("h0") is not None:
+                h += np.exp(a * cum[-1]) * p["h0"][b, d]
+            hl[b, d] = h
+    return y, hl
+
+
+def pin_scalar_a_semiseparable(o):
+    """With A[d, n] = a_d the oracle's recurrence equals the semiseparable
+    matrix form built from the shared Gram matrix of B and C (a different
+    evaluation: a matrix product over all pairs of tokens, decays as
+    exponentials of differences of cumulative steps).  Several channels with
+    different a_d (including a_d = 0 and a strongly decaying one), h0, skip
+    and gate."""
+    g = _rng(201)
+    Bsz, D, L, N = 2, 4, 50, 6
+    a = np.array([-0.5, -3.0, 0.0, -12.0])
+    p = dict(x=g.standard_normal((Bsz, D, L)), delta=np.exp(g.uniform(np.log(1e-3), np.log(0.5), (Bsz, D, L))),
+             A=np.repeat(a[:, None], N, axis=1), Bm=g.standard_normal((Bsz, N, L)), Cm=g.standard_normal((Bsz, N, L)),
+             Dskip=g.standard_normal(D), z=g.standard_normal((Bsz, D, L)), h0=g.standard_normal((Bsz, D, N)))
+    r = o.scan(**p)
+    y, hl = semiseparable_scalar_a(p)
+    assert np.max(np.abs(r["y"] - y) / r["m"]) < 1e-12, np.max(np.abs(r["y"] - y) / r["m"])
+    assert np.max(np.abs(r["h_last"] - hl) / r["H_last"]) < 1e-12
+
+
 PINS = [pin_zero_step_hand, pin_scalar_hand, pin_lti_convolution, pin_step_response,
         pin_brute_force, pin_tree_scan, pin_split_resume, pin_linearity_and_permutation,
         pin_gate_limits, pin_decode_equals_scan, pin_magnitude_bounds, pin_softplus_hand,
@@ -1129,4 +1186,5 @@ PINS = [pin_zero_step_hand, pin_scalar_hand, pin_lti_convolution, pin_step_respo
         pin_bwd_zoh_directional_brute_force, pin_bwd_zoh_elementwise_fd, pin_bwd_zoh_single_token,
         pin_conv_hand, pin_conv_numpy, pin_conv_split_resume, pin_conv_magnitude,
         pin_conv_scan_brute_force, pin_conv_bwd_chain_fd, pin_conv_bwd_numpy, pin_conv_bwd_magnitude,
-        pin_bwd_magnitudes, pin_conv_bwd_magnitude_bracket]
+        pin_bwd_magnitudes, pin_conv_bwd_magnitude_bracket,
+        pin_scalar_a_semiseparable]

@@ -51,6 +51,7 @@ def test_header_declares_the_entry_points():
                                   "s6_last_state_ex", "s6_last_state_workspace_size",
                                   "s6_scan_bwd", "s6_scan_bwd_ckpt", "s6_scan_bwd_ex", "s6_scan_bwd_workspace_size",
                                   "s6_scan_fwd", "s6_scan_fwd_ckpt", "s6_scan_fwd_ex", "s6_scan_fwd_workspace_size",
+                                  "s6_ssd_scan_fwd", "s6_ssd_scan_fwd_workspace_size",
                                   "s6_state_update", "s6_state_update_ex", "s6_status_str", "s6_version"]
 
 
@@ -344,3 +345,24 @@ def test_library_source_allocates_nothing():
         text = open(f).read()
         for word in ("hipMalloc", "hipFree", "hipHostMalloc", "hipMallocAsync"):
             assert word not in text, (f, word)
+
+
+def test_ssd_validation(lib, codes):
+    """The scalar-A chunked scan: dstate up to 16, the common checks, no
+    workspace at any size."""
+    def f(b=2, d=64, L=32, n=16, dt=1, x=P, y=P, A=P, z=None):
+        return lib.s6_ssd_scan_fwd(b, d, L, n, dt, x, P, A, P, P, None, z, None, y, None, None, 0, None)
+
+    assert f(n=17) == codes["S6_ERR_UNSUPPORTED"]
+    assert f(n=0) == codes["S6_ERR_UNSUPPORTED"]
+    assert f(dt=4) == codes["S6_ERR_DTYPE"]
+    assert f(L=-1) == codes["S6_ERR_SHAPE"]
+    assert f(x=None) == codes["S6_ERR_NULL"]
+    assert f(y=None) == codes["S6_ERR_NULL"]
+    assert f(A=None) == codes["S6_ERR_NULL"]
+    assert f(A=P_ODD) == codes["S6_ERR_ALIGN"]
+    assert f(dt=1, z=ctypes.c_void_p((1 << 20) + 1)) == codes["S6_ERR_ALIGN"]
+    assert f(b=0) == codes["S6_OK"]
+    for shape in ((8, 5120, 2048, 16), (1, 1536, 1 << 20, 16), (1, 16, 256, 4)):
+        assert _size(lib.s6_ssd_scan_fwd_workspace_size, *shape, 1) == (codes["S6_OK"], 0)
+    assert _size(lib.s6_ssd_scan_fwd_workspace_size, 1, 16, 256, 32, 1)[0] == codes["S6_ERR_UNSUPPORTED"]

@@ -126,7 +126,9 @@ def test_segmented_scan_graph_replays(torch_cuda):
     run()
     torch.cuda.synchronize()
     refs = (y.clone(), hl.clone(), hs.clone())
-    assert torch.equal(hl, hs)  # same segments, same fold
+    # the fused scan runs its last segment from the folded incoming state, the
+    # final-state scan folds that segment's aggregate too: equal to rounding
+    assert torch.allclose(hl, hs, rtol=1e-5, atol=1e-6)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         run()
