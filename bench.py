@@ -247,13 +247,13 @@ def bench_scan(w, steps, warmup, flush=False, softplus=False, zoh=False, conv_k=
 
 
 def ssd_mfma_flops(w):
-    """Matrix-core flops one s6_ssd_scan_fwd issues (bf16 inputs): per
-    16-token chunk and 16-channel tile, ten 16x16x16 products (two
-    transposes of B and C by the identity, the Gram matrix, tril(G) V as
-    three products of two-part operands, C H and B^T V as two each), 2 *
-    16^3 flops each."""
+    """Matrix-core flops one s6_ssd_scan_fwd issues, per precision: per
+    16-token chunk and 16-channel tile three bf16 16x16x16 products (B and C
+    made token-major by the identity, the Gram matrix; bf16 inputs) and
+    three fp32 16x16x16 products as twelve 16x16x4 ones (tril(G) V, C H,
+    B^T V), 2 * 16^3 flops per 16x16x16."""
     tiles = w.batch * ((w.dim + 15) // 16) * ((w.seqlen + 15) // 16)
-    return tiles * 10 * 2 * 16 ** 3
+    return {"bf16": tiles * 3 * 2 * 16 ** 3, "fp32": tiles * 3 * 2 * 16 ** 3}
 
 
 def bench_ssd(w, steps, warmup):
@@ -293,9 +293,9 @@ def bench_ssd(w, steps, warmup):
                  "token_channels_per_s": w.batch * w.dim * w.seqlen / (ms * 1e-3),
                  "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": byts,
-                              "mfma": {"flops_per_launch": fl, "achieved_TFLOPs": round(fl / (ms * 1e-3) / 1e12, 1),
-                                       "peak_bf16_TFLOPs": 2500.0,
-                                       "frac": round(fl / (ms * 1e-3) / 1e12 / 2500.0, 4)}},
+                              "mfma": {p: {"flops_per_launch": f, "achieved_TFLOPs": round(f / (ms * 1e-3) / 1e12, 1),
+                                           "peak_TFLOPs": pk, "frac": round(f / (ms * 1e-3) / 1e12 / pk, 4)}
+                                       for (p, f), pk in zip(fl.items(), (2500.0, 157.3))}},
                  "note": "s6_ssd_scan_fwd: one A value per channel, chunked matrix form on the matrix cores"}
 
 

@@ -23,8 +23,11 @@ LIB = os.path.join(PKG, "libs6.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed FP32 instructions are switched off: hipcc would otherwise pair
 # independent fp32 operations into v_pk_* forms.
+# MFMA results go to VGPRs (the matrix-core kernels read them with VALU
+# instructions; the accumulation-register form would add a copy per result).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", os.path.join(ROOT, "include")]
 
 

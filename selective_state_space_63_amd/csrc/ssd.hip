@@ -35,10 +35,10 @@
 // values it holds channel c, tokens 4g .. 4g+3 (the natural row-major layout
 // of x, delta, z and y, and the layout of a 16 x 16 x 16 MFMA's B operand
 // and result); B and C are loaded the same way (state c, tokens 4g .. 4g+3)
-// and turned token-major by an MFMA with the identity.  Operands in fp32
-// (V, G, the state) enter bf16 MFMAs as a sum of two bf16 parts (hi + lo,
-// three products, relative error below 2^-16); with fp32 inputs the products
-// run on fp32 MFMAs instead.
+// and turned token-major by an MFMA with the identity.  Products whose
+// operands are exact in bf16 (the transposes and the Gram matrix of bf16 B
+// and C) run on the bf16 matrix cores; the three with an fp32 operand (V, the
+// state) on the fp32 matrix cores, so no operand is rounded below fp32.
 #include "s6_internal.h"
 
 namespace s6i {
@@ -51,7 +51,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kQ = 16;                 // tokens per chunk
 constexpr int kTile = 16;              // channels per wave
-constexpr int kPF = 4;                 // chunks in flight (ring of staged loads)
 // Largest |a| c_16 (log2 units) for the separated decays: P, Q, e^{a r} stay
 // within 2^-80 .. 2^80 of the data, far from fp32's limits.
 constexpr float kRangeLog2 = 160.0f;
@@ -61,66 +60,101 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
 }
-
 __device__ __forceinline__ float bf_lo(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
 
-// An MFMA operand of four fp32 values per lane, as bf16 parts (hi, lo) or
-// as the fp32 values themselves.
-struct Opnd {
-  bf16x4 hi, lo;
-  float f[4];
+// Four tokens of one row as loaded: packed bf16 (uint2) or fp32 (float4).
+template <typename In>
+struct Four;
+template <>
+struct Four<uint16_t> {
+  uint2 v;
+  __device__ __forceinline__ void unpack(float f[4]) const {
+    f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+  }
+  __device__ __forceinline__ void pack(const float f[4]) { v.x = pack_bf16(f[0], f[1]); v.y = pack_bf16(f[2], f[3]); }
+  __device__ __forceinline__ void keep_if(bool k) { v.x = k ? v.x : 0u; v.y = k ? v.y : 0u; }
+};
+template <>
+struct Four<float> {
+  float4 v;
+  __device__ __forceinline__ void unpack(float f[4]) const { f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w; }
+  __device__ __forceinline__ void pack(const float f[4]) { v = make_float4(f[0], f[1], f[2], f[3]); }
+  __device__ __forceinline__ void keep_if(bool k) {
+    v.x = k ? v.x : 0.0f; v.y = k ? v.y : 0.0f; v.z = k ? v.z : 0.0f; v.w = k ? v.w : 0.0f;
+  }
 };
 
-template <bool F32>
-__device__ __forceinline__ void split(const float v[4], Opnd& o) {
-  if constexpr (F32) {
-    for (int j = 0; j < 4; ++j) o.f[j] = v[j];
+// Four tokens of one row at byte offset `off` from a wave-uniform base (the
+// tile's first row): one 8- or 16-byte load (VEC: L % 4 == 0, rows aligned;
+// groups past the end read the row's last group, masked by the caller), or
+// four clamped element loads.
+template <typename In, bool VEC>
+__device__ __forceinline__ Four<In> load4(const char* __restrict__ base, uint32_t row_off, int64_t t, int64_t L) {
+  Four<In> o;
+  if constexpr (VEC) {
+    const uint32_t tc = (uint32_t)(t < L ? t : L - 4);
+    const char* p = base + row_off + tc * (uint32_t)sizeof(In);
+    if constexpr (sizeof(In) == 2)
+      o.v = *reinterpret_cast<const uint2*>(p);
+    else
+      o.v = *reinterpret_cast<const float4*>(p);
   } else {
-    const uint32_t h01 = pack_bf16(v[0], v[1]), h23 = pack_bf16(v[2], v[3]);
-    const uint32_t l01 = pack_bf16(v[0] - bf_lo(h01), v[1] - bf_hi(h01));
-    const uint32_t l23 = pack_bf16(v[2] - bf_lo(h23), v[3] - bf_hi(h23));
-    o.hi = __builtin_bit_cast(bf16x4, (uint64_t)h01 | ((uint64_t)h23 << 32));
-    o.lo = __builtin_bit_cast(bf16x4, (uint64_t)l01 | ((uint64_t)l23 << 32));
+    In e[4];
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t tj = (uint32_t)(t + j < L ? t + j : L - 1);
+      e[j] = *reinterpret_cast<const In*>(base + row_off + tj * (uint32_t)sizeof(In));
+    }
+    if constexpr (sizeof(In) == 2)
+      o.v = make_uint2((uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16));
+    else
+      o.v = make_float4(e[0], e[1], e[2], e[3]);
   }
+  return o;
 }
 
-// Values that are exact in bf16 (inputs, transposed inputs): one part.
-template <bool F32>
-__device__ __forceinline__ void exact(const float v[4], Opnd& o) {
-  if constexpr (F32) {
-    for (int j = 0; j < 4; ++j) o.f[j] = v[j];
-  } else {
-    const uint32_t h01 = pack_bf16(v[0], v[1]), h23 = pack_bf16(v[2], v[3]);
-    o.hi = __builtin_bit_cast(bf16x4, (uint64_t)h01 | ((uint64_t)h23 << 32));
-  }
-}
-
-__device__ __forceinline__ f32x4 mma_bf(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
-// D += A B (16 x 16 x 16).  Lane 16 g + c holds A[c][4g + j] and B[4g + j][c]
-// (j = 0..3); D's lane holds D[4g + r][c] (r = 0..3).  EA / EB: the operand
-// is exact in one bf16 part; otherwise its lo part enters too (the lo x lo
-// product is left out).
-template <bool F32, bool EA, bool EB>
-__device__ __forceinline__ f32x4 mma(const Opnd& a, const Opnd& b, f32x4 d) {
-  if constexpr (F32) {
-    for (int j = 0; j < 4; ++j) d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f[j], b.f[j], d, 0, 0, 0);
-  } else {
-    d = mma_bf(a.hi, b.hi, d);
-    if constexpr (!EB) d = mma_bf(a.hi, b.lo, d);
-    if constexpr (!EA) d = mma_bf(a.lo, b.hi, d);
-  }
+// D += A B on the fp32 matrix cores (16 x 16 x 16 as four 16 x 16 x 4
+// products).  Lane 16 g + c holds A[c][4g + j] and B[4g + j][c] in a[j],
+// b[j]; D's lane holds D[4g + r][c] in d[r].
+__device__ __forceinline__ f32x4 mma_f32(const float a[4], const float b[4], f32x4 d) {
+  for (int j = 0; j < 4; ++j) d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], d, 0, 0, 0);
   return d;
+}
+
+// The same product with both operands exact in bf16 (inputs, transposed
+// inputs): one bf16 matrix-core instruction, or fp32 products for fp32 data.
+template <typename In>
+__device__ __forceinline__ f32x4 mma_in(const Four<In>& a, const Four<In>& b, f32x4 d) {
+  if constexpr (sizeof(In) == 2) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a.v), __builtin_bit_cast(bf16x4, b.v),
+                                                      d, 0, 0, 0);
+  } else {
+    float fa[4], fb[4];
+    a.unpack(fa);
+    b.unpack(fb);
+    return mma_f32(fa, fb, d);
+  }
 }
 
 // Raw inputs of one chunk for one lane: 4 tokens of x, delta, z of channel
 // c and 4 tokens of B and C of state c.
 template <typename In>
 struct Raw {
-  In x[4], dl[4], z[4], b[4], c[4];
+  Four<In> x, dl, z, b, c;
+};
+
+// A chunk's results that do not depend on the state entering it.
+template <typename In>
+struct Front {
+  f32x4 Yd;      // tril(G) V
+  f32x4 S;       // B^T V
+  float P[4];    // e^{a (c_t - r)} of the lane's 4 tokens
+  float ct[4];   // C token-major: lane (g, c) holds C[n = 4g + j][t = c] (A operand of C H)
+  float xv[4];   // x of the lane's 4 tokens (skip term)
+  Four<In> z;    // gate input
+  float kr;      // e^{a r} = e^{a (c_16 - r)}
+  float dec;     // e^{a c_16}
+  bool wide;     // a channel of the tile has |a| c_16 > kRangeLog2 (wave-uniform)
 };
 
 struct SsdArgs {
@@ -137,32 +171,26 @@ struct SsdArgs {
   int64_t D, L, N;
 };
 
-template <typename In, bool VEC>
-__device__ __forceinline__ void load4(const In* __restrict__ row, int64_t t, int64_t L, In out[4]) {
-  if constexpr (VEC) {
-    // L % 4 == 0 and rows aligned: a lane's 4 tokens are all in or all out;
-    // out-of-range groups read the row's last group (masked by the caller).
-    const int64_t tc = t < L ? t : L - 4;
-    if constexpr (sizeof(In) == 2) {
-      const uint2 v = *reinterpret_cast<const uint2*>(row + tc);
-      out[0] = (In)(v.x & 0xffff); out[1] = (In)(v.x >> 16);
-      out[2] = (In)(v.y & 0xffff); out[3] = (In)(v.y >> 16);
-    } else {
-      const float4 v = *reinterpret_cast<const float4*>(row + tc);
-      out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
-    }
-  } else {
-    for (int j = 0; j < 4; ++j) {
-      const int64_t tj = t + j < L ? t + j : L - 1;
-      out[j] = row[tj];
-    }
-  }
-}
+// Staging of 2-chunk groups through LDS (STG): per input one or two 16-byte
+// loads per lane cover the group's 32 tokens of the tile's 16 rows in runs of
+// 64 (bf16) or 128 (fp32) contiguous bytes, written to LDS and read back per
+// chunk in the MFMA layout; the group's y (16 rows x 32 fp32) is collected in
+// LDS and written as whole 128-byte lines.  Row pitches are padded against
+// bank conflicts and keep 16-byte alignment.
+constexpr int kGT = 2 * kQ;                    // tokens per staged group
+template <typename In>
+struct Stg {
+  static constexpr int kPitch = sizeof(In) == 2 ? 40 : 36;  // input row pitch (elements)
+  static constexpr int kLoads = sizeof(In) / 2;             // 16-byte loads per lane per input
+  static constexpr int kIn = 16 * kPitch;                   // elements per input tile
+};
+constexpr int kYPitch = 36;                    // y row pitch (floats)
 
-template <typename In, bool GATE, bool VEC>
-__global__ void __launch_bounds__(64) s6_ssd_kernel(SsdArgs a, int64_t batch) {
-  constexpr bool kF32 = std::is_same<In, float>::value;
-  __shared__ float lds[3 * kQ * kTile];  // the exact path's G, cumulative steps and inputs
+template <typename In, bool GATE, bool VEC, bool STG>
+__global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch) {
+  __shared__ float lds[3 * kQ * kTile];  // the unseparated path's G, cumulative steps and inputs
+  __shared__ __align__(16) In sin[STG ? 5 * Stg<In>::kIn : 1];  // staged inputs: x, delta, z, B, C
+  __shared__ __align__(16) float sy[STG ? 16 * kYPitch : 1];     // staged y of a group
 
   const int lane = threadIdx.x;
   const int g = lane >> 4, c = lane & 15;
@@ -170,160 +198,153 @@ __global__ void __launch_bounds__(64) s6_ssd_kernel(SsdArgs a, int64_t batch) {
   const int64_t d0 = (blockIdx.x / batch) * kTile;
   const int64_t D = a.D, L = a.L, N = a.N;
   const bool dval = d0 + c < D;
-  const int64_t dc = dval ? d0 + c : D - 1;          // clamped channel of this lane
+  const int cl = dval ? c : (int)(D - 1 - d0);       // clamped channel within the tile (never stored)
   const bool nval = c < N;
-  const int64_t nc = nval ? c : N - 1;               // clamped state of this lane
+  const int nc = nval ? c : (int)N - 1;              // clamped state (its B and C rows are zeroed)
 
-  const In* xr = static_cast<const In*>(a.x) + (b * D + dc) * L;
-  const In* dr = static_cast<const In*>(a.delta) + (b * D + dc) * L;
-  const In* zr = GATE ? static_cast<const In*>(a.z) + (b * D + dc) * L : nullptr;
-  const In* br = static_cast<const In*>(a.Bm) + (b * N + nc) * L;
-  const In* cr = static_cast<const In*>(a.Cm) + (b * N + nc) * L;
-  const float a2 = a.A[dc] * kLog2e;                  // a log2(e) <= 0
-  const float dsk = a.Dskip ? a.Dskip[dc] : 0.0f;
+  // wave-uniform bases of the tile's rows and 32-bit lane offsets
+  constexpr uint32_t esz = sizeof(In);
+  const char* xb = static_cast<const char*>(a.x) + (b * D + d0) * L * esz;
+  const char* db = static_cast<const char*>(a.delta) + (b * D + d0) * L * esz;
+  const char* zb = GATE ? static_cast<const char*>(a.z) + (b * D + d0) * L * esz : nullptr;
+  const char* bb = static_cast<const char*>(a.Bm) + b * N * L * esz;
+  const char* cb = static_cast<const char*>(a.Cm) + b * N * L * esz;
+  float* yb = a.y + (b * D + d0) * L;
+  const uint32_t xo = (uint32_t)cl * (uint32_t)L * esz;
+  const uint32_t no = (uint32_t)nc * (uint32_t)L * esz;
+  const uint32_t yo4 = (uint32_t)c * (uint32_t)L;
+  const float a2 = a.A[d0 + cl] * kLog2e;             // a log2(e)
+  const float dsk = a.Dskip ? a.Dskip[d0 + cl] : 0.0f;
 
-  // identity (B operand): lane (g, c) holds I[4g + j][c]
-  Opnd ident;
+  // identity (B operand): lane (g, c) holds I[4g + j][c]; lower-triangle mask
+  // of G (A layout: lane (g, c) holds G[t = c][s = 4g + j], kept for s <= t)
+  Four<In> ident;
+  float tri[4];
   {
     float v[4];
-    for (int j = 0; j < 4; ++j) v[j] = (4 * g + j == c) ? 1.0f : 0.0f;
-    exact<kF32>(v, ident);
+    for (int j = 0; j < 4; ++j) {
+      v[j] = (4 * g + j == c) ? 1.0f : 0.0f;
+      tri[j] = (4 * g + j <= c) ? 1.0f : 0.0f;
+    }
+    ident.pack(v);
   }
   // state tile: lane (g, c) holds H[n = 4g + r][d = c]
-  f32x4 H;
+  float H[4];
   for (int r = 0; r < 4; ++r) {
     const int n = 4 * g + r;
     H[r] = (a.h0 && dval && n < N) ? a.h0[(b * D + d0 + c) * N + n] : 0.0f;
   }
 
-  const int64_t nch = (L + kQ - 1) / kQ;
-  Raw<In> ring[kPF];
   auto issue = [&](Raw<In>& rw, int64_t k) {
     const int64_t t = k * kQ + 4 * g;
-    load4<In, VEC>(xr, t, L, rw.x);
-    load4<In, VEC>(dr, t, L, rw.dl);
-    if constexpr (GATE) load4<In, VEC>(zr, t, L, rw.z);
-    load4<In, VEC>(br, t, L, rw.b);
-    load4<In, VEC>(cr, t, L, rw.c);
+    rw.x = load4<In, VEC>(xb, xo, t, L);
+    rw.dl = load4<In, VEC>(db, xo, t, L);
+    if constexpr (GATE) rw.z = load4<In, VEC>(zb, xo, t, L);
+    rw.b = load4<In, VEC>(bb, no, t, L);
+    rw.c = load4<In, VEC>(cb, no, t, L);
   };
-  for (int i = 0; i < kPF; ++i) issue(ring[i], i);
 
-  auto chunk = [&](const Raw<In>& rw, int64_t k) {
-    const int64_t t0 = k * kQ + 4 * g;
-    float xv[4], dv[4], bv[4], cv[4];
-    for (int j = 0; j < 4; ++j) {
-      const bool ok = t0 + j < L;
-      xv[j] = (ok && dval) ? to_f32(rw.x[j]) : 0.0f;
-      dv[j] = (ok && dval) ? to_f32(rw.dl[j]) : 0.0f;
-      bv[j] = (ok && nval) ? to_f32(rw.b[j]) : 0.0f;
-      cv[j] = (ok && nval) ? to_f32(rw.c[j]) : 0.0f;
+  // Inputs of chunk k as values; mask: tokens past the end get a zero step,
+  // input, B and C (the state then passes through unchanged).  B and C rows
+  // of states >= N are zero.  Returns the cumulative step within the chunk
+  // (inclusive) in cs and its total.
+  auto prep = [&](Raw<In>& rw, int64_t k, bool mask, float xv[4], float dv[4], float cs[4], float& total) {
+    rw.x.unpack(xv);
+    rw.dl.unpack(dv);
+    rw.b.keep_if(nval);
+    rw.c.keep_if(nval);
+    if (mask) {
+      const int64_t t0 = k * kQ + 4 * g;
+      float bv[4], cv[4];
+      rw.b.unpack(bv);
+      rw.c.unpack(cv);
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = t0 + j < L;
+        xv[j] = ok ? xv[j] : 0.0f;
+        dv[j] = ok ? dv[j] : 0.0f;
+        bv[j] = ok ? bv[j] : 0.0f;
+        cv[j] = ok ? cv[j] : 0.0f;
+      }
+      rw.b.pack(bv);
+      rw.c.pack(cv);
     }
-    // cumulative step within the chunk: the lane's 4 tokens, then the
-    // groups before it (lanes c, c+16, c+32, c+48 hold the 4 groups)
-    float p[4];
-    p[0] = dv[0];
-    p[1] = p[0] + dv[1];
-    p[2] = p[1] + dv[2];
-    p[3] = p[2] + dv[3];
-    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[3]), __float_as_uint(p[3]), false, false);
+    // the lane's 4 tokens, then the groups before it (lanes c, c+16, c+32,
+    // c+48 hold the chunk's 4 groups)
+    float q[4];
+    q[0] = dv[0];
+    q[1] = q[0] + dv[1];
+    q[2] = q[1] + dv[2];
+    q[3] = q[2] + dv[3];
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(q[3]), __float_as_uint(q[3]), false, false);
     const float lo16 = __uint_as_float((unsigned)s16[0]), hi16 = __uint_as_float((unsigned)s16[1]);
     const float pair = lo16 + hi16;
     const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
     const float lo32 = __uint_as_float((unsigned)s32[0]), hi32 = __uint_as_float((unsigned)s32[1]);
-    const float total = lo32 + hi32;
+    total = lo32 + hi32;
     const float ex = ((g & 1) ? lo16 : 0.0f) + ((g & 2) ? lo32 : 0.0f);
-    float cs[4];
-    for (int j = 0; j < 4; ++j) cs[j] = ex + p[j];
+    for (int j = 0; j < 4; ++j) cs[j] = ex + q[j];
+  };
 
-    // B and C token-major: lane (g, c) holds X[n = 4g + j][t = c]
-    Opnd bn, cn;
-    exact<kF32>(bv, bn);
-    exact<kF32>(cv, cn);
+  // B and C token-major (an MFMA with the identity) and G^T = Bmat Cmat^T:
+  // lane (g, c) gets G[t = c][s = 4g + r], the A operand of tril(G) V.
+  auto gram = [&](const Raw<In>& rw, float ct[4], float gm[4]) {
     const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-    const f32x4 btf = mma<kF32, true, true>(bn, ident, z4);
-    const f32x4 ctf = mma<kF32, true, true>(cn, ident, z4);
-    Opnd bt, ct;
-    {
-      float v[4] = {btf[0], btf[1], btf[2], btf[3]};
-      exact<kF32>(v, bt);
-      float w[4] = {ctf[0], ctf[1], ctf[2], ctf[3]};
-      exact<kF32>(w, ct);
-    }
-    // G^T = Bmat Cmat^T: lane (g, c) gets G[t = c][s = 4g + r], the A
-    // operand of tril(G) V; entries with s > t are dropped
-    const f32x4 gt = mma<kF32, true, true>(bt, ct, z4);
-    float gv[4];
-    for (int r = 0; r < 4; ++r) gv[r] = (4 * g + r <= c) ? gt[r] : 0.0f;
+    const f32x4 btf = mma_in<In>(rw.b, ident, z4);
+    const f32x4 ctf = mma_in<In>(rw.c, ident, z4);
+    Four<In> bt, ctp;
+    float bv[4] = {btf[0], btf[1], btf[2], btf[3]};
+    for (int j = 0; j < 4; ++j) ct[j] = ctf[j];
+    bt.pack(bv);
+    ctp.pack(ct);
+    const f32x4 gt = mma_in<In>(bt, ctp, z4);
+    for (int j = 0; j < 4; ++j) gm[j] = gt[j] * tri[j];
+  };
 
-    float v[4];
-    for (int j = 0; j < 4; ++j) v[j] = dv[j] * xv[j];
-    const float rng = fabsf(a2) * total;  // |a| c_16 in log2 units
-    float P[4];
-    f32x4 Y;
-    const bool wide = __builtin_amdgcn_ballot_w64(rng > kRangeLog2) != 0;
-    if (!wide) {
-      const float half = 0.5f * total;
-      float V[4];
-      for (int j = 0; j < 4; ++j) {
-        const float u = a2 * (cs[j] - half);
-        P[j] = fast_exp2(u);
-        V[j] = v[j] * fast_exp2(-u);
-      }
-      const float kr = fast_exp2(a2 * half);  // e^{a r} = e^{a (c_16 - r)}
-      Opnd Vo, Go, Ho;
-      split<kF32>(V, Vo);
-      split<kF32>(gv, Go);
-      float hs[4] = {H[0] * kr, H[1] * kr, H[2] * kr, H[3] * kr};
-      split<kF32>(hs, Ho);
-      Y = mma<kF32, false, false>(Go, Vo, z4);
-      Y = mma<kF32, true, false>(ct, Ho, Y);
-      const f32x4 S = mma<kF32, true, false>(bn, Vo, z4);
-      const float dec = fast_exp2(a2 * total);
-      for (int r = 0; r < 4; ++r) H[r] = __builtin_fmaf(dec, H[r], kr * S[r]);
-    } else {
-      // decays to the chunk's ends (each <= 1) and per-pair decays within it
-      float W[4];
-      for (int j = 0; j < 4; ++j) {
-        P[j] = fast_exp2(a2 * cs[j]);
-        W[j] = v[j] * fast_exp2(a2 * (total - cs[j]));
-      }
-      Opnd Wo, Ho;
-      split<kF32>(W, Wo);
-      float hs[4] = {H[0], H[1], H[2], H[3]};
-      split<kF32>(hs, Ho);
-      const f32x4 Yo = mma<kF32, true, false>(ct, Ho, z4);
-      const f32x4 S = mma<kF32, true, false>(bn, Wo, z4);
-      const float dec = fast_exp2(a2 * total);
-      for (int r = 0; r < 4; ++r) H[r] = __builtin_fmaf(dec, H[r], S[r]);
-      float* sg = lds;                 // [t][s]
-      float* sc = lds + kQ * kTile;    // [channel][token] cumulative step
-      float* sv = sc + kQ * kTile;     // [channel][token] delta x
-      __syncthreads();
-      for (int r = 0; r < 4; ++r) sg[c * kQ + 4 * g + r] = gv[r];
-      for (int j = 0; j < 4; ++j) {
-        sc[c * kQ + 4 * g + j] = cs[j];
-        sv[c * kQ + 4 * g + j] = v[j];
-      }
-      __syncthreads();
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * g + r;
-        float acc = 0.0f;
-        for (int s = 0; s <= t; ++s)
-          acc = __builtin_fmaf(sg[t * kQ + s] * fast_exp2(a2 * (sc[c * kQ + t] - sc[c * kQ + s])), sv[c * kQ + s],
-                               acc);
-        Y[r] = __builtin_fmaf(P[r], Yo[r], acc);
-        P[r] = 1.0f;
-      }
+  // Everything of chunk k that does not depend on the state entering it,
+  // with the decays separated around the chunk's midpoint (the values are
+  // meaningless when f.wide; the chunk is then recomputed by `exact`).
+  auto front = [&](Raw<In>& rw, int64_t k, bool mask) {
+    Front<In> f;
+    float dv[4], cs[4], total;
+    prep(rw, k, mask, f.xv, dv, cs, total);
+    f.wide = __builtin_amdgcn_ballot_w64(!(fabsf(a2) * total <= kRangeLog2)) != 0;
+    const float ah = a2 * (0.5f * total);
+    float V[4];
+    for (int j = 0; j < 4; ++j) {
+      const float u = __builtin_fmaf(a2, cs[j], -ah);  // a (c_t - r) in log2 units
+      f.P[j] = fast_exp2(u);
+      V[j] = (dv[j] * f.xv[j]) * fast_exp2(-u);
     }
-    // output: y_t = P_t Y_t + D x_t, gated; lane (g, c) holds tokens 4g + r of channel c
+    f.kr = fast_exp2(ah);
+    f.dec = fast_exp2(a2 * total);
+    float gm[4], bn[4];
+    gram(rw, f.ct, gm);
+    rw.b.unpack(bn);
+    const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    f.Yd = mma_f32(gm, V, z4);   // tril(G) V
+    f.S = mma_f32(bn, V, z4);    // B^T V
+    f.z = rw.z;
+    return f;
+  };
+
+  // slot >= 0: chunk `slot` of a staged group, y goes to the LDS staging.
+  auto output = [&](const Four<In>& zr, const float P[4], const f32x4& Y, const float xv[4], int64_t k, bool mask,
+                    int slot) {
+    const int64_t t0 = k * kQ + 4 * g;
+    float zv[4];
+    if constexpr (GATE) zr.unpack(zv);
     float yo[4];
     for (int r = 0; r < 4; ++r) {
       float yy = __builtin_fmaf(P[r], Y[r], dsk * xv[r]);
-      if constexpr (GATE) yy *= silu(to_f32(rw.z[r]));
+      if constexpr (GATE) yy *= silu(zv[r]);
       yo[r] = yy;
     }
-    if (dval && t0 < L) {
-      float* yp = a.y + (b * D + d0 + c) * L + t0;
+    if (STG && slot >= 0) {
+      *reinterpret_cast<float4*>(sy + c * kYPitch + slot * kQ + 4 * g) = make_float4(yo[0], yo[1], yo[2], yo[3]);
+      return;
+    }
+    if (dval && (!mask || t0 < L)) {
+      float* yp = yb + yo4 + (uint32_t)t0;
       if constexpr (VEC) {
         *reinterpret_cast<float4*>(yp) = make_float4(yo[0], yo[1], yo[2], yo[3]);
       } else {
@@ -333,14 +354,145 @@ __global__ void __launch_bounds__(64) s6_ssd_kernel(SsdArgs a, int64_t batch) {
     }
   };
 
-  // Whole cycles of kPF chunks; chunks past the end are masked (zero step
-  // and input: the state passes through unchanged) and store nothing.
-  for (int64_t k = 0; k < nch; k += kPF) {
-#pragma unroll
-    for (int i = 0; i < kPF; ++i) {
-      chunk(ring[i], k + i);
-      issue(ring[i], k + i + kPF);
+  // The state-dependent rest of a chunk: C (e^{a r} H) joins tril(G) V, the
+  // state advances, the output is written.
+  auto back = [&](const Front<In>& f, int64_t k, bool mask, int slot) {
+    float hs[4];
+    for (int r = 0; r < 4; ++r) hs[r] = H[r] * f.kr;
+    const f32x4 Y = mma_f32(f.ct, hs, f.Yd);
+    for (int r = 0; r < 4; ++r) H[r] = __builtin_fmaf(f.dec, H[r], f.kr * f.S[r]);
+    output(f.z, f.P, Y, f.xv, k, mask, slot);
+  };
+
+  // Chunk k without the separation (reloads its inputs): decays to the
+  // chunk's ends (each <= 1) for the carried state and its update, per-pair
+  // decays within the chunk.
+  auto exact = [&](int64_t k, bool mask, int slot) {
+    Raw<In> rw;
+    issue(rw, k);
+    float xv[4], dv[4], cs[4], total;
+    prep(rw, k, mask, xv, dv, cs, total);
+    float P[4], W[4], v[4];
+    for (int j = 0; j < 4; ++j) {
+      v[j] = dv[j] * xv[j];
+      P[j] = fast_exp2(a2 * cs[j]);
+      W[j] = v[j] * fast_exp2(a2 * (total - cs[j]));
     }
+    float ct[4], gm[4], bn[4];
+    gram(rw, ct, gm);
+    rw.b.unpack(bn);
+    const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4 Yo = mma_f32(ct, H, z4);
+    const f32x4 S = mma_f32(bn, W, z4);
+    const float dec = fast_exp2(a2 * total);
+    for (int r = 0; r < 4; ++r) H[r] = __builtin_fmaf(dec, H[r], S[r]);
+    float* sg = lds;                 // [t][s]
+    float* sc = lds + kQ * kTile;    // [channel][token] cumulative step
+    float* sv = sc + kQ * kTile;     // [channel][token] step times input
+    __syncthreads();
+    for (int r = 0; r < 4; ++r) sg[c * kQ + 4 * g + r] = gm[r];
+    for (int j = 0; j < 4; ++j) {
+      sc[c * kQ + 4 * g + j] = cs[j];
+      sv[c * kQ + 4 * g + j] = v[j];
+    }
+    __syncthreads();
+    f32x4 Y;
+    float one[4];
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * g + r;
+      float acc = 0.0f;
+      for (int s = 0; s <= t; ++s)
+        acc = __builtin_fmaf(sg[t * kQ + s] * fast_exp2(a2 * (sc[c * kQ + t] - sc[c * kQ + s])), sv[c * kQ + s], acc);
+      Y[r] = __builtin_fmaf(P[r], Yo[r], acc);
+      one[r] = 1.0f;
+    }
+    output(rw.z, one, Y, xv, k, mask, slot);
+  };
+
+  // One chunk's back half; a chunk flagged wide is recomputed exactly from
+  // the state it entered with (the fast results are discarded).
+  auto finish = [&](const Front<In>& f, int64_t k, bool mask, int slot = -1) {
+    const float h0[4] = {H[0], H[1], H[2], H[3]};
+    back(f, k, mask, slot);
+    if (f.wide) {
+      for (int r = 0; r < 4; ++r) H[r] = h0[r];
+      exact(k, mask, slot);
+    }
+  };
+
+  const int64_t nch = (L + kQ - 1) / kQ;
+  int64_t k = 0;
+  if constexpr (STG) {
+    // Whole 32-token groups through the LDS staging; the next group's loads
+    // are in flight while a group is computed.
+    constexpr int NL = Stg<In>::kLoads;
+    constexpr int RPL = 16 / NL;                 // rows covered by one load instruction
+    constexpr int LPR = 64 / RPL;                // lanes per row
+    constexpr int EPP = 16 / (int)sizeof(In);    // elements per 16-byte piece
+    const int prow = lane / LPR, ppc = lane % LPR;  // this lane's row (within a load) and piece
+    u32x4 stage[5][NL];
+    const char* bases[5] = {xb, db, GATE ? zb : xb, bb, cb};
+    auto stage_rows = [&](int q, int in) {       // tile row this lane loads for load q of input in
+      const int r = prow + q * RPL;
+      if (in >= 3) return (uint32_t)(r < N ? r : N - 1);
+      return (uint32_t)(d0 + r < D ? r : (int)(D - 1 - d0));
+    };
+    auto load_group = [&](int64_t G) {
+      for (int in = 0; in < 5; ++in) {
+        if (!GATE && in == 2) continue;
+        for (int q = 0; q < NL; ++q) {
+          const uint32_t off = stage_rows(q, in) * (uint32_t)L * esz + (uint32_t)(G * kGT + ppc * EPP) * esz;
+          stage[in][q] = *reinterpret_cast<const u32x4*>(bases[in] + off);
+        }
+      }
+    };
+    const int64_t ngrp = L / kGT;
+    if (ngrp > 0) load_group(0);
+    for (int64_t G = 0; G < ngrp; ++G) {
+      __syncthreads();  // the previous group's reads of the staging are done
+      for (int in = 0; in < 5; ++in) {
+        if (!GATE && in == 2) continue;
+        for (int q = 0; q < NL; ++q)
+          *reinterpret_cast<u32x4*>(sin + in * Stg<In>::kIn + (prow + q * RPL) * Stg<In>::kPitch + ppc * EPP) =
+              stage[in][q];
+      }
+      if (G + 1 < ngrp) load_group(G + 1);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        // the lane's 4 tokens of chunk j: row c (channel or state), tokens 16 j + 4 g ..
+        Raw<In> rw;
+        const int eo = c * Stg<In>::kPitch + j * kQ + 4 * g;
+        Four<In>* dst[5] = {&rw.x, &rw.dl, &rw.z, &rw.b, &rw.c};
+        for (int in = 0; in < 5; ++in) {
+          if (!GATE && in == 2) continue;
+          const In* src = sin + in * Stg<In>::kIn + eo;
+          if constexpr (sizeof(In) == 2)
+            dst[in]->v = *reinterpret_cast<const uint2*>(src);
+          else
+            dst[in]->v = *reinterpret_cast<const float4*>(src);
+        }
+        const Front<In> f = front(rw, G * 2 + j, false);
+        finish(f, G * 2 + j, false, j);
+      }
+      __syncthreads();
+      // y of the group: 16 rows x 32 tokens, 8 lanes x 16 bytes per row
+      for (int h = 0; h < 2; ++h) {
+        const int r = (lane >> 3) + 8 * h, pc = lane & 7;
+        if (d0 + r < D)
+          *reinterpret_cast<float4*>(yb + (uint32_t)r * (uint32_t)L + (uint32_t)(G * kGT + pc * 4)) =
+              *reinterpret_cast<const float4*>(sy + r * kYPitch + pc * 4);
+      }
+    }
+    k = ngrp * 2;
+  }
+  // Chunks not covered by the staging (all of them without it; otherwise the
+  // last one or two), directly from global memory; tokens past the end masked.
+  for (; k < nch; ++k) {
+    Raw<In> rw;
+    issue(rw, k);
+    const Front<In> f = front(rw, k, true);
+    finish(f, k, true);
   }
   if (a.h_last && dval) {
     for (int r = 0; r < 4; ++r) {
@@ -351,13 +503,15 @@ __global__ void __launch_bounds__(64) s6_ssd_kernel(SsdArgs a, int64_t batch) {
 }
 
 template <typename In, bool GATE>
-int launch_ssd_t(const SsdArgs& a, int64_t batch, bool vec, hipStream_t st) {
+int launch_ssd_t(const SsdArgs& a, int64_t batch, bool vec, bool stg, hipStream_t st) {
   const int64_t tiles = (a.D + kTile - 1) / kTile;
   const dim3 grid((unsigned)(tiles * batch));
-  if (vec)
-    hipLaunchKernelGGL((s6_ssd_kernel<In, GATE, true>), grid, dim3(64), 0, st, a, batch);
+  if (stg)
+    hipLaunchKernelGGL((s6_ssd_kernel<In, GATE, true, true>), grid, dim3(64), 0, st, a, batch);
+  else if (vec)
+    hipLaunchKernelGGL((s6_ssd_kernel<In, GATE, true, false>), grid, dim3(64), 0, st, a, batch);
   else
-    hipLaunchKernelGGL((s6_ssd_kernel<In, GATE, false>), grid, dim3(64), 0, st, a, batch);
+    hipLaunchKernelGGL((s6_ssd_kernel<In, GATE, false, false>), grid, dim3(64), 0, st, a, batch);
   S6_HIP(hipGetLastError(), "s6_ssd_kernel launch");
   return S6_OK;
 }
@@ -407,12 +561,16 @@ int s6_ssd_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, 
   bool vec = seqlen % 4 == 0 && aligned(y, 16);
   for (const void* p : ins)
     if (p && !aligned(p, 4 * esz)) vec = false;
+  // LDS staging of 32-token groups: every row starts 16-byte aligned
+  bool stg = vec && (seqlen * (int64_t)esz) % 16 == 0;
+  for (const void* p : ins)
+    if (p && !aligned(p, 16)) stg = false;
   SsdArgs a;
   a.x = x; a.delta = delta; a.z = z; a.Bm = Bm; a.Cm = Cm; a.A = A; a.Dskip = Dskip; a.h0 = h0; a.y = y;
   a.h_last = h_last; a.D = dim; a.L = seqlen; a.N = dstate;
   if (in_dtype == S6_BF16)
-    return z ? launch_ssd_t<uint16_t, true>(a, batch, vec, st) : launch_ssd_t<uint16_t, false>(a, batch, vec, st);
-  return z ? launch_ssd_t<float, true>(a, batch, vec, st) : launch_ssd_t<float, false>(a, batch, vec, st);
+    return z ? launch_ssd_t<uint16_t, true>(a, batch, vec, stg, st) : launch_ssd_t<uint16_t, false>(a, batch, vec, stg, st);
+  return z ? launch_ssd_t<float, true>(a, batch, vec, stg, st) : launch_ssd_t<float, false>(a, batch, vec, stg, st);
 }
 
 }  // extern "C"

@@ -49,6 +49,8 @@ SHAPES = [
     (2, 33, 16, 130, synth.BF16, False),
     (2, 48, 16, 2048, synth.F32, True),
     (1, 16, 1, 64, synth.BF16, True),       # one state
+    (2, 40, 16, 2056, synth.BF16, True),    # staged 32-token groups, then a partial chunk
+    (1, 24, 16, 560, synth.F32, True),      # staged groups, then one whole chunk
 ]
 
 
