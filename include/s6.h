@@ -50,7 +50,8 @@
  *     before any HIP call, so a rejected call has no side effect.  Values are
  *     not checked: NaN/Inf propagate.  Accuracy is specified for A <= 0 and
  *     delta >= 0 (decaying states).
- *   Memory: the library allocates nothing and keeps no state between calls.
+ *   Memory: the library allocates nothing and keeps no state between calls
+ *     (except s6_scan_fwd_noalloc's static buffer, see there).
  *     Entry points that may need scratch memory take a caller-owned device
  *     workspace (void* workspace, size_t workspace_bytes), 256-byte aligned,
  *     of at least the size the matching *_workspace_size query returns for
@@ -114,6 +115,24 @@ int s6_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
                 const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
                 const float* Dskip, const void* z, const float* h0, float* y, float* h_last,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* s6_scan_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * no workspace argument; when the sequence is cut into segments, their
+ * carries go to a static device buffer of the library (8 MiB, one per GPU,
+ * held until the process ends; its address is looked up once per device on
+ * the first call there).  No hipMalloc, hipFree or allocating library call.
+ * A call that would need more than 8 MiB returns S6_ERR_WORKSPACE before any
+ * work is enqueued (on a 256-CU device a segmented forward needs at most
+ * about 6 MB, whatever the sequence length).  Every call on one GPU shares
+ * that buffer and leaves its contents behind (nothing in it needs to start
+ * at zero): calls that overlap on one GPU -- concurrent streams, or host
+ * threads -- race and must be serialised by the caller.  Same arguments,
+ * checks and results as s6_scan_fwd otherwise. */
+int s6_scan_fwd_noalloc(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                        const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
+                        const float* Dskip, const void* z, const float* h0, float* y, float* h_last,
+                        void* stream);
 
 /* Workspace size in bytes (*bytes) of the forward scans (s6_scan_fwd,
  * s6_scan_fwd_ex, s6_scan_fwd_ckpt, s6_conv_scan_fwd) and of the final-state

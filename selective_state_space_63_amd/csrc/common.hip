@@ -71,7 +71,9 @@ const char* s6_status_str(int status) {
     case S6_ERR_UNSUPPORTED: return "unsupported: dstate outside 1..32, filter width outside 1..4, or an option this entry point lacks";
     case S6_ERR_ALIGN: return "a pointer is not aligned to its element size";
     case S6_ERR_FLAGS: return "unknown option bits in flags";
-    case S6_ERR_WORKSPACE: return "the call needs a workspace: none given, or smaller than its *_workspace_size";
+    case S6_ERR_WORKSPACE:
+      return "the call needs a workspace: none given, or smaller than its *_workspace_size (s6_scan_fwd_noalloc: "
+             "more than its 8 MiB static scratch)";
     case S6_ERR_HIP: return g_err[0] ? g_err : "HIP error";
     default: return "unknown status";
   }

@@ -5,7 +5,16 @@
 // scan_ext.hip, scan_conv.hip and scan_hold.hip.
 #include "scan_kernel.h"
 
+#include <mutex>
+
 namespace s6i {
+
+// Device scratch of s6_scan_fwd_noalloc: every GPU the library runs on holds
+// its own copy for the life of the process.  In host code `scratch` is only a
+// stand-in for the symbol; its device address comes from hipGetSymbolAddress
+// (scratch_ptr), once per device.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -122,6 +131,28 @@ int launch_copy_state(const float* src, float* dst, int64_t n, hipStream_t st) {
 
 namespace {
 
+// Device address of this device's `scratch`, looked up on the first call on
+// each device (with that device current) and kept per device.
+int scratch_ptr(void** out) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDev];
+  int dev = 0;
+  S6_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDev) {
+    snprintf(g_err, sizeof(g_err), "device %d: the static scratch is kept for devices 0..%d", dev, kMaxDev - 1);
+    return S6_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    S6_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return S6_OK;
+}
+
 // The convolution front of s6_conv_scan_fwd: filter (D, width), bias,
 // state before token 0; all null for the plain scan.
 struct ConvFront {
@@ -137,7 +168,7 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
               const void* x, const void* delta, const float* dbias, int flags, const float* A,
               const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
               float* y, float* h_last, void* workspace, size_t workspace_bytes, void* stream,
-              const ConvFront& cf = ConvFront(), float* ckpt = nullptr) {
+              const ConvFront& cf = ConvFront(), float* ckpt = nullptr, bool static_ws = false) {
   int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
   if (rc) return rc;
   if (flags & ~(S6_DELTA_SOFTPLUS | S6_ZOH_EXACT)) return S6_ERR_FLAGS;
@@ -178,6 +209,13 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
   const bool gate = want_y && z != nullptr;
   const int64_t S = p.segs;
   const ScanWs wl = scan_ws_layout(want_y, p, batch, dim, dstate);
+  if (static_ws && wl.total > 0) {
+    // the library's own scratch instead of a caller's workspace
+    if (wl.total > kScratchBytes) return S6_ERR_WORKSPACE;
+    rc = scratch_ptr(&workspace);
+    if (rc) return rc;
+    workspace_bytes = kScratchBytes;
+  }
   if (wl.total > 0 && (!workspace || workspace_bytes < wl.total)) return S6_ERR_WORKSPACE;
   if (wl.total > 0 && !aligned(workspace, 256)) return S6_ERR_ALIGN;
 
@@ -263,6 +301,14 @@ int s6_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
                 void* workspace, size_t workspace_bytes, void* stream) {
   return scan_impl(true, batch, dim, seqlen, dstate, in_dtype, x, delta, nullptr, 0, A, Bm, Cm, Dskip,
                    z, h0, y, h_last, workspace, workspace_bytes, stream);
+}
+
+int s6_scan_fwd_noalloc(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
+                        const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
+                        const float* Dskip, const void* z, const float* h0, float* y, float* h_last,
+                        void* stream) {
+  return scan_impl(true, batch, dim, seqlen, dstate, in_dtype, x, delta, nullptr, 0, A, Bm, Cm, Dskip,
+                   z, h0, y, h_last, nullptr, 0, stream, ConvFront(), nullptr, true);
 }
 
 int s6_scan_fwd_ex(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,

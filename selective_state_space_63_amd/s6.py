@@ -70,6 +70,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         getattr(lib, q).argtypes = [i64, i64, i64, i64, i32, szp]
     lib.s6_scan_bwd_workspace_size.restype = i32
     lib.s6_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i32, i32, i32, szp]
+    lib.s6_scan_fwd_noalloc.restype = i32
+    lib.s6_scan_fwd_noalloc.argtypes = [i64, i64, i64, i64, i32] + [vp] * 11
     lib.s6_ssd_scan_fwd.restype = i32
     lib.s6_ssd_scan_fwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 10 + ws
     lib.s6_ssd_scan_fwd_workspace_size.restype = i32

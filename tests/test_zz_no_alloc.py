@@ -1,0 +1,60 @@
+"""s6_scan_fwd_noalloc (the forward for callers that cannot allocate: its
+segment carries live in the library's static device scratch) against
+s6_scan_fwd with a caller workspace, through the C ABI: two calls in a row,
+the second on a smaller input, each output equal to s6_scan_fwd's bit for
+bit (same kernels, same plan) and within the bar of the oracle on sampled
+channels."""
+import ctypes
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import TOL, host64, scaled  # noqa: E402
+from selective_state_space_63_amd import synth  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_63_amd import s6
+    s6.load_library()
+    return torch
+
+
+def _noalloc(lib, w, inp, y, hl, stream):
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    return lib.s6_scan_fwd_noalloc(w.batch, w.dim, w.seqlen, w.dstate, 1, P(inp["x"]), P(inp["delta"]), P(inp["A"]),
+                                   P(inp["Bm"]), P(inp["Cm"]), P(inp["Dskip"]), P(inp["z"]), None, P(y), P(hl), stream)
+
+
+@pytest.mark.parametrize("order", ["large_then_small"])
+def test_noalloc_matches_workspace_entry(torch_cuda, oracle, order):
+    import torch
+    from selective_state_space_63_amd import s6
+    lib = s6.load_library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    # (batch, dim, dstate, seqlen): both cut into segments; the second needs less scratch
+    shapes = [(1, 1536, 16, 65536), (1, 96, 16, 8192)]
+    sizes = [s6.workspace_size("scan_fwd", b, d, L, n) for b, d, n, L in shapes]
+    assert sizes[0] > sizes[1] > 0 and sizes[0] <= (8 << 20)
+    for i, (b, d, n, L) in enumerate(shapes):
+        w = synth.custom(b, d, n, L, synth.BF16, True, seed=6100 + i)
+        print(f"[case] noalloc call {i}: {w.name} (scratch {sizes[i]} bytes)", flush=True)
+        inp = synth.device_full(w)
+        y1 = torch.full((b, d, L), float("nan"), device="cuda")
+        h1 = torch.full((b, d, n), float("nan"), device="cuda")
+        assert _noalloc(lib, w, inp, y1, h1, stream) == 0
+        y2, h2 = s6.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], D=inp["Dskip"], z=inp["z"],
+                             return_last_state=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2) and torch.equal(h1, h2), i
+        ch = np.linspace(0, d - 1, 8).astype(int)
+        r = oracle.scan(host64(inp["x"][:, ch]), host64(inp["delta"][:, ch]), host64(inp["A"][ch]),
+                        host64(inp["Bm"]), host64(inp["Cm"]), Dskip=host64(inp["Dskip"][ch]),
+                        z=host64(inp["z"][:, ch]))
+        assert scaled(host64(y1[:, ch]), r["y"], r["m"]) <= TOL[synth.BF16]
+        assert scaled(host64(h1[:, ch]), r["h_last"], r["H_last"]) <= TOL[synth.BF16]
