@@ -402,7 +402,7 @@ def bench_decode(steps_total, warmup):
         "effective_GBps": gbs,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4)},
-        "note": "plain launches, state resident in device memory (fits the 256 MB Infinity Cache)",
+        "note": "plain launches, state (84 MB) resident in device memory and updated in place",
     }
     # The same S steps captured once in a HIP graph and replayed (the state
     # is reset eagerly before each replay); each replay must reproduce the
@@ -774,6 +774,8 @@ def main():
                     help="only time s6_scan_bwd on the workload (one JSON line; for profiling)")
     ap.add_argument("--conv-k", type=int, default=0,
                     help="with --backward-only: time s6_conv_scan_bwd with a filter of this width")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only time the decode steps (one JSON line; for profiling)")
     ap.add_argument("--ssd-only", action="store_true",
                     help="only time s6_ssd_scan_fwd on the scalar-A workload (one JSON line; for profiling)")
     args = ap.parse_args()
@@ -792,6 +794,9 @@ def main():
     s6.load_library()
     w = synth.WORKLOADS[args.workload]
     in_bytes = 2 if w.dtype == synth.BF16 else 4
+    if args.decode_only:
+        print(json.dumps({"decode": bench_decode(args.decode_steps, args.warmup)}), flush=True)
+        return
     if args.ssd_only:
         _, line = bench_ssd(synth.WORKLOADS["ssd3b"], args.steps, args.warmup)
         print(json.dumps({"ssd": line}), flush=True)

@@ -1,12 +1,14 @@
 """Full-size workloads, launched exactly as bench.py launches them, checked
-against the oracle on sampled (batch, channel) rows over their whole length:
-channel-block edges (63/64), the first and last channel, and random ones.
+against the oracle on every output:
 
-  m3b    : batch 8, D 5120, N 16, L 2048 (the benchmark workload)
-  long   : batch 1, D 1536, N 16, L 2^20 (segmented scan with carries)
-  decode : batch 256, D 5120, N 16, 1024 single-token steps
-  backward of m3b: one whole batch row (every channel, so dB and dC of that
-           row are complete) against the oracle's backward of that row
+  m3b    : batch 8, D 5120, N 16, L 2048 (the benchmark workload), batch
+           row by batch row
+  long   : batch 1, D 1536, N 16, L 2^20 (segmented scan with carries), in
+           streamed blocks of 64 channels over the whole length
+  decode : batch 256, D 5120, N 16, 1024 single-token steps, step by step
+           (every token's y) and the final state
+  backward of m3b: every gradient of the whole batch (dA and dD summed over
+           all rows), from the recomputing path and from checkpoints
 """
 import numpy as np
 import pytest
@@ -27,27 +29,16 @@ def torch_cuda():
     return torch
 
 
-def _sample(w, k, seed):
-    g = np.random.default_rng(seed)
-    fixed = [0, 63, 64, w.dim - 1]
-    rnd = g.choice(w.dim, size=k, replace=False)
-    ds = sorted(set([d for d in fixed if d < w.dim] + [int(v) for v in rnd]))
-    bs = sorted(set([0, w.batch - 1] + [int(v) for v in g.integers(0, w.batch, size=2)]))
-    return bs, ds
+def _oracle_block(oracle, inp, b, c0, c1):
+    """The oracle's scan of channels c0..c1-1 of batch row b (whole length)."""
+    return oracle.scan(x=host64(inp["x"][b:b + 1, c0:c1]), delta=host64(inp["delta"][b:b + 1, c0:c1]),
+                       A=host64(inp["A"][c0:c1]), Bm=host64(inp["Bm"][b:b + 1]), Cm=host64(inp["Cm"][b:b + 1]),
+                       Dskip=host64(inp["Dskip"][c0:c1]),
+                       z=None if inp["z"] is None else host64(inp["z"][b:b + 1, c0:c1]))
 
 
-def _oracle_rows(oracle, inp, b, ds, L=None, h0=None):
-    sl = slice(None) if L is None else slice(0, L)
-    idx = np.array(ds)
-    args = dict(x=host64(inp["x"][b:b + 1, idx, sl]), delta=host64(inp["delta"][b:b + 1, idx, sl]),
-                A=host64(inp["A"][idx]), Bm=host64(inp["Bm"][b:b + 1, :, sl]),
-                Cm=host64(inp["Cm"][b:b + 1, :, sl]), Dskip=host64(inp["Dskip"][idx]),
-                z=None if inp["z"] is None else host64(inp["z"][b:b + 1, idx, sl]), h0=h0)
-    return oracle.scan(**args)
-
-
-@pytest.mark.parametrize("name,k", [("m3b", 24), ("long", 6)])
-def test_scan_workload_sampled(torch_cuda, oracle, name, k):
+@pytest.mark.parametrize("name,block", [("m3b", None), ("long", 64)])
+def test_scan_workload_full(torch_cuda, oracle, name, block):
     from selective_state_space_63_amd import s6
     w = synth.WORKLOADS[name]
     print(f"[case] workload {w.name}", flush=True)
@@ -55,18 +46,23 @@ def test_scan_workload_sampled(torch_cuda, oracle, name, k):
     y, hl = s6.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], D=inp["Dskip"],
                         z=inp["z"], return_last_state=True)
     torch_cuda.cuda.synchronize()
-    bs, ds = _sample(w, k, seed={"m3b": 11, "long": 12}[name])
+    step = block or w.dim
     worst = 0.0
-    for b in bs:
-        r = _oracle_rows(oracle, inp, b, ds)
-        ey = scaled(host64(y[b, ds]), r["y"][0], r["m"][0])
-        eh = scaled(host64(hl[b, ds]), r["h_last"][0], r["H_last"][0])
-        worst = max(worst, ey, eh)
-        assert ey <= TOL[w.dtype] and eh <= TOL[w.dtype], (name, b, ey, eh)
-    print(f"[result] {w.name} max scaled error {worst:.3e}", flush=True)
+    for b in range(w.batch):
+        for c0 in range(0, w.dim, step):
+            c1 = min(w.dim, c0 + step)
+            r = _oracle_block(oracle, inp, b, c0, c1)
+            ey = scaled(host64(y[b:b + 1, c0:c1]), r["y"], r["m"])
+            eh = scaled(host64(hl[b:b + 1, c0:c1]), r["h_last"], r["H_last"])
+            worst = max(worst, ey, eh)
+            assert ey <= TOL[w.dtype] and eh <= TOL[w.dtype], (name, b, c0, ey, eh)
+    print(f"[result] {w.name} every output: max scaled error {worst:.3e}", flush=True)
 
 
-def test_decode_workload_sampled(torch_cuda, oracle):
+def test_decode_workload_full(torch_cuda, oracle):
+    """The 1024 decode steps as bench.py launches them; the oracle steps the
+    same inputs from h = 0, and every step's y (256 x 5120) and the final
+    state are compared."""
     from selective_state_space_63_amd import s6
     w = synth.WORKLOADS["decode"]
     print(f"[case] workload {w.name}", flush=True)
@@ -77,27 +73,32 @@ def test_decode_workload_sampled(torch_cuda, oracle):
     z = inp["z"].permute(2, 0, 1).contiguous()
     Bm = inp["Bm"].permute(2, 0, 1).contiguous()
     Cm = inp["Cm"].permute(2, 0, 1).contiguous()
+    del inp["x"], inp["delta"], inp["z"]
     h = torch_cuda.zeros((w.batch, w.dim, w.dstate), device="cuda", dtype=torch_cuda.float32)
     ys = torch_cuda.empty((S, w.batch, w.dim), device="cuda", dtype=torch_cuda.float32)
     for s in range(S):
         s6.state_update(h, x[s], dl[s], inp["A"], Bm[s], Cm[s], D=inp["Dskip"], z=z[s], y=ys[s])
     torch_cuda.cuda.synchronize()
-    bs, ds = _sample(w, 12, seed=4)
+    A, Dk = host64(inp["A"]), host64(inp["Dskip"])
+    ho = np.zeros((w.batch, w.dim, w.dstate))
+    Ho = np.zeros_like(ho)
     worst = 0.0
-    for b in bs:
-        r = _oracle_rows(oracle, inp, b, ds)
-        ey = scaled(host64(ys[:, b, ds]).T, r["y"][0], r["m"][0])
-        eh = scaled(host64(h[b, ds]), r["h_last"][0], r["H_last"][0])
-        worst = max(worst, ey, eh)
-        assert ey <= TOL[w.dtype] and eh <= TOL[w.dtype], (b, ey, eh)
-    print(f"[result] {w.name} max scaled error {worst:.3e}", flush=True)
+    for s in range(S):
+        yo, mo = oracle.step(ho, Ho, host64(x[s]), host64(dl[s]), A, host64(Bm[s]), host64(Cm[s]), Dskip=Dk,
+                             z=host64(z[s]))
+        e = scaled(host64(ys[s]), yo, mo)
+        worst = max(worst, e)
+        assert e <= TOL[w.dtype], (s, e)
+    eh = scaled(host64(h), ho, Ho)
+    assert eh <= TOL[w.dtype], eh
+    print(f"[result] {w.name} every step: max scaled error {max(worst, eh):.3e}", flush=True)
 
 
 @pytest.mark.parametrize("ckpt", [False, True], ids=["recompute", "checkpoints"])
-def test_backward_m3b_row(torch_cuda, oracle, ckpt):
-    """s6_scan_bwd on the whole 3B layer (as bench.py runs it); batch row 5
-    of every per-row gradient (dx, ddelta, dz, dB, dC, dh0) against the
-    oracle's backward of that row alone."""
+def test_backward_m3b_full(torch_cuda, oracle, ckpt):
+    """s6_scan_bwd on the whole 3B layer (as bench.py runs it); every
+    gradient -- dx, ddelta, dz, dB, dC, dh0 per row, and dA, dD summed over
+    all 8 rows -- against the oracle's backward of the whole batch."""
     from selective_state_space_63_amd import s6
     w = synth.WORKLOADS["m3b"]
     print(f"[case] backward workload {w.name}", flush=True)
@@ -112,14 +113,12 @@ def test_backward_m3b_row(torch_cuda, oracle, ckpt):
         kw["ckpt"] = ck
     g = s6.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], dy, D=inp["Dskip"], z=inp["z"], **kw)
     torch_cuda.cuda.synchronize()
-    b = 5
-    r = oracle.scan_bwd(host64(inp["x"][b:b + 1]), host64(inp["delta"][b:b + 1]), host64(inp["A"]),
-                        host64(inp["Bm"][b:b + 1]), host64(inp["Cm"][b:b + 1]), host64(dy[b:b + 1]),
-                        Dskip=host64(inp["Dskip"]), z=host64(inp["z"][b:b + 1]))
+    r = oracle.scan_bwd(host64(inp["x"]), host64(inp["delta"]), host64(inp["A"]), host64(inp["Bm"]),
+                        host64(inp["Cm"]), host64(dy), Dskip=host64(inp["Dskip"]), z=host64(inp["z"]))
     worst = 0.0
     for gk, ok in (("dx", "dx"), ("ddelta", "ddelta"), ("dz", "dz"), ("dBm", "dBm"), ("dCm", "dCm"),
-                   ("dh0", "dh0")):
-        e = scaled(host64(g[gk][b:b + 1]), r[ok], r["m" + ok])
+                   ("dh0", "dh0"), ("dA", "dA"), ("dD", "dDskip")):
+        e = scaled(host64(g[gk]), r[ok], r["m" + ok])
         worst = max(worst, e)
         assert e <= TOL[w.dtype], (gk, e)
-    print(f"[result] backward {w.name} row {b}: max scaled error {worst:.3e}", flush=True)
+    print(f"[result] backward {w.name} every gradient: max scaled error {worst:.3e}", flush=True)
