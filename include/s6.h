@@ -262,8 +262,11 @@ int s6_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
  * for s6_scan_bwd_ckpt (it needs no room for the recomputed segment
  * states).  Its largest parts are the per-16-channel-block partial sums of
  * dBm and dCm (2 * ceil(dim/16) * batch * dstate * seqlen floats) and, without
- * checkpoints, the state entering every 64-token segment (batch * dim *
- * dstate * ceil(seqlen/64) floats). */
+ * checkpoints, the recomputed states: where batch * ceil(dim/32) workgroups
+ * of a sequential scan fill the GPU, the state entering every 16-token chunk
+ * (batch * dim * dstate * ceil(seqlen/16) floats), otherwise that entering
+ * every 64-token segment with the segments' end states (about twice
+ * batch * dim * dstate * ceil(seqlen/64) floats). */
 int s6_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                                int conv_width, int from_ckpt, size_t* bytes);
 

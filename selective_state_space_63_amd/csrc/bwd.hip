@@ -34,8 +34,11 @@ constexpr int kBwdPitch = kBwdSeg + 4;
 // kernels take 103-128 VGPRs (four waves per SIMD), with two (N > 16) about
 // 180 (two waves per SIMD).  Several 4-wave workgroups per CU, whose barriers
 // fall at different times, run faster than fewer 8-wave ones.
+#ifndef S6_BWD_WAVES
+#define S6_BWD_WAVES 4
+#endif
 template <int SPL>
-constexpr int bwd_waves() { return 4; }
+constexpr int bwd_waves() { return S6_BWD_WAVES; }
 
 template <int SPL>
 constexpr size_t bwd_lds_bytes(bool sp) {
@@ -184,7 +187,11 @@ __device__ __forceinline__ float rows_sum4(const float (&v)[4]) {
 // The exact-hold and convolution levels would take about 140 VGPRs (three
 // waves per SIMD); held to 128 they spill a dozen values to scratch and run
 // 4-6% faster with the fourth wave.
-template <typename In, bool GATE, int SPL, int OPT>
+//
+// H16: a.hin holds the state entering every 16-token chunk (from a state-only
+// pass that wrote one per chunk), so the four chunk-start states of a segment
+// are loaded instead of recomputed from the segment's first state.
+template <typename In, bool GATE, int SPL, int OPT, bool H16>
 __global__ void __launch_bounds__(64 * bwd_waves<SPL>())
     __attribute__((amdgpu_waves_per_eu((OPT >= 2 && SPL == 1) ? 4 : 1))) s6_bwd_kernel(BwdArgs a) {
   constexpr bool SP = OPT >= 1;
@@ -279,7 +286,22 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>())
         hseg[j] = sv[j] ? a.hin[s * a.batch * D * N + (b * D + d) * N + n] : 0.0f;
       }
     };
-    if constexpr (OPT < 2) load_hseg();
+    // states at the four chunk starts of the segment (chunks past the end of
+    // the sequence: 0, their tokens are staged as delta = 0 and change nothing)
+    float hc[4][SPL];
+    if constexpr (H16) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int64_t q = s * (KS / 16) + k;
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+          const int64_t n = (int64_t)nl * SPL + j;
+          hc[k][j] = (sv[j] && q * 16 < L) ? a.hin[q * nstate + (b * D + d) * N + n] : 0.0f;
+        }
+      }
+    } else if constexpr (OPT < 2) {
+      load_hseg();
+    }
     __syncthreads();  // the previous segment's reads of the staged inputs are done
     for (int i = tid; i < CW * KS; i += NTHR) {
       const int cc = i / KS, t = i % KS;
@@ -371,9 +393,8 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>())
       __syncthreads();
     }
 
-    // states at the four chunk starts of the segment
-    float hc[4][SPL];
-    {
+    // states at the four chunk starts, recomputed from the segment's first
+    if constexpr (!H16) {
       if constexpr (OPT >= 2) load_hseg();
       float h[SPL];
 #pragma unroll
@@ -382,6 +403,7 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>())
       for (int k = 0; k < 4; ++k) {
 #pragma unroll
         for (int j = 0; j < SPL; ++j) hc[k][j] = h[j];
+        if (k == 3) break;  // the state after the last chunk is not needed
         for (int g = 0; g < 4; ++g) {
           // one group of 4 tokens at a time: the compiler would otherwise
           // hoist every LDS read of the segment and run out of registers
@@ -871,7 +893,7 @@ __global__ void s6_conv_bwd_reduce(const float* __restrict__ part, float* __rest
 }
 
 // carry: the part-carry kernel (parts 1 .. G-1) instead of the main kernel.
-template <typename In, bool GATE, int SPL, int OPT>
+template <typename In, bool GATE, int SPL, int OPT, bool H16>
 int launch_bwd_t(const BwdArgs& a, int64_t parts, bool carry, hipStream_t st) {
   constexpr int CW = 4 * bwd_waves<SPL>();
   const int64_t nblk = (a.D + CW - 1) / CW;
@@ -882,22 +904,30 @@ int launch_bwd_t(const BwdArgs& a, int64_t parts, bool carry, hipStream_t st) {
                        dim3((unsigned)(nblk * a.batch), (unsigned)(parts - 1)), block, lds, st, a);
     S6_HIP(hipGetLastError(), "s6_bwd_carry_kernel launch");
   } else {
-    hipLaunchKernelGGL((s6_bwd_kernel<In, GATE, SPL, OPT>), dim3((unsigned)(nblk * a.batch), (unsigned)parts), block,
+    hipLaunchKernelGGL((s6_bwd_kernel<In, GATE, SPL, OPT, H16>), dim3((unsigned)(nblk * a.batch), (unsigned)parts), block,
                        bwd_lds_bytes<SPL>(OPT >= 1), st, a);
     S6_HIP(hipGetLastError(), "s6_bwd_kernel launch");
   }
   return S6_OK;
 }
 
-template <typename In, int SPL, int OPT>
+template <typename In, int SPL, int OPT, bool H16 = false>
 int launch_bwd_g(const BwdArgs& a, bool gate, int64_t parts, bool carry, hipStream_t st) {
-  return gate ? launch_bwd_t<In, true, SPL, OPT>(a, parts, carry, st)
-              : launch_bwd_t<In, false, SPL, OPT>(a, parts, carry, st);
+  return gate ? launch_bwd_t<In, true, SPL, OPT, H16>(a, parts, carry, st)
+              : launch_bwd_t<In, false, SPL, OPT, H16>(a, parts, carry, st);
 }
 
+// h16: a.hin holds the state entering every chunk (plain and step-bias
+// levels only; one part).
 template <typename In>
-int launch_bwd(const BwdArgs& a, bool gate, int64_t parts, bool carry, hipStream_t st) {
+int launch_bwd(const BwdArgs& a, bool gate, int64_t parts, bool carry, bool h16, hipStream_t st) {
   const int opt = a.conv_w ? 3 : a.zoh ? 2 : (a.dbias || a.softplus || a.ddbias_part) ? 1 : 0;
+  if (h16) {
+    if (opt > 1 || parts != 1 || carry) return S6_ERR_UNSUPPORTED;
+    if (a.N <= 16)
+      return opt ? launch_bwd_g<In, 1, 1, true>(a, gate, 1, false, st) : launch_bwd_g<In, 1, 0, true>(a, gate, 1, false, st);
+    return opt ? launch_bwd_g<In, 2, 1, true>(a, gate, 1, false, st) : launch_bwd_g<In, 2, 0, true>(a, gate, 1, false, st);
+  }
   if (a.N <= 16) {
     if (opt == 3) return launch_bwd_g<In, 1, 3>(a, gate, parts, carry, st);
     if (opt == 2) return launch_bwd_g<In, 1, 2>(a, gate, parts, carry, st);
@@ -914,7 +944,9 @@ int bwd_channels_per_block(int64_t dstate) { return dstate <= 16 ? 4 * bwd_waves
 // buffers in the caller's workspace.
 struct BwdWs {
   int64_t S, nblkb, G, spp, nlb;  // segments, channel blocks, parts, segments per part, front blocks
+  bool h16;                       // the states of every chunk come from one sequential state-only pass
   size_t agg, sd, hin;            // checkpoint pass: segment end states, summed deltas, incoming states
+  size_t hin16;                   // h16: the state entering every 16-token chunk (over agg, sd, hin)
   size_t dap, ddp, dbp;           // per (part, row) partials of dA, dD and the bias gradient
   size_t dBp, dCp;                // per channel-block partials of dB and dC
   size_t cM, muin, cSD;           // parts: adjoint carries and summed deltas
@@ -953,9 +985,27 @@ BwdWs bwd_ws_layout(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, 
     off += up(bytes);
     return o;
   };
-  w.agg = take(ckpt ? 0 : (size_t)(nagg > 0 ? nagg : 0) * nstate * sizeof(float));
-  w.sd = take(ckpt ? 0 : (size_t)(nagg > 0 ? nagg : 0) * batch * dim * sizeof(float));
-  w.hin = take(ckpt ? 0 : (size_t)w.S * nstate * sizeof(float));
+  // Without checkpoints and with one part, when the sequential state-only
+  // scan has enough workgroups to fill the GPU on its own (the forward's
+  // plan keeps one segment), that scan writes the state entering every chunk
+  // and the adjoint kernel starts each chunk from it.  Otherwise (and under
+  // the exact hold or the convolution front, whose adjoint kernels recompute
+  // the chunk starts) 64-token segments are scanned side by side and folded.
+  // The two layouts share the region.
+  if (!ckpt && !conv && G == 1) {
+    const void* none[] = {nullptr};
+    w.h16 = make_plan(batch, dim, seqlen, dstate, 4, none, 1).segs == 1;
+  }
+  const size_t seg_bytes = ckpt ? 0
+                                : up((size_t)(nagg > 0 ? nagg : 0) * nstate * sizeof(float)) +
+                                      up((size_t)(nagg > 0 ? nagg : 0) * batch * dim * sizeof(float)) +
+                                      up((size_t)w.S * nstate * sizeof(float));
+  const size_t h16_bytes = w.h16 ? up((size_t)((seqlen + 15) / 16) * nstate * sizeof(float)) : 0;
+  const size_t base = take(seg_bytes > h16_bytes ? seg_bytes : h16_bytes);
+  w.agg = base;
+  w.sd = w.agg + up((size_t)(nagg > 0 ? nagg : 0) * nstate * sizeof(float));
+  w.hin = w.sd + up((size_t)(nagg > 0 ? nagg : 0) * batch * dim * sizeof(float));
+  w.hin16 = base;
   w.dap = take((size_t)w.G * nstate * sizeof(float));
   w.ddp = take((size_t)w.G * batch * dim * sizeof(float));
   w.dbp = take((size_t)w.G * batch * dim * sizeof(float));
@@ -1047,10 +1097,12 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
   if (!workspace || workspace_bytes < w.total) return S6_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return S6_ERR_ALIGN;
   const int64_t S = w.S, nagg = S - 1, nblkb = w.nblkb, G = w.G, spp = w.spp, nlb = w.nlb;
+  const bool h16 = w.h16 && !zoh;  // the exact hold's adjoint kernel recomputes the chunk starts
   char* wp = static_cast<char*>(workspace);
   float* agg = reinterpret_cast<float*>(wp + w.agg);
   float* sd = reinterpret_cast<float*>(wp + w.sd);
-  const float* hin = ckpt ? ckpt : reinterpret_cast<float*>(wp + w.hin);
+  float* hin16 = reinterpret_cast<float*>(wp + w.hin16);
+  const float* hin = ckpt ? ckpt : h16 ? hin16 : reinterpret_cast<float*>(wp + w.hin);
   float* dap = reinterpret_cast<float*>(wp + w.dap);
   float* ddp = reinterpret_cast<float*>(wp + w.ddp);
   float* dbp = reinterpret_cast<float*>(wp + w.dbp);  // bias gradient per part and row
@@ -1062,8 +1114,21 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
   float* dxo = conv ? reinterpret_cast<float*>(wp + w.dxo) : nullptr;
   float* cpart = reinterpret_cast<float*>(wp + w.cpart);
 
+  // the state entering every chunk: one sequential state-only scan from h0
+  if (h16) {
+    const void* vecptrs[] = {x, delta, Bm};
+    Plan p = make_plan(batch, dim, seqlen, dstate, esz, vecptrs, 3);
+    if (p.segs != 1) return S6_ERR_UNSUPPORTED;  // the layout's plan kept one segment
+    ScanArgs g;
+    memset(&g, 0, sizeof(g));
+    g.x = x; g.delta = delta; g.Bm = Bm; g.A = A;
+    g.hinit = h0; g.hinit_stride = 0; g.ckpt = hin16;
+    g.dbias = delta_bias; g.softplus = softplus;
+    g.D = dim; g.L = seqlen; g.N = dstate; g.seg_len = p.seg_len;
+    rc = launch_scan_any(in_dtype, kModeState, g, p, false, batch, 1, st);
+  }
   // pass 1: end state (from zero) and summed delta of every segment but the last
-  if (nagg > 0 && !ckpt) {
+  if (nagg > 0 && !ckpt && !h16) {
     const void* vecptrs[] = {x, delta, Bm};
     Plan p = make_plan(batch, dim, seqlen, dstate, esz, vecptrs, 3);
     ScanArgs g;
@@ -1076,7 +1141,7 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
     rc = launch_scan_any(in_dtype, kModeState, g, p, false, batch, nagg, st);
   }
   // the state entering every segment
-  if (rc == S6_OK && !ckpt) {
+  if (rc == S6_OK && !ckpt && !h16) {
     rc = launch_fold_carries(A, h0, agg, sd, const_cast<float*>(hin), nullptr, batch, dim, dstate, S, nagg, st);
   }
   if (rc == S6_OK) {
@@ -1093,7 +1158,8 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
     if (G > 1) {
       b.carry_M = cM;
       b.carry_SD = cSD;
-      rc = in_dtype == S6_BF16 ? launch_bwd<uint16_t>(b, gate, G, true, st) : launch_bwd<float>(b, gate, G, true, st);
+      rc = in_dtype == S6_BF16 ? launch_bwd<uint16_t>(b, gate, G, true, false, st)
+                               : launch_bwd<float>(b, gate, G, true, false, st);
       if (rc == S6_OK) {
         hipLaunchKernelGGL(s6_bwd_fold, dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0, st, A, dh_last, cM, cSD,
                            muin, batch, dim, dstate, G);
@@ -1103,7 +1169,8 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
       b.mu_in = muin;
     }
     if (rc == S6_OK)
-      rc = in_dtype == S6_BF16 ? launch_bwd<uint16_t>(b, gate, G, false, st) : launch_bwd<float>(b, gate, G, false, st);
+      rc = in_dtype == S6_BF16 ? launch_bwd<uint16_t>(b, gate, G, false, h16, st)
+                               : launch_bwd<float>(b, gate, G, false, h16, st);
   }
   if (rc == S6_OK) {
     const int64_t tot = batch * dstate * seqlen;

@@ -112,7 +112,7 @@ struct ScanArgs {
   const float* hinit;     // initial states or null (zero)
   float* y;               // kModeY output
   float* hout;            // final states or null
-  float* sumdelta;        // kModeState: per-segment sum of delta (S, batch, D) or null
+  float* sumdelta;        // kModeState without ckpt: per-segment sum of delta (S, batch, D) or null
   const float* dbias;     // (D) bias of the softplus step, or null (zero)
   int softplus;           // step = softplus(delta + dbias[d])  (option kernels only; the
                           // bias alone is added without it)
@@ -129,7 +129,9 @@ struct ScanArgs {
   int64_t hout_stride;    // elements between segments in hout
   int64_t hout_last_only; // 1: only the last segment writes hout (at offset 0)
   float* ckpt;            // kModeY: the state entering every kCkpt-token block,
-                          // (ceil(L / kCkpt), batch, D, N), or null
+                          // (ceil(L / kCkpt), batch, D, N); kModeState (plain and
+                          // step-bias kernels, one segment): the state entering
+                          // every kT-token chunk, (ceil(L / kT), batch, D, N); or null
 };
 
 struct Plan {

@@ -300,24 +300,40 @@ s6_scan_kernel(ScanArgs a) {
   // (The offsets are rebuilt from the thread index here, inside the rarely
   // taken branch: values kept from outside would hold registers through the
   // whole chunk loop.)
+  // (y kernels: every kCkpt tokens; state-only kernels: every chunk, the
+  // states the backward's adjoint kernel starts its chunks from)
+  // (y kernels: every kCkpt tokens; state-only kernels: every chunk, the
+  // states the backward's adjoint kernel starts its chunks from)
+  constexpr bool ck_chunk = MODE == kModeState;
+  constexpr int ck_shift = ck_chunk ? 4 : 6;  // log2 of kT, kCkpt
+  static_assert(kT == 16 && kCkpt == 64, "checkpoint strides");
+  // uniform: elements per checkpoint and this block's first one (a division
+  // here, not inside the chunk loop)
+  const int64_t ck_nst = (int64_t)(gridDim.x / nblk) * D * N;
+  const int64_t ck_off = (b * D + d0) * N;
   auto write_ckpt = [&](int64_t tok) {
-    const int64_t nst = (int64_t)(gridDim.x / nblk) * D * N;
-    float* base = a.ckpt + (tok / kCkpt) * nst + (b * D + d0) * N;  // uniform
+    float* base = a.ckpt + (tok >> ck_shift) * ck_nst + ck_off;  // uniform
     const int ln = (int)threadIdx.x & 63;
     const int c = ((ln >> 5) << 4) | (ln & 15);
     const int n0 = ((int)threadIdx.x >> 6) * 4 + 2 * ((ln >> 4) & 1);
     if (c < rows_valid) {
-      if (n0 < N) base[c * N + n0] = h[0];
-      if (n0 + 1 < N) base[c * N + n0 + 1] = h[1];
+      if ((N & 1) == 0 && n0 + 1 < N) {  // both states, 8-byte aligned
+        *reinterpret_cast<float2*>(base + c * N + n0) = make_float2(h[0], h[1]);
+      } else {
+        if (n0 < N) base[c * N + n0] = h[0];
+        if (n0 + 1 < N) base[c * N + n0 + 1] = h[1];
+      }
     }
   };
   // The plain and step-bias kernels write checkpoints only in their CK
   // instantiations (the write in the chunk loop costs registers); the
-  // exact-hold and convolution kernels check a.ckpt.
-  constexpr bool kCk = MODE == kModeY && (CK || EXT >= 2);
+  // exact-hold and convolution y kernels check a.ckpt.
+  constexpr bool kCk = CK || (MODE == kModeY && EXT >= 2);
   if (kCk && a.ckpt && tb < te) write_ckpt(tb);
   // Sum of delta over the segment (state mode), compensated (Neumaier):
   // dsum + dcomp.  (A double accumulator here costs dozens of registers.)
+  // The checkpoint-writing state kernels (one segment) write no sum.
+  constexpr bool kSum = MODE == kModeState && !CK;
   float dsum = 0.0f, dcomp = 0.0f;
 
   // This thread's pieces: slot s holds piece tid + s * NTHR of every chunk.
@@ -605,18 +621,18 @@ s6_scan_kernel(ScanArgs a) {
       token_group<MODE, EXT == 2>(dl, xv, A2, h, bc, zoh, ys);
       ysum[2 * g] = ys[0];
       ysum[2 * g + 1] = ys[1];
-      if constexpr (MODE == kModeState) cs += (dl[0] + dl[1]) + (dl[2] + dl[3]);
+      if constexpr (kSum) cs += (dl[0] + dl[1]) + (dl[2] + dl[3]);
     }
     // The chunk's state updates (and delta sum) complete here.  (Without
     // output terms nothing else ties them to the chunk, and the compiler would
     // sink them past the barriers, keeping every chunk's inputs live at once.)
     asm volatile("" : "+v"(h[0]), "+v"(h[1]), "+v"(cs));
-    if constexpr (kCk) {
+    if constexpr (kCk && MODE == kModeY) {
       // A block ends with this chunk: segments start at multiples of kCkpt
       // tokens, so with 4-chunk cycles only the cycle's last chunk can end one.
       if constexpr (2 * WIN != 4 || P == 3) {
         const int64_t tn = t0 + kT;  // tokens done after this chunk
-        if (a.ckpt && tn % kCkpt == 0 && tn < te) write_ckpt(tn);
+        if (a.ckpt && (tn & (kCkpt - 1)) == 0 && tn < te) write_ckpt(tn);
       }
     }
     float* pbuf = part + buf * (W * PART);
@@ -626,7 +642,7 @@ s6_scan_kernel(ScanArgs a) {
       *reinterpret_cast<float4*>(pp) = make_float4(ysum[0], ysum[1], ysum[2], ysum[3]);
       *reinterpret_cast<float4*>(pp + 4) = make_float4(ysum[4], ysum[5], ysum[6], ysum[7]);
     }
-    if constexpr (MODE == kModeState) {
+    if constexpr (kSum) {
       const float t = dsum + cs;
       dcomp += (fabsf(dsum) >= fabsf(cs)) ? (dsum - t) + cs : (cs - t) + dsum;
       dsum = t;
@@ -639,6 +655,12 @@ s6_scan_kernel(ScanArgs a) {
     else stage(buf ^ 1, k + 1, pre[SET][HALF], std::true_type{});
     __syncthreads();  // partial outputs of chunk k and the tiles of chunk k + 1 are complete
     if constexpr (HALF == WIN - 1) issue(tb + ((k + 1) / WIN + 2) * WT, pre[SET]);
+    if constexpr (kCk && ck_chunk) {
+      // the state after chunk k, stored after the window's loads are issued
+      // (as the y kernels store y)
+      const int64_t tn = t0 + kT;
+      if (a.ckpt && tn < te) write_ckpt(tn);
+    }
 
     if constexpr (MODE == kModeY) {
       float yo[TPL];
@@ -696,7 +718,7 @@ s6_scan_kernel(ScanArgs a) {
       if (n < N) a.hout[off + (b * D + d) * N + n] = h[j];
     }
   }
-  if constexpr (MODE == kModeState) {
+  if constexpr (kSum) {
     if (a.sumdelta && chv && w == 0 && r == 0)
       a.sumdelta[seg * (int64_t)(gridDim.x / nblk) * D + b * D + d] = dsum + dcomp;
   }
@@ -717,12 +739,12 @@ int launch_scan_t(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, 
   return S6_OK;
 }
 
-// The checkpoint-writing instantiation of a plain or step-bias fused kernel
-// when a.ckpt is set (the convolution and exact-hold kernels write them
-// whenever it is set).
+// The checkpoint-writing instantiation of a plain or step-bias kernel when
+// a.ckpt is set (the convolution and exact-hold y kernels write them
+// whenever it is set; their state-only kernels never do).
 template <typename In, int VEC, bool GATE, int MODE, int W, int EXT>
 int launch_scan_c(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, hipStream_t st) {
-  if constexpr (MODE == kModeY && EXT <= 1) {
+  if constexpr (EXT <= 1) {
     if (a.ckpt) return launch_scan_t<In, VEC, GATE, MODE, W, EXT, true>(a, batch, nblk, segs, st);
   }
   return launch_scan_t<In, VEC, GATE, MODE, W, EXT, false>(a, batch, nblk, segs, st);

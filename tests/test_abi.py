@@ -297,19 +297,24 @@ def test_workspace_size_queries(lib, codes):
     assert _size(lib.s6_scan_fwd_workspace_size, 1, 64, 4096, 40, 1)[0] == codes["S6_ERR_UNSUPPORTED"]
     assert _size(lib.s6_scan_fwd_workspace_size, 1, 64, 4096, 16, 9)[0] == codes["S6_ERR_DTYPE"]
     assert lib.s6_scan_fwd_workspace_size(1, 64, 4096, 16, 1, None) == codes["S6_ERR_NULL"]
-    # backward of the 3B layer (one part, 32 segments of 64 tokens): 31
-    # segment end states and summed deltas, 32 incoming states, the per-row
-    # partials of dA, dD and the bias gradient, and the per-16-channel-block
-    # dB/dC partials, which dominate
+    # backward of the 3B layer (one part; the sequential state-only scan
+    # fills the GPU): the state entering each of the 128 16-token chunks, the
+    # per-row partials of dA, dD and the bias gradient, and the
+    # per-16-channel-block dB/dC partials, which dominate
     rc, full = _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 2048, 16, 1, 0, 0)
     assert rc == ok
     st = 8 * 5120 * 16 * 4
     bc = (5120 // 16) * 8 * 16 * 2048 * 4
-    assert full == 31 * st + 31 * 8 * 5120 * 4 + 32 * st + st + 2 * 8 * 5120 * 4 + 2 * bc
+    rest = st + 2 * 8 * 5120 * 4 + 2 * bc
+    assert full == 128 * st + rest
     rc, ck = _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 2048, 16, 1, 0, 1)
-    assert rc == ok and ck == full - (31 * st + 31 * 8 * 5120 * 4 + 32 * st)
+    assert rc == ok and ck == rest
+    # with the convolution front: 64-token segments scanned side by side (31
+    # end states and summed deltas, 32 incoming states), the gradient of the
+    # filtered input and the filter/bias partials
     rc, conv = _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 2048, 16, 1, 4, 0)
-    assert rc == ok and conv == full + 8 * 5120 * 2048 * 4 + 8 * 1 * 5120 * 5 * 4
+    seg = 31 * st + 31 * 8 * 5120 * 4 + 32 * st
+    assert rc == ok and conv == seg + rest + 8 * 5120 * 2048 * 4 + 8 * 1 * 5120 * 5 * 4
     assert _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 2048, 16, 1, 5, 0)[0] == codes["S6_ERR_UNSUPPORTED"]
     assert _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 0, 16, 1, 0, 0) == (ok, 0)
 

@@ -114,6 +114,42 @@ def test_backward_small(torch_cuda, oracle, shape):
     _check_bwd(oracle, w)
 
 
+# Shapes whose sequential state-only scan fills the GPU (batch x ceil(dim/32)
+# workgroups above half its slots): the backward then takes the state
+# entering every 16-token chunk from that scan instead of recomputing the
+# chunk starts.  Short rows keep the oracle fast.
+CHUNK_STATE_SHAPES = [
+    (8, 2592, 16, 100, synth.BF16, True),   # 648 workgroups; ragged last segment
+    (2, 4128, 24, 70, synth.F32, True),     # two states per lane (8 waves): 258 workgroups
+    (4, 20512, 4, 40, synth.F32, False),    # one wave per workgroup: 2564 workgroups
+]
+
+
+def _chunk_state_layout(w):
+    """True when the backward's workspace holds one state per 16-token chunk
+    (the layout of the sequential state-only scan)."""
+    from selective_state_space_63_amd import s6
+    import torch
+    dt = torch.float32 if w.dtype == synth.F32 else torch.bfloat16
+    full = s6.workspace_size("scan_bwd", w.batch, w.dim, w.seqlen, w.dstate, dt)
+    rest = s6.workspace_size("scan_bwd", w.batch, w.dim, w.seqlen, w.dstate, dt, from_ckpt=True)
+    chunks = -(-w.seqlen // 16) * w.batch * w.dim * w.dstate * 4
+    return full - rest == (chunks + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("mode", [None, "softplus", "zoh"])
+@pytest.mark.parametrize("shape", CHUNK_STATE_SHAPES, ids=lambda s: "b{}_d{}_n{}_l{}_{}_{}".format(*s))
+def test_backward_chunk_states(torch_cuda, oracle, shape, mode):
+    """The backward whose chunk-start states come from one sequential
+    state-only scan (plain and step-bias levels; the exact hold keeps the
+    recomputed chunk starts in the same workspace layout)."""
+    b, dm, n, L, dt, gate = shape
+    w = synth.custom(b, dm, n, L, dt, gate, seed=4700 + L + dm)
+    assert _chunk_state_layout(w), "the shape should take the sequential state-only scan"
+    _say(f"[case] backward chunk states {mode} {w.name}")
+    _check_bwd(oracle, w, mode=mode)
+
+
 @pytest.mark.parametrize("mode", ["bias", "softplus", "zoh", "softplus_zoh"])
 @pytest.mark.parametrize("shape", [(1, 16, 4, 256, synth.F32, False), (2, 65, 16, 100, synth.BF16, True),
                                    (1, 32, 16, 5000, synth.BF16, True), (2, 40, 32, 48, synth.BF16, True),
