@@ -707,26 +707,29 @@ __global__ void s6_bwd_fold(const float* __restrict__ A, const float* __restrict
   }
 }
 
-// dB and dC: sums of the per-block partials over the channel blocks.  Four
-// running sums (blocks k = 4m + j go to sum j), added at the end in a fixed
-// order: the loads of four blocks are in flight at once, and the result does
-// not depend on the launch shape.
-__global__ void s6_bwd_reduce_bc(const float* __restrict__ part, float* __restrict__ out, int64_t nblk,
+// dB and dC (blockIdx.y = 0, 1): sums of the per-block partials over the
+// channel blocks.  Eight running sums (blocks k = 8m + j go to sum j), added
+// at the end in a fixed order: the loads of eight blocks are in flight at
+// once, and the result does not depend on the launch shape.
+__global__ void s6_bwd_reduce_bc(const float* __restrict__ part_b, const float* __restrict__ part_c,
+                                 float* __restrict__ out_b, float* __restrict__ out_c, int64_t nblk,
                                  int64_t total) {
+  const float* part = blockIdx.y ? part_c : part_b;
+  float* out = blockIdx.y ? out_c : out_b;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    float sm[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sm[j] = 0.0f;
     int64_t k = 0;
-    for (; k + 4 <= nblk; k += 4) {
-      s0 += part[k * total + i];
-      s1 += part[(k + 1) * total + i];
-      s2 += part[(k + 2) * total + i];
-      s3 += part[(k + 3) * total + i];
+    for (; k + 8 <= nblk; k += 8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sm[j] += part[(k + j) * total + i];
     }
-    if (k < nblk) s0 += part[k * total + i];
-    if (k + 1 < nblk) s1 += part[(k + 1) * total + i];
-    if (k + 2 < nblk) s2 += part[(k + 2) * total + i];
-    out[i] = (s0 + s1) + (s2 + s3);
+#pragma unroll
+    for (int j = 0; j < 7; ++j)
+      if (k + j < nblk) sm[j] += part[(k + j) * total + i];
+    out[i] = ((sm[0] + sm[1]) + (sm[2] + sm[3])) + ((sm[4] + sm[5]) + (sm[6] + sm[7]));
   }
 }
 
@@ -1176,8 +1179,8 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
     const int64_t tot = batch * dstate * seqlen;
     int64_t blocks = (tot + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3((unsigned)blocks), dim3(256), 0, st, dBp, dBm, nblkb, tot);
-    hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3((unsigned)blocks), dim3(256), 0, st, dcp, dCm, nblkb, tot);
+    hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3((unsigned)blocks, 2u), dim3(256), 0, st, dBp, dcp, dBm, dCm, nblkb,
+                       tot);
     const int64_t rows = dim * dstate;
     hipLaunchKernelGGL(s6_bwd_reduce_rows, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, dap, ddp, dbp,
                        dA, dDskip, ddelta_bias, G * batch, dim, dstate);
