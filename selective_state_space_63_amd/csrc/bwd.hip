@@ -289,7 +289,7 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>())
     // states at the four chunk starts of the segment (chunks past the end of
     // the sequence: 0, their tokens are staged as delta = 0 and change nothing)
     float hc[4][SPL];
-    if constexpr (H16) {
+    auto load_hc16 = [&]() {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int64_t q = s * (KS / 16) + k;
@@ -299,8 +299,11 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>())
           hc[k][j] = (sv[j] && q * 16 < L) ? a.hin[q * nstate + (b * D + d) * N + n] : 0.0f;
         }
       }
-    } else if constexpr (OPT < 2) {
-      load_hseg();
+    };
+    // (the kernels held to 128 VGPRs load them after the staging)
+    if constexpr (OPT < 2) {
+      if constexpr (H16) load_hc16();
+      else load_hseg();
     }
     __syncthreads();  // the previous segment's reads of the staged inputs are done
     for (int i = tid; i < CW * KS; i += NTHR) {
@@ -393,6 +396,7 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>())
       __syncthreads();
     }
 
+    if constexpr (H16 && OPT >= 2) load_hc16();
     // states at the four chunk starts, recomputed from the segment's first
     if constexpr (!H16) {
       if constexpr (OPT >= 2) load_hseg();
@@ -920,16 +924,23 @@ int launch_bwd_g(const BwdArgs& a, bool gate, int64_t parts, bool carry, hipStre
               : launch_bwd_t<In, false, SPL, OPT, H16>(a, parts, carry, st);
 }
 
-// h16: a.hin holds the state entering every chunk (plain and step-bias
-// levels only; one part).
+// h16: a.hin holds the state entering every chunk (one part).
+template <typename In, int SPL>
+int launch_bwd_h16(const BwdArgs& a, bool gate, int opt, hipStream_t st) {
+  switch (opt) {
+    case 0: return launch_bwd_g<In, SPL, 0, true>(a, gate, 1, false, st);
+    case 1: return launch_bwd_g<In, SPL, 1, true>(a, gate, 1, false, st);
+    case 2: return launch_bwd_g<In, SPL, 2, true>(a, gate, 1, false, st);
+    default: return launch_bwd_g<In, SPL, 3, true>(a, gate, 1, false, st);
+  }
+}
+
 template <typename In>
 int launch_bwd(const BwdArgs& a, bool gate, int64_t parts, bool carry, bool h16, hipStream_t st) {
   const int opt = a.conv_w ? 3 : a.zoh ? 2 : (a.dbias || a.softplus || a.ddbias_part) ? 1 : 0;
   if (h16) {
-    if (opt > 1 || parts != 1 || carry) return S6_ERR_UNSUPPORTED;
-    if (a.N <= 16)
-      return opt ? launch_bwd_g<In, 1, 1, true>(a, gate, 1, false, st) : launch_bwd_g<In, 1, 0, true>(a, gate, 1, false, st);
-    return opt ? launch_bwd_g<In, 2, 1, true>(a, gate, 1, false, st) : launch_bwd_g<In, 2, 0, true>(a, gate, 1, false, st);
+    if (parts != 1 || carry) return S6_ERR_UNSUPPORTED;
+    return a.N <= 16 ? launch_bwd_h16<In, 1>(a, gate, opt, st) : launch_bwd_h16<In, 2>(a, gate, opt, st);
   }
   if (a.N <= 16) {
     if (opt == 3) return launch_bwd_g<In, 1, 3>(a, gate, parts, carry, st);
@@ -991,11 +1002,10 @@ BwdWs bwd_ws_layout(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, 
   // Without checkpoints and with one part, when the sequential state-only
   // scan has enough workgroups to fill the GPU on its own (the forward's
   // plan keeps one segment), that scan writes the state entering every chunk
-  // and the adjoint kernel starts each chunk from it.  Otherwise (and under
-  // the exact hold or the convolution front, whose adjoint kernels recompute
-  // the chunk starts) 64-token segments are scanned side by side and folded.
-  // The two layouts share the region.
-  if (!ckpt && !conv && G == 1) {
+  // and the adjoint kernel starts each chunk from it.  Otherwise 64-token
+  // segments are scanned side by side and folded.  The two layouts share the
+  // region.
+  if (!ckpt && G == 1) {
     const void* none[] = {nullptr};
     w.h16 = make_plan(batch, dim, seqlen, dstate, 4, none, 1).segs == 1;
   }
@@ -1100,7 +1110,7 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
   if (!workspace || workspace_bytes < w.total) return S6_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return S6_ERR_ALIGN;
   const int64_t S = w.S, nagg = S - 1, nblkb = w.nblkb, G = w.G, spp = w.spp, nlb = w.nlb;
-  const bool h16 = w.h16 && !zoh;  // the exact hold's adjoint kernel recomputes the chunk starts
+  const bool h16 = w.h16;
   char* wp = static_cast<char*>(workspace);
   float* agg = reinterpret_cast<float*>(wp + w.agg);
   float* sd = reinterpret_cast<float*>(wp + w.sd);
@@ -1126,7 +1136,8 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
     memset(&g, 0, sizeof(g));
     g.x = x; g.delta = delta; g.Bm = Bm; g.A = A;
     g.hinit = h0; g.hinit_stride = 0; g.ckpt = hin16;
-    g.dbias = delta_bias; g.softplus = softplus;
+    g.dbias = delta_bias; g.softplus = softplus; g.zoh = zoh;
+    g.conv_w = cg.w; g.conv_b = cg.bias; g.conv_state = cg.state; g.conv_k = cg.width;
     g.D = dim; g.L = seqlen; g.N = dstate; g.seg_len = p.seg_len;
     rc = launch_scan_any(in_dtype, kModeState, g, p, false, batch, 1, st);
   }

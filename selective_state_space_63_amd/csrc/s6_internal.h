@@ -129,9 +129,9 @@ struct ScanArgs {
   int64_t hout_stride;    // elements between segments in hout
   int64_t hout_last_only; // 1: only the last segment writes hout (at offset 0)
   float* ckpt;            // kModeY: the state entering every kCkpt-token block,
-                          // (ceil(L / kCkpt), batch, D, N); kModeState (plain and
-                          // step-bias kernels, one segment): the state entering
-                          // every kT-token chunk, (ceil(L / kT), batch, D, N); or null
+                          // (ceil(L / kCkpt), batch, D, N); kModeState (one
+                          // segment): the state entering every kT-token chunk,
+                          // (ceil(L / kT), batch, D, N); or null
 };
 
 struct Plan {

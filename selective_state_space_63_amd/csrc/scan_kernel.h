@@ -739,12 +739,12 @@ int launch_scan_t(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, 
   return S6_OK;
 }
 
-// The checkpoint-writing instantiation of a plain or step-bias kernel when
-// a.ckpt is set (the convolution and exact-hold y kernels write them
-// whenever it is set; their state-only kernels never do).
+// The checkpoint-writing instantiation when a.ckpt is set: of the plain and
+// step-bias y kernels and of every state-only kernel (the convolution and
+// exact-hold y kernels write them whenever it is set).
 template <typename In, int VEC, bool GATE, int MODE, int W, int EXT>
 int launch_scan_c(const ScanArgs& a, int64_t batch, int64_t nblk, int64_t segs, hipStream_t st) {
-  if constexpr (EXT <= 1) {
+  if constexpr (EXT <= 1 || MODE == kModeState) {
     if (a.ckpt) return launch_scan_t<In, VEC, GATE, MODE, W, EXT, true>(a, batch, nblk, segs, st);
   }
   return launch_scan_t<In, VEC, GATE, MODE, W, EXT, false>(a, batch, nblk, segs, st);

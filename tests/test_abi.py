@@ -309,12 +309,18 @@ def test_workspace_size_queries(lib, codes):
     assert full == 128 * st + rest
     rc, ck = _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 2048, 16, 1, 0, 1)
     assert rc == ok and ck == rest
-    # with the convolution front: 64-token segments scanned side by side (31
-    # end states and summed deltas, 32 incoming states), the gradient of the
-    # filtered input and the filter/bias partials
+    # with the convolution front: also the gradient of the filtered input and
+    # the filter/bias partials
     rc, conv = _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 2048, 16, 1, 4, 0)
-    seg = 31 * st + 31 * 8 * 5120 * 4 + 32 * st
-    assert rc == ok and conv == seg + rest + 8 * 5120 * 2048 * 4 + 8 * 1 * 5120 * 5 * 4
+    assert rc == ok and conv == full + 8 * 5120 * 2048 * 4 + 8 * 1 * 5120 * 5 * 4
+    # a long row (batch 1, 1536 channels, 65536 tokens: the work runs in parts):
+    # the 64-token segments' 1023 end states and summed deltas and 1024
+    # incoming states stay
+    rc, lng = _size(lib.s6_scan_bwd_workspace_size, 1, 1536, 65536, 16, 1, 0, 0)
+    rc2, lck = _size(lib.s6_scan_bwd_workspace_size, 1, 1536, 65536, 16, 1, 0, 1)
+    st1 = 1536 * 16 * 4
+    seg = (1023 * st1 + 255) // 256 * 256 + (1023 * 1536 * 4 + 255) // 256 * 256 + 1024 * st1
+    assert rc == ok and rc2 == ok and lng - lck == seg
     assert _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 2048, 16, 1, 5, 0)[0] == codes["S6_ERR_UNSUPPORTED"]
     assert _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 0, 16, 1, 0, 0) == (ok, 0)
 

@@ -264,6 +264,25 @@ def test_conv_backward(torch_cuda, oracle, shape, K):
     _check_conv_bwd(oracle, w, K, with_state=(K != 3))
 
 
+@pytest.mark.parametrize("softplus", [False, True])
+@pytest.mark.parametrize("shape", [(8, 2592, 16, 100, synth.BF16, True), (2, 4128, 24, 70, synth.F32, True)],
+                         ids=lambda s: "b{}_d{}_n{}_l{}_{}_{}".format(*s))
+def test_conv_backward_chunk_states(torch_cuda, oracle, shape, softplus):
+    """Shapes whose sequential state-only scan fills the GPU: the first pass
+    (through the front) stores the state entering every 16-token chunk and
+    the adjoint kernel starts its chunks from those."""
+    from selective_state_space_63_amd import s6
+    import torch
+    b, dm, n, L, dt, gate = shape
+    w = synth.custom(b, dm, n, L, dt, gate, seed=4680 + L + dm)
+    tdt = torch.float32 if dt == synth.F32 else torch.bfloat16
+    full = s6.workspace_size("scan_bwd", b, dm, L, n, tdt, conv_width=4)
+    chunks = (-(-L // 16) * b * dm * n * 4 + 255) // 256 * 256
+    assert full - s6.workspace_size("scan_bwd", b, dm, L, n, tdt, conv_width=4, from_ckpt=True) == chunks
+    _say(f"[case] conv backward chunk states softplus={softplus} {w.name}")
+    _check_conv_bwd(oracle, w, 4, softplus=softplus)
+
+
 @pytest.mark.parametrize("shape", [(2, 65, 16, 100, synth.BF16, True), (3, 33, 16, 129, synth.F32, True)],
                          ids=lambda s: "b{}_d{}_n{}_l{}_{}_{}".format(*s))
 def test_conv_backward_softplus(torch_cuda, oracle, shape):
