@@ -135,12 +135,13 @@ def test_segmented_scan_graph_replays(torch_cuda):
     _replay_check(torch, g, (y, hl, hs), refs)
 
 
-@pytest.mark.parametrize("shape", [(2, 256, 1024), (1, 64, 8192)], ids=["rows", "parts"])
+@pytest.mark.parametrize("shape", [(2, 256, 1024), (1, 64, 8192), (8, 2592, 256)], ids=["rows", "parts", "chunks"])
 def test_backward_graph_replays(torch_cuda, shape):
     """The backward (checkpoint pass, adjoint kernel, fixed-order reductions;
-    with few long rows also the carry pass and fold over parts) captured with
-    its workspace and replayed: every gradient equal to the eager call bit
-    for bit."""
+    with few long rows also the carry pass and fold over parts; with rows
+    enough to fill the GPU the sequential first pass that stores every
+    chunk's state) captured with its workspace and replayed: every gradient
+    equal to the eager call bit for bit."""
     import torch
     from selective_state_space_63_amd import s6
     bsz, dim, L = shape
