@@ -119,10 +119,10 @@ int s6_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int 
 /* s6_scan_fwd for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation):
  * no workspace argument; when the sequence is cut into segments, their
- * carries go to a static device buffer of the library (8 MiB, one per GPU,
+ * carries go to a static device buffer of the library (16 MiB, one per GPU,
  * held until the process ends; its address is looked up once per device on
  * the first call there).  No hipMalloc, hipFree or allocating library call.
- * A call that would need more than 8 MiB returns S6_ERR_WORKSPACE before any
+ * A call that would need more than 16 MiB returns S6_ERR_WORKSPACE before any
  * work is enqueued (on a 256-CU device a segmented forward needs at most
  * about 6 MB, whatever the sequence length).  Every call on one GPU shares
  * that buffer and leaves its contents behind (nothing in it needs to start

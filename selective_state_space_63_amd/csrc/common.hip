@@ -73,7 +73,7 @@ const char* s6_status_str(int status) {
     case S6_ERR_FLAGS: return "unknown option bits in flags";
     case S6_ERR_WORKSPACE:
       return "the call needs a workspace: none given, or smaller than its *_workspace_size (s6_scan_fwd_noalloc: "
-             "more than its 8 MiB static scratch)";
+             "more than its 16 MiB static scratch)";
     case S6_ERR_HIP: return g_err[0] ? g_err : "HIP error";
     default: return "unknown status";
   }

@@ -13,7 +13,7 @@ namespace s6i {
 // its own copy for the life of the process.  In host code `scratch` is only a
 // stand-in for the symbol; its device address comes from hipGetSymbolAddress
 // (scratch_ptr), once per device.
-constexpr size_t kScratchBytes = (size_t)8 << 20;
+constexpr size_t kScratchBytes = (size_t)16 << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
@@ -68,7 +68,11 @@ Plan make_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, size_
   const int64_t slots = (int64_t)cu_count() * (p.W == 8 ? 2 : 20 / p.W);
   int64_t segs = 1;
   if (2 * wgs <= slots) {
-    segs = slots / wgs;
+    // twice as many segments as the workgroup slots hold at once (two rounds
+    // of workgroups): measured faster than one round, 12.1 against 13.1 ms
+    // on a million tokens of 1536 channels and 61 against 62.5 us on 2 x
+    // 1536 channels x 2048 tokens
+    segs = 2 * slots / wgs;
     const int64_t max_segs = (seqlen + 4 * kT - 1) / (4 * kT);
     if (segs > max_segs) segs = max_segs;
     if (segs < 1) segs = 1;

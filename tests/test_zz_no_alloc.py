@@ -40,7 +40,7 @@ def test_noalloc_matches_workspace_entry(torch_cuda, oracle, order):
     # (batch, dim, dstate, seqlen): both cut into segments; the second needs less scratch
     shapes = [(1, 1536, 16, 65536), (1, 96, 16, 8192)]
     sizes = [s6.workspace_size("scan_fwd", b, d, L, n) for b, d, n, L in shapes]
-    assert sizes[0] > sizes[1] > 0 and sizes[0] <= (8 << 20)
+    assert sizes[0] > sizes[1] > 0 and sizes[0] <= (16 << 20)
     for i, (b, d, n, L) in enumerate(shapes):
         w = synth.custom(b, d, n, L, synth.BF16, True, seed=6100 + i)
         print(f"[case] noalloc call {i}: {w.name} (scratch {sizes[i]} bytes)", flush=True)
