@@ -7,13 +7,15 @@ namespace s6i {
 namespace {
 
 // Reverse-mode gradients of the scan for the loss <dy, y> + <dh_last, h_last>
-// (plain step).  The states are recomputed, never stored per token: a
-// state-only pass and the carry fold give the state entering every segment of
-// kBwdSeg tokens (the same kernels as a segmented forward scan); this kernel
-// then walks the segments of a (batch row, 16-channel block) from the last to
-// the first.  Per segment it stages the inputs in LDS, recomputes the states
-// at the four chunk starts, and per 16-token chunk (last first) recomputes
-// the chunk's states and transitions in registers and runs the adjoint
+// (plain step).  The states are recomputed, never stored per token.  A first
+// pass gives either the state entering every 16-token chunk (one sequential
+// state-only scan, when its workgroups fill the GPU) or that entering every
+// segment of kBwdSeg tokens (segments scanned side by side from zero and
+// folded, the kernels of a segmented forward scan); this kernel then walks
+// the segments of a (batch row, 16-channel block) from the last to the first.
+// Per segment it stages the inputs in LDS, loads or recomputes the states at
+// the four chunk starts, and per 16-token chunk (last first) recomputes the
+// chunk's states and transitions in registers and runs the adjoint
 // lambda_t = dyc_t C_t + a_{t+1} lambda_{t+1} backwards through it.
 //
 // Lane l of wave w: channel c = 4w + (l >> 4) of the block, states
