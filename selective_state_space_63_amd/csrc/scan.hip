@@ -34,11 +34,21 @@ __global__ void s6_fold_carries(const float* __restrict__ A, const float* __rest
   const int64_t d = bd % D;
   const float A2 = A[d * N + n] * kLog2e;
   float H = h0 ? h0[i] : 0.0f;
-  for (int64_t s = 0; s < S; ++s) {
-    if (hin) hin[s * total + i] = H;
-    if (s < nagg) {
-      const float P = fast_exp2(A2 * sumdelta[s * batch * D + bd]);
-      H = __builtin_fmaf(P, H, agg[s * total + i]);
+  // Eight segments at a time: their loads are issued before the dependent
+  // chain through H (one load latency per eight steps, not per step); the
+  // last batch's loads past nagg reread aggregate nagg - 1 and are not used.
+  for (int64_t s = 0; s < S; s += 8) {
+    float ag[8], sd[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t sj = nagg > 0 ? (s + j < nagg ? s + j : nagg - 1) : 0;
+      ag[j] = nagg > 0 ? agg[sj * total + i] : 0.0f;
+      sd[j] = nagg > 0 ? sumdelta[sj * batch * D + bd] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s + j < S && hin) hin[(s + j) * total + i] = H;
+      if (s + j < nagg) H = __builtin_fmaf(fast_exp2(A2 * sd[j]), H, ag[j]);
     }
   }
   if (hlast) hlast[i] = H;
