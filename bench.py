@@ -964,6 +964,12 @@ def main():
             out["ssd"]["cpu_baseline"] = cpu_ssd_baseline(ws, inp_ssd)
         del inp_ssd
         torch.cuda.empty_cache()
+        print(f"[bench] scalar-A matrix-form scan {wl.name}", file=sys.stderr, flush=True)
+        _, out["ssd_long"] = bench_ssd(wl, 5, 2)
+        out["ssd_long"]["note"] = ("s6_ssd_scan_fwd on the million-token sequence with one A value per channel: "
+                                   "cut into segments (state-only pass, carry fold, the scan from the folded "
+                                   "states); mfma counts the scan pass only")
+        torch.cuda.empty_cache()
         print(f"[bench] scan {w.name} with the convolution front", file=sys.stderr, flush=True)
         _, tcv, _ = bench_scan(w, 50, 50, conv_k=4)
         out["conv"] = scan_line("conv", w, tcv, in_bytes, "convolution front (width 4, bias, SiLU) fused into the "

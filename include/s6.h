@@ -348,14 +348,17 @@ int s6_scan_bwd_ckpt(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
  *   y[b,d,t] = (sum_n Cm[b,n,t] * h[n] + Dskip[d] * x[b,d,t]) * SiLU(z[b,d,t])
  * evaluated per 16-token chunk as products with the Gram matrix of B and C
  * (shared by every channel of a batch row) and two exponentials per token
- * and channel.  With bf16 inputs the fp32 operands enter the bf16 matrix
- * cores as two bf16 parts each (about 2^-16 relative per product); with
- * fp32 inputs the products are fp32.
+ * and channel.  Products of inputs only (B, C and the Gram matrix of bf16
+ * inputs) run on the bf16 matrix cores, exactly; products with an fp32
+ * operand (the scaled inputs, the state) on the fp32 matrix cores.
  *   A : (dim) fp32, one value per channel (accuracy specified for A <= 0).
  *   dstate : 1..16 (else S6_ERR_UNSUPPORTED).
  *   Everything else (layouts, nullable Dskip, z, h0, h_last; errors; stream)
- *   as for s6_scan_fwd.  workspace: s6_ssd_scan_fwd_workspace_size bytes
- *   (currently 0 for every size: one pass over the sequence). */
+ *   as for s6_scan_fwd.  workspace: s6_ssd_scan_fwd_workspace_size bytes:
+ *   0 when the batch x ceil(dim/16) waves fill the GPU; for few long rows
+ *   the sequence is cut into segments (a state-only pass, the carry fold,
+ *   the scan of every segment from its incoming state) and the workspace
+ *   holds the segments' end states, summed steps and incoming states. */
 int s6_ssd_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int in_dtype,
                     const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
                     const float* Dskip, const void* z, const float* h0, float* y, float* h_last,

@@ -182,7 +182,7 @@ int launch_scan_hold(int in_dtype, int mode, const ScanArgs& a, const Plan& p, b
 // segment s, hlast (nullable) the state after the last of `nagg` aggregates.
 int launch_fold_carries(const float* A, const float* h0, const float* agg, const float* sumdelta, float* hin,
                         float* hlast, int64_t batch, int64_t D, int64_t N, int64_t S, int64_t nagg,
-                        hipStream_t st);
+                        hipStream_t st, bool a_per_channel = false);
 
 // dst[i] = src ? src[i] : 0 for i < n.
 int launch_copy_state(const float* src, float* dst, int64_t n, hipStream_t st);

@@ -21,18 +21,19 @@ namespace {
 // Fold segment aggregates into every segment's incoming state:
 // H_0 = h0 (or 0); H_{s+1} = exp(A * sum_delta_s) * H_s + S_s.
 // hin (S, batch*D*N) receives H_s for s < S; hlast (nullable) gets the state
-// after the last of the `nagg` aggregates.
+// after the last of the `nagg` aggregates.  A is (D, N), or (D) with one value
+// per channel when a_per_channel is set.
 __global__ void s6_fold_carries(const float* __restrict__ A, const float* __restrict__ h0,
                                 const float* __restrict__ agg, const float* __restrict__ sumdelta,
                                 float* __restrict__ hin, float* __restrict__ hlast, int64_t batch,
-                                int64_t D, int64_t N, int64_t S, int64_t nagg) {
+                                int64_t D, int64_t N, int64_t S, int64_t nagg, int a_per_channel) {
   const int64_t total = batch * D * N;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
   const int64_t n = i % N;
   const int64_t bd = i / N;
   const int64_t d = bd % D;
-  const float A2 = A[d * N + n] * kLog2e;
+  const float A2 = A[a_per_channel ? d : d * N + n] * kLog2e;
   float H = h0 ? h0[i] : 0.0f;
   // Eight segments at a time: their loads are issued before the dependent
   // chain through H (one load latency per eight steps, not per step); the
@@ -126,10 +127,10 @@ int launch_scan_any(int in_dtype, int mode, const ScanArgs& a, const Plan& p, bo
 
 int launch_fold_carries(const float* A, const float* h0, const float* agg, const float* sumdelta, float* hin,
                         float* hlast, int64_t batch, int64_t D, int64_t N, int64_t S, int64_t nagg,
-                        hipStream_t st) {
+                        hipStream_t st, bool a_per_channel) {
   const int64_t blocks = (batch * D * N + 255) / 256;
   hipLaunchKernelGGL(s6_fold_carries, dim3((unsigned)blocks), dim3(256), 0, st, A, h0, agg, sumdelta, hin, hlast,
-                     batch, D, N, S, nagg);
+                     batch, D, N, S, nagg, a_per_channel ? 1 : 0);
   S6_HIP(hipGetLastError(), "s6_fold_carries launch");
   return S6_OK;
 }
@@ -271,7 +272,7 @@ int scan_impl(bool want_y, int64_t batch, int64_t dim, int64_t seqlen, int64_t d
   if (rc == S6_OK) {
     const int64_t blocks = (nstate + 255) / 256;
     hipLaunchKernelGGL(s6_fold_carries, dim3((unsigned)blocks), dim3(256), 0, st, A, h0, agg, sd,
-                       want_y ? hin : nullptr, want_y ? nullptr : h_last, batch, dim, dstate, S, nagg);
+                       want_y ? hin : nullptr, want_y ? nullptr : h_last, batch, dim, dstate, S, nagg, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) rc = hip_fail(e, "s6_fold_carries launch");
   }

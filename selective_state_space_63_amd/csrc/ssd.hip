@@ -157,6 +157,26 @@ struct Front {
   bool wide;     // a channel of the tile has |a| c_16 > kRangeLog2 (wave-uniform)
 };
 
+// Cumulative step of a chunk: lane (g, c) holds tokens 4g .. 4g+3 of channel
+// c in dv; cs receives the inclusive cumulative step of those tokens within
+// the chunk and total the chunk's sum (lanes c, c+16, c+32, c+48 hold the
+// chunk's 4 groups).
+__device__ __forceinline__ void chunk_cumsum(const float dv[4], int g, float cs[4], float& total) {
+  float q[4];
+  q[0] = dv[0];
+  q[1] = q[0] + dv[1];
+  q[2] = q[1] + dv[2];
+  q[3] = q[2] + dv[3];
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(q[3]), __float_as_uint(q[3]), false, false);
+  const float lo16 = __uint_as_float((unsigned)s16[0]), hi16 = __uint_as_float((unsigned)s16[1]);
+  const float pair = lo16 + hi16;
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+  const float lo32 = __uint_as_float((unsigned)s32[0]), hi32 = __uint_as_float((unsigned)s32[1]);
+  total = lo32 + hi32;
+  const float ex = ((g & 1) ? lo16 : 0.0f) + ((g & 2) ? lo32 : 0.0f);
+  for (int j = 0; j < 4; ++j) cs[j] = ex + q[j];
+}
+
 struct SsdArgs {
   const void* x;
   const void* delta;
@@ -169,6 +189,14 @@ struct SsdArgs {
   float* y;
   float* h_last;       // nullable
   int64_t D, L, N;
+  // Segments along L (blockIdx.y), seg_len tokens each (a multiple of 32):
+  // the state entering segment s is hin[s] ((S, batch, D, N)), or h0 when
+  // hin is null (one segment).  State-only pass: agg[s] receives segment s's
+  // end state from a zero state, sumdelta[s] (S, batch, D) its summed step.
+  int64_t seg_len;
+  const float* hin;
+  float* agg;
+  float* sumdelta;
 };
 
 // Staging of 2-chunk groups through LDS (STG): per input one or two 16-byte
@@ -228,11 +256,18 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
     }
     ident.pack(v);
   }
+  // this wave's segment of the sequence: tokens [tb, te)
+  const int64_t seg = blockIdx.y;
+  const int64_t tb = seg * a.seg_len;
+  const int64_t te = tb + a.seg_len < L ? tb + a.seg_len : L;
   // state tile: lane (g, c) holds H[n = 4g + r][d = c]
   float H[4];
-  for (int r = 0; r < 4; ++r) {
-    const int n = 4 * g + r;
-    H[r] = (a.h0 && dval && n < N) ? a.h0[(b * D + d0 + c) * N + n] : 0.0f;
+  {
+    const float* h_in = a.hin ? a.hin + seg * batch * D * N : a.h0;
+    for (int r = 0; r < 4; ++r) {
+      const int n = 4 * g + r;
+      H[r] = (h_in && dval && n < N) ? h_in[(b * D + d0 + c) * N + n] : 0.0f;
+    }
   }
 
   auto issue = [&](Raw<In>& rw, int64_t k) {
@@ -268,21 +303,7 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
       rw.b.pack(bv);
       rw.c.pack(cv);
     }
-    // the lane's 4 tokens, then the groups before it (lanes c, c+16, c+32,
-    // c+48 hold the chunk's 4 groups)
-    float q[4];
-    q[0] = dv[0];
-    q[1] = q[0] + dv[1];
-    q[2] = q[1] + dv[2];
-    q[3] = q[2] + dv[3];
-    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(q[3]), __float_as_uint(q[3]), false, false);
-    const float lo16 = __uint_as_float((unsigned)s16[0]), hi16 = __uint_as_float((unsigned)s16[1]);
-    const float pair = lo16 + hi16;
-    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
-    const float lo32 = __uint_as_float((unsigned)s32[0]), hi32 = __uint_as_float((unsigned)s32[1]);
-    total = lo32 + hi32;
-    const float ex = ((g & 1) ? lo16 : 0.0f) + ((g & 2) ? lo32 : 0.0f);
-    for (int j = 0; j < 4; ++j) cs[j] = ex + q[j];
+    chunk_cumsum(dv, g, cs, total);
   };
 
   // B and C token-major (an MFMA with the identity) and G^T = Bmat Cmat^T:
@@ -420,8 +441,8 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
     }
   };
 
-  const int64_t nch = (L + kQ - 1) / kQ;
-  int64_t k = 0;
+  const int64_t nch = (te + kQ - 1) / kQ;  // chunks [tb / kQ, nch) of this segment
+  int64_t k = tb / kQ;
   if constexpr (STG) {
     // Whole 32-token groups through the LDS staging; the next group's loads
     // are in flight while a group is computed.
@@ -446,9 +467,9 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
         }
       }
     };
-    const int64_t ngrp = L / kGT;
-    if (ngrp > 0) load_group(0);
-    for (int64_t G = 0; G < ngrp; ++G) {
+    const int64_t g0 = tb / kGT, ngrp = te / kGT;  // whole groups of the segment
+    if (ngrp > g0) load_group(g0);
+    for (int64_t G = g0; G < ngrp; ++G) {
       __syncthreads();  // the previous group's reads of the staging are done
       for (int in = 0; in < 5; ++in) {
         if (!GATE && in == 2) continue;
@@ -484,7 +505,7 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
               *reinterpret_cast<const float4*>(sy + r * kYPitch + pc * 4);
       }
     }
-    k = ngrp * 2;
+    k = ngrp > g0 ? ngrp * 2 : k;
   }
   // Chunks not covered by the staging (all of them without it; otherwise the
   // last one or two), directly from global memory; tokens past the end masked.
@@ -494,7 +515,7 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
     const Front<In> f = front(rw, k, true);
     finish(f, k, true);
   }
-  if (a.h_last && dval) {
+  if (a.h_last && dval && seg == (int64_t)gridDim.y - 1) {
     for (int r = 0; r < 4; ++r) {
       const int n = 4 * g + r;
       if (n < N) a.h_last[(b * D + d0 + c) * N + n] = H[r];
@@ -502,10 +523,142 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
   }
 }
 
-template <typename In, bool GATE>
-int launch_ssd_t(const SsdArgs& a, int64_t batch, bool vec, bool stg, hipStream_t st) {
+// State-only pass of a segmented scan (segments 0 .. gridDim.y - 1, every one
+// whole: seg_len tokens): the segment's end state from a zero state,
+// H' = e^{a c_16} H + B^T W per chunk with W_s = Delta_s x_s e^{a (c_16 - c_s)}
+// (each decay <= 1 for a <= 0, so no range split is needed), and its summed
+// step (compensated).  Same lane layout as s6_ssd_kernel.  Two register sets
+// of kPB chunks' loads alternate, so a set's loads are issued kPB to 2 kPB
+// chunks ahead of their use (loads past the segment reread its last chunk and
+// are not used).
+template <typename In, bool VEC>
+__global__ void __launch_bounds__(64) s6_ssd_state_kernel(SsdArgs a, int64_t batch) {
+  const int lane = threadIdx.x;
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t b = blockIdx.x % batch;
+  const int64_t d0 = (blockIdx.x / batch) * kTile;
+  const int64_t D = a.D, L = a.L, N = a.N;
+  const bool dval = d0 + c < D;
+  const int cl = dval ? c : (int)(D - 1 - d0);
+  const bool nval = c < N;
+  const int nc = nval ? c : (int)N - 1;
+  constexpr uint32_t esz = sizeof(In);
+  const char* xb = static_cast<const char*>(a.x) + (b * D + d0) * L * esz;
+  const char* db = static_cast<const char*>(a.delta) + (b * D + d0) * L * esz;
+  const char* bb = static_cast<const char*>(a.Bm) + b * N * L * esz;
+  const uint32_t xo = (uint32_t)cl * (uint32_t)L * esz;
+  const uint32_t no = (uint32_t)nc * (uint32_t)L * esz;
+  const float a2 = a.A[d0 + cl] * kLog2e;
+  const int64_t seg = blockIdx.y;
+  const int64_t kb = seg * a.seg_len / kQ, ke = (seg + 1) * a.seg_len / kQ;
+  float H[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float dsum = 0.0f, dcomp = 0.0f;
+  constexpr int kPB = 4;  // chunks per register set
+  Four<In> px[2][kPB], pd[2][kPB], pb[2][kPB];
+  auto issue = [&](auto setc, int64_t k0) {
+    constexpr int SET = decltype(setc)::value;
+#pragma unroll
+    for (int i = 0; i < kPB; ++i) {
+      const int64_t k = k0 + i < ke ? k0 + i : ke - 1;
+      const int64_t t = k * kQ + 4 * g;
+      px[SET][i] = load4<In, VEC>(xb, xo, t, L);
+      pd[SET][i] = load4<In, VEC>(db, xo, t, L);
+      pb[SET][i] = load4<In, VEC>(bb, no, t, L);
+    }
+  };
+  auto compute = [&](auto setc, int64_t k0) {
+    constexpr int SET = decltype(setc)::value;
+#pragma unroll
+    for (int i = 0; i < kPB; ++i) {
+      if (k0 + i >= ke) break;  // uniform
+      float xv[4], dv[4], bn[4];
+      px[SET][i].unpack(xv);
+      pd[SET][i].unpack(dv);
+      pb[SET][i].keep_if(nval);
+      pb[SET][i].unpack(bn);
+      float cs[4], total;
+      chunk_cumsum(dv, g, cs, total);
+      float W[4];
+      for (int j = 0; j < 4; ++j) W[j] = (dv[j] * xv[j]) * fast_exp2(a2 * (total - cs[j]));
+      const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4 S = mma_f32(bn, W, z4);  // B^T W: lane (g, c) gets states 4g + r of channel c
+      const float dec = fast_exp2(a2 * total);
+      for (int r = 0; r < 4; ++r) H[r] = __builtin_fmaf(dec, H[r], S[r]);
+      const float t = dsum + total;
+      dcomp += (fabsf(dsum) >= fabsf(total)) ? (dsum - t) + total : (total - t) + dsum;
+      dsum = t;
+    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  issue(S0{}, kb);
+  issue(S1{}, kb + kPB);
+  for (int64_t k0 = kb; k0 < ke; k0 += 2 * kPB) {
+    compute(S0{}, k0);
+    issue(S0{}, k0 + 2 * kPB);
+    compute(S1{}, k0 + kPB);
+    issue(S1{}, k0 + 3 * kPB);
+  }
+  if (dval) {
+    const int64_t nstate = batch * D * N;
+    for (int r = 0; r < 4; ++r) {
+      const int n = 4 * g + r;
+      if (n < N) a.agg[seg * nstate + (b * D + d0 + c) * N + n] = H[r];
+    }
+    if (g == 0) a.sumdelta[seg * batch * D + b * D + d0 + c] = dsum + dcomp;
+  }
+}
+
+// Segments along L for few long rows: when the batch x tile waves fill less
+// than half of the wave slots (3 per SIMD), the sequence is cut into
+// segments of whole 32-token groups, as many as fill the slots twice; their
+// carries go to the caller's workspace: end states from zero and summed
+// steps (S - 1 of each), incoming states (S).
+struct SsdPlan {
+  int64_t S, seg_len;
+  size_t agg, sd, hin, total;
+};
+SsdPlan ssd_plan(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate) {
+  SsdPlan p{1, seqlen, 0, 0, 0, 0};
+  const int64_t waves = batch * ((dim + kTile - 1) / kTile);
+  const int64_t slots = (int64_t)cu_count() * 4 * 3;
+  if (waves > 0 && 2 * waves <= slots) {
+    int64_t S = 2 * slots / waves;
+    const int64_t max_s = (seqlen + kGT - 1) / kGT;
+    if (S > max_s) S = max_s;
+    if (S > 1) {
+      const int64_t sl = ((seqlen + S - 1) / S + kGT - 1) / kGT * kGT;
+      p.seg_len = sl;
+      p.S = (seqlen + sl - 1) / sl;
+    }
+  }
+  if (p.S > 1) {
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const size_t nstate = (size_t)batch * dim * dstate;
+    p.agg = 0;
+    p.sd = up((size_t)(p.S - 1) * nstate * sizeof(float));
+    p.hin = p.sd + up((size_t)(p.S - 1) * batch * dim * sizeof(float));
+    p.total = p.hin + up((size_t)p.S * nstate * sizeof(float));
+  }
+  return p;
+}
+
+template <typename In>
+int launch_ssd_state(const SsdArgs& a, int64_t batch, bool vec, int64_t segs, hipStream_t st) {
   const int64_t tiles = (a.D + kTile - 1) / kTile;
-  const dim3 grid((unsigned)(tiles * batch));
+  const dim3 grid((unsigned)(tiles * batch), (unsigned)segs);
+  if (vec)
+    hipLaunchKernelGGL((s6_ssd_state_kernel<In, true>), grid, dim3(64), 0, st, a, batch);
+  else
+    hipLaunchKernelGGL((s6_ssd_state_kernel<In, false>), grid, dim3(64), 0, st, a, batch);
+  S6_HIP(hipGetLastError(), "s6_ssd_state_kernel launch");
+  return S6_OK;
+}
+
+template <typename In, bool GATE>
+int launch_ssd_t(const SsdArgs& a, int64_t batch, int64_t segs, bool vec, bool stg, hipStream_t st) {
+  const int64_t tiles = (a.D + kTile - 1) / kTile;
+  const dim3 grid((unsigned)(tiles * batch), (unsigned)segs);
   if (stg)
     hipLaunchKernelGGL((s6_ssd_kernel<In, GATE, true, true>), grid, dim3(64), 0, st, a, batch);
   else if (vec)
@@ -531,6 +684,8 @@ int s6_ssd_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen, i
   if (rc) return rc;
   if (dstate > 16) return S6_ERR_UNSUPPORTED;
   *bytes = 0;
+  if (batch == 0 || dim == 0 || seqlen == 0) return S6_OK;
+  *bytes = ssd_plan(batch, dim, seqlen, dstate).total;
   return S6_OK;
 }
 
@@ -538,8 +693,6 @@ int s6_ssd_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, 
                     const void* delta, const float* A, const void* Bm, const void* Cm, const float* Dskip,
                     const void* z, const float* h0, float* y, float* h_last, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   int rc = check_common(batch, dim, seqlen, dstate, in_dtype);
   if (rc) return rc;
   if (dstate > 16) return S6_ERR_UNSUPPORTED;
@@ -565,12 +718,32 @@ int s6_ssd_scan_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, 
   bool stg = vec && (seqlen * (int64_t)esz) % 16 == 0;
   for (const void* p : ins)
     if (p && !aligned(p, 16)) stg = false;
+  const SsdPlan pl = ssd_plan(batch, dim, seqlen, dstate);
+  if (pl.total > 0 && (!workspace || workspace_bytes < pl.total)) return S6_ERR_WORKSPACE;
+  if (pl.total > 0 && !aligned(workspace, 256)) return S6_ERR_ALIGN;
   SsdArgs a;
+  memset(&a, 0, sizeof(a));
   a.x = x; a.delta = delta; a.z = z; a.Bm = Bm; a.Cm = Cm; a.A = A; a.Dskip = Dskip; a.h0 = h0; a.y = y;
-  a.h_last = h_last; a.D = dim; a.L = seqlen; a.N = dstate;
-  if (in_dtype == S6_BF16)
-    return z ? launch_ssd_t<uint16_t, true>(a, batch, vec, stg, st) : launch_ssd_t<uint16_t, false>(a, batch, vec, stg, st);
-  return z ? launch_ssd_t<float, true>(a, batch, vec, stg, st) : launch_ssd_t<float, false>(a, batch, vec, stg, st);
+  a.h_last = h_last; a.D = dim; a.L = seqlen; a.N = dstate; a.seg_len = pl.seg_len;
+  const bool bf = in_dtype == S6_BF16;
+  if (pl.S > 1) {
+    // pass 1: end states (from zero) and summed steps of all segments but the
+    // last; the fold gives every segment's incoming state
+    char* wp = static_cast<char*>(workspace);
+    SsdArgs g = a;
+    g.agg = reinterpret_cast<float*>(wp + pl.agg);
+    g.sumdelta = reinterpret_cast<float*>(wp + pl.sd);
+    float* hin = reinterpret_cast<float*>(wp + pl.hin);
+    rc = bf ? launch_ssd_state<uint16_t>(g, batch, vec, pl.S - 1, st) : launch_ssd_state<float>(g, batch, vec, pl.S - 1, st);
+    if (rc == S6_OK)
+      rc = launch_fold_carries(A, h0, g.agg, g.sumdelta, hin, nullptr, batch, dim, dstate, pl.S, pl.S - 1, st, true);
+    if (rc) return rc;
+    a.hin = hin;
+  }
+  if (bf)
+    return z ? launch_ssd_t<uint16_t, true>(a, batch, pl.S, vec, stg, st)
+             : launch_ssd_t<uint16_t, false>(a, batch, pl.S, vec, stg, st);
+  return z ? launch_ssd_t<float, true>(a, batch, pl.S, vec, stg, st) : launch_ssd_t<float, false>(a, batch, pl.S, vec, stg, st);
 }
 
 }  // extern "C"

@@ -362,8 +362,8 @@ def test_library_source_allocates_nothing():
 
 
 def test_ssd_validation(lib, codes):
-    """The scalar-A chunked scan: dstate up to 16, the common checks, no
-    workspace at any size."""
+    """The scalar-A chunked scan: dstate up to 16, the common checks; a
+    workspace only when few long rows are cut into segments."""
     def f(b=2, d=64, L=32, n=16, dt=1, x=P, y=P, A=P, z=None):
         return lib.s6_ssd_scan_fwd(b, d, L, n, dt, x, P, A, P, P, None, z, None, y, None, None, 0, None)
 
@@ -377,8 +377,16 @@ def test_ssd_validation(lib, codes):
     assert f(A=P_ODD) == codes["S6_ERR_ALIGN"]
     assert f(dt=1, z=ctypes.c_void_p((1 << 20) + 1)) == codes["S6_ERR_ALIGN"]
     assert f(b=0) == codes["S6_OK"]
-    for shape in ((8, 5120, 2048, 16), (1, 1536, 1 << 20, 16), (1, 16, 256, 4)):
-        assert _size(lib.s6_ssd_scan_fwd_workspace_size, *shape, 1) == (codes["S6_OK"], 0)
+    # the 3B layer's 2560 waves fill the slots: one segment, no workspace
+    assert _size(lib.s6_ssd_scan_fwd_workspace_size, 8, 5120, 2048, 16, 1) == (codes["S6_OK"], 0)
+    # 1M tokens of 1536 channels (96 waves): 2 x 3072 slots / 96 = 64 segments
+    # of 16384 tokens; 63 end states and summed steps, 64 incoming states
+    st = 1536 * 16 * 4
+    want = 63 * st + (63 * 1536 * 4 + 255) // 256 * 256 + 64 * st
+    assert _size(lib.s6_ssd_scan_fwd_workspace_size, 1, 1536, 1 << 20, 16, 1) == (codes["S6_OK"], want)
+    # one 16-channel tile of 256 tokens: 8 segments of 32 tokens
+    assert _size(lib.s6_ssd_scan_fwd_workspace_size, 1, 16, 256, 4, 1) == (codes["S6_OK"], 1792 + 512 + 2048)
+    assert f(b=1, d=16, L=256, n=4) == codes["S6_ERR_WORKSPACE"]
     assert _size(lib.s6_ssd_scan_fwd_workspace_size, 1, 16, 256, 32, 1)[0] == codes["S6_ERR_UNSUPPORTED"]
 
 

@@ -51,6 +51,10 @@ SHAPES = [
     (1, 16, 1, 64, synth.BF16, True),       # one state
     (2, 40, 16, 2056, synth.BF16, True),    # staged 32-token groups, then a partial chunk
     (1, 24, 16, 560, synth.F32, True),      # staged groups, then one whole chunk
+    # few long rows: cut into segments (state-only pass, fold, scan from the
+    # folded states); the last segment partial
+    (1, 48, 16, 40010, synth.BF16, True),
+    (2, 20, 16, 12288, synth.F32, True),
 ]
 
 
@@ -63,6 +67,9 @@ def test_ssd_small(torch_cuda, oracle, shape, with_h0):
     _say(f"[case] ssd {w.name} h0={with_h0}")
     dd, o = problem(w, with_h0)
     a, A2 = _scalar(w)
+    import torch
+    tdt = torch.float32 if dt == synth.F32 else torch.bfloat16
+    print(f"[case] workspace {s6.workspace_size('ssd_scan_fwd', b, d, L, n, tdt)} bytes", flush=True)
     y, hl = s6.ssd_scan_fwd(dd["x"], dd["delta"], dev(a, synth.F32), dd["Bm"], dd["Cm"], D=dd["D"], z=dd["z"],
                             h0=dd["h0"], return_last_state=True)
     torch_cuda.cuda.synchronize()
@@ -156,3 +163,32 @@ def test_ssd_full_workload(torch_cuda, oracle):
                         host64(inp["Cm"][b:b + 1]), Dskip=host64(inp["Dskip"]), z=host64(inp["z"][b:b + 1]))
         assert scaled(host64(y[b:b + 1]), r["y"], r["m"], guard=GUARD[w.dtype]) <= TOL[w.dtype], b
         assert scaled(host64(hl[b:b + 1]), r["h_last"], r["H_last"], guard=GUARD[w.dtype]) <= TOL[w.dtype], b
+
+
+def test_ssd_long_workload(torch_cuda, oracle):
+    """The scalar-A scan of the million-token sequence (batch 1, 1536
+    channels, 16 states, 2^20 tokens; one A value per channel drawn as for the
+    scalar-A workload): cut into segments, every output compared in blocks of
+    64 channels over the whole length."""
+    import torch
+    from selective_state_space_63_amd import s6
+    w = synth.WORKLOADS["long"]
+    _say(f"[case] ssd long {w.name}")
+    inp = synth.device_full(w)
+    a = synth.scalar_a_device(w)
+    y, hl = s6.ssd_scan_fwd(inp["x"], inp["delta"], a, inp["Bm"], inp["Cm"], D=inp["Dskip"], z=inp["z"],
+                            return_last_state=True)
+    torch.cuda.synchronize()
+    av = host64(a)
+    Bm, Cm = host64(inp["Bm"]), host64(inp["Cm"])
+    worst = 0.0
+    for c0 in range(0, w.dim, 64):
+        c1 = min(w.dim, c0 + 64)
+        A2 = np.repeat(av[c0:c1, None], w.dstate, axis=1)
+        r = oracle.scan(host64(inp["x"][:, c0:c1]), host64(inp["delta"][:, c0:c1]), A2, Bm, Cm,
+                        Dskip=host64(inp["Dskip"][c0:c1]), z=host64(inp["z"][:, c0:c1]))
+        ey = scaled(host64(y[:, c0:c1]), r["y"], r["m"], guard=GUARD[w.dtype])
+        eh = scaled(host64(hl[:, c0:c1]), r["h_last"], r["H_last"], guard=GUARD[w.dtype])
+        worst = max(worst, ey, eh)
+        assert ey <= TOL[w.dtype] and eh <= TOL[w.dtype], (c0, ey, eh)
+    _say(f"[result] ssd long every output: max scaled error {worst:.3e}")
