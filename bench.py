@@ -279,13 +279,18 @@ def bench_scan(w, steps, warmup, flush=False, softplus=False, zoh=False, conv_k=
 
 
 def ssd_mfma_flops(w):
-    """Matrix-core flops one s6_ssd_scan_fwd issues, per precision: per
-    16-token chunk and 16-channel tile three bf16 16x16x16 products (B and C
-    made token-major by the identity, the Gram matrix; bf16 inputs) and
-    three fp32 16x16x16 products as twelve 16x16x4 ones (tril(G) V, C H,
-    B^T V), 2 * 16^3 flops per 16x16x16."""
+    """Matrix-core flops one s6_ssd_scan_fwd issues, per precision, 2 * 16^3
+    flops per 16x16x16 product.  Per 16-token chunk and 16-channel tile:
+    B and C made token-major by the identity and the Gram matrix (3
+    products), then tril(G) V, C H and B^T V.  bf16 inputs run all of them
+    on bf16 matrix cores, the last three with each fp32 operand split into
+    two bf16 parts (3 + 2 + 2 products): 10 bf16 products.  fp32 inputs
+    run all six as fp32 (four 16x16x4 each)."""
+    from selective_state_space_63_amd import synth
     tiles = w.batch * ((w.dim + 15) // 16) * ((w.seqlen + 15) // 16)
-    return {"bf16": tiles * 3 * 2 * 16 ** 3, "fp32": tiles * 3 * 2 * 16 ** 3}
+    if w.dtype == synth.BF16:
+        return {"bf16": tiles * 10 * 2 * 16 ** 3, "fp32": 0}
+    return {"bf16": 0, "fp32": tiles * 6 * 2 * 16 ** 3}
 
 
 def bench_ssd(w, steps, warmup):
@@ -328,7 +333,7 @@ def bench_ssd(w, steps, warmup):
                               "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": byts,
                               "mfma": {p: {"flops_per_launch": f, "achieved_TFLOPs": round(f / (ms * 1e-3) / 1e12, 1),
                                            "peak_TFLOPs": pk, "frac": round(f / (ms * 1e-3) / 1e12 / pk, 4)}
-                                       for (p, f), pk in zip(fl.items(), (2500.0, 157.3))}},
+                                       for (p, f), pk in zip(fl.items(), (2500.0, 157.3)) if f}},
                  "note": "s6_ssd_scan_fwd: one A value per channel, chunked matrix form on the matrix cores"}
 
 

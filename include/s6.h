@@ -348,9 +348,11 @@ int s6_scan_bwd_ckpt(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
  *   y[b,d,t] = (sum_n Cm[b,n,t] * h[n] + Dskip[d] * x[b,d,t]) * SiLU(z[b,d,t])
  * evaluated per 16-token chunk as products with the Gram matrix of B and C
  * (shared by every channel of a batch row) and two exponentials per token
- * and channel.  Products of inputs only (B, C and the Gram matrix of bf16
- * inputs) run on the bf16 matrix cores, exactly; products with an fp32
- * operand (the scaled inputs, the state) on the fp32 matrix cores.
+ * and channel.  bf16 inputs: every product runs on the bf16 matrix cores;
+ * those of inputs only (B, C, their Gram matrix) are exact, and each fp32
+ * operand (the scaled inputs, the state, the decayed Gram matrix) enters as
+ * the sum of two bf16 parts, within 2^-17 of its value.  fp32 inputs: every
+ * product on the fp32 matrix cores.
  *   A : (dim) fp32, one value per channel (accuracy specified for A <= 0).
  *   dstate : 1..16 (else S6_ERR_UNSUPPORTED).
  *   Everything else (layouts, nullable Dskip, z, h0, h_last; errors; stream)

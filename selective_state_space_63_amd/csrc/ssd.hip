@@ -136,6 +136,19 @@ __device__ __forceinline__ f32x4 mma_in(const Four<In>& a, const Four<In>& b, f3
   }
 }
 
+// An fp32 operand as the sum of two bf16 parts: hi = bf16(v), lo = bf16(v -
+// hi) (v - hi is exact in fp32); hi + lo is within 2^-17 |v| of v.  A product
+// with an exact bf16 operand then takes two bf16 matrix-core instructions,
+// a product of two split operands three (the lo x lo term, below 2^-32 of
+// the product, is left out).
+__device__ __forceinline__ void split_bf16(const float v[4], Four<uint16_t>& hi, Four<uint16_t>& lo) {
+  hi.pack(v);
+  float h[4], r[4];
+  hi.unpack(h);
+  for (int j = 0; j < 4; ++j) r[j] = v[j] - h[j];
+  lo.pack(r);
+}
+
 // Raw inputs of one chunk for one lane: 4 tokens of x, delta, z of channel
 // c and 4 tokens of B and C of state c.
 template <typename In>
@@ -150,6 +163,7 @@ struct Front {
   f32x4 S;       // B^T V
   float P[4];    // e^{a (c_t - r)} of the lane's 4 tokens
   float ct[4];   // C token-major: lane (g, c) holds C[n = 4g + j][t = c] (A operand of C H)
+  Four<In> ctp;  // the same packed (exact: C's own values)
   float xv[4];   // x of the lane's 4 tokens (skip term)
   Four<In> z;    // gate input
   float kr;      // e^{a r} = e^{a (c_16 - r)}
@@ -308,11 +322,11 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
 
   // B and C token-major (an MFMA with the identity) and G^T = Bmat Cmat^T:
   // lane (g, c) gets G[t = c][s = 4g + r], the A operand of tril(G) V.
-  auto gram = [&](const Raw<In>& rw, float ct[4], float gm[4]) {
+  auto gram = [&](const Raw<In>& rw, float ct[4], float gm[4], Four<In>& ctp) {
     const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4 btf = mma_in<In>(rw.b, ident, z4);
     const f32x4 ctf = mma_in<In>(rw.c, ident, z4);
-    Four<In> bt, ctp;
+    Four<In> bt;
     float bv[4] = {btf[0], btf[1], btf[2], btf[3]};
     for (int j = 0; j < 4; ++j) ct[j] = ctf[j];
     bt.pack(bv);
@@ -338,12 +352,26 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
     }
     f.kr = fast_exp2(ah);
     f.dec = fast_exp2(a2 * total);
-    float gm[4], bn[4];
-    gram(rw, f.ct, gm);
-    rw.b.unpack(bn);
+    float gm[4];
+    gram(rw, f.ct, gm, f.ctp);
     const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-    f.Yd = mma_f32(gm, V, z4);   // tril(G) V
-    f.S = mma_f32(bn, V, z4);    // B^T V
+    if constexpr (sizeof(In) == 2) {
+      // bf16 matrix cores with V and tril(G) split into two bf16 parts; B
+      // is its own bf16 values
+      Four<In> vh, vl, gh, gl;
+      split_bf16(V, vh, vl);
+      split_bf16(gm, gh, gl);
+      f.Yd = mma_in<In>(gh, vh, z4);  // tril(G) V
+      f.Yd = mma_in<In>(gh, vl, f.Yd);
+      f.Yd = mma_in<In>(gl, vh, f.Yd);
+      f.S = mma_in<In>(rw.b, vh, z4);  // B^T V
+      f.S = mma_in<In>(rw.b, vl, f.S);
+    } else {
+      float bn[4];
+      rw.b.unpack(bn);
+      f.Yd = mma_f32(gm, V, z4);   // tril(G) V
+      f.S = mma_f32(bn, V, z4);    // B^T V
+    }
     f.z = rw.z;
     return f;
   };
@@ -380,7 +408,15 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
   auto back = [&](const Front<In>& f, int64_t k, bool mask, int slot) {
     float hs[4];
     for (int r = 0; r < 4; ++r) hs[r] = H[r] * f.kr;
-    const f32x4 Y = mma_f32(f.ct, hs, f.Yd);
+    f32x4 Y;
+    if constexpr (sizeof(In) == 2) {
+      Four<In> hh, hl;
+      split_bf16(hs, hh, hl);
+      Y = mma_in<In>(f.ctp, hh, f.Yd);
+      Y = mma_in<In>(f.ctp, hl, Y);
+    } else {
+      Y = mma_f32(f.ct, hs, f.Yd);
+    }
     for (int r = 0; r < 4; ++r) H[r] = __builtin_fmaf(f.dec, H[r], f.kr * f.S[r]);
     output(f.z, f.P, Y, f.xv, k, mask, slot);
   };
@@ -400,7 +436,8 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
       W[j] = v[j] * fast_exp2(a2 * (total - cs[j]));
     }
     float ct[4], gm[4], bn[4];
-    gram(rw, ct, gm);
+    Four<In> ctp;
+    gram(rw, ct, gm, ctp);
     rw.b.unpack(bn);
     const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4 Yo = mma_f32(ct, H, z4);
@@ -581,7 +618,16 @@ __global__ void __launch_bounds__(64) s6_ssd_state_kernel(SsdArgs a, int64_t bat
       float W[4];
       for (int j = 0; j < 4; ++j) W[j] = (dv[j] * xv[j]) * fast_exp2(a2 * (total - cs[j]));
       const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-      const f32x4 S = mma_f32(bn, W, z4);  // B^T W: lane (g, c) gets states 4g + r of channel c
+      // B^T W: lane (g, c) gets states 4g + r of channel c
+      f32x4 S;
+      if constexpr (sizeof(In) == 2) {
+        Four<In> wh, wl;
+        split_bf16(W, wh, wl);
+        S = mma_in<In>(pb[SET][i], wh, z4);
+        S = mma_in<In>(pb[SET][i], wl, S);
+      } else {
+        S = mma_f32(bn, W, z4);
+      }
       const float dec = fast_exp2(a2 * total);
       for (int r = 0; r < 4; ++r) H[r] = __builtin_fmaf(dec, H[r], S[r]);
       const float t = dsum + total;
