@@ -86,9 +86,15 @@ __device__ __forceinline__ float row_bcast(float v) {
 
 // Offset (floats) of the 4-token group `grp` of channel row c in a
 // channel-major tile of pitch kT = 16.  The group index is XORed with
-// (c >> 1) & 3 so that 16-byte reads of one group by 8 consecutive lanes
-// fall on 8 distinct 4-bank groups (no padding needed).
-__device__ __forceinline__ int tsw(int c, int grp) { return c * kP + ((grp ^ ((c >> 1) & 3)) << 2); }
+// ((c >> 2) & 3) ^ ((c >> 1) & 1), a swizzle that leaves no bank conflicts
+// on gfx950 in either direction (measured with SQ_LDS_BANK_CONFLICT on
+// each access pattern alone): 16-byte reads there take 16 lanes per cycle
+// over 64 banks, so one group of 16 consecutive channels must cover all 64
+// banks; 16-byte writes take 8 lanes over 32 banks, and the staging writes
+// two groups of each of 4 consecutive rows at once.
+__device__ __forceinline__ int tsw(int c, int grp) {
+  return c * kP + ((grp ^ ((c >> 2) & 3) ^ ((c >> 1) & 1)) << 2);
+}
 
 // Value of lane CTRL's DPP source (a DPP control code: quad permutation, row
 // rotation, row mirror, ...) in this lane; lanes whose source is outside the

@@ -71,14 +71,16 @@ struct ChunkPieces {
 // token group g (4 tokens), wave w and row parity r (state pair 4w + 2r,
 // 4w + 2r + 1), a block of 16 slots read by the 16 lanes of the row: B of
 // pair member m, token k at slot 4m + k; C at slot 8 + 4m + k.  The four
-// 4-slot quarters of a block are permuted by XOR with f(g, w) so that the
-// 16-byte writes of one instruction spread over the banks; readers apply
-// the same permutation, so lane x of a row still receives slot x.  States
-// beyond N stay zero.
+// 4-slot quarters of a block are permuted by XOR with f(g, w), readers
+// applying the same permutation, so lane x of a row still receives slot x.
+// A staging write covers groups g and g + 2 of one state (16-byte writes
+// take 8 lanes per cycle over 32 banks on gfx950: two pair members x two
+// groups x two row parities must fill the 32 banks), so bit 1 of f flips
+// between g and g + 2.  States beyond N stay zero.
 template <int W>
 struct BCLayout {
   static constexpr int kFloats = (kT / 4) * W * 2 * 16;  // floats per chunk
-  __device__ __forceinline__ static int quarter(int g, int w, int q) { return q ^ (((g >> 1) ^ w) & 3); }
+  __device__ __forceinline__ static int quarter(int g, int w, int q) { return q ^ (((g >> 1) & 1) << 1) ^ (w & 3); }
   __device__ __forceinline__ static int pos(int g, int w, int r, int x) {
     return ((g * W + w) * 2 + r) * 16 + (quarter(g, w, x >> 2) << 2) + (x & 3);
   }
@@ -637,10 +639,13 @@ s6_scan_kernel(ScanArgs a) {
     }
     float* pbuf = part + buf * (W * PART);
     if constexpr (MODE == kModeY) {
-      // ysum[i] is this wave's sum for token 2i + r: part[buf][w][r][cl][i]
+      // ysum[i] is this wave's sum for token 2i + r: part[buf][w][r][cl][i],
+      // the two halves of the row swapped for channels with bit 2 set (so
+      // the 16-byte writes of 8 consecutive channels meet no bank twice)
       float* pp = pbuf + w * PART + (r * kCW + cl) * (kT / 2);
-      *reinterpret_cast<float4*>(pp) = make_float4(ysum[0], ysum[1], ysum[2], ysum[3]);
-      *reinterpret_cast<float4*>(pp + 4) = make_float4(ysum[4], ysum[5], ysum[6], ysum[7]);
+      const int sw = cl & 4;
+      *reinterpret_cast<float4*>(pp + sw) = make_float4(ysum[0], ysum[1], ysum[2], ysum[3]);
+      *reinterpret_cast<float4*>(pp + (sw ^ 4)) = make_float4(ysum[4], ysum[5], ysum[6], ysum[7]);
     }
     if constexpr (kSum) {
       const float t = dsum + cs;
@@ -669,7 +674,7 @@ s6_scan_kernel(ScanArgs a) {
         const int t = ft + i;  // token within the chunk
         float acc = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < W; ++ww) acc += pbuf[ww * PART + ((t & 1) * kCW + fc) * (kT / 2) + (t >> 1)];
+        for (int ww = 0; ww < W; ++ww) acc += pbuf[ww * PART + ((t & 1) * kCW + fc) * (kT / 2) + ((t >> 1) ^ (fc & 4))];
         acc = __builtin_fmaf(dsk, xfin[i], acc);
         if constexpr (GATE) acc *= silu(zfin[i]);
         yo[i] = acc;
