@@ -217,16 +217,32 @@ struct SsdArgs {
 // loads per lane cover the group's 32 tokens of the tile's 16 rows in runs of
 // 64 (bf16) or 128 (fp32) contiguous bytes, written to LDS and read back per
 // chunk in the MFMA layout; the group's y (16 rows x 32 fp32) is collected in
-// LDS and written as whole 128-byte lines.  Row pitches are padded against
-// bank conflicts and keep 16-byte alignment.
+// LDS and written as whole 128-byte lines.
+//
+// Bank conflicts (gfx950, as measured: 16-byte reads take 16 lanes per cycle
+// over 64 banks; 16-byte writes 8 lanes, 8-byte accesses 16 lanes, over 32):
+// * bf16 inputs: rows of 64 bytes, the 8-byte slot s (tokens 4s .. 4s+3) of
+//   row c stored at slot s ^ ((c >> 1) & 7), each loaded 16-byte piece
+//   written as its two 8-byte halves.  The chunk reads (8 bytes of 16
+//   consecutive rows per cycle) and the half writes (4 rows x 4 pieces)
+//   then meet every bank once.  No padding gives both: 16-byte aligned rows
+//   leave 8-byte reads of 16 rows at most 8 distinct bank pairs.
+// * fp32 inputs: rows padded to 36 floats.
+// * y: rows of 32 floats, the 16-byte piece p of row c stored at p ^ (c & 7),
+//   so that the writes of 8 channels and the reads of two rows each cover
+//   the banks once.
 constexpr int kGT = 2 * kQ;                    // tokens per staged group
 template <typename In>
 struct Stg {
-  static constexpr int kPitch = sizeof(In) == 2 ? 40 : 36;  // input row pitch (elements)
+  static constexpr int kPitch = sizeof(In) == 2 ? 32 : 36;  // input row pitch (elements)
   static constexpr int kLoads = sizeof(In) / 2;             // 16-byte loads per lane per input
   static constexpr int kIn = 16 * kPitch;                   // elements per input tile
 };
-constexpr int kYPitch = 36;                    // y row pitch (floats)
+constexpr int kYPitch = 32;                    // y row pitch (floats)
+// element offset of the 4 bf16 tokens in slot s of staged row c
+__device__ __forceinline__ int stg_slot(int c, int s) { return c * 32 + 4 * (s ^ ((c >> 1) & 7)); }
+// float offset of the 16-byte piece p of y row c
+__device__ __forceinline__ int y_piece(int c, int p) { return c * kYPitch + 4 * (p ^ (c & 7)); }
 
 template <typename In, bool GATE, bool VEC, bool STG>
 __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch) {
@@ -389,7 +405,7 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
       yo[r] = yy;
     }
     if (STG && slot >= 0) {
-      *reinterpret_cast<float4*>(sy + c * kYPitch + slot * kQ + 4 * g) = make_float4(yo[0], yo[1], yo[2], yo[3]);
+      *reinterpret_cast<float4*>(sy + y_piece(c, slot * 4 + g)) = make_float4(yo[0], yo[1], yo[2], yo[3]);
       return;
     }
     if (dval && (!mask || t0 < L)) {
@@ -510,9 +526,16 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
       __syncthreads();  // the previous group's reads of the staging are done
       for (int in = 0; in < 5; ++in) {
         if (!GATE && in == 2) continue;
-        for (int q = 0; q < NL; ++q)
-          *reinterpret_cast<u32x4*>(sin + in * Stg<In>::kIn + (prow + q * RPL) * Stg<In>::kPitch + ppc * EPP) =
-              stage[in][q];
+        for (int q = 0; q < NL; ++q) {
+          const int row = prow + q * RPL;
+          if constexpr (sizeof(In) == 2) {
+            In* t = sin + in * Stg<In>::kIn;
+            *reinterpret_cast<uint2*>(t + stg_slot(row, 2 * ppc)) = make_uint2(stage[in][q].x, stage[in][q].y);
+            *reinterpret_cast<uint2*>(t + stg_slot(row, 2 * ppc + 1)) = make_uint2(stage[in][q].z, stage[in][q].w);
+          } else {
+            *reinterpret_cast<u32x4*>(sin + in * Stg<In>::kIn + row * Stg<In>::kPitch + ppc * EPP) = stage[in][q];
+          }
+        }
       }
       if (G + 1 < ngrp) load_group(G + 1);
       __syncthreads();
@@ -520,7 +543,7 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
       for (int j = 0; j < 2; ++j) {
         // the lane's 4 tokens of chunk j: row c (channel or state), tokens 16 j + 4 g ..
         Raw<In> rw;
-        const int eo = c * Stg<In>::kPitch + j * kQ + 4 * g;
+        const int eo = sizeof(In) == 2 ? stg_slot(c, 4 * j + g) : c * Stg<In>::kPitch + j * kQ + 4 * g;
         Four<In>* dst[5] = {&rw.x, &rw.dl, &rw.z, &rw.b, &rw.c};
         for (int in = 0; in < 5; ++in) {
           if (!GATE && in == 2) continue;
@@ -539,7 +562,7 @@ __global__ void __launch_bounds__(64, 3) s6_ssd_kernel(SsdArgs a, int64_t batch)
         const int r = (lane >> 3) + 8 * h, pc = lane & 7;
         if (d0 + r < D)
           *reinterpret_cast<float4*>(yb + (uint32_t)r * (uint32_t)L + (uint32_t)(G * kGT + pc * 4)) =
-              *reinterpret_cast<const float4*>(sy + r * kYPitch + pc * 4);
+              *reinterpret_cast<const float4*>(sy + y_piece(r, pc));
       }
     }
     k = ngrp > g0 ? ngrp * 2 : k;
