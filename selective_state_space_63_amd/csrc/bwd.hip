@@ -739,6 +739,41 @@ __global__ void s6_bwd_reduce_bc(const float* __restrict__ part_b, const float* 
   }
 }
 
+// The same sums four adjacent elements at a time (16-byte loads; total a
+// multiple of 4, every pointer 16-byte aligned): each element is added in
+// the same order as above, so the results are the same bit for bit.
+__global__ void s6_bwd_reduce_bc4(const float4* __restrict__ part_b, const float4* __restrict__ part_c,
+                                  float4* __restrict__ out_b, float4* __restrict__ out_c, int64_t nblk,
+                                  int64_t total4) {
+  const float4* part = blockIdx.y ? part_c : part_b;
+  float4* out = blockIdx.y ? out_c : out_b;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float4 sm[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sm[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    auto add = [](float4& a, const float4& v) { a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w; };
+    int64_t k = 0;
+    for (; k + 8 <= nblk; k += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = part[(k + j) * total4 + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) add(sm[j], v[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 7; ++j)
+      if (k + j < nblk) add(sm[j], part[(k + j) * total4 + i]);
+    auto tree = [&](float s0, float s1, float s2, float s3, float s4, float s5, float s6, float s7) {
+      return ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7));
+    };
+    out[i] = make_float4(tree(sm[0].x, sm[1].x, sm[2].x, sm[3].x, sm[4].x, sm[5].x, sm[6].x, sm[7].x),
+                         tree(sm[0].y, sm[1].y, sm[2].y, sm[3].y, sm[4].y, sm[5].y, sm[6].y, sm[7].y),
+                         tree(sm[0].z, sm[1].z, sm[2].z, sm[3].z, sm[4].z, sm[5].z, sm[6].z, sm[7].z),
+                         tree(sm[0].w, sm[1].w, sm[2].w, sm[3].w, sm[4].w, sm[5].w, sm[6].w, sm[7].w));
+  }
+}
+
 // dA (D, N) and dD (D): sums over batch rows, in order.
 __global__ void s6_bwd_reduce_rows(const float* __restrict__ dA_part, const float* __restrict__ dD_part,
                                    const float* __restrict__ db_part, float* __restrict__ dA,
@@ -1192,10 +1227,21 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
   }
   if (rc == S6_OK) {
     const int64_t tot = batch * dstate * seqlen;
-    int64_t blocks = (tot + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3((unsigned)blocks, 2u), dim3(256), 0, st, dBp, dcp, dBm, dCm, nblkb,
-                       tot);
+    const void* bcp[] = {dBp, dcp, dBm, dCm};
+    bool v4 = tot % 4 == 0;
+    for (const void* q : bcp) v4 = v4 && aligned(q, 16);
+    if (v4) {
+      int64_t blocks = (tot / 4 + 255) / 256;
+      if (blocks > 65536) blocks = 65536;
+      hipLaunchKernelGGL(s6_bwd_reduce_bc4, dim3((unsigned)blocks, 2u), dim3(256), 0, st,
+                         reinterpret_cast<const float4*>(dBp), reinterpret_cast<const float4*>(dcp),
+                         reinterpret_cast<float4*>(dBm), reinterpret_cast<float4*>(dCm), nblkb, tot / 4);
+    } else {
+      int64_t blocks = (tot + 255) / 256;
+      if (blocks > 65536) blocks = 65536;
+      hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3((unsigned)blocks, 2u), dim3(256), 0, st, dBp, dcp, dBm, dCm,
+                         nblkb, tot);
+    }
     const int64_t rows = dim * dstate;
     hipLaunchKernelGGL(s6_bwd_reduce_rows, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, dap, ddp, dbp,
                        dA, dDskip, ddelta_bias, G * batch, dim, dstate);
