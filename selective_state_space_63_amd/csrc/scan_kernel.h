@@ -268,12 +268,26 @@ s6_scan_kernel(ScanArgs a) {
   const int ft = (tid % LPR) * TPL;                          // its first token within a chunk
   const int64_t D = a.D, L = a.L, N = a.N;
   const int64_t nblk = (D + kCW - 1) / kCW;
-  const int64_t b = blockIdx.x / nblk;
-  const int64_t d0 = (int64_t)(blockIdx.x % nblk) * kCW;
+  // Workgroup -> (segment, batch row, channel block).  The dispatcher
+  // hands workgroups to the 8 XCDs in turn (linear id i to XCD i mod 8) and
+  // each XCD has its own L2.  Without segments the ids are remapped to give
+  // every XCD a contiguous run of the (row, block) order (a bijection for
+  // any count): the workgroups of one batch row, which read the same B and
+  // C, then share one L2 (3B layer: one batch row per XCD; 0.9% faster).
+  // Segmented grids keep the plain order: the same remap over (segment,
+  // block) made the million-token scan 1.5% slower.
+  uint32_t wgx = blockIdx.x, wgz = blockIdx.z;
+  if (gridDim.z == 1) {
+    const uint32_t nx = gridDim.x;
+    const uint32_t q = nx / 8, rem = nx % 8, xcd = wgx % 8;
+    wgx = xcd * q + (xcd < rem ? xcd : rem) + wgx / 8;
+  }
+  const int64_t b = wgx / nblk;
+  const int64_t d0 = (int64_t)(wgx % nblk) * kCW;
   const int64_t d = d0 + cl;
   const bool chv = d < D;
   const int64_t rows_valid = D - d0;
-  const int64_t seg = blockIdx.z;
+  const int64_t seg = wgz;
   const int64_t tb = seg * a.seg_len;
   const int64_t te = (tb + a.seg_len < L) ? tb + a.seg_len : L;
   const int64_t row0 = b * D + d0;
@@ -350,7 +364,7 @@ s6_scan_kernel(ScanArgs a) {
   const bool softplus = EXT && a.softplus;
   const bool dstep = EXT && (a.softplus || a.dbias);  // delta is rewritten while staged
   const bool zoh = EXT == 2 && a.zoh;
-  const int rot = EXT ? (int)(blockIdx.x % W) * 64 : 0;
+  const int rot = EXT ? (int)(wgx % W) * 64 : 0;
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     int p = ((tid + rot) & (NTHR - 1)) + s * NTHR;
