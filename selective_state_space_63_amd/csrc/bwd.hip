@@ -225,8 +225,16 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>())
   const int c = 4 * w + row;
   const int64_t D = a.D, L = a.L, N = a.N;
   const int64_t nblk = (D + CW - 1) / CW;
-  const int64_t blk = blockIdx.x % nblk;
-  const int64_t b = blockIdx.x / nblk;
+  // Without parts, each of the 8 XCDs (workgroups are dispatched to them in
+  // turn, each has its own L2) takes a contiguous run of (row, block), so
+  // the workgroups that stage the same B and C share one L2.
+  uint32_t wgx = blockIdx.x;
+  if (gridDim.y == 1) {
+    const uint32_t nx = gridDim.x, q = nx / 8, rem = nx % 8, xcd = wgx % 8;
+    wgx = xcd * q + (xcd < rem ? xcd : rem) + wgx / 8;
+  }
+  const int64_t blk = wgx % nblk;
+  const int64_t b = wgx / nblk;
   const int64_t d0 = blk * CW;
   const int64_t rows_valid = D - d0 < CW ? D - d0 : CW;
   const int64_t d = d0 + c;
