@@ -8,10 +8,11 @@ namespace {
 
 // Reverse-mode gradients of the scan for the loss <dy, y> + <dh_last, h_last>
 // (plain step).  The states are recomputed, never stored per token.  A first
-// pass gives either the state entering every 16-token chunk (one sequential
-// state-only scan, when its workgroups fill the GPU) or that entering every
-// segment of kBwdSeg tokens (segments scanned side by side from zero and
-// folded, the kernels of a segmented forward scan); this kernel then walks
+// pass gives the state entering every segment of kBwdSeg tokens (one
+// sequential state-only scan when its workgroups fill the GPU, else the
+// segments scanned side by side from zero and folded, the kernels of a
+// segmented forward scan) or, from the sequential scan for the exact hold and
+// the convolution front, the state entering every 16-token chunk; this kernel then walks
 // the segments of a (batch row, 16-channel block) from the last to the first.
 // Per segment it stages the inputs in LDS, loads or recomputes the states at
 // the four chunk starts, and per 16-token chunk (last first) recomputes the
@@ -1003,9 +1004,9 @@ int bwd_channels_per_block(int64_t dstate) { return dstate <= 16 ? 4 * bwd_waves
 // buffers in the caller's workspace.
 struct BwdWs {
   int64_t S, nblkb, G, spp, nlb;  // segments, channel blocks, parts, segments per part, front blocks
-  bool h16;                       // the states of every chunk come from one sequential state-only pass
+  bool h16;                       // the states come from one sequential state-only pass (every 16 or 64 tokens)
   size_t agg, sd, hin;            // checkpoint pass: segment end states, summed deltas, incoming states
-  size_t hin16;                   // h16: the state entering every 16-token chunk (over agg, sd, hin)
+  size_t hin16;                   // h16: the state entering every 16- or 64-token block (over agg, sd, hin)
   size_t dap, ddp, dbp;           // per (part, row) partials of dA, dD and the bias gradient
   size_t dBp, dCp;                // per channel-block partials of dB and dC
   size_t cM, muin, cSD;           // parts: adjoint carries and summed deltas
@@ -1048,10 +1049,11 @@ BwdWs bwd_ws_layout(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, 
   };
   // Without checkpoints and with one part, when the sequential state-only
   // scan has enough workgroups to fill the GPU on its own (the forward's
-  // plan keeps one segment), that scan writes the state entering every chunk
-  // and the adjoint kernel starts each chunk from it.  Otherwise 64-token
-  // segments are scanned side by side and folded.  The two layouts share the
-  // region.
+  // plan keeps one segment), that scan writes the state entering every
+  // 64-token segment, or every 16-token chunk for the exact hold and the
+  // convolution front (the region is sized for the chunks: the size query
+  // takes no options).  Otherwise 64-token segments are scanned side by side
+  // and folded.  The layouts share the region.
   if (!ckpt && G == 1) {
     const void* none[] = {nullptr};
     w.h16 = make_plan(batch, dim, seqlen, dstate, 4, none, 1).segs == 1;
@@ -1158,6 +1160,14 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
   if (!aligned(workspace, 256)) return S6_ERR_ALIGN;
   const int64_t S = w.S, nagg = S - 1, nblkb = w.nblkb, G = w.G, spp = w.spp, nlb = w.nlb;
   const bool h16 = w.h16;
+  // The sequential state-only scan stores the state entering every 16-token
+  // chunk for the exact hold and the convolution front, whose adjoint
+  // kernels would spend more recomputing the chunk starts (4.00 against
+  // 3.81 ms, 2.82 against 2.73 ms on the 3B layer), and the state entering
+  // every 64-token block otherwise, from which the adjoint kernel recomputes
+  // the chunk starts (1.873 against 1.930 ms: a quarter of the states
+  // written; bit-identical gradients).  The region is sized for the former.
+  const bool chunk16 = zoh || conv;
   char* wp = static_cast<char*>(workspace);
   float* agg = reinterpret_cast<float*>(wp + w.agg);
   float* sd = reinterpret_cast<float*>(wp + w.sd);
@@ -1174,7 +1184,7 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
   float* dxo = conv ? reinterpret_cast<float*>(wp + w.dxo) : nullptr;
   float* cpart = reinterpret_cast<float*>(wp + w.cpart);
 
-  // the state entering every chunk: one sequential state-only scan from h0
+  // the state entering every segment (or chunk): one sequential state-only scan from h0
   if (h16) {
     const void* vecptrs[] = {x, delta, Bm};
     Plan p = make_plan(batch, dim, seqlen, dstate, esz, vecptrs, 3);
@@ -1182,7 +1192,7 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
     ScanArgs g;
     memset(&g, 0, sizeof(g));
     g.x = x; g.delta = delta; g.Bm = Bm; g.A = A;
-    g.hinit = h0; g.hinit_stride = 0; g.ckpt = hin16;
+    g.hinit = h0; g.hinit_stride = 0; g.ckpt = hin16; g.ckpt_log2 = chunk16 ? 4 : 6;
     g.dbias = delta_bias; g.softplus = softplus; g.zoh = zoh;
     g.conv_w = cg.w; g.conv_b = cg.bias; g.conv_state = cg.state; g.conv_k = cg.width;
     g.D = dim; g.L = seqlen; g.N = dstate; g.seg_len = p.seg_len;
@@ -1230,8 +1240,8 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
       b.mu_in = muin;
     }
     if (rc == S6_OK)
-      rc = in_dtype == S6_BF16 ? launch_bwd<uint16_t>(b, gate, G, false, h16, st)
-                               : launch_bwd<float>(b, gate, G, false, h16, st);
+      rc = in_dtype == S6_BF16 ? launch_bwd<uint16_t>(b, gate, G, false, h16 && chunk16, st)
+                               : launch_bwd<float>(b, gate, G, false, h16 && chunk16, st);
   }
   if (rc == S6_OK) {
     const int64_t tot = batch * dstate * seqlen;

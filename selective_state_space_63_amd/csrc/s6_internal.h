@@ -136,8 +136,9 @@ struct ScanArgs {
   int64_t hout_last_only; // 1: only the last segment writes hout (at offset 0)
   float* ckpt;            // kModeY: the state entering every kCkpt-token block,
                           // (ceil(L / kCkpt), batch, D, N); kModeState (one
-                          // segment): the state entering every kT-token chunk,
-                          // (ceil(L / kT), batch, D, N); or null
+                          // segment): the state entering every 2^ckpt_log2
+                          // tokens, (ceil(L / 2^ckpt_log2), batch, D, N); or null
+  int ckpt_log2;          // kModeState with ckpt: 4 (every kT-token chunk) or 6 (every kCkpt tokens)
 };
 
 struct Plan {

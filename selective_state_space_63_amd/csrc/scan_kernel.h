@@ -316,12 +316,9 @@ s6_scan_kernel(ScanArgs a) {
   // (The offsets are rebuilt from the thread index here, inside the rarely
   // taken branch: values kept from outside would hold registers through the
   // whole chunk loop.)
-  // (y kernels: every kCkpt tokens; state-only kernels: every chunk, the
-  // states the backward's adjoint kernel starts its chunks from)
-  // (y kernels: every kCkpt tokens; state-only kernels: every chunk, the
-  // states the backward's adjoint kernel starts its chunks from)
-  constexpr bool ck_chunk = MODE == kModeState;
-  constexpr int ck_shift = ck_chunk ? 4 : 6;  // log2 of kT, kCkpt
+  // (The state-only kernels write the states the backward's adjoint kernel
+  // starts from: every kCkpt tokens, or every chunk when a.ckpt_log2 is 4.)
+  const int ck_shift = MODE == kModeState ? a.ckpt_log2 : 6;  // log2 of kT or kCkpt
   static_assert(kT == 16 && kCkpt == 64, "checkpoint strides");
   // uniform: elements per checkpoint and this block's first one (a division
   // here, not inside the chunk loop)
@@ -674,11 +671,11 @@ s6_scan_kernel(ScanArgs a) {
     else stage(buf ^ 1, k + 1, pre[SET][HALF], std::true_type{});
     __syncthreads();  // partial outputs of chunk k and the tiles of chunk k + 1 are complete
     if constexpr (HALF == WIN - 1) issue(tb + ((k + 1) / WIN + 2) * WT, pre[SET]);
-    if constexpr (kCk && ck_chunk) {
-      // the state after chunk k, stored after the window's loads are issued
-      // (as the y kernels store y)
+    if constexpr (kCk && MODE == kModeState) {
+      // the state after chunk k when a stride ends with it, stored after the
+      // window's loads are issued (as the y kernels store y)
       const int64_t tn = t0 + kT;
-      if (a.ckpt && tn < te) write_ckpt(tn);
+      if (a.ckpt && (tn & ((1 << ck_shift) - 1)) == 0 && tn < te) write_ckpt(tn);
     }
 
     if constexpr (MODE == kModeY) {

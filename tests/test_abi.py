@@ -300,9 +300,10 @@ def test_workspace_size_queries(lib, codes):
     assert _size(lib.s6_scan_fwd_workspace_size, 1, 64, 4096, 16, 9)[0] == codes["S6_ERR_DTYPE"]
     assert lib.s6_scan_fwd_workspace_size(1, 64, 4096, 16, 1, None) == codes["S6_ERR_NULL"]
     # backward of the 3B layer (one part; the sequential state-only scan
-    # fills the GPU): the state entering each of the 128 16-token chunks, the
-    # per-row partials of dA, dD and the bias gradient, and the
-    # per-16-channel-block dB/dC partials, which dominate
+    # fills the GPU): room for the state entering each of the 128 16-token
+    # chunks (the exact hold stores them all; the other levels one per
+    # 64-token segment), the per-row partials of dA, dD and the bias
+    # gradient, and the per-16-channel-block dB/dC partials, which dominate
     rc, full = _size(lib.s6_scan_bwd_workspace_size, 8, 5120, 2048, 16, 1, 0, 0)
     assert rc == ok
     st = 8 * 5120 * 16 * 4

@@ -116,8 +116,9 @@ def test_backward_small(torch_cuda, oracle, shape):
 
 # Shapes whose sequential state-only scan fills the GPU (batch x ceil(dim/32)
 # workgroups above half its slots): the backward then takes the state
-# entering every 16-token chunk from that scan instead of recomputing the
-# chunk starts.  Short rows keep the oracle fast.
+# entering every 64-token segment from that scan (every 16-token chunk under
+# the exact hold) instead of scanning segments side by side and folding them.
+# Short rows keep the oracle fast.
 CHUNK_STATE_SHAPES = [
     (8, 2592, 16, 100, synth.BF16, True),   # 648 workgroups; ragged last segment
     (2, 4128, 24, 70, synth.F32, True),     # two states per lane (8 waves): 258 workgroups
@@ -126,8 +127,8 @@ CHUNK_STATE_SHAPES = [
 
 
 def _chunk_state_layout(w):
-    """True when the backward's workspace holds one state per 16-token chunk
-    (the layout of the sequential state-only scan)."""
+    """True when the backward's workspace has room for one state per
+    16-token chunk (the region of the sequential state-only scan)."""
     from selective_state_space_63_amd import s6
     import torch
     dt = torch.float32 if w.dtype == synth.F32 else torch.bfloat16
@@ -140,9 +141,10 @@ def _chunk_state_layout(w):
 @pytest.mark.parametrize("mode", [None, "softplus", "zoh"])
 @pytest.mark.parametrize("shape", CHUNK_STATE_SHAPES, ids=lambda s: "b{}_d{}_n{}_l{}_{}_{}".format(*s))
 def test_backward_chunk_states(torch_cuda, oracle, shape, mode):
-    """The backward whose chunk-start states come from one sequential
-    state-only scan (plain and step-bias levels; the exact hold keeps the
-    recomputed chunk starts in the same workspace layout)."""
+    """The backward whose states come from one sequential state-only scan:
+    the state entering every 64-token segment, from which the adjoint kernel
+    recomputes the chunk starts (plain and step-bias levels), or every
+    16-token chunk (the exact hold)."""
     b, dm, n, L, dt, gate = shape
     w = synth.custom(b, dm, n, L, dt, gate, seed=4700 + L + dm)
     assert _chunk_state_layout(w), "the shape should take the sequential state-only scan"
