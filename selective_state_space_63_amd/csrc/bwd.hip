@@ -191,12 +191,14 @@ __device__ __forceinline__ float rows_sum4(const float (&v)[4]) {
 // waves per SIMD); held to 128 they spill a dozen values to scratch and run
 // 4-6% faster with the fourth wave.
 //
-// H16: a.hin holds the state entering every 16-token chunk (from a state-only
-// pass that wrote one per chunk), so the four chunk-start states of a segment
-// are loaded instead of recomputed from the segment's first state.
+// H16 (exact-hold and convolution levels): a.hin holds the state entering
+// every 16-token chunk (from a state-only pass that wrote one per chunk), so
+// the four chunk-start states of a segment are loaded instead of recomputed
+// from the segment's first state.
 template <typename In, bool GATE, int SPL, int OPT, bool H16>
 __global__ void __launch_bounds__(64 * bwd_waves<SPL>())
     __attribute__((amdgpu_waves_per_eu((OPT >= 2 && SPL == 1) ? 4 : 1))) s6_bwd_kernel(BwdArgs a) {
+  static_assert(!H16 || OPT >= 2, "per-chunk states: exact-hold and convolution levels only");
   constexpr bool SP = OPT >= 1;
   constexpr bool ZOH = OPT == 2;
   constexpr bool CONV = OPT == 3;  // the convolution front (its own kernels: it costs registers)
@@ -312,10 +314,7 @@ __global__ void __launch_bounds__(64 * bwd_waves<SPL>())
       }
     };
     // (the kernels held to 128 VGPRs load them after the staging)
-    if constexpr (OPT < 2) {
-      if constexpr (H16) load_hc16();
-      else load_hseg();
-    }
+    if constexpr (OPT < 2) load_hseg();
     __syncthreads();  // the previous segment's reads of the staged inputs are done
     for (int i = tid; i < CW * KS; i += NTHR) {
       const int cc = i / KS, t = i % KS;
@@ -970,14 +969,15 @@ int launch_bwd_g(const BwdArgs& a, bool gate, int64_t parts, bool carry, hipStre
               : launch_bwd_t<In, false, SPL, OPT, H16>(a, parts, carry, st);
 }
 
-// h16: a.hin holds the state entering every chunk (one part).
+// h16: a.hin holds the state entering every chunk (one part): the exact
+// hold and the convolution front only (the other levels start from one
+// state per 64-token segment).
 template <typename In, int SPL>
 int launch_bwd_h16(const BwdArgs& a, bool gate, int opt, hipStream_t st) {
   switch (opt) {
-    case 0: return launch_bwd_g<In, SPL, 0, true>(a, gate, 1, false, st);
-    case 1: return launch_bwd_g<In, SPL, 1, true>(a, gate, 1, false, st);
     case 2: return launch_bwd_g<In, SPL, 2, true>(a, gate, 1, false, st);
-    default: return launch_bwd_g<In, SPL, 3, true>(a, gate, 1, false, st);
+    case 3: return launch_bwd_g<In, SPL, 3, true>(a, gate, 1, false, st);
+    default: return S6_ERR_UNSUPPORTED;
   }
 }
 
