@@ -1165,8 +1165,9 @@ int scan_bwd_impl(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, in
   // kernels would spend more recomputing the chunk starts (4.00 against
   // 3.81 ms, 2.82 against 2.73 ms on the 3B layer), and the state entering
   // every 64-token block otherwise, from which the adjoint kernel recomputes
-  // the chunk starts (1.873 against 1.930 ms: a quarter of the states
-  // written; bit-identical gradients).  The region is sized for the former.
+  // the chunk starts (1.873-1.882 against 1.935-1.936 ms: a quarter of the
+  // states written; bit-identical gradients).  The region is sized for the
+  // former.
   const bool chunk16 = zoh || conv;
   char* wp = static_cast<char*>(workspace);
   float* agg = reinterpret_cast<float*>(wp + w.agg);
